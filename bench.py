@@ -1,0 +1,374 @@
+"""Benchmark of the gradient-bucket reduction path on one MI355X.
+
+Default workload (the headline metric): ZeRO-2 gradient sync of K = 8
+simulated ranks, 2,376,274,560 bf16 gradient elements per rank (~N(0, 1e-3),
+seeded), in five 500M-element buckets through the scheduler; each bucket is
+one fused ring-order reduce-scatter + /8 + fp32 cast into the ranks'
+partitioned flat gradients. One step = the whole sync (all five buckets).
+
+Byte model (the method's minimum traffic, each input read once, each output
+written once): per element index K*2 bytes read + 4 bytes written = 20 B,
+so 47.53 GB per step. `value` = those bytes / step time.
+
+Other workloads (--workload): zero3_ag (the 32-layer transformer all-gather
+in 162 prefetch buckets), allreduce64 (K = 64, N = 1,000,000,007 fused
+in-place all-reduce), flatten8 (the 64-fragment bucket flatten).
+
+Prints one JSON line. Only one GPU is used; --gpus above 1 exits.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import threading
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "gradient_sync_zr_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name, src_hash, bytes_per_launch):
+    """HBM traffic per launch from a committed rocprofv3 counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != src_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def host_cores():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def events_ms(pairs):
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+# ----------------------------------------------------------------- zero2
+def bench_zero2(args):
+    import numpy as np
+    import torch
+
+    import synth
+    from gradient_sync_zr_amd.steps import Zero2GradSync
+    from synth import workloads as W
+
+    cfg = W.ZERO2
+    K, N, bucket, sigma = cfg["K"], cfg["N_total"], cfg["bucket"], cfg["sigma"]
+    seed = W.seed_of(3)
+    grads = [torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    for r in range(K):
+        synth.dev_normal_bf16(grads[r], seed, r, 0, sigma)
+    buckets = W.zero2_buckets(N, bucket)
+    P = sum(-(-n // K) for _, n in buckets)
+    parts = [torch.empty(P, dtype=torch.float32, device="cuda") for _ in range(K)]
+    red = torch.cuda.Stream()
+    sync = Zero2GradSync(grads, parts, bucket, chunk_shift=cfg["shift"], average=True,
+                         reduction_stream=red)
+    torch.cuda.synchronize()
+    print(f"# zero2: K={K} N={N} buckets={len(buckets)} inputs resident", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        sync.step()
+    torch.cuda.synchronize()
+    timing = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        sync.step(timing=timing)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    step_bytes = sum(n * (2 * K + 4) for _, n in buckets)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    launch_ms = events_ms(timing)
+    launch_bytes = [n * (2 * K + 4) for _, n in buckets] * args.steps
+    achieved = sum(launch_bytes) / (sum(launch_ms) * 1e-3) / 1e9
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    bytes_per_launch = sum(launch_bytes) / len(launch_bytes)
+    src = kernel_source_hash(["zr_rs.hip", "zr_fold.hpp", "zr_device.hpp"])
+    traffic = read_traffic("rs_ring_bf16_f32_k8_zero2.counters.txt", src, bytes_per_launch)
+    print(f"# zero2: {ms_step:.3f} ms/step, kernel avg {avg_launch_ms:.3f} ms", file=sys.stderr,
+          flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_zero2(grads, parts, buckets[0], K, args)
+    sync.close()
+    return {
+        "metric": "reduce-scatter+avg+cast GB/s and % of HBM peak, K=8, 2.38B-elem bf16 grads",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic: seeded counter-based generator on the device, bf16 ~N(0,1e-3)",
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "reads_only_GBps": round(K * N * 2 / (ms_step * 1e-3) / 1e9, 1),
+        "config": {"workload": "zero2_grad_sync: K=8 simulated ranks in one HBM, "
+                               "2,376,274,560 bf16 grad elements per rank, 5 buckets of "
+                               "500M elements via the ping-pong scheduler, ring-order "
+                               "reduce-scatter + /8 + fp32 cast into the partitioned flat grad",
+                   "K": K, "N_per_rank": N, "bucket_elems": bucket, "n_buckets": len(buckets),
+                   "chunk_shift": 1, "io": "bf16 in, f32 out", "bytes_per_step": step_bytes,
+                   "parallelism": "1 GPU (K ranks simulated)"},
+        "roofline": {"bound": "hbm", "kernel": "rs_kernel<bf16,f32,K=8,avg,ring>",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "avg_launch_ms": round(avg_launch_ms, 4),
+                     "algorithmic_bytes_per_launch": int(bytes_per_launch),
+                     "kernel_source_sha256_16": src},
+        "cpu_baseline": cpu,
+    }
+
+
+def cpu_baseline_zero2(grads, parts, first_bucket, K, args):
+    """The oracle on bucket 0 of the same resident inputs (copied to the host,
+    not timed), split over host threads by chunk offset; also checks the GPU
+    partitions of that bucket bit for bit."""
+    import numpy as np
+    import torch
+
+    import oracle
+    start, n = first_bucket
+    C = -(-n // K)
+    M = min(C, args.cpu_sample_elems // K) if args.cpu_sample_elems else C
+    # the sample: offsets [0, M) of every chunk of bucket 0, as its own
+    # reduce-scatter problem with chunk size M
+    xs = []
+    for r in range(K):
+        rows = [grads[r][start + j * C:start + j * C + M].view(torch.int16).cpu().numpy()
+                for j in range(K)]
+        xs.append(np.concatenate(rows).view(np.uint16))
+    outs = [np.empty(M, dtype=np.float32) for _ in range(K)]
+    T = host_cores()
+
+    def work(i):
+        lo, hi = i * M // T, (i + 1) * M // T
+        oracle.reduce_scatter(xs, K * M, np.float32, shift=1, average=True, o_range=(lo, hi),
+                              out=outs)
+
+    th = [threading.Thread(target=work, args=(i,)) for i in range(T)]
+    t0 = time.perf_counter()
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    dt = time.perf_counter() - t0
+    gbs = K * M * (2 * K + 4) / dt / 1e9
+    exact = all(np.array_equal(parts[q][:M].cpu().numpy().view(np.uint32), outs[q].view(np.uint32))
+                for q in range(K))
+    return {"value": round(gbs, 2), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"offsets [0,{M}) of each of the 8 chunks of bucket 0 "
+                      f"({K * M} element indices, {K * M * (2 * K + 4) / 1e9:.2f} GB under "
+                      f"the same byte model); GPU partitions bit-exact on it: {exact}"}
+
+
+# ----------------------------------------------------------------- zero3
+def bench_zero3(args):
+    import torch
+
+    import synth
+    from gradient_sync_zr_amd.steps import Zero3Gather
+    from synth import workloads as W
+
+    cfg = W.ZERO3
+    K, sigma, shift = cfg["K"], cfg["sigma"], cfg["shift"]
+    seed = W.seed_of(4)
+    numels = [p.numel for p in W.llama_like_params()]
+    shard_numel = sum(-(-n // K) for n in numels)
+    full_numel = sum(numels)
+    shards = [torch.zeros(shard_numel, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    fulls = [torch.empty(full_numel, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    soff = 0
+    for p, n in enumerate(numels):
+        C = -(-n // K)
+        for r in range(K):
+            j = (r + shift) % K
+            cnt = max(0, min(C, n - j * C))
+            if cnt:
+                synth.dev_normal_bf16(shards[r][soff:soff + cnt], seed, p, j * C, sigma)
+        soff += C
+    gather = Zero3Gather(shards, fulls, numels, cfg["prefetch_bytes"] // cfg["elem_bytes"],
+                         chunk_shift=shift)
+    for _ in range(args.warmup):
+        gather.step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        gather.step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    step_bytes = full_numel * 2 + K * full_numel * 2   # shards read once + K full copies
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    return {
+        "metric": "all-gather GB/s (shard read + K full writes), K=8, 6.74B-param transformer",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded generator, bf16 ~N(0,0.02)",
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "config": {"workload": "zero3_allgather: 226 params (32 layers, hidden 4096, FFN 11008, "
+                               "vocab 32000), 1/8 shards, 162 greedy 50 MB prefetch buckets",
+                   "K": K, "params": len(numels), "n_buckets": len(gather.buckets),
+                   "bytes_per_step": step_bytes},
+        "roofline": {"bound": "hbm", "kernel": "ag_kernel<bf16,K=8>", "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "achieved": round(value, 1),
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+
+
+# ------------------------------------------------------------ allreduce64
+def bench_allreduce64(args):
+    import torch
+
+    import synth
+    import gradient_sync_zr_amd as zr
+    from synth import workloads as W
+
+    cfg = W.ALLREDUCE64
+    K, N = cfg["K"], cfg["N"]
+    seed = W.seed_of(5)
+    stride = -(-N // 128) * 128
+    buf = torch.empty(K * stride, dtype=torch.bfloat16, device="cuda")
+    ranks = [buf[r * stride:r * stride + N] for r in range(K)]
+    ptrs = [t.data_ptr() for t in ranks]
+
+    def regen():
+        for r in range(K):
+            synth.dev_normal_bf16(ranks[r], seed, r, 0, cfg["sigma"], cfg["outlier_p"],
+                                  cfg["outlier_mag"])
+
+    times = []
+    for i in range(args.warmup + args.steps):
+        regen()  # in-place sums grow, so every step starts from the same inputs (untimed)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        zr.zr_allreduce(ptrs, ptrs, N, average=False, fused=True, dtype=torch.bfloat16)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            times.append(e0.elapsed_time(e1))
+    ms_step = sum(times) / len(times)
+    step_bytes = 2 * K * N * 2
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    return {
+        "metric": "fused all-reduce GB/s (K reads + K writes), K=64, 1e9 bf16 elements",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic: seeded generator, bf16 ~N(0,1) with 1% at +-1e4",
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "config": {"workload": "allreduce64: K=64, N=1,000,000,007 per rank, in place, ring "
+                               "order, fp32 accumulation, bf16 out (step = the all-reduce; "
+                               "inputs regenerated untimed between steps)",
+                   "K": K, "N": N, "bytes_per_step": step_bytes},
+        "roofline": {"bound": "hbm", "kernel": "ar_kernel<bf16,K=64,ring>", "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "achieved": round(value, 1),
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+
+
+# -------------------------------------------------------------- flatten8
+def bench_flatten8(args):
+    import torch
+
+    import synth
+    import gradient_sync_zr_amd as zr
+    from synth import workloads as W
+
+    K, F = W.FLATTEN8["K"], W.FLATTEN8["n_frag"]
+    seed = W.seed_of(2)
+    sizes = W.flatten8_numels(F)
+    P = -(-sum(sizes) // K) * K
+    frags = [[torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in sizes] for _ in range(K)]
+    for r in range(K):
+        for p in range(F):
+            synth.dev_normal_bf16(frags[r][p], seed, W.flatten8_frag_stream(r, p), 0, 1e-3)
+    buckets = [torch.empty(P, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    parts = [torch.empty(P // K, dtype=torch.float32, device="cuda") for _ in range(K)]
+    fp = [[t.data_ptr() for t in row] for row in frags]
+    bp = [t.data_ptr() for t in buckets]
+    pp = [t.data_ptr() for t in parts]
+
+    def step():
+        zr.zr_flatten_bucket(fp, sizes, bp, P, dtype=torch.bfloat16)
+        zr.zr_reduce_scatter_avg(bp, P, pp, chunk_shift=1, average=True, in_dtype=torch.bfloat16,
+                                 out_dtype=torch.float32)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / args.steps
+    return {
+        "metric": "flatten + reduce-scatter-avg microseconds per bucket, K=8, 64 fragments",
+        "value": round(us, 2), "unit": "us", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic: seeded generator, bf16 ~N(0,1e-3)",
+        "config": {"workload": f"flatten8: K=8, 64 log-uniform fragments ({sum(sizes)} elements), "
+                               f"bucket padded to {P}, then RS + /8 + fp32 cast (cache-resident, "
+                               "launch-bound)", "K": K},
+        "roofline": None, "cpu_baseline": None,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="zero2",
+                    choices=["zero2", "zero3_ag", "allreduce64", "flatten8"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-elems", type=int, default=0,
+                    help="element indices in the CPU-baseline sample (default: all of bucket 0)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build simulates the K ranks on one GPU; --gpus {args.gpus} is not "
+              "supported (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    fn = {"zero2": bench_zero2, "zero3_ag": bench_zero3, "allreduce64": bench_allreduce64,
+          "flatten8": bench_flatten8}[args.workload]
+    print(json.dumps(fn(args)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

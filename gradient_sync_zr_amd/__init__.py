@@ -1,0 +1,218 @@
+"""Python binding of libzr: gradient-bucket reduction on MI355X (gfx950).
+
+Argument marshalling only. Every function here has the name of the C call it
+forwards to (see ``include/zr.h`` for the full contract) and does no
+arithmetic of its own: it turns per-rank torch tensors into tables of device
+pointers, torch streams into ``hipStream_t`` handles, and a non-OK status into
+:class:`ZrError`. PyTorch supplies device memory and streams, nothing else.
+
+The library must be built (``__graft_entry__.build()``); importing this module
+does not build it, and every call raises if ``libzr.so`` is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzr.so")
+
+ZR_OK, ZR_ERR_INVALID, ZR_ERR_ALIGN, ZR_ERR_ALIAS, ZR_ERR_UNSUPPORTED, ZR_ERR_HIP = range(6)
+ZR_BF16, ZR_FP32 = 0, 1
+ZR_ORDER_RING, ZR_ORDER_FREE = 0, 1
+STATUS_NAMES = {0: "ZR_OK", 1: "ZR_ERR_INVALID", 2: "ZR_ERR_ALIGN", 3: "ZR_ERR_ALIAS",
+                4: "ZR_ERR_UNSUPPORTED", 5: "ZR_ERR_HIP"}
+
+EXPORTS = ("zr_last_error", "zr_version", "zr_flatten_bucket", "zr_reduce_scatter_avg",
+           "zr_all_gather", "zr_allreduce", "zr_plan_buckets", "zr_sched_create",
+           "zr_sched_acquire", "zr_sched_submit_rs", "zr_sched_flush", "zr_sched_destroy")
+
+
+class ZrError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class zr_seg(ctypes.Structure):
+    _fields_ = [("shard_off", ctypes.c_int64), ("full_off", ctypes.c_int64),
+                ("numel", ctypes.c_int64)]
+
+
+_lib = None
+_i32, _i64, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libzr (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} not found: the HIP library is not built "
+                               "(run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        L.zr_last_error.restype = ctypes.c_char_p
+        L.zr_version.restype = ctypes.c_int
+        L.zr_flatten_bucket.argtypes = [_i32, _i32, _PP, ctypes.POINTER(_i64), _PP, _i64, _i32, _vp]
+        L.zr_reduce_scatter_avg.argtypes = [_i32, _PP, _i32, _i64, _PP, _i32, _i32, _i32, _i32, _vp]
+        L.zr_all_gather.argtypes = [_i32, _PP, _PP, _i32, ctypes.POINTER(zr_seg), _i32, _i32, _vp]
+        L.zr_allreduce.argtypes = [_i32, _PP, _PP, _i32, _i64, _i32, _i32, _i32, _vp, _vp]
+        L.zr_plan_buckets.argtypes = [_i32, ctypes.POINTER(_i64), _i64, ctypes.POINTER(ctypes.c_int32),
+                                      ctypes.POINTER(ctypes.c_int32)]
+        L.zr_sched_create.argtypes = [ctypes.POINTER(_vp), _i32, _i32, _vp]
+        L.zr_sched_acquire.argtypes = [_vp, _i32, _vp]
+        L.zr_sched_submit_rs.argtypes = [_vp, _i32, _PP, _i32, _i32, _PP, _i32, _i64, _PP, _i32,
+                                         _i32, _i32, _i32]
+        L.zr_sched_flush.argtypes = [_vp, _vp]
+        L.zr_sched_destroy.argtypes = [_vp]
+        for f in EXPORTS[2:]:
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != ZR_OK:
+        raise ZrError(status, lib().zr_last_error().decode(errors="replace"))
+
+
+# ------------------------------------------------------------ marshalling
+def _ptr(x) -> int:
+    """Device address of a tensor, or an int address passed through."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _table(xs: Optional[Sequence]):
+    if xs is None:
+        return None
+    return (ctypes.c_void_p * max(1, len(xs)))(*[_ptr(x) for x in xs])
+
+
+def _dtype(x) -> int:
+    import torch
+    if isinstance(x, int):
+        return x
+    dt = x if isinstance(x, torch.dtype) else x.dtype
+    if dt == torch.bfloat16:
+        return ZR_BF16
+    if dt == torch.float32:
+        return ZR_FP32
+    raise TypeError(f"unsupported dtype {dt}: bfloat16 or float32")
+
+
+def _stream(stream) -> int:
+    """hipStream_t of a torch stream (None = torch's current stream)."""
+    if isinstance(stream, int):
+        return stream
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------- calls
+def zr_version() -> int:
+    return lib().zr_version()
+
+
+def zr_last_error() -> str:
+    return lib().zr_last_error().decode(errors="replace")
+
+
+def zr_flatten_bucket(frags: Sequence[Sequence], numels: Sequence[int], buckets: Sequence,
+                      padded_numel: int, dtype=None, stream=None) -> None:
+    """frags[r][p] = fragment p of rank r; buckets[r] = rank r's flat bucket."""
+    K = len(buckets)
+    F = len(numels)
+    flat = [f for row in frags for f in row]
+    if len(flat) != K * F:
+        raise ValueError("frags must be K lists of len(numels) tensors")
+    dt = _dtype(dtype if dtype is not None else buckets[0])
+    nums = (ctypes.c_int64 * max(1, F))(*numels)
+    _check(lib().zr_flatten_bucket(K, F, _table(flat), nums, _table(buckets), padded_numel, dt,
+                                   _stream(stream)))
+
+
+def zr_reduce_scatter_avg(inputs: Sequence, N: int, outputs: Sequence, chunk_shift: int = 1,
+                          average: bool = True, order: int = ZR_ORDER_RING, in_dtype=None,
+                          out_dtype=None, stream=None) -> None:
+    K = len(inputs)
+    in_dt = _dtype(in_dtype if in_dtype is not None else inputs[0])
+    out_dt = _dtype(out_dtype if out_dtype is not None else outputs[0])
+    _check(lib().zr_reduce_scatter_avg(K, _table(inputs), in_dt, N, _table(outputs), out_dt,
+                                       chunk_shift, 1 if average else 0, order, _stream(stream)))
+
+
+def zr_all_gather(shards: Sequence, fulls: Sequence, segs: Sequence, chunk_shift: int = 0,
+                  dtype=None, stream=None) -> None:
+    """segs: (shard_off, full_off, numel) triples."""
+    K = len(shards)
+    dt = _dtype(dtype if dtype is not None else shards[0])
+    arr = (zr_seg * max(1, len(segs)))(*[zr_seg(*s) for s in segs])
+    _check(lib().zr_all_gather(K, _table(shards), _table(fulls), dt, arr, len(segs), chunk_shift,
+                               _stream(stream)))
+
+
+def zr_allreduce(inputs: Sequence, outputs: Sequence, N: int, average: bool = False,
+                 order: int = ZR_ORDER_RING, fused: bool = True, scratch=None, dtype=None,
+                 stream=None) -> None:
+    K = len(inputs)
+    dt = _dtype(dtype if dtype is not None else inputs[0])
+    _check(lib().zr_allreduce(K, _table(inputs), _table(outputs), dt, N, 1 if average else 0,
+                              order, 1 if fused else 0, _ptr(scratch), _stream(stream)))
+
+
+def zr_plan_buckets(numels: Sequence[int], cap: int):
+    """Returns (bucket_of list, n_buckets)."""
+    n = len(numels)
+    arr = (ctypes.c_int64 * max(1, n))(*numels)
+    out = (ctypes.c_int32 * max(1, n))()
+    nb = ctypes.c_int32(0)
+    _check(lib().zr_plan_buckets(n, arr, cap, out, ctypes.byref(nb)))
+    return list(out)[:n], nb.value
+
+
+class Sched:
+    """zr_sched_*: ping-pong IPG buffers with per-buffer completion events."""
+
+    def __init__(self, n_buffers: int = 2, max_producers: int = 4, reduction_stream=None):
+        h = ctypes.c_void_p()
+        self.reduction_stream = reduction_stream
+        _check(lib().zr_sched_create(ctypes.byref(h), n_buffers, max_producers,
+                                     _stream(reduction_stream)))
+        self._h = h
+
+    def acquire(self, buf: int, producer_stream=None) -> None:
+        _check(lib().zr_sched_acquire(self._h, buf, _stream(producer_stream)))
+
+    def submit_rs(self, buf: int, producer_streams: Sequence, inputs: Sequence, N: int,
+                  outputs: Sequence, chunk_shift: int = 1, average: bool = True,
+                  order: int = ZR_ORDER_RING, in_dtype=None, out_dtype=None) -> None:
+        K = len(inputs)
+        prods = (ctypes.c_void_p * max(1, len(producer_streams)))(
+            *[_stream(p) for p in producer_streams])
+        in_dt = _dtype(in_dtype if in_dtype is not None else inputs[0])
+        out_dt = _dtype(out_dtype if out_dtype is not None else outputs[0])
+        _check(lib().zr_sched_submit_rs(self._h, buf, prods, len(producer_streams), K,
+                                        _table(inputs), in_dt, N, _table(outputs), out_dt,
+                                        chunk_shift, 1 if average else 0, order))
+
+    def flush(self, caller_stream=None) -> None:
+        _check(lib().zr_sched_flush(self._h, _stream(caller_stream)))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().zr_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

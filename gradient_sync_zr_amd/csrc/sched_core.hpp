@@ -1,0 +1,130 @@
+// Bucket/stream scheduler logic, independent of the runtime it drives.
+//
+// The reduction runs on its own stream. Each physical IPG buffer index owns a
+// reduction-complete event; before a producer writes a buffer again it waits
+// on that buffer's event only, never on the whole reduction stream, and the
+// reduction stream waits on every stream that wrote the bucket before it
+// reads it. This is the per-buffer design proposed in "ZeRO-1/2
+// average_tensor serializes backward compute behind the preceding
+// reduction" (DeepSpeed issue 8364, Proposed design direction, steps 1-5):
+// the blanket reverse wait there made compute stall on the previous bucket's
+// collective. The epilogue flush makes the caller wait for everything
+// submitted ("DeepSpeed ZeRO-3 源码解析", 5.4).
+//
+// Backend requirements: types Stream and Event, and
+//   int create(Event*), int destroy(Event), int record(Event, Stream),
+//   int wait(Stream, Event)
+// returning 0 on success. wait() must capture the event's most recent
+// record at call time (HIP and CUDA stream semantics), which is what lets a
+// producer event be re-recorded for the next bucket while an earlier wait on
+// it is still queued.
+#pragma once
+
+#include <vector>
+
+namespace zr {
+
+enum class SchedErr { kOk = 0, kBadBuf, kBadState, kTooManyProducers, kBackend, kBadArg };
+
+template <class Backend>
+class SchedCore {
+  public:
+    using Stream = typename Backend::Stream;
+    using Event = typename Backend::Event;
+
+    SchedCore(Backend& be, Stream reduction) : be_(be), red_(reduction) {}
+    SchedCore(const SchedCore&) = delete;
+    SchedCore& operator=(const SchedCore&) = delete;
+
+    // Creates every event up front; nothing is created on the hot path.
+    SchedErr init(int n_buffers, int max_producers) {
+        if (n_buffers < 1 || max_producers < 0) return SchedErr::kBadArg;
+        max_prod_ = max_producers;
+        bufs_.resize(n_buffers);
+        for (Buf& b : bufs_) {
+            if (be_.create(&b.done)) return SchedErr::kBackend;
+            b.has_done = true;
+            b.prod.resize(max_producers);
+            for (int i = 0; i < max_producers; ++i) {
+                if (be_.create(&b.prod[i])) return SchedErr::kBackend;
+                ++b.n_prod_created;
+            }
+        }
+        if (be_.create(&tail_)) return SchedErr::kBackend;
+        has_tail_ = true;
+        return SchedErr::kOk;
+    }
+
+    void release() {
+        for (Buf& b : bufs_) {
+            if (b.has_done) be_.destroy(b.done);
+            for (int i = 0; i < b.n_prod_created; ++i) be_.destroy(b.prod[i]);
+            b.has_done = false;
+            b.n_prod_created = 0;
+        }
+        if (has_tail_) be_.destroy(tail_);
+        has_tail_ = false;
+    }
+
+    int n_buffers() const { return (int)bufs_.size(); }
+
+    // The producer is about to overwrite buffer `buf`: it waits for the
+    // reduction that last read this buffer, if one was submitted.
+    SchedErr acquire(int buf, Stream producer) {
+        if (buf < 0 || buf >= (int)bufs_.size()) return SchedErr::kBadBuf;
+        Buf& b = bufs_[buf];
+        if (b.state == State::kAcquired) return SchedErr::kBadState;
+        if (b.state == State::kSubmitted && be_.wait(producer, b.done)) return SchedErr::kBackend;
+        b.state = State::kAcquired;
+        return SchedErr::kOk;
+    }
+
+    // The bucket in `buf` is complete. The reduction stream waits on every
+    // producer stream, `launch(reduction_stream)` enqueues the reduction
+    // (returns true on success), and the buffer's completion event is
+    // recorded after it.
+    template <class Launch>
+    SchedErr submit(int buf, const Stream* producers, int n_prod, Launch&& launch) {
+        if (buf < 0 || buf >= (int)bufs_.size()) return SchedErr::kBadBuf;
+        Buf& b = bufs_[buf];
+        if (b.state != State::kAcquired) return SchedErr::kBadState;
+        if (n_prod < 0 || n_prod > max_prod_) return SchedErr::kTooManyProducers;
+        if (n_prod > 0 && !producers) return SchedErr::kBadArg;
+        for (int i = 0; i < n_prod; ++i) {
+            if (be_.record(b.prod[i], producers[i])) return SchedErr::kBackend;
+            if (be_.wait(red_, b.prod[i])) return SchedErr::kBackend;
+        }
+        if (!launch(red_)) return SchedErr::kBackend;
+        if (be_.record(b.done, red_)) return SchedErr::kBackend;
+        b.state = State::kSubmitted;
+        any_submitted_ = true;
+        return SchedErr::kOk;
+    }
+
+    // Epilogue: the caller waits for all reduction work submitted so far.
+    SchedErr flush(Stream caller) {
+        if (!any_submitted_) return SchedErr::kOk;
+        if (be_.record(tail_, red_)) return SchedErr::kBackend;
+        if (be_.wait(caller, tail_)) return SchedErr::kBackend;
+        return SchedErr::kOk;
+    }
+
+  private:
+    enum class State { kIdle, kAcquired, kSubmitted };
+    struct Buf {
+        State state = State::kIdle;
+        Event done{};
+        bool has_done = false;
+        std::vector<Event> prod;
+        int n_prod_created = 0;
+    };
+    Backend& be_;
+    Stream red_;
+    int max_prod_ = 0;
+    std::vector<Buf> bufs_;
+    Event tail_{};
+    bool has_tail_ = false;
+    bool any_submitted_ = false;
+};
+
+}  // namespace zr

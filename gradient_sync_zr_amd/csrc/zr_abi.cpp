@@ -1,0 +1,377 @@
+// C-ABI layer: argument validation (before any HIP call), error reporting,
+// launch-shape tuning, and dispatch to the kernels. Nothing here allocates
+// device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+#include <vector>
+
+#include "zr.h"
+#include "zr_internal.hpp"
+
+namespace zr {
+
+namespace {
+
+thread_local std::string g_err;
+
+zr_status fail(zr_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+zr_status ok() { return ZR_OK; }
+
+// Largest element count per rank buffer (2^40): keeps every tile index of the
+// kernels within 32 bits.
+constexpr int64_t kMaxElems = 1LL << 40;
+
+zr_status hip_fail(hipError_t e, const char* what) {
+    return fail(ZR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dt_valid(int dt) { return dt == ZR_BF16 || dt == ZR_FP32; }
+int64_t dt_bytes(zr_dtype dt) { return dt == ZR_BF16 ? 2 : 4; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
+Range range_of(const void* p, int64_t elems, int64_t es) {
+    return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)(elems * es)};
+}
+
+int env_int(const char* name, int dflt, int lo, int hi) {
+    const char* v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    int x = std::atoi(v);
+    return x < lo ? lo : (x > hi ? hi : x);
+}
+
+zr_status check_k(int K) {
+    if (K < 1 || K > kMaxRanks) return fail(ZR_ERR_INVALID, "K=%d out of range [1, %d]", K, kMaxRanks);
+    return ok();
+}
+
+// Non-null and aligned to the element size.
+zr_status check_table(const void* const* t, int K, int64_t es, const char* name) {
+    if (!t) return fail(ZR_ERR_INVALID, "%s table is NULL", name);
+    for (int r = 0; r < K; ++r) {
+        if (!t[r]) return fail(ZR_ERR_INVALID, "%s[%d] is NULL", name, r);
+        if (((uintptr_t)t[r]) % (uintptr_t)es)
+            return fail(ZR_ERR_ALIGN, "%s[%d]=%p is not aligned to %lld bytes", name, r, t[r],
+                        (long long)es);
+    }
+    return ok();
+}
+
+// The K ranges of one table must be pairwise disjoint.
+zr_status check_distinct(const std::vector<Range>& rs, const char* name) {
+    for (size_t a = 0; a < rs.size(); ++a)
+        for (size_t b = a + 1; b < rs.size(); ++b)
+            if (overlaps(rs[a], rs[b]))
+                return fail(ZR_ERR_ALIAS, "%s[%zu] and %s[%zu] overlap", name, a, name, b);
+    return ok();
+}
+
+zr_status check_disjoint(const std::vector<Range>& xs, const char* xn, const std::vector<Range>& ys,
+                         const char* yn) {
+    for (size_t a = 0; a < xs.size(); ++a)
+        for (size_t b = 0; b < ys.size(); ++b)
+            if (overlaps(xs[a], ys[b]))
+                return fail(ZR_ERR_ALIAS, "%s[%zu] overlaps %s[%zu]", xn, a, yn, b);
+    return ok();
+}
+
+#define ZR_TRY(expr)                       \
+    do {                                   \
+        zr_status st_ = (expr);            \
+        if (st_ != ZR_OK) return st_;      \
+    } while (0)
+
+}  // namespace
+
+zr_status set_error(zr_status st, const char* msg) {
+    g_err = msg ? msg : "";
+    return st;
+}
+
+const Tuning& tuning() {
+    static const Tuning t = {
+        env_int("ZR_RS_BLOCKS_PER_CU", 8, 1, 64),
+        env_int("ZR_AR_BLOCKS_PER_CU", 8, 1, 64),
+        env_int("ZR_AG_BLOCKS_PER_CU", 8, 1, 64),
+        env_int("ZR_NONTEMPORAL", 0, 0, 1),
+    };
+    return t;
+}
+
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (dev < 64) {
+        int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Validation of a reduce-scatter call; shared with the scheduler.
+zr_status validate_rs(int K, const void* const* in, zr_dtype in_dt, int64_t N, void* const* out,
+                      zr_dtype out_dt, int shift, zr_order order, bool* no_work) {
+    ZR_TRY(check_k(K));
+    if (N < 0) return fail(ZR_ERR_INVALID, "N=%lld is negative", (long long)N);
+    if (!dt_valid(in_dt) || !dt_valid(out_dt))
+        return fail(ZR_ERR_UNSUPPORTED, "dtype pair (%d, %d) not supported", (int)in_dt, (int)out_dt);
+    if (shift < 0 || shift >= K) return fail(ZR_ERR_INVALID, "chunk_shift=%d not in [0, %d)", shift, K);
+    if (order != ZR_ORDER_RING && order != ZR_ORDER_FREE)
+        return fail(ZR_ERR_INVALID, "order=%d is not a zr_order", (int)order);
+    *no_work = (N == 0);
+    if (N == 0) return ok();
+    if (N > kMaxElems) return fail(ZR_ERR_INVALID, "N=%lld too large", (long long)N);
+    const int64_t C = (N + K - 1) / K;
+    ZR_TRY(check_table(in, K, dt_bytes(in_dt), "in"));
+    ZR_TRY(check_table(const_cast<const void* const*>(out), K, dt_bytes(out_dt), "out"));
+    std::vector<Range> ri(K), ro(K);
+    for (int r = 0; r < K; ++r) {
+        ri[r] = range_of(in[r], N, dt_bytes(in_dt));
+        ro[r] = range_of(out[r], C, dt_bytes(out_dt));
+    }
+    ZR_TRY(check_distinct(ro, "out"));
+    ZR_TRY(check_disjoint(ro, "out", ri, "in"));
+    return ok();
+}
+
+zr_status run_rs(int K, const void* const* in, zr_dtype in_dt, int64_t N, void* const* out,
+                 zr_dtype out_dt, int shift, int average, zr_order order, hipStream_t stream) {
+    ConstPtrs ip{};
+    MutPtrs op{};
+    for (int r = 0; r < K; ++r) {
+        ip.p[r] = in[r];
+        op.p[r] = out[r];
+    }
+    hipError_t e = launch_reduce_scatter(K, ip, in_dt, N, op, out_dt, shift, average ? 1 : 0, order, stream);
+    if (e != hipSuccess) return hip_fail(e, "reduce-scatter launch");
+    return ok();
+}
+
+zr_status validate_ag(int K, const void* const* shards, void* const* fulls, zr_dtype dt,
+                      const zr_seg* segs, int n_segs, int shift, bool* no_work) {
+    ZR_TRY(check_k(K));
+    if (!dt_valid(dt)) return fail(ZR_ERR_UNSUPPORTED, "dtype %d not supported", (int)dt);
+    if (shift < 0 || shift >= K) return fail(ZR_ERR_INVALID, "chunk_shift=%d not in [0, %d)", shift, K);
+    if (n_segs < 0) return fail(ZR_ERR_INVALID, "n_segs=%d is negative", n_segs);
+    if (n_segs > 0 && !segs) return fail(ZR_ERR_INVALID, "segs is NULL");
+    int64_t full_lo = INT64_MAX, full_hi = 0, shard_lo = INT64_MAX, shard_hi = 0;
+    std::vector<std::pair<int64_t, int64_t>> fr;
+    for (int s = 0; s < n_segs; ++s) {
+        if (segs[s].numel < 0 || segs[s].shard_off < 0 || segs[s].full_off < 0)
+            return fail(ZR_ERR_INVALID, "segment %d has a negative field", s);
+        if (segs[s].numel == 0) continue;
+        if (segs[s].numel > kMaxElems) return fail(ZR_ERR_INVALID, "segment %d too large", s);
+        const int64_t C = (segs[s].numel + K - 1) / K;
+        full_lo = std::min(full_lo, segs[s].full_off);
+        full_hi = std::max(full_hi, segs[s].full_off + segs[s].numel);
+        shard_lo = std::min(shard_lo, segs[s].shard_off);
+        shard_hi = std::max(shard_hi, segs[s].shard_off + C);
+        fr.push_back({segs[s].full_off, segs[s].full_off + segs[s].numel});
+    }
+    *no_work = fr.empty();
+    if (fr.empty()) return ok();
+    std::sort(fr.begin(), fr.end());
+    for (size_t i = 1; i < fr.size(); ++i)
+        if (fr[i].first < fr[i - 1].second)
+            return fail(ZR_ERR_ALIAS, "two segments write overlapping full ranges");
+    const int64_t es = dt_bytes(dt);
+    ZR_TRY(check_table(shards, K, es, "shards"));
+    ZR_TRY(check_table(const_cast<const void* const*>(fulls), K, es, "fulls"));
+    std::vector<Range> rf(K), rsh(K);
+    for (int r = 0; r < K; ++r) {
+        rf[r] = Range{(uintptr_t)fulls[r] + (uintptr_t)(full_lo * es), (uintptr_t)fulls[r] + (uintptr_t)(full_hi * es)};
+        rsh[r] = Range{(uintptr_t)shards[r] + (uintptr_t)(shard_lo * es), (uintptr_t)shards[r] + (uintptr_t)(shard_hi * es)};
+    }
+    ZR_TRY(check_distinct(rf, "fulls"));
+    ZR_TRY(check_disjoint(rf, "fulls", rsh, "shards"));
+    return ok();
+}
+
+zr_status run_ag(int K, const void* const* shards, void* const* fulls, zr_dtype dt, const zr_seg* segs,
+                 int n_segs, int shift, hipStream_t stream) {
+    ConstPtrs sp{};
+    MutPtrs fp{};
+    for (int r = 0; r < K; ++r) {
+        sp.p[r] = shards[r];
+        fp.p[r] = fulls[r];
+    }
+    for (int s0 = 0; s0 < n_segs; s0 += kAgSegsPerLaunch) {
+        const int n = std::min(kAgSegsPerLaunch, n_segs - s0);
+        hipError_t e = launch_all_gather(K, sp, fp, dt, segs + s0, n, shift, stream);
+        if (e != hipSuccess) return hip_fail(e, "all-gather launch");
+    }
+    return ok();
+}
+
+}  // namespace zr
+
+using namespace zr;
+
+extern "C" {
+
+const char* zr_last_error(void) { return g_err.c_str(); }
+
+int zr_version(void) { return 100; }  // 0.1.0
+
+zr_status zr_reduce_scatter_avg(int K, const void* const* in, zr_dtype in_dt, int64_t N,
+                                void* const* out, zr_dtype out_dt, int chunk_shift, int average,
+                                zr_order order, void* stream) {
+    bool no_work = false;
+    ZR_TRY(validate_rs(K, in, in_dt, N, out, out_dt, chunk_shift, order, &no_work));
+    if (no_work) return ok();
+    return run_rs(K, in, in_dt, N, out, out_dt, chunk_shift, average, order, (hipStream_t)stream);
+}
+
+zr_status zr_all_gather(int K, const void* const* shards, void* const* fulls, zr_dtype dt,
+                        const zr_seg* segs, int n_segs, int chunk_shift, void* stream) {
+    bool no_work = false;
+    ZR_TRY(validate_ag(K, shards, fulls, dt, segs, n_segs, chunk_shift, &no_work));
+    if (no_work) return ok();
+    return run_ag(K, shards, fulls, dt, segs, n_segs, chunk_shift, (hipStream_t)stream);
+}
+
+zr_status zr_allreduce(int K, const void* const* in, void* const* out, zr_dtype dt, int64_t N,
+                       int average, zr_order order, int fused, void* scratch, void* stream) {
+    ZR_TRY(check_k(K));
+    if (N < 0) return fail(ZR_ERR_INVALID, "N=%lld is negative", (long long)N);
+    if (!dt_valid(dt)) return fail(ZR_ERR_UNSUPPORTED, "dtype %d not supported", (int)dt);
+    if (order != ZR_ORDER_RING && order != ZR_ORDER_FREE)
+        return fail(ZR_ERR_INVALID, "order=%d is not a zr_order", (int)order);
+    if (N == 0) return ok();
+    const int64_t es = dt_bytes(dt);
+    const int64_t C = (N + K - 1) / K;
+    if (N > kMaxElems) return fail(ZR_ERR_INVALID, "N=%lld too large", (long long)N);
+    ZR_TRY(check_table(in, K, es, "in"));
+    ZR_TRY(check_table(const_cast<const void* const*>(out), K, es, "out"));
+    std::vector<Range> ri(K), ro(K);
+    for (int r = 0; r < K; ++r) {
+        ri[r] = range_of(in[r], N, es);
+        ro[r] = range_of(out[r], N, es);
+    }
+    ZR_TRY(check_distinct(ro, "out"));
+    for (int a = 0; a < K; ++a)
+        for (int b = 0; b < K; ++b) {
+            if (a == b && in[a] == out[a]) continue;
+            if (overlaps(ro[a], ri[b]))
+                return fail(ZR_ERR_ALIAS, "out[%d] overlaps in[%d] (only out[r] == in[r] is allowed)", a, b);
+        }
+    hipStream_t s = (hipStream_t)stream;
+    if (fused) {
+        ConstPtrs ip{};
+        MutPtrs op{};
+        for (int r = 0; r < K; ++r) {
+            ip.p[r] = in[r];
+            op.p[r] = out[r];
+        }
+        hipError_t e = launch_allreduce_fused(K, ip, op, dt, N, average ? 1 : 0, order, s);
+        if (e != hipSuccess) return hip_fail(e, "all-reduce launch");
+        return ok();
+    }
+    if (!scratch) return fail(ZR_ERR_INVALID, "scratch is NULL (needed when fused == 0)");
+    if (((uintptr_t)scratch) % (uintptr_t)es) return fail(ZR_ERR_ALIGN, "scratch is not aligned");
+    const Range rsc = range_of(scratch, K * C, es);
+    for (int r = 0; r < K; ++r)
+        if (overlaps(rsc, ri[r]) || overlaps(rsc, ro[r]))
+            return fail(ZR_ERR_ALIAS, "scratch overlaps rank %d's buffers", r);
+    std::vector<void*> sh(K);
+    for (int q = 0; q < K; ++q) sh[q] = (char*)scratch + (size_t)(q * C * es);
+    ZR_TRY(run_rs(K, in, dt, N, sh.data(), dt, 1, average, order, s));
+    zr_seg seg{0, 0, N};
+    return run_ag(K, const_cast<const void* const*>(sh.data()), out, dt, &seg, 1, 1, s);
+}
+
+zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const int64_t* numels,
+                            void* const* buckets, int64_t padded_numel, zr_dtype dt, void* stream) {
+    ZR_TRY(check_k(K));
+    if (n_frag < 0) return fail(ZR_ERR_INVALID, "n_frag=%d is negative", n_frag);
+    if (!dt_valid(dt)) return fail(ZR_ERR_UNSUPPORTED, "dtype %d not supported", (int)dt);
+    if (n_frag > 0 && (!frags || !numels)) return fail(ZR_ERR_INVALID, "frags or numels is NULL");
+    const int64_t es = dt_bytes(dt);
+    int64_t total = 0;
+    for (int p = 0; p < n_frag; ++p) {
+        if (numels[p] < 0) return fail(ZR_ERR_INVALID, "numels[%d] is negative", p);
+        total += numels[p];
+    }
+    if (padded_numel < total)
+        return fail(ZR_ERR_INVALID, "padded_numel=%lld < total fragment size %lld", (long long)padded_numel,
+                    (long long)total);
+    if (padded_numel == 0) return ok();
+    ZR_TRY(check_table(const_cast<const void* const*>(buckets), K, es, "buckets"));
+    std::vector<Range> rb(K), rf;
+    for (int r = 0; r < K; ++r) rb[r] = range_of(buckets[r], padded_numel, es);
+    ZR_TRY(check_distinct(rb, "buckets"));
+    for (int r = 0; r < K; ++r)
+        for (int p = 0; p < n_frag; ++p) {
+            const void* f = frags[(size_t)r * n_frag + p];
+            if (numels[p] == 0) continue;
+            if (!f) return fail(ZR_ERR_INVALID, "fragment %d of rank %d is NULL", p, r);
+            if (((uintptr_t)f) % (uintptr_t)es)
+                return fail(ZR_ERR_ALIGN, "fragment %d of rank %d is not aligned", p, r);
+            rf.push_back(range_of(f, numels[p], es));
+        }
+    ZR_TRY(check_disjoint(rb, "buckets", rf, "fragment"));
+    std::vector<CopyJob> jobs;
+    jobs.reserve((size_t)K * (n_frag + 1));
+    for (int r = 0; r < K; ++r) {
+        int64_t off = 0;
+        char* b = static_cast<char*>(buckets[r]);
+        for (int p = 0; p < n_frag; ++p) {
+            if (numels[p] > 0) jobs.push_back(CopyJob{frags[(size_t)r * n_frag + p], b + off * es, numels[p]});
+            off += numels[p];
+        }
+        if (padded_numel > off) jobs.push_back(CopyJob{nullptr, b + off * es, padded_numel - off});
+    }
+    hipStream_t s = (hipStream_t)stream;
+    for (size_t i = 0; i < jobs.size(); i += kFlatJobsPerLaunch) {
+        const int n = (int)std::min<size_t>(kFlatJobsPerLaunch, jobs.size() - i);
+        hipError_t e = launch_flatten(jobs.data() + i, n, (int)es, s);
+        if (e != hipSuccess) return hip_fail(e, "flatten launch");
+    }
+    return ok();
+}
+
+zr_status zr_plan_buckets(int n, const int64_t* numels, int64_t cap, int32_t* bucket_of,
+                          int32_t* n_buckets) {
+    if (n < 0) return fail(ZR_ERR_INVALID, "n=%d is negative", n);
+    if (cap < 1) return fail(ZR_ERR_INVALID, "cap=%lld < 1", (long long)cap);
+    if (!n_buckets || (n > 0 && (!numels || !bucket_of)))
+        return fail(ZR_ERR_INVALID, "NULL argument");
+    int32_t b = -1;
+    int64_t total = 0;
+    for (int i = 0; i < n; ++i) {
+        if (numels[i] < 0) return fail(ZR_ERR_INVALID, "numels[%d] is negative", i);
+        if (b < 0 || total >= cap) {
+            ++b;
+            total = 0;
+        }
+        bucket_of[i] = b;
+        total += numels[i];
+    }
+    *n_buckets = b + 1;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// All-gather of sharded tensors into K full copies.
+//
+// ZeRO-3 keeps each parameter as 1/K shards and gathers the full tensor
+// before use ("DeepSpeed ZeRO-3 源码解析", sections 1 and 2.1); the ring's
+// second phase forwards each reduced chunk around the ring, receivers
+// overwriting their copy ("图解 Ring All-Reduce", Phase 2). On one device the
+// forwarding collapses to: chunk j of the full tensor is shard
+// (j - shift) mod K, copied to every rank's full buffer.
+//
+// Grid: blockIdx.y = segment (one tensor), blockIdx.x strides over
+// (chunk, 2048-element tile) pairs of that segment. A lane loads its 8 shard
+// elements once (16 bytes) and stores them to all K full buffers, so each
+// shard byte is read once and written K times. Chunk starts that are not
+// 16-byte aligned on either side, and ragged ends, copy element by element.
+#include "zr_device.hpp"
+#include "zr_internal.hpp"
+
+namespace zr {
+namespace {
+
+struct AgSeg {
+    int64_t shard_off, full_off, numel, C;
+    uint64_t vec_mask;  // bit j: chunk j is 16-byte aligned in shard and full
+    int tiles_per_chunk;
+    int pad_;
+};
+
+struct AgArgs {
+    ConstPtrs shards;
+    MutPtrs fulls;
+    AgSeg seg[kAgSegsPerLaunch];
+    int K, shift;
+};
+
+template <typename T, int KS, bool NT>
+__global__ void __launch_bounds__(kThreads) ag_kernel(const AgArgs a) {
+    const int K = KS > 0 ? KS : a.K;
+    const AgSeg& sg = a.seg[blockIdx.y];
+    const int total = K * sg.tiles_per_chunk;
+    for (int u = blockIdx.x; u < total; u += gridDim.x) {
+        const int j = u / sg.tiles_per_chunk;
+        const int t = u - j * sg.tiles_per_chunk;
+        int holder = j - a.shift;
+        if (holder < 0) holder += K;
+        const int64_t o = (int64_t)t * kTile + (int64_t)threadIdx.x * kGroup;
+        const int64_t g = (int64_t)j * sg.C + o;
+        if (o >= sg.C || g >= sg.numel) continue;
+        const T* src = static_cast<const T*>(a.shards.p[holder]) + sg.shard_off + o;
+        const int64_t dst_off = sg.full_off + g;
+        if (((sg.vec_mask >> j) & 1ull) && o + kGroup <= sg.C && g + kGroup <= sg.numel) {
+            const Group<T> v = load_group<T, NT>(src);
+            if constexpr (KS > 0) {
+#pragma unroll
+                for (int r = 0; r < KS; ++r) store_group<T, NT>(static_cast<T*>(a.fulls.p[r]) + dst_off, v);
+            } else {
+                for (int r = 0; r < K; ++r) store_group<T, NT>(static_cast<T*>(a.fulls.p[r]) + dst_off, v);
+            }
+        } else {
+            int64_t n = sg.C - o;
+            if (sg.numel - g < n) n = sg.numel - g;
+            if (n > kGroup) n = kGroup;
+            for (int e = 0; e < (int)n; ++e) {
+                const T v = src[e];
+                for (int r = 0; r < K; ++r) static_cast<T*>(a.fulls.p[r])[dst_off + e] = v;
+            }
+        }
+    }
+}
+
+template <typename T, int KS, bool NT>
+hipError_t launch_t(const AgArgs& a, int n_segs, int max_units, hipStream_t stream) {
+    int64_t want = (int64_t)device_cu_count() * tuning().ag_blocks_per_cu / n_segs;
+    if (want < 1) want = 1;
+    const int gx = (int)(want < max_units ? want : max_units);
+    hipLaunchKernelGGL((ag_kernel<T, KS, NT>), dim3(gx, n_segs), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T, int KS>
+hipError_t pick_nt(const AgArgs& a, int n_segs, int max_units, hipStream_t s) {
+    return tuning().nontemporal ? launch_t<T, KS, true>(a, n_segs, max_units, s)
+                                : launch_t<T, KS, false>(a, n_segs, max_units, s);
+}
+
+template <typename T>
+hipError_t pick_k(const AgArgs& a, int n_segs, int max_units, hipStream_t s) {
+    switch (a.K) {
+        case 8: return pick_nt<T, 8>(a, n_segs, max_units, s);
+        default: return pick_nt<T, 0>(a, n_segs, max_units, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_all_gather(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype dt,
+                             const zr_seg* segs, int n_segs, int shift, hipStream_t stream) {
+    AgArgs a;
+    a.shards = shards;
+    a.fulls = fulls;
+    a.K = K;
+    a.shift = shift;
+    const int es = dt == ZR_BF16 ? 2 : 4;
+    bool bases = true;
+    for (int r = 0; r < K; ++r)
+        bases = bases && (((uintptr_t)shards.p[r]) & 15) == 0 && (((uintptr_t)fulls.p[r]) & 15) == 0;
+    int used = 0, max_units = 1;
+    for (int s = 0; s < n_segs; ++s) {
+        if (segs[s].numel == 0) continue;
+        AgSeg& d = a.seg[used++];
+        d.shard_off = segs[s].shard_off;
+        d.full_off = segs[s].full_off;
+        d.numel = segs[s].numel;
+        d.C = (d.numel + K - 1) / K;
+        d.tiles_per_chunk = (int)((d.C + kTile - 1) / kTile);
+        d.pad_ = 0;
+        d.vec_mask = 0;
+        for (int j = 0; j < K; ++j) {
+            const bool ok = bases && ((d.shard_off * es) & 15) == 0 &&
+                            (((d.full_off + (int64_t)j * d.C) * es) & 15) == 0;
+            if (ok) d.vec_mask |= 1ull << j;
+        }
+        const int units = K * d.tiles_per_chunk;
+        if (units > max_units) max_units = units;
+    }
+    if (used == 0) return hipSuccess;
+    if (dt == ZR_BF16) return pick_k<uint16_t>(a, used, max_units, stream);
+    return pick_k<float>(a, used, max_units, stream);
+}
+
+}  // namespace zr

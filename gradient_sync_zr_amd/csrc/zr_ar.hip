@@ -1,0 +1,137 @@
+// Fused all-reduce: reduce-scatter and all-gather in one pass.
+//
+// All-reduce is reduce-scatter followed by all-gather (CMU 11-868 lecture 14
+// notes, 2.2). On one device the two phases need not meet in memory: each
+// lane reads the K values of its 8 global indices, folds them in the ring
+// order of the chunk they belong to ("图解 Ring All-Reduce", Phase 1), rounds
+// once to the buffer dtype, and writes the same bits to all K ranks (the
+// all-gather result of Phase 2, where every rank ends with identical sums).
+// Output may be the input (in place): a lane writes index g only after it
+// has read index g from every rank, and no other lane touches g.
+//
+// Tiles are 2048 aligned global indices. A tile that lies inside one chunk
+// and below N takes the 16-byte path with the chunk (hence the fold's first
+// rank) uniform across the block; a tile that straddles a chunk boundary or
+// the end of the buffer (at most K of them) folds element by element, reading
+// the rank pointers from an LDS table.
+#include "zr_fold.hpp"
+
+namespace zr {
+namespace {
+
+struct ArArgs {
+    ConstPtrs in;
+    MutPtrs out;
+    int64_t N, C, n_tiles;
+    int K;
+    int vec;  // every in/out base 16-byte aligned
+    float inv_k, kf;
+};
+
+template <typename T, int KS, int AVG, bool RING, bool NT>
+__global__ void __launch_bounds__(kThreads) ar_kernel(const ArArgs a) {
+    const int K = KS > 0 ? KS : a.K;
+    __shared__ const void* s_in[kMaxRanks];
+    if (threadIdx.x == 0)
+        for (int r = 0; r < K; ++r) s_in[r] = a.in.p[r];
+    __syncthreads();
+    auto lds_ptr = [&](int r) { return s_in[r]; };
+    const int64_t N = a.N, C = a.C;
+
+    for (int64_t t = blockIdx.x; t < a.n_tiles; t += gridDim.x) {
+        const int64_t t0 = t * kTile;
+        const int64_t t1 = (t0 + kTile < N) ? t0 + kTile : N;
+        const int j0 = (int)(t0 / C);
+        const int j1 = (int)((t1 - 1) / C);
+        const int64_t g = t0 + (int64_t)threadIdx.x * kGroup;
+        if (a.vec && j0 == j1 && t1 - t0 == kTile) {
+            float acc[8];
+            if constexpr (RING && KS > 0 && KS <= 16)
+                fold_ring_group_static<T, KS, NT>(RingBases<T, KS>(a.in, j0), g, acc);
+            else if constexpr (RING)
+                fold_ring_group<T, KS, NT>(a.in, K, j0, g, acc);
+            else
+                fold_free_group<T, KS, NT>(a.in, K, g, acc);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = average<AVG>(acc[e], a.inv_k, a.kf);
+            const Group<T> res = pack<T>(acc);
+            if constexpr (KS > 0) {
+#pragma unroll
+                for (int r = 0; r < KS; ++r) store_group<T, NT>(static_cast<T*>(a.out.p[r]) + g, res);
+            } else {
+                for (int r = 0; r < K; ++r) store_group<T, NT>(static_cast<T*>(a.out.p[r]) + g, res);
+            }
+        } else if (g < N) {
+            const int n = (int)((N - g) < kGroup ? (N - g) : kGroup);
+            for (int e = 0; e < n; ++e) {
+                const int64_t ge = g + e;
+                float s = RING ? fold_ring_elem<T>(lds_ptr, K, (int)(ge / C), ge)
+                               : fold_free_elem<T>(lds_ptr, K, ge);
+                s = average<AVG>(s, a.inv_k, a.kf);
+                T v;
+                store_elem(&v, s);
+                for (int r = 0; r < K; ++r) static_cast<T*>(a.out.p[r])[ge] = v;
+            }
+        }
+    }
+}
+
+template <typename T, int KS, int AVG, bool RING, bool NT>
+hipError_t launch_t(const ArArgs& a, hipStream_t stream) {
+    int64_t want = (int64_t)device_cu_count() * tuning().ar_blocks_per_cu;
+    if (want < 1) want = 1;
+    const int gx = (int)(want < a.n_tiles ? want : a.n_tiles);
+    hipLaunchKernelGGL((ar_kernel<T, KS, AVG, RING, NT>), dim3(gx), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T, int KS, int AVG, bool RING>
+hipError_t pick_nt(const ArArgs& a, hipStream_t s) {
+    return tuning().nontemporal ? launch_t<T, KS, AVG, RING, true>(a, s)
+                                : launch_t<T, KS, AVG, RING, false>(a, s);
+}
+
+template <typename T, int AVG>
+hipError_t pick_k(const ArArgs& a, bool ring, hipStream_t s) {
+    if (!ring) return pick_nt<T, 0, AVG, false>(a, s);
+    switch (a.K) {
+        case 8: return pick_nt<T, 8, AVG, true>(a, s);
+        case 64: return pick_nt<T, 64, AVG, true>(a, s);
+        default: return pick_nt<T, 0, AVG, true>(a, s);
+    }
+}
+
+template <typename T>
+hipError_t pick_avg(const ArArgs& a, int avg_mode, bool ring, hipStream_t s) {
+    switch (avg_mode) {
+        case 1: return pick_k<T, 1>(a, ring, s);
+        case 2: return pick_k<T, 2>(a, ring, s);
+        default: return pick_k<T, 0>(a, ring, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_allreduce_fused(int K, const ConstPtrs& in, const MutPtrs& out, zr_dtype dt,
+                                  int64_t N, int average, zr_order order, hipStream_t stream) {
+    ArArgs a;
+    a.in = in;
+    a.out = out;
+    a.N = N;
+    a.K = K;
+    a.C = (N + K - 1) / K;
+    a.n_tiles = (N + kTile - 1) / kTile;
+    a.inv_k = 1.0f / (float)K;
+    a.kf = (float)K;
+    bool vec = true;
+    for (int r = 0; r < K; ++r)
+        vec = vec && (((uintptr_t)in.p[r]) & 15) == 0 && (((uintptr_t)out.p[r]) & 15) == 0;
+    a.vec = vec ? 1 : 0;
+    const bool pow2 = (K & (K - 1)) == 0;
+    const int avg_mode = !average ? 0 : (pow2 ? 1 : 2);
+    const bool ring = order == ZR_ORDER_RING;
+    if (dt == ZR_BF16) return pick_avg<uint16_t>(a, avg_mode, ring, stream);
+    return pick_avg<float>(a, avg_mode, ring, stream);
+}
+
+}  // namespace zr

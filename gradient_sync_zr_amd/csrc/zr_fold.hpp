@@ -1,0 +1,128 @@
+// Per-lane folds over K rank buffers, shared by the reduce-scatter and the
+// fused all-reduce kernels.
+//
+// Ring order (the path a chunk takes around the ring, "图解 Ring All-Reduce",
+// Phase 1): chunk j starts with rank j's value and adds ranks j+1, ..., j-1
+// (mod K), one fp32 add per hop, so the result is
+//     (((x_j + x_{j+1}) + x_{j+2}) + ... ) + x_{j-1}.
+// The fold keeps up to eight ranks' 16-byte loads in flight per lane, then
+// adds them strictly in that order: the loads may be issued in any order,
+// the adds may not.
+//
+// Free order: ranks 0..K-1 in batches of eight, each batch summed as a
+// balanced pairwise tree, batches added in sequence. Not bit-identical to the
+// ring order; within the fp32 summation error bound of the exact sum.
+#pragma once
+
+#include "zr_device.hpp"
+#include "zr_internal.hpp"
+
+namespace zr {
+
+__device__ __forceinline__ int wrap(int r, int K) { return r >= K ? r - K : r; }
+
+// Rank buffers in ring order for chunk j, held in scalar registers for the
+// whole kernel when K is a small compile-time constant.
+template <typename TIn, int KS>
+struct RingBases {
+    const TIn* p[KS];
+    __device__ __forceinline__ RingBases(const ConstPtrs& in, int j) {
+#pragma unroll
+        for (int h = 0; h < KS; ++h) p[h] = static_cast<const TIn*>(in.p[wrap(j + h, KS)]);
+    }
+};
+
+// Ring-order fold of the 8-element group at global index g (16-byte aligned
+// in every rank buffer), K = KS <= 16 known at compile time: all K loads are
+// issued before the first add (the scheduling barrier keeps the compiler
+// from waiting on the first load early), then the adds run in ring order.
+template <typename TIn, int KS, bool NT>
+__device__ __forceinline__ void fold_ring_group_static(const RingBases<TIn, KS>& b, int64_t g,
+                                                       float acc[8]) {
+    Group<TIn> v[KS];
+#pragma unroll
+    for (int h = 0; h < KS; ++h) v[h] = load_group<TIn, NT>(b.p[h] + g);
+    __builtin_amdgcn_sched_barrier(0);
+    widen(v[0], acc);
+#pragma unroll
+    for (int h = 1; h < KS; ++h) accumulate(acc, v[h]);
+}
+
+// Ring-order fold for any K: batches of eight ranks' loads in flight, folded
+// in ring order batch after batch. `in.p[...]` is indexed with block-uniform
+// values, so the pointers come from scalar loads.
+template <typename TIn, int KS, bool NT>
+__device__ __forceinline__ void fold_ring_group(const ConstPtrs& in, int K, int j, int64_t g,
+                                                float acc[8]) {
+    constexpr int B = 8;
+    const int Kr = KS > 0 ? KS : K;
+    for (int h0 = 0; h0 < Kr; h0 += B) {
+        Group<TIn> v[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+            if (h0 + b < Kr)
+                v[b] = load_group<TIn, NT>(static_cast<const TIn*>(in.p[wrap(j + h0 + b, Kr)]) + g);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (h0 + b < Kr) {
+                if (h0 + b == 0)
+                    widen(v[b], acc);
+                else
+                    accumulate(acc, v[b]);
+            }
+        }
+    }
+}
+
+// Free-order fold of a group (pairwise within batches of eight ranks).
+template <typename TIn, int KS, bool NT>
+__device__ __forceinline__ void fold_free_group(const ConstPtrs& in, int K, int64_t g,
+                                                float acc[8]) {
+    constexpr int B = 8;
+    const int Kr = KS > 0 ? KS : K;
+    for (int h0 = 0; h0 < Kr; h0 += B) {
+        float f[B][8];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (h0 + b < Kr) {
+                widen(load_group<TIn, NT>(static_cast<const TIn*>(in.p[h0 + b]) + g), f[b]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[b][e] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int s = 1; s < B; s *= 2)
+#pragma unroll
+            for (int b = 0; b + s < B; b += 2 * s)
+                if (h0 + b + s < Kr)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) f[b][e] = __fadd_rn(f[b][e], f[b + s][e]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = (h0 == 0) ? f[0][e] : __fadd_rn(acc[e], f[0][e]);
+    }
+}
+
+// Scalar ring-order fold of one element (index g < N) of chunk j, with the
+// rank pointers read through `ptr(r)` (kernel arguments or an LDS table).
+template <typename TIn, typename PtrFn>
+__device__ __forceinline__ float fold_ring_elem(PtrFn ptr, int K, int j, int64_t g) {
+    float acc = load_elem(static_cast<const TIn*>(ptr(j)) + g);
+    int r = j;
+    for (int h = 1; h < K; ++h) {
+        r = wrap(r + 1, K);
+        acc = __fadd_rn(acc, load_elem(static_cast<const TIn*>(ptr(r)) + g));
+    }
+    return acc;
+}
+
+// Scalar free-order fold (ranks in index order).
+template <typename TIn, typename PtrFn>
+__device__ __forceinline__ float fold_free_elem(PtrFn ptr, int K, int64_t g) {
+    float acc = load_elem(static_cast<const TIn*>(ptr(0)) + g);
+    for (int r = 1; r < K; ++r) acc = __fadd_rn(acc, load_elem(static_cast<const TIn*>(ptr(r)) + g));
+    return acc;
+}
+
+}  // namespace zr

@@ -1,0 +1,57 @@
+// Internal launch interface between the C-ABI layer (zr_abi.cpp,
+// zr_sched.cpp) and the HIP kernels. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zr.h"
+
+namespace zr {
+
+constexpr int kMaxRanks = ZR_MAX_RANKS;
+constexpr int kAgSegsPerLaunch = 32;   // segments carried in one all-gather launch
+constexpr int kFlatJobsPerLaunch = 96; // copy jobs carried in one flatten launch
+
+// Rank pointer tables travel by value in kernel arguments (K <= 64 -> 512 B).
+struct ConstPtrs {
+    const void* p[kMaxRanks];
+};
+struct MutPtrs {
+    void* p[kMaxRanks];
+};
+
+// One contiguous copy of a flatten call: `n` elements from src to dst;
+// src == nullptr means "write n zeros".
+struct CopyJob {
+    const void* src;
+    void* dst;
+    int64_t n;
+};
+
+// Launch-shape knobs, read once from the environment (for tuning sweeps);
+// defaults are the measured best.
+struct Tuning {
+    int rs_blocks_per_cu;  // resident blocks per CU the RS grid is sized for
+    int ar_blocks_per_cu;
+    int ag_blocks_per_cu;
+    int nontemporal;       // 1: streaming (non-temporal) loads/stores on the big kernels
+};
+const Tuning& tuning();
+int device_cu_count();  // CUs of the current device (cached per device)
+
+hipError_t launch_reduce_scatter(int K, const ConstPtrs& in, zr_dtype in_dt, int64_t N,
+                                 const MutPtrs& out, zr_dtype out_dt, int shift, int average,
+                                 zr_order order, hipStream_t stream);
+
+hipError_t launch_allreduce_fused(int K, const ConstPtrs& in, const MutPtrs& out, zr_dtype dt,
+                                  int64_t N, int average, zr_order order, hipStream_t stream);
+
+// segs: up to kAgSegsPerLaunch segments per call.
+hipError_t launch_all_gather(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype dt,
+                             const zr_seg* segs, int n_segs, int shift, hipStream_t stream);
+
+// jobs: up to kFlatJobsPerLaunch per call.
+hipError_t launch_flatten(const CopyJob* jobs, int n_jobs, int elem_bytes, hipStream_t stream);
+
+}  // namespace zr

@@ -1,0 +1,125 @@
+"""Host-side drivers of the reduction path: what a data-parallel trainer's
+reducer does with the C ABI, one step at a time.
+
+* :class:`Zero2GradSync` - a flat per-rank gradient reduced bucket by bucket
+  through the scheduler (ping-pong buffer indices, per-buffer completion
+  events), each bucket a fused reduce-scatter + average + cast into the
+  rank's fp32 partitioned flat gradient ("ZeRO-1/2 average_tensor serializes
+  backward compute behind the preceding reduction", Proposed design
+  direction; "DeepSpeed ZeRO-3 源码解析", 3.1 bucketing, 5.3 partition write,
+  5.4 epilogue flush).
+* :class:`Zero3Gather` - full parameters gathered from 1/K shards in greedy
+  prefetch buckets ("DeepSpeed ZeRO-3 源码解析", 2.1 fetch/prefetch and 2.2
+  the prefetch size cap), one all-gather launch set per bucket.
+
+All tensors are torch CUDA tensors used only as device memory; every
+computation happens in libzr's kernels.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+from . import (ZR_BF16, ZR_FP32, ZR_ORDER_RING, Sched, zr_all_gather, zr_plan_buckets,
+               _dtype)
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+class Zero2GradSync:
+    """Bucketed reduce-scatter of K flat gradients into K fp32 partitions.
+
+    grads[r]      : rank r's flat gradient, N_total elements (bf16 or fp32)
+    partitions[r] : rank r's partitioned flat gradient; bucket b's chunk is
+                    written at the sum of the previous buckets' chunk sizes
+    bucket        : elements per bucket (the last bucket takes the rest)
+    """
+
+    def __init__(self, grads: Sequence, partitions: Sequence, bucket: int, chunk_shift: int = 1,
+                 average: bool = True, order: int = ZR_ORDER_RING, n_buffers: int = 2,
+                 reduction_stream=None):
+        self.K = len(grads)
+        self.grads, self.partitions = list(grads), list(partitions)
+        self.N_total = grads[0].numel()
+        self.in_dt, self.out_dt = _dtype(grads[0]), _dtype(partitions[0])
+        self.in_es = 2 if self.in_dt == ZR_BF16 else 4
+        self.out_es = 2 if self.out_dt == ZR_BF16 else 4
+        self.shift, self.average, self.order = chunk_shift, average, order
+        self.n_buffers = n_buffers
+        self.buckets = []  # (N_b, input pointers, output pointers)
+        start, poff = 0, 0
+        while start < self.N_total:
+            n = min(bucket, self.N_total - start)
+            C = ceil_div(n, self.K)
+            ins = [g.data_ptr() + start * self.in_es for g in self.grads]
+            outs = [p.data_ptr() + poff * self.out_es for p in self.partitions]
+            self.buckets.append((n, ins, outs, start, poff))
+            start += n
+            poff += C
+        self.partition_numel = poff
+        for p in self.partitions:
+            if p.numel() < poff:
+                raise ValueError(f"partition holds {p.numel()} elements, needs {poff}")
+        self.reduction_stream = reduction_stream
+        self.sched = Sched(n_buffers=n_buffers, max_producers=1,
+                           reduction_stream=reduction_stream)
+
+    def step(self, producer_stream=None, timing: Optional[List] = None) -> None:
+        """One gradient sync. `timing`, if given, receives (start, end) torch
+        events recorded on the reduction stream around each bucket's launch."""
+        import torch
+        prod = producer_stream if producer_stream is not None else torch.cuda.current_stream()
+        for i, (n, ins, outs, _, _) in enumerate(self.buckets):
+            buf = i % self.n_buffers
+            self.sched.acquire(buf, prod)
+            # the backward pass would write this bucket's gradients here, on `prod`
+            if timing is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(self.reduction_stream)
+            self.sched.submit_rs(buf, [prod], ins, n, outs, chunk_shift=self.shift,
+                                 average=self.average, order=self.order, in_dtype=self.in_dt,
+                                 out_dtype=self.out_dt)
+            if timing is not None:
+                e1.record(self.reduction_stream)
+                timing.append((e0, e1))
+        self.sched.flush(prod)
+
+    def close(self):
+        self.sched.close()
+
+
+class Zero3Gather:
+    """Gather K full parameter buffers from K shard buffers, bucket by bucket.
+
+    numels      : parameter sizes in trace order
+    cap         : prefetch bucket size in elements
+    Shard p of every rank is ceil(numel_p / K) elements at the running offset
+    of the shard buffer; parameter p sits at the running offset of the full
+    buffer.
+    """
+
+    def __init__(self, shards: Sequence, fulls: Sequence, numels: Sequence[int], cap: int,
+                 chunk_shift: int = 0):
+        self.K = len(shards)
+        self.shards, self.fulls = list(shards), list(fulls)
+        self.dt = _dtype(shards[0])
+        self.shift = chunk_shift
+        bucket_of, nb = zr_plan_buckets(list(numels), cap)
+        self.buckets: List[List[tuple]] = [[] for _ in range(nb)]
+        soff, foff = 0, 0
+        self.param_offsets = []
+        for p, n in enumerate(numels):
+            self.buckets[bucket_of[p]].append((soff, foff, n))
+            self.param_offsets.append((soff, foff, n))
+            soff += ceil_div(n, self.K)
+            foff += n
+        self.shard_numel, self.full_numel = soff, foff
+        self._sp = [t.data_ptr() for t in self.shards]
+        self._fp = [t.data_ptr() for t in self.fulls]
+
+    def step(self, stream=None) -> None:
+        for segs in self.buckets:
+            zr_all_gather(self._sp, self._fp, segs, chunk_shift=self.shift, dtype=self.dt,
+                          stream=stream)

@@ -1,0 +1,223 @@
+/*
+ * zr.h - gradient-bucket reduction for data-parallel training, MI355X (gfx950).
+ *
+ * K data-parallel ranks are K buffers in one GPU's HBM. The library flattens
+ * fragmented gradients into a flat bucket, reduce-scatters the bucket across
+ * the K ranks in the ring's chunk order with fp32 accumulation, averages by
+ * K and writes each rank's partition in one pass, gathers full parameters
+ * back from 1/K shards, and composes the two into an all-reduce. A small
+ * scheduler keeps the reduction on its own stream with per-buffer
+ * completion events.
+ *
+ * Pages the operations follow (title, then section):
+ *  [RING]  "图解 Ring All-Reduce：分布式训练梯度同步的核心算法": Phase 1
+ *          (Scatter-Reduce) and Phase 2 (All-Gather).
+ *  [L14]   CMU 11-868 lecture 14 notes, "Distributed Training I:
+ *          Communication and Data Parallelism": 2.1 (every operation is bound
+ *          to a stream), 2.2 (primitives; all-reduce = reduce-scatter +
+ *          all-gather), 3.2 (ring rounds and placement), 4.1 (average =
+ *          SUM / world size).
+ *  [ZERO3] "DeepSpeed ZeRO-3 源码解析：前向与反向": 1 (data-flow overview:
+ *          bucket -> reduce -> partition copy -> single bf16->fp32 cast),
+ *          2.1/2.2 (parameter all-gather in prefetch buckets), 3.1/3.2
+ *          (bucketing, contiguous flat buffer), 5.1-5.4 (bucket insert,
+ *          reduce paths, partition write, epilogue).
+ *  [ISSUE] "ZeRO-1/2 average_tensor serializes backward compute behind the
+ *          preceding reduction" (DeepSpeed issue 8364): Proposed design
+ *          direction (per-buffer reduction-complete events) and Validation
+ *          requirements.
+ *
+ * Conventions for every call
+ *  - Pointer tables (`in`, `out`, `shards`, ...) are HOST arrays of K DEVICE
+ *    pointers; rank r's buffer is entry r. The library copies the tables
+ *    into kernel arguments at launch; it keeps no reference after returning.
+ *  - Sizes are element counts. bf16 data is raw 16-bit patterns.
+ *  - Chunking: C = ceil(N / K); chunk j covers global indices [jC, jC + C)
+ *    of every rank's buffer; indices >= N are zero padding.
+ *  - chunk_shift s: after reduce-scatter rank q holds chunk (q + s) mod K,
+ *    i.e. chunk j lands on rank (j - s) mod K. s = 1 is where the ring
+ *    leaves each fully reduced chunk [RING Phase 1; L14 3.2]; s = 0 is the
+ *    "rank r keeps slice r" convention of the contiguous path [ZERO3 5.2].
+ *  - Ring order: chunk j is summed as (((x_j + x_{j+1}) + x_{j+2}) + ...
+ *    + x_{j-1}) with ranks mod K, each input widened exactly to fp32, one
+ *    fp32 round-to-nearest-even add per hop [RING Phase 1 rule].
+ *  - Streams are hipStream_t passed as void*; NULL is the null stream. Work
+ *    is enqueued asynchronously [L14 2.1]; buffers must stay alive until
+ *    the stream has finished with them. No call allocates device memory.
+ *  - Errors: every call returns a zr_status; nothing throws or aborts across
+ *    the boundary. Arguments are validated before any HIP call, so a bad
+ *    argument enqueues nothing. zr_last_error() describes the last failure
+ *    on the calling thread. N == 0 (or no work) returns ZR_OK and enqueues
+ *    nothing.
+ */
+#ifndef ZR_H
+#define ZR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ZR_OK = 0,
+    ZR_ERR_INVALID = 1,     /* bad count, rank, shift, null pointer, state */
+    ZR_ERR_ALIGN = 2,       /* pointer not aligned to its element size */
+    ZR_ERR_ALIAS = 3,       /* overlapping buffers that must not overlap */
+    ZR_ERR_UNSUPPORTED = 4, /* dtype or dtype pair not supported */
+    ZR_ERR_HIP = 5          /* a HIP runtime call or launch failed */
+} zr_status;
+
+typedef enum { ZR_BF16 = 0, ZR_FP32 = 1 } zr_dtype;
+
+/* ZR_ORDER_RING: the ring order above, bit-exact and deterministic.
+ * ZR_ORDER_FREE: ranks summed in an order of the library's choosing (fp32
+ * accumulation); the result is within the usual fp32 summation error bound
+ * of the exact sum but need not match the ring order bit for bit. */
+typedef enum { ZR_ORDER_RING = 0, ZR_ORDER_FREE = 1 } zr_order;
+
+/* One tensor of an all-gather: its shard starts at element shard_off of
+ * every rank's shard buffer and holds C = ceil(numel / K) elements; the
+ * full tensor starts at element full_off of every rank's full buffer. */
+typedef struct {
+    int64_t shard_off;
+    int64_t full_off;
+    int64_t numel;
+} zr_seg;
+
+#define ZR_MAX_RANKS 64
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* zr_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int zr_version(void);
+
+/*
+ * Bucket flatten [ZERO3 3.2, 5.1]: on every rank r, fragment p is copied to
+ * bucket_r at element offset n_0 + ... + n_{p-1}, then positions
+ * n_0 + ... + n_{F-1} .. padded_numel - 1 are set to +0.
+ *
+ *  K            ranks, 1..ZR_MAX_RANKS
+ *  n_frag       fragments per rank F (>= 0); every rank has the same sizes
+ *  frags        host array [K * n_frag] of device pointers, rank-major:
+ *               frags[r * n_frag + p] is fragment p of rank r (may be NULL
+ *               only when numels[p] == 0)
+ *  numels       host array [n_frag] of fragment sizes (>= 0)
+ *  buckets      host array [K] of device pointers, padded_numel elements each
+ *  padded_numel >= sum(numels); callers pad to a multiple of K for the
+ *               reduce-scatter that follows
+ *  dt           ZR_BF16 or ZR_FP32 (a bitwise copy either way)
+ * Buckets must not overlap each other or any fragment (ZR_ERR_ALIAS).
+ * Copy jobs travel in kernel arguments, 96 per launch.
+ */
+zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const int64_t* numels,
+                            void* const* buckets, int64_t padded_numel, zr_dtype dt,
+                            void* stream);
+
+/*
+ * Fused reduce-scatter + average + cast [RING Phase 1; L14 3.2, 4.1;
+ * ZERO3 1, 5.2, 5.3]. For every holder rank q and o in [0, C), with
+ * j = (q + chunk_shift) mod K and g = j*C + o:
+ *     S        = ring-order fp32 fold of in_{j}[g], in_{j+1}[g], ..., in_{j-1}[g]
+ *                (0 when g >= N)
+ *     out_q[o] = S / K if average else S   (one IEEE fp32 divide; exact
+ *                multiply by 1/K when K is a power of two)
+ * written as fp32 (no intermediate bf16 rounding) or rounded once to bf16.
+ * Positions with g >= N receive +0.
+ *
+ *  in        host array [K] of device pointers, N elements each (in_dt)
+ *  out       host array [K] of device pointers, C elements each (out_dt)
+ *  in_dt     ZR_BF16 or ZR_FP32; out_dt ZR_FP32 or ZR_BF16
+ *  order     ZR_ORDER_RING (bit-exact ring order) or ZR_ORDER_FREE
+ * Outputs must be distinct and must not overlap any input (ZR_ERR_ALIAS).
+ * Reads K*N elements once and writes K*C elements.
+ */
+zr_status zr_reduce_scatter_avg(int K, const void* const* in, zr_dtype in_dt, int64_t N,
+                                void* const* out, zr_dtype out_dt, int chunk_shift,
+                                int average, zr_order order, void* stream);
+
+/*
+ * All-gather of sharded tensors into full tensors [RING Phase 2; L14 3.2;
+ * ZERO3 1, 2.1]. For each segment and every destination rank r:
+ *     full_r[full_off + j*C + o] = shard_{(j - chunk_shift) mod K}[shard_off + o]
+ * for every j*C + o < numel, C = ceil(numel / K). Shard padding beyond
+ * numel is never read into a full tensor.
+ *
+ *  shards    host array [K] of device pointers
+ *  fulls     host array [K] of device pointers
+ *  segs      host array [n_segs], n_segs >= 0 (32 segments per launch);
+ *            numel >= 0, offsets >= 0; segments must not write overlapping
+ *            full ranges; each shard buffer must hold shard_off + C elements
+ * The written extent of each full buffer (lowest full_off to highest
+ * full_off + numel) must not overlap another rank's, nor any shard extent
+ * (ZR_ERR_ALIAS). Reads each shard element once and writes it K times.
+ */
+zr_status zr_all_gather(int K, const void* const* shards, void* const* fulls, zr_dtype dt,
+                        const zr_seg* segs, int n_segs, int chunk_shift, void* stream);
+
+/*
+ * All-reduce = reduce-scatter followed by all-gather [L14 2.2; RING].
+ * Every rank receives, at every g < N, the ring-order fp32 fold of chunk
+ * j = g / C (divided by K if average), stored once in dt: the same bits on
+ * all K ranks.
+ *
+ *  in, out   host arrays [K] of device pointers, N elements of dt each;
+ *            out[r] == in[r] for every r is allowed (in place); any other
+ *            overlap is ZR_ERR_ALIAS
+ *  fused     1: one pass that reads K values and writes the result to all K
+ *            ranks; 0: zr_reduce_scatter_avg into `scratch`, then
+ *            zr_all_gather from it (same bits either way)
+ *  scratch   device buffer of K * C elements of dt when fused == 0, else
+ *            ignored; must not overlap in/out
+ */
+zr_status zr_allreduce(int K, const void* const* in, void* const* out, zr_dtype dt, int64_t N,
+                       int average, zr_order order, int fused, void* scratch, void* stream);
+
+/*
+ * Greedy bucket plan (host only, no GPU) [ZERO3 2.1 step 3, 2.2]: walk the
+ * sizes in order; a bucket keeps taking the next item while its running total
+ * is below `cap`, so the item that reaches or crosses the cap still joins it
+ * (one oversized item may make a bucket larger than the cap). bucket_of[i]
+ * receives the bucket index of item i (host array [n]); *n_buckets the number
+ * of buckets. numels >= 0, cap >= 1.
+ */
+zr_status zr_plan_buckets(int n, const int64_t* numels, int64_t cap, int32_t* bucket_of,
+                          int32_t* n_buckets);
+
+/* ------------------------------------------------------------- scheduler
+ * Bucket/stream scheduler with per-buffer completion events [ISSUE,
+ * Proposed design direction; ZERO3 3.3, 5.4].
+ *
+ * The reduction runs on `reduction_stream`. Buffer indices 0..n_buffers-1
+ * name the physical IPG buffers (2 = ping-pong). Life of a buffer index:
+ *   zr_sched_acquire(buf, producer): the producer stream waits on the event
+ *       recorded after the last reduction that read this buffer, and on
+ *       nothing else; the producer may then write the buffer;
+ *   zr_sched_submit_rs(buf, producers, ...): the reduction stream waits on
+ *       every listed producer stream (all streams that wrote the bucket),
+ *       runs zr_reduce_scatter_avg, and records the buffer's completion
+ *       event;
+ *   zr_sched_flush(caller): the caller stream waits for all reduction work
+ *       submitted so far (epilogue of the backward pass).
+ * acquire on a buffer already acquired, or submit on one not acquired, is
+ * ZR_ERR_INVALID. The scheduler owns only its HIP events (created in
+ * zr_sched_create, destroyed in zr_sched_destroy); it is not thread-safe.
+ */
+typedef struct zr_sched zr_sched;
+
+zr_status zr_sched_create(zr_sched** out, int n_buffers, int max_producers,
+                          void* reduction_stream);
+zr_status zr_sched_acquire(zr_sched* s, int buf, void* producer_stream);
+zr_status zr_sched_submit_rs(zr_sched* s, int buf, void* const* producer_streams, int n_prod,
+                             int K, const void* const* in, zr_dtype in_dt, int64_t N,
+                             void* const* out, zr_dtype out_dt, int chunk_shift, int average,
+                             zr_order order);
+zr_status zr_sched_flush(zr_sched* s, void* caller_stream);
+zr_status zr_sched_destroy(zr_sched* s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZR_H */

@@ -1,0 +1,285 @@
+"""GPU parity of every entry point against the CPU oracle, at sizes the oracle
+finishes in seconds: several 2048-element tiles plus ragged tails, misaligned
+bases (the element-wise paths), every dtype pair, chunk shifts, averaging,
+K from 1 to 64, and the degenerate cases (N = 0, N < K, K = 1).
+
+Ring order must match the oracle bit for bit; the free order must lie within
+1e-5 of the sum of magnitudes (/K when averaging) of the exact sum, plus one
+bf16 ulp for bf16 outputs. Every buffer is guarded by a sentinel band.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import Guarded, bf16_ulp, bits
+
+pytestmark = pytest.mark.gpu
+
+SEED = 0x5A5200A0
+
+
+def zr():
+    import gradient_sync_zr_amd as m
+    return m
+
+
+def torch_dt(is_bf16):
+    import torch
+    return torch.bfloat16 if is_bf16 else torch.float32
+
+
+def make_inputs(K, N, bf16, case):
+    """Normal values with 1% of large outliers: sums cancel, so the order of
+    fp32 additions shows in the last bits."""
+    xs = [synth.host_normal_bf16(SEED + case, r, 0, N, 1.0, 0.01, 1e4) for r in range(K)]
+    if bf16:
+        return xs
+    rng = np.random.default_rng(case)
+    return [oracle.bf16_to_f32(x) * (1 + rng.standard_normal(N).astype(np.float32) * 1e-3)
+            for x in xs]
+
+
+RS_CASES = [
+    # K, N, in_bf16, out_bf16, shift, average, offset
+    (1, 1000, True, False, 0, True, 0),
+    (2, 2, True, False, 1, True, 0),
+    (3, 2, True, False, 1, False, 0),           # N < K: last chunk(s) all padding
+    (4, 16, False, False, 1, False, 0),
+    (8, 8 * 2048 * 3, True, False, 1, True, 0),  # exact tiles
+    (8, 8 * 2048 * 3 + 8 * 13, True, False, 1, True, 0),  # C % 8 != 0 ... ragged
+    (8, 8 * 2048 * 2 + 61, True, False, 1, True, 0),      # ragged tail, padding
+    (8, 100003, True, True, 1, True, 0),
+    (8, 100003, False, False, 0, True, 0),
+    (8, 100003, False, True, 3, False, 0),
+    (8, 65536, True, False, 1, True, 1),         # misaligned bases: element-wise path
+    (8, 65536 + 5, False, False, 1, True, 3),
+    (5, 77777, True, False, 2, True, 0),         # non power of two: IEEE divide
+    (3, 50001, False, True, 1, True, 0),
+    (7, 7 * 4096, True, False, 6, True, 0),
+    (16, 16 * 2048 + 3, True, False, 1, True, 0),
+    (16, 160000, True, True, 15, False, 0),
+    (64, 64 * 2048 + 17, True, False, 1, True, 0),
+    (64, 300007, True, True, 1, False, 0),
+    (64, 200000, False, False, 0, True, 1),
+    (33, 33 * 3000 + 1, True, False, 1, True, 0),
+]
+
+
+@pytest.mark.parametrize("K,N,in_bf16,out_bf16,shift,average,offset", RS_CASES)
+def test_reduce_scatter_ring_bit_exact(K, N, in_bf16, out_bf16, shift, average, offset):
+    import torch
+    case = K * 1000003 + N
+    xs = make_inputs(K, N, in_bf16, case)
+    C = -(-N // K)
+    ins = [Guarded(N, torch_dt(in_bf16), offset, xs[r]) for r in range(K)]
+    outs = [Guarded(C, torch_dt(out_bf16), offset) for _ in range(K)]
+    zr().zr_reduce_scatter_avg([g.ptr() for g in ins], N, [g.ptr() for g in outs],
+                               chunk_shift=shift, average=average, in_dtype=torch_dt(in_bf16),
+                               out_dtype=torch_dt(out_bf16))
+    torch.cuda.synchronize()
+    want = oracle.reduce_scatter(xs, N, np.uint16 if out_bf16 else np.float32, shift=shift,
+                                 average=average)
+    for r in range(K):
+        got = outs[r].get()
+        assert np.array_equal(bits(got), bits(want[r])), f"rank {r}"
+        assert outs[r].guards_intact() and ins[r].guards_intact()
+
+
+@pytest.mark.parametrize("K,N,in_bf16,out_bf16,average", [
+    (8, 100003, True, False, True), (64, 70001, True, True, False), (5, 30000, False, False, True),
+    (16, 16 * 2048 * 2, True, False, True)])
+def test_reduce_scatter_free_order_within_tolerance(K, N, in_bf16, out_bf16, average):
+    import torch
+    xs = make_inputs(K, N, in_bf16, 77 + K)
+    C = -(-N // K)
+    ins = [Guarded(N, torch_dt(in_bf16), 0, xs[r]) for r in range(K)]
+    outs = [Guarded(C, torch_dt(out_bf16), 0) for _ in range(K)]
+    zr().zr_reduce_scatter_avg([g.ptr() for g in ins], N, [g.ptr() for g in outs], chunk_shift=1,
+                               average=average, order=zr().ZR_ORDER_FREE,
+                               in_dtype=torch_dt(in_bf16), out_dtype=torch_dt(out_bf16))
+    torch.cuda.synchronize()
+    xf = np.stack([oracle.bf16_to_f32(x) if in_bf16 else x for x in xs])
+    xp = np.zeros((K, K * C), dtype=np.float32)
+    xp[:, :N] = xf
+    exact, absum = oracle.exact_sum_points(xp)
+    scale = 1.0 / K if average else 1.0
+    ring = oracle.reduce_scatter(xs, N, np.float32, shift=1, average=average)
+    differs = False
+    for q in range(K):
+        j = (q + 1) % K
+        got = outs[q].get()
+        gotf = oracle.bf16_to_f32(got) if out_bf16 else got
+        ex = exact[j * C:(j + 1) * C] * scale
+        tol = 1e-5 * absum[j * C:(j + 1) * C] * scale
+        if out_bf16:
+            tol = tol + bf16_ulp(ex)
+        assert np.all(np.abs(gotf.astype(np.float64) - ex) <= tol), f"rank {q}"
+        differs |= not np.array_equal(bits(gotf.astype(np.float32)), bits(ring[q]))
+        assert outs[q].guards_intact()
+    if K >= 16 and not out_bf16:
+        assert differs  # the free order is a different order
+
+
+AR_CASES = [
+    # K, N, bf16, average, fused, inplace, offset
+    (4, 16, False, False, True, False, 0),
+    (4, 16, False, False, False, False, 0),
+    (8, 8 * 2048 * 4, True, False, True, True, 0),
+    (8, 8 * 2048 * 4 + 77, True, True, True, False, 0),
+    (8, 8 * 2048 * 4 + 77, True, True, False, True, 0),
+    (8, 123457, False, False, True, True, 0),
+    (8, 123457, True, False, True, True, 1),   # misaligned: element-wise fold
+    (3, 30001, True, True, True, False, 0),
+    (64, 64 * 2048 + 9, True, False, True, True, 0),
+    (64, 200003, True, False, False, True, 0),
+    (64, 1000, True, False, True, False, 0),   # C < tile: every tile straddles chunks
+    (1, 5000, True, True, True, True, 0),
+    (2, 1, False, False, True, True, 0),
+    (17, 17 * 2048 + 1, False, True, True, False, 0),
+]
+
+
+@pytest.mark.parametrize("K,N,bf16,average,fused,inplace,offset", AR_CASES)
+def test_allreduce_bit_exact(K, N, bf16, average, fused, inplace, offset):
+    import torch
+    xs = make_inputs(K, N, bf16, 5000 + K * 7 + N)
+    ins = [Guarded(N, torch_dt(bf16), offset, xs[r]) for r in range(K)]
+    outs = ins if inplace else [Guarded(N, torch_dt(bf16), offset) for _ in range(K)]
+    C = -(-N // K)
+    scratch = None if fused else Guarded(K * C, torch_dt(bf16), 0)
+    zr().zr_allreduce([g.ptr() for g in ins], [g.ptr() for g in outs], N, average=average,
+                      fused=fused, scratch=None if scratch is None else scratch.ptr(),
+                      dtype=torch_dt(bf16))
+    torch.cuda.synchronize()
+    want = oracle.allreduce(xs, N, average=average)
+    for r in range(K):
+        assert np.array_equal(bits(outs[r].get()), bits(want[r])), f"rank {r}"
+        assert outs[r].guards_intact()
+    if scratch is not None:
+        assert scratch.guards_intact()
+
+
+@pytest.mark.parametrize("K,N,bf16", [(8, 99991, True), (64, 64 * 2048 * 2 + 5, True),
+                                      (5, 44444, False)])
+def test_allreduce_fused_equals_rs_then_ag(K, N, bf16):
+    # all-reduce = reduce-scatter then all-gather (lecture 14, 2.2), on the GPU
+    import torch
+    xs = make_inputs(K, N, bf16, 9000 + K)
+    ins = [Guarded(N, torch_dt(bf16), 0, xs[r]) for r in range(K)]
+    a = [Guarded(N, torch_dt(bf16), 0) for _ in range(K)]
+    b = [Guarded(N, torch_dt(bf16), 0) for _ in range(K)]
+    C = -(-N // K)
+    sh = [Guarded(C, torch_dt(bf16), 0) for _ in range(K)]
+    m = zr()
+    m.zr_allreduce([g.ptr() for g in ins], [g.ptr() for g in a], N, fused=True,
+                   dtype=torch_dt(bf16))
+    m.zr_reduce_scatter_avg([g.ptr() for g in ins], N, [g.ptr() for g in sh], chunk_shift=1,
+                            average=False, in_dtype=torch_dt(bf16), out_dtype=torch_dt(bf16))
+    m.zr_all_gather([g.ptr() for g in sh], [g.ptr() for g in b], [(0, 0, N)], chunk_shift=1,
+                    dtype=torch_dt(bf16))
+    torch.cuda.synchronize()
+    ref = a[0].get()
+    for r in range(K):
+        assert np.array_equal(bits(a[r].get()), bits(b[r].get()))
+        assert np.array_equal(bits(a[r].get()), bits(ref))   # identical on every rank
+
+
+def test_allreduce_free_order_tolerance_and_identical_ranks():
+    import torch
+    K, N = 64, 64 * 2048 + 999
+    xs = make_inputs(K, N, True, 31337)
+    ins = [Guarded(N, torch.bfloat16, 0, xs[r]) for r in range(K)]
+    zr().zr_allreduce([g.ptr() for g in ins], [g.ptr() for g in ins], N,
+                      order=zr().ZR_ORDER_FREE, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    xf = np.stack([oracle.bf16_to_f32(x) for x in xs])
+    exact, absum = oracle.exact_sum_points(xf)
+    ref = ins[0].get()
+    got = oracle.bf16_to_f32(ref).astype(np.float64)
+    assert np.all(np.abs(got - exact) <= 1e-5 * absum + bf16_ulp(exact))
+    for r in range(1, K):
+        assert np.array_equal(ins[r].get(), ref)
+
+
+AG_CASES = [
+    # K, sizes, shift, bf16, offset, full gap
+    (8, [8 * 2048 * 2, 8 * 2048 * 3 + 8, 5000, 1, 7], 0, True, 0, 0),
+    (8, [100003, 64, 3], 1, True, 0, 3),
+    (8, [65536] * 40, 0, True, 0, 0),          # more than one launch of segments
+    (3, [10, 30001, 2], 2, False, 1, 1),
+    (64, [64 * 2048 + 5, 640, 63], 0, True, 0, 0),
+    (1, [12345], 0, True, 0, 0),
+    (5, [0, 4, 0, 99999], 3, True, 1, 2),
+]
+
+
+@pytest.mark.parametrize("K,sizes,shift,bf16,offset,gap", AG_CASES)
+def test_all_gather_bit_exact(K, sizes, shift, bf16, offset, gap):
+    import torch
+    rng = np.random.default_rng(sum(sizes) + K)
+    segs, soff, foff = [], 0, 0
+    for n in sizes:
+        segs.append((soff, foff, n))
+        soff += -(-n // K) + gap
+        foff += n + gap
+    dt = np.uint16 if bf16 else np.float32
+    shard_np = [(rng.integers(0, 65535, size=soff).astype(np.uint16) if bf16 else
+                 rng.standard_normal(soff).astype(np.float32)) for _ in range(K)]
+    shards = [Guarded(soff, torch_dt(bf16), offset, shard_np[r]) for r in range(K)]
+    fill = np.zeros(foff, dtype=dt)
+    fulls = [Guarded(foff, torch_dt(bf16), offset, fill) for _ in range(K)]
+    zr().zr_all_gather([g.ptr() for g in shards], [g.ptr() for g in fulls], segs,
+                       chunk_shift=shift, dtype=torch_dt(bf16))
+    torch.cuda.synchronize()
+    want = [np.zeros(foff, dtype=dt) for _ in range(K)]
+    oracle.all_gather(shard_np, want, segs, shift)
+    for r in range(K):
+        assert np.array_equal(bits(fulls[r].get()), bits(want[r])), f"rank {r}"
+        assert fulls[r].guards_intact() and shards[r].guards_intact()
+
+
+@pytest.mark.parametrize("K,sizes,bf16,offset,extra", [
+    (8, None, True, 0, None),                      # the 64 log-uniform fragments
+    (3, [5, 0, 1, 2049, 7, 4096, 33], True, 0, 11),
+    (4, [8, 16, 24, 4096 * 3], False, 0, 4),       # aligned: 16-byte copies
+    (2, [1000, 3, 5], True, 1, 0),
+    (64, [100, 1], True, 0, 27),
+])
+def test_flatten_bit_exact(K, sizes, bf16, offset, extra):
+    import torch
+    from synth import workloads as W
+    if sizes is None:
+        sizes = W.flatten8_numels()
+    total = sum(sizes)
+    padded = -(-total // K) * K if extra is None else total + extra
+    frags_np = []
+    for r in range(K):
+        row = []
+        for p, n in enumerate(sizes):
+            h = synth.host_normal_bf16(SEED, W.flatten8_frag_stream(r, p), 0, n, 1e-3)
+            row.append(h if bf16 else oracle.bf16_to_f32(h))
+        frags_np.append(row)
+    frags = [[Guarded(n, torch_dt(bf16), offset, frags_np[r][p]) for p, n in enumerate(sizes)]
+             for r in range(K)]
+    buckets = [Guarded(padded, torch_dt(bf16), offset,
+                       np.full(padded, 0x3F80 if bf16 else 1.0,
+                               dtype=np.uint16 if bf16 else np.float32)) for _ in range(K)]
+    zr().zr_flatten_bucket([[g.ptr() for g in row] for row in frags], sizes,
+                           [b.ptr() for b in buckets], padded, dtype=torch_dt(bf16))
+    torch.cuda.synchronize()
+    want = oracle.flatten(frags_np, sizes, padded)
+    for r in range(K):
+        assert np.array_equal(bits(buckets[r].get()), bits(want[r])), f"rank {r}"
+        assert buckets[r].guards_intact()
+
+
+def test_zero_sized_calls_enqueue_nothing():
+    import torch
+    m = zr()
+    t = torch.empty(16, dtype=torch.bfloat16, device="cuda")
+    m.zr_reduce_scatter_avg([t] * 4, 0, [t] * 4)
+    m.zr_allreduce([t] * 4, [t] * 4, 0)
+    m.zr_all_gather([t] * 4, [t] * 4, [])
+    m.zr_flatten_bucket([[] for _ in range(4)], [], [t] * 4, 0)
+    torch.cuda.synchronize()
