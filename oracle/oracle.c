@@ -254,10 +254,12 @@ int orc_allreduce(int K, int64_t N, int dt, const void* const* in, void* const* 
     void** shards = (void**)malloc(sizeof(void*) * (size_t)K);
     if (!shard_mem || !shards) { free(shard_mem); free(shards); return -1; }
     for (int q = 0; q < K; ++q) shards[q] = shard_mem + (size_t)q * es * (size_t)C;
-    int rc = orc_reduce_scatter(K, N, dt, in, dt, shards, 1, average);
+    /* ring placement: rank q holds chunk (q + 1) mod K, a shift of 1 mod K */
+    int shift = 1 % K;
+    int rc = orc_reduce_scatter(K, N, dt, in, dt, shards, shift, average);
     if (rc == 0) {
         int64_t seg[3] = {0, 0, N};
-        rc = orc_all_gather(K, dt, (const void* const*)shards, out, seg, 1, 1);
+        rc = orc_all_gather(K, dt, (const void* const*)shards, out, seg, 1, shift);
     }
     free(shard_mem);
     free(shards);

@@ -312,7 +312,8 @@ def test_all_gather_rebuilds_original(K, shift):
 
 
 @pytest.mark.parametrize("K,N,dt", [(4, 16, np.float32), (8, 100, np.uint16),
-                                    (3, 10, np.float32), (16, 33, np.uint16)])
+                                    (3, 10, np.float32), (16, 33, np.uint16),
+                                    (1, 7, np.uint16), (2, 1, np.float32)])
 def test_allreduce_equals_ring_sim_and_rs_then_ag(K, N, dt):
     # lecture 14, 2.2: all-reduce = reduce-scatter then all-gather; the literal
     # ring (both phases) must give the same numbers on every rank.
@@ -332,9 +333,9 @@ def test_allreduce_equals_ring_sim_and_rs_then_ag(K, N, dt):
     for r in range(K):
         assert np.array_equal(out[r].view(np.uint8), np.asarray(want).view(np.uint8))
     # composition through the public RS and AG of the oracle
-    sh = oracle.reduce_scatter(ins, N, dt, shift=1, average=False)
+    sh = oracle.reduce_scatter(ins, N, dt, shift=1 % K, average=False)
     fulls = [np.zeros(N, dtype=dt) for _ in range(K)]
-    oracle.all_gather(sh, fulls, [(0, 0, N)], shift=1)
+    oracle.all_gather(sh, fulls, [(0, 0, N)], shift=1 % K)
     for r in range(K):
         assert np.array_equal(fulls[r].view(np.uint8), out[r].view(np.uint8))
 
