@@ -348,8 +348,8 @@ def bench_flatten8(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="zero2",
                     choices=["zero2", "zero3_ag", "allreduce64", "flatten8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -78,8 +78,8 @@ hipError_t launch_t(const AgArgs& a, int n_segs, int max_units, hipStream_t stre
 
 template <typename T, int KS>
 hipError_t pick_nt(const AgArgs& a, int n_segs, int max_units, hipStream_t s) {
-    return tuning().nontemporal ? launch_t<T, KS, true>(a, n_segs, max_units, s)
-                                : launch_t<T, KS, false>(a, n_segs, max_units, s);
+    return tuning().ag_nontemporal ? launch_t<T, KS, true>(a, n_segs, max_units, s)
+                                   : launch_t<T, KS, false>(a, n_segs, max_units, s);
 }
 
 template <typename T>

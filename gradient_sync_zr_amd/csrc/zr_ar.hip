@@ -9,11 +9,13 @@
 // Output may be the input (in place): a lane writes index g only after it
 // has read index g from every rank, and no other lane touches g.
 //
-// Tiles are 2048 aligned global indices. A tile that lies inside one chunk
-// and below N takes the 16-byte path with the chunk (hence the fold's first
-// rank) uniform across the block; a tile that straddles a chunk boundary or
-// the end of the buffer (at most K of them) folds element by element, reading
-// the rank pointers from an LDS table.
+// Tiles are 4 waves x S slices x 256 global indices, lanes on 4-element quads
+// (as in the reduce-scatter kernel, so every store instruction writes one
+// contiguous span). A tile that lies inside one chunk and below N takes the
+// vector path with the chunk (hence the fold's first rank) uniform across the
+// block; a tile that straddles a chunk boundary or the end of the buffer (at
+// most K of them) folds element by element, reading the rank pointers from an
+// LDS table.
 #include "zr_fold.hpp"
 
 namespace zr {
@@ -24,12 +26,19 @@ struct ArArgs {
     MutPtrs out;
     int64_t N, C, n_tiles;
     int K;
-    int vec;  // every in/out base 16-byte aligned
+    int vec;  // every in/out base aligned for quad access
     float inv_k, kf;
 };
 
+template <typename T>
+constexpr int kArSlices = sizeof(T) == 2 ? 4 : 2;
+template <typename T>
+constexpr int64_t kArTile = (int64_t)(kThreads / 64) * kArSlices<T> * 256;
+
 template <typename T, int KS, int AVG, bool RING, bool NT>
 __global__ void __launch_bounds__(kThreads) ar_kernel(const ArArgs a) {
+    constexpr int S = kArSlices<T>;
+    constexpr int64_t TT = kArTile<T>;
     const int K = KS > 0 ? KS : a.K;
     __shared__ const void* s_in[kMaxRanks];
     if (threadIdx.x == 0)
@@ -37,40 +46,48 @@ __global__ void __launch_bounds__(kThreads) ar_kernel(const ArArgs a) {
     __syncthreads();
     auto lds_ptr = [&](int r) { return s_in[r]; };
     const int64_t N = a.N, C = a.C;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
 
     for (int64_t t = blockIdx.x; t < a.n_tiles; t += gridDim.x) {
-        const int64_t t0 = t * kTile;
-        const int64_t t1 = (t0 + kTile < N) ? t0 + kTile : N;
+        const int64_t t0 = t * TT;
+        const int64_t t1 = (t0 + TT < N) ? t0 + TT : N;
         const int j0 = (int)(t0 / C);
         const int j1 = (int)((t1 - 1) / C);
-        const int64_t g = t0 + (int64_t)threadIdx.x * kGroup;
-        if (a.vec && j0 == j1 && t1 - t0 == kTile) {
-            float acc[8];
-            if constexpr (RING && KS > 0 && KS <= 16)
-                fold_ring_group_static<T, KS, NT>(RingBases<T, KS>(a.in, j0), g, acc);
+        const int64_t g0 = t0 + (int64_t)wave * (S * 256) + lane * 4;
+        if (a.vec && j0 == j1 && t1 - t0 == TT) {
+            float acc[S][4];
+            if constexpr (RING && KS > 0 && KS <= 8)
+                fold_ring_quads_static<T, KS, NT, S>(RingBases<T, KS>(a.in, j0), g0, acc);
             else if constexpr (RING)
-                fold_ring_group<T, KS, NT>(a.in, K, j0, g, acc);
+                fold_ring_quads<T, KS, NT, S>(a.in, K, j0, g0, acc);
             else
-                fold_free_group<T, KS, NT>(a.in, K, g, acc);
+                fold_free_quads<T, KS, NT, S>(a.in, K, g0, acc);
+            Quad<T> res[S];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = average<AVG>(acc[e], a.inv_k, a.kf);
-            const Group<T> res = pack<T>(acc);
-            if constexpr (KS > 0) {
+            for (int k = 0; k < S; ++k) {
 #pragma unroll
-                for (int r = 0; r < KS; ++r) store_group<T, NT>(static_cast<T*>(a.out.p[r]) + g, res);
-            } else {
-                for (int r = 0; r < K; ++r) store_group<T, NT>(static_cast<T*>(a.out.p[r]) + g, res);
+                for (int e = 0; e < 4; ++e) acc[k][e] = average<AVG>(acc[k][e], a.inv_k, a.kf);
+                res[k] = pack4<T>(acc[k]);
             }
-        } else if (g < N) {
-            const int n = (int)((N - g) < kGroup ? (N - g) : kGroup);
-            for (int e = 0; e < n; ++e) {
-                const int64_t ge = g + e;
-                float s = RING ? fold_ring_elem<T>(lds_ptr, K, (int)(ge / C), ge)
-                               : fold_free_elem<T>(lds_ptr, K, ge);
-                s = average<AVG>(s, a.inv_k, a.kf);
-                T v;
-                store_elem(&v, s);
-                for (int r = 0; r < K; ++r) static_cast<T*>(a.out.p[r])[ge] = v;
+            // the all-gather: the same bits to every rank
+            for (int r = 0; r < K; ++r) {
+                T* o = static_cast<T*>(a.out.p[r]) + g0;
+#pragma unroll
+                for (int k = 0; k < S; ++k) store_quad<T, NT>(o + 256 * k, res[k]);
+            }
+        } else {
+            for (int k = 0; k < S; ++k) {
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t ge = g0 + 256 * k + e;
+                    if (ge >= N) continue;
+                    float s = RING ? fold_ring_elem<T>(lds_ptr, K, (int)(ge / C), ge)
+                                   : fold_free_elem<T>(lds_ptr, K, ge);
+                    s = average<AVG>(s, a.inv_k, a.kf);
+                    T v;
+                    store_elem(&v, s);
+                    for (int r = 0; r < K; ++r) static_cast<T*>(a.out.p[r])[ge] = v;
+                }
             }
         }
     }
@@ -87,8 +104,8 @@ hipError_t launch_t(const ArArgs& a, hipStream_t stream) {
 
 template <typename T, int KS, int AVG, bool RING>
 hipError_t pick_nt(const ArArgs& a, hipStream_t s) {
-    return tuning().nontemporal ? launch_t<T, KS, AVG, RING, true>(a, s)
-                                : launch_t<T, KS, AVG, RING, false>(a, s);
+    return tuning().ar_nontemporal ? launch_t<T, KS, AVG, RING, true>(a, s)
+                                   : launch_t<T, KS, AVG, RING, false>(a, s);
 }
 
 template <typename T, int AVG>
@@ -120,12 +137,14 @@ hipError_t launch_allreduce_fused(int K, const ConstPtrs& in, const MutPtrs& out
     a.N = N;
     a.K = K;
     a.C = (N + K - 1) / K;
-    a.n_tiles = (N + kTile - 1) / kTile;
     a.inv_k = 1.0f / (float)K;
     a.kf = (float)K;
+    const int64_t tile = dt == ZR_BF16 ? kArTile<uint16_t> : kArTile<float>;
+    a.n_tiles = (N + tile - 1) / tile;
+    const uintptr_t al = dt == ZR_BF16 ? 8 : 16;  // quad size
     bool vec = true;
     for (int r = 0; r < K; ++r)
-        vec = vec && (((uintptr_t)in.p[r]) & 15) == 0 && (((uintptr_t)out.p[r]) & 15) == 0;
+        vec = vec && ((uintptr_t)in.p[r] % al) == 0 && ((uintptr_t)out.p[r] % al) == 0;
     a.vec = vec ? 1 : 0;
     const bool pow2 = (K & (K - 1)) == 0;
     const int avg_mode = !average ? 0 : (pow2 ? 1 : 2);

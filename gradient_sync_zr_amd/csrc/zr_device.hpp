@@ -162,3 +162,73 @@ __device__ __forceinline__ float average(float s, float inv_k, float kf) {
 }
 
 }  // namespace zr
+
+// ---------------------------------------------------------------- quads
+// A quad is 4 consecutive elements: 8 bytes of bf16 or 16 bytes of fp32.
+// Kernels that lay lanes out on quads make every load and store instruction
+// of a wave cover one contiguous span (64 lanes x 4 elements), so stores
+// write whole cache lines per instruction.
+namespace zr {
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct Quad;
+template <>
+struct Quad<uint16_t> {
+    u32x2 v;
+};
+template <>
+struct Quad<float> {
+    f32x4 v;
+};
+
+template <typename T, bool NT>
+__device__ __forceinline__ Quad<T> load_quad(const T* p) {
+    if constexpr (sizeof(T) == 2)
+        return {ld<NT>(reinterpret_cast<const u32x2*>(p))};
+    else
+        return {ld<NT>(reinterpret_cast<const f32x4*>(p))};
+}
+
+__device__ __forceinline__ void widen4(const Quad<uint16_t>& q, float f[4]) {
+    f[0] = __uint_as_float(q.v.x << 16);
+    f[1] = __uint_as_float(q.v.x & 0xFFFF0000u);
+    f[2] = __uint_as_float(q.v.y << 16);
+    f[3] = __uint_as_float(q.v.y & 0xFFFF0000u);
+}
+__device__ __forceinline__ void widen4(const Quad<float>& q, float f[4]) {
+    f[0] = q.v.x; f[1] = q.v.y; f[2] = q.v.z; f[3] = q.v.w;
+}
+
+template <typename T>
+__device__ __forceinline__ void accumulate4(float acc[4], const Quad<T>& q) {
+    float f[4];
+    widen4(q, f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = __fadd_rn(acc[e], f[e]);
+}
+
+template <typename T>
+__device__ __forceinline__ Quad<T> pack4(const float f[4]);
+template <>
+__device__ __forceinline__ Quad<uint16_t> pack4<uint16_t>(const float f[4]) {
+    Quad<uint16_t> q;
+    q.v.x = bf16_round(f[0]) | (bf16_round(f[1]) << 16);
+    q.v.y = bf16_round(f[2]) | (bf16_round(f[3]) << 16);
+    return q;
+}
+template <>
+__device__ __forceinline__ Quad<float> pack4<float>(const float f[4]) {
+    return {f32x4{f[0], f[1], f[2], f[3]}};
+}
+
+template <typename T, bool NT>
+__device__ __forceinline__ void store_quad(T* p, const Quad<T>& q) {
+    if constexpr (sizeof(T) == 2)
+        st<NT>(reinterpret_cast<u32x2*>(p), q.v);
+    else
+        st<NT>(reinterpret_cast<f32x4*>(p), q.v);
+}
+
+}  // namespace zr

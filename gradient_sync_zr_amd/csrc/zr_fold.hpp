@@ -104,6 +104,96 @@ __device__ __forceinline__ void fold_free_group(const ConstPtrs& in, int K, int6
     }
 }
 
+// ------------------------------------------------------------------ quads
+// A wave owns S slices of 256 consecutive elements; lane l holds quad l of
+// each slice (elements 4l..4l+3), so every load and store instruction of the
+// wave covers one contiguous span. g0 is the lane's first element; slice k
+// is at g0 + 256*k.
+
+// Ring order with K = KS <= 8 known at compile time: all S*KS loads are issued
+// before the first add, then each slice is folded in ring order.
+template <typename TIn, int KS, bool NT, int S>
+__device__ __forceinline__ void fold_ring_quads_static(const RingBases<TIn, KS>& b, int64_t g0,
+                                                       float acc[S][4]) {
+    Quad<TIn> v[S][KS];
+#pragma unroll
+    for (int k = 0; k < S; ++k)
+#pragma unroll
+        for (int h = 0; h < KS; ++h) v[k][h] = load_quad<TIn, NT>(b.p[h] + g0 + 256 * k);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+        widen4(v[k][0], acc[k]);
+#pragma unroll
+        for (int h = 1; h < KS; ++h) accumulate4(acc[k], v[k][h]);
+    }
+}
+
+// Ring order for any K: batches of eight ranks, every slice's loads of a batch
+// in flight together, batches folded in ring order one after the other.
+template <typename TIn, int KS, bool NT, int S>
+__device__ __forceinline__ void fold_ring_quads(const ConstPtrs& in, int K, int j, int64_t g0,
+                                                float acc[S][4]) {
+    constexpr int B = 8;
+    const int Kr = KS > 0 ? KS : K;
+    for (int h0 = 0; h0 < Kr; h0 += B) {
+        Quad<TIn> v[S][B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (h0 + b < Kr) {
+                const TIn* p = static_cast<const TIn*>(in.p[wrap(j + h0 + b, Kr)]);
+#pragma unroll
+                for (int k = 0; k < S; ++k) v[k][b] = load_quad<TIn, NT>(p + g0 + 256 * k);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (h0 + b < Kr) {
+#pragma unroll
+                for (int k = 0; k < S; ++k) {
+                    if (h0 + b == 0)
+                        widen4(v[k][b], acc[k]);
+                    else
+                        accumulate4(acc[k], v[k][b]);
+                }
+            }
+        }
+    }
+}
+
+// Free order: ranks 0..K-1 in batches of eight, pairwise within a batch.
+template <typename TIn, int KS, bool NT, int S>
+__device__ __forceinline__ void fold_free_quads(const ConstPtrs& in, int K, int64_t g0,
+                                                float acc[S][4]) {
+    constexpr int B = 8;
+    const int Kr = KS > 0 ? KS : K;
+    for (int h0 = 0; h0 < Kr; h0 += B) {
+#pragma unroll
+        for (int k = 0; k < S; ++k) {
+            float f[B][4];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                if (h0 + b < Kr) {
+                    widen4(load_quad<TIn, NT>(static_cast<const TIn*>(in.p[h0 + b]) + g0 + 256 * k), f[b]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) f[b][e] = 0.0f;
+                }
+            }
+#pragma unroll
+            for (int s = 1; s < B; s *= 2)
+#pragma unroll
+                for (int b = 0; b + s < B; b += 2 * s)
+                    if (h0 + b + s < Kr)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) f[b][e] = __fadd_rn(f[b][e], f[b + s][e]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[k][e] = (h0 == 0) ? f[0][e] : __fadd_rn(acc[k][e], f[0][e]);
+        }
+    }
+}
+
 // Scalar ring-order fold of one element (index g < N) of chunk j, with the
 // rank pointers read through `ptr(r)` (kernel arguments or an LDS table).
 template <typename TIn, typename PtrFn>

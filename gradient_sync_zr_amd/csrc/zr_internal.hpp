@@ -35,7 +35,9 @@ struct Tuning {
     int rs_blocks_per_cu;  // resident blocks per CU the RS grid is sized for
     int ar_blocks_per_cu;
     int ag_blocks_per_cu;
-    int nontemporal;       // 1: streaming (non-temporal) loads/stores on the big kernels
+    int nontemporal;       // reduce-scatter: streaming (non-temporal) loads and stores
+    int ar_nontemporal;    // fused all-reduce
+    int ag_nontemporal;    // all-gather
 };
 const Tuning& tuning();
 int device_cu_count();  // CUs of the current device (cached per device)

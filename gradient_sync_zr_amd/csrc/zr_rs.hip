@@ -11,11 +11,17 @@
 // ZeRO-3 data flow, section 1, moved into the reduction's only write).
 //
 // Grid: blockIdx.y = chunk j (so j, the holder and every rank pointer are
-// uniform per block), blockIdx.x strides over 2048-element tiles of the
-// chunk. Each lane owns 8 consecutive outputs: one 16-byte load per rank for
-// bf16 input, two 16-byte stores for fp32 output. A chunk whose input start
-// j*C is not 16-byte aligned, and the ragged tail of the last chunk, take the
-// element-wise path; positions g >= N are padding and receive +0.
+// uniform per block), blockIdx.x strides over tiles of the chunk. A tile is
+// 4 waves x S slices x 256 elements; lane l of a wave owns elements 4l..4l+3
+// of each of its slices, so each load instruction reads, and each store
+// instruction writes, one contiguous span of whole cache lines. All K ranks'
+// loads of all S slices are issued before the first add. Loads and stores
+// are non-temporal by default: every byte is touched exactly once.
+//
+// Tiles that are whole, inside the chunk and below N, in a chunk whose start
+// j*C is aligned for quad access, take that vector path. The last tile of a
+// chunk and chunks with an unaligned start fold element by element. Positions
+// g >= N are padding and receive +0.
 #include "zr_fold.hpp"
 
 namespace zr {
@@ -25,18 +31,24 @@ struct RsArgs {
     ConstPtrs in;
     MutPtrs out;
     int64_t N, C;
-    uint64_t vec_mask;  // bit j: chunk j takes the 16-byte path
+    uint64_t vec_mask;  // bit j: chunk j takes the vector path
     int K, shift;
     int tiles_per_chunk;
     float inv_k, kf;
 };
 
-// K small and known at compile time: the static ring fold with hoisted bases.
-template <int KS>
-constexpr bool kStaticFold = KS > 0 && KS <= 16;
+// Slices per wave: 4 for bf16 input (32 loads of 8 bytes in flight per lane
+// at K = 8), 2 for fp32 input (same bytes in flight).
+template <typename TIn>
+constexpr int kSlices = sizeof(TIn) == 2 ? 4 : 2;
+template <typename TIn>
+constexpr int64_t kRsTile = (int64_t)(kThreads / 64) * kSlices<TIn> * 256;
 
 template <typename TIn, typename TOut, int KS, int AVG, bool RING, bool NT>
 __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
+    constexpr int S = kSlices<TIn>;
+    constexpr int64_t T = kRsTile<TIn>;
+    constexpr bool kStatic = RING && KS > 0 && KS <= 8;
     const int K = KS > 0 ? KS : a.K;
     const int j = blockIdx.y;
     const int holder = wrap(j - a.shift + K, K);
@@ -45,34 +57,41 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
     const int64_t chunk_base = (int64_t)j * C;
     TOut* outp = static_cast<TOut*>(a.out.p[holder]);
     auto ptr = [&](int r) { return a.in.p[r]; };
-    constexpr int KB = kStaticFold<KS> ? KS : 1;
-    const RingBases<TIn, KB> bases(a.in, kStaticFold<KS> ? j : 0);
+    const RingBases<TIn, kStatic ? KS : 1> bases(a.in, kStatic ? j : 0);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
 
     for (int t = blockIdx.x; t < a.tiles_per_chunk; t += gridDim.x) {
-        const int64_t o = (int64_t)t * kTile + (int64_t)threadIdx.x * kGroup;
-        if (o >= C) continue;
-        const int64_t g = chunk_base + o;
-        if (vec && o + kGroup <= C && g + kGroup <= N) {
-            float acc[8];
-            if constexpr (RING && kStaticFold<KS>)
-                fold_ring_group_static<TIn, KS, NT>(bases, g, acc);
+        const int64_t o0 = (int64_t)t * T + (int64_t)wave * (S * 256) + lane * 4;  // chunk-local
+        const int64_t tile_end = (int64_t)(t + 1) * T;
+        if (vec && tile_end <= C && chunk_base + tile_end <= N) {
+            float acc[S][4];
+            const int64_t g0 = chunk_base + o0;
+            if constexpr (kStatic)
+                fold_ring_quads_static<TIn, KS, NT, S>(bases, g0, acc);
             else if constexpr (RING)
-                fold_ring_group<TIn, KS, NT>(a.in, K, j, g, acc);
+                fold_ring_quads<TIn, KS, NT, S>(a.in, K, j, g0, acc);
             else
-                fold_free_group<TIn, KS, NT>(a.in, K, g, acc);
+                fold_free_quads<TIn, KS, NT, S>(a.in, K, g0, acc);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = average<AVG>(acc[e], a.inv_k, a.kf);
-            store_group<TOut, NT>(outp + o, pack<TOut>(acc));
+            for (int k = 0; k < S; ++k) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[k][e] = average<AVG>(acc[k][e], a.inv_k, a.kf);
+                store_quad<TOut, NT>(outp + o0 + 256 * k, pack4<TOut>(acc[k]));
+            }
         } else {
-            const int n_out = (int)((C - o) < kGroup ? (C - o) : kGroup);
-            for (int e = 0; e < n_out; ++e) {
-                const int64_t ge = g + e;
-                float s = 0.0f;
-                if (ge < N) {
-                    s = RING ? fold_ring_elem<TIn>(ptr, K, j, ge) : fold_free_elem<TIn>(ptr, K, ge);
-                    s = average<AVG>(s, a.inv_k, a.kf);
+            for (int k = 0; k < S; ++k) {
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t o = o0 + 256 * k + e;
+                    if (o >= C) continue;
+                    const int64_t g = chunk_base + o;
+                    float s = 0.0f;
+                    if (g < N) {
+                        s = RING ? fold_ring_elem<TIn>(ptr, K, j, g) : fold_free_elem<TIn>(ptr, K, g);
+                        s = average<AVG>(s, a.inv_k, a.kf);
+                    }
+                    store_elem(outp + o, s);
                 }
-                store_elem(outp + o + e, s);
             }
         }
     }
@@ -114,6 +133,24 @@ hipError_t pick_avg(const RsArgs& a, int avg_mode, bool ring, hipStream_t s) {
     }
 }
 
+template <typename TIn, typename TOut>
+hipError_t launch_typed(RsArgs& a, int avg_mode, bool ring, hipStream_t s) {
+    constexpr int64_t T = kRsTile<TIn>;
+    a.tiles_per_chunk = (int)((a.C + T - 1) / T);
+    // Vector path: every rank's input at j*C and every output base must be
+    // aligned for quad access (8 bytes for bf16 quads, 16 for fp32 quads).
+    const uintptr_t in_al = sizeof(TIn) * 4, out_al = sizeof(TOut) * 4;
+    bool bases = true;
+    for (int r = 0; r < a.K; ++r) {
+        bases = bases && ((uintptr_t)a.in.p[r] % in_al) == 0;
+        bases = bases && ((uintptr_t)a.out.p[r] % out_al) == 0;
+    }
+    a.vec_mask = 0;
+    for (int j = 0; j < a.K; ++j)
+        if (bases && ((uintptr_t)(a.C * j * (int64_t)sizeof(TIn)) % in_al) == 0) a.vec_mask |= 1ull << j;
+    return pick_avg<TIn, TOut>(a, avg_mode, ring, s);
+}
+
 }  // namespace
 
 hipError_t launch_reduce_scatter(int K, const ConstPtrs& in, zr_dtype in_dt, int64_t N,
@@ -126,25 +163,15 @@ hipError_t launch_reduce_scatter(int K, const ConstPtrs& in, zr_dtype in_dt, int
     a.K = K;
     a.C = (N + K - 1) / K;
     a.shift = shift;
-    a.tiles_per_chunk = (int)((a.C + kTile - 1) / kTile);
     a.inv_k = 1.0f / (float)K;
     a.kf = (float)K;
-    const int in_es = in_dt == ZR_BF16 ? 2 : 4;
-    bool bases = true;
-    for (int r = 0; r < K; ++r) {
-        bases = bases && (((uintptr_t)in.p[r]) & 15) == 0;
-        bases = bases && (((uintptr_t)out.p[r]) & 15) == 0;
-    }
-    a.vec_mask = 0;
-    for (int j = 0; j < K; ++j)
-        if (bases && ((a.C * j * in_es) & 15) == 0) a.vec_mask |= 1ull << j;
     const bool pow2 = (K & (K - 1)) == 0;
     const int avg_mode = !average ? 0 : (pow2 ? 1 : 2);
     const bool ring = order == ZR_ORDER_RING;
-    if (in_dt == ZR_BF16 && out_dt == ZR_FP32) return pick_avg<uint16_t, float>(a, avg_mode, ring, stream);
-    if (in_dt == ZR_BF16 && out_dt == ZR_BF16) return pick_avg<uint16_t, uint16_t>(a, avg_mode, ring, stream);
-    if (in_dt == ZR_FP32 && out_dt == ZR_FP32) return pick_avg<float, float>(a, avg_mode, ring, stream);
-    return pick_avg<float, uint16_t>(a, avg_mode, ring, stream);
+    if (in_dt == ZR_BF16 && out_dt == ZR_FP32) return launch_typed<uint16_t, float>(a, avg_mode, ring, stream);
+    if (in_dt == ZR_BF16 && out_dt == ZR_BF16) return launch_typed<uint16_t, uint16_t>(a, avg_mode, ring, stream);
+    if (in_dt == ZR_FP32 && out_dt == ZR_FP32) return launch_typed<float, float>(a, avg_mode, ring, stream);
+    return launch_typed<float, uint16_t>(a, avg_mode, ring, stream);
 }
 
 }  // namespace zr

@@ -32,3 +32,51 @@ extern "C" int tk_clock_khz(int* khz) {
     if (hipGetDevice(&dev) != hipSuccess) return 2;
     return hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess ? 0 : 2;
 }
+
+// tk_copy: a plain streaming copy of `bytes` bytes (a multiple of 16), each
+// lane moving 16 bytes per iteration of a grid-stride loop. Used to calibrate
+// the hardware byte counters (a copy reads and writes exactly `bytes`) and as
+// the practical HBM ceiling a bandwidth-bound kernel can be compared with.
+__global__ void __launch_bounds__(256) tk_copy_kernel(const uint4* __restrict__ src,
+                                                      uint4* __restrict__ dst, long long n16) {
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        dst[i] = src[i];
+}
+
+extern "C" int tk_copy(const void* src, void* dst, long long bytes, int blocks, void* stream) {
+    if (bytes < 0 || (bytes & 15) || blocks < 1 || !src || !dst) return 1;
+    if (bytes == 0) return 0;
+    hipLaunchKernelGGL(tk_copy_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const uint4*)src, (uint4*)dst, bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// tk_read: reads `bytes` bytes (a multiple of 16) and writes one 16-byte
+// value per block (so the loads cannot be removed): a read-only stream.
+__global__ void __launch_bounds__(256) tk_read_kernel(const uint4* __restrict__ src,
+                                                      uint4* __restrict__ sink, long long n16) {
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    uint4 acc = make_uint4(0, 0, 0, 0);
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+        uint4 v = src[i];
+        acc.x ^= v.x; acc.y ^= v.y; acc.z ^= v.z; acc.w ^= v.w;
+    }
+    __shared__ uint4 red[256];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int t = 1; t < 256; ++t) {
+            acc.x ^= red[t].x; acc.y ^= red[t].y; acc.z ^= red[t].z; acc.w ^= red[t].w;
+        }
+        sink[blockIdx.x] = acc;
+    }
+}
+
+extern "C" int tk_read(const void* src, void* sink, long long bytes, int blocks, void* stream) {
+    if (bytes < 0 || (bytes & 15) || blocks < 1 || !src || !sink) return 1;
+    if (bytes == 0) return 0;
+    hipLaunchKernelGGL(tk_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const uint4*)src, (uint4*)sink, bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
