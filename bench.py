@@ -39,9 +39,10 @@ def kernel_source_hash(files):
     return h.hexdigest()[:16]
 
 
-def read_traffic(name, src_hash, bytes_per_launch):
-    """HBM traffic per launch from a committed rocprofv3 counter summary, or
-    None when it is missing or was taken on a different kernel source."""
+def read_traffic(name, src_hash, algorithmic, key="hbm_bytes_per_launch"):
+    """HBM bytes per launch (or per step) from a committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known size),
+    or None when it is missing or was taken on a different kernel source."""
     path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
@@ -53,7 +54,7 @@ def read_traffic(name, src_hash, bytes_per_launch):
     if kv.get("kernel_source_sha256_16") != src_hash:
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return int(float(kv[key]))
     except (KeyError, ValueError):
         return None
 
@@ -227,6 +228,9 @@ def bench_zero3(args):
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     step_bytes = full_numel * 2 + K * full_numel * 2   # shards read once + K full copies
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    kernel_ms = e0.elapsed_time(e1) / args.steps
+    src = kernel_source_hash(["zr_ag.hip", "zr_device.hpp"])
+    traffic = read_traffic("ag_bf16_k8_zero3.counters.txt", src, step_bytes, key="hbm_bytes_per_step")
     return {
         "metric": "all-gather GB/s (shard read + K full writes), K=8, 6.74B-param transformer",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -238,9 +242,12 @@ def bench_zero3(args):
                                "vocab 32000), 1/8 shards, 162 greedy 50 MB prefetch buckets",
                    "K": K, "params": len(numels), "n_buckets": len(gather.buckets),
                    "bytes_per_step": step_bytes},
-        "roofline": {"bound": "hbm", "kernel": "ag_kernel<bf16,K=8>", "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "achieved": round(value, 1),
-                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": "ag_kernel<bf16,K=8> (162 launches per step)",
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "achieved": round(step_bytes / (kernel_ms * 1e-3) / 1e9, 1),
+                     "frac": round(step_bytes / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "traffic_unit": "bytes per step",
+                     "kernel_source_sha256_16": src},
         "cpu_baseline": None,
     }
 
@@ -279,6 +286,8 @@ def bench_allreduce64(args):
     ms_step = sum(times) / len(times)
     step_bytes = 2 * K * N * 2
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    src = kernel_source_hash(["zr_ar.hip", "zr_fold.hpp", "zr_device.hpp"])
+    traffic = read_traffic("ar_ring_bf16_k64_allreduce64.counters.txt", src, step_bytes)
     return {
         "metric": "fused all-reduce GB/s (K reads + K writes), K=64, 1e9 bf16 elements",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -292,7 +301,9 @@ def bench_allreduce64(args):
                    "K": K, "N": N, "bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "kernel": "ar_kernel<bf16,K=64,ring>", "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "achieved": round(value, 1),
-                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": step_bytes,
+                     "kernel_source_sha256_16": src},
         "cpu_baseline": None,
     }
 
