@@ -16,7 +16,9 @@ import os
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libzr.so")
+# ZR_LIBRARY may name another build of the same library (a different file
+# with the same ABI); by default the in-tree build is used.
+LIB_PATH = os.environ.get("ZR_LIBRARY") or os.path.join(_HERE, "libzr.so")
 
 ZR_OK, ZR_ERR_INVALID, ZR_ERR_ALIGN, ZR_ERR_ALIAS, ZR_ERR_UNSUPPORTED, ZR_ERR_HIP = range(6)
 ZR_BF16, ZR_FP32 = 0, 1

@@ -18,10 +18,13 @@
 // loads of all S slices are issued before the first add. Loads and stores
 // are non-temporal by default: every byte is touched exactly once.
 //
-// Tiles that are whole, inside the chunk and below N, in a chunk whose start
-// j*C is aligned for quad access, take that vector path. The last tile of a
-// chunk and chunks with an unaligned start fold element by element. Positions
-// g >= N are padding and receive +0.
+// In a chunk whose start j*C allows quad access (j*C a multiple of 4), the
+// vector tiles begin at the chunk's first input element that starts a
+// 128-byte line (a head of fewer than one line of elements), so the K input
+// streams are read in whole lines; the head, the ragged tail and the padding
+// fold element by element in one extra tile. Chunks whose start does not
+// allow quad access fold element by element tile by tile. Positions g >= N
+// are padding and receive +0.
 #include "zr_fold.hpp"
 
 namespace zr {
@@ -31,16 +34,24 @@ struct RsArgs {
     ConstPtrs in;
     MutPtrs out;
     int64_t N, C;
-    uint64_t vec_mask;  // bit j: chunk j takes the vector path
+    uint64_t vec_mask;         // bit j: chunk j takes the vector path
+    int16_t head[kMaxRanks];   // chunk j's vector tiles start at chunk offset head[j]
     int K, shift;
-    int tiles_per_chunk;
+    int tiles_per_chunk;       // ceil(C / tile) + 1: the extra tile folds head and tail
     float inv_k, kf;
 };
 
 // Slices per wave: 4 for bf16 input (32 loads of 8 bytes in flight per lane
-// at K = 8), 2 for fp32 input (same bytes in flight).
+// at K = 8), 2 for fp32 input (same bytes in flight). Build-time knobs for
+// tuning sweeps.
+#ifndef ZR_RS_SLICES_BF16
+#define ZR_RS_SLICES_BF16 4
+#endif
+#ifndef ZR_RS_SLICES_FP32
+#define ZR_RS_SLICES_FP32 2
+#endif
 template <typename TIn>
-constexpr int kSlices = sizeof(TIn) == 2 ? 4 : 2;
+constexpr int kSlices = sizeof(TIn) == 2 ? ZR_RS_SLICES_BF16 : ZR_RS_SLICES_FP32;
 template <typename TIn>
 constexpr int64_t kRsTile = (int64_t)(kThreads / 64) * kSlices<TIn> * 256;
 
@@ -61,10 +72,23 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 
+    // one output element, folded element-wise (padding past N gets +0)
+    auto elem = [&](int64_t o) {
+        const int64_t g = chunk_base + o;
+        float s = 0.0f;
+        if (g < N) {
+            s = RING ? fold_ring_elem<TIn>(ptr, K, j, g) : fold_free_elem<TIn>(ptr, K, g);
+            s = average<AVG>(s, a.inv_k, a.kf);
+        }
+        store_elem(outp + o, s);
+    };
+    const int64_t h = vec ? a.head[j] : 0;
+    const int64_t valid = (N - chunk_base < C) ? N - chunk_base : C;  // non-padding extent
+    const int64_t nt = (vec && valid > h) ? (valid - h) / T : 0;      // whole vector tiles
+
     for (int t = blockIdx.x; t < a.tiles_per_chunk; t += gridDim.x) {
-        const int64_t o0 = (int64_t)t * T + (int64_t)wave * (S * 256) + lane * 4;  // chunk-local
-        const int64_t tile_end = (int64_t)(t + 1) * T;
-        if (vec && tile_end <= C && chunk_base + tile_end <= N) {
+        if (t < nt) {
+            const int64_t o0 = h + (int64_t)t * T + (int64_t)wave * (S * 256) + lane * 4;
             float acc[S][4];
             const int64_t g0 = chunk_base + o0;
             if constexpr (kStatic)
@@ -79,20 +103,14 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
                 for (int e = 0; e < 4; ++e) acc[k][e] = average<AVG>(acc[k][e], a.inv_k, a.kf);
                 store_quad<TOut, NT>(outp + o0 + 256 * k, pack4<TOut>(acc[k]));
             }
+        } else if (vec) {
+            if (t != nt) continue;
+            for (int64_t o = threadIdx.x; o < h && o < C; o += kThreads) elem(o);
+            for (int64_t o = h + nt * T + threadIdx.x; o < C; o += kThreads) elem(o);
         } else {
-            for (int k = 0; k < S; ++k) {
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t o = o0 + 256 * k + e;
-                    if (o >= C) continue;
-                    const int64_t g = chunk_base + o;
-                    float s = 0.0f;
-                    if (g < N) {
-                        s = RING ? fold_ring_elem<TIn>(ptr, K, j, g) : fold_free_elem<TIn>(ptr, K, g);
-                        s = average<AVG>(s, a.inv_k, a.kf);
-                    }
-                    store_elem(outp + o, s);
-                }
-            }
+            const int64_t lo = (int64_t)t * T;
+            const int64_t hi = (lo + T < C) ? lo + T : C;
+            for (int64_t o = lo + threadIdx.x; o < hi; o += kThreads) elem(o);
         }
     }
 }
@@ -136,18 +154,28 @@ hipError_t pick_avg(const RsArgs& a, int avg_mode, bool ring, hipStream_t s) {
 template <typename TIn, typename TOut>
 hipError_t launch_typed(RsArgs& a, int avg_mode, bool ring, hipStream_t s) {
     constexpr int64_t T = kRsTile<TIn>;
-    a.tiles_per_chunk = (int)((a.C + T - 1) / T);
-    // Vector path: every rank's input at j*C and every output base must be
-    // aligned for quad access (8 bytes for bf16 quads, 16 for fp32 quads).
+    a.tiles_per_chunk = (int)((a.C + T - 1) / T) + 1;
+    // Vector path: every base aligned for quad access (8 bytes for bf16
+    // quads, 16 for fp32 quads) and j*C a multiple of 4 elements, so that a
+    // vector tile start j*C + head is a quad boundary on the input side and
+    // head a quad boundary on the output side. head moves the tile start to
+    // the next 128-byte line of the input (lines hold 128 / sizeof(TIn)
+    // elements, a multiple of 4).
     const uintptr_t in_al = sizeof(TIn) * 4, out_al = sizeof(TOut) * 4;
+    const int64_t line = 128 / (int64_t)sizeof(TIn);
     bool bases = true;
     for (int r = 0; r < a.K; ++r) {
         bases = bases && ((uintptr_t)a.in.p[r] % in_al) == 0;
         bases = bases && ((uintptr_t)a.out.p[r] % out_al) == 0;
     }
     a.vec_mask = 0;
-    for (int j = 0; j < a.K; ++j)
-        if (bases && ((uintptr_t)(a.C * j * (int64_t)sizeof(TIn)) % in_al) == 0) a.vec_mask |= 1ull << j;
+    for (int j = 0; j < kMaxRanks; ++j) a.head[j] = 0;
+    for (int j = 0; j < a.K; ++j) {
+        const int64_t start = a.C * j;
+        if (!bases || (start % 4) != 0) continue;
+        a.vec_mask |= 1ull << j;
+        a.head[j] = (int16_t)((line - start % line) % line);
+    }
     return pick_avg<TIn, TOut>(a, avg_mode, ring, s);
 }
 
