@@ -72,7 +72,7 @@ def events_ms(pairs):
 
 
 # ----------------------------------------------------------------- zero2
-def bench_zero2(args):
+def bench_zero2(args, accumulate=False):
     import numpy as np
     import torch
 
@@ -94,20 +94,24 @@ def bench_zero2(args):
                          reduction_stream=red)
     torch.cuda.synchronize()
     print(f"# zero2: K={K} N={N} buckets={len(buckets)} inputs resident", file=sys.stderr, flush=True)
+    # an accumulation micro-step also reads the fp32 partition back
+    per_elem = 2 * K + (8 if accumulate else 4)
+    micro = 1 if accumulate else 0
+    sync.step()
     for _ in range(args.warmup):
-        sync.step()
+        sync.step(micro_step=micro)
     torch.cuda.synchronize()
     timing = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        sync.step(timing=timing)
+        sync.step(timing=timing, micro_step=micro)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    step_bytes = sum(n * (2 * K + 4) for _, n in buckets)
+    step_bytes = sum(n * per_elem for _, n in buckets)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     launch_ms = events_ms(timing)
-    launch_bytes = [n * (2 * K + 4) for _, n in buckets] * args.steps
+    launch_bytes = [n * per_elem for _, n in buckets] * args.steps
     achieved = sum(launch_bytes) / (sum(launch_ms) * 1e-3) / 1e9
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
     bytes_per_launch = sum(launch_bytes) / len(launch_bytes)
@@ -117,11 +121,16 @@ def bench_zero2(args):
           flush=True)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not accumulate:
         cpu = cpu_baseline_zero2(grads, parts, buckets[0], K, args)
     sync.close()
+    if accumulate:
+        metric = ("reduce-scatter+avg+accumulate GB/s (gradient-accumulation micro-step), K=8, "
+                  "2.38B-elem bf16 grads")
+    else:
+        metric = "reduce-scatter+avg+cast GB/s and % of HBM peak, K=8, 2.38B-elem bf16 grads"
     return {
-        "metric": "reduce-scatter+avg+cast GB/s and % of HBM peak, K=8, 2.38B-elem bf16 grads",
+        "metric": metric,
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
@@ -133,7 +142,9 @@ def bench_zero2(args):
                                "500M elements via the ping-pong scheduler, ring-order "
                                "reduce-scatter + /8 + fp32 cast into the partitioned flat grad",
                    "K": K, "N_per_rank": N, "bucket_elems": bucket, "n_buckets": len(buckets),
-                   "chunk_shift": 1, "io": "bf16 in, f32 out", "bytes_per_step": step_bytes,
+                   "chunk_shift": 1, "io": "bf16 in, f32 out" + (", f32 partition read back and "
+                                                                   "added" if accumulate else ""),
+                   "bytes_per_step": step_bytes,
                    "parallelism": "1 GPU (K ranks simulated)"},
         "roofline": {"bound": "hbm", "kernel": "rs_kernel<bf16,f32,K=8,avg,ring>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -362,7 +373,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="zero2",
-                    choices=["zero2", "zero3_ag", "allreduce64", "flatten8"])
+                    choices=["zero2", "zero2_accum", "zero3_ag", "allreduce64", "flatten8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-elems", type=int, default=0,
                     help="element indices in the CPU-baseline sample (default: all of bucket 0)")
@@ -376,7 +387,8 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    fn = {"zero2": bench_zero2, "zero3_ag": bench_zero3, "allreduce64": bench_allreduce64,
+    fn = {"zero2": bench_zero2, "zero2_accum": lambda a: bench_zero2(a, accumulate=True),
+          "zero3_ag": bench_zero3, "allreduce64": bench_allreduce64,
           "flatten8": bench_flatten8}[args.workload]
     print(json.dumps(fn(args)), flush=True)
 

@@ -23,6 +23,7 @@ LIB_PATH = os.environ.get("ZR_LIBRARY") or os.path.join(_HERE, "libzr.so")
 ZR_OK, ZR_ERR_INVALID, ZR_ERR_ALIGN, ZR_ERR_ALIAS, ZR_ERR_UNSUPPORTED, ZR_ERR_HIP = range(6)
 ZR_BF16, ZR_FP32 = 0, 1
 ZR_ORDER_RING, ZR_ORDER_FREE = 0, 1
+ZR_AVERAGE, ZR_ACCUMULATE = 1, 2
 STATUS_NAMES = {0: "ZR_OK", 1: "ZR_ERR_INVALID", 2: "ZR_ERR_ALIGN", 3: "ZR_ERR_ALIAS",
                 4: "ZR_ERR_UNSUPPORTED", 5: "ZR_ERR_HIP"}
 
@@ -141,14 +142,19 @@ def zr_flatten_bucket(frags: Sequence[Sequence], numels: Sequence[int], buckets:
                                    _stream(stream)))
 
 
+def _flags(average: bool, accumulate: bool) -> int:
+    return (ZR_AVERAGE if average else 0) | (ZR_ACCUMULATE if accumulate else 0)
+
+
 def zr_reduce_scatter_avg(inputs: Sequence, N: int, outputs: Sequence, chunk_shift: int = 1,
                           average: bool = True, order: int = ZR_ORDER_RING, in_dtype=None,
-                          out_dtype=None, stream=None) -> None:
+                          out_dtype=None, stream=None, accumulate: bool = False) -> None:
     K = len(inputs)
     in_dt = _dtype(in_dtype if in_dtype is not None else inputs[0])
     out_dt = _dtype(out_dtype if out_dtype is not None else outputs[0])
     _check(lib().zr_reduce_scatter_avg(K, _table(inputs), in_dt, N, _table(outputs), out_dt,
-                                       chunk_shift, 1 if average else 0, order, _stream(stream)))
+                                       chunk_shift, _flags(average, accumulate), order,
+                                       _stream(stream)))
 
 
 def zr_all_gather(shards: Sequence, fulls: Sequence, segs: Sequence, chunk_shift: int = 0,
@@ -195,7 +201,8 @@ class Sched:
 
     def submit_rs(self, buf: int, producer_streams: Sequence, inputs: Sequence, N: int,
                   outputs: Sequence, chunk_shift: int = 1, average: bool = True,
-                  order: int = ZR_ORDER_RING, in_dtype=None, out_dtype=None) -> None:
+                  order: int = ZR_ORDER_RING, in_dtype=None, out_dtype=None,
+                  accumulate: bool = False) -> None:
         K = len(inputs)
         prods = (ctypes.c_void_p * max(1, len(producer_streams)))(
             *[_stream(p) for p in producer_streams])
@@ -203,7 +210,7 @@ class Sched:
         out_dt = _dtype(out_dtype if out_dtype is not None else outputs[0])
         _check(lib().zr_sched_submit_rs(self._h, buf, prods, len(producer_streams), K,
                                         _table(inputs), in_dt, N, _table(outputs), out_dt,
-                                        chunk_shift, 1 if average else 0, order))
+                                        chunk_shift, _flags(average, accumulate), order))
 
     def flush(self, caller_stream=None) -> None:
         _check(lib().zr_sched_flush(self._h, _stream(caller_stream)))

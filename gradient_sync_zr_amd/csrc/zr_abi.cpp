@@ -135,8 +135,9 @@ int device_cu_count() {
 
 // Validation of a reduce-scatter call; shared with the scheduler.
 zr_status validate_rs(int K, const void* const* in, zr_dtype in_dt, int64_t N, void* const* out,
-                      zr_dtype out_dt, int shift, zr_order order, bool* no_work) {
+                      zr_dtype out_dt, int shift, int flags, zr_order order, bool* no_work) {
     ZR_TRY(check_k(K));
+    if (flags & ~(ZR_AVERAGE | ZR_ACCUMULATE)) return fail(ZR_ERR_INVALID, "flags=%d has unknown bits", flags);
     if (N < 0) return fail(ZR_ERR_INVALID, "N=%lld is negative", (long long)N);
     if (!dt_valid(in_dt) || !dt_valid(out_dt))
         return fail(ZR_ERR_UNSUPPORTED, "dtype pair (%d, %d) not supported", (int)in_dt, (int)out_dt);
@@ -160,14 +161,14 @@ zr_status validate_rs(int K, const void* const* in, zr_dtype in_dt, int64_t N, v
 }
 
 zr_status run_rs(int K, const void* const* in, zr_dtype in_dt, int64_t N, void* const* out,
-                 zr_dtype out_dt, int shift, int average, zr_order order, hipStream_t stream) {
+                 zr_dtype out_dt, int shift, int flags, zr_order order, hipStream_t stream) {
     ConstPtrs ip{};
     MutPtrs op{};
     for (int r = 0; r < K; ++r) {
         ip.p[r] = in[r];
         op.p[r] = out[r];
     }
-    hipError_t e = launch_reduce_scatter(K, ip, in_dt, N, op, out_dt, shift, average ? 1 : 0, order, stream);
+    hipError_t e = launch_reduce_scatter(K, ip, in_dt, N, op, out_dt, shift, flags, order, stream);
     if (e != hipSuccess) return hip_fail(e, "reduce-scatter launch");
     return ok();
 }
@@ -239,12 +240,12 @@ const char* zr_last_error(void) { return g_err.c_str(); }
 int zr_version(void) { return 100; }  // 0.1.0
 
 zr_status zr_reduce_scatter_avg(int K, const void* const* in, zr_dtype in_dt, int64_t N,
-                                void* const* out, zr_dtype out_dt, int chunk_shift, int average,
+                                void* const* out, zr_dtype out_dt, int chunk_shift, int flags,
                                 zr_order order, void* stream) {
     bool no_work = false;
-    ZR_TRY(validate_rs(K, in, in_dt, N, out, out_dt, chunk_shift, order, &no_work));
+    ZR_TRY(validate_rs(K, in, in_dt, N, out, out_dt, chunk_shift, flags, order, &no_work));
     if (no_work) return ok();
-    return run_rs(K, in, in_dt, N, out, out_dt, chunk_shift, average, order, (hipStream_t)stream);
+    return run_rs(K, in, in_dt, N, out, out_dt, chunk_shift, flags, order, (hipStream_t)stream);
 }
 
 zr_status zr_all_gather(int K, const void* const* shards, void* const* fulls, zr_dtype dt,
@@ -300,9 +301,9 @@ zr_status zr_allreduce(int K, const void* const* in, void* const* out, zr_dtype 
             return fail(ZR_ERR_ALIAS, "scratch overlaps rank %d's buffers", r);
     std::vector<void*> sh(K);
     for (int q = 0; q < K; ++q) sh[q] = (char*)scratch + (size_t)(q * C * es);
-    ZR_TRY(run_rs(K, in, dt, N, sh.data(), dt, 1, average, order, s));
+    ZR_TRY(run_rs(K, in, dt, N, sh.data(), dt, 1 % K, average ? ZR_AVERAGE : 0, order, s));
     zr_seg seg{0, 0, N};
-    return run_ag(K, const_cast<const void* const*>(sh.data()), out, dt, &seg, 1, 1, s);
+    return run_ag(K, const_cast<const void* const*>(sh.data()), out, dt, &seg, 1, 1 % K, s);
 }
 
 zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const int64_t* numels,

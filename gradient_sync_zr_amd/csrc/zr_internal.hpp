@@ -42,8 +42,9 @@ struct Tuning {
 const Tuning& tuning();
 int device_cu_count();  // CUs of the current device (cached per device)
 
+// flags: ZR_AVERAGE | ZR_ACCUMULATE
 hipError_t launch_reduce_scatter(int K, const ConstPtrs& in, zr_dtype in_dt, int64_t N,
-                                 const MutPtrs& out, zr_dtype out_dt, int shift, int average,
+                                 const MutPtrs& out, zr_dtype out_dt, int shift, int flags,
                                  zr_order order, hipStream_t stream);
 
 hipError_t launch_allreduce_fused(int K, const ConstPtrs& in, const MutPtrs& out, zr_dtype dt,

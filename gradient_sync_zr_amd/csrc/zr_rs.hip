@@ -38,6 +38,7 @@ struct RsArgs {
     int16_t head[kMaxRanks];   // chunk j's vector tiles start at chunk offset head[j]
     int K, shift;
     int tiles_per_chunk;       // ceil(C / tile) + 1: the extra tile folds head and tail
+    int accumulate;            // 1: out = old + result (gradient accumulation)
     float inv_k, kf;
 };
 
@@ -80,6 +81,7 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
             s = RING ? fold_ring_elem<TIn>(ptr, K, j, g) : fold_free_elem<TIn>(ptr, K, g);
             s = average<AVG>(s, a.inv_k, a.kf);
         }
+        if (a.accumulate) s = __fadd_rn(load_elem(outp + o), s);
         store_elem(outp + o, s);
     };
     const int64_t h = vec ? a.head[j] : 0;
@@ -98,11 +100,20 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
             else
                 fold_free_quads<TIn, KS, NT, S>(a.in, K, g0, acc);
 #pragma unroll
-            for (int k = 0; k < S; ++k) {
+            for (int k = 0; k < S; ++k)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[k][e] = average<AVG>(acc[k][e], a.inv_k, a.kf);
-                store_quad<TOut, NT>(outp + o0 + 256 * k, pack4<TOut>(acc[k]));
+            if (a.accumulate) {
+#pragma unroll
+                for (int k = 0; k < S; ++k) {
+                    float old[4];
+                    widen4(load_quad<TOut, NT>(outp + o0 + 256 * k), old);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[k][e] = __fadd_rn(old[e], acc[k][e]);
+                }
             }
+#pragma unroll
+            for (int k = 0; k < S; ++k) store_quad<TOut, NT>(outp + o0 + 256 * k, pack4<TOut>(acc[k]));
         } else if (vec) {
             if (t != nt) continue;
             for (int64_t o = threadIdx.x; o < h && o < C; o += kThreads) elem(o);
@@ -182,7 +193,7 @@ hipError_t launch_typed(RsArgs& a, int avg_mode, bool ring, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_reduce_scatter(int K, const ConstPtrs& in, zr_dtype in_dt, int64_t N,
-                                 const MutPtrs& out, zr_dtype out_dt, int shift, int average,
+                                 const MutPtrs& out, zr_dtype out_dt, int shift, int flags,
                                  zr_order order, hipStream_t stream) {
     RsArgs a;
     a.in = in;
@@ -193,8 +204,9 @@ hipError_t launch_reduce_scatter(int K, const ConstPtrs& in, zr_dtype in_dt, int
     a.shift = shift;
     a.inv_k = 1.0f / (float)K;
     a.kf = (float)K;
+    a.accumulate = (flags & ZR_ACCUMULATE) ? 1 : 0;
     const bool pow2 = (K & (K - 1)) == 0;
-    const int avg_mode = !average ? 0 : (pow2 ? 1 : 2);
+    const int avg_mode = !(flags & ZR_AVERAGE) ? 0 : (pow2 ? 1 : 2);
     const bool ring = order == ZR_ORDER_RING;
     if (in_dt == ZR_BF16 && out_dt == ZR_FP32) return launch_typed<uint16_t, float>(a, avg_mode, ring, stream);
     if (in_dt == ZR_BF16 && out_dt == ZR_BF16) return launch_typed<uint16_t, uint16_t>(a, avg_mode, ring, stream);

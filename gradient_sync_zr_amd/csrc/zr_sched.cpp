@@ -9,9 +9,9 @@
 
 namespace zr {
 zr_status validate_rs(int K, const void* const* in, zr_dtype in_dt, int64_t N, void* const* out,
-                      zr_dtype out_dt, int shift, zr_order order, bool* no_work);
+                      zr_dtype out_dt, int shift, int flags, zr_order order, bool* no_work);
 zr_status run_rs(int K, const void* const* in, zr_dtype in_dt, int64_t N, void* const* out,
-                 zr_dtype out_dt, int shift, int average, zr_order order, hipStream_t stream);
+                 zr_dtype out_dt, int shift, int flags, zr_order order, hipStream_t stream);
 zr_status set_error(zr_status st, const char* msg);
 
 namespace {
@@ -80,15 +80,15 @@ zr_status zr_sched_acquire(zr_sched* s, int buf, void* producer_stream) {
 
 zr_status zr_sched_submit_rs(zr_sched* s, int buf, void* const* producer_streams, int n_prod, int K,
                              const void* const* in, zr_dtype in_dt, int64_t N, void* const* out,
-                             zr_dtype out_dt, int chunk_shift, int average, zr_order order) {
+                             zr_dtype out_dt, int chunk_shift, int flags, zr_order order) {
     if (!s) return zr::set_error(ZR_ERR_INVALID, "scheduler is NULL");
     bool no_work = false;
-    zr_status st = zr::validate_rs(K, in, in_dt, N, out, out_dt, chunk_shift, order, &no_work);
+    zr_status st = zr::validate_rs(K, in, in_dt, N, out, out_dt, chunk_shift, flags, order, &no_work);
     if (st != ZR_OK) return st;
     zr_status launch_st = ZR_OK;
     auto launch = [&](hipStream_t red) {
         if (no_work) return true;
-        launch_st = zr::run_rs(K, in, in_dt, N, out, out_dt, chunk_shift, average, order, red);
+        launch_st = zr::run_rs(K, in, in_dt, N, out, out_dt, chunk_shift, flags, order, red);
         return launch_st == ZR_OK;
     };
     zr::SchedErr e = s->core.submit(buf, reinterpret_cast<const hipStream_t*>(producer_streams), n_prod, launch);

@@ -65,9 +65,13 @@ class Zero2GradSync:
         self.sched = Sched(n_buffers=n_buffers, max_producers=1,
                            reduction_stream=reduction_stream)
 
-    def step(self, producer_stream=None, timing: Optional[List] = None) -> None:
+    def step(self, producer_stream=None, timing: Optional[List] = None,
+             micro_step: int = 0) -> None:
         """One gradient sync. `timing`, if given, receives (start, end) torch
-        events recorded on the reduction stream around each bucket's launch."""
+        events recorded on the reduction stream around each bucket's launch.
+        Micro-step 0 overwrites the partitions; later micro-steps of a
+        gradient-accumulation window add to them ("DeepSpeed ZeRO-3 源码解析",
+        5.3 and 6)."""
         import torch
         prod = producer_stream if producer_stream is not None else torch.cuda.current_stream()
         for i, (n, ins, outs, _, _) in enumerate(self.buckets):
@@ -80,7 +84,7 @@ class Zero2GradSync:
                 e0.record(self.reduction_stream)
             self.sched.submit_rs(buf, [prod], ins, n, outs, chunk_shift=self.shift,
                                  average=self.average, order=self.order, in_dtype=self.in_dt,
-                                 out_dtype=self.out_dt)
+                                 out_dtype=self.out_dt, accumulate=micro_step > 0)
             if timing is not None:
                 e1.record(self.reduction_stream)
                 timing.append((e0, e1))

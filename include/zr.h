@@ -115,27 +115,38 @@ zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const i
                             void* const* buckets, int64_t padded_numel, zr_dtype dt,
                             void* stream);
 
+/* Flags of the reduce-scatter calls. */
+#define ZR_AVERAGE 1    /* divide the sum by K */
+#define ZR_ACCUMULATE 2 /* add into the existing partition instead of overwriting it */
+
 /*
  * Fused reduce-scatter + average + cast [RING Phase 1; L14 3.2, 4.1;
- * ZERO3 1, 5.2, 5.3]. For every holder rank q and o in [0, C), with
+ * ZERO3 1, 5.2, 5.3, 6]. For every holder rank q and o in [0, C), with
  * j = (q + chunk_shift) mod K and g = j*C + o:
  *     S        = ring-order fp32 fold of in_{j}[g], in_{j+1}[g], ..., in_{j-1}[g]
  *                (0 when g >= N)
- *     out_q[o] = S / K if average else S   (one IEEE fp32 divide; exact
- *                multiply by 1/K when K is a power of two)
+ *     A        = S / K if (flags & ZR_AVERAGE) else S   (one IEEE fp32 divide;
+ *                exact multiply by 1/K when K is a power of two)
+ *     out_q[o] = A, or old + A in fp32 if (flags & ZR_ACCUMULATE), where old is
+ *                the value already in out_q[o] widened to fp32
  * written as fp32 (no intermediate bf16 rounding) or rounded once to bf16.
- * Positions with g >= N receive +0.
+ * ZR_ACCUMULATE is gradient accumulation over micro-steps: the first
+ * micro-step overwrites the partition, later ones add to it in place
+ * [ZERO3 5.3, 6]. Positions with g >= N receive +0 (or keep old + 0).
  *
  *  in        host array [K] of device pointers, N elements each (in_dt)
  *  out       host array [K] of device pointers, C elements each (out_dt)
  *  in_dt     ZR_BF16 or ZR_FP32; out_dt ZR_FP32 or ZR_BF16
+ *  flags     0..3: ZR_AVERAGE and/or ZR_ACCUMULATE; other bits are ZR_ERR_INVALID
  *  order     ZR_ORDER_RING (bit-exact ring order) or ZR_ORDER_FREE
  * Outputs must be distinct and must not overlap any input (ZR_ERR_ALIAS).
- * Reads K*N elements once and writes K*C elements.
+ * Reads K*N elements once (plus the K*C old outputs when accumulating) and
+ * writes K*C elements.
  */
 zr_status zr_reduce_scatter_avg(int K, const void* const* in, zr_dtype in_dt, int64_t N,
                                 void* const* out, zr_dtype out_dt, int chunk_shift,
-                                int average, zr_order order, void* stream);
+                                int flags /* ZR_AVERAGE | ZR_ACCUMULATE */, zr_order order,
+                                void* stream);
 
 /*
  * All-gather of sharded tensors into full tensors [RING Phase 2; L14 3.2;
@@ -211,8 +222,8 @@ zr_status zr_sched_create(zr_sched** out, int n_buffers, int max_producers,
 zr_status zr_sched_acquire(zr_sched* s, int buf, void* producer_stream);
 zr_status zr_sched_submit_rs(zr_sched* s, int buf, void* const* producer_streams, int n_prod,
                              int K, const void* const* in, zr_dtype in_dt, int64_t N,
-                             void* const* out, zr_dtype out_dt, int chunk_shift, int average,
-                             zr_order order);
+                             void* const* out, zr_dtype out_dt, int chunk_shift,
+                             int flags /* as zr_reduce_scatter_avg */, zr_order order);
 zr_status zr_sched_flush(zr_sched* s, void* caller_stream);
 zr_status zr_sched_destroy(zr_sched* s);
 

@@ -127,20 +127,25 @@ def exact_sum_points(xs: np.ndarray):
     return out, ab
 
 
-def reduce_scatter(inputs, N, out_dtype, shift=1, average=True, o_range=None, out=None):
+def reduce_scatter(inputs, N, out_dtype, shift=1, average=True, o_range=None, out=None,
+                   accumulate=False):
     """inputs: list of K arrays (uint16 bf16 or float32) of >= N elements.
-    Returns (or fills) K arrays of C = ceil(N/K) elements of out_dtype."""
+    Returns (or fills) K arrays of C = ceil(N/K) elements of out_dtype. With
+    accumulate=True, `out` holds the previous partitions and is added into."""
     K = len(inputs)
     C = chunk_size(N, K)
     ins = [np.ascontiguousarray(a) for a in inputs]
     in_dt = _dt(ins[0])
     assert all(_dt(a) == in_dt and a.size >= N for a in ins)
     if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs the previous partitions in `out`")
         out = [np.empty(C, dtype=out_dtype) for _ in range(K)]
     out_dt = _dt(out[0])
     lo, hi = (0, C) if o_range is None else o_range
+    flags = (1 if average else 0) | (2 if accumulate else 0)
     rc = _load().orc_reduce_scatter_part(K, N, in_dt, _ptrs(ins), out_dt, _ptrs(out), shift,
-                                         1 if average else 0, lo, hi)
+                                         flags, lo, hi)
     _check(rc, "reduce_scatter")
     return out
 

@@ -183,12 +183,17 @@ void orc_exact_sum_points(int K, int64_t n, const float* xs, double* out, double
  * For every holder rank q and every offset o in [o_lo, o_hi) of its chunk:
  *   j = (q + shift) mod K, g = j*C + o,
  *   S = ring-order fold of x_{j}, x_{j+1}, ..., x_{j-1} at g (0 if g >= N),
- *   out_q[o] = S / K if average else S, stored as fp32 or rounded to bf16.
+ *   A = S / K if (flags & 1) else S,
+ *   out_q[o] = A, or, if (flags & 2), the value already in out_q[o] plus A
+ *   in one fp32 add (gradient accumulation: the first micro-step copies,
+ *   later ones add in place [ZERO3 5.3, 6]),
+ * stored as fp32 or rounded to bf16.
  */
 int orc_reduce_scatter_part(int K, int64_t N, int in_dt, const void* const* in, int out_dt,
-                            void* const* out, int shift, int average, int64_t o_lo,
+                            void* const* out, int shift, int flags, int64_t o_lo,
                             int64_t o_hi) {
-    if (K < 1 || N < 0 || shift < 0 || shift >= K) return -1;
+    if (K < 1 || N < 0 || shift < 0 || shift >= K || (flags & ~3)) return -1;
+    int average = flags & 1, accumulate = flags & 2;
     int64_t C = chunk_of(N, K);
     if (o_lo < 0 || o_hi > C || o_lo > o_hi) return -1;
     for (int q = 0; q < K; ++q) {
@@ -201,6 +206,7 @@ int orc_reduce_scatter_part(int K, int64_t N, int in_dt, const void* const* in, 
                 for (int h = 1; h < K; ++h) acc = acc + load_elem(in[(j + h) % K], in_dt, g);
                 if (average) acc = acc / (float)K;
             }
+            if (accumulate) acc = load_elem(out[q], out_dt, o) + acc;
             store_elem(out[q], out_dt, o, acc);
         }
     }
@@ -208,9 +214,8 @@ int orc_reduce_scatter_part(int K, int64_t N, int in_dt, const void* const* in, 
 }
 
 int orc_reduce_scatter(int K, int64_t N, int in_dt, const void* const* in, int out_dt,
-                       void* const* out, int shift, int average) {
-    return orc_reduce_scatter_part(K, N, in_dt, in, out_dt, out, shift, average, 0,
-                                   chunk_of(N, K));
+                       void* const* out, int shift, int flags) {
+    return orc_reduce_scatter_part(K, N, in_dt, in, out_dt, out, shift, flags, 0, chunk_of(N, K));
 }
 
 /* --------------------------------------------------------------- all-gather
@@ -256,7 +261,7 @@ int orc_allreduce(int K, int64_t N, int dt, const void* const* in, void* const* 
     for (int q = 0; q < K; ++q) shards[q] = shard_mem + (size_t)q * es * (size_t)C;
     /* ring placement: rank q holds chunk (q + 1) mod K, a shift of 1 mod K */
     int shift = 1 % K;
-    int rc = orc_reduce_scatter(K, N, dt, in, dt, shards, shift, average);
+    int rc = orc_reduce_scatter(K, N, dt, in, dt, shards, shift, average ? 1 : 0);
     if (rc == 0) {
         int64_t seg[3] = {0, 0, N};
         rc = orc_all_gather(K, dt, (const void* const*)shards, out, seg, 1, shift);

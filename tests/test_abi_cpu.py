@@ -85,6 +85,16 @@ def test_rs_validation_errors():
     expect(zr.ZR_ERR_ALIAS, rs, outs=[A + 64] + ranks(7, base=A + (1 << 40)))
 
 
+def test_rs_rejects_unknown_flag_bits():
+    lib = zr.lib()
+    t = (ctypes.c_void_p * 8)(*ranks(8))
+    o = (ctypes.c_void_p * 8)(*ranks(8, base=A + (1 << 40)))
+    for flags in (4, 8, -1, 7):
+        assert lib.zr_reduce_scatter_avg(8, t, 0, 100, o, 1, 1, flags, 0, None) == zr.ZR_ERR_INVALID
+    for flags in (0, 1, 2, 3):   # valid flags, N = 0: no work, no HIP call
+        assert lib.zr_reduce_scatter_avg(8, t, 0, 0, o, 1, 1, flags, 0, None) == zr.ZR_OK
+
+
 def test_rs_duplicate_inputs_and_zero_n_are_accepted_without_work():
     rs(N=0)                                  # no work: OK before any HIP call
     rs(N=0, ins=[0] * 8, outs=[0] * 8)       # tables unused when N == 0

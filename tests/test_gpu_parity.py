@@ -86,6 +86,40 @@ def test_reduce_scatter_ring_bit_exact(K, N, in_bf16, out_bf16, shift, average, 
         assert outs[r].guards_intact() and ins[r].guards_intact()
 
 
+ACC_CASES = [
+    # K, N, in_bf16, out_bf16, shift, average, offset
+    (8, 8 * 4096 * 3 + 8 * 40, True, False, 1, True, 0),
+    (8, 100003, True, True, 1, True, 0),
+    (5, 77777, False, False, 2, True, 0),
+    (8, 65536 + 5, True, False, 0, False, 1),     # element-wise path
+    (64, 64 * 4096 + 3, True, False, 1, True, 0),
+    (3, 2, True, False, 1, True, 0),
+]
+
+
+@pytest.mark.parametrize("K,N,in_bf16,out_bf16,shift,average,offset", ACC_CASES)
+def test_reduce_scatter_accumulate_bit_exact(K, N, in_bf16, out_bf16, shift, average, offset):
+    # gradient accumulation: micro-step 0 overwrites, micro-steps 1.. add in place
+    import torch
+    C = -(-N // K)
+    steps = [make_inputs(K, N, in_bf16, 777 + K + N + m) for m in range(3)]
+    ins = [Guarded(N, torch_dt(in_bf16), offset) for _ in range(K)]
+    outs = [Guarded(C, torch_dt(out_bf16), offset) for _ in range(K)]
+    want = None
+    for m, xs in enumerate(steps):
+        for r in range(K):
+            ins[r].set(xs[r])
+        zr().zr_reduce_scatter_avg([g.ptr() for g in ins], N, [g.ptr() for g in outs],
+                                   chunk_shift=shift, average=average, accumulate=m > 0,
+                                   in_dtype=torch_dt(in_bf16), out_dtype=torch_dt(out_bf16))
+        want = oracle.reduce_scatter(xs, N, np.uint16 if out_bf16 else np.float32, shift=shift,
+                                     average=average, out=want, accumulate=m > 0)
+    torch.cuda.synchronize()
+    for r in range(K):
+        assert np.array_equal(bits(outs[r].get()), bits(want[r])), f"rank {r}"
+        assert outs[r].guards_intact()
+
+
 @pytest.mark.parametrize("K,N,in_bf16,out_bf16,average", [
     (8, 100003, True, False, True), (64, 70001, True, True, False), (5, 30000, False, False, True),
     (16, 16 * 2048 * 2, True, False, True)])

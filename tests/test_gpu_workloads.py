@@ -152,8 +152,16 @@ def test_zero2_grad_sync_full_size_sampled():
             got = parts[q].index_select(0, idx).cpu().numpy()
             assert np.array_equal(bits(got), bits(want[q])), f"bucket at {start}, rank {q}"
         poff += Cb
+    # gradient accumulation at full size: a second micro-step of the same
+    # gradients adds the same averages, so every partition doubles exactly
+    first = [p.clone() for p in parts]
+    sync.step(micro_step=1)
+    torch.cuda.synchronize()
+    for q in range(K):
+        assert torch.equal(parts[q], first[q] * 2), f"accumulate rank {q}"
+    del first
     sync.close()
-    say("zero2: sampled outputs bit-exact")
+    say("zero2: sampled outputs bit-exact; accumulation micro-step doubles exactly")
 
 
 # ---------------------------------------------------------- zero3_ag (cfg 4)

@@ -437,3 +437,59 @@ def test_bf16_round_matches_exact_rational_and_torch():
     assert np.all(np.isnan(oracle.bf16_to_f32(nb)))
     inf = oracle.f32_to_bf16(np.array([np.inf, -np.inf], dtype=np.float32))
     assert inf.tolist() == [0x7F80, 0xFF80]
+
+
+# ----------------------------------------------------- gradient accumulation
+def test_accumulate_integer_micro_steps_exact():
+    # "DeepSpeed ZeRO-3 源码解析" 5.3 / 6: micro-step 0 copies, later micro-steps
+    # add into the same partition. Integer gradients keep every sum exact, so
+    # the partition after M micro-steps is the int64 sum over all of them.
+    rng = np.random.default_rng(21)
+    K, N, M = 4, 4 * 13 + 2, 3
+    steps = [rng.integers(-8, 9, size=(K, N)) for _ in range(M)]
+    out = oracle.reduce_scatter([s.astype(np.float32) for s in steps[0]], N, np.float32,
+                                shift=1, average=False)
+    for s in steps[1:]:
+        oracle.reduce_scatter([x.astype(np.float32) for x in s], N, np.float32, shift=1,
+                              average=False, out=out, accumulate=True)
+    total = sum(s.sum(axis=0) for s in steps)
+    C = -(-N // K)
+    for q in range(K):
+        j = (q + 1) % K
+        for o in range(C):
+            g = j * C + o
+            assert out[q][o] == (total[g] if g < N else 0)
+
+
+@pytest.mark.parametrize("K,out_bf16", [(8, False), (8, True), (3, False), (5, True)])
+def test_accumulate_is_one_add_of_old_and_average(K, out_bf16):
+    import torch
+    rng = np.random.default_rng(K * 2 + out_bf16)
+    N = K * 40 + 3
+    a = [wide_random(N, rng) for _ in range(K)]
+    b = [wide_random(N, rng) for _ in range(K)]
+    dt = np.uint16 if out_bf16 else np.float32
+    first = oracle.reduce_scatter(a, N, dt, shift=1, average=True)
+    alone = oracle.reduce_scatter(b, N, np.float32, shift=1, average=True)
+    acc = [x.copy() for x in first]
+    oracle.reduce_scatter(b, N, dt, shift=1, average=True, out=acc, accumulate=True)
+    for q in range(K):
+        if out_bf16:
+            old = torch.from_numpy(first[q].view(np.int16).copy()).view(torch.bfloat16).float()
+            want = (old + torch.from_numpy(alone[q])).to(torch.bfloat16).view(torch.int16)
+            assert np.array_equal(acc[q], want.numpy().view(np.uint16))
+        else:
+            assert np.array_equal(acc[q].view(np.uint32), (first[q] + alone[q]).view(np.uint32))
+
+
+def test_accumulate_into_zero_equals_plain():
+    rng = np.random.default_rng(4)
+    K, N = 8, 8 * 33
+    xs = [wide_random(N, rng) for _ in range(K)]
+    plain = oracle.reduce_scatter(xs, N, np.float32, shift=0, average=True)
+    acc = [np.zeros(-(-N // K), dtype=np.float32) for _ in range(K)]
+    oracle.reduce_scatter(xs, N, np.float32, shift=0, average=True, out=acc, accumulate=True)
+    for q in range(K):
+        # +0 + v == v for every v except -0 (which becomes +0)
+        same = (plain[q] == acc[q]) & ~((plain[q] == 0) & np.signbit(plain[q]))
+        assert np.all(same | ((plain[q] == 0) & (acc[q] == 0)))
