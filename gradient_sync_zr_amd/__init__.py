@@ -22,14 +22,19 @@ LIB_PATH = os.environ.get("ZR_LIBRARY") or os.path.join(_HERE, "libzr.so")
 
 ZR_OK, ZR_ERR_INVALID, ZR_ERR_ALIGN, ZR_ERR_ALIAS, ZR_ERR_UNSUPPORTED, ZR_ERR_HIP = range(6)
 ZR_BF16, ZR_FP32 = 0, 1
-ZR_ORDER_RING, ZR_ORDER_FREE = 0, 1
+ZR_ORDER_RING, ZR_ORDER_FREE, ZR_ORDER_RING_WIRE = 0, 1, 2
 ZR_AVERAGE, ZR_ACCUMULATE = 1, 2
 STATUS_NAMES = {0: "ZR_OK", 1: "ZR_ERR_INVALID", 2: "ZR_ERR_ALIGN", 3: "ZR_ERR_ALIAS",
                 4: "ZR_ERR_UNSUPPORTED", 5: "ZR_ERR_HIP"}
 
+COST_EXPORTS = ("zr_cost_ring_allreduce", "zr_cost_ring_reduce_scatter", "zr_cost_tree_allreduce",
+                "zr_cost_naive_allreduce", "zr_cost_pipelined_broadcast",
+                "zr_cost_best_broadcast_segments", "zr_cost_ring_tree_crossover",
+                "zr_cost_ring_naive_crossover", "zr_cost_dp_speedup")
 EXPORTS = ("zr_last_error", "zr_version", "zr_flatten_bucket", "zr_reduce_scatter_avg",
            "zr_all_gather", "zr_allreduce", "zr_plan_buckets", "zr_sched_create",
-           "zr_sched_acquire", "zr_sched_submit_rs", "zr_sched_flush", "zr_sched_destroy")
+           "zr_sched_acquire", "zr_sched_submit_rs", "zr_sched_flush",
+           "zr_sched_destroy") + COST_EXPORTS
 
 
 class ZrError(RuntimeError):
@@ -72,6 +77,21 @@ def lib() -> ctypes.CDLL:
         L.zr_sched_destroy.argtypes = [_vp]
         for f in EXPORTS[2:]:
             getattr(L, f).restype = ctypes.c_int
+        _d = ctypes.c_double
+        for f in ("zr_cost_ring_allreduce", "zr_cost_ring_reduce_scatter",
+                  "zr_cost_tree_allreduce", "zr_cost_naive_allreduce"):
+            getattr(L, f).argtypes = [_i32, _d, _d, _d]
+            getattr(L, f).restype = _d
+        L.zr_cost_pipelined_broadcast.argtypes = [_i32, _d, _i32, _d, _d]
+        L.zr_cost_pipelined_broadcast.restype = _d
+        L.zr_cost_best_broadcast_segments.argtypes = [_i32, _d, _d, _d, _i32,
+                                                      ctypes.POINTER(_d)]
+        L.zr_cost_best_broadcast_segments.restype = _i32
+        for f in ("zr_cost_ring_tree_crossover", "zr_cost_ring_naive_crossover"):
+            getattr(L, f).argtypes = [_i32, _d, _d]
+            getattr(L, f).restype = _d
+        L.zr_cost_dp_speedup.argtypes = [_i32, _d, _d, _d, _d]
+        L.zr_cost_dp_speedup.restype = _d
         _lib = L
     return _lib
 
@@ -184,6 +204,47 @@ def zr_plan_buckets(numels: Sequence[int], cap: int):
     nb = ctypes.c_int32(0)
     _check(lib().zr_plan_buckets(n, arr, cap, out, ctypes.byref(nb)))
     return list(out)[:n], nb.value
+
+
+# ------------------------------------------------------------- cost model
+def zr_cost_ring_allreduce(K, nbytes, alpha, beta):
+    return lib().zr_cost_ring_allreduce(K, nbytes, alpha, beta)
+
+
+def zr_cost_ring_reduce_scatter(K, nbytes, alpha, beta):
+    return lib().zr_cost_ring_reduce_scatter(K, nbytes, alpha, beta)
+
+
+def zr_cost_tree_allreduce(K, nbytes, alpha, beta):
+    return lib().zr_cost_tree_allreduce(K, nbytes, alpha, beta)
+
+
+def zr_cost_naive_allreduce(K, nbytes, alpha, beta):
+    return lib().zr_cost_naive_allreduce(K, nbytes, alpha, beta)
+
+
+def zr_cost_pipelined_broadcast(K, nbytes, segments, alpha, beta):
+    return lib().zr_cost_pipelined_broadcast(K, nbytes, segments, alpha, beta)
+
+
+def zr_cost_best_broadcast_segments(K, nbytes, alpha, beta, max_segments=1 << 20):
+    """Returns (segments, time)."""
+    t = ctypes.c_double(0.0)
+    s = lib().zr_cost_best_broadcast_segments(K, nbytes, alpha, beta, max_segments,
+                                              ctypes.byref(t))
+    return s, t.value
+
+
+def zr_cost_ring_tree_crossover(K, alpha, beta):
+    return lib().zr_cost_ring_tree_crossover(K, alpha, beta)
+
+
+def zr_cost_ring_naive_crossover(K, alpha, beta):
+    return lib().zr_cost_ring_naive_crossover(K, alpha, beta)
+
+
+def zr_cost_dp_speedup(K, t1, grad_bytes, alpha, beta):
+    return lib().zr_cost_dp_speedup(K, t1, grad_bytes, alpha, beta)
 
 
 class Sched:

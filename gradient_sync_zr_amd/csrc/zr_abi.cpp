@@ -142,7 +142,7 @@ zr_status validate_rs(int K, const void* const* in, zr_dtype in_dt, int64_t N, v
     if (!dt_valid(in_dt) || !dt_valid(out_dt))
         return fail(ZR_ERR_UNSUPPORTED, "dtype pair (%d, %d) not supported", (int)in_dt, (int)out_dt);
     if (shift < 0 || shift >= K) return fail(ZR_ERR_INVALID, "chunk_shift=%d not in [0, %d)", shift, K);
-    if (order != ZR_ORDER_RING && order != ZR_ORDER_FREE)
+    if (order != ZR_ORDER_RING && order != ZR_ORDER_FREE && order != ZR_ORDER_RING_WIRE)
         return fail(ZR_ERR_INVALID, "order=%d is not a zr_order", (int)order);
     *no_work = (N == 0);
     if (N == 0) return ok();
@@ -261,7 +261,7 @@ zr_status zr_allreduce(int K, const void* const* in, void* const* out, zr_dtype 
     ZR_TRY(check_k(K));
     if (N < 0) return fail(ZR_ERR_INVALID, "N=%lld is negative", (long long)N);
     if (!dt_valid(dt)) return fail(ZR_ERR_UNSUPPORTED, "dtype %d not supported", (int)dt);
-    if (order != ZR_ORDER_RING && order != ZR_ORDER_FREE)
+    if (order != ZR_ORDER_RING && order != ZR_ORDER_FREE && order != ZR_ORDER_RING_WIRE)
         return fail(ZR_ERR_INVALID, "order=%d is not a zr_order", (int)order);
     if (N == 0) return ok();
     const int64_t es = dt_bytes(dt);

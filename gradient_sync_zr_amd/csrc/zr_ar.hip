@@ -35,7 +35,7 @@ constexpr int kArSlices = sizeof(T) == 2 ? 4 : 2;
 template <typename T>
 constexpr int64_t kArTile = (int64_t)(kThreads / 64) * kArSlices<T> * 256;
 
-template <typename T, int KS, int AVG, bool RING, bool NT>
+template <typename T, int KS, int AVG, int ORDER, bool NT>
 __global__ void __launch_bounds__(kThreads) ar_kernel(const ArArgs a) {
     constexpr int S = kArSlices<T>;
     constexpr int64_t TT = kArTile<T>;
@@ -57,12 +57,9 @@ __global__ void __launch_bounds__(kThreads) ar_kernel(const ArArgs a) {
         const int64_t g0 = t0 + (int64_t)wave * (S * 256) + lane * 4;
         if (a.vec && j0 == j1 && t1 - t0 == TT) {
             float acc[S][4];
-            if constexpr (RING && KS > 0 && KS <= 8)
-                fold_ring_quads_static<T, KS, NT, S>(RingBases<T, KS>(a.in, j0), g0, acc);
-            else if constexpr (RING)
-                fold_ring_quads<T, KS, NT, S>(a.in, K, j0, g0, acc);
-            else
-                fold_free_quads<T, KS, NT, S>(a.in, K, g0, acc);
+            constexpr bool kStatic = ORDER != kFree && KS > 0 && KS <= 8;
+            fold_quads<T, KS, NT, S, ORDER, kStatic>(RingBases<T, kStatic ? KS : 1>(a.in, kStatic ? j0 : 0),
+                                                      a.in, K, j0, g0, acc);
             Quad<T> res[S];
 #pragma unroll
             for (int k = 0; k < S; ++k) {
@@ -81,8 +78,7 @@ __global__ void __launch_bounds__(kThreads) ar_kernel(const ArArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     const int64_t ge = g0 + 256 * k + e;
                     if (ge >= N) continue;
-                    float s = RING ? fold_ring_elem<T>(lds_ptr, K, (int)(ge / C), ge)
-                                   : fold_free_elem<T>(lds_ptr, K, ge);
+                    float s = fold_elem<T, ORDER>(lds_ptr, K, (int)(ge / C), ge);
                     s = average<AVG>(s, a.inv_k, a.kf);
                     T v;
                     store_elem(&v, s);
@@ -93,37 +89,38 @@ __global__ void __launch_bounds__(kThreads) ar_kernel(const ArArgs a) {
     }
 }
 
-template <typename T, int KS, int AVG, bool RING, bool NT>
+template <typename T, int KS, int AVG, int ORDER, bool NT>
 hipError_t launch_t(const ArArgs& a, hipStream_t stream) {
     int64_t want = (int64_t)device_cu_count() * tuning().ar_blocks_per_cu;
     if (want < 1) want = 1;
     const int gx = (int)(want < a.n_tiles ? want : a.n_tiles);
-    hipLaunchKernelGGL((ar_kernel<T, KS, AVG, RING, NT>), dim3(gx), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((ar_kernel<T, KS, AVG, ORDER, NT>), dim3(gx), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-template <typename T, int KS, int AVG, bool RING>
+template <typename T, int KS, int AVG, int ORDER>
 hipError_t pick_nt(const ArArgs& a, hipStream_t s) {
-    return tuning().ar_nontemporal ? launch_t<T, KS, AVG, RING, true>(a, s)
-                                   : launch_t<T, KS, AVG, RING, false>(a, s);
+    return tuning().ar_nontemporal ? launch_t<T, KS, AVG, ORDER, true>(a, s)
+                                   : launch_t<T, KS, AVG, ORDER, false>(a, s);
 }
 
 template <typename T, int AVG>
-hipError_t pick_k(const ArArgs& a, bool ring, hipStream_t s) {
-    if (!ring) return pick_nt<T, 0, AVG, false>(a, s);
+hipError_t pick_k(const ArArgs& a, int order, hipStream_t s) {
+    if (order == kFree) return pick_nt<T, 0, AVG, kFree>(a, s);
+    if (order == kWire && sizeof(T) == 2) return pick_nt<T, 0, AVG, kWire>(a, s);
     switch (a.K) {
-        case 8: return pick_nt<T, 8, AVG, true>(a, s);
-        case 64: return pick_nt<T, 64, AVG, true>(a, s);
-        default: return pick_nt<T, 0, AVG, true>(a, s);
+        case 8: return pick_nt<T, 8, AVG, kRing>(a, s);
+        case 64: return pick_nt<T, 64, AVG, kRing>(a, s);
+        default: return pick_nt<T, 0, AVG, kRing>(a, s);
     }
 }
 
 template <typename T>
-hipError_t pick_avg(const ArArgs& a, int avg_mode, bool ring, hipStream_t s) {
+hipError_t pick_avg(const ArArgs& a, int avg_mode, int order, hipStream_t s) {
     switch (avg_mode) {
-        case 1: return pick_k<T, 1>(a, ring, s);
-        case 2: return pick_k<T, 2>(a, ring, s);
-        default: return pick_k<T, 0>(a, ring, s);
+        case 1: return pick_k<T, 1>(a, order, s);
+        case 2: return pick_k<T, 2>(a, order, s);
+        default: return pick_k<T, 0>(a, order, s);
     }
 }
 
@@ -148,9 +145,9 @@ hipError_t launch_allreduce_fused(int K, const ConstPtrs& in, const MutPtrs& out
     a.vec = vec ? 1 : 0;
     const bool pow2 = (K & (K - 1)) == 0;
     const int avg_mode = !average ? 0 : (pow2 ? 1 : 2);
-    const bool ring = order == ZR_ORDER_RING;
-    if (dt == ZR_BF16) return pick_avg<uint16_t>(a, avg_mode, ring, stream);
-    return pick_avg<float>(a, avg_mode, ring, stream);
+    const int ord = order == ZR_ORDER_FREE ? kFree : (order == ZR_ORDER_RING_WIRE ? kWire : kRing);
+    if (dt == ZR_BF16) return pick_avg<uint16_t>(a, avg_mode, ord, stream);
+    return pick_avg<float>(a, avg_mode, ord, stream);
 }
 
 }  // namespace zr

@@ -12,6 +12,10 @@
 // Free order: ranks 0..K-1 in batches of eight, each batch summed as a
 // balanced pairwise tree, batches added in sequence. Not bit-identical to the
 // ring order; within the fp32 summation error bound of the exact sum.
+//
+// Wire order: the ring order with every hop's partial sum rounded to bf16
+// before the next hop adds to it, as a ring that carries bf16 partial sums
+// between ranks does (the receiver adds in fp32 and sends on a bf16 value).
 #pragma once
 
 #include "zr_device.hpp"
@@ -20,6 +24,24 @@
 namespace zr {
 
 __device__ __forceinline__ int wrap(int r, int K) { return r >= K ? r - K : r; }
+
+// Fold orders (template arguments of the kernels).
+constexpr int kRing = 0;
+constexpr int kFree = 1;
+constexpr int kWire = 2;
+
+// The fp32 value of v rounded to bf16 (nearest even), used between hops of
+// the wire order.
+__device__ __forceinline__ float wire_round(float v) { return __uint_as_float(bf16_round(v) << 16); }
+
+template <bool WIRE>
+__device__ __forceinline__ void hop4(float acc[4], const float f[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        acc[e] = __fadd_rn(acc[e], f[e]);
+        if constexpr (WIRE) acc[e] = wire_round(acc[e]);
+    }
+}
 
 // Rank buffers in ring order for chunk j, held in scalar registers for the
 // whole kernel when K is a small compile-time constant.
@@ -112,7 +134,7 @@ __device__ __forceinline__ void fold_free_group(const ConstPtrs& in, int K, int6
 
 // Ring order with K = KS <= 8 known at compile time: all S*KS loads are issued
 // before the first add, then each slice is folded in ring order.
-template <typename TIn, int KS, bool NT, int S>
+template <typename TIn, int KS, bool NT, int S, bool WIRE = false>
 __device__ __forceinline__ void fold_ring_quads_static(const RingBases<TIn, KS>& b, int64_t g0,
                                                        float acc[S][4]) {
     Quad<TIn> v[S][KS];
@@ -125,13 +147,17 @@ __device__ __forceinline__ void fold_ring_quads_static(const RingBases<TIn, KS>&
     for (int k = 0; k < S; ++k) {
         widen4(v[k][0], acc[k]);
 #pragma unroll
-        for (int h = 1; h < KS; ++h) accumulate4(acc[k], v[k][h]);
+        for (int h = 1; h < KS; ++h) {
+            float f[4];
+            widen4(v[k][h], f);
+            hop4<WIRE>(acc[k], f);
+        }
     }
 }
 
 // Ring order for any K: batches of eight ranks, every slice's loads of a batch
 // in flight together, batches folded in ring order one after the other.
-template <typename TIn, int KS, bool NT, int S>
+template <typename TIn, int KS, bool NT, int S, bool WIRE = false>
 __device__ __forceinline__ void fold_ring_quads(const ConstPtrs& in, int K, int j, int64_t g0,
                                                 float acc[S][4]) {
     constexpr int B = 8;
@@ -152,10 +178,13 @@ __device__ __forceinline__ void fold_ring_quads(const ConstPtrs& in, int K, int 
             if (h0 + b < Kr) {
 #pragma unroll
                 for (int k = 0; k < S; ++k) {
-                    if (h0 + b == 0)
+                    if (h0 + b == 0) {
                         widen4(v[k][b], acc[k]);
-                    else
-                        accumulate4(acc[k], v[k][b]);
+                    } else {
+                        float f[4];
+                        widen4(v[k][b], f);
+                        hop4<WIRE>(acc[k], f);
+                    }
                 }
             }
         }
@@ -196,16 +225,18 @@ __device__ __forceinline__ void fold_free_quads(const ConstPtrs& in, int K, int6
 
 // Scalar ring-order fold of one element (index g < N) of chunk j, with the
 // rank pointers read through `ptr(r)` (kernel arguments or an LDS table).
-template <typename TIn, typename PtrFn>
+template <typename TIn, typename PtrFn, bool WIRE = false>
 __device__ __forceinline__ float fold_ring_elem(PtrFn ptr, int K, int j, int64_t g) {
     float acc = load_elem(static_cast<const TIn*>(ptr(j)) + g);
     int r = j;
     for (int h = 1; h < K; ++h) {
         r = wrap(r + 1, K);
         acc = __fadd_rn(acc, load_elem(static_cast<const TIn*>(ptr(r)) + g));
+        if constexpr (WIRE) acc = wire_round(acc);
     }
     return acc;
 }
+
 
 // Scalar free-order fold (ranks in index order).
 template <typename TIn, typename PtrFn>
@@ -213,6 +244,27 @@ __device__ __forceinline__ float fold_free_elem(PtrFn ptr, int K, int64_t g) {
     float acc = load_elem(static_cast<const TIn*>(ptr(0)) + g);
     for (int r = 1; r < K; ++r) acc = __fadd_rn(acc, load_elem(static_cast<const TIn*>(ptr(r)) + g));
     return acc;
+}
+
+// A wave's S quads in the given order; kStatic uses the bases held in scalar
+// registers (ring or wire order, K = KS <= 8).
+template <typename TIn, int KS, bool NT, int S, int ORDER, bool kStatic>
+__device__ __forceinline__ void fold_quads(const RingBases<TIn, kStatic ? KS : 1>& bases,
+                                           const ConstPtrs& in, int K, int j, int64_t g0,
+                                           float acc[S][4]) {
+    if constexpr (ORDER == kFree)
+        fold_free_quads<TIn, KS, NT, S>(in, K, g0, acc);
+    else if constexpr (kStatic)
+        fold_ring_quads_static<TIn, KS, NT, S, ORDER == kWire>(bases, g0, acc);
+    else
+        fold_ring_quads<TIn, KS, NT, S, ORDER == kWire>(in, K, j, g0, acc);
+}
+
+// One element in the given order (ring, free or wire).
+template <typename TIn, int ORDER, typename PtrFn>
+__device__ __forceinline__ float fold_elem(PtrFn ptr, int K, int j, int64_t g) {
+    if constexpr (ORDER == kFree) return fold_free_elem<TIn>(ptr, K, g);
+    return fold_ring_elem<TIn, PtrFn, ORDER == kWire>(ptr, K, j, g);
 }
 
 }  // namespace zr

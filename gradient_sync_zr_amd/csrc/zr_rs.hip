@@ -56,11 +56,11 @@ constexpr int kSlices = sizeof(TIn) == 2 ? ZR_RS_SLICES_BF16 : ZR_RS_SLICES_FP32
 template <typename TIn>
 constexpr int64_t kRsTile = (int64_t)(kThreads / 64) * kSlices<TIn> * 256;
 
-template <typename TIn, typename TOut, int KS, int AVG, bool RING, bool NT>
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT>
 __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
     constexpr int S = kSlices<TIn>;
     constexpr int64_t T = kRsTile<TIn>;
-    constexpr bool kStatic = RING && KS > 0 && KS <= 8;
+    constexpr bool kStatic = ORDER != kFree && KS > 0 && KS <= 8;
     const int K = KS > 0 ? KS : a.K;
     const int j = blockIdx.y;
     const int holder = wrap(j - a.shift + K, K);
@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
         const int64_t g = chunk_base + o;
         float s = 0.0f;
         if (g < N) {
-            s = RING ? fold_ring_elem<TIn>(ptr, K, j, g) : fold_free_elem<TIn>(ptr, K, g);
+            s = fold_elem<TIn, ORDER>(ptr, K, j, g);
             s = average<AVG>(s, a.inv_k, a.kf);
         }
         if (a.accumulate) s = __fadd_rn(load_elem(outp + o), s);
@@ -93,12 +93,7 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
             const int64_t o0 = h + (int64_t)t * T + (int64_t)wave * (S * 256) + lane * 4;
             float acc[S][4];
             const int64_t g0 = chunk_base + o0;
-            if constexpr (kStatic)
-                fold_ring_quads_static<TIn, KS, NT, S>(bases, g0, acc);
-            else if constexpr (RING)
-                fold_ring_quads<TIn, KS, NT, S>(a.in, K, j, g0, acc);
-            else
-                fold_free_quads<TIn, KS, NT, S>(a.in, K, g0, acc);
+            fold_quads<TIn, KS, NT, S, ORDER, kStatic>(bases, a.in, K, j, g0, acc);
 #pragma unroll
             for (int k = 0; k < S; ++k)
 #pragma unroll
@@ -126,44 +121,51 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
     }
 }
 
-template <typename TIn, typename TOut, int KS, int AVG, bool RING, bool NT>
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT>
 hipError_t launch_t(const RsArgs& a, hipStream_t stream) {
     const int cus = device_cu_count();
     int64_t want = (int64_t)cus * tuning().rs_blocks_per_cu / a.K;
     if (want < 1) want = 1;
     const int gx = (int)(want < a.tiles_per_chunk ? want : a.tiles_per_chunk);
-    hipLaunchKernelGGL((rs_kernel<TIn, TOut, KS, AVG, RING, NT>), dim3(gx, a.K), dim3(kThreads), 0,
+    hipLaunchKernelGGL((rs_kernel<TIn, TOut, KS, AVG, ORDER, NT>), dim3(gx, a.K), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
 }
 
-template <typename TIn, typename TOut, int KS, int AVG, bool RING>
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER>
 hipError_t pick_nt(const RsArgs& a, hipStream_t s) {
-    return tuning().nontemporal ? launch_t<TIn, TOut, KS, AVG, RING, true>(a, s)
-                                : launch_t<TIn, TOut, KS, AVG, RING, false>(a, s);
+    return tuning().nontemporal ? launch_t<TIn, TOut, KS, AVG, ORDER, true>(a, s)
+                                : launch_t<TIn, TOut, KS, AVG, ORDER, false>(a, s);
 }
 
+// Orders: the free order has one generic instantiation; ring and wire orders
+// have K = 8 specialised. With fp32 input the wire order is the ring order
+// (rounding every hop to fp32 is what the fp32 adds already do).
 template <typename TIn, typename TOut, int AVG>
-hipError_t pick_k(const RsArgs& a, bool ring, hipStream_t s) {
-    if (!ring) return pick_nt<TIn, TOut, 0, AVG, false>(a, s);
+hipError_t pick_k(const RsArgs& a, int order, hipStream_t s) {
+    if (order == kFree) return pick_nt<TIn, TOut, 0, AVG, kFree>(a, s);
+    if (order == kWire && sizeof(TIn) == 2) {
+        if (a.K == 8) return pick_nt<TIn, TOut, 8, AVG, kWire>(a, s);
+        return pick_nt<TIn, TOut, 0, AVG, kWire>(a, s);
+    }
     switch (a.K) {
-        case 8: return pick_nt<TIn, TOut, 8, AVG, true>(a, s);
-        case 64: return pick_nt<TIn, TOut, 64, AVG, true>(a, s);
-        default: return pick_nt<TIn, TOut, 0, AVG, true>(a, s);
+        case 8: return pick_nt<TIn, TOut, 8, AVG, kRing>(a, s);
+        case 64: return pick_nt<TIn, TOut, 64, AVG, kRing>(a, s);
+        default: return pick_nt<TIn, TOut, 0, AVG, kRing>(a, s);
     }
 }
 
 template <typename TIn, typename TOut>
-hipError_t pick_avg(const RsArgs& a, int avg_mode, bool ring, hipStream_t s) {
+hipError_t pick_avg(const RsArgs& a, int avg_mode, int order, hipStream_t s) {
     switch (avg_mode) {
-        case 1: return pick_k<TIn, TOut, 1>(a, ring, s);
-        case 2: return pick_k<TIn, TOut, 2>(a, ring, s);
-        default: return pick_k<TIn, TOut, 0>(a, ring, s);
+        case 1: return pick_k<TIn, TOut, 1>(a, order, s);
+        case 2: return pick_k<TIn, TOut, 2>(a, order, s);
+        default: return pick_k<TIn, TOut, 0>(a, order, s);
     }
 }
 
 template <typename TIn, typename TOut>
-hipError_t launch_typed(RsArgs& a, int avg_mode, bool ring, hipStream_t s) {
+hipError_t launch_typed(RsArgs& a, int avg_mode, int order, hipStream_t s) {
     constexpr int64_t T = kRsTile<TIn>;
     a.tiles_per_chunk = (int)((a.C + T - 1) / T) + 1;
     // Vector path: every base aligned for quad access (8 bytes for bf16
@@ -187,7 +189,7 @@ hipError_t launch_typed(RsArgs& a, int avg_mode, bool ring, hipStream_t s) {
         a.vec_mask |= 1ull << j;
         a.head[j] = (int16_t)((line - start % line) % line);
     }
-    return pick_avg<TIn, TOut>(a, avg_mode, ring, s);
+    return pick_avg<TIn, TOut>(a, avg_mode, order, s);
 }
 
 }  // namespace
@@ -207,11 +209,11 @@ hipError_t launch_reduce_scatter(int K, const ConstPtrs& in, zr_dtype in_dt, int
     a.accumulate = (flags & ZR_ACCUMULATE) ? 1 : 0;
     const bool pow2 = (K & (K - 1)) == 0;
     const int avg_mode = !(flags & ZR_AVERAGE) ? 0 : (pow2 ? 1 : 2);
-    const bool ring = order == ZR_ORDER_RING;
-    if (in_dt == ZR_BF16 && out_dt == ZR_FP32) return launch_typed<uint16_t, float>(a, avg_mode, ring, stream);
-    if (in_dt == ZR_BF16 && out_dt == ZR_BF16) return launch_typed<uint16_t, uint16_t>(a, avg_mode, ring, stream);
-    if (in_dt == ZR_FP32 && out_dt == ZR_FP32) return launch_typed<float, float>(a, avg_mode, ring, stream);
-    return launch_typed<float, uint16_t>(a, avg_mode, ring, stream);
+    const int ord = order == ZR_ORDER_FREE ? kFree : (order == ZR_ORDER_RING_WIRE ? kWire : kRing);
+    if (in_dt == ZR_BF16 && out_dt == ZR_FP32) return launch_typed<uint16_t, float>(a, avg_mode, ord, stream);
+    if (in_dt == ZR_BF16 && out_dt == ZR_BF16) return launch_typed<uint16_t, uint16_t>(a, avg_mode, ord, stream);
+    if (in_dt == ZR_FP32 && out_dt == ZR_FP32) return launch_typed<float, float>(a, avg_mode, ord, stream);
+    return launch_typed<float, uint16_t>(a, avg_mode, ord, stream);
 }
 
 }  // namespace zr

@@ -74,8 +74,13 @@ typedef enum { ZR_BF16 = 0, ZR_FP32 = 1 } zr_dtype;
 /* ZR_ORDER_RING: the ring order above, bit-exact and deterministic.
  * ZR_ORDER_FREE: ranks summed in an order of the library's choosing (fp32
  * accumulation); the result is within the usual fp32 summation error bound
- * of the exact sum but need not match the ring order bit for bit. */
-typedef enum { ZR_ORDER_RING = 0, ZR_ORDER_FREE = 1 } zr_order;
+ * of the exact sum but need not match the ring order bit for bit.
+ * ZR_ORDER_RING_WIRE: the ring order with each hop's partial sum rounded to
+ * the input dtype before the next hop, as on a ring that carries bf16
+ * partial sums between ranks (the issue page's setup communicates in bf16):
+ * acc = x_j; acc = RNE_bf16(acc + x_{j+1}); ...; bit-exact and deterministic.
+ * For fp32 input it is the same as ZR_ORDER_RING. */
+typedef enum { ZR_ORDER_RING = 0, ZR_ORDER_FREE = 1, ZR_ORDER_RING_WIRE = 2 } zr_order;
 
 /* One tensor of an all-gather: its shard starts at element shard_off of
  * every rank's shard buffer and holds C = ceil(numel / K) elements; the
@@ -195,6 +200,32 @@ zr_status zr_allreduce(int K, const void* const* in, void* const* out, zr_dtype 
  */
 zr_status zr_plan_buckets(int n, const int64_t* numels, int64_t cap, int32_t* bucket_of,
                           int32_t* n_buckets);
+
+/* ------------------------------------------------------------ cost model
+ * alpha-beta model of collective time [L14 3.1, 3.4, 4.4], host only, no
+ * GPU: a message of n bytes costs alpha + n / beta. Times in seconds, sizes
+ * in bytes, alpha in seconds, beta in bytes per second. Invalid arguments
+ * (K < 1, negative size or alpha, beta <= 0) return NaN (-1 for the segment
+ * search).
+ *   ring all-reduce       2(K-1)(alpha + N/(K beta))
+ *   ring reduce-scatter   (K-1)(alpha + N/(K beta))
+ *   tree all-reduce       2 ceil(log2 K)(alpha + N/beta)
+ *   naive all-reduce      2(alpha + (K-1) N/beta)
+ *   pipelined broadcast   (K-2+S)(alpha + N/(S beta)), K >= 2, S >= 1
+ *   dp speedup            t1 / (t1/K + ring all-reduce of the gradients)
+ */
+double zr_cost_ring_allreduce(int K, double bytes, double alpha, double beta);
+double zr_cost_ring_reduce_scatter(int K, double bytes, double alpha, double beta);
+double zr_cost_tree_allreduce(int K, double bytes, double alpha, double beta);
+double zr_cost_naive_allreduce(int K, double bytes, double alpha, double beta);
+double zr_cost_pipelined_broadcast(int K, double bytes, int segments, double alpha, double beta);
+/* Best power-of-two segment count in [1, max_segments]; its time in *time. */
+int zr_cost_best_broadcast_segments(int K, double bytes, double alpha, double beta,
+                                    int max_segments, double* time);
+/* Message sizes (bytes) where ring equals tree / naive all-reduce. */
+double zr_cost_ring_tree_crossover(int K, double alpha, double beta);
+double zr_cost_ring_naive_crossover(int K, double alpha, double beta);
+double zr_cost_dp_speedup(int K, double t1, double grad_bytes, double alpha, double beta);
 
 /* ------------------------------------------------------------- scheduler
  * Bucket/stream scheduler with per-buffer completion events [ISSUE,

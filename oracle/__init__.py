@@ -34,8 +34,8 @@ def _load():
         lib.orc_f32_to_bf16.restype = ctypes.c_uint16
         lib.orc_bf16_to_f32_array.argtypes = [_vp, _vp, _i64]
         lib.orc_f32_to_bf16_array.argtypes = [_vp, _vp, _i64]
-        lib.orc_ring_run.argtypes = [_i32, _i64, _vp, _i32, _i32, _vp]
-        lib.orc_fold_points.argtypes = [_i32, _i64, _vp, _vp, _vp]
+        lib.orc_ring_run.argtypes = [_i32, _i64, _vp, _i32, _i32, _vp, _i32]
+        lib.orc_fold_points.argtypes = [_i32, _i64, _vp, _vp, _vp, _i32]
         lib.orc_exact_sum_points.argtypes = [_i32, _i64, _vp, _vp, _vp]
         lib.orc_reduce_scatter_part.argtypes = [_i32, _i64, _i32, _vp, _i32, _vp, _i32, _i32,
                                                 _i64, _i64]
@@ -91,30 +91,32 @@ def f32_to_bf16(f: np.ndarray) -> np.ndarray:
 
 
 # ------------------------------------------------------------ ring simulator
-def ring_run(x: np.ndarray, n_rs: int, n_ag: int = 0):
+def ring_run(x: np.ndarray, n_rs: int, n_ag: int = 0, wire: bool = False):
     """x: float32 [K, K*C] per-rank inputs. Runs n_rs scatter-reduce rounds and
     then n_ag all-gather rounds of the literal ring. Returns (state [K, K, C],
-    sent [K]) where sent counts the elements each rank put on the wire."""
+    sent [K]) where sent counts the elements each rank put on the wire. With
+    wire=True partial sums are rounded to bf16 as they travel."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     K = x.shape[0]
     assert x.shape[1] % K == 0
     C = x.shape[1] // K
     state = x.reshape(K, K, C).copy()
     sent = np.zeros(K, dtype=np.int64)
-    _check(_load().orc_ring_run(K, C, state.ctypes.data, n_rs, n_ag, sent.ctypes.data),
-           "ring_run")
+    _check(_load().orc_ring_run(K, C, state.ctypes.data, n_rs, n_ag, sent.ctypes.data,
+                                1 if wire else 0), "ring_run")
     return state, sent
 
 
 # -------------------------------------------------------------- direct fold
-def fold_points(xs: np.ndarray, start: np.ndarray) -> np.ndarray:
+def fold_points(xs: np.ndarray, start: np.ndarray, wire: bool = False) -> np.ndarray:
     """xs float32 [K, n]; start int [n] (rank each point's fold starts at)."""
     xs = np.ascontiguousarray(xs, dtype=np.float32)
     K, n = xs.shape
     st = np.ascontiguousarray(start, dtype=np.int32)
     assert st.shape == (n,) and (n == 0 or (st.min() >= 0 and st.max() < K))
     out = np.empty(n, dtype=np.float32)
-    _load().orc_fold_points(K, n, xs.ctypes.data, st.ctypes.data, out.ctypes.data)
+    _load().orc_fold_points(K, n, xs.ctypes.data, st.ctypes.data, out.ctypes.data,
+                            1 if wire else 0)
     return out
 
 
@@ -128,7 +130,7 @@ def exact_sum_points(xs: np.ndarray):
 
 
 def reduce_scatter(inputs, N, out_dtype, shift=1, average=True, o_range=None, out=None,
-                   accumulate=False):
+                   accumulate=False, wire=False):
     """inputs: list of K arrays (uint16 bf16 or float32) of >= N elements.
     Returns (or fills) K arrays of C = ceil(N/K) elements of out_dtype. With
     accumulate=True, `out` holds the previous partitions and is added into."""
@@ -143,7 +145,7 @@ def reduce_scatter(inputs, N, out_dtype, shift=1, average=True, o_range=None, ou
         out = [np.empty(C, dtype=out_dtype) for _ in range(K)]
     out_dt = _dt(out[0])
     lo, hi = (0, C) if o_range is None else o_range
-    flags = (1 if average else 0) | (2 if accumulate else 0)
+    flags = (1 if average else 0) | (2 if accumulate else 0) | (4 if wire else 0)
     rc = _load().orc_reduce_scatter_part(K, N, in_dt, _ptrs(ins), out_dt, _ptrs(out), shift,
                                          flags, lo, hi)
     _check(rc, "reduce_scatter")
@@ -161,13 +163,14 @@ def all_gather(shards, fulls, segs, shift):
     return fulls
 
 
-def allreduce(inputs, N, average=False, out=None):
+def allreduce(inputs, N, average=False, out=None, wire=False):
     K = len(inputs)
     ins = [np.ascontiguousarray(a) for a in inputs]
     dt = _dt(ins[0])
     if out is None:
         out = [np.empty(N, dtype=ins[0].dtype) for _ in range(K)]
-    rc = _load().orc_allreduce(K, N, dt, _ptrs(ins), _ptrs(out), 1 if average else 0)
+    rc = _load().orc_allreduce(K, N, dt, _ptrs(ins), _ptrs(out),
+                               (1 if average else 0) | (4 if wire else 0))
     _check(rc, "allreduce")
     return out
 

@@ -110,9 +110,11 @@ static int mod(int64_t a, int K) {
  * All sends of a round are collected before any receive is applied, as in a
  * real synchronous round. `sent[r]` accumulates the elements rank r sent.
  * Runs the first n_rs scatter-reduce rounds, then (only if n_rs == K-1) the
- * first n_ag all-gather rounds. Returns 0, or -1 on bad arguments.
+ * first n_ag all-gather rounds. With wire != 0 the ring carries bf16: the
+ * receiver's new partial sum is rounded to bf16 before it is kept (and sent
+ * on in the next round). Returns 0, or -1 on bad arguments.
  */
-int orc_ring_run(int K, int64_t C, float* state, int n_rs, int n_ag, int64_t* sent) {
+int orc_ring_run(int K, int64_t C, float* state, int n_rs, int n_ag, int64_t* sent, int wire) {
     if (K < 1 || C < 0 || n_rs < 0 || n_rs > K - 1 || n_ag < 0 || n_ag > K - 1) return -1;
     if (n_ag > 0 && n_rs != K - 1) return -1;
     float* msg = (float*)malloc(sizeof(float) * (size_t)(K * (C > 0 ? C : 1)));
@@ -136,10 +138,12 @@ int orc_ring_run(int K, int64_t C, float* state, int n_rs, int n_ag, int64_t* se
                 float* dst = state + ((int64_t)r * K + c) * C;
                 const float* m = msg + (int64_t)from * C;
                 for (int64_t o = 0; o < C; ++o) {
-                    if (phase == 0)
+                    if (phase == 0) {
                         dst[o] = dst[o] + m[o];
-                    else
+                        if (wire) dst[o] = orc_bf16_to_f32(orc_f32_to_bf16(dst[o]));
+                    } else {
                         dst[o] = m[o];
+                    }
                 }
             }
         }
@@ -152,13 +156,19 @@ int orc_ring_run(int K, int64_t C, float* state, int n_rs, int n_ag, int64_t* se
 /* ------------------------------------------------------------ direct fold
  * Ring-order fold at explicit points. xs holds K rows of n values (row r =
  * rank r); point p starts with rank start[p] and adds the others in ring
- * order: acc = x[s], acc = acc + x[s+1], ..., acc = acc + x[s-1].
+ * order: acc = x[s], acc = acc + x[s+1], ..., acc = acc + x[s-1]. With
+ * wire != 0 every partial sum is rounded to bf16 (a ring that carries bf16).
  */
-void orc_fold_points(int K, int64_t n, const float* xs, const int32_t* start, float* out) {
+static float hop(float acc, float x, int wire) {
+    acc = acc + x;
+    return wire ? orc_bf16_to_f32(orc_f32_to_bf16(acc)) : acc;
+}
+
+void orc_fold_points(int K, int64_t n, const float* xs, const int32_t* start, float* out, int wire) {
     for (int64_t p = 0; p < n; ++p) {
         int s = start[p];
         float acc = xs[(int64_t)s * n + p];
-        for (int h = 1; h < K; ++h) acc = acc + xs[(int64_t)((s + h) % K) * n + p];
+        for (int h = 1; h < K; ++h) acc = hop(acc, xs[(int64_t)((s + h) % K) * n + p], wire);
         out[p] = acc;
     }
 }
@@ -187,13 +197,16 @@ void orc_exact_sum_points(int K, int64_t n, const float* xs, double* out, double
  *   out_q[o] = A, or, if (flags & 2), the value already in out_q[o] plus A
  *   in one fp32 add (gradient accumulation: the first micro-step copies,
  *   later ones add in place [ZERO3 5.3, 6]),
- * stored as fp32 or rounded to bf16.
+ * stored as fp32 or rounded to bf16. With (flags & 4) the fold rounds every
+ * partial sum to bf16 (a ring carrying bf16 partial sums); for fp32 input
+ * this has no effect on the meaning of "the ring", so it is applied only to
+ * bf16 input.
  */
 int orc_reduce_scatter_part(int K, int64_t N, int in_dt, const void* const* in, int out_dt,
                             void* const* out, int shift, int flags, int64_t o_lo,
                             int64_t o_hi) {
-    if (K < 1 || N < 0 || shift < 0 || shift >= K || (flags & ~3)) return -1;
-    int average = flags & 1, accumulate = flags & 2;
+    if (K < 1 || N < 0 || shift < 0 || shift >= K || (flags & ~7)) return -1;
+    int average = flags & 1, accumulate = flags & 2, wire = (flags & 4) && in_dt == ORC_BF16;
     int64_t C = chunk_of(N, K);
     if (o_lo < 0 || o_hi > C || o_lo > o_hi) return -1;
     for (int q = 0; q < K; ++q) {
@@ -203,7 +216,7 @@ int orc_reduce_scatter_part(int K, int64_t N, int in_dt, const void* const* in, 
             float acc = 0.0f;
             if (g < N) {
                 acc = load_elem(in[j], in_dt, g);
-                for (int h = 1; h < K; ++h) acc = acc + load_elem(in[(j + h) % K], in_dt, g);
+                for (int h = 1; h < K; ++h) acc = hop(acc, load_elem(in[(j + h) % K], in_dt, g), wire);
                 if (average) acc = acc / (float)K;
             }
             if (accumulate) acc = load_elem(out[q], out_dt, o) + acc;
@@ -247,11 +260,11 @@ int orc_all_gather(int K, int dt, const void* const* shards, void* const* fulls,
 
 /* ---------------------------------------------------------------- all-reduce
  * All-reduce = reduce-scatter followed by all-gather [L14 2.2]: each chunk
- * is folded in ring order, divided by K when averaging, stored in the output
- * dtype once, and every rank receives the same stored value.
- * in and out may be the same buffers.
+ * is folded in ring order, divided by K when averaging (flags & 1), stored in
+ * the output dtype once, and every rank receives the same stored value.
+ * (flags & 4) selects the bf16-wire fold. in and out may be the same buffers.
  */
-int orc_allreduce(int K, int64_t N, int dt, const void* const* in, void* const* out, int average) {
+int orc_allreduce(int K, int64_t N, int dt, const void* const* in, void* const* out, int flags) {
     if (K < 1 || N < 0) return -1;
     int64_t C = chunk_of(N, K);
     size_t es = dt == ORC_BF16 ? 2 : 4;
@@ -261,7 +274,7 @@ int orc_allreduce(int K, int64_t N, int dt, const void* const* in, void* const* 
     for (int q = 0; q < K; ++q) shards[q] = shard_mem + (size_t)q * es * (size_t)C;
     /* ring placement: rank q holds chunk (q + 1) mod K, a shift of 1 mod K */
     int shift = 1 % K;
-    int rc = orc_reduce_scatter(K, N, dt, in, dt, shards, shift, average ? 1 : 0);
+    int rc = orc_reduce_scatter(K, N, dt, in, dt, shards, shift, flags & 5);
     if (rc == 0) {
         int64_t seg[3] = {0, 0, N};
         rc = orc_all_gather(K, dt, (const void* const*)shards, out, seg, 1, shift);

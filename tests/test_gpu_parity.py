@@ -120,6 +120,59 @@ def test_reduce_scatter_accumulate_bit_exact(K, N, in_bf16, out_bf16, shift, ave
         assert outs[r].guards_intact()
 
 
+WIRE_CASES = [
+    # K, N, out_bf16, shift, average, offset
+    (8, 8 * 4096 * 3 + 8 * 40, False, 1, True, 0),
+    (8, 100003, True, 1, False, 0),
+    (8, 65536 + 5, False, 0, True, 1),          # element-wise path
+    (5, 77777, False, 2, True, 0),
+    (64, 64 * 4096 + 3, True, 1, False, 0),
+]
+
+
+@pytest.mark.parametrize("K,N,out_bf16,shift,average,offset", WIRE_CASES)
+def test_reduce_scatter_bf16_wire_bit_exact(K, N, out_bf16, shift, average, offset):
+    import torch
+    xs = make_inputs(K, N, True, 4242 + K + N)
+    C = -(-N // K)
+    ins = [Guarded(N, torch.bfloat16, offset, xs[r]) for r in range(K)]
+    outs = [Guarded(C, torch_dt(out_bf16), offset) for _ in range(K)]
+    zr().zr_reduce_scatter_avg([g.ptr() for g in ins], N, [g.ptr() for g in outs],
+                               chunk_shift=shift, average=average, order=zr().ZR_ORDER_RING_WIRE,
+                               in_dtype=torch.bfloat16, out_dtype=torch_dt(out_bf16))
+    torch.cuda.synchronize()
+    want = oracle.reduce_scatter(xs, N, np.uint16 if out_bf16 else np.float32, shift=shift,
+                                 average=average, wire=True)
+    ring = oracle.reduce_scatter(xs, N, np.uint16 if out_bf16 else np.float32, shift=shift,
+                                 average=average)
+    differs = False
+    for r in range(K):
+        got = outs[r].get()
+        assert np.array_equal(bits(got), bits(want[r])), f"rank {r}"
+        differs |= not np.array_equal(bits(got), bits(ring[r]))
+        assert outs[r].guards_intact()
+    assert differs  # per-hop rounding shows on these inputs
+
+
+@pytest.mark.parametrize("K,N,fused,average", [(8, 8 * 4096 * 2 + 77, True, False),
+                                               (8, 8 * 4096 * 2 + 77, False, True),
+                                               (64, 64 * 4096 + 9, True, False),
+                                               (3, 30001, True, True)])
+def test_allreduce_bf16_wire_bit_exact(K, N, fused, average):
+    import torch
+    xs = make_inputs(K, N, True, 5151 + K + N)
+    ins = [Guarded(N, torch.bfloat16, 0, xs[r]) for r in range(K)]
+    C = -(-N // K)
+    scratch = None if fused else Guarded(K * C, torch.bfloat16, 0)
+    zr().zr_allreduce([g.ptr() for g in ins], [g.ptr() for g in ins], N, average=average,
+                      order=zr().ZR_ORDER_RING_WIRE, fused=fused,
+                      scratch=None if scratch is None else scratch.ptr(), dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    want = oracle.allreduce(xs, N, average=average, wire=True)
+    for r in range(K):
+        assert np.array_equal(ins[r].get(), want[r]), f"rank {r}"
+
+
 @pytest.mark.parametrize("K,N,in_bf16,out_bf16,average", [
     (8, 100003, True, False, True), (64, 70001, True, True, False), (5, 30000, False, False, True),
     (16, 16 * 2048 * 2, True, False, True)])

@@ -493,3 +493,58 @@ def test_accumulate_into_zero_equals_plain():
         # +0 + v == v for every v except -0 (which becomes +0)
         same = (plain[q] == acc[q]) & ~((plain[q] == 0) & np.signbit(plain[q]))
         assert np.all(same | ((plain[q] == 0) & (acc[q] == 0)))
+
+
+# ------------------------------------------------------- bf16 wire order
+def bf16_random(shape, rng):
+    return oracle.bf16_to_f32(oracle.f32_to_bf16(wide_random(shape, rng)))
+
+
+@pytest.mark.parametrize("K", [2, 3, 4, 7, 8, 16])
+def test_wire_fold_equals_literal_bf16_ring(K):
+    # a ring that carries bf16: each receiver adds in fp32 and keeps (and
+    # forwards) the bf16 rounding of the new partial sum
+    rng = np.random.default_rng(300 + K)
+    C = 29
+    x = bf16_random((K, K * C), rng)
+    state, _ = oracle.ring_run(x, K - 1, 0, wire=True)
+    for j in range(K):
+        got = oracle.fold_points(x[:, j * C:(j + 1) * C], np.full(C, j), wire=True)
+        assert np.array_equal(got.view(np.uint32), state[(j - 1) % K, j].view(np.uint32))
+        # every partial that travels is a bf16 value, so the result is one too
+        assert np.array_equal(got, oracle.bf16_to_f32(oracle.f32_to_bf16(got)))
+    # and the all-gather phase hands everyone the same bf16 sums
+    full, _ = oracle.ring_run(x, K - 1, K - 1, wire=True)
+    ar = oracle.allreduce([oracle.f32_to_bf16(x[r]) for r in range(K)], K * C, wire=True)
+    for r in range(K):
+        assert np.array_equal(oracle.bf16_to_f32(ar[r]), full[r].reshape(-1))
+
+
+def test_wire_order_handworked_ties():
+    """Ranks 0..3 hold (1, d, d, d) with d = 2^-8 (bf16 keeps 8 significant bits).
+    bf16 wire, by start rank (ties go to the even significand):
+      start 0: 1+d ties to 1, again 1, again 1                      -> 1
+      start 1: d+d = 2d, +d = 3d (exact), +1 = 1+3d ties to 1+4d   -> 1.015625
+      start 2: d+d = 2d, +1 = 1+2d (exact), +d = 1+3d -> 1+4d      -> 1.015625
+      start 3: d+1 ties to 1, +d -> 1, +d -> 1                      -> 1
+    With fp32 accumulation every start gives 1+3d, rounded once to bf16: 1+4d."""
+    d = 2.0 ** -8
+    K, C = 4, 3
+    vals = (1.0, d, d, d)
+    ins = [oracle.f32_to_bf16(np.full(K * C, v, dtype=np.float32)) for v in vals]
+    wire = oracle.reduce_scatter(ins, K * C, np.float32, shift=1, average=False, wire=True)
+    ring = oracle.reduce_scatter(ins, K * C, np.uint16, shift=1, average=False)
+    want_wire = (1.0, 1.015625, 1.015625, 1.0)
+    for j in range(K):
+        assert np.all(wire[(j - 1) % K] == np.float32(want_wire[j])), j
+        assert np.all(oracle.bf16_to_f32(ring[(j - 1) % K]) == np.float32(1.015625))
+
+
+def test_wire_flag_has_no_effect_on_fp32_input():
+    rng = np.random.default_rng(8)
+    K, N = 8, 8 * 21
+    xs = [wide_random(N, rng) for _ in range(K)]
+    a = oracle.reduce_scatter(xs, N, np.float32, shift=1, average=True)
+    b = oracle.reduce_scatter(xs, N, np.float32, shift=1, average=True, wire=True)
+    for q in range(K):
+        assert np.array_equal(a[q].view(np.uint32), b[q].view(np.uint32))
