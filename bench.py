@@ -319,6 +319,75 @@ def bench_allreduce64(args):
     }
 
 
+# ------------------------------------------------------------ frags_layer
+def bench_frags_layer(args):
+    """Discrete path at bandwidth scale: the seven gradients of one transformer
+    layer (q, k, v, o: 4096x4096; gate, up, down: 4096x11008) per rank, reduced
+    straight from the fragments, against flatten-into-a-bucket + reduce-scatter."""
+    import torch
+
+    import synth
+    import gradient_sync_zr_amd as zr
+    from synth import workloads as W
+
+    K = 8
+    sizes = [p.numel for p in W.llama_like_params(layers=1)[1:8]]
+    N = sum(sizes)          # 202,375,168: a multiple of 8
+    seed = W.seed_of(3)
+    frags = [[torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in sizes] for _ in range(K)]
+    for r in range(K):
+        for p in range(len(sizes)):
+            synth.dev_normal_bf16(frags[r][p], seed, 1000 + r * 8 + p, 0, 1e-3)
+    buckets = [torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    parts = [torch.empty(N // K, dtype=torch.float32, device="cuda") for _ in range(K)]
+    fp = [[t.data_ptr() for t in row] for row in frags]
+    bp = [t.data_ptr() for t in buckets]
+    pp = [t.data_ptr() for t in parts]
+
+    def discrete():
+        zr.zr_reduce_scatter_frags(fp, sizes, N, pp, chunk_shift=1, average=True,
+                                   in_dtype=torch.bfloat16, out_dtype=torch.float32)
+
+    def flat_rs():
+        zr.zr_flatten_bucket(fp, sizes, bp, N, dtype=torch.bfloat16)
+        zr.zr_reduce_scatter_avg(bp, N, pp, chunk_shift=1, average=True, in_dtype=torch.bfloat16,
+                                 out_dtype=torch.float32)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_flat = timed(flat_rs)
+    ms = timed(discrete)
+    step_bytes = N * (2 * K + 4)
+    value = step_bytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": "discrete reduce-scatter+avg+cast GB/s from 7 fragments per rank, K=8",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic: seeded generator, bf16 ~N(0,1e-3)",
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "flatten_then_rs_ms": round(ms_flat, 4),
+        "speedup_over_flatten_then_rs": round(ms_flat / ms, 3),
+        "config": {"workload": "frags_layer: K=8, one transformer layer's 7 gradients per rank "
+                               f"({N} elements), bucket never materialised",
+                   "K": K, "N": N, "bytes_per_step": step_bytes},
+        "roofline": {"bound": "hbm", "kernel": "rsf_kernel<bf16,f32,avg,ring>", "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "achieved": round(value, 1),
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+
+
 # -------------------------------------------------------------- flatten8
 def bench_flatten8(args):
     import torch
@@ -346,20 +415,29 @@ def bench_flatten8(args):
         zr.zr_reduce_scatter_avg(bp, P, pp, chunk_shift=1, average=True, in_dtype=torch.bfloat16,
                                  out_dtype=torch.float32)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    us = (time.perf_counter() - t0) * 1e6 / args.steps
+    def step_discrete():
+        zr.zr_reduce_scatter_frags(fp, sizes, P, pp, chunk_shift=1, average=True,
+                                   in_dtype=torch.bfloat16, out_dtype=torch.float32)
+
+    def wall_us(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / args.steps
+
+    us = wall_us(step)
+    us_discrete = wall_us(step_discrete)
     return {
         "metric": "flatten + reduce-scatter-avg microseconds per bucket, K=8, 64 fragments",
         "value": round(us, 2), "unit": "us", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic: seeded generator, bf16 ~N(0,1e-3)",
+        "discrete_path_us": round(us_discrete, 2),
         "config": {"workload": f"flatten8: K=8, 64 log-uniform fragments ({sum(sizes)} elements), "
                                f"bucket padded to {P}, then RS + /8 + fp32 cast (cache-resident, "
                                "launch-bound)", "K": K},
@@ -373,7 +451,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="zero2",
-                    choices=["zero2", "zero2_accum", "zero3_ag", "allreduce64", "flatten8"])
+                    choices=["zero2", "zero2_accum", "zero3_ag", "allreduce64", "flatten8",
+                             "frags_layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-elems", type=int, default=0,
                     help="element indices in the CPU-baseline sample (default: all of bucket 0)")
@@ -389,7 +468,7 @@ def main():
     torch.cuda.set_device(0)
     fn = {"zero2": bench_zero2, "zero2_accum": lambda a: bench_zero2(a, accumulate=True),
           "zero3_ag": bench_zero3, "allreduce64": bench_allreduce64,
-          "flatten8": bench_flatten8}[args.workload]
+          "flatten8": bench_flatten8, "frags_layer": bench_frags_layer}[args.workload]
     print(json.dumps(fn(args)), flush=True)
 
 

@@ -32,7 +32,7 @@ COST_EXPORTS = ("zr_cost_ring_allreduce", "zr_cost_ring_reduce_scatter", "zr_cos
                 "zr_cost_best_broadcast_segments", "zr_cost_ring_tree_crossover",
                 "zr_cost_ring_naive_crossover", "zr_cost_dp_speedup")
 EXPORTS = ("zr_last_error", "zr_version", "zr_flatten_bucket", "zr_reduce_scatter_avg",
-           "zr_all_gather", "zr_allreduce", "zr_plan_buckets", "zr_sched_create",
+           "zr_reduce_scatter_frags", "zr_all_gather", "zr_allreduce", "zr_plan_buckets", "zr_sched_create",
            "zr_sched_acquire", "zr_sched_submit_rs", "zr_sched_flush",
            "zr_sched_destroy") + COST_EXPORTS
 
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.zr_flatten_bucket.argtypes = [_i32, _i32, _PP, ctypes.POINTER(_i64), _PP, _i64, _i32, _vp]
         L.zr_reduce_scatter_avg.argtypes = [_i32, _PP, _i32, _i64, _PP, _i32, _i32, _i32, _i32, _vp]
         L.zr_all_gather.argtypes = [_i32, _PP, _PP, _i32, ctypes.POINTER(zr_seg), _i32, _i32, _vp]
+        L.zr_reduce_scatter_frags.argtypes = [_i32, _i32, _PP, ctypes.POINTER(_i64), _i64, _i32, _PP,
+                                              _i32, _i32, _i32, _i32, _vp]
         L.zr_allreduce.argtypes = [_i32, _PP, _PP, _i32, _i64, _i32, _i32, _i32, _vp, _vp]
         L.zr_plan_buckets.argtypes = [_i32, ctypes.POINTER(_i64), _i64, ctypes.POINTER(ctypes.c_int32),
                                       ctypes.POINTER(ctypes.c_int32)]
@@ -175,6 +177,24 @@ def zr_reduce_scatter_avg(inputs: Sequence, N: int, outputs: Sequence, chunk_shi
     _check(lib().zr_reduce_scatter_avg(K, _table(inputs), in_dt, N, _table(outputs), out_dt,
                                        chunk_shift, _flags(average, accumulate), order,
                                        _stream(stream)))
+
+
+def zr_reduce_scatter_frags(frags: Sequence[Sequence], numels: Sequence[int], N: int,
+                            outputs: Sequence, chunk_shift: int = 1, average: bool = True,
+                            order: int = ZR_ORDER_RING, in_dtype=None, out_dtype=None,
+                            stream=None, accumulate: bool = False) -> None:
+    """frags[r][p] = fragment p of rank r (same numels on every rank)."""
+    K = len(outputs)
+    F = len(numels)
+    flat = [f for row in frags for f in row]
+    if len(flat) != K * F:
+        raise ValueError("frags must be K lists of len(numels) tensors")
+    in_dt = _dtype(in_dtype if in_dtype is not None else flat[0])
+    out_dt = _dtype(out_dtype if out_dtype is not None else outputs[0])
+    nums = (ctypes.c_int64 * max(1, F))(*numels)
+    _check(lib().zr_reduce_scatter_frags(K, F, _table(flat), nums, N, in_dt, _table(outputs),
+                                         out_dt, chunk_shift, _flags(average, accumulate), order,
+                                         _stream(stream)))
 
 
 def zr_all_gather(shards: Sequence, fulls: Sequence, segs: Sequence, chunk_shift: int = 0,

@@ -23,7 +23,7 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
-SOURCES = ["zr_rs.hip", "zr_ar.hip", "zr_ag.hip", "zr_flatten.hip", "zr_abi.cpp", "zr_sched.cpp",
+SOURCES = ["zr_rs.hip", "zr_rsf.hip", "zr_ar.hip", "zr_ag.hip", "zr_flatten.hip", "zr_abi.cpp", "zr_sched.cpp",
            "zr_cost.cpp"]
 
 

@@ -356,6 +356,75 @@ zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const i
     return ok();
 }
 
+zr_status zr_reduce_scatter_frags(int K, int n_frag, const void* const* frags,
+                                  const int64_t* numels, int64_t N, zr_dtype in_dt,
+                                  void* const* out, zr_dtype out_dt, int chunk_shift, int flags,
+                                  zr_order order, void* stream) {
+    ZR_TRY(check_k(K));
+    if (n_frag < 0) return fail(ZR_ERR_INVALID, "n_frag=%d is negative", n_frag);
+    if (N < 0) return fail(ZR_ERR_INVALID, "N=%lld is negative", (long long)N);
+    if (!dt_valid(in_dt) || !dt_valid(out_dt))
+        return fail(ZR_ERR_UNSUPPORTED, "dtype pair (%d, %d) not supported", (int)in_dt, (int)out_dt);
+    if (chunk_shift < 0 || chunk_shift >= K)
+        return fail(ZR_ERR_INVALID, "chunk_shift=%d not in [0, %d)", chunk_shift, K);
+    if (flags & ~(ZR_AVERAGE | ZR_ACCUMULATE)) return fail(ZR_ERR_INVALID, "flags=%d has unknown bits", flags);
+    if (order != ZR_ORDER_RING && order != ZR_ORDER_FREE && order != ZR_ORDER_RING_WIRE)
+        return fail(ZR_ERR_INVALID, "order=%d is not a zr_order", (int)order);
+    if (n_frag > 0 && (!frags || !numels)) return fail(ZR_ERR_INVALID, "frags or numels is NULL");
+    int64_t total = 0;
+    for (int p = 0; p < n_frag; ++p) {
+        if (numels[p] < 0) return fail(ZR_ERR_INVALID, "numels[%d] is negative", p);
+        total += numels[p];
+    }
+    if (N < total)
+        return fail(ZR_ERR_INVALID, "N=%lld < total fragment size %lld", (long long)N, (long long)total);
+    if (N == 0) return ok();
+    if (N > kMaxElems) return fail(ZR_ERR_INVALID, "N=%lld too large", (long long)N);
+    const int64_t ies = dt_bytes(in_dt), oes = dt_bytes(out_dt);
+    const int64_t C = (N + K - 1) / K;
+    ZR_TRY(check_table(const_cast<const void* const*>(out), K, oes, "out"));
+    std::vector<Range> ro(K), rf;
+    for (int r = 0; r < K; ++r) ro[r] = range_of(out[r], C, oes);
+    ZR_TRY(check_distinct(ro, "out"));
+    for (int r = 0; r < K; ++r)
+        for (int p = 0; p < n_frag; ++p) {
+            if (numels[p] == 0) continue;
+            const void* f = frags[(size_t)r * n_frag + p];
+            if (!f) return fail(ZR_ERR_INVALID, "fragment %d of rank %d is NULL", p, r);
+            if (((uintptr_t)f) % (uintptr_t)ies)
+                return fail(ZR_ERR_ALIGN, "fragment %d of rank %d is not aligned", p, r);
+            rf.push_back(range_of(f, numels[p], ies));
+        }
+    ZR_TRY(check_disjoint(ro, "out", rf, "fragment"));
+    std::vector<FragEntry> entries;
+    entries.reserve((size_t)n_frag + 1);
+    int64_t off = 0;
+    for (int p = 0; p < n_frag; ++p) {
+        if (numels[p] > 0) {
+            FragEntry e{};
+            for (int r = 0; r < K; ++r) e.ptr[r] = frags[(size_t)r * n_frag + p];
+            e.off = off;
+            e.n = numels[p];
+            entries.push_back(e);
+        }
+        off += numels[p];
+    }
+    // the zero padding: null pointers, up to the end of the last chunk (K*C),
+    // where the contiguous reduce-scatter also writes +0 past N
+    if (K * C > off) {
+        FragEntry e{};
+        e.off = off;
+        e.n = K * C - off;
+        entries.push_back(e);
+    }
+    MutPtrs op{};
+    for (int r = 0; r < K; ++r) op.p[r] = out[r];
+    hipError_t e = launch_reduce_scatter_frags(K, entries.data(), (int)entries.size(), N, in_dt, op,
+                                               out_dt, chunk_shift, flags, order, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "discrete reduce-scatter launch");
+    return ok();
+}
+
 zr_status zr_plan_buckets(int n, const int64_t* numels, int64_t cap, int32_t* bucket_of,
                           int32_t* n_buckets) {
     if (n < 0) return fail(ZR_ERR_INVALID, "n=%d is negative", n);

@@ -12,6 +12,8 @@ namespace zr {
 constexpr int kMaxRanks = ZR_MAX_RANKS;
 constexpr int kAgSegsPerLaunch = 32;   // segments carried in one all-gather launch
 constexpr int kFlatJobsPerLaunch = 96; // copy jobs carried in one flatten launch
+constexpr int kRsfPtrsPerLaunch = 320;   // rank pointers of fragments in one discrete-RS launch
+constexpr int kRsfEntriesPerLaunch = 40; // fragments in one discrete-RS launch
 
 // Rank pointer tables travel by value in kernel arguments (K <= 64 -> 512 B).
 struct ConstPtrs {
@@ -27,6 +29,14 @@ struct CopyJob {
     const void* src;
     void* dst;
     int64_t n;
+};
+
+// One fragment of the discrete reduce-scatter: its K rank pointers (all null
+// for the zero padding after the last fragment), its offset in the virtual
+// bucket, and its size.
+struct FragEntry {
+    const void* ptr[kMaxRanks];
+    int64_t off, n;
 };
 
 // Launch-shape knobs, read once from the environment (for tuning sweeps);
@@ -53,6 +63,11 @@ hipError_t launch_allreduce_fused(int K, const ConstPtrs& in, const MutPtrs& out
 // segs: up to kAgSegsPerLaunch segments per call.
 hipError_t launch_all_gather(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype dt,
                              const zr_seg* segs, int n_segs, int shift, hipStream_t stream);
+
+// Discrete reduce-scatter over fragment entries (any count; batched inside).
+hipError_t launch_reduce_scatter_frags(int K, const FragEntry* entries, int n_entries, int64_t N,
+                                       zr_dtype in_dt, const MutPtrs& out, zr_dtype out_dt,
+                                       int shift, int flags, zr_order order, hipStream_t stream);
 
 // jobs: up to kFlatJobsPerLaunch per call.
 hipError_t launch_flatten(const CopyJob* jobs, int n_jobs, int elem_bytes, hipStream_t stream);

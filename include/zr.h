@@ -154,6 +154,27 @@ zr_status zr_reduce_scatter_avg(int K, const void* const* in, zr_dtype in_dt, in
                                 void* stream);
 
 /*
+ * Reduce-scatter straight from fragmented gradients, the discrete path
+ * [ZERO3 5.2 (discrete path), 3.2]: bit for bit the result of
+ * zr_flatten_bucket(K, n_frag, frags, numels, buckets, N) followed by
+ * zr_reduce_scatter_avg(K, buckets, in_dt, N, out, ...), without writing the
+ * bucket: every fragment element is read once where it lies.
+ *
+ *  frags     host array [K * n_frag] of device pointers, rank-major as in
+ *            zr_flatten_bucket (NULL only where numels[p] == 0)
+ *  numels    host array [n_frag]; N >= sum(numels); positions past the last
+ *            fragment are zero padding
+ *  out, flags, order, chunk_shift: as zr_reduce_scatter_avg
+ * Outputs must be distinct and must not overlap any fragment (ZR_ERR_ALIAS).
+ * Fragment tables travel in kernel arguments, 40 fragments per launch at
+ * K <= 8 (320 rank pointers per launch).
+ */
+zr_status zr_reduce_scatter_frags(int K, int n_frag, const void* const* frags,
+                                  const int64_t* numels, int64_t N, zr_dtype in_dt,
+                                  void* const* out, zr_dtype out_dt, int chunk_shift, int flags,
+                                  zr_order order, void* stream);
+
+/*
  * All-gather of sharded tensors into full tensors [RING Phase 2; L14 3.2;
  * ZERO3 1, 2.1]. For each segment and every destination rank r:
  *     full_r[full_off + j*C + o] = shard_{(j - chunk_shift) mod K}[shard_off + o]

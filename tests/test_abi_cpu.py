@@ -169,6 +169,36 @@ def test_flatten_validation():
     assert call([1, 2, 3], 8, frags=frags) == zr.ZR_ERR_INVALID
 
 
+def test_reduce_scatter_frags_validation():
+    lib = zr.lib()
+    K, F = 2, 3
+
+    def call(numels, N, frags=None, outs=None, flags=1, shift=1, order=0, in_dt=0, out_dt=1):
+        fr = (ctypes.c_void_p * (K * F))(*(frags or ranks(K * F)))
+        nm = (ctypes.c_int64 * F)(*numels)
+        o = (ctypes.c_void_p * K)(*(outs or ranks(K, base=A + (1 << 40))))
+        return lib.zr_reduce_scatter_frags(K, F, fr, nm, N, in_dt, o, out_dt, shift, flags, order,
+                                           None)
+
+    assert call([0, 0, 0], 0) == zr.ZR_OK
+    assert call([1, 2, 3], 0) == zr.ZR_ERR_INVALID            # N < total
+    assert call([1, 2, 3], 5) == zr.ZR_ERR_INVALID
+    assert call([1, -2, 3], 8) == zr.ZR_ERR_INVALID
+    assert call([1, 2, 3], 8, flags=4) == zr.ZR_ERR_INVALID
+    assert call([1, 2, 3], 8, shift=2) == zr.ZR_ERR_INVALID
+    assert call([1, 2, 3], 8, order=3) == zr.ZR_ERR_INVALID
+    assert call([1, 2, 3], 8, in_dt=5) == zr.ZR_ERR_UNSUPPORTED
+    frags = ranks(K * F)
+    frags[2] = A + (1 << 40) + 8                              # fragment inside out[0]
+    assert call([1, 2, 3], 8, frags=frags) == zr.ZR_ERR_ALIAS
+    frags = ranks(K * F)
+    frags[4] = 0
+    assert call([1, 2, 3], 8, frags=frags) == zr.ZR_ERR_INVALID
+    frags[4] = A + 1                                           # odd bf16 address
+    assert call([1, 2, 3], 8, frags=frags) == zr.ZR_ERR_ALIGN
+    assert call([1, 2, 3], 8, outs=[A + (1 << 40)] * 2) == zr.ZR_ERR_ALIAS
+
+
 def greedy_reference(numels, cap):
     """The prefetch loop of the ZeRO-3 parameter coordinator as the page
     describes it (DeepSpeed ZeRO-3 源码解析, 2.1 step 3 and 2.2): keep taking

@@ -361,6 +361,109 @@ def test_flatten_bit_exact(K, sizes, bf16, offset, extra):
         assert buckets[r].guards_intact()
 
 
+FRAG_CASES = [
+    # K, sizes (None = the 64 log-uniform fragments), extra padding, in_bf16, out_bf16,
+    # shift, average, order, offset, accumulate
+    (8, None, None, True, False, 1, True, 0, 0, False),
+    (8, [5, 0, 1, 2049, 7, 4096 * 3, 33, 64], 11, True, False, 1, True, 0, 0, False),
+    (8, [4096, 8192, 16, 24], 0, True, True, 0, False, 0, 0, False),
+    (8, [1000, 3, 5, 100000], 3, True, False, 1, True, 0, 1, False),   # misaligned fragments
+    (5, [77, 7777, 1], 4, False, False, 2, True, 0, 0, False),
+    (64, [100, 1, 4096 * 5 + 3, 64 * 7], 64 * 3, True, False, 1, True, 0, 0, False),
+    (8, [30001, 40000], 7, True, False, 1, True, 2, 0, False),        # bf16 wire order
+    (16, [30001, 40000], 0, True, False, 1, True, 1, 0, False),       # free order
+    (8, [30001, 40000, 9], 0, True, False, 1, True, 0, 0, True),      # accumulate
+    (3, [], 10, True, False, 1, True, 0, 0, False),                   # padding only
+]
+
+
+@pytest.mark.parametrize("K,sizes,extra,in_bf16,out_bf16,shift,average,order,offset,acc",
+                         FRAG_CASES)
+def test_reduce_scatter_frags_bit_exact(K, sizes, extra, in_bf16, out_bf16, shift, average,
+                                        order, offset, acc):
+    # the discrete path equals flatten-into-a-bucket then reduce-scatter
+    import torch
+    from synth import workloads as W
+    if sizes is None:
+        sizes = W.flatten8_numels()
+    total = sum(sizes)
+    N = -(-total // K) * K if extra is None else total + extra
+    C = -(-N // K)
+    frags_np = []
+    for r in range(K):
+        row = []
+        for p, n in enumerate(sizes):
+            h = synth.host_normal_bf16(SEED + 77, r * 4096 + p, 0, n, 1.0, 0.01, 1e4)
+            row.append(h if in_bf16 else oracle.bf16_to_f32(h))
+        frags_np.append(row)
+    frags = [[Guarded(n, torch_dt(in_bf16), offset, frags_np[r][p]) for p, n in enumerate(sizes)]
+             for r in range(K)]
+    odt = np.uint16 if out_bf16 else np.float32
+    rng = np.random.default_rng(K + N)
+    init = [oracle.f32_to_bf16(rng.standard_normal(C).astype(np.float32)) if out_bf16 else
+            rng.standard_normal(C).astype(np.float32) for _ in range(K)]
+    outs = [Guarded(C, torch_dt(out_bf16), offset, init[r]) for r in range(K)]
+    zr().zr_reduce_scatter_frags([[g.ptr() for g in row] for row in frags], sizes, N,
+                                 [g.ptr() for g in outs], chunk_shift=shift, average=average,
+                                 order=order, accumulate=acc, in_dtype=torch_dt(in_bf16),
+                                 out_dtype=torch_dt(out_bf16))
+    torch.cuda.synchronize()
+    bucket = oracle.flatten(frags_np, sizes, N) if sizes else \
+        [np.zeros(N, dtype=np.uint16 if in_bf16 else np.float32) for _ in range(K)]
+    if order == 1:
+        # free order: compare with the GPU's own contiguous free-order path
+        bt = [Guarded(N, torch_dt(in_bf16), 0, bucket[r]) for r in range(K)]
+        ref = [Guarded(C, torch_dt(out_bf16), 0) for _ in range(K)]
+        zr().zr_reduce_scatter_avg([g.ptr() for g in bt], N, [g.ptr() for g in ref],
+                                   chunk_shift=shift, average=average, order=1,
+                                   in_dtype=torch_dt(in_bf16), out_dtype=torch_dt(out_bf16))
+        torch.cuda.synchronize()
+        xf = np.stack([oracle.bf16_to_f32(x) if in_bf16 else x for x in bucket])
+        xp = np.zeros((K, K * C), dtype=np.float32)
+        xp[:, :N] = xf
+        exact, absum = oracle.exact_sum_points(xp)
+        scale = 1.0 / K if average else 1.0
+        for q in range(K):
+            j = (q + shift) % K
+            got = outs[q].get()
+            gotf = (oracle.bf16_to_f32(got) if out_bf16 else got).astype(np.float64)
+            ex = exact[j * C:(j + 1) * C] * scale
+            assert np.all(np.abs(gotf - ex) <= 1e-5 * absum[j * C:(j + 1) * C] * scale +
+                          (bf16_ulp(ex) if out_bf16 else 0))
+        return
+    want = [x.copy() for x in init]
+    oracle.reduce_scatter(bucket, N, odt, shift=shift, average=average, out=want,
+                          accumulate=acc, wire=(order == 2))
+    for r in range(K):
+        assert np.array_equal(bits(outs[r].get()), bits(want[r])), f"rank {r}"
+        assert outs[r].guards_intact()
+    for row in frags:
+        for g in row:
+            assert g.guards_intact()
+
+
+def test_reduce_scatter_frags_equals_gpu_flatten_then_rs():
+    import torch
+    from synth import workloads as W
+    K = 8
+    sizes = W.flatten8_numels()
+    N = -(-sum(sizes) // K) * K
+    C = N // K
+    frags = [[torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in sizes] for _ in range(K)]
+    for r in range(K):
+        for p in range(len(sizes)):
+            synth.dev_normal_bf16(frags[r][p], SEED + 5, r * 64 + p, 0, 1e-3)
+    buckets = [torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    a = [torch.empty(C, dtype=torch.float32, device="cuda") for _ in range(K)]
+    b = [torch.empty(C, dtype=torch.float32, device="cuda") for _ in range(K)]
+    zr().zr_flatten_bucket(frags, sizes, buckets, N)
+    zr().zr_reduce_scatter_avg(buckets, N, a, chunk_shift=1, average=True)
+    zr().zr_reduce_scatter_frags(frags, sizes, N, b, chunk_shift=1, average=True)
+    torch.cuda.synchronize()
+    for r in range(K):
+        assert torch.equal(a[r].view(torch.int32), b[r].view(torch.int32))
+
+
 def test_zero_sized_calls_enqueue_nothing():
     import torch
     m = zr()
