@@ -330,14 +330,15 @@ def bench_frags_layer(args):
     import gradient_sync_zr_amd as zr
     from synth import workloads as W
 
-    K = 8
-    sizes = [p.numel for p in W.llama_like_params(layers=1)[1:8]]
+    cfg = W.FRAGS_LAYER
+    K = cfg["K"]
+    sizes = W.frags_layer_numels()
     N = sum(sizes)          # 202,375,168: a multiple of 8
-    seed = W.seed_of(3)
+    seed = W.seed_of(cfg["seed_cfg"])
     frags = [[torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in sizes] for _ in range(K)]
     for r in range(K):
         for p in range(len(sizes)):
-            synth.dev_normal_bf16(frags[r][p], seed, 1000 + r * 8 + p, 0, 1e-3)
+            synth.dev_normal_bf16(frags[r][p], seed, W.frags_layer_stream(r, p), 0, cfg["sigma"])
     buckets = [torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
     parts = [torch.empty(N // K, dtype=torch.float32, device="cuda") for _ in range(K)]
     fp = [[t.data_ptr() for t in row] for row in frags]
@@ -367,8 +368,10 @@ def bench_frags_layer(args):
 
     ms_flat = timed(flat_rs)
     ms = timed(discrete)
-    step_bytes = N * (2 * K + 4)
+    step_bytes = N * (2 * K + 4)  # one launch per step
     value = step_bytes / (ms * 1e-3) / 1e9
+    src = kernel_source_hash(["zr_rsf.hip", "zr_fold.hpp", "zr_device.hpp"])
+    traffic = read_traffic("rsf_ring_bf16_f32_k8_frags_layer.counters.txt", src, step_bytes)
     return {
         "metric": "discrete reduce-scatter+avg+cast GB/s from 7 fragments per rank, K=8",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -383,7 +386,8 @@ def bench_frags_layer(args):
                    "K": K, "N": N, "bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "kernel": "rsf_kernel<bf16,f32,avg,ring>", "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "achieved": round(value, 1),
-                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel_source_sha256_16": src},
         "cpu_baseline": None,
     }
 

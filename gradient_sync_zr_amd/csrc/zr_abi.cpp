@@ -111,7 +111,6 @@ const Tuning& tuning() {
         env_int("ZR_RS_BLOCKS_PER_CU", 8, 1, 64),
         env_int("ZR_AR_BLOCKS_PER_CU", 8, 1, 64),
         env_int("ZR_AG_BLOCKS_PER_CU", 8, 1, 64),
-        env_int("ZR_NONTEMPORAL", 1, 0, 1),
         env_int("ZR_AR_NONTEMPORAL", 1, 0, 1),
         env_int("ZR_AG_NONTEMPORAL", 1, 0, 1),
     };

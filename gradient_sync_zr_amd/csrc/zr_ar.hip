@@ -58,8 +58,9 @@ __global__ void __launch_bounds__(kThreads) ar_kernel(const ArArgs a) {
         if (a.vec && j0 == j1 && t1 - t0 == TT) {
             float acc[S][4];
             constexpr bool kStatic = ORDER != kFree && KS > 0 && KS <= 8;
-            fold_quads<T, KS, NT, S, ORDER, kStatic>(RingBases<T, kStatic ? KS : 1>(a.in, kStatic ? j0 : 0),
-                                                      a.in, K, j0, g0, acc);
+            auto ptr = [&](int r) { return a.in.p[r]; };
+            fold_quads<T, KS, NT, S, ORDER, kStatic>(RingBases<T, kStatic ? KS : 1>(ptr, kStatic ? j0 : 0),
+                                                      ptr, K, j0, g0, acc);
             Quad<T> res[S];
 #pragma unroll
             for (int k = 0; k < S; ++k) {
@@ -78,7 +79,7 @@ __global__ void __launch_bounds__(kThreads) ar_kernel(const ArArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     const int64_t ge = g0 + 256 * k + e;
                     if (ge >= N) continue;
-                    float s = fold_elem<T, ORDER>(lds_ptr, K, (int)(ge / C), ge);
+                    float s = fold_elem<T, KS, ORDER>(lds_ptr, K, (int)(ge / C), ge);
                     s = average<AVG>(s, a.inv_k, a.kf);
                     T v;
                     store_elem(&v, s);

@@ -12,8 +12,9 @@ namespace zr {
 constexpr int kMaxRanks = ZR_MAX_RANKS;
 constexpr int kAgSegsPerLaunch = 32;   // segments carried in one all-gather launch
 constexpr int kFlatJobsPerLaunch = 96; // copy jobs carried in one flatten launch
-constexpr int kRsfPtrsPerLaunch = 320;   // rank pointers of fragments in one discrete-RS launch
-constexpr int kRsfEntriesPerLaunch = 40; // fragments in one discrete-RS launch
+constexpr int kRsfPtrsPerLaunch = 256;   // rank pointers of fragments in one discrete-RS launch
+constexpr int kRsfEntriesPerLaunch = 32; // fragments in one discrete-RS launch
+constexpr int kRsfSegsPerLaunch = 96;    // (fragment, chunk) segments in one discrete-RS launch
 
 // Rank pointer tables travel by value in kernel arguments (K <= 64 -> 512 B).
 struct ConstPtrs {
@@ -45,8 +46,7 @@ struct Tuning {
     int rs_blocks_per_cu;  // resident blocks per CU the RS grid is sized for
     int ar_blocks_per_cu;
     int ag_blocks_per_cu;
-    int nontemporal;       // reduce-scatter: streaming (non-temporal) loads and stores
-    int ar_nontemporal;    // fused all-reduce
+    int ar_nontemporal;    // fused all-reduce: streaming (non-temporal) loads and stores
     int ag_nontemporal;    // all-gather
 };
 const Tuning& tuning();

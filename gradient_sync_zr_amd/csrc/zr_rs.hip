@@ -20,11 +20,12 @@
 //
 // In a chunk whose start j*C allows quad access (j*C a multiple of 4), the
 // vector tiles begin at the chunk's first input element that starts a
-// 128-byte line (a head of fewer than one line of elements), so the K input
-// streams are read in whole lines; the head, the ragged tail and the padding
-// fold element by element in one extra tile. Chunks whose start does not
-// allow quad access fold element by element tile by tile. Positions g >= N
-// are padding and receive +0.
+// 128-byte line, so the K input streams are read in whole lines; the first
+// tile also folds the head (fewer than one line of elements) element by
+// element, and the last tile folds its whole quads below N as vectors and
+// the few elements after them one by one. Chunks whose start does not allow
+// quad access fold element by element tile by tile. Positions g >= N are
+// padding and receive +0.
 #include "zr_fold.hpp"
 
 namespace zr {
@@ -37,24 +38,10 @@ struct RsArgs {
     uint64_t vec_mask;         // bit j: chunk j takes the vector path
     int16_t head[kMaxRanks];   // chunk j's vector tiles start at chunk offset head[j]
     int K, shift;
-    int tiles_per_chunk;       // ceil(C / tile) + 1: the extra tile folds head and tail
+    int tiles_per_chunk;       // ceil(C / tile): no chunk has more tiles
     int accumulate;            // 1: out = old + result (gradient accumulation)
     float inv_k, kf;
 };
-
-// Slices per wave: 4 for bf16 input (32 loads of 8 bytes in flight per lane
-// at K = 8), 2 for fp32 input (same bytes in flight). Build-time knobs for
-// tuning sweeps.
-#ifndef ZR_RS_SLICES_BF16
-#define ZR_RS_SLICES_BF16 4
-#endif
-#ifndef ZR_RS_SLICES_FP32
-#define ZR_RS_SLICES_FP32 2
-#endif
-template <typename TIn>
-constexpr int kSlices = sizeof(TIn) == 2 ? ZR_RS_SLICES_BF16 : ZR_RS_SLICES_FP32;
-template <typename TIn>
-constexpr int64_t kRsTile = (int64_t)(kThreads / 64) * kSlices<TIn> * 256;
 
 template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT>
 __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
@@ -68,55 +55,79 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
     const int64_t C = a.C, N = a.N;
     const int64_t chunk_base = (int64_t)j * C;
     TOut* outp = static_cast<TOut*>(a.out.p[holder]);
-    auto ptr = [&](int r) { return a.in.p[r]; };
-    const RingBases<TIn, kStatic ? KS : 1> bases(a.in, kStatic ? j : 0);
+    auto ptr = [&](int r) __attribute__((always_inline)) { return a.in.p[r]; };
+    const RingBases<TIn, kStatic ? KS : 1> bases(ptr, kStatic ? j : 0);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 
     // one output element, folded element-wise (padding past N gets +0)
-    auto elem = [&](int64_t o) {
+    auto elem = [&](int64_t o) __attribute__((always_inline)) {
         const int64_t g = chunk_base + o;
         float s = 0.0f;
         if (g < N) {
-            s = fold_elem<TIn, ORDER>(ptr, K, j, g);
+            s = fold_elem<TIn, KS, ORDER>(ptr, K, j, g);
             s = average<AVG>(s, a.inv_k, a.kf);
         }
         if (a.accumulate) s = __fadd_rn(load_elem(outp + o), s);
         store_elem(outp + o, s);
     };
+    // S folded quads at chunk offsets o0 + 256k: average, accumulate, store
+    auto emit = [&](int64_t o0, auto& acc, auto slices) __attribute__((always_inline)) {
+        constexpr int SS = decltype(slices)::value;
+#pragma unroll
+        for (int k = 0; k < SS; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[k][e] = average<AVG>(acc[k][e], a.inv_k, a.kf);
+        if (a.accumulate) {
+#pragma unroll
+            for (int k = 0; k < SS; ++k) {
+                float old[4];
+                widen4(load_quad<TOut, NT>(outp + o0 + 256 * k), old);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[k][e] = __fadd_rn(old[e], acc[k][e]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < SS; ++k) store_quad<TOut, NT>(outp + o0 + 256 * k, pack4<TOut>(acc[k]));
+    };
     const int64_t h = vec ? a.head[j] : 0;
     const int64_t valid = (N - chunk_base < C) ? N - chunk_base : C;  // non-padding extent
-    const int64_t nt = (vec && valid > h) ? (valid - h) / T : 0;      // whole vector tiles
+    // a vector chunk's tiles cover [h, C), the last one possibly partial, and
+    // tile 0 also folds the head [0, h); other chunks go element-wise by tiles
+    const int64_t ntiles = vec ? (C > h ? (C - h + T - 1) / T : 1) : (C + T - 1) / T;
 
-    for (int t = blockIdx.x; t < a.tiles_per_chunk; t += gridDim.x) {
-        if (t < nt) {
-            const int64_t o0 = h + (int64_t)t * T + (int64_t)wave * (S * 256) + lane * 4;
-            float acc[S][4];
-            const int64_t g0 = chunk_base + o0;
-            fold_quads<TIn, KS, NT, S, ORDER, kStatic>(bases, a.in, K, j, g0, acc);
-#pragma unroll
-            for (int k = 0; k < S; ++k)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[k][e] = average<AVG>(acc[k][e], a.inv_k, a.kf);
-            if (a.accumulate) {
-#pragma unroll
-                for (int k = 0; k < S; ++k) {
-                    float old[4];
-                    widen4(load_quad<TOut, NT>(outp + o0 + 256 * k), old);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[k][e] = __fadd_rn(old[e], acc[k][e]);
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < S; ++k) store_quad<TOut, NT>(outp + o0 + 256 * k, pack4<TOut>(acc[k]));
-        } else if (vec) {
-            if (t != nt) continue;
-            for (int64_t o = threadIdx.x; o < h && o < C; o += kThreads) elem(o);
-            for (int64_t o = h + nt * T + threadIdx.x; o < C; o += kThreads) elem(o);
-        } else {
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        if (!vec) {
             const int64_t lo = (int64_t)t * T;
             const int64_t hi = (lo + T < C) ? lo + T : C;
             for (int64_t o = lo + threadIdx.x; o < hi; o += kThreads) elem(o);
+            continue;
+        }
+        if (t == 0)
+            for (int64_t o = threadIdx.x; o < h && o < C; o += kThreads) elem(o);
+        const int64_t ot = h + (int64_t)t * T;
+        if (ot >= C) continue;
+        const int64_t o0 = ot + (int64_t)wave * (S * 256) + lane * 4;
+        if (ot + T <= valid) {
+            float acc[S][4];
+            fold_quads<TIn, KS, NT, S, ORDER, kStatic>(bases, ptr, K, j, chunk_base + o0, acc);
+            emit(o0, acc, std::integral_constant<int, S>{});
+        } else {
+            // the last tile: whole quads below the padding fold as vectors,
+            // the rest up to C element by element
+#pragma unroll 1
+            for (int k = 0; k < S; ++k) {
+                const int64_t q = o0 + 256 * k;
+                if (q + 4 <= valid) {
+                    float acc[1][4];
+                    fold_quads<TIn, KS, NT, 1, ORDER, kStatic>(bases, ptr, K, j, chunk_base + q, acc);
+                    emit(q, acc, std::integral_constant<int, 1>{});
+                } else {
+#pragma unroll 1
+                    for (int e = 0; e < 4; ++e)
+                        if (q + e < C) elem(q + e);
+                }
+            }
         }
     }
 }
@@ -132,26 +143,20 @@ hipError_t launch_t(const RsArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename TIn, typename TOut, int KS, int AVG, int ORDER>
-hipError_t pick_nt(const RsArgs& a, hipStream_t s) {
-    return tuning().nontemporal ? launch_t<TIn, TOut, KS, AVG, ORDER, true>(a, s)
-                                : launch_t<TIn, TOut, KS, AVG, ORDER, false>(a, s);
-}
-
 // Orders: the free order has one generic instantiation; ring and wire orders
-// have K = 8 specialised. With fp32 input the wire order is the ring order
+// have K = 8 specialised, other K take the generic kernel (batches of eight
+// ranks in flight). With fp32 input the wire order is the ring order
 // (rounding every hop to fp32 is what the fp32 adds already do).
 template <typename TIn, typename TOut, int AVG>
 hipError_t pick_k(const RsArgs& a, int order, hipStream_t s) {
-    if (order == kFree) return pick_nt<TIn, TOut, 0, AVG, kFree>(a, s);
+    if (order == kFree) return launch_t<TIn, TOut, 0, AVG, kFree, kRsNontemporal>(a, s);
     if (order == kWire && sizeof(TIn) == 2) {
-        if (a.K == 8) return pick_nt<TIn, TOut, 8, AVG, kWire>(a, s);
-        return pick_nt<TIn, TOut, 0, AVG, kWire>(a, s);
+        if (a.K == 8) return launch_t<TIn, TOut, 8, AVG, kWire, kRsNontemporal>(a, s);
+        return launch_t<TIn, TOut, 0, AVG, kWire, kRsNontemporal>(a, s);
     }
     switch (a.K) {
-        case 8: return pick_nt<TIn, TOut, 8, AVG, kRing>(a, s);
-        case 64: return pick_nt<TIn, TOut, 64, AVG, kRing>(a, s);
-        default: return pick_nt<TIn, TOut, 0, AVG, kRing>(a, s);
+        case 8: return launch_t<TIn, TOut, 8, AVG, kRing, kRsNontemporal>(a, s);
+        default: return launch_t<TIn, TOut, 0, AVG, kRing, kRsNontemporal>(a, s);
     }
 }
 
@@ -167,7 +172,7 @@ hipError_t pick_avg(const RsArgs& a, int avg_mode, int order, hipStream_t s) {
 template <typename TIn, typename TOut>
 hipError_t launch_typed(RsArgs& a, int avg_mode, int order, hipStream_t s) {
     constexpr int64_t T = kRsTile<TIn>;
-    a.tiles_per_chunk = (int)((a.C + T - 1) / T) + 1;
+    a.tiles_per_chunk = (int)((a.C + T - 1) / T);
     // Vector path: every base aligned for quad access (8 bytes for bf16
     // quads, 16 for fp32 quads) and j*C a multiple of 4 elements, so that a
     // vector tile start j*C + head is a quad boundary on the input side and

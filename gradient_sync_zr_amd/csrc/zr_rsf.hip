@@ -5,147 +5,270 @@
 // per-parameter gradients ("DeepSpeed ZeRO-3 源码解析", 5.2, the discrete
 // path; 3.2 on when gradients stay fragmented). Here the result is defined as
 // flattening the fragments into a virtual bucket of N elements (fragment p at
-// offset n_0 + ... + n_{p-1}, zero padding after the last one) and reducing
-// that bucket exactly as the contiguous reduce-scatter does: chunk j = g / C
-// folded in its order, averaged, written to rank (j - shift) mod K at g - jC.
-// The bucket itself is never written: each input element is read once from its
-// fragment.
+// offset n_0 + ... + n_{p-1}, zero padding after the last one up to K*C) and
+// reducing that bucket exactly as the contiguous reduce-scatter does: chunk
+// j = g / C folded in its order, averaged, written to rank (j - shift) mod K
+// at g - jC. The bucket itself is never written: each input element is read
+// once from its fragment.
 //
-// A launch carries a batch of fragments (their K rank pointers, offsets and
-// sizes) in its kernel arguments; the padding tail is one more entry whose
-// pointers are null (it reads as zeros). blockIdx.y = entry, blockIdx.x
-// strides over 2048-element tiles of the entry; a lane owns 8 consecutive
-// elements of the fragment. The block copies its entry's K pointers to LDS, so
-// a lane can fold any chunk's ring order. Groups of 8 that lie in one chunk
-// and start 16-byte aligned in every rank's fragment load 16 bytes per rank;
-// their outputs are stored as one group when aligned, else element by element.
+// Work is cut into segments: the part of one fragment that falls in one
+// chunk. A segment is a contiguous run of the fragment on every rank that
+// lands contiguously in one holder's partition, so it is reduced like a chunk
+// of the contiguous kernel: the same 4-wave x S-slice x 256-element tiles of
+// lane-owned quads, every rank's loads in flight before the ring-order adds,
+// non-temporal streams. A launch carries up to 32 fragments' rank pointers,
+// their segments and each segment's first tile in its kernel arguments; the
+// grid strides over the launch's tiles in order, so blocks stay balanced
+// however unequal the fragments are. A segment whose rank buffers share one
+// quad phase starts its vector tiles at rank j's next 128-byte line: the
+// first tile also folds the head element by element, the last folds its whole
+// quads as vectors and the last few elements one by one, and the stores fall
+// back to single elements when the partition side is not quad aligned. Other
+// segments fold element by element, 1024 elements per tile. The padding entry
+// has null pointers and writes +0 (old + 0 when accumulating).
 #include "zr_fold.hpp"
 
 namespace zr {
 namespace {
 
 struct RsfArgs {
-    const void* ptr[kRsfPtrsPerLaunch];  // entry-major: ptr[m * K + r]
-    int64_t off[kRsfEntriesPerLaunch];   // virtual-bucket offset of entry m
-    int64_t n[kRsfEntriesPerLaunch];     // elements of entry m
+    const void* ptr[kRsfPtrsPerLaunch];    // entry-major: ptr[m * K + r]; null: padding entry
+    int64_t off[kRsfEntriesPerLaunch];     // virtual-bucket offset of entry m
+    int64_t n[kRsfEntriesPerLaunch];       // elements of entry m
     MutPtrs out;
-    int64_t N, C;
-    int K, shift, accumulate, pad_;
+    int32_t tile0[kRsfSegsPerLaunch + 1];  // first tile of segment s; tile0[nseg] = all tiles
+    uint8_t seg_m[kRsfSegsPerLaunch];      // entry of segment s
+    uint8_t seg_j[kRsfSegsPerLaunch];      // chunk of segment s
+    int16_t seg_head[kRsfSegsPerLaunch];   // vector tiles start at this offset; -1: element-wise
+    int64_t C;
+    int K, shift, accumulate, nseg;
     float inv_k, kf;
 };
+static_assert(sizeof(RsfArgs) <= 4096, "discrete reduce-scatter arguments exceed 4 KB");
 
-template <typename TIn, typename TOut, int AVG, int ORDER>
+// Elements per tile of a segment that folds element by element (4 per thread).
+constexpr int64_t kElemTile = kThreads * 4;
+
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT>
 __global__ void __launch_bounds__(kThreads) rsf_kernel(const RsfArgs a) {
-    const int K = a.K;
-    const int m = blockIdx.y;
-    __shared__ const void* sp[kMaxRanks];
-    if (threadIdx.x == 0)
-        for (int r = 0; r < K; ++r) sp[r] = a.ptr[m * K + r];
-    __syncthreads();
-    const bool padding = sp[0] == nullptr;
-    auto ptr = [&](int r) { return sp[r]; };
-    const int64_t n = a.n[m], off = a.off[m], C = a.C;
-    const int64_t tiles = (n + kTile - 1) / kTile;
+    constexpr int S = kSlices<TIn>;
+    constexpr int64_t T = kRsTile<TIn>;
+    constexpr bool kStatic = ORDER != kFree && KS > 0 && KS <= 8;
+    const int K = KS > 0 ? KS : a.K;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int total = a.tile0[a.nseg];
+    int s = 0;
+    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+        while (t >= a.tile0[s + 1]) ++s;  // a block's tiles only grow: segments in order
+        const int m = a.seg_m[s], j = a.seg_j[s];
+        const int64_t jc = (int64_t)j * a.C;
+        const int64_t f0 = a.off[m], f1 = a.off[m] + a.n[m];
+        const int64_t lo = f0 > jc ? f0 : jc;
+        const int64_t hi = f1 < jc + a.C ? f1 : jc + a.C;
+        const int64_t l_lo = lo - f0, len = hi - lo;  // fragment-local start, length
+        TOut* outp = static_cast<TOut*>(a.out.p[wrap(j - a.shift + K, K)]) + (lo - jc);
+        auto ptr = [&](int r) __attribute__((always_inline)) { return a.ptr[m * K + r]; };
+        const bool pad = ptr(0) == nullptr;
+        const int64_t tt = t - a.tile0[s];
+        const int64_t h = a.seg_head[s];
 
-    // one output element at virtual index g (fragment-local l)
-    auto elem = [&](int64_t l, int64_t g, int j) {
-        float s = 0.0f;
-        if (!padding) {
-            s = fold_elem<TIn, ORDER>(ptr, K, j, l);
-            s = average<AVG>(s, a.inv_k, a.kf);
+        // one output element (segment offset o), folded element-wise
+        auto elem = [&](int64_t o) __attribute__((always_inline)) {
+            float v = 0.0f;
+            if (!pad) v = average<AVG>(fold_elem<TIn, KS, ORDER>(ptr, K, j, l_lo + o), a.inv_k, a.kf);
+            if (a.accumulate) v = __fadd_rn(load_elem(outp + o), v);
+            store_elem(outp + o, v);
+        };
+        if (h < 0) {
+            const int64_t e0 = tt * kElemTile, e1 = (e0 + kElemTile < len) ? e0 + kElemTile : len;
+            for (int64_t o = e0 + threadIdx.x; o < e1; o += kThreads) elem(o);
+            continue;
         }
-        TOut* o = static_cast<TOut*>(a.out.p[wrap(j - a.shift + K, K)]) + (g - (int64_t)j * C);
-        if (a.accumulate) s = __fadd_rn(load_elem(o), s);
-        store_elem(o, s);
-    };
-
-    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-        const int64_t l0 = t * kTile + (int64_t)threadIdx.x * kGroup;
-        if (l0 >= n) continue;
-        const int64_t g0 = off + l0;
-        const int j0 = (int)(g0 / C);
-        const int cnt = (int)((n - l0) < kGroup ? (n - l0) : kGroup);
-        const bool one_chunk = (g0 + cnt - 1) < (int64_t)(j0 + 1) * C;
-        bool aligned = !padding && cnt == kGroup && one_chunk;
-        if (aligned)
-            for (int r = 0; r < K; ++r)
-                aligned = aligned && ((uintptr_t)(static_cast<const TIn*>(sp[r]) + l0) & 15) == 0;
-        if (aligned) {
-            // ring / wire / free order over 16-byte groups, pointers from LDS
-            float acc[8];
-            if constexpr (ORDER == kFree) {
-                widen(load_group<TIn, false>(static_cast<const TIn*>(sp[0]) + l0), acc);
-                for (int r = 1; r < K; ++r) {
-                    float f[8];
-                    widen(load_group<TIn, false>(static_cast<const TIn*>(sp[r]) + l0), f);
+        // the partition side is quad aligned at the vector tiles' start or not
+        // at all (the tiles advance in whole quads)
+        const bool out_quad = (((uintptr_t)(outp + h)) & (4 * sizeof(TOut) - 1)) == 0;
+        // SS folded quads at segment offsets o0 + 256k: average, accumulate, store
+        auto emit = [&](int64_t o0, auto& acc, auto slices) __attribute__((always_inline)) {
+            constexpr int SS = decltype(slices)::value;
+            if (!pad) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[e] = __fadd_rn(acc[e], f[e]);
-                }
-            } else {
-                widen(load_group<TIn, false>(static_cast<const TIn*>(sp[j0]) + l0), acc);
-                int r = j0;
-                for (int h = 1; h < K; ++h) {
-                    r = wrap(r + 1, K);
-                    float f[8];
-                    widen(load_group<TIn, false>(static_cast<const TIn*>(sp[r]) + l0), f);
+                for (int k = 0; k < SS; ++k)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        acc[e] = __fadd_rn(acc[e], f[e]);
-                        if constexpr (ORDER == kWire) acc[e] = wire_round(acc[e]);
+                    for (int e = 0; e < 4; ++e) acc[k][e] = average<AVG>(acc[k][e], a.inv_k, a.kf);
+            }
+            if (out_quad) {
+                if (a.accumulate) {
+#pragma unroll
+                    for (int k = 0; k < SS; ++k) {
+                        float old[4];
+                        widen4(load_quad<TOut, NT>(outp + o0 + 256 * k), old);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[k][e] = __fadd_rn(old[e], acc[k][e]);
                     }
                 }
-            }
-            TOut* o = static_cast<TOut*>(a.out.p[wrap(j0 - a.shift + K, K)]) + (g0 - (int64_t)j0 * C);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = average<AVG>(acc[e], a.inv_k, a.kf);
-            if (((uintptr_t)o & 15) == 0) {
-                if (a.accumulate) {
-                    float old[8];
-                    widen(load_group<TOut, false>(o), old);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[e] = __fadd_rn(old[e], acc[e]);
-                }
-                store_group<TOut, false>(o, pack<TOut>(acc));
+                for (int k = 0; k < SS; ++k) store_quad<TOut, NT>(outp + o0 + 256 * k, pack4<TOut>(acc[k]));
             } else {
-                for (int e = 0; e < 8; ++e) {
-                    float s = acc[e];
-                    if (a.accumulate) s = __fadd_rn(load_elem(o + e), s);
-                    store_elem(o + e, s);
-                }
+#pragma unroll
+                for (int k = 0; k < SS; ++k)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        TOut* o = outp + o0 + 256 * k + e;
+                        float v = acc[k][e];
+                        if (a.accumulate) v = __fadd_rn(load_elem(o), v);
+                        store_elem(o, v);
+                    }
             }
+        };
+        // SS quads of the fragment (zeros for the padding entry)
+        auto fold = [&](int64_t o0, auto& acc, auto slices) __attribute__((always_inline)) {
+            constexpr int SS = decltype(slices)::value;
+            if (pad) {
+#pragma unroll
+                for (int k = 0; k < SS; ++k)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[k][e] = 0.0f;
+            } else {
+                const RingBases<TIn, kStatic ? KS : 1> bases(ptr, kStatic ? j : 0);
+                fold_quads<TIn, KS, NT, SS, ORDER, kStatic>(bases, ptr, K, j, l_lo + o0, acc);
+            }
+        };
+        // tiles cover [h, len), the last one possibly partial; tile 0 also
+        // folds the head [0, h)
+        if (tt == 0)
+            for (int64_t o = threadIdx.x; o < h && o < len; o += kThreads) elem(o);
+        const int64_t ot = h + tt * T;
+        if (ot >= len) continue;
+        const int64_t o0 = ot + (int64_t)wave * (S * 256) + lane * 4;
+        if (ot + T <= len) {
+            float acc[S][4];
+            fold(o0, acc, std::integral_constant<int, S>{});
+            emit(o0, acc, std::integral_constant<int, S>{});
         } else {
-            for (int e = 0; e < cnt; ++e) {
-                const int64_t g = g0 + e;
-                elem(l0 + e, g, (int)(g / C));
+#pragma unroll 1
+            for (int k = 0; k < S; ++k) {
+                const int64_t q = o0 + 256 * k;
+                if (q + 4 <= len) {
+                    float acc[1][4];
+                    fold(q, acc, std::integral_constant<int, 1>{});
+                    emit(q, acc, std::integral_constant<int, 1>{});
+                } else {
+#pragma unroll 1
+                    for (int e = 0; e < 4; ++e)
+                        if (q + e < len) elem(q + e);
+                }
             }
         }
     }
 }
 
-template <typename TIn, typename TOut, int AVG, int ORDER>
-hipError_t launch_t(const RsfArgs& a, int entries, int64_t max_tiles, hipStream_t stream) {
-    int64_t want = (int64_t)device_cu_count() * 8 / entries;
-    if (want < 1) want = 1;
-    const int gx = (int)(want < max_tiles ? want : max_tiles);
-    hipLaunchKernelGGL((rsf_kernel<TIn, TOut, AVG, ORDER>), dim3(gx, entries), dim3(kThreads), 0,
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT>
+hipError_t launch_t(const RsfArgs& a, hipStream_t stream) {
+    const int total = a.tile0[a.nseg];
+    int64_t want = (int64_t)device_cu_count() * tuning().rs_blocks_per_cu;
+    const int gx = (int)(want < total ? want : total);
+    hipLaunchKernelGGL((rsf_kernel<TIn, TOut, KS, AVG, ORDER, NT>), dim3(gx), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
 }
 
+// Ring and wire order at K = 8 specialised, the rest generic (batches of
+// eight ranks in flight); fp32 input makes the wire order the ring order.
 template <typename TIn, typename TOut, int AVG>
-hipError_t pick_order(const RsfArgs& a, int entries, int64_t mt, int order, hipStream_t s) {
-    if (order == kFree) return launch_t<TIn, TOut, AVG, kFree>(a, entries, mt, s);
-    if (order == kWire && sizeof(TIn) == 2) return launch_t<TIn, TOut, AVG, kWire>(a, entries, mt, s);
-    return launch_t<TIn, TOut, AVG, kRing>(a, entries, mt, s);
+hipError_t pick_k(const RsfArgs& a, int order, hipStream_t s) {
+    if (order == kFree) return launch_t<TIn, TOut, 0, AVG, kFree, kRsNontemporal>(a, s);
+    if (order == kWire && sizeof(TIn) == 2) {
+        if (a.K == 8) return launch_t<TIn, TOut, 8, AVG, kWire, kRsNontemporal>(a, s);
+        return launch_t<TIn, TOut, 0, AVG, kWire, kRsNontemporal>(a, s);
+    }
+    switch (a.K) {
+        case 8: return launch_t<TIn, TOut, 8, AVG, kRing, kRsNontemporal>(a, s);
+        default: return launch_t<TIn, TOut, 0, AVG, kRing, kRsNontemporal>(a, s);
+    }
 }
 
 template <typename TIn, typename TOut>
-hipError_t pick_avg(const RsfArgs& a, int entries, int64_t mt, int avg, int order, hipStream_t s) {
+hipError_t pick_avg(const RsfArgs& a, int avg, int order, hipStream_t s) {
     switch (avg) {
-        case 1: return pick_order<TIn, TOut, 1>(a, entries, mt, order, s);
-        case 2: return pick_order<TIn, TOut, 2>(a, entries, mt, order, s);
-        default: return pick_order<TIn, TOut, 0>(a, entries, mt, order, s);
+        case 1: return pick_k<TIn, TOut, 1>(a, order, s);
+        case 2: return pick_k<TIn, TOut, 2>(a, order, s);
+        default: return pick_k<TIn, TOut, 0>(a, order, s);
     }
+}
+
+// Head of a segment whose K rank runs start at byte addresses addr[r]: the
+// elements before rank j's next 128-byte line, or -1 when the runs do not
+// share one quad phase (no offset aligns them all for quad loads).
+int16_t segment_head(const uintptr_t* addr, int K, int j, uintptr_t es) {
+    const uintptr_t quad = 4 * es;
+    for (int r = 1; r < K; ++r)
+        if ((addr[r] - addr[0]) % quad != 0) return -1;
+    return (int16_t)(((128 - addr[j] % 128) % 128) / es);
+}
+
+template <typename TIn, typename TOut>
+hipError_t launch_typed(RsfArgs& a, const FragEntry* entries, int n_entries, int avg, int order,
+                        hipStream_t stream) {
+    constexpr int64_t T = kRsTile<TIn>;
+    const int K = a.K;
+    const int64_t C = a.C;
+    const int max_entries = (kRsfPtrsPerLaunch / K) < kRsfEntriesPerLaunch ? (kRsfPtrsPerLaunch / K)
+                                                                         : kRsfEntriesPerLaunch;
+    int m = 0;
+    int64_t tiles = 0;
+    a.nseg = 0;
+    auto flush = [&]() -> hipError_t {
+        if (m == 0) return hipSuccess;
+        a.tile0[a.nseg] = (int32_t)tiles;
+        hipError_t e = pick_avg<TIn, TOut>(a, avg, order, stream);
+        m = 0;
+        tiles = 0;
+        a.nseg = 0;
+        return e;
+    };
+    for (int ei = 0; ei < n_entries; ++ei) {
+        const FragEntry& f = entries[ei];
+        const int j0 = (int)(f.off / C), j1 = (int)((f.off + f.n - 1) / C);
+        if (m == max_entries || a.nseg + (j1 - j0 + 1) > kRsfSegsPerLaunch) {
+            hipError_t e = flush();
+            if (e != hipSuccess) return e;
+        }
+        a.off[m] = f.off;
+        a.n[m] = f.n;
+        for (int r = 0; r < K; ++r) a.ptr[m * K + r] = f.ptr[r];
+        const bool pad = f.ptr[0] == nullptr;
+        for (int j = j0; j <= j1; ++j) {
+            const int64_t jc = (int64_t)j * C;
+            const int64_t lo = f.off > jc ? f.off : jc;
+            const int64_t hi = (f.off + f.n) < jc + C ? (f.off + f.n) : jc + C;
+            const int64_t len = hi - lo;
+            uintptr_t addr[kMaxRanks];
+            int16_t h;
+            if (pad) {
+                // no input: align the partition side to its 128-byte lines
+                const int q = ((j - a.shift) % K + K) % K;
+                const uintptr_t o = (uintptr_t)a.out.p[q] + (uintptr_t)(lo - jc) * sizeof(TOut);
+                h = (int16_t)(((128 - o % 128) % 128) / sizeof(TOut));
+            } else {
+                for (int r = 0; r < K; ++r)
+                    addr[r] = (uintptr_t)f.ptr[r] + (uintptr_t)(lo - f.off) * sizeof(TIn);
+                h = segment_head(addr, K, j, sizeof(TIn));
+            }
+            const int s = a.nseg++;
+            a.seg_m[s] = (uint8_t)m;
+            a.seg_j[s] = (uint8_t)j;
+            a.seg_head[s] = h;
+            a.tile0[s] = (int32_t)tiles;
+            tiles += h < 0 ? (len + kElemTile - 1) / kElemTile : (len > h ? (len - h + T - 1) / T : 1);
+        }
+        ++m;
+        if (tiles > INT32_MAX / 2) {
+            hipError_t e = flush();
+            if (e != hipSuccess) return e;
+        }
+    }
+    return flush();
 }
 
 }  // namespace
@@ -155,43 +278,23 @@ hipError_t launch_reduce_scatter_frags(int K, const FragEntry* entries, int n_en
                                        int shift, int flags, zr_order order, hipStream_t stream) {
     RsfArgs a;
     a.out = out;
-    a.N = N;
     a.K = K;
     a.C = (N + K - 1) / K;
     a.shift = shift;
     a.accumulate = (flags & ZR_ACCUMULATE) ? 1 : 0;
-    a.pad_ = 0;
+    a.nseg = 0;
     a.inv_k = 1.0f / (float)K;
     a.kf = (float)K;
     const bool pow2 = (K & (K - 1)) == 0;
     const int avg = !(flags & ZR_AVERAGE) ? 0 : (pow2 ? 1 : 2);
     const int ord = order == ZR_ORDER_FREE ? kFree : (order == ZR_ORDER_RING_WIRE ? kWire : kRing);
-    // entries per launch: bounded by the entry slots and by the pointer slots
-    const int per = (kRsfPtrsPerLaunch / K) < kRsfEntriesPerLaunch ? (kRsfPtrsPerLaunch / K)
-                                                                   : kRsfEntriesPerLaunch;
-    for (int e0 = 0; e0 < n_entries; e0 += per) {
-        const int cnt = (n_entries - e0) < per ? (n_entries - e0) : per;
-        int64_t max_tiles = 1;
-        for (int m = 0; m < cnt; ++m) {
-            const FragEntry& f = entries[e0 + m];
-            a.off[m] = f.off;
-            a.n[m] = f.n;
-            for (int r = 0; r < K; ++r) a.ptr[m * K + r] = f.ptr[r];
-            const int64_t t = (f.n + kTile - 1) / kTile;
-            if (t > max_tiles) max_tiles = t;
-        }
-        hipError_t e;
-        if (in_dt == ZR_BF16 && out_dt == ZR_FP32)
-            e = pick_avg<uint16_t, float>(a, cnt, max_tiles, avg, ord, stream);
-        else if (in_dt == ZR_BF16 && out_dt == ZR_BF16)
-            e = pick_avg<uint16_t, uint16_t>(a, cnt, max_tiles, avg, ord, stream);
-        else if (in_dt == ZR_FP32 && out_dt == ZR_FP32)
-            e = pick_avg<float, float>(a, cnt, max_tiles, avg, ord, stream);
-        else
-            e = pick_avg<float, uint16_t>(a, cnt, max_tiles, avg, ord, stream);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    if (in_dt == ZR_BF16 && out_dt == ZR_FP32)
+        return launch_typed<uint16_t, float>(a, entries, n_entries, avg, ord, stream);
+    if (in_dt == ZR_BF16 && out_dt == ZR_BF16)
+        return launch_typed<uint16_t, uint16_t>(a, entries, n_entries, avg, ord, stream);
+    if (in_dt == ZR_FP32 && out_dt == ZR_FP32)
+        return launch_typed<float, float>(a, entries, n_entries, avg, ord, stream);
+    return launch_typed<float, uint16_t>(a, entries, n_entries, avg, ord, stream);
 }
 
 }  // namespace zr

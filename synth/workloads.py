@@ -89,3 +89,18 @@ ZERO3 = dict(id=4, K=8, sigma=0.02, shift=0, prefetch_bytes=50_000_000, elem_byt
 
 # ------------------------------------------------------------------ cfg 5
 ALLREDUCE64 = dict(id=5, K=64, N=1_000_000_007, sigma=1.0, outlier_p=0.01, outlier_mag=1e4)
+
+
+# ------------------------------------------- discrete path at full scale
+# The seven weight gradients of one transformer layer of the parameter set
+# above (q, k, v, o, gate, up, down: 202,375,168 elements) per rank, reduced
+# straight from the fragments; seeded under the ZeRO-2 gradient seed.
+FRAGS_LAYER = dict(K=8, sigma=1e-3, shift=1, seed_cfg=3)
+
+
+def frags_layer_numels() -> List[int]:
+    return [p.numel for p in llama_like_params(layers=1)[1:8]]
+
+
+def frags_layer_stream(rank: int, frag: int) -> int:
+    return 1000 + rank * 8 + frag

@@ -374,6 +374,11 @@ FRAG_CASES = [
     (16, [30001, 40000], 0, True, False, 1, True, 1, 0, False),       # free order
     (8, [30001, 40000, 9], 0, True, False, 1, True, 0, 0, True),      # accumulate
     (3, [], 10, True, False, 1, True, 0, 0, False),                   # padding only
+    (64, [300000, 5], 59, True, False, 1, True, 0, 0, False),         # K = 64 vector tiles
+    (8, [30001, 40000, 9], 5, True, True, 1, True, 0, -1, False),     # ranks in different quad phases
+    (8, [6, 30000, 40000], 2, True, True, 1, True, 0, 0, False),      # bf16 partition side unaligned
+    (8, [6, 30000, 40000], 2, False, False, 1, True, 0, 0, True),     # fp32, unaligned, accumulate
+    (8, [6, 30000, 40000], 2, True, False, 0, True, 2, -1, False),    # wire order, mixed phases
 ]
 
 
@@ -381,7 +386,9 @@ FRAG_CASES = [
                          FRAG_CASES)
 def test_reduce_scatter_frags_bit_exact(K, sizes, extra, in_bf16, out_bf16, shift, average,
                                         order, offset, acc):
-    # the discrete path equals flatten-into-a-bucket then reduce-scatter
+    # the discrete path equals flatten-into-a-bucket then reduce-scatter;
+    # offset -1: rank r's fragments at element offset r % 4 (the ranks' buffers
+    # in different quad phases), every partition at offset 1
     import torch
     from synth import workloads as W
     if sizes is None:
@@ -396,13 +403,15 @@ def test_reduce_scatter_frags_bit_exact(K, sizes, extra, in_bf16, out_bf16, shif
             h = synth.host_normal_bf16(SEED + 77, r * 4096 + p, 0, n, 1.0, 0.01, 1e4)
             row.append(h if in_bf16 else oracle.bf16_to_f32(h))
         frags_np.append(row)
-    frags = [[Guarded(n, torch_dt(in_bf16), offset, frags_np[r][p]) for p, n in enumerate(sizes)]
+    f_off = (lambda r: r % 4) if offset == -1 else (lambda r: offset)
+    o_off = 1 if offset == -1 else offset
+    frags = [[Guarded(n, torch_dt(in_bf16), f_off(r), frags_np[r][p]) for p, n in enumerate(sizes)]
              for r in range(K)]
     odt = np.uint16 if out_bf16 else np.float32
     rng = np.random.default_rng(K + N)
     init = [oracle.f32_to_bf16(rng.standard_normal(C).astype(np.float32)) if out_bf16 else
             rng.standard_normal(C).astype(np.float32) for _ in range(K)]
-    outs = [Guarded(C, torch_dt(out_bf16), offset, init[r]) for r in range(K)]
+    outs = [Guarded(C, torch_dt(out_bf16), o_off, init[r]) for r in range(K)]
     zr().zr_reduce_scatter_frags([[g.ptr() for g in row] for row in frags], sizes, N,
                                  [g.ptr() for g in outs], chunk_shift=shift, average=average,
                                  order=order, accumulate=acc, in_dtype=torch_dt(in_bf16),

@@ -1,8 +1,9 @@
-"""The five workloads at their full sizes, in the launch configuration the
-benchmark uses, checked against the CPU oracle on sampled outputs (the oracle
-computes each sampled output from the same seeded inputs) and by properties
-that hold at any size (every rank identical after all-reduce, gathered
-parameters equal to the generator's weights, every partition element written).
+"""The five workloads, and the discrete path on one layer, at their full sizes,
+in the launch configuration the benchmark uses, checked against the CPU oracle
+on sampled outputs (the oracle computes each sampled output from the same
+seeded inputs) and by properties that hold at any size (every rank identical
+after all-reduce, gathered parameters equal to the generator's weights, every
+partition element written).
 
 Small workloads (the 4-rank ring example and the 64-fragment bucket) are
 checked in full.
@@ -162,6 +163,63 @@ def test_zero2_grad_sync_full_size_sampled():
     del first
     sync.close()
     say("zero2: sampled outputs bit-exact; accumulation micro-step doubles exactly")
+
+
+# ------------------------------------------------ discrete path, one layer
+def test_frags_layer_discrete_full_size():
+    """The discrete reduce-scatter over one layer's seven gradients per rank,
+    at full size: sampled outputs against the oracle, every output equal to
+    flatten + contiguous reduce-scatter on the GPU, every element written."""
+    import torch
+    cfg = W.FRAGS_LAYER
+    K, sigma, shift = cfg["K"], cfg["sigma"], cfg["shift"]
+    seed = W.seed_of(cfg["seed_cfg"])
+    sizes = W.frags_layer_numels()
+    N = sum(sizes)
+    C = -(-N // K)
+    say(f"frags_layer: {K} x {len(sizes)} fragments, {N} elements per rank")
+    frags = [[torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in sizes] for _ in range(K)]
+    for r in range(K):
+        for p in range(len(sizes)):
+            synth.dev_normal_bf16(frags[r][p], seed, W.frags_layer_stream(r, p), 0, sigma)
+    parts = [torch.empty(C, dtype=torch.float32, device="cuda") for _ in range(K)]
+    for p in parts:
+        p.view(torch.int32).fill_(-1)  # NaN sentinel: every element must be written
+    zr().zr_reduce_scatter_frags(frags, sizes, N, parts, chunk_shift=shift, average=True,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for p in parts:
+        assert not bool(torch.isnan(p).any())
+    # sampled outputs: virtual index g lies in fragment p at local offset g - start_p
+    starts = np.cumsum([0] + sizes)
+    offs = sample_offsets(np.random.default_rng(6), C, 3000)
+    M = offs.size
+    X = np.zeros((K, K * M), dtype=np.uint16)
+    for j in range(K):
+        g = j * C + offs
+        ok = g < N
+        gg = np.minimum(g, N - 1)
+        frag = np.searchsorted(starts, gg, side="right") - 1
+        for r in range(K):
+            streams = np.array([W.frags_layer_stream(r, int(f)) for f in frag])
+            vals = synth.host_points_normal_bf16(seed, streams, gg - starts[frag], sigma)
+            X[r, j * M:(j + 1) * M] = np.where(ok, vals, 0)
+    want = oracle.reduce_scatter([X[r] for r in range(K)], K * M, np.float32, shift=shift,
+                                 average=True)
+    idx = torch.from_numpy(offs).cuda()
+    for q in range(K):
+        got = parts[q].index_select(0, idx).cpu().numpy()
+        assert np.array_equal(bits(got), bits(want[q])), f"rank {q}"
+    # whole outputs: the same as flattening into a bucket and reducing it
+    buckets = [torch.empty(K * C, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    zr().zr_flatten_bucket(frags, sizes, buckets, K * C)
+    del frags
+    ref = [torch.empty(C, dtype=torch.float32, device="cuda") for _ in range(K)]
+    zr().zr_reduce_scatter_avg(buckets, K * C, ref, chunk_shift=shift, average=True)
+    torch.cuda.synchronize()
+    for q in range(K):
+        assert torch.equal(parts[q].view(torch.int32), ref[q].view(torch.int32)), f"rank {q}"
+    say("frags_layer: sampled outputs bit-exact; equal to flatten + reduce-scatter")
 
 
 # ---------------------------------------------------------- zero3_ag (cfg 4)
