@@ -21,21 +21,23 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # with the same ABI); by default the in-tree build is used.
 LIB_PATH = os.environ.get("ZR_LIBRARY") or os.path.join(_HERE, "libzr.so")
 
-ZR_OK, ZR_ERR_INVALID, ZR_ERR_ALIGN, ZR_ERR_ALIAS, ZR_ERR_UNSUPPORTED, ZR_ERR_HIP = range(6)
+ZR_OK, ZR_ERR_INVALID, ZR_ERR_ALIGN, ZR_ERR_ALIAS, ZR_ERR_UNSUPPORTED, ZR_ERR_HIP, ZR_ERR_NOMEM = range(7)
 ZR_BF16, ZR_FP32 = 0, 1
 ZR_ORDER_RING, ZR_ORDER_FREE, ZR_ORDER_RING_WIRE = 0, 1, 2
 ZR_AVERAGE, ZR_ACCUMULATE = 1, 2
 STATUS_NAMES = {0: "ZR_OK", 1: "ZR_ERR_INVALID", 2: "ZR_ERR_ALIGN", 3: "ZR_ERR_ALIAS",
-                4: "ZR_ERR_UNSUPPORTED", 5: "ZR_ERR_HIP"}
+                4: "ZR_ERR_UNSUPPORTED", 5: "ZR_ERR_HIP", 6: "ZR_ERR_NOMEM"}
 
 COST_EXPORTS = ("zr_cost_ring_allreduce", "zr_cost_ring_reduce_scatter", "zr_cost_tree_allreduce",
                 "zr_cost_naive_allreduce", "zr_cost_pipelined_broadcast",
                 "zr_cost_best_broadcast_segments", "zr_cost_ring_tree_crossover",
                 "zr_cost_ring_naive_crossover", "zr_cost_dp_speedup")
+PF_EXPORTS = ("zr_pf_create", "zr_pf_fetch", "zr_pf_release", "zr_pf_full", "zr_pf_get_stats",
+              "zr_pf_destroy", "zr_pf_plan")
 EXPORTS = ("zr_last_error", "zr_version", "zr_flatten_bucket", "zr_reduce_scatter_avg",
            "zr_reduce_scatter_frags", "zr_all_gather", "zr_allreduce", "zr_plan_buckets", "zr_sched_create",
            "zr_sched_acquire", "zr_sched_submit_rs", "zr_sched_flush",
-           "zr_sched_destroy") + COST_EXPORTS
+           "zr_sched_destroy") + COST_EXPORTS + PF_EXPORTS
 
 
 class ZrError(RuntimeError):
@@ -47,6 +49,30 @@ class ZrError(RuntimeError):
 class zr_seg(ctypes.Structure):
     _fields_ = [("shard_off", ctypes.c_int64), ("full_off", ctypes.c_int64),
                 ("numel", ctypes.c_int64)]
+
+
+class zr_pf_config(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int), ("dtype", ctypes.c_int), ("n_params", ctypes.c_int),
+                ("numels", ctypes.POINTER(ctypes.c_int64)),
+                ("shard_offsets", ctypes.POINTER(ctypes.c_int64)),
+                ("shards", ctypes.POINTER(ctypes.c_void_p)),
+                ("arenas", ctypes.POINTER(ctypes.c_void_p)),
+                ("arena_numel", ctypes.c_int64), ("chunk_shift", ctypes.c_int),
+                ("n_steps", ctypes.c_int), ("step_offsets", ctypes.POINTER(ctypes.c_int32)),
+                ("step_params", ctypes.POINTER(ctypes.c_int32)),
+                ("prefetch_bucket_numel", ctypes.c_int64), ("max_live_numel", ctypes.c_int64),
+                ("max_reuse_numel", ctypes.c_int64),
+                ("max_ongoing_fetches", ctypes.c_int), ("gather_stream", ctypes.c_void_p),
+                ("compute_stream", ctypes.c_void_p)]
+
+
+PF_STAT_FIELDS = ("gathers", "immediate_gathers", "immediate_numel", "prefetch_numel", "host_syncs",
+                  "stream_waits", "live", "peak_live", "peak_ongoing", "arena_peak",
+                  "prefetch_trimmed", "retained")
+
+
+class zr_pf_stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in PF_STAT_FIELDS]
 
 
 _lib = None
@@ -78,6 +104,14 @@ def lib() -> ctypes.CDLL:
                                          _i32, _i32, _i32]
         L.zr_sched_flush.argtypes = [_vp, _vp]
         L.zr_sched_destroy.argtypes = [_vp]
+        _cfgp = ctypes.POINTER(zr_pf_config)
+        L.zr_pf_create.argtypes = [_cfgp, ctypes.POINTER(_vp)]
+        L.zr_pf_fetch.argtypes = [_vp, _i32]
+        L.zr_pf_release.argtypes = [_vp, _i32]
+        L.zr_pf_full.argtypes = [_vp, _i32, _i32, ctypes.POINTER(_vp)]
+        L.zr_pf_get_stats.argtypes = [_vp, ctypes.POINTER(zr_pf_stats)]
+        L.zr_pf_destroy.argtypes = [_vp]
+        L.zr_pf_plan.argtypes = [_cfgp, _i32, ctypes.POINTER(zr_pf_stats)]
         for f in EXPORTS[2:]:
             getattr(L, f).restype = ctypes.c_int
         _d = ctypes.c_double
@@ -317,6 +351,110 @@ class Sched:
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:
             lib().zr_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---------------------------------------------------- prefetch coordinator
+def _pf_config(K, dtype, numels, steps, prefetch_bucket_numel, max_live_numel, arena_numel,
+               max_ongoing_fetches=2, max_reuse_numel=0, shard_offsets=None, shards=None,
+               arenas=None, chunk_shift=0, gather_stream=None, compute_stream=None):
+    """zr_pf_config plus the arrays it points to (kept alive with it).
+    steps: one list of parameter ids per step, in trace order."""
+    offs, flat = [0], []
+    for st in steps:
+        flat.extend(int(p) for p in st)
+        offs.append(len(flat))
+    keep = {
+        "numels": _int64s(numels),
+        "step_offsets": (ctypes.c_int32 * len(offs))(*offs),
+        "step_params": (ctypes.c_int32 * max(1, len(flat)))(*flat),
+    }
+    c = zr_pf_config()
+    c.K, c.dtype, c.n_params = K, _dtype(dtype), len(numels)
+    c.numels = keep["numels"]
+    if shard_offsets is not None:
+        keep["shard_offsets"] = _int64s(shard_offsets)
+        c.shard_offsets = keep["shard_offsets"]
+    if shards is not None:
+        keep["shards"] = _table(shards)
+        c.shards = keep["shards"]
+    if arenas is not None:
+        keep["arenas"] = _table(arenas)
+        c.arenas = keep["arenas"]
+    c.arena_numel, c.chunk_shift = arena_numel, chunk_shift
+    c.n_steps = len(steps)
+    c.step_offsets, c.step_params = keep["step_offsets"], keep["step_params"]
+    c.prefetch_bucket_numel, c.max_live_numel = prefetch_bucket_numel, max_live_numel
+    c.max_reuse_numel = max_reuse_numel
+    c.max_ongoing_fetches = max_ongoing_fetches
+    c.gather_stream = _stream(gather_stream) if gather_stream is not None or shards is not None else None
+    c.compute_stream = _stream(compute_stream) if compute_stream is not None or shards is not None else None
+    c._keep = keep
+    return c
+
+
+def _stats_dict(st: zr_pf_stats) -> dict:
+    return {n: getattr(st, n) for n in PF_STAT_FIELDS}
+
+
+def zr_pf_plan(numels: Sequence[int], steps: Sequence[Sequence[int]], prefetch_bucket_numel: int,
+               max_live_numel: int, arena_numel: int, max_ongoing_fetches: int = 2,
+               max_reuse_numel: int = 0, iterations: int = 1, K: int = 8, dtype=ZR_BF16) -> dict:
+    """Host-only run of the trace (gathers finish at once): the counters a
+    coordinator with this config reaches, e.g. peak live elements and the
+    arena peak, to size an arena."""
+    c = _pf_config(K, dtype, numels, steps, prefetch_bucket_numel, max_live_numel, arena_numel,
+                   max_ongoing_fetches, max_reuse_numel)
+    st = zr_pf_stats()
+    _check(lib().zr_pf_plan(ctypes.byref(c), iterations, ctypes.byref(st)))
+    return _stats_dict(st)
+
+
+class Prefetcher:
+    """zr_pf_*: ZeRO-3 fetch / prefetch of full parameters into per-rank
+    arenas, gathers on `gather_stream`, consumers on `compute_stream`."""
+
+    def __init__(self, numels: Sequence[int], shard_offsets: Sequence[int], shards: Sequence,
+                 arenas: Sequence, arena_numel: int, steps: Sequence[Sequence[int]],
+                 prefetch_bucket_numel: int, max_live_numel: int, max_ongoing_fetches: int = 2,
+                 max_reuse_numel: int = 0, chunk_shift: int = 0, gather_stream=None,
+                 compute_stream=None, dtype=None):
+        self.K = len(shards)
+        self.n_steps = len(steps)
+        dt = dtype if dtype is not None else shards[0]
+        self._cfg = _pf_config(self.K, dt, numels, steps, prefetch_bucket_numel, max_live_numel,
+                               arena_numel, max_ongoing_fetches, max_reuse_numel, shard_offsets,
+                               shards, arenas, chunk_shift, gather_stream, compute_stream)
+        h = ctypes.c_void_p()
+        _check(lib().zr_pf_create(ctypes.byref(self._cfg), ctypes.byref(h)))
+        self._h = h
+
+    def fetch(self, step: int) -> None:
+        _check(lib().zr_pf_fetch(self._h, step))
+
+    def release(self, step: int) -> None:
+        _check(lib().zr_pf_release(self._h, step))
+
+    def full(self, param: int, rank: int) -> int:
+        """Device address of a live parameter's full copy on `rank`."""
+        p = ctypes.c_void_p()
+        _check(lib().zr_pf_full(self._h, param, rank, ctypes.byref(p)))
+        return p.value
+
+    def stats(self) -> dict:
+        st = zr_pf_stats()
+        _check(lib().zr_pf_get_stats(self._h, ctypes.byref(st)))
+        return _stats_dict(st)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().zr_pf_destroy(self._h)
             self._h = None
 
     def __del__(self):

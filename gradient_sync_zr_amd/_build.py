@@ -29,7 +29,7 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=
          "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 SOURCES = ["zr_rs.hip", "zr_rsf.hip", "zr_ar.hip", "zr_ag.hip", "zr_flatten.hip", "zr_abi.cpp", "zr_sched.cpp",
-           "zr_cost.cpp"]
+           "zr_prefetch.cpp", "zr_cost.cpp"]
 
 
 _REMARK = re.compile(r"remark:\s+(Function Name: (\S+)|ScratchSize \[bytes/lane\]: (\d+))")

@@ -212,6 +212,60 @@ zr_status validate_ag(int K, const void* const* shards, void* const* fulls, zr_d
     return ok();
 }
 
+// The prefetch coordinator's configuration; `buffers` also checks the shard
+// and arena tables (zr_pf_plan needs only the sizes and the trace).
+zr_status validate_pf(const zr_pf_config* c, bool buffers) {
+    if (!c) return fail(ZR_ERR_INVALID, "config is NULL");
+    ZR_TRY(check_k(c->K));
+    if (!dt_valid(c->dtype)) return fail(ZR_ERR_UNSUPPORTED, "dtype %d not supported", (int)c->dtype);
+    if (c->n_params < 1) return fail(ZR_ERR_INVALID, "n_params=%d < 1", c->n_params);
+    if (!c->numels) return fail(ZR_ERR_INVALID, "numels is NULL");
+    for (int p = 0; p < c->n_params; ++p)
+        if (c->numels[p] < 1 || c->numels[p] > kMaxElems)
+            return fail(ZR_ERR_INVALID, "numels[%d]=%lld not in [1, 2^40]", p, (long long)c->numels[p]);
+    if (c->arena_numel < 1 || c->arena_numel > kMaxElems)
+        return fail(ZR_ERR_INVALID, "arena_numel=%lld not in [1, 2^40]", (long long)c->arena_numel);
+    if (c->chunk_shift < 0 || c->chunk_shift >= c->K)
+        return fail(ZR_ERR_INVALID, "chunk_shift=%d not in [0, %d)", c->chunk_shift, c->K);
+    if (c->n_steps < 1) return fail(ZR_ERR_INVALID, "n_steps=%d < 1", c->n_steps);
+    if (!c->step_offsets) return fail(ZR_ERR_INVALID, "step_offsets is NULL");
+    if (c->step_offsets[0] != 0) return fail(ZR_ERR_INVALID, "step_offsets[0] is not 0");
+    for (int t = 0; t < c->n_steps; ++t)
+        if (c->step_offsets[t + 1] < c->step_offsets[t])
+            return fail(ZR_ERR_INVALID, "step_offsets decrease at step %d", t);
+    const int total = c->step_offsets[c->n_steps];
+    if (total > 0 && !c->step_params) return fail(ZR_ERR_INVALID, "step_params is NULL");
+    for (int i = 0; i < total; ++i)
+        if (c->step_params[i] < 0 || c->step_params[i] >= c->n_params)
+            return fail(ZR_ERR_INVALID, "step_params[%d]=%d not a parameter id", i, c->step_params[i]);
+    if (c->prefetch_bucket_numel < 1) return fail(ZR_ERR_INVALID, "prefetch_bucket_numel < 1");
+    if (c->max_live_numel < 1) return fail(ZR_ERR_INVALID, "max_live_numel < 1");
+    if (c->max_reuse_numel < 0) return fail(ZR_ERR_INVALID, "max_reuse_numel < 0");
+    if (c->max_ongoing_fetches < 1 || c->max_ongoing_fetches > 64)
+        return fail(ZR_ERR_INVALID, "max_ongoing_fetches=%d not in [1, 64]", c->max_ongoing_fetches);
+    if (!buffers) return ok();
+    const int K = c->K;
+    const int64_t es = dt_bytes(c->dtype);
+    if (!c->shard_offsets) return fail(ZR_ERR_INVALID, "shard_offsets is NULL");
+    int64_t lo = INT64_MAX, hi = 0;
+    for (int p = 0; p < c->n_params; ++p) {
+        if (c->shard_offsets[p] < 0 || c->shard_offsets[p] > kMaxElems)
+            return fail(ZR_ERR_INVALID, "shard_offsets[%d] out of range", p);
+        lo = std::min(lo, c->shard_offsets[p]);
+        hi = std::max(hi, c->shard_offsets[p] + (c->numels[p] + K - 1) / K);
+    }
+    ZR_TRY(check_table(c->shards, K, es, "shards"));
+    ZR_TRY(check_table(const_cast<const void* const*>(c->arenas), K, es, "arenas"));
+    std::vector<Range> ra(K), rs(K);
+    for (int r = 0; r < K; ++r) {
+        ra[r] = range_of(c->arenas[r], c->arena_numel, es);
+        rs[r] = Range{(uintptr_t)c->shards[r] + (uintptr_t)(lo * es), (uintptr_t)c->shards[r] + (uintptr_t)(hi * es)};
+    }
+    ZR_TRY(check_distinct(ra, "arenas"));
+    ZR_TRY(check_disjoint(ra, "arenas", rs, "shards"));
+    return ok();
+}
+
 zr_status run_ag(int K, const void* const* shards, void* const* fulls, zr_dtype dt, const zr_seg* segs,
                  int n_segs, int shift, hipStream_t stream) {
     ConstPtrs sp{};

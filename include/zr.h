@@ -19,7 +19,8 @@
  *          SUM / world size).
  *  [ZERO3] "DeepSpeed ZeRO-3 源码解析：前向与反向": 1 (data-flow overview:
  *          bucket -> reduce -> partition copy -> single bf16->fp32 cast),
- *          2.1/2.2 (parameter all-gather in prefetch buckets), 3.1/3.2
+ *          2.1/2.2 (parameter fetch and prefetch, its two caps and the
+ *          limit on queued fetches), 2.4 (conservative release), 3.1/3.2
  *          (bucketing, contiguous flat buffer), 5.1-5.4 (bucket insert,
  *          reduce paths, partition write, epilogue).
  *  [ISSUE] "ZeRO-1/2 average_tensor serializes backward compute behind the
@@ -66,7 +67,8 @@ typedef enum {
     ZR_ERR_ALIGN = 2,       /* pointer not aligned to its element size */
     ZR_ERR_ALIAS = 3,       /* overlapping buffers that must not overlap */
     ZR_ERR_UNSUPPORTED = 4, /* dtype or dtype pair not supported */
-    ZR_ERR_HIP = 5          /* a HIP runtime call or launch failed */
+    ZR_ERR_HIP = 5,         /* a HIP runtime call or launch failed */
+    ZR_ERR_NOMEM = 6        /* a caller-provided arena cannot hold what must be live */
 } zr_status;
 
 typedef enum { ZR_BF16 = 0, ZR_FP32 = 1 } zr_dtype;
@@ -278,6 +280,104 @@ zr_status zr_sched_submit_rs(zr_sched* s, int buf, void* const* producer_streams
                              int flags /* as zr_reduce_scatter_avg */, zr_order order);
 zr_status zr_sched_flush(zr_sched* s, void* caller_stream);
 zr_status zr_sched_destroy(zr_sched* s);
+
+/* ------------------------------------------------- prefetch coordinator
+ * ZeRO-3 parameter fetch and prefetch [ZERO3 2.1, 2.2]. Full parameters are
+ * gathered from their 1/K shards (zr_all_gather's layout) into a caller-
+ * provided arena per rank, only while they are live.
+ *
+ * The trace is fixed: step t (a module visit; forward then backward) uses
+ * parameters step_params[step_offsets[t] .. step_offsets[t+1]). Per step:
+ *   zr_pf_fetch(t): (1) gathers, on gather_stream, every parameter of step t
+ *       that is not live; (2) makes compute_stream wait for the gathers that
+ *       produce step t's parameters (none for gathers the host has seen
+ *       finish); (3) prefetches: walks the trace after step t, skips live
+ *       parameters, and gathers the others as one batch, stopping once the
+ *       batch reaches min(max_live_numel - live, prefetch_bucket_numel)
+ *       elements (the parameter that crosses the cap is included; nothing
+ *       is prefetched while live >= max_live_numel). `live` is the element
+ *       count of every gathered or in-flight full parameter.
+ *   (the caller enqueues step t's compute on compute_stream, reading the
+ *       addresses from zr_pf_full)
+ *   zr_pf_release(t): step t's parameters stop being live, except those
+ *       used again within max_reuse_numel elements of parameters after step
+ *       t (the steps after t are scanned in order, a step at a time, until
+ *       the parameters seen reach max_reuse_numel; the scan stays within this
+ *       pass of the trace) [ZERO3 2.4]; the arena ranges of released
+ *       parameters are reused only after compute_stream has passed this
+ *       point.
+ * At most max_ongoing_fetches gathers are outstanding (the page's value is
+ * 2): before a new gather the host drops finished ones and blocks on the
+ * oldest until fewer remain. Steps are fetched and released in trace order;
+ * after the last step is released the trace starts over at step 0. Calls out
+ * of order are ZR_ERR_INVALID.
+ *
+ * Arena: arena_numel elements in every rank's buffer, handed out first-fit
+ * in 256-byte-aligned ranges at the same offsets on every rank. It must hold
+ * every single step's parameters (checked at create, else ZR_ERR_NOMEM).
+ * A prefetch that does not fit is cut to the part that fits; a step whose
+ * parameters cannot be placed fails with ZR_ERR_NOMEM. Sizing: max_live_numel
+ * plus the largest step and the largest parameter is enough without
+ * fragmentation; zr_pf_plan reports the exact peak for a trace.
+ * gather_stream == compute_stream runs gathers and compute in series (no
+ * overlap). The coordinator owns its HIP events and its copy of the trace;
+ * it keeps the shard, arena and stream handles; it is not thread-safe.
+ */
+typedef struct zr_pf zr_pf;
+
+typedef struct {
+    int K;                         /* ranks, 1..ZR_MAX_RANKS */
+    zr_dtype dtype;
+    int n_params;
+    const int64_t* numels;         /* [n_params] full sizes, each >= 1 */
+    const int64_t* shard_offsets;  /* [n_params] offset of each shard in every
+                                      rank's shard buffer */
+    const void* const* shards;     /* [K] shard buffers; parameter p's shard
+                                      holds ceil(numels[p] / K) elements */
+    void* const* arenas;           /* [K] arena buffers of arena_numel elements */
+    int64_t arena_numel;
+    int chunk_shift;               /* rank r holds chunk (r + s) mod K; ZeRO-3: 0 */
+    int n_steps;
+    const int32_t* step_offsets;   /* [n_steps + 1], step_offsets[0] = 0 */
+    const int32_t* step_params;    /* parameter ids, trace order */
+    int64_t prefetch_bucket_numel; /* >= 1 */
+    int64_t max_live_numel;        /* >= 1 */
+    int64_t max_reuse_numel;       /* conservative-release window, >= 0 */
+    int max_ongoing_fetches;       /* >= 1 */
+    void* gather_stream;           /* hipStream_t */
+    void* compute_stream;          /* hipStream_t */
+} zr_pf_config;
+
+typedef struct {
+    int64_t gathers;            /* gather batches issued */
+    int64_t immediate_gathers;  /* batches of part (1): parameters not prefetched */
+    int64_t immediate_numel;
+    int64_t prefetch_numel;
+    int64_t host_syncs;         /* host blocked on the oldest gather */
+    int64_t stream_waits;       /* compute_stream waits on a gather */
+    int64_t live;               /* elements live now */
+    int64_t peak_live;
+    int64_t peak_ongoing;       /* most gathers outstanding at once */
+    int64_t arena_peak;         /* highest arena element offset used */
+    int64_t prefetch_trimmed;   /* prefetches cut short by a full arena */
+    int64_t retained;           /* releases skipped: the parameter is reused soon */
+} zr_pf_stats;
+
+/* Validates the whole config (buffers distinct and disjoint from the shard
+ * ranges, trace ids in range) and creates the coordinator's events. */
+zr_status zr_pf_create(const zr_pf_config* cfg, zr_pf** out);
+zr_status zr_pf_fetch(zr_pf* pf, int step);
+zr_status zr_pf_release(zr_pf* pf, int step);
+/* Device address of live parameter `param` in rank `rank`'s arena;
+ * ZR_ERR_INVALID when it is not live. */
+zr_status zr_pf_full(const zr_pf* pf, int param, int rank, void** full);
+zr_status zr_pf_get_stats(const zr_pf* pf, zr_pf_stats* out);
+zr_status zr_pf_destroy(zr_pf* pf);
+/* Host only (no GPU): runs the trace `iterations` times through the same
+ * coordinator with gathers that finish at once, and reports the resulting
+ * counters (peak live elements, arena peak, ...). Uses only the sizes, the
+ * trace, the caps and arena_numel of cfg; pointers and streams may be NULL. */
+zr_status zr_pf_plan(const zr_pf_config* cfg, int iterations, zr_pf_stats* out);
 
 #ifdef __cplusplus
 }

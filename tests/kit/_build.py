@@ -1,4 +1,4 @@
-"""Build the test kit: libsched_sim.so (g++) and libtestkit.so (hipcc, gfx950)."""
+"""Build the test kit: libsched_sim.so and libpf_sim.so (g++), libtestkit.so (hipcc, gfx950)."""
 import os
 import subprocess
 
@@ -12,6 +12,9 @@ def build(verbose: bool = False):
         ["g++", "-O1", "-std=c++17", "-fPIC", "-shared", "-Wall",
          "-I", os.path.join(ROOT, "gradient_sync_zr_amd", "csrc"),
          "-o", os.path.join(HERE, "libsched_sim.so"), os.path.join(HERE, "sched_sim.cpp")],
+        ["g++", "-O1", "-std=c++17", "-fPIC", "-shared", "-Wall",
+         "-I", os.path.join(ROOT, "gradient_sync_zr_amd", "csrc"),
+         "-o", os.path.join(HERE, "libpf_sim.so"), os.path.join(HERE, "pf_sim.cpp")],
         [HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-o", os.path.join(HERE, "libtestkit.so"), os.path.join(HERE, "testkit.hip")],
