@@ -263,6 +263,138 @@ def bench_zero3(args):
     }
 
 
+# --------------------------------------------------------- zero3_prefetch
+def kit_delay():
+    """delay(us, stream): the test kit's bounded wall-clock spin kernel, a
+    stand-in for a module's compute, calibrated against events on the device."""
+    import ctypes
+
+    import torch
+    L = ctypes.CDLL(os.path.join(ROOT, "tests", "kit", "libtestkit.so"))
+    L.tk_delay.argtypes = [ctypes.c_longlong, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_void_p]
+    L.tk_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int)]
+    khz = ctypes.c_int(0)
+    if L.tk_clock_khz(ctypes.byref(khz)) != 0 or khz.value <= 0:
+        raise RuntimeError("wall clock rate unavailable")
+    s = torch.cuda.current_stream()
+    nominal = 2 * khz.value  # 2 ms at the reported rate
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = []
+    for _ in range(3):
+        e0.record(s)
+        L.tk_delay(nominal, 50_000_000, None, s.cuda_stream)
+        e1.record(s)
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    ticks_per_us = nominal / (sorted(ms)[1] * 1e3)
+
+    def delay(us, stream):
+        if L.tk_delay(int(us * ticks_per_us), 50_000_000, None, stream.cuda_stream) != 0:
+            raise RuntimeError("delay launch failed")
+    return delay
+
+
+def bench_zero3_prefetch(args):
+    """The ZeRO-3 fetch/prefetch coordinator on workload 4's full trace
+    (forward then backward, one parameter per module visit) with a synthetic
+    compute stream: each step's compute is a spin of `compute_ratio` times
+    that step's all-gather time at the measured gather rate."""
+    import torch
+
+    import synth
+    import gradient_sync_zr_amd as zr
+    from synth import workloads as W
+
+    cfg = W.ZERO3
+    K, sigma, shift = cfg["K"], cfg["sigma"], cfg["shift"]
+    seed = W.seed_of(4)
+    numels = [p.numel for p in W.llama_like_params()]
+    steps = W.zero3_trace(len(numels))
+    offs, soff = [], 0
+    for n in numels:
+        offs.append(soff)
+        soff += -(-n // K)
+    shards = [torch.zeros(soff, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    for p, n in enumerate(numels):
+        C = -(-n // K)
+        for r in range(K):
+            j = (r + shift) % K
+            cnt = max(0, min(C, n - j * C))
+            if cnt:
+                synth.dev_normal_bf16(shards[r][offs[p]:offs[p] + cnt], seed, p, j * C, sigma)
+    bucket = cfg["prefetch_bytes"] // cfg["elem_bytes"]
+    caps = dict(prefetch_bucket_numel=bucket, max_live_numel=cfg["max_live"],
+                max_reuse_numel=cfg["max_reuse"], max_ongoing_fetches=cfg["max_ongoing"])
+    arena = args.arena_numel
+    plan = zr.zr_pf_plan(numels, steps, bucket, cfg["max_live"], arena,
+                         max_ongoing_fetches=cfg["max_ongoing"], max_reuse_numel=cfg["max_reuse"])
+    arenas = [torch.empty(arena, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    gs, cs = torch.cuda.Stream(), torch.cuda.Stream()
+    delay = kit_delay()
+    # the gather rate, from one gathers-only pass (kernel time on the gather stream)
+    visit_numel = sum(numels[p] for st in steps for p in st)
+
+    def walk(serial=False, compute_us=None, gathers=True, passes=1):
+        pf = zr.Prefetcher(numels, offs, shards, arenas, arena, steps, chunk_shift=shift,
+                           gather_stream=cs if serial else gs, compute_stream=cs,
+                           **caps) if gathers else None
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(passes):
+            for t in range(len(steps)):
+                if pf:
+                    pf.fetch(t)
+                if compute_us is not None:
+                    delay(compute_us[t], cs)
+                if pf:
+                    pf.release(t)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / passes
+        st = pf.stats() if pf else None
+        if pf:
+            pf.close()
+        return ms, st
+
+    passes = max(1, min(args.steps, 5))
+    walk()  # warm-up
+    ms_gather, st_g = walk(passes=passes)
+    gathered = (st_g["prefetch_numel"] + st_g["immediate_numel"]) / passes
+    gather_bytes = gathered * 2 * (K + 1)      # shard read once + K full copies
+    rate = gather_bytes / (ms_gather * 1e-3)   # bytes per second, host loop included
+    compute_us = [args.compute_ratio * sum(numels[p] for p in st) * 2 * (K + 1) / rate * 1e6
+                  for st in steps]
+    ms_compute, _ = walk(compute_us=compute_us, gathers=False, passes=passes)
+    ms_overlap, st = walk(compute_us=compute_us, passes=passes)
+    ms_serial, _ = walk(serial=True, compute_us=compute_us, passes=passes)
+    exposed = max(0.0, ms_overlap - ms_compute)
+    return {
+        "metric": "ZeRO-3 fetch/prefetch: ms per forward+backward pass with the gathers "
+                  "overlapped, K=8, 6.74B-param transformer",
+        "value": round(ms_overlap, 3), "unit": "ms", "n_gpus": 1, "steps": passes,
+        "warmup": 1, "ms_per_step": round(ms_overlap, 3), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded generator, bf16 ~N(0,0.02); compute is a calibrated spin",
+        "serial_ms": round(ms_serial, 3), "compute_only_ms": round(ms_compute, 3),
+        "gathers_only_ms": round(ms_gather, 3),
+        "exposed_gather_ms": round(exposed, 3),
+        "hidden_fraction": round(1.0 - exposed / ms_gather, 4),
+        "gathers_only_GBps": round(rate / 1e9, 1),
+        "coordinator": {k: st[k] // (passes if k in ("gathers", "immediate_gathers",
+                                                     "immediate_numel", "prefetch_numel",
+                                                     "host_syncs", "stream_waits", "retained",
+                                                     "prefetch_trimmed") else 1)
+                        for k in st},
+        "plan_arena_peak": plan["arena_peak"],
+        "config": {"workload": "zero3_prefetch: 226 params (32 layers, hidden 4096, FFN 11008, "
+                               "vocab 32000), 452 module visits per pass, 1/8 shards",
+                   "K": K, "prefetch_bucket_numel": bucket, "max_live_numel": cfg["max_live"],
+                   "max_reuse_numel": cfg["max_reuse"], "max_ongoing_fetches": cfg["max_ongoing"],
+                   "arena_numel": arena, "compute_ratio": args.compute_ratio,
+                   "gathered_numel_per_pass": int(gathered), "visit_numel_per_pass": visit_numel},
+        "roofline": None, "cpu_baseline": None,
+    }
+
+
 # ------------------------------------------------------------ allreduce64
 def bench_allreduce64(args):
     import torch
@@ -455,9 +587,13 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="zero2",
-                    choices=["zero2", "zero2_accum", "zero3_ag", "allreduce64", "flatten8",
-                             "frags_layer"])
+                    choices=["zero2", "zero2_accum", "zero3_ag", "zero3_prefetch", "allreduce64",
+                             "flatten8", "frags_layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--compute-ratio", type=float, default=1.5,
+                    help="zero3_prefetch: each step's synthetic compute, in units of its gather time")
+    ap.add_argument("--arena-numel", type=int, default=1_600_000_000,
+                    help="zero3_prefetch: arena elements per rank")
     ap.add_argument("--cpu-sample-elems", type=int, default=0,
                     help="element indices in the CPU-baseline sample (default: all of bucket 0)")
     args = ap.parse_args()
@@ -471,7 +607,8 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     fn = {"zero2": bench_zero2, "zero2_accum": lambda a: bench_zero2(a, accumulate=True),
-          "zero3_ag": bench_zero3, "allreduce64": bench_allreduce64,
+          "zero3_ag": bench_zero3, "zero3_prefetch": bench_zero3_prefetch,
+          "allreduce64": bench_allreduce64,
           "flatten8": bench_flatten8, "frags_layer": bench_frags_layer}[args.workload]
     print(json.dumps(fn(args)), flush=True)
 

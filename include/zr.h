@@ -312,13 +312,17 @@ zr_status zr_sched_destroy(zr_sched* s);
  * after the last step is released the trace starts over at step 0. Calls out
  * of order are ZR_ERR_INVALID.
  *
- * Arena: arena_numel elements in every rank's buffer, handed out first-fit
- * in 256-byte-aligned ranges at the same offsets on every rank. It must hold
- * every single step's parameters (checked at create, else ZR_ERR_NOMEM).
- * A prefetch that does not fit is cut to the part that fits; a step whose
- * parameters cannot be placed fails with ZR_ERR_NOMEM. Sizing: max_live_numel
- * plus the largest step and the largest parameter is enough without
- * fragmentation; zr_pf_plan reports the exact peak for a trace.
+ * Arena: arena_numel elements in every rank's buffer, handed out in
+ * 256-byte-aligned ranges at the same offsets on every rank. A gather takes
+ * the free range released longest ago (never-used memory first), so it waits
+ * only for the compute that last read that memory; a larger arena is used
+ * whole before memory is reused. It must hold every single step's
+ * parameters (checked at create, else ZR_ERR_NOMEM). A prefetch that does
+ * not fit is cut to the part that fits; a step whose parameters cannot be
+ * placed fails with ZR_ERR_NOMEM. Sizing: max_live_numel plus the largest
+ * step and the largest parameter, plus room for fragmentation; zr_pf_plan
+ * runs a trace on the host and reports whether a capacity works (no
+ * ZR_ERR_NOMEM) and how many prefetches it trims.
  * gather_stream == compute_stream runs gathers and compute in series (no
  * overlap). The coordinator owns its HIP events and its copy of the trace;
  * it keeps the shard, arena and stream handles; it is not thread-safe.

@@ -85,7 +85,15 @@ def llama_like_params(layers: int = 32, hidden: int = 4096, ffn: int = 11008,
     return ps
 
 
-ZERO3 = dict(id=4, K=8, sigma=0.02, shift=0, prefetch_bytes=50_000_000, elem_bytes=2)
+ZERO3 = dict(id=4, K=8, sigma=0.02, shift=0, prefetch_bytes=50_000_000, elem_bytes=2,
+             max_live=1_000_000_000, max_reuse=1_000_000_000, max_ongoing=2)
+
+
+def zero3_trace(n_params: int) -> List[List[int]]:
+    """One parameter per module visit: forward in order, then backward in
+    reverse order."""
+    fwd = [[p] for p in range(n_params)]
+    return fwd + fwd[::-1]
 
 # ------------------------------------------------------------------ cfg 5
 ALLREDUCE64 = dict(id=5, K=64, N=1_000_000_007, sigma=1.0, outlier_p=0.01, outlier_mag=1e4)
