@@ -565,8 +565,12 @@ def bench_flatten8(args):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e6 / args.steps
 
+    plan = zr.RsfPlan(fp, sizes, P, pp, chunk_shift=1, average=True, in_dtype=torch.bfloat16,
+                      out_dtype=torch.float32)
     us = wall_us(step)
     us_discrete = wall_us(step_discrete)
+    us_plan = wall_us(plan.launch)
+    plan.close()
     return {
         "metric": "flatten + reduce-scatter-avg microseconds per bucket, K=8, 64 fragments",
         "value": round(us, 2), "unit": "us", "n_gpus": 1, "steps": args.steps,
@@ -574,6 +578,7 @@ def bench_flatten8(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic: seeded generator, bf16 ~N(0,1e-3)",
         "discrete_path_us": round(us_discrete, 2),
+        "discrete_plan_us": round(us_plan, 2),
         "config": {"workload": f"flatten8: K=8, 64 log-uniform fragments ({sum(sizes)} elements), "
                                f"bucket padded to {P}, then RS + /8 + fp32 cast (cache-resident, "
                                "launch-bound)", "K": K},

@@ -32,12 +32,13 @@ COST_EXPORTS = ("zr_cost_ring_allreduce", "zr_cost_ring_reduce_scatter", "zr_cos
                 "zr_cost_naive_allreduce", "zr_cost_pipelined_broadcast",
                 "zr_cost_best_broadcast_segments", "zr_cost_ring_tree_crossover",
                 "zr_cost_ring_naive_crossover", "zr_cost_dp_speedup")
+RSF_PLAN_EXPORTS = ("zr_rsf_plan_create", "zr_rsf_plan_launch", "zr_rsf_plan_destroy")
 PF_EXPORTS = ("zr_pf_create", "zr_pf_fetch", "zr_pf_release", "zr_pf_full", "zr_pf_get_stats",
               "zr_pf_destroy", "zr_pf_plan")
 EXPORTS = ("zr_last_error", "zr_version", "zr_flatten_bucket", "zr_reduce_scatter_avg",
            "zr_reduce_scatter_frags", "zr_all_gather", "zr_allreduce", "zr_plan_buckets", "zr_sched_create",
            "zr_sched_acquire", "zr_sched_submit_rs", "zr_sched_flush",
-           "zr_sched_destroy") + COST_EXPORTS + PF_EXPORTS
+           "zr_sched_destroy") + COST_EXPORTS + PF_EXPORTS + RSF_PLAN_EXPORTS
 
 
 class ZrError(RuntimeError):
@@ -104,6 +105,10 @@ def lib() -> ctypes.CDLL:
                                          _i32, _i32, _i32]
         L.zr_sched_flush.argtypes = [_vp, _vp]
         L.zr_sched_destroy.argtypes = [_vp]
+        L.zr_rsf_plan_create.argtypes = [_i32, _i32, _PP, ctypes.POINTER(_i64), _i64, _i32, _PP, _i32,
+                                         _i32, _i32, _i32, ctypes.POINTER(_vp)]
+        L.zr_rsf_plan_launch.argtypes = [_vp, _vp]
+        L.zr_rsf_plan_destroy.argtypes = [_vp]
         _cfgp = ctypes.POINTER(zr_pf_config)
         L.zr_pf_create.argtypes = [_cfgp, ctypes.POINTER(_vp)]
         L.zr_pf_fetch.argtypes = [_vp, _i32]
@@ -247,6 +252,41 @@ def zr_reduce_scatter_frags(frags: Sequence[Sequence], numels: Sequence[int], N:
     _check(lib().zr_reduce_scatter_frags(K, F, _table(flat), nums, N, in_dt, _table(outputs),
                                          out_dt, chunk_shift, _flags(average, accumulate), order,
                                          _stream(stream)))
+
+
+class RsfPlan:
+    """zr_rsf_plan_*: a discrete reduce-scatter validated and built once;
+    launch() enqueues it on a stream (torch's current one by default)."""
+
+    def __init__(self, frags: Sequence[Sequence], numels: Sequence[int], N: int, outputs: Sequence,
+                 chunk_shift: int = 1, average: bool = True, order: int = ZR_ORDER_RING,
+                 in_dtype=None, out_dtype=None, accumulate: bool = False):
+        K = len(outputs)
+        F = len(numels)
+        flat = [f for row in frags for f in row]
+        if len(flat) != K * F:
+            raise ValueError("frags must be K lists of len(numels) tensors")
+        in_dt = _dtype(in_dtype if in_dtype is not None else flat[0])
+        out_dt = _dtype(out_dtype if out_dtype is not None else outputs[0])
+        h = ctypes.c_void_p()
+        _check(lib().zr_rsf_plan_create(K, F, _table(flat), _int64s(numels), N, in_dt,
+                                        _table(outputs), out_dt, chunk_shift,
+                                        _flags(average, accumulate), order, ctypes.byref(h)))
+        self._h = h
+
+    def launch(self, stream=None) -> None:
+        _check(lib().zr_rsf_plan_launch(self._h, _stream(stream)))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().zr_rsf_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def zr_all_gather(shards: Sequence, fulls: Sequence, segs: Sequence, chunk_shift: int = 0,

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <string>
+#include <new>
 #include <vector>
 
 #include "zr.h"
@@ -409,10 +410,17 @@ zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const i
     return ok();
 }
 
-zr_status zr_reduce_scatter_frags(int K, int n_frag, const void* const* frags,
-                                  const int64_t* numels, int64_t N, zr_dtype in_dt,
-                                  void* const* out, zr_dtype out_dt, int chunk_shift, int flags,
-                                  zr_order order, void* stream) {
+}  // extern "C"
+
+namespace zr {
+namespace {
+
+// Validates a discrete reduce-scatter and builds its launches. *plan is NULL
+// (with ZR_OK) when there is nothing to do (N == 0).
+zr_status make_frags_plan(int K, int n_frag, const void* const* frags, const int64_t* numels,
+                          int64_t N, zr_dtype in_dt, void* const* out, zr_dtype out_dt,
+                          int chunk_shift, int flags, zr_order order, RsfPlan** plan) {
+    *plan = nullptr;
     ZR_TRY(check_k(K));
     if (n_frag < 0) return fail(ZR_ERR_INVALID, "n_frag=%d is negative", n_frag);
     if (N < 0) return fail(ZR_ERR_INVALID, "N=%lld is negative", (long long)N);
@@ -472,9 +480,64 @@ zr_status zr_reduce_scatter_frags(int K, int n_frag, const void* const* frags,
     }
     MutPtrs op{};
     for (int r = 0; r < K; ++r) op.p[r] = out[r];
-    hipError_t e = launch_reduce_scatter_frags(K, entries.data(), (int)entries.size(), N, in_dt, op,
-                                               out_dt, chunk_shift, flags, order, (hipStream_t)stream);
+    *plan = rsf_plan_build(K, entries.data(), (int)entries.size(), N, in_dt, op, out_dt, chunk_shift,
+                           flags, order);
+    if (!*plan) return fail(ZR_ERR_INVALID, "out of host memory");
+    return ok();
+}
+
+}  // namespace
+}  // namespace zr
+
+struct zr_rsf_plan {
+    zr::RsfPlan* plan;  // NULL: nothing to launch
+};
+
+extern "C" {
+
+zr_status zr_reduce_scatter_frags(int K, int n_frag, const void* const* frags,
+                                  const int64_t* numels, int64_t N, zr_dtype in_dt,
+                                  void* const* out, zr_dtype out_dt, int chunk_shift, int flags,
+                                  zr_order order, void* stream) {
+    RsfPlan* plan = nullptr;
+    ZR_TRY(make_frags_plan(K, n_frag, frags, numels, N, in_dt, out, out_dt, chunk_shift, flags, order,
+                           &plan));
+    if (!plan) return ok();
+    const hipError_t e = rsf_plan_launch(plan, (hipStream_t)stream);
+    rsf_plan_free(plan);
     if (e != hipSuccess) return hip_fail(e, "discrete reduce-scatter launch");
+    return ok();
+}
+
+zr_status zr_rsf_plan_create(int K, int n_frag, const void* const* frags, const int64_t* numels,
+                             int64_t N, zr_dtype in_dt, void* const* out, zr_dtype out_dt,
+                             int chunk_shift, int flags, zr_order order, zr_rsf_plan** plan) {
+    if (!plan) return fail(ZR_ERR_INVALID, "plan is NULL");
+    *plan = nullptr;
+    RsfPlan* p = nullptr;
+    ZR_TRY(make_frags_plan(K, n_frag, frags, numels, N, in_dt, out, out_dt, chunk_shift, flags, order,
+                           &p));
+    zr_rsf_plan* h = new (std::nothrow) zr_rsf_plan{p};
+    if (!h) {
+        if (p) rsf_plan_free(p);
+        return fail(ZR_ERR_INVALID, "out of host memory");
+    }
+    *plan = h;
+    return ok();
+}
+
+zr_status zr_rsf_plan_launch(const zr_rsf_plan* plan, void* stream) {
+    if (!plan) return fail(ZR_ERR_INVALID, "plan is NULL");
+    if (!plan->plan) return ok();
+    const hipError_t e = rsf_plan_launch(plan->plan, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "discrete reduce-scatter launch");
+    return ok();
+}
+
+zr_status zr_rsf_plan_destroy(zr_rsf_plan* plan) {
+    if (!plan) return ok();
+    if (plan->plan) rsf_plan_free(plan->plan);
+    delete plan;
     return ok();
 }
 

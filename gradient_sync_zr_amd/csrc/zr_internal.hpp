@@ -64,10 +64,14 @@ hipError_t launch_allreduce_fused(int K, const ConstPtrs& in, const MutPtrs& out
 hipError_t launch_all_gather(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype dt,
                              const zr_seg* segs, int n_segs, int shift, hipStream_t stream);
 
-// Discrete reduce-scatter over fragment entries (any count; batched inside).
-hipError_t launch_reduce_scatter_frags(int K, const FragEntry* entries, int n_entries, int64_t N,
-                                       zr_dtype in_dt, const MutPtrs& out, zr_dtype out_dt,
-                                       int shift, int flags, zr_order order, hipStream_t stream);
+// Discrete reduce-scatter over fragment entries (any count): the launches'
+// argument blocks are built once into a plan and can be launched many times.
+// rsf_plan_build returns NULL when host memory runs out.
+struct RsfPlan;
+RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t N, zr_dtype in_dt,
+                        const MutPtrs& out, zr_dtype out_dt, int shift, int flags, zr_order order);
+hipError_t rsf_plan_launch(const RsfPlan* plan, hipStream_t stream);
+void rsf_plan_free(RsfPlan* plan);
 
 // jobs: up to kFlatJobsPerLaunch per call.
 hipError_t launch_flatten(const CopyJob* jobs, int n_jobs, int elem_bytes, hipStream_t stream);

@@ -26,6 +26,9 @@
 // back to single elements when the partition side is not quad aligned. Other
 // segments fold element by element, 1024 elements per tile. The padding entry
 // has null pointers and writes +0 (old + 0 when accumulating).
+#include <new>
+#include <vector>
+
 #include "zr_fold.hpp"
 
 namespace zr {
@@ -173,27 +176,27 @@ hipError_t launch_t(const RsfArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+using LaunchFn = hipError_t (*)(const RsfArgs&, hipStream_t);
+
 // Ring and wire order at K = 8 specialised, the rest generic (batches of
 // eight ranks in flight); fp32 input makes the wire order the ring order.
 template <typename TIn, typename TOut, int AVG>
-hipError_t pick_k(const RsfArgs& a, int order, hipStream_t s) {
-    if (order == kFree) return launch_t<TIn, TOut, 0, AVG, kFree, kRsNontemporal>(a, s);
+LaunchFn pick_k(int K, int order) {
+    if (order == kFree) return &launch_t<TIn, TOut, 0, AVG, kFree, kRsNontemporal>;
     if (order == kWire && sizeof(TIn) == 2) {
-        if (a.K == 8) return launch_t<TIn, TOut, 8, AVG, kWire, kRsNontemporal>(a, s);
-        return launch_t<TIn, TOut, 0, AVG, kWire, kRsNontemporal>(a, s);
+        if (K == 8) return &launch_t<TIn, TOut, 8, AVG, kWire, kRsNontemporal>;
+        return &launch_t<TIn, TOut, 0, AVG, kWire, kRsNontemporal>;
     }
-    switch (a.K) {
-        case 8: return launch_t<TIn, TOut, 8, AVG, kRing, kRsNontemporal>(a, s);
-        default: return launch_t<TIn, TOut, 0, AVG, kRing, kRsNontemporal>(a, s);
-    }
+    if (K == 8) return &launch_t<TIn, TOut, 8, AVG, kRing, kRsNontemporal>;
+    return &launch_t<TIn, TOut, 0, AVG, kRing, kRsNontemporal>;
 }
 
 template <typename TIn, typename TOut>
-hipError_t pick_avg(const RsfArgs& a, int avg, int order, hipStream_t s) {
+LaunchFn pick_avg(int K, int avg, int order) {
     switch (avg) {
-        case 1: return pick_k<TIn, TOut, 1>(a, order, s);
-        case 2: return pick_k<TIn, TOut, 2>(a, order, s);
-        default: return pick_k<TIn, TOut, 0>(a, order, s);
+        case 1: return pick_k<TIn, TOut, 1>(K, order);
+        case 2: return pick_k<TIn, TOut, 2>(K, order);
+        default: return pick_k<TIn, TOut, 0>(K, order);
     }
 }
 
@@ -207,9 +210,11 @@ int16_t segment_head(const uintptr_t* addr, int K, int j, uintptr_t es) {
     return (int16_t)(((128 - addr[j] % 128) % 128) / es);
 }
 
+// Cuts the entries into launches: each fills one argument block with up to
+// kRsfEntriesPerLaunch fragments (and kRsfPtrsPerLaunch rank pointers) and
+// the segments they form with the chunks.
 template <typename TIn, typename TOut>
-hipError_t launch_typed(RsfArgs& a, const FragEntry* entries, int n_entries, int avg, int order,
-                        hipStream_t stream) {
+void build_typed(RsfArgs& a, const FragEntry* entries, int n_entries, std::vector<RsfArgs>* out) {
     constexpr int64_t T = kRsTile<TIn>;
     const int K = a.K;
     const int64_t C = a.C;
@@ -218,22 +223,18 @@ hipError_t launch_typed(RsfArgs& a, const FragEntry* entries, int n_entries, int
     int m = 0;
     int64_t tiles = 0;
     a.nseg = 0;
-    auto flush = [&]() -> hipError_t {
-        if (m == 0) return hipSuccess;
+    auto flush = [&]() {
+        if (m == 0) return;
         a.tile0[a.nseg] = (int32_t)tiles;
-        hipError_t e = pick_avg<TIn, TOut>(a, avg, order, stream);
+        out->push_back(a);
         m = 0;
         tiles = 0;
         a.nseg = 0;
-        return e;
     };
     for (int ei = 0; ei < n_entries; ++ei) {
         const FragEntry& f = entries[ei];
         const int j0 = (int)(f.off / C), j1 = (int)((f.off + f.n - 1) / C);
-        if (m == max_entries || a.nseg + (j1 - j0 + 1) > kRsfSegsPerLaunch) {
-            hipError_t e = flush();
-            if (e != hipSuccess) return e;
-        }
+        if (m == max_entries || a.nseg + (j1 - j0 + 1) > kRsfSegsPerLaunch) flush();
         a.off[m] = f.off;
         a.n[m] = f.n;
         for (int r = 0; r < K; ++r) a.ptr[m * K + r] = f.ptr[r];
@@ -263,19 +264,22 @@ hipError_t launch_typed(RsfArgs& a, const FragEntry* entries, int n_entries, int
             tiles += h < 0 ? (len + kElemTile - 1) / kElemTile : (len > h ? (len - h + T - 1) / T : 1);
         }
         ++m;
-        if (tiles > INT32_MAX / 2) {
-            hipError_t e = flush();
-            if (e != hipSuccess) return e;
-        }
+        if (tiles > INT32_MAX / 2) flush();
     }
-    return flush();
+    flush();
 }
 
 }  // namespace
 
-hipError_t launch_reduce_scatter_frags(int K, const FragEntry* entries, int n_entries, int64_t N,
-                                       zr_dtype in_dt, const MutPtrs& out, zr_dtype out_dt,
-                                       int shift, int flags, zr_order order, hipStream_t stream) {
+struct RsfPlan {
+    std::vector<RsfArgs> launches;
+    LaunchFn fn = nullptr;
+};
+
+RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t N, zr_dtype in_dt,
+                        const MutPtrs& out, zr_dtype out_dt, int shift, int flags, zr_order order) {
+    RsfPlan* plan = new (std::nothrow) RsfPlan();
+    if (!plan) return nullptr;
     RsfArgs a;
     a.out = out;
     a.K = K;
@@ -288,13 +292,35 @@ hipError_t launch_reduce_scatter_frags(int K, const FragEntry* entries, int n_en
     const bool pow2 = (K & (K - 1)) == 0;
     const int avg = !(flags & ZR_AVERAGE) ? 0 : (pow2 ? 1 : 2);
     const int ord = order == ZR_ORDER_FREE ? kFree : (order == ZR_ORDER_RING_WIRE ? kWire : kRing);
-    if (in_dt == ZR_BF16 && out_dt == ZR_FP32)
-        return launch_typed<uint16_t, float>(a, entries, n_entries, avg, ord, stream);
-    if (in_dt == ZR_BF16 && out_dt == ZR_BF16)
-        return launch_typed<uint16_t, uint16_t>(a, entries, n_entries, avg, ord, stream);
-    if (in_dt == ZR_FP32 && out_dt == ZR_FP32)
-        return launch_typed<float, float>(a, entries, n_entries, avg, ord, stream);
-    return launch_typed<float, uint16_t>(a, entries, n_entries, avg, ord, stream);
+    try {
+        if (in_dt == ZR_BF16 && out_dt == ZR_FP32) {
+            build_typed<uint16_t, float>(a, entries, n_entries, &plan->launches);
+            plan->fn = pick_avg<uint16_t, float>(K, avg, ord);
+        } else if (in_dt == ZR_BF16 && out_dt == ZR_BF16) {
+            build_typed<uint16_t, uint16_t>(a, entries, n_entries, &plan->launches);
+            plan->fn = pick_avg<uint16_t, uint16_t>(K, avg, ord);
+        } else if (in_dt == ZR_FP32 && out_dt == ZR_FP32) {
+            build_typed<float, float>(a, entries, n_entries, &plan->launches);
+            plan->fn = pick_avg<float, float>(K, avg, ord);
+        } else {
+            build_typed<float, uint16_t>(a, entries, n_entries, &plan->launches);
+            plan->fn = pick_avg<float, uint16_t>(K, avg, ord);
+        }
+    } catch (...) {
+        delete plan;
+        return nullptr;
+    }
+    return plan;
 }
+
+hipError_t rsf_plan_launch(const RsfPlan* plan, hipStream_t stream) {
+    for (const RsfArgs& a : plan->launches) {
+        hipError_t e = plan->fn(a, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+void rsf_plan_free(RsfPlan* plan) { delete plan; }
 
 }  // namespace zr

@@ -168,8 +168,9 @@ zr_status zr_reduce_scatter_avg(int K, const void* const* in, zr_dtype in_dt, in
  *            fragment are zero padding
  *  out, flags, order, chunk_shift: as zr_reduce_scatter_avg
  * Outputs must be distinct and must not overlap any fragment (ZR_ERR_ALIAS).
- * Fragment tables travel in kernel arguments, 40 fragments per launch at
- * K <= 8 (320 rank pointers per launch).
+ * Fragment tables travel in kernel arguments: a launch carries up to 32
+ * fragments (256 rank pointers at most, so 4 fragments at K = 64) and the
+ * at most 96 (fragment, chunk) pieces they form.
  */
 zr_status zr_reduce_scatter_frags(int K, int n_frag, const void* const* frags,
                                   const int64_t* numels, int64_t N, zr_dtype in_dt,
@@ -249,6 +250,23 @@ int zr_cost_best_broadcast_segments(int K, double bytes, double alpha, double be
 double zr_cost_ring_tree_crossover(int K, double alpha, double beta);
 double zr_cost_ring_naive_crossover(int K, double alpha, double beta);
 double zr_cost_dp_speedup(int K, double t1, double grad_bytes, double alpha, double beta);
+
+/* A discrete reduce-scatter prepared once and launched many times: for a
+ * bucket whose fragments stay at the same addresses from step to step (the
+ * usual ZeRO layout), zr_rsf_plan_create validates everything and builds the
+ * launches' kernel arguments, and each zr_rsf_plan_launch only enqueues
+ * them. Arguments and results are exactly those of zr_reduce_scatter_frags
+ * with the same arguments (the flags, including ZR_ACCUMULATE, are fixed at
+ * create). The plan keeps the fragment and output addresses, not their
+ * contents: the buffers must stay allocated while the plan is launched. The
+ * plan owns only host memory; N == 0 gives a plan that launches nothing. */
+typedef struct zr_rsf_plan zr_rsf_plan;
+
+zr_status zr_rsf_plan_create(int K, int n_frag, const void* const* frags, const int64_t* numels,
+                             int64_t N, zr_dtype in_dt, void* const* out, zr_dtype out_dt,
+                             int chunk_shift, int flags, zr_order order, zr_rsf_plan** plan);
+zr_status zr_rsf_plan_launch(const zr_rsf_plan* plan, void* stream);
+zr_status zr_rsf_plan_destroy(zr_rsf_plan* plan);
 
 /* ------------------------------------------------------------- scheduler
  * Bucket/stream scheduler with per-buffer completion events [ISSUE,

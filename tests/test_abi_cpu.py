@@ -169,7 +169,10 @@ def test_flatten_validation():
     assert call([1, 2, 3], 8, frags=frags) == zr.ZR_ERR_INVALID
 
 
-def test_reduce_scatter_frags_validation():
+@pytest.mark.parametrize("entry", ["call", "plan"])
+def test_reduce_scatter_frags_validation(entry):
+    # the one-shot call and the plan share their validation; a valid plan is
+    # built on the host alone, so it is created (and destroyed) here too
     lib = zr.lib()
     K, F = 2, 3
 
@@ -177,10 +180,24 @@ def test_reduce_scatter_frags_validation():
         fr = (ctypes.c_void_p * (K * F))(*(frags or ranks(K * F)))
         nm = (ctypes.c_int64 * F)(*numels)
         o = (ctypes.c_void_p * K)(*(outs or ranks(K, base=A + (1 << 40))))
-        return lib.zr_reduce_scatter_frags(K, F, fr, nm, N, in_dt, o, out_dt, shift, flags, order,
-                                           None)
+        if entry == "call":
+            return lib.zr_reduce_scatter_frags(K, F, fr, nm, N, in_dt, o, out_dt, shift, flags,
+                                               order, None)
+        h = ctypes.c_void_p(1234)
+        st = lib.zr_rsf_plan_create(K, F, fr, nm, N, in_dt, o, out_dt, shift, flags, order,
+                                    ctypes.byref(h))
+        if st == zr.ZR_OK:
+            if N == 0:
+                assert lib.zr_rsf_plan_launch(h, None) == zr.ZR_OK  # launches nothing
+            assert lib.zr_rsf_plan_destroy(h) == zr.ZR_OK
+        else:
+            assert not h.value  # nothing was handed out
+        return st
 
     assert call([0, 0, 0], 0) == zr.ZR_OK
+    if entry == "plan":
+        for kw in ({}, dict(flags=3, order=2), dict(in_dt=1, out_dt=0, shift=0, order=1)):
+            assert call([1, 2, 3], 8, **kw) == zr.ZR_OK
     assert call([1, 2, 3], 0) == zr.ZR_ERR_INVALID            # N < total
     assert call([1, 2, 3], 5) == zr.ZR_ERR_INVALID
     assert call([1, -2, 3], 8) == zr.ZR_ERR_INVALID

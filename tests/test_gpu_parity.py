@@ -451,6 +451,50 @@ def test_reduce_scatter_frags_bit_exact(K, sizes, extra, in_bf16, out_bf16, shif
             assert g.guards_intact()
 
 
+@pytest.mark.parametrize("case", [FRAG_CASES[i] for i in (0, 1, 3, 5, 6, 7, 8, 11, 13)])
+def test_rsf_plan_launches_equal_the_call(case):
+    # a plan built once, launched twice (the fragments rewritten in place in
+    # between), against the one-shot call with the same arguments each time
+    import torch
+    import gradient_sync_zr_amd as zrm
+    from synth import workloads as W
+    K, sizes, extra, in_bf16, out_bf16, shift, average, order, offset, acc = case
+    if sizes is None:
+        sizes = W.flatten8_numels()
+    total = sum(sizes)
+    N = -(-total // K) * K if extra is None else total + extra
+    C = -(-N // K)
+    f_off = (lambda r: r % 4) if offset == -1 else (lambda r: offset)
+    o_off = 1 if offset == -1 else offset
+    frags = [[Guarded(n, torch_dt(in_bf16), f_off(r)) for n in sizes] for r in range(K)]
+
+    def fill(tag):
+        for r in range(K):
+            for p, n in enumerate(sizes):
+                h = synth.host_normal_bf16(SEED + 300 + tag, r * 4096 + p, 0, n, 1.0, 0.01, 1e4)
+                frags[r][p].set(h if in_bf16 else oracle.bf16_to_f32(h))
+    rng = np.random.default_rng(K + N + 1)
+    init = [rng.standard_normal(C).astype(np.float32) for _ in range(K)]
+    if out_bf16:
+        init = [oracle.f32_to_bf16(x) for x in init]
+    by_call = [Guarded(C, torch_dt(out_bf16), o_off, init[r]) for r in range(K)]
+    by_plan = [Guarded(C, torch_dt(out_bf16), o_off, init[r]) for r in range(K)]
+    fp = [[g.ptr() for g in row] for row in frags]
+    kw = dict(chunk_shift=shift, average=average, order=order, accumulate=acc,
+              in_dtype=torch_dt(in_bf16), out_dtype=torch_dt(out_bf16))
+    plan = zrm.RsfPlan(fp, sizes, N, [g.ptr() for g in by_plan], **kw)
+    for tag in (0, 1):
+        fill(tag)
+        torch.cuda.synchronize()
+        zr().zr_reduce_scatter_frags(fp, sizes, N, [g.ptr() for g in by_call], **kw)
+        plan.launch()
+        torch.cuda.synchronize()
+        for r in range(K):
+            assert np.array_equal(bits(by_plan[r].get()), bits(by_call[r].get())), f"launch {tag} rank {r}"
+            assert by_plan[r].guards_intact()
+    plan.close()
+
+
 def test_reduce_scatter_frags_equals_gpu_flatten_then_rs():
     import torch
     from synth import workloads as W
