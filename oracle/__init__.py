@@ -15,7 +15,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIBRARY may name another build of oracle.c (the mutation test loads
+# deliberately broken copies through it); by default the in-tree build is used.
+LIB = os.environ.get("ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 
 BF16, FP32 = 0, 1
 _i32, _i64, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p

@@ -5,15 +5,18 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def build(verbose: bool = False) -> str:
-    src = os.path.join(HERE, "oracle.c")
-    out = os.path.join(HERE, "liboracle.so")
+def compile_oracle(src: str, out: str, verbose: bool = False) -> str:
+    """Compiles one oracle source into a shared library with the oracle's flags."""
     cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
            "-Wall", "-Wextra", "-o", out, src, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
     return out
+
+
+def build(verbose: bool = False) -> str:
+    return compile_oracle(os.path.join(HERE, "oracle.c"), os.path.join(HERE, "liboracle.so"), verbose)
 
 
 if __name__ == "__main__":

@@ -127,6 +127,31 @@ def test_allreduce_all_ranks_identical_and_exact(K):
         assert np.array_equal(state[r], want.astype(np.float32))
 
 
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 5, 7, 8, 16])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_allreduce_average_is_the_exact_sum_over_k(K, dt):
+    # SUM then divide by the world size (lecture 14, 4.1). Integer inputs make
+    # the sum exact; for power-of-two K the quotient is exact as well, and for
+    # other K the correctly rounded fp32 quotient equals rounding the fp64
+    # quotient (s/K has a periodic binary expansion, never within fp64
+    # precision of an fp32 midpoint). A bf16 output is one rounding of it.
+    rng = np.random.default_rng(100 + K)
+    C = 7
+    N = K * C - (1 if K > 1 else 0)
+    xi = rng.integers(-8, 9, size=(K, K * C))
+    xi[:, N:] = 0
+    want32 = (xi.sum(axis=0).astype(np.float64) / K).astype(np.float32)[:N]
+    if dt == "f32":
+        ins = [xi[r].astype(np.float32) for r in range(K)]
+        want = want32
+    else:
+        ins = [oracle.f32_to_bf16(xi[r].astype(np.float32)) for r in range(K)]
+        want = oracle.f32_to_bf16(want32)
+    out = oracle.allreduce(ins, N, average=True)
+    for r in range(K):
+        assert np.array_equal(out[r][:N].view(want.dtype), want), (K, dt, r)
+
+
 # ------------------------------------------------------------ direct fold
 def wide_random(shape, rng):
     """fp32 values spread over many binades with both signs, so that the
