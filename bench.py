@@ -190,10 +190,16 @@ def cpu_baseline_zero2(grads, parts, first_bucket, K, args):
         t.join()
     dt = time.perf_counter() - t0
     gbs = K * M * (2 * K + 4) / dt / 1e9
+    # one host core on the first 1/16 of the same offsets
+    M1 = max(1, M // 16)
+    t1 = time.perf_counter()
+    oracle.reduce_scatter(xs, K * M, np.float32, shift=1, average=True, o_range=(0, M1), out=outs)
+    gbs1 = K * M1 * (2 * K + 4) / (time.perf_counter() - t1) / 1e9
     exact = all(np.array_equal(parts[q][:M].cpu().numpy().view(np.uint32), outs[q].view(np.uint32))
                 for q in range(K))
     return {"value": round(gbs, 2), "unit": "GB/s", "cores": T, "kind": "oracle",
-            "seconds": round(dt, 3),
+            "seconds": round(dt, 3), "single_core_GBps": round(gbs1, 2),
+            "single_core_sample": f"offsets [0,{M1}) of each chunk of bucket 0",
             "sample": f"offsets [0,{M}) of each of the 8 chunks of bucket 0 "
                       f"({K * M} element indices, {K * M * (2 * K + 4) / 1e9:.2f} GB under "
                       f"the same byte model); GPU partitions bit-exact on it: {exact}"}
