@@ -576,6 +576,11 @@ def bench_flatten8(args):
     us = wall_us(step)
     us_discrete = wall_us(step_discrete)
     us_plan = wall_us(plan.launch)
+    # the plan's launches captured once in a HIP graph and replayed
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.launch()
+    us_graph = wall_us(graph.replay)
     plan.close()
     return {
         "metric": "flatten + reduce-scatter-avg microseconds per bucket, K=8, 64 fragments",
@@ -585,6 +590,7 @@ def bench_flatten8(args):
         "data": "synthetic: seeded generator, bf16 ~N(0,1e-3)",
         "discrete_path_us": round(us_discrete, 2),
         "discrete_plan_us": round(us_plan, 2),
+        "discrete_plan_graph_us": round(us_graph, 2),
         "config": {"workload": f"flatten8: K=8, 64 log-uniform fragments ({sum(sizes)} elements), "
                                f"bucket padded to {P}, then RS + /8 + fp32 cast (cache-resident, "
                                "launch-bound)", "K": K},

@@ -1,0 +1,91 @@
+"""The hot path captured in a HIP graph.
+
+The library's calls allocate nothing, issue no memset and never synchronise
+the device, so a caller can capture them. One graph holds a reduce-scatter,
+an accumulating reduce-scatter, a discrete reduce-scatter (the one-shot call
+and a prepared plan) and an all-gather. It is replayed several times; before
+each replay the program rewrites the inputs eagerly and synchronises, and
+after it every output is compared bit for bit with the same calls made
+eagerly on the same inputs.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import bits
+
+pytestmark = pytest.mark.gpu
+
+K = 8
+N = K * 4096 * 3 + 40
+SIZES = [5000, 37, 12288, 4096 * 3 + 17]
+SEED = 0x5A5200C0
+
+
+def test_graph_replays_match_eager_calls():
+    import torch
+    import gradient_sync_zr_amd as zr
+    C = -(-N // K)
+    F = sum(SIZES)
+    NF = -(-F // K) * K
+    CF = NF // K
+    x = [torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    frags = [[torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in SIZES] for _ in range(K)]
+    shards = [torch.empty(C, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    segs = [(0, 0, N)]
+
+    def outputs():
+        return dict(rs=[torch.empty(C, dtype=torch.float32, device="cuda") for _ in range(K)],
+                    acc=[torch.empty(C, dtype=torch.float32, device="cuda") for _ in range(K)],
+                    frag=[torch.empty(CF, dtype=torch.float32, device="cuda") for _ in range(K)],
+                    plan=[torch.empty(CF, dtype=torch.float32, device="cuda") for _ in range(K)],
+                    ag=[torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(K)])
+
+    g_out, e_out = outputs(), outputs()
+    g_plan = zr.RsfPlan(frags, SIZES, NF, g_out["plan"], chunk_shift=1, average=True)
+    e_plan = zr.RsfPlan(frags, SIZES, NF, e_out["plan"], chunk_shift=1, average=True)
+
+    def work(o, plan):
+        zr.zr_reduce_scatter_avg(x, N, o["rs"], chunk_shift=1, average=True)
+        zr.zr_reduce_scatter_avg(x, N, o["acc"], chunk_shift=1, average=True, accumulate=True)
+        zr.zr_reduce_scatter_frags(frags, SIZES, NF, o["frag"], chunk_shift=1, average=True)
+        plan.launch()
+        zr.zr_all_gather(shards, o["ag"], segs, chunk_shift=0)
+
+    def fill(tag):
+        for r in range(K):
+            synth.dev_normal_bf16(x[r], SEED + tag, r, 0, 1.0)
+            synth.dev_normal_bf16(shards[r], SEED + tag, 100 + r, 0, 1.0)
+            for p in range(len(SIZES)):
+                synth.dev_normal_bf16(frags[r][p], SEED + tag, 200 + 8 * r + p, 0, 1.0)
+        for o in (g_out, e_out):
+            for r in range(K):
+                o["acc"][r].fill_(0.5 * (tag + 1))
+        torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    fill(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work(g_out, g_plan)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        work(g_out, g_plan)
+    torch.cuda.synchronize()
+    for tag in (1, 2, 3):
+        fill(tag)
+        graph.replay()
+        torch.cuda.synchronize()
+        work(e_out, e_plan)
+        torch.cuda.synchronize()
+        for key in ("rs", "acc", "frag", "plan", "ag"):
+            for r in range(K):
+                got = g_out[key][r].cpu()
+                want = e_out[key][r].cpu()
+                if key == "ag":
+                    got, want = got.view(torch.int16), want.view(torch.int16)
+                assert np.array_equal(bits(got.numpy()), bits(want.numpy())), (tag, key, r)
+    g_plan.close()
+    e_plan.close()
