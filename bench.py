@@ -114,6 +114,9 @@ def bench_zero2(args, accumulate=False):
     launch_bytes = [n * per_elem for _, n in buckets] * args.steps
     achieved = sum(launch_bytes) / (sum(launch_ms) * 1e-3) / 1e9
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    # the 500M-element buckets alone (the last bucket is smaller)
+    full = sorted(ms for ms, b in zip(launch_ms, launch_bytes) if b == max(launch_bytes))
+    full_med, full_min = full[len(full) // 2], full[0]
     bytes_per_launch = sum(launch_bytes) / len(launch_bytes)
     src = kernel_source_hash(["zr_rs.hip", "zr_fold.hpp", "zr_device.hpp"])
     traffic = read_traffic("rs_ring_bf16_f32_k8_zero2.counters.txt", src, bytes_per_launch)
@@ -150,6 +153,8 @@ def bench_zero2(args, accumulate=False):
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "avg_launch_ms": round(avg_launch_ms, 4),
+                     "full_bucket_launch_ms_median": round(full_med, 4),
+                     "full_bucket_launch_ms_min": round(full_min, 4),
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
                      "kernel_source_sha256_16": src},
         "cpu_baseline": cpu,
