@@ -402,11 +402,8 @@ zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const i
         if (padded_numel > off) jobs.push_back(CopyJob{nullptr, b + off * es, padded_numel - off});
     }
     hipStream_t s = (hipStream_t)stream;
-    for (size_t i = 0; i < jobs.size(); i += kFlatJobsPerLaunch) {
-        const int n = (int)std::min<size_t>(kFlatJobsPerLaunch, jobs.size() - i);
-        hipError_t e = launch_flatten(jobs.data() + i, n, (int)es, s);
-        if (e != hipSuccess) return hip_fail(e, "flatten launch");
-    }
+    hipError_t e = launch_flatten(jobs.data(), (int)jobs.size(), (int)es, s);
+    if (e != hipSuccess) return hip_fail(e, "flatten launch");
     return ok();
 }
 

@@ -152,6 +152,23 @@ __device__ __forceinline__ float load_elem(const float* p) { return *p; }
 __device__ __forceinline__ void store_elem(uint16_t* p, float v) { *p = (uint16_t)bf16_round(v); }
 __device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
 
+// The slot holding item t of a flat item space cut into n slots, where
+// start[0..n] is nondecreasing, start[0] = 0 and start[n] > t; the search
+// begins at slot m (a lower bound). The wave's lanes read 64 starts at once
+// and count those <= t with a ballot: the slot is the last of them (empty
+// slots, whose start repeats the next one's, are passed over). t and m are
+// uniform across the wave; one round unless t lies 64 or more slots ahead.
+__device__ __forceinline__ int find_slot(const int32_t* start, int n, int m, int t) {
+    const int lane = threadIdx.x & 63;
+    while (true) {
+        const int idx = m + lane;
+        const bool le = idx <= n && start[idx <= n ? idx : n] <= t;
+        const int c = __popcll(__ballot(le));
+        if (c < 64) return m + c - 1;
+        m += 64;
+    }
+}
+
 // Average: AVG 0 = none, 1 = multiply by the exact reciprocal (K a power of
 // two, identical to dividing), 2 = IEEE correctly rounded divide by K.
 template <int AVG>

@@ -4,78 +4,147 @@
 // offset n_0 + ... + n_{p-1} of the flat buffer; 3.1: one large contiguous
 // message instead of one per parameter).
 //
-// A launch carries up to 96 copy jobs in its kernel arguments (no device
-// descriptor table, no staging copy). blockIdx.y = job, blockIdx.x strides
-// over 4 KiB tiles of the job; a lane moves 16 bytes. When source and
-// destination are both 16-byte aligned the lane copies with one 16-byte load
-// and store; otherwise (the usual case inside a bucket, since offsets are
-// prefix sums of arbitrary sizes) it copies its 16 destination bytes element
-// by element. A job with no source writes zeros.
+// A launch carries up to 96 copy jobs and each job's first tile in its
+// kernel arguments (no device descriptor table, no staging copy); the grid
+// strides over the launch's tiles in order, so blocks stay balanced however
+// unequal the jobs are. A tile is 16 KiB of destination (4 KiB in launches
+// too small to fill the device): lane l of wave w moves the 16-byte units
+// w*64*U + k*64 + l (k < U = 4 or 1), so every load and store instruction of
+// a wave covers 1 KiB contiguously, with all loads in flight before the
+// stores; loads and stores are non-temporal (each byte is touched once). A job whose source and destination both start 16-byte
+// aligned copies whole units; its last partial unit, and every unit of a job
+// that is not aligned so (possible inside a bucket, where offsets are prefix
+// sums of arbitrary sizes), copies element by element. A job with no source
+// writes zeros.
 #include "zr_device.hpp"
 #include "zr_internal.hpp"
 
 namespace zr {
 namespace {
 
-constexpr int kFlatTileBytes = kThreads * 16;
+// 16-byte units per lane: 4 (16 KiB tiles) for launches with enough tiles to
+// fill the device, else 1 (4 KiB tiles, four times as many blocks).
+template <int U>
+constexpr int64_t kFlatTileBytes = (int64_t)kThreads * 16 * U;
 
 struct FlatArgs {
     CopyJob job[kFlatJobsPerLaunch];
-    int es;  // element bytes, 2 or 4
+    int32_t tile0[kFlatJobsPerLaunch + 1];  // first tile of job m; tile0[n_jobs] = all tiles
+    int n_jobs;
 };
+static_assert(sizeof(FlatArgs) <= 4096, "flatten arguments exceed 4 KB");
 
-template <typename T>
-__device__ __forceinline__ void copy_elems(const T* src, T* dst, int n) {
-    if (src) {
-        for (int e = 0; e < n; ++e) dst[e] = src[e];
-    } else {
-        for (int e = 0; e < n; ++e) dst[e] = T(0);
-    }
-}
-
-template <typename T>
+template <typename T, int U>
 __global__ void __launch_bounds__(kThreads) flatten_kernel(const FlatArgs a) {
-    const CopyJob jb = a.job[blockIdx.y];
-    const int64_t bytes = jb.n * (int64_t)sizeof(T);
-    const int64_t tiles = (bytes + kFlatTileBytes - 1) / kFlatTileBytes;
-    const bool vec = ((((uintptr_t)jb.dst) & 15) == 0) &&
-                     (jb.src == nullptr || (((uintptr_t)jb.src) & 15) == 0);
-    constexpr int per = 16 / sizeof(T);  // elements per lane
-    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-        const int64_t e0 = (t * kFlatTileBytes + (int64_t)threadIdx.x * 16) / (int64_t)sizeof(T);
-        if (e0 >= jb.n) continue;
-        T* d = static_cast<T*>(jb.dst) + e0;
-        const T* s = jb.src ? static_cast<const T*>(jb.src) + e0 : nullptr;
-        if (vec && e0 + per <= jb.n) {
-            u32x4 v = s ? *reinterpret_cast<const u32x4*>(s) : u32x4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(d) = v;
-        } else {
-            const int n = (int)((jb.n - e0) < per ? (jb.n - e0) : per);
-            copy_elems<T>(s, d, n);
+    constexpr int per = 16 / sizeof(T);  // elements per 16-byte unit
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int total = a.tile0[a.n_jobs];
+    int m = 0;
+    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+        m = find_slot(a.tile0, a.n_jobs, m, t);  // a block's tiles only grow: jobs in order
+        const CopyJob jb = a.job[m];
+        const int64_t tt = t - a.tile0[m];
+        const bool vec = ((((uintptr_t)jb.dst) & 15) == 0) &&
+                         (jb.src == nullptr || (((uintptr_t)jb.src) & 15) == 0);
+        const T* src = static_cast<const T*>(jb.src);
+        T* dst = static_cast<T*>(jb.dst);
+        const int64_t u0 = tt * (kFlatTileBytes<U> / 16) + wave * 64 * U + lane;  // first unit
+        if (vec && (u0 + 64 * (U - 1) + 1) * per <= jb.n) {
+            // every unit of this lane is whole
+            u32x4 v[U];
+#pragma unroll
+            for (int k = 0; k < U; ++k)
+                v[k] = src ? ld<true>(reinterpret_cast<const u32x4*>(src + (u0 + 64 * k) * per))
+                           : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int k = 0; k < U; ++k)
+                st<true>(reinterpret_cast<u32x4*>(dst + (u0 + 64 * k) * per), v[k]);
+            continue;
+        }
+        // some unit of this lane is partial or unaligned: every load is issued
+        // before the first store (a store may not overtake the loads, so the
+        // lane waits on one memory latency, not one per element)
+        u32x4 vv[U];
+        T ev[U][per];
+        int cnt[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t e0 = (u0 + 64 * k) * per;
+            cnt[k] = e0 >= jb.n ? 0 : (int)((jb.n - e0) < per ? (jb.n - e0) : per);
+            if (vec && cnt[k] == per) {
+                vv[k] = src ? ld<true>(reinterpret_cast<const u32x4*>(src + e0)) : u32x4{0u, 0u, 0u, 0u};
+            } else {
+#pragma unroll
+                for (int e = 0; e < per; ++e)
+                    if (e < cnt[k]) ev[k][e] = src ? src[e0 + e] : T(0);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t e0 = (u0 + 64 * k) * per;
+            if (vec && cnt[k] == per) {
+                st<true>(reinterpret_cast<u32x4*>(dst + e0), vv[k]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < per; ++e)
+                    if (e < cnt[k]) dst[e0 + e] = ev[k][e];
+            }
         }
     }
 }
 
+template <typename T, int U>
+hipError_t launch_batch(const FlatArgs& a, int64_t tiles, hipStream_t stream) {
+    const int64_t want = (int64_t)device_cu_count() * 8;
+    const int gx = (int)(want < tiles ? want : tiles);
+    hipLaunchKernelGGL((flatten_kernel<T, U>), dim3(gx), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+int64_t tiles_of(int64_t bytes, int64_t tile) { return (bytes + tile - 1) / tile; }
+
 }  // namespace
 
+// Jobs go out in launches of at most kFlatJobsPerLaunch jobs and about 2^30
+// tiles (a single job has at most 2^28 tiles), so tile numbers fit in 32 bits.
+// A launch with fewer 16 KiB tiles than two per CU uses 4 KiB tiles.
 hipError_t launch_flatten(const CopyJob* jobs, int n_jobs, int elem_bytes, hipStream_t stream) {
-    if (n_jobs <= 0) return hipSuccess;
     FlatArgs a;
-    a.es = elem_bytes;
-    int64_t max_tiles = 1;
+    int first = 0, count = 0;
+    int64_t big = 0;  // tiles of the batch at 16 KiB
+    auto flush = [&]() -> hipError_t {
+        if (count == 0) return hipSuccess;
+        const bool small = big < 2LL * device_cu_count();
+        const int64_t tile = small ? kFlatTileBytes<1> : kFlatTileBytes<4>;
+        int64_t tiles = 0;
+        for (int i = 0; i < count; ++i) {
+            a.job[i] = jobs[first + i];
+            a.tile0[i] = (int32_t)tiles;
+            tiles += tiles_of(jobs[first + i].n * elem_bytes, tile);
+        }
+        a.tile0[count] = (int32_t)tiles;
+        a.n_jobs = count;
+        hipError_t e = hipSuccess;
+        if (tiles > 0) {
+            if (elem_bytes == 2)
+                e = small ? launch_batch<uint16_t, 1>(a, tiles, stream) : launch_batch<uint16_t, 4>(a, tiles, stream);
+            else
+                e = small ? launch_batch<uint32_t, 1>(a, tiles, stream) : launch_batch<uint32_t, 4>(a, tiles, stream);
+        }
+        first += count;
+        count = 0;
+        big = 0;
+        return e;
+    };
     for (int i = 0; i < n_jobs; ++i) {
-        a.job[i] = jobs[i];
-        const int64_t t = (jobs[i].n * elem_bytes + kFlatTileBytes - 1) / kFlatTileBytes;
-        if (t > max_tiles) max_tiles = t;
+        if (count == kFlatJobsPerLaunch || big > (1LL << 28)) {
+            hipError_t e = flush();
+            if (e != hipSuccess) return e;
+        }
+        big += tiles_of(jobs[i].n * elem_bytes, kFlatTileBytes<4>);
+        ++count;
     }
-    int64_t want = (int64_t)device_cu_count() * 8 / n_jobs;
-    if (want < 1) want = 1;
-    const int gx = (int)(want < max_tiles ? want : max_tiles);
-    if (elem_bytes == 2)
-        hipLaunchKernelGGL(flatten_kernel<uint16_t>, dim3(gx, n_jobs), dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(flatten_kernel<uint32_t>, dim3(gx, n_jobs), dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+    return flush();
 }
 
 }  // namespace zr

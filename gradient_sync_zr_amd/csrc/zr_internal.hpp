@@ -73,7 +73,7 @@ RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t 
 hipError_t rsf_plan_launch(const RsfPlan* plan, hipStream_t stream);
 void rsf_plan_free(RsfPlan* plan);
 
-// jobs: up to kFlatJobsPerLaunch per call.
+// Any number of jobs; launched kFlatJobsPerLaunch (or fewer) at a time.
 hipError_t launch_flatten(const CopyJob* jobs, int n_jobs, int elem_bytes, hipStream_t stream);
 
 }  // namespace zr

@@ -63,7 +63,7 @@ __global__ void __launch_bounds__(kThreads) rsf_kernel(const RsfArgs a) {
     const int total = a.tile0[a.nseg];
     int s = 0;
     for (int t = blockIdx.x; t < total; t += gridDim.x) {
-        while (t >= a.tile0[s + 1]) ++s;  // a block's tiles only grow: segments in order
+        s = find_slot(a.tile0, a.nseg, s, t);  // a block's tiles only grow: segments in order
         const int m = a.seg_m[s], j = a.seg_j[s];
         const int64_t jc = (int64_t)j * a.C;
         const int64_t f0 = a.off[m], f1 = a.off[m] + a.n[m];
