@@ -252,3 +252,56 @@ def test_plan_buckets_transformer_50mb():
     assert nb == len(greedy_reference([p.numel for p in ps], cap))
     with pytest.raises(zr.ZrError):
         zr.zr_plan_buckets([1, 2], 0)
+
+
+def test_prefetch_config_validation():
+    # every rejection happens before a HIP call, so it is visible without a GPU
+    lib = zr.lib()
+    K = 2
+    numels = [100, 7]
+
+    def create(**over):
+        kw = dict(shard_offsets=[0, 50], shards=ranks(K), arenas=ranks(K, base=A + (1 << 40)),
+                  arena_numel=1000, steps=[[0], [1]], bucket=10, max_live=100, reuse=0, ongoing=2,
+                  shift=0, dtype=zr.ZR_BF16, K=K, numels=numels)
+        kw.update(over)
+        # stream handles are placeholders: a rejected config never reaches them
+        c = zr._pf_config(kw["K"], kw["dtype"], kw["numels"], kw["steps"], kw["bucket"],
+                          kw["max_live"], kw["arena_numel"], kw["ongoing"], kw["reuse"],
+                          kw["shard_offsets"], kw["shards"], kw["arenas"], kw["shift"],
+                          gather_stream=0, compute_stream=0)
+        h = ctypes.c_void_p(77)
+        st = lib.zr_pf_create(ctypes.byref(c), ctypes.byref(h))
+        assert st == zr.ZR_OK or not h.value
+        return st
+
+    assert create(K=0) == zr.ZR_ERR_INVALID
+    assert create(dtype=7) == zr.ZR_ERR_UNSUPPORTED
+    assert create(numels=[100, 0]) == zr.ZR_ERR_INVALID
+    assert create(arena_numel=0) == zr.ZR_ERR_INVALID
+    assert create(shift=2) == zr.ZR_ERR_INVALID
+    assert create(steps=[[0], [2]]) == zr.ZR_ERR_INVALID           # not a parameter id
+    assert create(bucket=0) == zr.ZR_ERR_INVALID
+    assert create(max_live=0) == zr.ZR_ERR_INVALID
+    assert create(reuse=-1) == zr.ZR_ERR_INVALID
+    assert create(ongoing=0) == zr.ZR_ERR_INVALID
+    assert create(shard_offsets=[0, -1]) == zr.ZR_ERR_INVALID
+    assert create(shards=[A, 0]) == zr.ZR_ERR_INVALID
+    assert create(arenas=[A + (1 << 40) + 1, A + (1 << 41)]) == zr.ZR_ERR_ALIGN
+    assert create(arenas=[A + (1 << 40)] * 2) == zr.ZR_ERR_ALIAS    # one arena for both ranks
+    assert create(arenas=[A + 64, A + (1 << 41)]) == zr.ZR_ERR_ALIAS  # arena over rank 0's shards
+    assert lib.zr_pf_create(None, ctypes.byref(ctypes.c_void_p())) == zr.ZR_ERR_INVALID
+    assert lib.zr_pf_destroy(None) == zr.ZR_OK
+
+
+def test_prefetch_plan_on_the_host():
+    # zr_pf_plan needs no buffers: the same core run with gathers that finish
+    # at once; a capacity that cannot hold a step is ZR_ERR_NOMEM
+    numels = [40, 30, 20, 10]
+    steps = [[0], [1, 2], [3], [2], [1], [0]]
+    st = zr.zr_pf_plan(numels, steps, 30, 60, 1000, max_reuse_numel=25, iterations=2)
+    assert st["live"] == 0 and st["peak_live"] <= 60 + 40 + 40
+    assert st["immediate_gathers"] >= 2
+    with pytest.raises(zr.ZrError) as e:
+        zr.zr_pf_plan(numels, steps, 30, 60, 40, max_reuse_numel=0)  # step 1 needs 50
+    assert e.value.status == zr.ZR_ERR_NOMEM
