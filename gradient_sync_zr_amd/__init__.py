@@ -8,6 +8,32 @@ pointers, torch streams into ``hipStream_t`` handles, and a non-OK status into
 
 The library must be built (``__graft_entry__.build()``); importing this module
 does not build it, and every call raises if ``libzr.so`` is missing.
+
+Calls (a list holds one buffer per rank, as tensors or integer addresses;
+streams default to torch's current stream):
+
+* ``zr_reduce_scatter_avg(inputs, N, outputs, chunk_shift=1, average=True,
+  order=ZR_ORDER_RING, accumulate=False)``: ring-order reduce-scatter, /K,
+  cast, one write of each rank's partition of ``ceil(N / K)`` elements.
+* ``zr_reduce_scatter_frags(frags, numels, N, outputs, ...)``: the same from
+  per-parameter fragments, without a bucket; ``RsfPlan(...)`` builds it once
+  and ``.launch()`` repeats it.
+* ``zr_all_gather(shards, fulls, segs, chunk_shift=0)`` and
+  ``zr_allreduce(inputs, outputs, N, average=False, fused=True)``.
+* ``zr_flatten_bucket(frags, numels, buckets, padded_numel)``.
+* ``Sched``: ping-pong bucket buffers with per-buffer completion events
+  (``acquire``, ``submit_rs``, ``flush``).
+* ``Prefetcher``: ZeRO-3 fetch and prefetch of full parameters into per-rank
+  arenas (``fetch``, ``full``, ``release``, ``stats``).
+* Host only: ``zr_pf_plan``, ``zr_plan_buckets``, ``zr_cost_*``.
+
+Example: eight ranks' bf16 gradients of N elements reduced into fp32
+partitions (rank q receives chunk (q + 1) mod 8, averaged)::
+
+    import torch, gradient_sync_zr_amd as zr
+    grads = [torch.randn(N, device="cuda").bfloat16() for _ in range(8)]
+    parts = [torch.empty(-(-N // 8), device="cuda") for _ in range(8)]
+    zr.zr_reduce_scatter_avg(grads, N, parts)
 """
 from __future__ import annotations
 
