@@ -77,9 +77,13 @@ constexpr int kSlices = sizeof(TIn) == 2 ? ZR_RS_SLICES_BF16 : ZR_RS_SLICES_FP32
 #define ZR_RS_NONTEMPORAL 1
 #endif
 constexpr bool kRsNontemporal = ZR_RS_NONTEMPORAL != 0;
-// Elements per reduce-scatter tile: 4 waves x S slices x 256.
+// Elements per reduce-scatter tile of S slices: 4 waves x S x 256. Launches
+// too small to give every CU two tiles use one slice per wave (four times as
+// many, shorter tiles), in the ring order.
+template <int S>
+constexpr int64_t kRsTileOf = (int64_t)(kThreads / 64) * S * 256;
 template <typename TIn>
-constexpr int64_t kRsTile = (int64_t)(kThreads / 64) * kSlices<TIn> * 256;
+constexpr int64_t kRsTile = kRsTileOf<kSlices<TIn>>;
 
 // A wave owns S slices of 256 consecutive elements; lane l holds quad l of
 // each slice (elements 4l..4l+3), so every load and store instruction of the

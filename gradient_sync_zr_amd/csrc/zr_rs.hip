@@ -43,10 +43,9 @@ struct RsArgs {
     float inv_k, kf;
 };
 
-template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT>
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
 __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
-    constexpr int S = kSlices<TIn>;
-    constexpr int64_t T = kRsTile<TIn>;
+    constexpr int64_t T = kRsTileOf<S>;
     constexpr bool kStatic = ORDER != kFree && KS > 0 && KS <= 8;
     const int K = KS > 0 ? KS : a.K;
     const int j = blockIdx.y;
@@ -132,13 +131,13 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
     }
 }
 
-template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT>
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
 hipError_t launch_t(const RsArgs& a, hipStream_t stream) {
     const int cus = device_cu_count();
     int64_t want = (int64_t)cus * tuning().rs_blocks_per_cu / a.K;
     if (want < 1) want = 1;
     const int gx = (int)(want < a.tiles_per_chunk ? want : a.tiles_per_chunk);
-    hipLaunchKernelGGL((rs_kernel<TIn, TOut, KS, AVG, ORDER, NT>), dim3(gx, a.K), dim3(kThreads), 0,
+    hipLaunchKernelGGL((rs_kernel<TIn, TOut, KS, AVG, ORDER, NT, S>), dim3(gx, a.K), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
 }
@@ -146,33 +145,37 @@ hipError_t launch_t(const RsArgs& a, hipStream_t stream) {
 // Orders: the free order has one generic instantiation; ring and wire orders
 // have K = 8 specialised, other K take the generic kernel (batches of eight
 // ranks in flight). With fp32 input the wire order is the ring order
-// (rounding every hop to fp32 is what the fp32 adds already do).
+// (rounding every hop to fp32 is what the fp32 adds already do). Small
+// launches in the ring order use one slice per wave.
 template <typename TIn, typename TOut, int AVG>
-hipError_t pick_k(const RsArgs& a, int order, hipStream_t s) {
-    if (order == kFree) return launch_t<TIn, TOut, 0, AVG, kFree, kRsNontemporal>(a, s);
+hipError_t pick_k(const RsArgs& a, int order, bool small, hipStream_t s) {
+    constexpr int S = kSlices<TIn>;
+    constexpr bool NT = kRsNontemporal;
+    if (order == kFree) return launch_t<TIn, TOut, 0, AVG, kFree, NT, S>(a, s);
     if (order == kWire && sizeof(TIn) == 2) {
-        if (a.K == 8) return launch_t<TIn, TOut, 8, AVG, kWire, kRsNontemporal>(a, s);
-        return launch_t<TIn, TOut, 0, AVG, kWire, kRsNontemporal>(a, s);
+        if (a.K == 8) return launch_t<TIn, TOut, 8, AVG, kWire, NT, S>(a, s);
+        return launch_t<TIn, TOut, 0, AVG, kWire, NT, S>(a, s);
     }
-    switch (a.K) {
-        case 8: return launch_t<TIn, TOut, 8, AVG, kRing, kRsNontemporal>(a, s);
-        default: return launch_t<TIn, TOut, 0, AVG, kRing, kRsNontemporal>(a, s);
-    }
+    if (a.K == 8)
+        return small ? launch_t<TIn, TOut, 8, AVG, kRing, NT, 1>(a, s) : launch_t<TIn, TOut, 8, AVG, kRing, NT, S>(a, s);
+    return small ? launch_t<TIn, TOut, 0, AVG, kRing, NT, 1>(a, s) : launch_t<TIn, TOut, 0, AVG, kRing, NT, S>(a, s);
 }
 
 template <typename TIn, typename TOut>
-hipError_t pick_avg(const RsArgs& a, int avg_mode, int order, hipStream_t s) {
+hipError_t pick_avg(const RsArgs& a, int avg_mode, int order, bool small, hipStream_t s) {
     switch (avg_mode) {
-        case 1: return pick_k<TIn, TOut, 1>(a, order, s);
-        case 2: return pick_k<TIn, TOut, 2>(a, order, s);
-        default: return pick_k<TIn, TOut, 0>(a, order, s);
+        case 1: return pick_k<TIn, TOut, 1>(a, order, small, s);
+        case 2: return pick_k<TIn, TOut, 2>(a, order, small, s);
+        default: return pick_k<TIn, TOut, 0>(a, order, small, s);
     }
 }
 
 template <typename TIn, typename TOut>
 hipError_t launch_typed(RsArgs& a, int avg_mode, int order, hipStream_t s) {
     constexpr int64_t T = kRsTile<TIn>;
-    a.tiles_per_chunk = (int)((a.C + T - 1) / T);
+    const bool small = order == kRing && ((a.C + T - 1) / T) * a.K < 2LL * device_cu_count();
+    const int64_t Tl = small ? kRsTileOf<1> : T;
+    a.tiles_per_chunk = (int)((a.C + Tl - 1) / Tl);
     // Vector path: every base aligned for quad access (8 bytes for bf16
     // quads, 16 for fp32 quads) and j*C a multiple of 4 elements, so that a
     // vector tile start j*C + head is a quad boundary on the input side and
@@ -194,7 +197,7 @@ hipError_t launch_typed(RsArgs& a, int avg_mode, int order, hipStream_t s) {
         a.vec_mask |= 1ull << j;
         a.head[j] = (int16_t)((line - start % line) % line);
     }
-    return pick_avg<TIn, TOut>(a, avg_mode, order, s);
+    return pick_avg<TIn, TOut>(a, avg_mode, order, small, s);
 }
 
 }  // namespace

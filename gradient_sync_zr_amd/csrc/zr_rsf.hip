@@ -52,10 +52,9 @@ static_assert(sizeof(RsfArgs) <= 4096, "discrete reduce-scatter arguments exceed
 // Elements per tile of a segment that folds element by element (4 per thread).
 constexpr int64_t kElemTile = kThreads * 4;
 
-template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT>
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
 __global__ void __launch_bounds__(kThreads) rsf_kernel(const RsfArgs a) {
-    constexpr int S = kSlices<TIn>;
-    constexpr int64_t T = kRsTile<TIn>;
+    constexpr int64_t T = kRsTileOf<S>;
     constexpr bool kStatic = ORDER != kFree && KS > 0 && KS <= 8;
     const int K = KS > 0 ? KS : a.K;
     const int lane = threadIdx.x & 63;
@@ -166,12 +165,12 @@ __global__ void __launch_bounds__(kThreads) rsf_kernel(const RsfArgs a) {
     }
 }
 
-template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT>
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
 hipError_t launch_t(const RsfArgs& a, hipStream_t stream) {
     const int total = a.tile0[a.nseg];
     int64_t want = (int64_t)device_cu_count() * tuning().rs_blocks_per_cu;
     const int gx = (int)(want < total ? want : total);
-    hipLaunchKernelGGL((rsf_kernel<TIn, TOut, KS, AVG, ORDER, NT>), dim3(gx), dim3(kThreads), 0,
+    hipLaunchKernelGGL((rsf_kernel<TIn, TOut, KS, AVG, ORDER, NT, S>), dim3(gx), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
 }
@@ -180,23 +179,26 @@ using LaunchFn = hipError_t (*)(const RsfArgs&, hipStream_t);
 
 // Ring and wire order at K = 8 specialised, the rest generic (batches of
 // eight ranks in flight); fp32 input makes the wire order the ring order.
+// Small plans in the ring order use one slice per wave.
 template <typename TIn, typename TOut, int AVG>
-LaunchFn pick_k(int K, int order) {
-    if (order == kFree) return &launch_t<TIn, TOut, 0, AVG, kFree, kRsNontemporal>;
+LaunchFn pick_k(int K, int order, bool small) {
+    constexpr int S = kSlices<TIn>;
+    constexpr bool NT = kRsNontemporal;
+    if (order == kFree) return &launch_t<TIn, TOut, 0, AVG, kFree, NT, S>;
     if (order == kWire && sizeof(TIn) == 2) {
-        if (K == 8) return &launch_t<TIn, TOut, 8, AVG, kWire, kRsNontemporal>;
-        return &launch_t<TIn, TOut, 0, AVG, kWire, kRsNontemporal>;
+        if (K == 8) return &launch_t<TIn, TOut, 8, AVG, kWire, NT, S>;
+        return &launch_t<TIn, TOut, 0, AVG, kWire, NT, S>;
     }
-    if (K == 8) return &launch_t<TIn, TOut, 8, AVG, kRing, kRsNontemporal>;
-    return &launch_t<TIn, TOut, 0, AVG, kRing, kRsNontemporal>;
+    if (K == 8) return small ? &launch_t<TIn, TOut, 8, AVG, kRing, NT, 1> : &launch_t<TIn, TOut, 8, AVG, kRing, NT, S>;
+    return small ? &launch_t<TIn, TOut, 0, AVG, kRing, NT, 1> : &launch_t<TIn, TOut, 0, AVG, kRing, NT, S>;
 }
 
 template <typename TIn, typename TOut>
-LaunchFn pick_avg(int K, int avg, int order) {
+LaunchFn pick_avg(int K, int avg, int order, bool small) {
     switch (avg) {
-        case 1: return pick_k<TIn, TOut, 1>(K, order);
-        case 2: return pick_k<TIn, TOut, 2>(K, order);
-        default: return pick_k<TIn, TOut, 0>(K, order);
+        case 1: return pick_k<TIn, TOut, 1>(K, order, small);
+        case 2: return pick_k<TIn, TOut, 2>(K, order, small);
+        default: return pick_k<TIn, TOut, 0>(K, order, small);
     }
 }
 
@@ -214,8 +216,8 @@ int16_t segment_head(const uintptr_t* addr, int K, int j, uintptr_t es) {
 // kRsfEntriesPerLaunch fragments (and kRsfPtrsPerLaunch rank pointers) and
 // the segments they form with the chunks.
 template <typename TIn, typename TOut>
-void build_typed(RsfArgs& a, const FragEntry* entries, int n_entries, std::vector<RsfArgs>* out) {
-    constexpr int64_t T = kRsTile<TIn>;
+void build_typed(RsfArgs& a, const FragEntry* entries, int n_entries, int64_t T,
+                 std::vector<RsfArgs>* out) {
     const int K = a.K;
     const int64_t C = a.C;
     const int max_entries = (kRsfPtrsPerLaunch / K) < kRsfEntriesPerLaunch ? (kRsfPtrsPerLaunch / K)
@@ -292,20 +294,30 @@ RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t 
     const bool pow2 = (K & (K - 1)) == 0;
     const int avg = !(flags & ZR_AVERAGE) ? 0 : (pow2 ? 1 : 2);
     const int ord = order == ZR_ORDER_FREE ? kFree : (order == ZR_ORDER_RING_WIRE ? kWire : kRing);
-    try {
-        if (in_dt == ZR_BF16 && out_dt == ZR_FP32) {
-            build_typed<uint16_t, float>(a, entries, n_entries, &plan->launches);
-            plan->fn = pick_avg<uint16_t, float>(K, avg, ord);
-        } else if (in_dt == ZR_BF16 && out_dt == ZR_BF16) {
-            build_typed<uint16_t, uint16_t>(a, entries, n_entries, &plan->launches);
-            plan->fn = pick_avg<uint16_t, uint16_t>(K, avg, ord);
-        } else if (in_dt == ZR_FP32 && out_dt == ZR_FP32) {
-            build_typed<float, float>(a, entries, n_entries, &plan->launches);
-            plan->fn = pick_avg<float, float>(K, avg, ord);
-        } else {
-            build_typed<float, uint16_t>(a, entries, n_entries, &plan->launches);
-            plan->fn = pick_avg<float, uint16_t>(K, avg, ord);
+    // the tiles at full size decide the tile: plans whose launches would give
+    // fewer than two tiles per CU (ring order) use one slice per wave
+    auto build = [&](auto tin, auto tout) {
+        using TIn = decltype(tin);
+        using TOut = decltype(tout);
+        build_typed<TIn, TOut>(a, entries, n_entries, kRsTile<TIn>, &plan->launches);
+        int64_t most = 0;
+        for (const RsfArgs& l : plan->launches) most = most > l.tile0[l.nseg] ? most : l.tile0[l.nseg];
+        const bool small = ord == kRing && most < 2LL * device_cu_count();
+        if (small) {
+            plan->launches.clear();
+            build_typed<TIn, TOut>(a, entries, n_entries, kRsTileOf<1>, &plan->launches);
         }
+        plan->fn = pick_avg<TIn, TOut>(K, avg, ord, small);
+    };
+    try {
+        if (in_dt == ZR_BF16 && out_dt == ZR_FP32)
+            build(uint16_t{}, float{});
+        else if (in_dt == ZR_BF16 && out_dt == ZR_BF16)
+            build(uint16_t{}, uint16_t{});
+        else if (in_dt == ZR_FP32 && out_dt == ZR_FP32)
+            build(float{}, float{});
+        else
+            build(float{}, uint16_t{});
     } catch (...) {
         delete plan;
         return nullptr;

@@ -63,6 +63,10 @@ RS_CASES = [
     (64, 300007, True, True, 1, False, 0),
     (64, 200000, False, False, 0, True, 1),
     (33, 33 * 3000 + 1, True, False, 1, True, 0),
+    # large enough for full four-slice tiles (smaller launches use one slice)
+    (8, 8 * 300000 + 13, True, False, 1, True, 0),
+    (16, 16 * 150000 + 5, False, True, 1, True, 0),
+    (64, 64 * 40000 + 7, True, False, 1, False, 0),
 ]
 
 
@@ -94,6 +98,7 @@ ACC_CASES = [
     (8, 65536 + 5, True, False, 0, False, 1),     # element-wise path
     (64, 64 * 4096 + 3, True, False, 1, True, 0),
     (3, 2, True, False, 1, True, 0),
+    (8, 8 * 300000 + 13, True, False, 1, True, 0),   # four-slice tiles
 ]
 
 
@@ -379,6 +384,8 @@ FRAG_CASES = [
     (8, [6, 30000, 40000], 2, True, True, 1, True, 0, 0, False),      # bf16 partition side unaligned
     (8, [6, 30000, 40000], 2, False, False, 1, True, 0, 0, True),     # fp32, unaligned, accumulate
     (8, [6, 30000, 40000], 2, True, False, 0, True, 2, -1, False),    # wire order, mixed phases
+    (8, [1000000, 1500001, 3], 5, True, False, 1, True, 0, 0, False), # four-slice tiles
+    (8, [1000000, 1500001, 3], 5, True, False, 1, True, 0, 0, True),  # four-slice, accumulate
 ]
 
 
