@@ -264,7 +264,14 @@ class PrefetchCore {
         return PfErr::kOk;
     }
 
+    // Blocks until the outstanding gathers have finished (they write the
+    // arena), then frees the events. Errors are ignored: nothing is left to
+    // report them to.
     void destroy() {
+        while (!ongoing_.empty()) {
+            be_.sync(slots_[ongoing_.front()].ev);
+            retire_front();
+        }
         for (Slot& s : slots_)
             if (s.created) be_.destroy(s.ev);
         slots_.clear();

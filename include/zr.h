@@ -344,6 +344,8 @@ zr_status zr_sched_destroy(zr_sched* s);
  * gather_stream == compute_stream runs gathers and compute in series (no
  * overlap). The coordinator owns its HIP events and its copy of the trace;
  * it keeps the shard, arena and stream handles; it is not thread-safe.
+ * zr_pf_destroy blocks until the gathers it issued have finished; the
+ * caller frees the arenas once its own compute that reads them is done.
  */
 typedef struct zr_pf zr_pf;
 

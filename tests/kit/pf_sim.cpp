@@ -134,6 +134,9 @@ void pf_log(void* h, int64_t* out) {
     for (size_t i = 0; i < s->be.log.size(); ++i) out[i] = s->be.log[i];
 }
 
+// The core's destroy() alone (its log stays readable); pf_destroy frees.
+void pf_shutdown(void* h) { static_cast<Sim*>(h)->core.destroy(); }
+
 void pf_destroy(void* h) {
     Sim* s = static_cast<Sim*>(h);
     s->core.destroy();

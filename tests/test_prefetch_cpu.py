@@ -56,6 +56,7 @@ def lib():
         L.pf_log_size.restype = i64
         L.pf_log.argtypes = [vp, vp]
         L.pf_destroy.argtypes = [vp]
+        L.pf_shutdown.argtypes = [vp]
         _lib = L
     return _lib
 
@@ -406,6 +407,24 @@ def test_random_traces_have_no_stream_races(seed):
     r.walk(iterations=rng.randint(1, 3))
     r.check()
     assert r.stats()["live"] == 0
+    r.close()
+
+
+def test_destroy_waits_for_the_outstanding_gathers():
+    # the host never sees a gather finish, so the last ones are still writing
+    # the arena when the coordinator goes away: destroy blocks on each first
+    r = Run([100] * 8, [[p] for p in range(8)], bucket=200, max_live=10_000, arena=10_000,
+            query="never", g_per=10.0)
+    for t in range(3):
+        assert r.fetch(t) == OK
+        r.compute(t)
+        assert r.release(t) == OK
+    spans, _ = r.replay()
+    gather_end = max(spans[(g["stream"], g["idx"])][1] for g in r.gathers)
+    assert r.host < gather_end
+    lib().pf_shutdown(r.h)
+    r._drain()
+    assert r.host >= gather_end
     r.close()
 
 
