@@ -286,6 +286,8 @@ zr_status zr_rsf_plan_destroy(zr_rsf_plan* plan);
  * acquire on a buffer already acquired, or submit on one not acquired, is
  * ZR_ERR_INVALID. The scheduler owns only its HIP events (created in
  * zr_sched_create, destroyed in zr_sched_destroy); it is not thread-safe.
+ * zr_sched_destroy does not wait for queued reductions: flush into a stream
+ * the caller synchronises before freeing the buffers they read or write.
  */
 typedef struct zr_sched zr_sched;
 
