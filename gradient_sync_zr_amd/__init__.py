@@ -51,6 +51,7 @@ ZR_OK, ZR_ERR_INVALID, ZR_ERR_ALIGN, ZR_ERR_ALIAS, ZR_ERR_UNSUPPORTED, ZR_ERR_HI
 ZR_BF16, ZR_FP32 = 0, 1
 ZR_ORDER_RING, ZR_ORDER_FREE, ZR_ORDER_RING_WIRE = 0, 1, 2
 ZR_AVERAGE, ZR_ACCUMULATE = 1, 2
+ZR_MAX_RANKS, ZR_MAX_ELEMS = 64, 1 << 40
 STATUS_NAMES = {0: "ZR_OK", 1: "ZR_ERR_INVALID", 2: "ZR_ERR_ALIGN", 3: "ZR_ERR_ALIAS",
                 4: "ZR_ERR_UNSUPPORTED", 5: "ZR_ERR_HIP", 6: "ZR_ERR_NOMEM"}
 

@@ -190,6 +190,7 @@ class PrefetchCore {
     };
 
     explicit PrefetchCore(Backend& be) : be_(be) {}
+    ~PrefetchCore() { destroy(); }  // the backend must outlive the core
     PrefetchCore(const PrefetchCore&) = delete;
     PrefetchCore& operator=(const PrefetchCore&) = delete;
 

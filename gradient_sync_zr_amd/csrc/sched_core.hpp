@@ -33,6 +33,7 @@ class SchedCore {
     using Event = typename Backend::Event;
 
     SchedCore(Backend& be, Stream reduction) : be_(be), red_(reduction) {}
+    ~SchedCore() { release(); }  // the backend must outlive the core
     SchedCore(const SchedCore&) = delete;
     SchedCore& operator=(const SchedCore&) = delete;
 

@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "zr.h"
+#include "zr_guard.hpp"
 #include "zr_internal.hpp"
 
 namespace zr {
@@ -33,9 +34,9 @@ zr_status fail(zr_status st, const char* fmt, ...) {
 
 zr_status ok() { return ZR_OK; }
 
-// Largest element count per rank buffer (2^40): keeps every tile index of the
+// Largest element count per rank buffer: keeps every tile index of the
 // kernels within 32 bits.
-constexpr int64_t kMaxElems = 1LL << 40;
+constexpr int64_t kMaxElems = ZR_MAX_ELEMS;
 
 zr_status hip_fail(hipError_t e, const char* what) {
     return fail(ZR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -92,6 +93,18 @@ zr_status check_disjoint(const std::vector<Range>& xs, const char* xn, const std
             if (overlaps(xs[a], ys[b]))
                 return fail(ZR_ERR_ALIAS, "%s[%zu] overlaps %s[%zu]", xn, a, yn, b);
     return ok();
+}
+
+// Fragment sizes: each in [0, kMaxElems], and so is their running total.
+zr_status check_sizes(const int64_t* numels, int n, int64_t* total) {
+    *total = 0;
+    for (int p = 0; p < n; ++p) {
+        if (numels[p] < 0 || numels[p] > kMaxElems)
+            return fail(ZR_ERR_INVALID, "numels[%d]=%lld not in [0, 2^40]", p, (long long)numels[p]);
+        *total += numels[p];
+        if (*total > kMaxElems) return fail(ZR_ERR_INVALID, "fragments total more than 2^40 elements");
+    }
+    return ZR_OK;
 }
 
 #define ZR_TRY(expr)                       \
@@ -186,7 +199,8 @@ zr_status validate_ag(int K, const void* const* shards, void* const* fulls, zr_d
         if (segs[s].numel < 0 || segs[s].shard_off < 0 || segs[s].full_off < 0)
             return fail(ZR_ERR_INVALID, "segment %d has a negative field", s);
         if (segs[s].numel == 0) continue;
-        if (segs[s].numel > kMaxElems) return fail(ZR_ERR_INVALID, "segment %d too large", s);
+        if (segs[s].numel > kMaxElems || segs[s].shard_off > kMaxElems || segs[s].full_off > kMaxElems)
+            return fail(ZR_ERR_INVALID, "segment %d has a field above 2^40", s);
         const int64_t C = (segs[s].numel + K - 1) / K;
         full_lo = std::min(full_lo, segs[s].full_off);
         full_hi = std::max(full_hi, segs[s].full_off + segs[s].numel);
@@ -296,115 +310,122 @@ int zr_version(void) { return 100; }  // 0.1.0
 zr_status zr_reduce_scatter_avg(int K, const void* const* in, zr_dtype in_dt, int64_t N,
                                 void* const* out, zr_dtype out_dt, int chunk_shift, int flags,
                                 zr_order order, void* stream) {
-    bool no_work = false;
-    ZR_TRY(validate_rs(K, in, in_dt, N, out, out_dt, chunk_shift, flags, order, &no_work));
-    if (no_work) return ok();
-    return run_rs(K, in, in_dt, N, out, out_dt, chunk_shift, flags, order, (hipStream_t)stream);
+    return zr::guarded([&]() -> zr_status {
+        bool no_work = false;
+        ZR_TRY(validate_rs(K, in, in_dt, N, out, out_dt, chunk_shift, flags, order, &no_work));
+        if (no_work) return ok();
+        return run_rs(K, in, in_dt, N, out, out_dt, chunk_shift, flags, order, (hipStream_t)stream);
+    });
 }
 
 zr_status zr_all_gather(int K, const void* const* shards, void* const* fulls, zr_dtype dt,
                         const zr_seg* segs, int n_segs, int chunk_shift, void* stream) {
-    bool no_work = false;
-    ZR_TRY(validate_ag(K, shards, fulls, dt, segs, n_segs, chunk_shift, &no_work));
-    if (no_work) return ok();
-    return run_ag(K, shards, fulls, dt, segs, n_segs, chunk_shift, (hipStream_t)stream);
+    return zr::guarded([&]() -> zr_status {
+        bool no_work = false;
+        ZR_TRY(validate_ag(K, shards, fulls, dt, segs, n_segs, chunk_shift, &no_work));
+        if (no_work) return ok();
+        return run_ag(K, shards, fulls, dt, segs, n_segs, chunk_shift, (hipStream_t)stream);
+    });
 }
 
 zr_status zr_allreduce(int K, const void* const* in, void* const* out, zr_dtype dt, int64_t N,
                        int average, zr_order order, int fused, void* scratch, void* stream) {
-    ZR_TRY(check_k(K));
-    if (N < 0) return fail(ZR_ERR_INVALID, "N=%lld is negative", (long long)N);
-    if (!dt_valid(dt)) return fail(ZR_ERR_UNSUPPORTED, "dtype %d not supported", (int)dt);
-    if (order != ZR_ORDER_RING && order != ZR_ORDER_FREE && order != ZR_ORDER_RING_WIRE)
-        return fail(ZR_ERR_INVALID, "order=%d is not a zr_order", (int)order);
-    if (N == 0) return ok();
-    const int64_t es = dt_bytes(dt);
-    const int64_t C = (N + K - 1) / K;
-    if (N > kMaxElems) return fail(ZR_ERR_INVALID, "N=%lld too large", (long long)N);
-    ZR_TRY(check_table(in, K, es, "in"));
-    ZR_TRY(check_table(const_cast<const void* const*>(out), K, es, "out"));
-    std::vector<Range> ri(K), ro(K);
-    for (int r = 0; r < K; ++r) {
-        ri[r] = range_of(in[r], N, es);
-        ro[r] = range_of(out[r], N, es);
-    }
-    ZR_TRY(check_distinct(ro, "out"));
-    for (int a = 0; a < K; ++a)
-        for (int b = 0; b < K; ++b) {
-            if (a == b && in[a] == out[a]) continue;
-            if (overlaps(ro[a], ri[b]))
-                return fail(ZR_ERR_ALIAS, "out[%d] overlaps in[%d] (only out[r] == in[r] is allowed)", a, b);
-        }
-    hipStream_t s = (hipStream_t)stream;
-    if (fused) {
-        ConstPtrs ip{};
-        MutPtrs op{};
+    return zr::guarded([&]() -> zr_status {
+        ZR_TRY(check_k(K));
+        if (N < 0) return fail(ZR_ERR_INVALID, "N=%lld is negative", (long long)N);
+        if (!dt_valid(dt)) return fail(ZR_ERR_UNSUPPORTED, "dtype %d not supported", (int)dt);
+        if (order != ZR_ORDER_RING && order != ZR_ORDER_FREE && order != ZR_ORDER_RING_WIRE)
+            return fail(ZR_ERR_INVALID, "order=%d is not a zr_order", (int)order);
+        if (N == 0) return ok();
+        const int64_t es = dt_bytes(dt);
+        const int64_t C = (N + K - 1) / K;
+        if (N > kMaxElems) return fail(ZR_ERR_INVALID, "N=%lld too large", (long long)N);
+        ZR_TRY(check_table(in, K, es, "in"));
+        ZR_TRY(check_table(const_cast<const void* const*>(out), K, es, "out"));
+        std::vector<Range> ri(K), ro(K);
         for (int r = 0; r < K; ++r) {
-            ip.p[r] = in[r];
-            op.p[r] = out[r];
+            ri[r] = range_of(in[r], N, es);
+            ro[r] = range_of(out[r], N, es);
         }
-        hipError_t e = launch_allreduce_fused(K, ip, op, dt, N, average ? 1 : 0, order, s);
-        if (e != hipSuccess) return hip_fail(e, "all-reduce launch");
-        return ok();
-    }
-    if (!scratch) return fail(ZR_ERR_INVALID, "scratch is NULL (needed when fused == 0)");
-    if (((uintptr_t)scratch) % (uintptr_t)es) return fail(ZR_ERR_ALIGN, "scratch is not aligned");
-    const Range rsc = range_of(scratch, K * C, es);
-    for (int r = 0; r < K; ++r)
-        if (overlaps(rsc, ri[r]) || overlaps(rsc, ro[r]))
-            return fail(ZR_ERR_ALIAS, "scratch overlaps rank %d's buffers", r);
-    std::vector<void*> sh(K);
-    for (int q = 0; q < K; ++q) sh[q] = (char*)scratch + (size_t)(q * C * es);
-    ZR_TRY(run_rs(K, in, dt, N, sh.data(), dt, 1 % K, average ? ZR_AVERAGE : 0, order, s));
-    zr_seg seg{0, 0, N};
-    return run_ag(K, const_cast<const void* const*>(sh.data()), out, dt, &seg, 1, 1 % K, s);
+        ZR_TRY(check_distinct(ro, "out"));
+        for (int a = 0; a < K; ++a)
+            for (int b = 0; b < K; ++b) {
+                if (a == b && in[a] == out[a]) continue;
+                if (overlaps(ro[a], ri[b]))
+                    return fail(ZR_ERR_ALIAS, "out[%d] overlaps in[%d] (only out[r] == in[r] is allowed)", a, b);
+            }
+        hipStream_t s = (hipStream_t)stream;
+        if (fused) {
+            ConstPtrs ip{};
+            MutPtrs op{};
+            for (int r = 0; r < K; ++r) {
+                ip.p[r] = in[r];
+                op.p[r] = out[r];
+            }
+            hipError_t e = launch_allreduce_fused(K, ip, op, dt, N, average ? 1 : 0, order, s);
+            if (e != hipSuccess) return hip_fail(e, "all-reduce launch");
+            return ok();
+        }
+        if (!scratch) return fail(ZR_ERR_INVALID, "scratch is NULL (needed when fused == 0)");
+        if (((uintptr_t)scratch) % (uintptr_t)es) return fail(ZR_ERR_ALIGN, "scratch is not aligned");
+        const Range rsc = range_of(scratch, K * C, es);
+        for (int r = 0; r < K; ++r)
+            if (overlaps(rsc, ri[r]) || overlaps(rsc, ro[r]))
+                return fail(ZR_ERR_ALIAS, "scratch overlaps rank %d's buffers", r);
+        std::vector<void*> sh(K);
+        for (int q = 0; q < K; ++q) sh[q] = (char*)scratch + (size_t)(q * C * es);
+        ZR_TRY(run_rs(K, in, dt, N, sh.data(), dt, 1 % K, average ? ZR_AVERAGE : 0, order, s));
+        zr_seg seg{0, 0, N};
+        return run_ag(K, const_cast<const void* const*>(sh.data()), out, dt, &seg, 1, 1 % K, s);
+    });
 }
 
 zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const int64_t* numels,
                             void* const* buckets, int64_t padded_numel, zr_dtype dt, void* stream) {
-    ZR_TRY(check_k(K));
-    if (n_frag < 0) return fail(ZR_ERR_INVALID, "n_frag=%d is negative", n_frag);
-    if (!dt_valid(dt)) return fail(ZR_ERR_UNSUPPORTED, "dtype %d not supported", (int)dt);
-    if (n_frag > 0 && (!frags || !numels)) return fail(ZR_ERR_INVALID, "frags or numels is NULL");
-    const int64_t es = dt_bytes(dt);
-    int64_t total = 0;
-    for (int p = 0; p < n_frag; ++p) {
-        if (numels[p] < 0) return fail(ZR_ERR_INVALID, "numels[%d] is negative", p);
-        total += numels[p];
-    }
-    if (padded_numel < total)
-        return fail(ZR_ERR_INVALID, "padded_numel=%lld < total fragment size %lld", (long long)padded_numel,
-                    (long long)total);
-    if (padded_numel == 0) return ok();
-    ZR_TRY(check_table(const_cast<const void* const*>(buckets), K, es, "buckets"));
-    std::vector<Range> rb(K), rf;
-    for (int r = 0; r < K; ++r) rb[r] = range_of(buckets[r], padded_numel, es);
-    ZR_TRY(check_distinct(rb, "buckets"));
-    for (int r = 0; r < K; ++r)
-        for (int p = 0; p < n_frag; ++p) {
-            const void* f = frags[(size_t)r * n_frag + p];
-            if (numels[p] == 0) continue;
-            if (!f) return fail(ZR_ERR_INVALID, "fragment %d of rank %d is NULL", p, r);
-            if (((uintptr_t)f) % (uintptr_t)es)
-                return fail(ZR_ERR_ALIGN, "fragment %d of rank %d is not aligned", p, r);
-            rf.push_back(range_of(f, numels[p], es));
+    return zr::guarded([&]() -> zr_status {
+        ZR_TRY(check_k(K));
+        if (n_frag < 0) return fail(ZR_ERR_INVALID, "n_frag=%d is negative", n_frag);
+        if (!dt_valid(dt)) return fail(ZR_ERR_UNSUPPORTED, "dtype %d not supported", (int)dt);
+        if (n_frag > 0 && (!frags || !numels)) return fail(ZR_ERR_INVALID, "frags or numels is NULL");
+        const int64_t es = dt_bytes(dt);
+        int64_t total = 0;
+        ZR_TRY(check_sizes(numels, n_frag, &total));
+        if (padded_numel > kMaxElems)
+            return fail(ZR_ERR_INVALID, "padded_numel=%lld too large", (long long)padded_numel);
+        if (padded_numel < total)
+            return fail(ZR_ERR_INVALID, "padded_numel=%lld < total fragment size %lld", (long long)padded_numel,
+                        (long long)total);
+        if (padded_numel == 0) return ok();
+        ZR_TRY(check_table(const_cast<const void* const*>(buckets), K, es, "buckets"));
+        std::vector<Range> rb(K), rf;
+        for (int r = 0; r < K; ++r) rb[r] = range_of(buckets[r], padded_numel, es);
+        ZR_TRY(check_distinct(rb, "buckets"));
+        for (int r = 0; r < K; ++r)
+            for (int p = 0; p < n_frag; ++p) {
+                const void* f = frags[(size_t)r * n_frag + p];
+                if (numels[p] == 0) continue;
+                if (!f) return fail(ZR_ERR_INVALID, "fragment %d of rank %d is NULL", p, r);
+                if (((uintptr_t)f) % (uintptr_t)es)
+                    return fail(ZR_ERR_ALIGN, "fragment %d of rank %d is not aligned", p, r);
+                rf.push_back(range_of(f, numels[p], es));
+            }
+        ZR_TRY(check_disjoint(rb, "buckets", rf, "fragment"));
+        std::vector<CopyJob> jobs;
+        jobs.reserve((size_t)K * (n_frag + 1));
+        for (int r = 0; r < K; ++r) {
+            int64_t off = 0;
+            char* b = static_cast<char*>(buckets[r]);
+            for (int p = 0; p < n_frag; ++p) {
+                if (numels[p] > 0) jobs.push_back(CopyJob{frags[(size_t)r * n_frag + p], b + off * es, numels[p]});
+                off += numels[p];
+            }
+            if (padded_numel > off) jobs.push_back(CopyJob{nullptr, b + off * es, padded_numel - off});
         }
-    ZR_TRY(check_disjoint(rb, "buckets", rf, "fragment"));
-    std::vector<CopyJob> jobs;
-    jobs.reserve((size_t)K * (n_frag + 1));
-    for (int r = 0; r < K; ++r) {
-        int64_t off = 0;
-        char* b = static_cast<char*>(buckets[r]);
-        for (int p = 0; p < n_frag; ++p) {
-            if (numels[p] > 0) jobs.push_back(CopyJob{frags[(size_t)r * n_frag + p], b + off * es, numels[p]});
-            off += numels[p];
-        }
-        if (padded_numel > off) jobs.push_back(CopyJob{nullptr, b + off * es, padded_numel - off});
-    }
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_flatten(jobs.data(), (int)jobs.size(), (int)es, s);
-    if (e != hipSuccess) return hip_fail(e, "flatten launch");
-    return ok();
+        hipStream_t s = (hipStream_t)stream;
+        hipError_t e = launch_flatten(jobs.data(), (int)jobs.size(), (int)es, s);
+        if (e != hipSuccess) return hip_fail(e, "flatten launch");
+        return ok();
+    });
 }
 
 }  // extern "C"
@@ -430,10 +451,7 @@ zr_status make_frags_plan(int K, int n_frag, const void* const* frags, const int
         return fail(ZR_ERR_INVALID, "order=%d is not a zr_order", (int)order);
     if (n_frag > 0 && (!frags || !numels)) return fail(ZR_ERR_INVALID, "frags or numels is NULL");
     int64_t total = 0;
-    for (int p = 0; p < n_frag; ++p) {
-        if (numels[p] < 0) return fail(ZR_ERR_INVALID, "numels[%d] is negative", p);
-        total += numels[p];
-    }
+    ZR_TRY(check_sizes(numels, n_frag, &total));
     if (N < total)
         return fail(ZR_ERR_INVALID, "N=%lld < total fragment size %lld", (long long)N, (long long)total);
     if (N == 0) return ok();
@@ -479,7 +497,7 @@ zr_status make_frags_plan(int K, int n_frag, const void* const* frags, const int
     for (int r = 0; r < K; ++r) op.p[r] = out[r];
     *plan = rsf_plan_build(K, entries.data(), (int)entries.size(), N, in_dt, op, out_dt, chunk_shift,
                            flags, order);
-    if (!*plan) return fail(ZR_ERR_INVALID, "out of host memory");
+    if (!*plan) return fail(ZR_ERR_NOMEM, "out of host memory");
     return ok();
 }
 
@@ -496,31 +514,35 @@ zr_status zr_reduce_scatter_frags(int K, int n_frag, const void* const* frags,
                                   const int64_t* numels, int64_t N, zr_dtype in_dt,
                                   void* const* out, zr_dtype out_dt, int chunk_shift, int flags,
                                   zr_order order, void* stream) {
-    RsfPlan* plan = nullptr;
-    ZR_TRY(make_frags_plan(K, n_frag, frags, numels, N, in_dt, out, out_dt, chunk_shift, flags, order,
-                           &plan));
-    if (!plan) return ok();
-    const hipError_t e = rsf_plan_launch(plan, (hipStream_t)stream);
-    rsf_plan_free(plan);
-    if (e != hipSuccess) return hip_fail(e, "discrete reduce-scatter launch");
-    return ok();
+    return zr::guarded([&]() -> zr_status {
+        RsfPlan* plan = nullptr;
+        ZR_TRY(make_frags_plan(K, n_frag, frags, numels, N, in_dt, out, out_dt, chunk_shift, flags, order,
+                               &plan));
+        if (!plan) return ok();
+        const hipError_t e = rsf_plan_launch(plan, (hipStream_t)stream);
+        rsf_plan_free(plan);
+        if (e != hipSuccess) return hip_fail(e, "discrete reduce-scatter launch");
+        return ok();
+    });
 }
 
 zr_status zr_rsf_plan_create(int K, int n_frag, const void* const* frags, const int64_t* numels,
                              int64_t N, zr_dtype in_dt, void* const* out, zr_dtype out_dt,
                              int chunk_shift, int flags, zr_order order, zr_rsf_plan** plan) {
-    if (!plan) return fail(ZR_ERR_INVALID, "plan is NULL");
-    *plan = nullptr;
-    RsfPlan* p = nullptr;
-    ZR_TRY(make_frags_plan(K, n_frag, frags, numels, N, in_dt, out, out_dt, chunk_shift, flags, order,
-                           &p));
-    zr_rsf_plan* h = new (std::nothrow) zr_rsf_plan{p};
-    if (!h) {
-        if (p) rsf_plan_free(p);
-        return fail(ZR_ERR_INVALID, "out of host memory");
-    }
-    *plan = h;
-    return ok();
+    return zr::guarded([&]() -> zr_status {
+        if (!plan) return fail(ZR_ERR_INVALID, "plan is NULL");
+        *plan = nullptr;
+        RsfPlan* p = nullptr;
+        ZR_TRY(make_frags_plan(K, n_frag, frags, numels, N, in_dt, out, out_dt, chunk_shift, flags, order,
+                               &p));
+        zr_rsf_plan* h = new (std::nothrow) zr_rsf_plan{p};
+        if (!h) {
+            if (p) rsf_plan_free(p);
+            return fail(ZR_ERR_NOMEM, "out of host memory");
+        }
+        *plan = h;
+        return ok();
+    });
 }
 
 zr_status zr_rsf_plan_launch(const zr_rsf_plan* plan, void* stream) {
@@ -547,7 +569,8 @@ zr_status zr_plan_buckets(int n, const int64_t* numels, int64_t cap, int32_t* bu
     int32_t b = -1;
     int64_t total = 0;
     for (int i = 0; i < n; ++i) {
-        if (numels[i] < 0) return fail(ZR_ERR_INVALID, "numels[%d] is negative", i);
+        if (numels[i] < 0 || numels[i] > kMaxElems)
+            return fail(ZR_ERR_INVALID, "numels[%d]=%lld not in [0, 2^40]", i, (long long)numels[i]);
         if (b < 0 || total >= cap) {
             ++b;
             total = 0;

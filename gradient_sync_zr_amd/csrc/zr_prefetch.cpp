@@ -3,10 +3,11 @@
 // gathers finish at once, to size an arena on the host.
 #include <hip/hip_runtime.h>
 
-#include <new>
+#include <memory>
 #include <vector>
 
 #include "prefetch_core.hpp"
+#include "zr_guard.hpp"
 #include "zr.h"
 #include "zr_internal.hpp"
 
@@ -139,42 +140,42 @@ zr_status map_err(const zr::PfHip* be, zr::PfErr e, const char* what) {
 extern "C" {
 
 zr_status zr_pf_create(const zr_pf_config* cfg, zr_pf** out) {
-    if (!out) return zr::set_error(ZR_ERR_INVALID, "out is NULL");
-    *out = nullptr;
-    zr_status st = zr::validate_pf(cfg, true);
-    if (st != ZR_OK) return st;
-    zr_pf* pf = new (std::nothrow) zr_pf();
-    if (!pf) return zr::set_error(ZR_ERR_INVALID, "out of host memory");
-    zr::PfHip& be = pf->be;
-    be.K = cfg->K;
-    be.shift = cfg->chunk_shift;
-    be.dt = cfg->dtype;
-    be.shards.assign(cfg->shards, cfg->shards + cfg->K);
-    be.arenas.assign(cfg->arenas, cfg->arenas + cfg->K);
-    be.numels.assign(cfg->numels, cfg->numels + cfg->n_params);
-    be.shard_off.assign(cfg->shard_offsets, cfg->shard_offsets + cfg->n_params);
-    pf->es = cfg->dtype == ZR_BF16 ? 2 : 4;
-    zr::PfErr e = pf->core.init(zr::core_config<zr::PrefetchCore<zr::PfHip>>(
-        cfg, (hipStream_t)cfg->gather_stream, (hipStream_t)cfg->compute_stream));
-    if (e != zr::PfErr::kOk) {
-        st = map_err(&pf->be, e, "invalid trace");
-        pf->core.destroy();
-        delete pf;
-        return st;
-    }
-    *out = pf;
-    return ZR_OK;
+    return zr::guarded([&]() -> zr_status {
+        if (!out) return zr::set_error(ZR_ERR_INVALID, "out is NULL");
+        *out = nullptr;
+        zr_status st = zr::validate_pf(cfg, true);
+        if (st != ZR_OK) return st;
+        std::unique_ptr<zr_pf> pf(new zr_pf());
+        zr::PfHip& be = pf->be;
+        be.K = cfg->K;
+        be.shift = cfg->chunk_shift;
+        be.dt = cfg->dtype;
+        be.shards.assign(cfg->shards, cfg->shards + cfg->K);
+        be.arenas.assign(cfg->arenas, cfg->arenas + cfg->K);
+        be.numels.assign(cfg->numels, cfg->numels + cfg->n_params);
+        be.shard_off.assign(cfg->shard_offsets, cfg->shard_offsets + cfg->n_params);
+        pf->es = cfg->dtype == ZR_BF16 ? 2 : 4;
+        zr::PfErr e = pf->core.init(zr::core_config<zr::PrefetchCore<zr::PfHip>>(
+            cfg, (hipStream_t)cfg->gather_stream, (hipStream_t)cfg->compute_stream));
+        if (e != zr::PfErr::kOk) return map_err(&pf->be, e, "invalid trace");
+        *out = pf.release();
+        return ZR_OK;
+    });
 }
 
 zr_status zr_pf_fetch(zr_pf* pf, int step) {
-    if (!pf) return zr::set_error(ZR_ERR_INVALID, "coordinator is NULL");
-    pf->be.gather_st = ZR_OK;
-    return map_err(&pf->be, pf->core.fetch(step), "step out of range");
+    return zr::guarded([&]() -> zr_status {
+        if (!pf) return zr::set_error(ZR_ERR_INVALID, "coordinator is NULL");
+        pf->be.gather_st = ZR_OK;
+        return map_err(&pf->be, pf->core.fetch(step), "step out of range");
+    });
 }
 
 zr_status zr_pf_release(zr_pf* pf, int step) {
-    if (!pf) return zr::set_error(ZR_ERR_INVALID, "coordinator is NULL");
-    return map_err(&pf->be, pf->core.release(step), "step out of range");
+    return zr::guarded([&]() -> zr_status {
+        if (!pf) return zr::set_error(ZR_ERR_INVALID, "coordinator is NULL");
+        return map_err(&pf->be, pf->core.release(step), "step out of range");
+    });
 }
 
 zr_status zr_pf_full(const zr_pf* pf, int param, int rank, void** full) {
@@ -193,28 +194,28 @@ zr_status zr_pf_get_stats(const zr_pf* pf, zr_pf_stats* out) {
 }
 
 zr_status zr_pf_destroy(zr_pf* pf) {
-    if (!pf) return ZR_OK;
-    pf->core.destroy();
     delete pf;
     return ZR_OK;
 }
 
 zr_status zr_pf_plan(const zr_pf_config* cfg, int iterations, zr_pf_stats* out) {
-    if (!out) return zr::set_error(ZR_ERR_INVALID, "out is NULL");
-    if (iterations < 1) return zr::set_error(ZR_ERR_INVALID, "iterations < 1");
-    zr_status st = zr::validate_pf(cfg, false);
-    if (st != ZR_OK) return st;
-    zr::PfNull be;
-    zr::PrefetchCore<zr::PfNull> core(be);
-    zr::PfErr e = core.init(zr::core_config<zr::PrefetchCore<zr::PfNull>>(cfg, 0, 0));
-    for (int it = 0; it < iterations && e == zr::PfErr::kOk; ++it)
-        for (int t = 0; t < cfg->n_steps && e == zr::PfErr::kOk; ++t) {
-            e = core.fetch(t);
-            if (e == zr::PfErr::kOk) e = core.release(t);
-        }
-    zr::copy_stats(core.stats(), out);
-    core.destroy();
-    return map_err(nullptr, e, "invalid trace");
+    return zr::guarded([&]() -> zr_status {
+        if (!out) return zr::set_error(ZR_ERR_INVALID, "out is NULL");
+        if (iterations < 1) return zr::set_error(ZR_ERR_INVALID, "iterations < 1");
+        zr_status st = zr::validate_pf(cfg, false);
+        if (st != ZR_OK) return st;
+        zr::PfNull be;
+        zr::PrefetchCore<zr::PfNull> core(be);
+        zr::PfErr e = core.init(zr::core_config<zr::PrefetchCore<zr::PfNull>>(cfg, 0, 0));
+        for (int it = 0; it < iterations && e == zr::PfErr::kOk; ++it)
+            for (int t = 0; t < cfg->n_steps && e == zr::PfErr::kOk; ++t) {
+                e = core.fetch(t);
+                if (e == zr::PfErr::kOk) e = core.release(t);
+            }
+        zr::copy_stats(core.stats(), out);
+        core.destroy();
+        return map_err(nullptr, e, "invalid trace");
+    });
 }
 
 }  // extern "C"

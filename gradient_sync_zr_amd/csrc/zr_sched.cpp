@@ -1,7 +1,9 @@
 // C-ABI of the bucket/stream scheduler: SchedCore driven by HIP events.
 #include <hip/hip_runtime.h>
 
-#include <new>
+#include <memory>
+
+#include "zr_guard.hpp"
 
 #include "sched_core.hpp"
 #include "zr.h"
@@ -55,55 +57,55 @@ zr_status map_err(zr_sched* s, zr::SchedErr e, const char* what) {
 extern "C" {
 
 zr_status zr_sched_create(zr_sched** out, int n_buffers, int max_producers, void* reduction_stream) {
-    if (!out) return zr::set_error(ZR_ERR_INVALID, "out is NULL");
-    *out = nullptr;
-    if (n_buffers < 1 || n_buffers > 64) return zr::set_error(ZR_ERR_INVALID, "n_buffers not in [1, 64]");
-    if (max_producers < 0 || max_producers > 64)
-        return zr::set_error(ZR_ERR_INVALID, "max_producers not in [0, 64]");
-    zr_sched* s = new (std::nothrow) zr_sched((hipStream_t)reduction_stream);
-    if (!s) return zr::set_error(ZR_ERR_INVALID, "out of host memory");
-    zr::SchedErr e = s->core.init(n_buffers, max_producers);
-    if (e != zr::SchedErr::kOk) {
-        zr_status st = map_err(s, e, "init");
-        s->core.release();
-        delete s;
-        return st;
-    }
-    *out = s;
-    return ZR_OK;
+    return zr::guarded([&]() -> zr_status {
+        if (!out) return zr::set_error(ZR_ERR_INVALID, "out is NULL");
+        *out = nullptr;
+        if (n_buffers < 1 || n_buffers > 64) return zr::set_error(ZR_ERR_INVALID, "n_buffers not in [1, 64]");
+        if (max_producers < 0 || max_producers > 64)
+            return zr::set_error(ZR_ERR_INVALID, "max_producers not in [0, 64]");
+        std::unique_ptr<zr_sched> s(new zr_sched((hipStream_t)reduction_stream));
+        zr::SchedErr e = s->core.init(n_buffers, max_producers);
+        if (e != zr::SchedErr::kOk) return map_err(s.get(), e, "init");
+        *out = s.release();
+        return ZR_OK;
+    });
 }
 
 zr_status zr_sched_acquire(zr_sched* s, int buf, void* producer_stream) {
-    if (!s) return zr::set_error(ZR_ERR_INVALID, "scheduler is NULL");
-    return map_err(s, s->core.acquire(buf, (hipStream_t)producer_stream), "acquire");
+    return zr::guarded([&]() -> zr_status {
+        if (!s) return zr::set_error(ZR_ERR_INVALID, "scheduler is NULL");
+        return map_err(s, s->core.acquire(buf, (hipStream_t)producer_stream), "acquire");
+    });
 }
 
 zr_status zr_sched_submit_rs(zr_sched* s, int buf, void* const* producer_streams, int n_prod, int K,
                              const void* const* in, zr_dtype in_dt, int64_t N, void* const* out,
                              zr_dtype out_dt, int chunk_shift, int flags, zr_order order) {
-    if (!s) return zr::set_error(ZR_ERR_INVALID, "scheduler is NULL");
-    bool no_work = false;
-    zr_status st = zr::validate_rs(K, in, in_dt, N, out, out_dt, chunk_shift, flags, order, &no_work);
-    if (st != ZR_OK) return st;
-    zr_status launch_st = ZR_OK;
-    auto launch = [&](hipStream_t red) {
-        if (no_work) return true;
-        launch_st = zr::run_rs(K, in, in_dt, N, out, out_dt, chunk_shift, flags, order, red);
-        return launch_st == ZR_OK;
-    };
-    zr::SchedErr e = s->core.submit(buf, reinterpret_cast<const hipStream_t*>(producer_streams), n_prod, launch);
-    if (e == zr::SchedErr::kBackend && launch_st != ZR_OK) return launch_st;
-    return map_err(s, e, "submit");
+    return zr::guarded([&]() -> zr_status {
+        if (!s) return zr::set_error(ZR_ERR_INVALID, "scheduler is NULL");
+        bool no_work = false;
+        zr_status st = zr::validate_rs(K, in, in_dt, N, out, out_dt, chunk_shift, flags, order, &no_work);
+        if (st != ZR_OK) return st;
+        zr_status launch_st = ZR_OK;
+        auto launch = [&](hipStream_t red) {
+            if (no_work) return true;
+            launch_st = zr::run_rs(K, in, in_dt, N, out, out_dt, chunk_shift, flags, order, red);
+            return launch_st == ZR_OK;
+        };
+        zr::SchedErr e = s->core.submit(buf, reinterpret_cast<const hipStream_t*>(producer_streams), n_prod, launch);
+        if (e == zr::SchedErr::kBackend && launch_st != ZR_OK) return launch_st;
+        return map_err(s, e, "submit");
+    });
 }
 
 zr_status zr_sched_flush(zr_sched* s, void* caller_stream) {
-    if (!s) return zr::set_error(ZR_ERR_INVALID, "scheduler is NULL");
-    return map_err(s, s->core.flush((hipStream_t)caller_stream), "flush");
+    return zr::guarded([&]() -> zr_status {
+        if (!s) return zr::set_error(ZR_ERR_INVALID, "scheduler is NULL");
+        return map_err(s, s->core.flush((hipStream_t)caller_stream), "flush");
+    });
 }
 
 zr_status zr_sched_destroy(zr_sched* s) {
-    if (!s) return ZR_OK;
-    s->core.release();
     delete s;
     return ZR_OK;
 }

@@ -68,7 +68,8 @@ typedef enum {
     ZR_ERR_ALIAS = 3,       /* overlapping buffers that must not overlap */
     ZR_ERR_UNSUPPORTED = 4, /* dtype or dtype pair not supported */
     ZR_ERR_HIP = 5,         /* a HIP runtime call or launch failed */
-    ZR_ERR_NOMEM = 6        /* a caller-provided arena cannot hold what must be live */
+    ZR_ERR_NOMEM = 6        /* host memory ran out, or a caller-provided arena
+                               cannot hold what must be live */
 } zr_status;
 
 typedef enum { ZR_BF16 = 0, ZR_FP32 = 1 } zr_dtype;
@@ -94,6 +95,9 @@ typedef struct {
 } zr_seg;
 
 #define ZR_MAX_RANKS 64
+/* Largest element count of any one buffer, fragment, bucket, segment or
+ * offset (2^40); larger sizes are ZR_ERR_INVALID. */
+#define ZR_MAX_ELEMS (1LL << 40)
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* zr_last_error(void);

@@ -252,6 +252,45 @@ def test_plan_buckets_transformer_50mb():
     assert nb == len(greedy_reference([p.numel for p in ps], cap))
     with pytest.raises(zr.ZrError):
         zr.zr_plan_buckets([1, 2], 0)
+    with pytest.raises(zr.ZrError):
+        zr.zr_plan_buckets([1, zr.ZR_MAX_ELEMS + 1], 10)
+
+
+def test_header_constants_match_the_binding():
+    text = open(os.path.join(ROOT, "include", "zr.h")).read()
+    assert re.search(r"#define ZR_MAX_RANKS 64\b", text) and zr.ZR_MAX_RANKS == 64
+    assert re.search(r"#define ZR_MAX_ELEMS \(1LL << 40\)", text) and zr.ZR_MAX_ELEMS == 1 << 40
+
+
+def test_sizes_above_the_element_limit_are_rejected():
+    # every size, offset and running total stays within ZR_MAX_ELEMS, so tile
+    # numbers fit the kernels' 32 bits; rejected before any HIP call
+    lib = zr.lib()
+    big = zr.ZR_MAX_ELEMS
+    K, F = 2, 3
+    fr = (ctypes.c_void_p * (K * F))(*ranks(K * F))
+    o = (ctypes.c_void_p * K)(*ranks(K, base=A + (1 << 41)))
+
+    def flatten(numels, padded):
+        nm = (ctypes.c_int64 * F)(*numels)
+        return lib.zr_flatten_bucket(K, F, fr, nm, o, padded, zr.ZR_BF16, None)
+
+    def frags(numels, N):
+        nm = (ctypes.c_int64 * F)(*numels)
+        return lib.zr_reduce_scatter_frags(K, F, fr, nm, N, zr.ZR_BF16, o, zr.ZR_FP32, 1, 1, 0, None)
+
+    for fn in (flatten, frags):
+        assert fn([1, big + 1, 3], big + 8) == zr.ZR_ERR_INVALID       # one fragment too large
+        assert fn([big, 1, 0], big + 1) == zr.ZR_ERR_INVALID          # their total too large
+        assert fn([1 << 62, 1 << 62, 1 << 62], 8) == zr.ZR_ERR_INVALID  # a total that would wrap
+    assert flatten([1, 2, 3], big + 1) == zr.ZR_ERR_INVALID           # the padded bucket
+    s = (ctypes.c_void_p * 8)(*ranks(8))
+    f = (ctypes.c_void_p * 8)(*ranks(8, base=A + (1 << 41)))
+    for seg in ((big + 1, 0, 10), (0, big + 1, 10), (0, 0, big + 1)):
+        arr = (zr.zr_seg * 1)(zr.zr_seg(*seg))
+        assert lib.zr_all_gather(8, s, f, zr.ZR_BF16, arr, 1, 0, None) == zr.ZR_ERR_INVALID
+    t = (ctypes.c_void_p * 8)(*ranks(8))
+    assert lib.zr_reduce_scatter_avg(8, t, 0, big + 1, f, 1, 1, 1, 0, None) == zr.ZR_ERR_INVALID
 
 
 def test_prefetch_config_validation():
