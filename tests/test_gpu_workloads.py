@@ -224,8 +224,10 @@ def test_zero2_grad_sync_full_size_sampled():
 # ------------------------------------------------ discrete path, one layer
 def test_frags_layer_discrete_full_size():
     """The discrete reduce-scatter over one layer's seven gradients per rank,
-    at full size: sampled outputs against the oracle, every output equal to
-    flatten + contiguous reduce-scatter on the GPU, every element written."""
+    at full size: sampled outputs against the oracle from the host generator,
+    every output against the oracle's flatten + reduce-scatter of the
+    fragments copied to the host, every output equal to flatten + contiguous
+    reduce-scatter on the GPU, every element written."""
     import torch
     cfg = W.FRAGS_LAYER
     K, sigma, shift = cfg["K"], cfg["sigma"], cfg["shift"]
@@ -266,6 +268,17 @@ def test_frags_layer_discrete_full_size():
     for q in range(K):
         got = parts[q].index_select(0, idx).cpu().numpy()
         assert np.array_equal(bits(got), bits(want[q])), f"rank {q}"
+    # whole outputs against the oracle: the fragments copied to the host,
+    # flattened into padded buckets and reduced there
+    fh = [[down16(f) for f in frags[r]] for r in range(K)]
+    bh = oracle.flatten(fh, sizes, K * C)
+    del fh
+    want = oracle_rs_threaded(bh, N, shift)
+    del bh
+    for q in range(K):
+        assert np.array_equal(bits(parts[q].cpu().numpy()), bits(want[q])), f"rank {q}"
+    del want
+    say("frags_layer: every output bit-exact against the oracle")
     # whole outputs: the same as flattening into a bucket and reducing it
     buckets = [torch.empty(K * C, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
     zr().zr_flatten_bucket(frags, sizes, buckets, K * C)
