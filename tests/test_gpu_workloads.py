@@ -46,16 +46,21 @@ def zr():
 THREADS = 16  # host threads for whole-output oracle checks
 
 
-def oracle_rs_threaded(xs, N, shift):
+def oracle_rs_threaded(xs, N, shift, old=None):
     """The oracle's reduce-scatter + /K of a whole bucket into fp32, split over
-    host threads by chunk offset."""
+    host threads by chunk offset; with `old` (the K partitions before the
+    call) it accumulates into them."""
     K = len(xs)
     C = -(-N // K)
-    outs = [np.empty(C, dtype=np.float32) for _ in range(K)]
+    if old is None:
+        outs = [np.empty(C, dtype=np.float32) for _ in range(K)]
+    else:
+        outs = [np.array(o, dtype=np.float32) for o in old]
 
     def work(i):
         oracle.reduce_scatter(xs, N, np.float32, shift=shift, average=True,
-                              o_range=(i * C // THREADS, (i + 1) * C // THREADS), out=outs)
+                              o_range=(i * C // THREADS, (i + 1) * C // THREADS), out=outs,
+                              accumulate=old is not None)
     th = [threading.Thread(target=work, args=(i,)) for i in range(THREADS)]
     for t in th:
         t.start()
@@ -209,16 +214,28 @@ def test_zero2_grad_sync_full_size_sampled():
         del xs, want
         poff += Cb
     say("zero2: every partition element bit-exact against the oracle")
-    # gradient accumulation at full size: a second micro-step of the same
-    # gradients adds the same averages, so every partition doubles exactly
-    first = [p.clone() for p in parts]
+    # gradient accumulation at full size: a second micro-step with new
+    # gradients adds its averages to the partitions; every element against
+    # the oracle's accumulating reduce-scatter
+    first = [p.cpu().numpy() for p in parts]
+    for r in range(K):
+        synth.dev_normal_bf16(grads[r], seed + 0x100, r, 0, sigma)
     sync.step(micro_step=1)
     torch.cuda.synchronize()
-    for q in range(K):
-        assert torch.equal(parts[q], first[q] * 2), f"accumulate rank {q}"
+    poff = 0
+    for (start, n) in buckets:
+        Cb = -(-n // K)
+        xs = [grads[r][start:start + n].view(torch.int16).cpu().numpy().view(np.uint16)
+              for r in range(K)]
+        want = oracle_rs_threaded(xs, n, cfg["shift"], old=[f[poff:poff + Cb] for f in first])
+        for q in range(K):
+            got = parts[q][poff:poff + Cb].cpu().numpy()
+            assert np.array_equal(bits(got), bits(want[q])), f"accumulate bucket at {start}, rank {q}"
+        del xs, want
+        poff += Cb
     del first
     sync.close()
-    say("zero2: sampled outputs bit-exact; accumulation micro-step doubles exactly")
+    say("zero2: sampled outputs bit-exact; accumulation micro-step bit-exact on every element")
 
 
 # ------------------------------------------------ discrete path, one layer
