@@ -10,9 +10,15 @@ Byte model (the method's minimum traffic, each input read once, each output
 written once): per element index K*2 bytes read + 4 bytes written = 20 B,
 so 47.53 GB per step. `value` = those bytes / step time.
 
-Other workloads (--workload): zero3_ag (the 32-layer transformer all-gather
-in 162 prefetch buckets), allreduce64 (K = 64, N = 1,000,000,007 fused
-in-place all-reduce), flatten8 (the 64-fragment bucket flatten).
+Other workloads (--workload):
+  zero2_accum     the same sync as a later micro-step (adds into the partitions)
+  zero3_ag        the 32-layer transformer all-gather in 162 prefetch buckets
+  zero3_prefetch  the prefetch coordinator walking that model's trace, with a
+                  synthetic compute per step; reports the pass time in ms
+  allreduce64     K = 64, N = 1,000,000,007 fused in-place all-reduce
+  flatten8        the 64-fragment bucket: flatten + reduce-scatter against the
+                  discrete path, in microseconds per call (cache-resident)
+  frags_layer     the discrete reduce-scatter over one layer's seven gradients
 
 Prints one JSON line. Only one GPU is used; --gpus above 1 exits.
 """
