@@ -16,8 +16,9 @@
 // lands contiguously in one holder's partition, so it is reduced like a chunk
 // of the contiguous kernel: the same 4-wave x S-slice x 256-element tiles of
 // lane-owned quads, every rank's loads in flight before the ring-order adds,
-// non-temporal streams. A launch carries up to 32 fragments' rank pointers,
-// their segments and each segment's first tile in its kernel arguments; the
+// non-temporal streams. A launch carries up to 32 fragments' rank pointers
+// (the padding entry, which has none, takes a spare slot after them), their
+// segments and each segment's first tile in its kernel arguments; the
 // grid strides over the launch's tiles in order, so blocks stay balanced
 // however unequal the fragments are. A segment whose rank buffers share one
 // quad phase starts its vector tiles at rank j's next 128-byte line: the
@@ -34,10 +35,14 @@
 namespace zr {
 namespace {
 
+// Entry slots: kRsfEntriesPerLaunch fragments with rank pointers, plus one
+// more for the padding entry, which has none.
+constexpr int kRsfSlots = kRsfEntriesPerLaunch + 1;
+
 struct RsfArgs {
-    const void* ptr[kRsfPtrsPerLaunch];    // entry-major: ptr[m * K + r]; null: padding entry
-    int64_t off[kRsfEntriesPerLaunch];     // virtual-bucket offset of entry m
-    int64_t n[kRsfEntriesPerLaunch];       // elements of entry m
+    const void* ptr[kRsfPtrsPerLaunch];    // entry-major: ptr[m * K + r]
+    int64_t off[kRsfSlots];                // virtual-bucket offset of entry m
+    int64_t n[kRsfSlots];                  // elements of entry m
     MutPtrs out;
     int32_t tile0[kRsfSegsPerLaunch + 1];  // first tile of segment s; tile0[nseg] = all tiles
     uint8_t seg_m[kRsfSegsPerLaunch];      // entry of segment s
@@ -45,6 +50,7 @@ struct RsfArgs {
     int16_t seg_head[kRsfSegsPerLaunch];   // vector tiles start at this offset; -1: element-wise
     int64_t C;
     int K, shift, accumulate, nseg;
+    int pad_m;                             // the padding entry (writes +0), -1: none
     float inv_k, kf;
 };
 static_assert(sizeof(RsfArgs) <= 4096, "discrete reduce-scatter arguments exceed 4 KB");
@@ -71,7 +77,7 @@ __global__ void __launch_bounds__(kThreads) rsf_kernel(const RsfArgs a) {
         const int64_t l_lo = lo - f0, len = hi - lo;  // fragment-local start, length
         TOut* outp = static_cast<TOut*>(a.out.p[wrap(j - a.shift + K, K)]) + (lo - jc);
         auto ptr = [&](int r) __attribute__((always_inline)) { return a.ptr[m * K + r]; };
-        const bool pad = ptr(0) == nullptr;
+        const bool pad = m == a.pad_m;
         const int64_t tt = t - a.tile0[s];
         const int64_t h = a.seg_head[s];
 
@@ -213,8 +219,9 @@ int16_t segment_head(const uintptr_t* addr, int K, int j, uintptr_t es) {
 }
 
 // Cuts the entries into launches: each fills one argument block with up to
-// kRsfEntriesPerLaunch fragments (and kRsfPtrsPerLaunch rank pointers) and
-// the segments they form with the chunks.
+// kRsfEntriesPerLaunch fragments (and kRsfPtrsPerLaunch rank pointers), the
+// padding entry if it comes next (it takes no pointers), and the segments
+// they form with the chunks.
 template <typename TIn, typename TOut>
 void build_typed(RsfArgs& a, const FragEntry* entries, int n_entries, int64_t T,
                  std::vector<RsfArgs>* out) {
@@ -225,6 +232,7 @@ void build_typed(RsfArgs& a, const FragEntry* entries, int n_entries, int64_t T,
     int m = 0;
     int64_t tiles = 0;
     a.nseg = 0;
+    a.pad_m = -1;
     auto flush = [&]() {
         if (m == 0) return;
         a.tile0[a.nseg] = (int32_t)tiles;
@@ -232,15 +240,21 @@ void build_typed(RsfArgs& a, const FragEntry* entries, int n_entries, int64_t T,
         m = 0;
         tiles = 0;
         a.nseg = 0;
+        a.pad_m = -1;
     };
     for (int ei = 0; ei < n_entries; ++ei) {
         const FragEntry& f = entries[ei];
+        const bool pad = f.ptr[0] == nullptr;
         const int j0 = (int)(f.off / C), j1 = (int)((f.off + f.n - 1) / C);
-        if (m == max_entries || a.nseg + (j1 - j0 + 1) > kRsfSegsPerLaunch) flush();
+        if (m == (pad ? max_entries + 1 : max_entries) || a.pad_m >= 0 ||
+            a.nseg + (j1 - j0 + 1) > kRsfSegsPerLaunch)
+            flush();
         a.off[m] = f.off;
         a.n[m] = f.n;
-        for (int r = 0; r < K; ++r) a.ptr[m * K + r] = f.ptr[r];
-        const bool pad = f.ptr[0] == nullptr;
+        if (pad)
+            a.pad_m = m;
+        else
+            for (int r = 0; r < K; ++r) a.ptr[m * K + r] = f.ptr[r];
         for (int j = j0; j <= j1; ++j) {
             const int64_t jc = (int64_t)j * C;
             const int64_t lo = f.off > jc ? f.off : jc;

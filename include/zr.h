@@ -173,8 +173,9 @@ zr_status zr_reduce_scatter_avg(int K, const void* const* in, zr_dtype in_dt, in
  *  out, flags, order, chunk_shift: as zr_reduce_scatter_avg
  * Outputs must be distinct and must not overlap any fragment (ZR_ERR_ALIAS).
  * Fragment tables travel in kernel arguments: a launch carries up to 32
- * fragments (256 rank pointers at most, so 4 fragments at K = 64) and the
- * at most 96 (fragment, chunk) pieces they form.
+ * fragments (256 rank pointers at most, so 4 fragments at K = 64), the zero
+ * padding when it comes next (it has no pointers), and the at most 96
+ * (fragment, chunk) pieces they form.
  */
 zr_status zr_reduce_scatter_frags(int K, int n_frag, const void* const* frags,
                                   const int64_t* numels, int64_t N, zr_dtype in_dt,

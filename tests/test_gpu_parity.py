@@ -386,6 +386,10 @@ FRAG_CASES = [
     (8, [6, 30000, 40000], 2, True, False, 0, True, 2, -1, False),    # wire order, mixed phases
     (8, [1000000, 1500001, 3], 5, True, False, 1, True, 0, 0, False), # four-slice tiles
     (8, [1000000, 1500001, 3], 5, True, False, 1, True, 0, 0, True),  # four-slice, accumulate
+    # the padding entry takes the slot after the last fragment of a launch
+    (8, [97 * (i + 1) for i in range(32)], 20000, True, False, 1, True, 0, 0, False),  # over 3 chunks
+    (8, [50 + 13 * i for i in range(33)], 9, True, False, 1, True, 0, 0, True),  # 32 + (1 + padding)
+    (64, [32000] * 6, 64 * 40, True, False, 1, True, 0, 0, False),     # 4 fragments per launch
 ]
 
 
@@ -458,7 +462,7 @@ def test_reduce_scatter_frags_bit_exact(K, sizes, extra, in_bf16, out_bf16, shif
             assert g.guards_intact()
 
 
-@pytest.mark.parametrize("case", [FRAG_CASES[i] for i in (0, 1, 3, 5, 6, 7, 8, 11, 13)])
+@pytest.mark.parametrize("case", [FRAG_CASES[i] for i in (0, 1, 3, 5, 6, 7, 8, 11, 13, 17, 18, 19)])
 def test_rsf_plan_launches_equal_the_call(case):
     # a plan built once, launched twice (the fragments rewritten in place in
     # between), against the one-shot call with the same arguments each time
