@@ -410,19 +410,35 @@ zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const i
                 rf.push_back(range_of(f, numels[p], es));
             }
         ZR_TRY(check_disjoint(rb, "buckets", rf, "fragment"));
-        std::vector<CopyJob> jobs;
-        jobs.reserve((size_t)K * (n_frag + 1));
-        for (int r = 0; r < K; ++r) {
-            int64_t off = 0;
-            char* b = static_cast<char*>(buckets[r]);
-            for (int p = 0; p < n_frag; ++p) {
-                if (numels[p] > 0) jobs.push_back(CopyJob{frags[(size_t)r * n_frag + p], b + off * es, numels[p]});
-                off += numels[p];
+        // one entry per fragment (every rank's copy of it), then the padding;
+        // a fragment of more than 2^28 / K tiles of 16 KiB per rank is cut
+        // into pieces of that many, so tile numbers fit the kernel's 32 bits
+        const int64_t piece = ((1LL << 28) / K) * (16384 / es);
+        std::vector<FragEntry> entries;
+        auto add = [&](const void* const* ptrs, int64_t off, int64_t n) {
+            for (int64_t o = 0; o < n; o += piece) {
+                FragEntry f{};
+                if (ptrs)
+                    for (int r = 0; r < K; ++r) f.ptr[r] = static_cast<const char*>(ptrs[r]) + o * es;
+                f.off = off + o;
+                f.n = std::min(piece, n - o);
+                entries.push_back(f);
             }
-            if (padded_numel > off) jobs.push_back(CopyJob{nullptr, b + off * es, padded_numel - off});
+        };
+        std::vector<const void*> rp(K);
+        int64_t off = 0;
+        for (int p = 0; p < n_frag; ++p) {
+            if (numels[p] > 0) {
+                for (int r = 0; r < K; ++r) rp[r] = frags[(size_t)r * n_frag + p];
+                add(rp.data(), off, numels[p]);
+            }
+            off += numels[p];
         }
+        if (padded_numel > off) add(nullptr, off, padded_numel - off);
+        MutPtrs bp{};
+        for (int r = 0; r < K; ++r) bp.p[r] = buckets[r];
         hipStream_t s = (hipStream_t)stream;
-        hipError_t e = launch_flatten(jobs.data(), (int)jobs.size(), (int)es, s);
+        hipError_t e = launch_flatten(K, entries.data(), (int)entries.size(), bp, (int)es, s);
         if (e != hipSuccess) return hip_fail(e, "flatten launch");
         return ok();
     });

@@ -4,18 +4,25 @@
 // offset n_0 + ... + n_{p-1} of the flat buffer; 3.1: one large contiguous
 // message instead of one per parameter).
 //
-// A launch carries up to 96 copy jobs and each job's first tile in its
-// kernel arguments (no device descriptor table, no staging copy); the grid
-// strides over the launch's tiles in order, so blocks stay balanced however
-// unequal the jobs are. A tile is 16 KiB of destination (4 KiB in launches
-// too small to fill the device): lane l of wave w moves the 16-byte units
-// w*64*U + k*64 + l (k < U = 4 or 1), so every load and store instruction of
-// a wave covers 1 KiB contiguously, with all loads in flight before the
-// stores; loads and stores are non-temporal (each byte is touched once). A job whose source and destination both start 16-byte
-// aligned copies whole units; its last partial unit, and every unit of a job
-// that is not aligned so (possible inside a bucket, where offsets are prefix
-// sums of arbitrary sizes), copies element by element. A job with no source
-// writes zeros.
+// Every rank has the same fragment sizes, so a fragment is one entry: its
+// bucket offset and size, shared by the ranks, and its K source pointers. A
+// launch carries up to 32 entries' pointers (256 pointers, so 4 entries at
+// K = 64), the zero padding in a spare slot after them (it has no source),
+// the K bucket bases and each entry's first tile, all in its kernel
+// arguments: no device descriptor table, no staging copy. Entry m owns K
+// runs of tiles_per_rank[m] tiles, rank by rank; the grid strides over the
+// launch's tiles in order, so blocks stay balanced however unequal the
+// fragments are.
+//
+// A tile is 16 KiB of destination (4 KiB in launches too small to fill the
+// device): lane l of wave w moves the 16-byte units w*64*U + k*64 + l
+// (k < U = 4 or 1), so every load and store instruction of a wave covers
+// 1 KiB contiguously, with all loads in flight before the stores; loads and
+// stores are non-temporal (each byte is touched once). A copy whose source
+// and destination both start 16-byte aligned moves whole units; its last
+// partial unit, and every unit of a copy that is not aligned so (possible
+// inside a bucket, where offsets are prefix sums of arbitrary sizes), copies
+// element by element.
 #include "zr_device.hpp"
 #include "zr_internal.hpp"
 
@@ -27,10 +34,17 @@ namespace {
 template <int U>
 constexpr int64_t kFlatTileBytes = (int64_t)kThreads * 16 * U;
 
+// Entry slots: fragments with source pointers, plus one for the padding.
+constexpr int kFlatSlots = kFlatEntriesPerLaunch + 1;
+
 struct FlatArgs {
-    CopyJob job[kFlatJobsPerLaunch];
-    int32_t tile0[kFlatJobsPerLaunch + 1];  // first tile of job m; tile0[n_jobs] = all tiles
-    int n_jobs;
+    const void* src[kFlatPtrsPerLaunch];  // entry-major: src[m * K + r]
+    void* bucket[kMaxRanks];               // rank r's bucket
+    int64_t off[kFlatSlots];               // bucket offset of entry m (elements)
+    int64_t n[kFlatSlots];                 // elements of entry m
+    int32_t tile0[kFlatSlots + 1];         // first tile of entry m; tile0[nent] = all tiles
+    int32_t tpr[kFlatSlots];               // tiles of entry m per rank
+    int K, nent, pad_m;                    // pad_m: the padding entry (writes zeros), -1: none
 };
 static_assert(sizeof(FlatArgs) <= 4096, "flatten arguments exceed 4 KB");
 
@@ -38,18 +52,19 @@ template <typename T, int U>
 __global__ void __launch_bounds__(kThreads) flatten_kernel(const FlatArgs a) {
     constexpr int per = 16 / sizeof(T);  // elements per 16-byte unit
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int total = a.tile0[a.n_jobs];
+    const int total = a.tile0[a.nent];
     int m = 0;
     for (int t = blockIdx.x; t < total; t += gridDim.x) {
-        m = find_slot(a.tile0, a.n_jobs, m, t);  // a block's tiles only grow: jobs in order
-        const CopyJob jb = a.job[m];
-        const int64_t tt = t - a.tile0[m];
-        const bool vec = ((((uintptr_t)jb.dst) & 15) == 0) &&
-                         (jb.src == nullptr || (((uintptr_t)jb.src) & 15) == 0);
-        const T* src = static_cast<const T*>(jb.src);
-        T* dst = static_cast<T*>(jb.dst);
-        const int64_t u0 = tt * (kFlatTileBytes<U> / 16) + wave * 64 * U + lane;  // first unit
-        if (vec && (u0 + 64 * (U - 1) + 1) * per <= jb.n) {
+        m = find_slot(a.tile0, a.nent, m, t);  // a block's tiles only grow: entries in order
+        const int tt = t - a.tile0[m];
+        const int r = tt / a.tpr[m];            // the entry's tiles run rank by rank
+        const int64_t lt = tt - (int64_t)r * a.tpr[m];
+        const int64_t n = a.n[m];
+        const T* src = m == a.pad_m ? nullptr : static_cast<const T*>(a.src[m * a.K + r]);
+        T* dst = static_cast<T*>(a.bucket[r]) + a.off[m];
+        const bool vec = ((((uintptr_t)dst) & 15) == 0) && (src == nullptr || (((uintptr_t)src) & 15) == 0);
+        const int64_t u0 = lt * (kFlatTileBytes<U> / 16) + wave * 64 * U + lane;  // first unit
+        if (vec && (u0 + 64 * (U - 1) + 1) * per <= n) {
             // every unit of this lane is whole
             u32x4 v[U];
 #pragma unroll
@@ -70,7 +85,7 @@ __global__ void __launch_bounds__(kThreads) flatten_kernel(const FlatArgs a) {
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             const int64_t e0 = (u0 + 64 * k) * per;
-            cnt[k] = e0 >= jb.n ? 0 : (int)((jb.n - e0) < per ? (jb.n - e0) : per);
+            cnt[k] = e0 >= n ? 0 : (int)((n - e0) < per ? (n - e0) : per);
             if (vec && cnt[k] == per) {
                 vv[k] = src ? ld<true>(reinterpret_cast<const u32x4*>(src + e0)) : u32x4{0u, 0u, 0u, 0u};
             } else {
@@ -94,7 +109,8 @@ __global__ void __launch_bounds__(kThreads) flatten_kernel(const FlatArgs a) {
 }
 
 template <typename T, int U>
-hipError_t launch_batch(const FlatArgs& a, int64_t tiles, hipStream_t stream) {
+hipError_t launch_batch(const FlatArgs& a, hipStream_t stream) {
+    const int64_t tiles = a.tile0[a.nent];
     const int64_t want = (int64_t)device_cu_count() * 8;
     const int gx = (int)(want < tiles ? want : tiles);
     hipLaunchKernelGGL((flatten_kernel<T, U>), dim3(gx), dim3(kThreads), 0, stream, a);
@@ -105,12 +121,18 @@ int64_t tiles_of(int64_t bytes, int64_t tile) { return (bytes + tile - 1) / tile
 
 }  // namespace
 
-// Jobs go out in launches of at most kFlatJobsPerLaunch jobs and about 2^30
-// tiles (a single job has at most 2^28 tiles), so tile numbers fit in 32 bits.
+// Entries go out in launches of at most 32 fragments (256 source pointers)
+// plus the padding entry if it comes next, and about 2^30 tiles; a larger
+// entry has already been split by the caller, so tile numbers fit in 32 bits.
 // A launch with fewer 16 KiB tiles than two per CU uses 4 KiB tiles.
-hipError_t launch_flatten(const CopyJob* jobs, int n_jobs, int elem_bytes, hipStream_t stream) {
+hipError_t launch_flatten(int K, const FragEntry* entries, int n_entries, const MutPtrs& buckets,
+                          int elem_bytes, hipStream_t stream) {
+    const int max_entries = (kFlatPtrsPerLaunch / K) < kFlatEntriesPerLaunch ? (kFlatPtrsPerLaunch / K)
+                                                                           : kFlatEntriesPerLaunch;
     FlatArgs a;
-    int first = 0, count = 0;
+    a.K = K;
+    for (int r = 0; r < K; ++r) a.bucket[r] = buckets.p[r];
+    int first = 0, count = 0, pad = -1;
     int64_t big = 0;  // tiles of the batch at 16 KiB
     auto flush = [&]() -> hipError_t {
         if (count == 0) return hipSuccess;
@@ -118,30 +140,39 @@ hipError_t launch_flatten(const CopyJob* jobs, int n_jobs, int elem_bytes, hipSt
         const int64_t tile = small ? kFlatTileBytes<1> : kFlatTileBytes<4>;
         int64_t tiles = 0;
         for (int i = 0; i < count; ++i) {
-            a.job[i] = jobs[first + i];
+            const FragEntry& f = entries[first + i];
+            a.off[i] = f.off;
+            a.n[i] = f.n;
+            if (i != pad)
+                for (int r = 0; r < K; ++r) a.src[i * K + r] = f.ptr[r];
+            a.tpr[i] = (int32_t)tiles_of(f.n * elem_bytes, tile);
             a.tile0[i] = (int32_t)tiles;
-            tiles += tiles_of(jobs[first + i].n * elem_bytes, tile);
+            tiles += (int64_t)K * a.tpr[i];
         }
         a.tile0[count] = (int32_t)tiles;
-        a.n_jobs = count;
+        a.nent = count;
+        a.pad_m = pad;
         hipError_t e = hipSuccess;
         if (tiles > 0) {
             if (elem_bytes == 2)
-                e = small ? launch_batch<uint16_t, 1>(a, tiles, stream) : launch_batch<uint16_t, 4>(a, tiles, stream);
+                e = small ? launch_batch<uint16_t, 1>(a, stream) : launch_batch<uint16_t, 4>(a, stream);
             else
-                e = small ? launch_batch<uint32_t, 1>(a, tiles, stream) : launch_batch<uint32_t, 4>(a, tiles, stream);
+                e = small ? launch_batch<uint32_t, 1>(a, stream) : launch_batch<uint32_t, 4>(a, stream);
         }
         first += count;
         count = 0;
+        pad = -1;
         big = 0;
         return e;
     };
-    for (int i = 0; i < n_jobs; ++i) {
-        if (count == kFlatJobsPerLaunch || big > (1LL << 28)) {
+    for (int i = 0; i < n_entries; ++i) {
+        const bool is_pad = entries[i].ptr[0] == nullptr;
+        if (count == (is_pad ? max_entries + 1 : max_entries) || pad >= 0 || big > (1LL << 28)) {
             hipError_t e = flush();
             if (e != hipSuccess) return e;
         }
-        big += tiles_of(jobs[i].n * elem_bytes, kFlatTileBytes<4>);
+        if (is_pad) pad = count;
+        big += (int64_t)K * tiles_of(entries[i].n * elem_bytes, kFlatTileBytes<4>);
         ++count;
     }
     return flush();

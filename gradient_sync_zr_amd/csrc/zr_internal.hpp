@@ -11,7 +11,8 @@ namespace zr {
 
 constexpr int kMaxRanks = ZR_MAX_RANKS;
 constexpr int kAgSegsPerLaunch = 32;   // segments carried in one all-gather launch
-constexpr int kFlatJobsPerLaunch = 96; // copy jobs carried in one flatten launch
+constexpr int kFlatPtrsPerLaunch = 256;    // source pointers of fragments in one flatten launch
+constexpr int kFlatEntriesPerLaunch = 32;  // fragments in one flatten launch
 constexpr int kRsfPtrsPerLaunch = 256;   // rank pointers of fragments in one discrete-RS launch
 constexpr int kRsfEntriesPerLaunch = 32; // fragments in one discrete-RS launch
 constexpr int kRsfSegsPerLaunch = 96;    // (fragment, chunk) segments in one discrete-RS launch
@@ -24,17 +25,9 @@ struct MutPtrs {
     void* p[kMaxRanks];
 };
 
-// One contiguous copy of a flatten call: `n` elements from src to dst;
-// src == nullptr means "write n zeros".
-struct CopyJob {
-    const void* src;
-    void* dst;
-    int64_t n;
-};
-
-// One fragment of the discrete reduce-scatter: its K rank pointers (all null
-// for the zero padding after the last fragment), its offset in the virtual
-// bucket, and its size.
+// One fragment of a flatten or a discrete reduce-scatter: its K rank
+// pointers (all null for the zero padding after the last fragment), its
+// offset in the (virtual) bucket, and its size.
 struct FragEntry {
     const void* ptr[kMaxRanks];
     int64_t off, n;
@@ -73,7 +66,9 @@ RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t 
 hipError_t rsf_plan_launch(const RsfPlan* plan, hipStream_t stream);
 void rsf_plan_free(RsfPlan* plan);
 
-// Any number of jobs; launched kFlatJobsPerLaunch (or fewer) at a time.
-hipError_t launch_flatten(const CopyJob* jobs, int n_jobs, int elem_bytes, hipStream_t stream);
+// Any number of entries, each with at most 2^28 / K tiles of 16 KiB per
+// rank; launched kFlatEntriesPerLaunch (or fewer) at a time.
+hipError_t launch_flatten(int K, const FragEntry* entries, int n_entries, const MutPtrs& buckets,
+                          int elem_bytes, hipStream_t stream);
 
 }  // namespace zr

@@ -120,7 +120,9 @@ int zr_version(void);
  *               reduce-scatter that follows
  *  dt           ZR_BF16 or ZR_FP32 (a bitwise copy either way)
  * Buckets must not overlap each other or any fragment (ZR_ERR_ALIAS).
- * Copy jobs travel in kernel arguments, 96 per launch.
+ * Fragment tables travel in kernel arguments: a launch carries up to 32
+ * fragments' rank pointers (256 at most, so 4 fragments at K = 64) and the
+ * zero padding when it comes next.
  */
 zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const int64_t* numels,
                             void* const* buckets, int64_t padded_numel, zr_dtype dt,
