@@ -337,6 +337,15 @@ def test_all_gather_bit_exact(K, sizes, shift, bf16, offset, gap):
     (4, [8, 16, 24, 4096 * 3], False, 0, 4),       # aligned: 16-byte copies
     (2, [1000, 3, 5], True, 1, 0),
     (64, [100, 1], True, 0, 27),
+    # a launch carries 32 fragments' rank pointers (4 at K = 64) and the
+    # padding in a spare slot after them
+    (8, [97 * (i + 1) for i in range(32)], True, 0, 20000),
+    (8, [50 + 13 * i for i in range(33)], False, 1, 9),
+    (64, [3000 + i for i in range(9)], True, 0, 100),
+    (16, [], True, 0, 777),                        # padding only
+    # launches large enough for 16 KiB tiles
+    (8, [600000, 5, 700001], True, 0, 3),
+    (4, [300001, 7, 500000], False, 1, 0),
 ])
 def test_flatten_bit_exact(K, sizes, bf16, offset, extra):
     import torch
