@@ -12,6 +12,8 @@ so 47.53 GB per step. `value` = those bytes / step time.
 
 Other workloads (--workload):
   zero2_accum     the same sync as a later micro-step (adds into the partitions)
+  zero2_overlap   the same sync under a synthetic backward pass: each bucket's
+                  compute then its reduction, scheduler against one buffer
   zero3_ag        the 32-layer transformer all-gather in 162 prefetch buckets
   zero3_prefetch  the prefetch coordinator walking that model's trace, with a
                   synthetic compute per step; reports the pass time in ms
@@ -309,6 +311,85 @@ def kit_delay():
         if L.tk_delay(int(us * ticks_per_us), 50_000_000, None, stream.cuda_stream) != 0:
             raise RuntimeError("delay launch failed")
     return delay
+
+
+def bench_zero2_overlap(args):
+    """The scheduler against the dependency the issue page reports: each
+    bucket's backward compute (a calibrated spin of `compute_ratio` times that
+    bucket's reduction time, on the producer stream) followed by its
+    reduction. Two buffers let the compute of bucket i+1 run under the
+    reduction of bucket i; one buffer makes every bucket's compute wait for
+    the previous reduction, which is the serialisation the issue describes."""
+    import torch
+
+    import synth
+    from gradient_sync_zr_amd.steps import Zero2GradSync
+    from synth import workloads as W
+
+    cfg = W.ZERO2
+    K, N, bucket, sigma = cfg["K"], cfg["N_total"], cfg["bucket"], cfg["sigma"]
+    seed = W.seed_of(3)
+    grads = [torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    for r in range(K):
+        synth.dev_normal_bf16(grads[r], seed, r, 0, sigma)
+    buckets = W.zero2_buckets(N, bucket)
+    P = sum(-(-n // K) for _, n in buckets)
+    parts = [torch.empty(P, dtype=torch.float32, device="cuda") for _ in range(K)]
+    red, prod = torch.cuda.Stream(), torch.cuda.Stream()
+    syncs = {nb: Zero2GradSync(grads, parts, bucket, chunk_shift=cfg["shift"], average=True,
+                               n_buffers=nb, reduction_stream=red) for nb in (1, 2)}
+    delay = kit_delay()
+    torch.cuda.synchronize()
+    # each bucket's reduction time, alone
+    syncs[2].step(producer_stream=prod)
+    timing = []
+    syncs[2].step(producer_stream=prod, timing=timing)
+    torch.cuda.synchronize()
+    red_ms = events_ms(timing)
+    compute_us = [args.compute_ratio * ms * 1e3 for ms in red_ms]
+    passes = max(1, min(args.steps, 10))
+
+    def wall(fn):
+        fn()  # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(passes):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / passes
+
+    def produce(i, stream):
+        delay(compute_us[i], stream)
+
+    def compute_only():
+        for i in range(len(buckets)):
+            delay(compute_us[i], prod)
+
+    ms_compute = wall(compute_only)
+    ms_reduce = wall(lambda: syncs[2].step(producer_stream=prod))
+    ms_overlap = wall(lambda: syncs[2].step(producer_stream=prod, produce=produce))
+    ms_serial = wall(lambda: syncs[1].step(producer_stream=prod, produce=produce))
+    for s_ in syncs.values():
+        s_.close()
+    exposed = max(0.0, ms_overlap - ms_compute)
+    return {
+        "metric": "ZeRO-2 backward with bucket reductions overlapped by the scheduler: ms per "
+                  "sync, K=8, 2.38B-elem bf16 grads",
+        "value": round(ms_overlap, 3), "unit": "ms", "n_gpus": 1, "steps": passes, "warmup": 1,
+        "ms_per_step": round(ms_overlap, 3), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic: seeded generator, bf16 ~N(0,1e-3); compute is a calibrated spin",
+        "serial_one_buffer_ms": round(ms_serial, 3), "compute_only_ms": round(ms_compute, 3),
+        "reductions_only_ms": round(ms_reduce, 3), "exposed_reduction_ms": round(exposed, 3),
+        "hidden_fraction": round(1.0 - exposed / ms_reduce, 4),
+        "bucket_reduction_ms": [round(x, 4) for x in red_ms],
+        "config": {"workload": "zero2_overlap: K=8, 2,376,274,560 bf16 grad elements per rank, "
+                               "5 buckets; per bucket a spin on the producer stream, then the "
+                               "reduction through the scheduler (2 buffers, or 1 for the serial "
+                               "line)",
+                   "K": K, "n_buckets": len(buckets), "compute_ratio": args.compute_ratio},
+        "roofline": None, "cpu_baseline": None,
+    }
 
 
 def bench_zero3_prefetch(args):
@@ -615,11 +696,12 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="zero2",
-                    choices=["zero2", "zero2_accum", "zero3_ag", "zero3_prefetch", "allreduce64",
-                             "flatten8", "frags_layer"])
+                    choices=["zero2", "zero2_accum", "zero2_overlap", "zero3_ag", "zero3_prefetch",
+                             "allreduce64", "flatten8", "frags_layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--compute-ratio", type=float, default=1.5,
-                    help="zero3_prefetch: each step's synthetic compute, in units of its gather time")
+                    help="zero3_prefetch, zero2_overlap: each step's synthetic compute, in units "
+                         "of its gather or reduction time")
     ap.add_argument("--arena-numel", type=int, default=1_600_000_000,
                     help="zero3_prefetch: arena elements per rank")
     ap.add_argument("--cpu-sample-elems", type=int, default=0,
@@ -635,6 +717,7 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     fn = {"zero2": bench_zero2, "zero2_accum": lambda a: bench_zero2(a, accumulate=True),
+          "zero2_overlap": bench_zero2_overlap,
           "zero3_ag": bench_zero3, "zero3_prefetch": bench_zero3_prefetch,
           "allreduce64": bench_allreduce64,
           "flatten8": bench_flatten8, "frags_layer": bench_frags_layer}[args.workload]

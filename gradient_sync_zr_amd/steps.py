@@ -17,7 +17,7 @@ computation happens in libzr's kernels.
 """
 from __future__ import annotations
 
-from typing import List, Optional, Sequence
+from typing import Callable, List, Optional, Sequence
 
 from . import (ZR_BF16, ZR_FP32, ZR_ORDER_RING, Sched, zr_all_gather, zr_plan_buckets,
                _dtype)
@@ -66,18 +66,22 @@ class Zero2GradSync:
                            reduction_stream=reduction_stream)
 
     def step(self, producer_stream=None, timing: Optional[List] = None,
-             micro_step: int = 0) -> None:
-        """One gradient sync. `timing`, if given, receives (start, end) torch
-        events recorded on the reduction stream around each bucket's launch.
-        Micro-step 0 overwrites the partitions; later micro-steps of a
-        gradient-accumulation window add to them ("DeepSpeed ZeRO-3 源码解析",
-        5.3 and 6)."""
+             micro_step: int = 0, produce: Optional[Callable] = None) -> None:
+        """One gradient sync. `produce(i, stream)`, if given, enqueues the work
+        that writes bucket i's gradients (the backward pass) on the producer
+        stream, after the stream has waited for the buffer to be free and
+        before the bucket's reduction, which waits for it. `timing`, if given,
+        receives (start, end) torch events recorded on the reduction stream
+        around each bucket's launch. Micro-step 0 overwrites the partitions;
+        later micro-steps of a gradient-accumulation window add to them
+        ("DeepSpeed ZeRO-3 源码解析", 5.3 and 6)."""
         import torch
         prod = producer_stream if producer_stream is not None else torch.cuda.current_stream()
         for i, (n, ins, outs, _, _) in enumerate(self.buckets):
             buf = i % self.n_buffers
             self.sched.acquire(buf, prod)
-            # the backward pass would write this bucket's gradients here, on `prod`
+            if produce is not None:
+                produce(i, prod)
             if timing is not None:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)

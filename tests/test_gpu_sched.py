@@ -217,6 +217,41 @@ def test_rapid_reuse_and_flush_match_serial_results():
     sched.close()
 
 
+def test_zero2_sync_reduces_what_the_producer_wrote():
+    # the backward pass, through Zero2GradSync's produce hook, writes each
+    # bucket's gradients on the producer stream after a delay: a reduction
+    # that did not wait for its producer would reduce the zeros left there
+    import torch
+    from gradient_sync_zr_amd.steps import Zero2GradSync
+    red, prod = streams()
+    bucket = 8 * 4096 + 5
+    total = 3 * bucket + 1234
+    grads = [torch.zeros(total, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    P = sum(-(-min(bucket, total - s) // K) for s in range(0, total, bucket))
+    parts = [torch.empty(P, dtype=torch.float32, device="cuda") for _ in range(K)]
+    sync = Zero2GradSync(grads, parts, bucket, chunk_shift=1, average=True, reduction_stream=red)
+    seen = []
+
+    def produce(i, stream):
+        n, _, _, start, _ = sync.buckets[i]
+        seen.append(i)
+        delay(20, stream)
+        for r in range(K):
+            synth.dev_normal_bf16(grads[r][start:start + n], SEED + 9, r, start, 1.0, stream=stream)
+
+    sync.step(producer_stream=prod, produce=produce)
+    torch.cuda.synchronize()
+    assert seen == list(range(len(sync.buckets)))
+    for n, _, _, start, poff in sync.buckets:
+        xs = [synth.host_normal_bf16(SEED + 9, r, start, n, 1.0) for r in range(K)]
+        want = oracle.reduce_scatter(xs, n, np.float32, shift=1, average=True)
+        C = -(-n // K)
+        for q in range(K):
+            got = parts[q][poff:poff + C].cpu().numpy()
+            assert np.array_equal(bits(got), bits(want[q])), f"bucket at {start}, rank {q}"
+    sync.close()
+
+
 def test_scheduler_errors_on_gpu():
     torch, red, prod, bufs, outs, sched = setup()
     import gradient_sync_zr_amd as zr
