@@ -122,9 +122,6 @@ zr_status set_error(zr_status st, const char* msg) {
 
 const Tuning& tuning() {
     static const Tuning t = {
-        env_int("ZR_RS_BLOCKS_PER_CU", 8, 1, 64),
-        env_int("ZR_AR_BLOCKS_PER_CU", 8, 1, 64),
-        env_int("ZR_AG_BLOCKS_PER_CU", 8, 1, 64),
         env_int("ZR_AR_NONTEMPORAL", 1, 0, 1),
         env_int("ZR_AG_NONTEMPORAL", 1, 0, 1),
     };

@@ -11,7 +11,8 @@
 //
 // Tiles are 4 waves x S slices x 256 global indices, lanes on 4-element quads
 // (as in the reduce-scatter kernel, so every store instruction writes one
-// contiguous span). A tile that lies inside one chunk and below N takes the
+// contiguous span), one block per tile in index order (a persistent grid
+// striding over the tiles ran a few percent slower). A tile that lies inside one chunk and below N takes the
 // vector path with the chunk (hence the fold's first rank) uniform across the
 // block; a tile that straddles a chunk boundary or the end of the buffer (at
 // most K of them) folds element by element, reading the rank pointers from an
@@ -92,9 +93,7 @@ __global__ void __launch_bounds__(kThreads) ar_kernel(const ArArgs a) {
 
 template <typename T, int KS, int AVG, int ORDER, bool NT>
 hipError_t launch_t(const ArArgs& a, hipStream_t stream) {
-    int64_t want = (int64_t)device_cu_count() * tuning().ar_blocks_per_cu;
-    if (want < 1) want = 1;
-    const int gx = (int)(want < a.n_tiles ? want : a.n_tiles);
+    const int gx = (int)(a.n_tiles < (1LL << 30) ? a.n_tiles : (1LL << 30));  // one block per tile
     hipLaunchKernelGGL((ar_kernel<T, KS, AVG, ORDER, NT>), dim3(gx), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

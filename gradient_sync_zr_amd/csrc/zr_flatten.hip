@@ -10,9 +10,11 @@
 // K = 64), the zero padding in a spare slot after them (it has no source),
 // the K bucket bases and each entry's first tile, all in its kernel
 // arguments: no device descriptor table, no staging copy. Entry m owns K
-// runs of tiles_per_rank[m] tiles, rank by rank; the grid strides over the
-// launch's tiles in order, so blocks stay balanced however unequal the
-// fragments are.
+// runs of tiles_per_rank[m] tiles, rank by rank. The grid has one block per
+// tile of the launch, in order, so blocks stay balanced however unequal the
+// fragments are, and the blocks in flight work on one compact window of
+// memory (a persistent grid striding over the tiles ran 15-20% slower on a
+// plain copy).
 //
 // A tile is 16 KiB of destination (4 KiB in launches too small to fill the
 // device): lane l of wave w moves the 16-byte units w*64*U + k*64 + l
@@ -111,8 +113,7 @@ __global__ void __launch_bounds__(kThreads) flatten_kernel(const FlatArgs a) {
 template <typename T, int U>
 hipError_t launch_batch(const FlatArgs& a, hipStream_t stream) {
     const int64_t tiles = a.tile0[a.nent];
-    const int64_t want = (int64_t)device_cu_count() * 8;
-    const int gx = (int)(want < tiles ? want : tiles);
+    const int gx = (int)(tiles < (1LL << 30) ? tiles : (1LL << 30));  // one block per tile
     hipLaunchKernelGGL((flatten_kernel<T, U>), dim3(gx), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

@@ -33,12 +33,10 @@ struct FragEntry {
     int64_t off, n;
 };
 
-// Launch-shape knobs, read once from the environment (for tuning sweeps);
-// defaults are the measured best.
+// Cache-policy knobs, read once from the environment (for tuning sweeps);
+// defaults are the measured best. Every kernel launches one block per tile,
+// so there is no grid-size knob.
 struct Tuning {
-    int rs_blocks_per_cu;  // resident blocks per CU the RS grid is sized for
-    int ar_blocks_per_cu;
-    int ag_blocks_per_cu;
     int ar_nontemporal;    // fused all-reduce: streaming (non-temporal) loads and stores
     int ag_nontemporal;    // all-gather
 };
