@@ -408,9 +408,9 @@ zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const i
             }
         ZR_TRY(check_disjoint(rb, "buckets", rf, "fragment"));
         // one entry per fragment (every rank's copy of it), then the padding;
-        // a fragment of more than 2^28 / K tiles of 16 KiB per rank is cut
+        // a fragment of more than 2^28 / K tiles of 4 KiB per rank is cut
         // into pieces of that many, so tile numbers fit the kernel's 32 bits
-        const int64_t piece = ((1LL << 28) / K) * (16384 / es);
+        const int64_t piece = ((1LL << 28) / K) * (4096 / es);
         std::vector<FragEntry> entries;
         auto add = [&](const void* const* ptrs, int64_t off, int64_t n) {
             for (int64_t o = 0; o < n; o += piece) {

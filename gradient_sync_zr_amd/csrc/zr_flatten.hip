@@ -16,11 +16,12 @@
 // memory (a persistent grid striding over the tiles ran 15-20% slower on a
 // plain copy).
 //
-// A tile is 16 KiB of destination (4 KiB in launches too small to fill the
-// device): lane l of wave w moves the 16-byte units w*64*U + k*64 + l
-// (k < U = 4 or 1), so every load and store instruction of a wave covers
-// 1 KiB contiguously, with all loads in flight before the stores; loads and
-// stores are non-temporal (each byte is touched once). A copy whose source
+// A tile is 4 KiB of destination: lane l of wave w moves the 16-byte unit
+// w*64 + l, so every load and store instruction of a wave covers 1 KiB
+// contiguously; loads and stores are non-temporal (each byte is touched
+// once). (At one block per tile a plain copy ran 10-15% faster with 4 KiB
+// tiles than with 16 KiB tiles of four units per lane; in the flatten the
+// two sizes measure the same, and one size needs no small-launch mode.) A copy whose source
 // and destination both start 16-byte aligned moves whole units; its last
 // partial unit, and every unit of a copy that is not aligned so (possible
 // inside a bucket, where offsets are prefix sums of arbitrary sizes), copies
@@ -31,10 +32,9 @@
 namespace zr {
 namespace {
 
-// 16-byte units per lane: 4 (16 KiB tiles) for launches with enough tiles to
-// fill the device, else 1 (4 KiB tiles, four times as many blocks).
-template <int U>
-constexpr int64_t kFlatTileBytes = (int64_t)kThreads * 16 * U;
+// 16-byte units per lane, and the tile they make.
+constexpr int kUnits = 1;
+constexpr int64_t kFlatTileBytes = (int64_t)kThreads * 16 * kUnits;
 
 // Entry slots: fragments with source pointers, plus one for the padding.
 constexpr int kFlatSlots = kFlatEntriesPerLaunch + 1;
@@ -50,7 +50,7 @@ struct FlatArgs {
 };
 static_assert(sizeof(FlatArgs) <= 4096, "flatten arguments exceed 4 KB");
 
-template <typename T, int U>
+template <typename T>
 __global__ void __launch_bounds__(kThreads) flatten_kernel(const FlatArgs a) {
     constexpr int per = 16 / sizeof(T);  // elements per 16-byte unit
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -65,27 +65,27 @@ __global__ void __launch_bounds__(kThreads) flatten_kernel(const FlatArgs a) {
         const T* src = m == a.pad_m ? nullptr : static_cast<const T*>(a.src[m * a.K + r]);
         T* dst = static_cast<T*>(a.bucket[r]) + a.off[m];
         const bool vec = ((((uintptr_t)dst) & 15) == 0) && (src == nullptr || (((uintptr_t)src) & 15) == 0);
-        const int64_t u0 = lt * (kFlatTileBytes<U> / 16) + wave * 64 * U + lane;  // first unit
-        if (vec && (u0 + 64 * (U - 1) + 1) * per <= n) {
+        const int64_t u0 = lt * (kFlatTileBytes / 16) + wave * 64 * kUnits + lane;  // first unit
+        if (vec && (u0 + 64 * (kUnits - 1) + 1) * per <= n) {
             // every unit of this lane is whole
-            u32x4 v[U];
+            u32x4 v[kUnits];
 #pragma unroll
-            for (int k = 0; k < U; ++k)
+            for (int k = 0; k < kUnits; ++k)
                 v[k] = src ? ld<true>(reinterpret_cast<const u32x4*>(src + (u0 + 64 * k) * per))
                            : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int k = 0; k < U; ++k)
+            for (int k = 0; k < kUnits; ++k)
                 st<true>(reinterpret_cast<u32x4*>(dst + (u0 + 64 * k) * per), v[k]);
             continue;
         }
         // some unit of this lane is partial or unaligned: every load is issued
         // before the first store (a store may not overtake the loads, so the
         // lane waits on one memory latency, not one per element)
-        u32x4 vv[U];
-        T ev[U][per];
-        int cnt[U];
+        u32x4 vv[kUnits];
+        T ev[kUnits][per];
+        int cnt[kUnits];
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
+        for (int k = 0; k < kUnits; ++k) {
             const int64_t e0 = (u0 + 64 * k) * per;
             cnt[k] = e0 >= n ? 0 : (int)((n - e0) < per ? (n - e0) : per);
             if (vec && cnt[k] == per) {
@@ -97,7 +97,7 @@ __global__ void __launch_bounds__(kThreads) flatten_kernel(const FlatArgs a) {
             }
         }
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
+        for (int k = 0; k < kUnits; ++k) {
             const int64_t e0 = (u0 + 64 * k) * per;
             if (vec && cnt[k] == per) {
                 st<true>(reinterpret_cast<u32x4*>(dst + e0), vv[k]);
@@ -110,11 +110,11 @@ __global__ void __launch_bounds__(kThreads) flatten_kernel(const FlatArgs a) {
     }
 }
 
-template <typename T, int U>
+template <typename T>
 hipError_t launch_batch(const FlatArgs& a, hipStream_t stream) {
     const int64_t tiles = a.tile0[a.nent];
     const int gx = (int)(tiles < (1LL << 30) ? tiles : (1LL << 30));  // one block per tile
-    hipLaunchKernelGGL((flatten_kernel<T, U>), dim3(gx), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((flatten_kernel<T>), dim3(gx), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -123,9 +123,8 @@ int64_t tiles_of(int64_t bytes, int64_t tile) { return (bytes + tile - 1) / tile
 }  // namespace
 
 // Entries go out in launches of at most 32 fragments (256 source pointers)
-// plus the padding entry if it comes next, and about 2^30 tiles; a larger
+// plus the padding entry if it comes next, and about 2^29 tiles; a larger
 // entry has already been split by the caller, so tile numbers fit in 32 bits.
-// A launch with fewer 16 KiB tiles than two per CU uses 4 KiB tiles.
 hipError_t launch_flatten(int K, const FragEntry* entries, int n_entries, const MutPtrs& buckets,
                           int elem_bytes, hipStream_t stream) {
     const int max_entries = (kFlatPtrsPerLaunch / K) < kFlatEntriesPerLaunch ? (kFlatPtrsPerLaunch / K)
@@ -134,11 +133,10 @@ hipError_t launch_flatten(int K, const FragEntry* entries, int n_entries, const 
     a.K = K;
     for (int r = 0; r < K; ++r) a.bucket[r] = buckets.p[r];
     int first = 0, count = 0, pad = -1;
-    int64_t big = 0;  // tiles of the batch at 16 KiB
+    int64_t batch = 0;  // tiles of the batch
     auto flush = [&]() -> hipError_t {
         if (count == 0) return hipSuccess;
-        const bool small = big < 2LL * device_cu_count();
-        const int64_t tile = small ? kFlatTileBytes<1> : kFlatTileBytes<4>;
+        const int64_t tile = kFlatTileBytes;
         int64_t tiles = 0;
         for (int i = 0; i < count; ++i) {
             const FragEntry& f = entries[first + i];
@@ -154,26 +152,22 @@ hipError_t launch_flatten(int K, const FragEntry* entries, int n_entries, const 
         a.nent = count;
         a.pad_m = pad;
         hipError_t e = hipSuccess;
-        if (tiles > 0) {
-            if (elem_bytes == 2)
-                e = small ? launch_batch<uint16_t, 1>(a, stream) : launch_batch<uint16_t, 4>(a, stream);
-            else
-                e = small ? launch_batch<uint32_t, 1>(a, stream) : launch_batch<uint32_t, 4>(a, stream);
-        }
+        if (tiles > 0)
+            e = elem_bytes == 2 ? launch_batch<uint16_t>(a, stream) : launch_batch<uint32_t>(a, stream);
         first += count;
         count = 0;
         pad = -1;
-        big = 0;
+        batch = 0;
         return e;
     };
     for (int i = 0; i < n_entries; ++i) {
         const bool is_pad = entries[i].ptr[0] == nullptr;
-        if (count == (is_pad ? max_entries + 1 : max_entries) || pad >= 0 || big > (1LL << 28)) {
+        if (count == (is_pad ? max_entries + 1 : max_entries) || pad >= 0 || batch > (1LL << 28)) {
             hipError_t e = flush();
             if (e != hipSuccess) return e;
         }
         if (is_pad) pad = count;
-        big += (int64_t)K * tiles_of(entries[i].n * elem_bytes, kFlatTileBytes<4>);
+        batch += (int64_t)K * tiles_of(entries[i].n * elem_bytes, kFlatTileBytes);
         ++count;
     }
     return flush();

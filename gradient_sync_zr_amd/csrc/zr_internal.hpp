@@ -64,7 +64,7 @@ RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t 
 hipError_t rsf_plan_launch(const RsfPlan* plan, hipStream_t stream);
 void rsf_plan_free(RsfPlan* plan);
 
-// Any number of entries, each with at most 2^28 / K tiles of 16 KiB per
+// Any number of entries, each with at most 2^28 / K tiles of 4 KiB per
 // rank; launched kFlatEntriesPerLaunch (or fewer) at a time.
 hipError_t launch_flatten(int K, const FragEntry* entries, int n_entries, const MutPtrs& buckets,
                           int elem_bytes, hipStream_t stream);
