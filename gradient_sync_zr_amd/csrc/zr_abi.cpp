@@ -124,6 +124,7 @@ const Tuning& tuning() {
     static const Tuning t = {
         env_int("ZR_AR_NONTEMPORAL", 1, 0, 1),
         env_int("ZR_AG_NONTEMPORAL", 1, 0, 1),
+        env_int("ZR_MAX_GRID", 1 << 30, 1, 1 << 30),
     };
     return t;
 }

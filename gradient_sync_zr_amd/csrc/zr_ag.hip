@@ -72,8 +72,7 @@ __global__ void __launch_bounds__(kThreads) ag_kernel(const AgArgs a) {
 
 template <typename T, int KS, bool NT>
 hipError_t launch_t(const AgArgs& a, int n_segs, int max_units, hipStream_t stream) {
-    const int64_t cap = (1LL << 30) / n_segs;
-    const int gx = (int)(max_units < cap ? max_units : cap);  // one block per unit of the largest segment
+    const int gx = grid_for(max_units, n_segs);  // one block per unit of the largest segment
     hipLaunchKernelGGL((ag_kernel<T, KS, NT>), dim3(gx, n_segs), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(kThreads) ar_kernel(const ArArgs a) {
 
 template <typename T, int KS, int AVG, int ORDER, bool NT>
 hipError_t launch_t(const ArArgs& a, hipStream_t stream) {
-    const int gx = (int)(a.n_tiles < (1LL << 30) ? a.n_tiles : (1LL << 30));  // one block per tile
+    const int gx = grid_for(a.n_tiles);  // one block per tile
     hipLaunchKernelGGL((ar_kernel<T, KS, AVG, ORDER, NT>), dim3(gx), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

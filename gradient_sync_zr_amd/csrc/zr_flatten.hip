@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(kThreads) flatten_kernel(const FlatArgs a) {
 template <typename T>
 hipError_t launch_batch(const FlatArgs& a, hipStream_t stream) {
     const int64_t tiles = a.tile0[a.nent];
-    const int gx = (int)(tiles < (1LL << 30) ? tiles : (1LL << 30));  // one block per tile
+    const int gx = grid_for(tiles);  // one block per tile
     hipLaunchKernelGGL((flatten_kernel<T>), dim3(gx), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

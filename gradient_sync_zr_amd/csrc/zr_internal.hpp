@@ -33,14 +33,21 @@ struct FragEntry {
     int64_t off, n;
 };
 
-// Cache-policy knobs, read once from the environment (for tuning sweeps);
-// defaults are the measured best. Every kernel launches one block per tile,
-// so there is no grid-size knob.
+// Knobs read once from the environment (for tuning sweeps and tests);
+// defaults are the measured best.
 struct Tuning {
     int ar_nontemporal;    // fused all-reduce: streaming (non-temporal) loads and stores
     int ag_nontemporal;    // all-gather
+    int max_grid;          // blocks per launch at most (ZR_MAX_GRID, default 2^30): every
+                           // kernel launches one block per tile up to it, and its blocks
+                           // stride over the tiles beyond it
 };
 const Tuning& tuning();
+// Blocks for a launch of `tiles` tiles: one per tile, at most tuning().max_grid.
+inline int grid_for(int64_t tiles, int64_t cap_divisor = 1) {
+    const int64_t cap = tuning().max_grid / cap_divisor > 0 ? tuning().max_grid / cap_divisor : 1;
+    return (int)(tiles < cap ? tiles : cap);
+}
 int device_cu_count();  // CUs of the current device (cached per device)
 
 // flags: ZR_AVERAGE | ZR_ACCUMULATE

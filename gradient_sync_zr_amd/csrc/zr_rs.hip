@@ -146,11 +146,11 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
     }
 }
 
-// One block per tile, up to 2^30 blocks (beyond that the blocks stride).
+// One block per tile, up to tuning().max_grid blocks (beyond that they stride).
 template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
 hipError_t launch_t(const RsArgs& a, hipStream_t stream) {
     const int64_t total = a.tile0[a.K];
-    const int gx = (int)(total < (1LL << 30) ? total : (1LL << 30));
+    const int gx = grid_for(total);
     hipLaunchKernelGGL((rs_kernel<TIn, TOut, KS, AVG, ORDER, NT, S>), dim3(gx), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();

@@ -176,7 +176,7 @@ __global__ void __launch_bounds__(kThreads) rsf_kernel(const RsfArgs a) {
 template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
 hipError_t launch_t(const RsfArgs& a, hipStream_t stream) {
     const int total = a.tile0[a.nseg];
-    const int gx = (int)(total < (1LL << 30) ? total : (1LL << 30));  // one block per tile
+    const int gx = grid_for(total);  // one block per tile
     hipLaunchKernelGGL((rsf_kernel<TIn, TOut, KS, AVG, ORDER, NT, S>), dim3(gx), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
