@@ -7,11 +7,12 @@
 // forwarding collapses to: chunk j of the full tensor is shard
 // (j - shift) mod K, copied to every rank's full buffer.
 //
-// Grid: blockIdx.y = segment (one tensor), blockIdx.x = one (chunk,
-// 2048-element tile) pair of that segment: one block per tile, as many
-// columns as the largest segment of the launch has tiles (blocks past a
-// smaller segment's end exit at once). A persistent grid striding over the
-// tiles ran 10-15% slower. A lane loads its 8 shard
+// Grid: one block per tile of the launch. The tiles of a segment (one
+// tensor) are its (chunk, 2048-element tile) pairs, chunk by chunk, and the
+// segments' tiles follow each other, so blocks stay balanced however unequal
+// the tensors are; a block finds its segment by a uniform binary search over
+// the segments' first tiles. (A persistent grid striding over the tiles ran
+// 10-15% slower.) A lane loads its 8 shard
 // elements once (16 bytes) and stores them to all K full buffers, so each
 // shard byte is read once and written K times. Chunk starts that are not
 // 16-byte aligned on either side, and ragged ends, copy element by element.
@@ -32,17 +33,28 @@ struct AgArgs {
     ConstPtrs shards;
     MutPtrs fulls;
     AgSeg seg[kAgSegsPerLaunch];
-    int K, shift;
+    int64_t unit0[kAgSegsPerLaunch + 1];  // first tile of segment s; unit0[nseg] = all tiles
+    int K, shift, nseg;
 };
+static_assert(sizeof(AgArgs) <= 4096, "all-gather arguments exceed 4 KB");
 
 template <typename T, int KS, bool NT>
 __global__ void __launch_bounds__(kThreads) ag_kernel(const AgArgs a) {
     const int K = KS > 0 ? KS : a.K;
-    const AgSeg& sg = a.seg[blockIdx.y];
-    const int total = K * sg.tiles_per_chunk;
-    for (int u = blockIdx.x; u < total; u += gridDim.x) {
-        const int j = u / sg.tiles_per_chunk;
-        const int t = u - j * sg.tiles_per_chunk;
+    for (int64_t u = blockIdx.x; u < a.unit0[a.nseg]; u += gridDim.x) {
+        // the tile's segment: the last s with unit0[s] <= u (uniform)
+        int s = 0;
+        for (int hi = a.nseg; hi - s > 1;) {
+            const int mid = (s + hi) >> 1;
+            if (a.unit0[mid] <= u)
+                s = mid;
+            else
+                hi = mid;
+        }
+        const AgSeg& sg = a.seg[s];
+        const int ul = (int)(u - a.unit0[s]);  // < K * tiles_per_chunk <= 2^29: 32-bit division
+        const int j = ul / sg.tiles_per_chunk;
+        const int t = ul - j * sg.tiles_per_chunk;
         int holder = j - a.shift;
         if (holder < 0) holder += K;
         const int64_t o = (int64_t)t * kTile + (int64_t)threadIdx.x * kGroup;
@@ -71,23 +83,22 @@ __global__ void __launch_bounds__(kThreads) ag_kernel(const AgArgs a) {
 }
 
 template <typename T, int KS, bool NT>
-hipError_t launch_t(const AgArgs& a, int n_segs, int max_units, hipStream_t stream) {
-    const int gx = grid_for(max_units, n_segs);  // one block per unit of the largest segment
-    hipLaunchKernelGGL((ag_kernel<T, KS, NT>), dim3(gx, n_segs), dim3(kThreads), 0, stream, a);
+hipError_t launch_t(const AgArgs& a, hipStream_t stream) {
+    const int gx = grid_for(a.unit0[a.nseg]);  // one block per tile
+    hipLaunchKernelGGL((ag_kernel<T, KS, NT>), dim3(gx), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
 template <typename T, int KS>
-hipError_t pick_nt(const AgArgs& a, int n_segs, int max_units, hipStream_t s) {
-    return tuning().ag_nontemporal ? launch_t<T, KS, true>(a, n_segs, max_units, s)
-                                   : launch_t<T, KS, false>(a, n_segs, max_units, s);
+hipError_t pick_nt(const AgArgs& a, hipStream_t s) {
+    return tuning().ag_nontemporal ? launch_t<T, KS, true>(a, s) : launch_t<T, KS, false>(a, s);
 }
 
 template <typename T>
-hipError_t pick_k(const AgArgs& a, int n_segs, int max_units, hipStream_t s) {
+hipError_t pick_k(const AgArgs& a, hipStream_t s) {
     switch (a.K) {
-        case 8: return pick_nt<T, 8>(a, n_segs, max_units, s);
-        default: return pick_nt<T, 0>(a, n_segs, max_units, s);
+        case 8: return pick_nt<T, 8>(a, s);
+        default: return pick_nt<T, 0>(a, s);
     }
 }
 
@@ -104,9 +115,11 @@ hipError_t launch_all_gather(int K, const ConstPtrs& shards, const MutPtrs& full
     bool bases = true;
     for (int r = 0; r < K; ++r)
         bases = bases && (((uintptr_t)shards.p[r]) & 15) == 0 && (((uintptr_t)fulls.p[r]) & 15) == 0;
-    int used = 0, max_units = 1;
+    int used = 0;
+    int64_t units = 0;
     for (int s = 0; s < n_segs; ++s) {
         if (segs[s].numel == 0) continue;
+        a.unit0[used] = units;
         AgSeg& d = a.seg[used++];
         d.shard_off = segs[s].shard_off;
         d.full_off = segs[s].full_off;
@@ -120,12 +133,13 @@ hipError_t launch_all_gather(int K, const ConstPtrs& shards, const MutPtrs& full
                             (((d.full_off + (int64_t)j * d.C) * es) & 15) == 0;
             if (ok) d.vec_mask |= 1ull << j;
         }
-        const int units = K * d.tiles_per_chunk;
-        if (units > max_units) max_units = units;
+        units += (int64_t)K * d.tiles_per_chunk;
     }
     if (used == 0) return hipSuccess;
-    if (dt == ZR_BF16) return pick_k<uint16_t>(a, used, max_units, stream);
-    return pick_k<float>(a, used, max_units, stream);
+    a.unit0[used] = units;
+    a.nseg = used;
+    if (dt == ZR_BF16) return pick_k<uint16_t>(a, stream);
+    return pick_k<float>(a, stream);
 }
 
 }  // namespace zr
