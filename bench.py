@@ -365,9 +365,13 @@ def bench_zero2_overlap(args):
         for i in range(len(buckets)):
             delay(compute_us[i], prod)
 
+    # the phases are 10 ms apart (idle, untimed), so a kernel trace shows them apart
     ms_compute = wall(compute_only)
+    time.sleep(0.01)
     ms_reduce = wall(lambda: syncs[2].step(producer_stream=prod))
+    time.sleep(0.01)
     ms_overlap = wall(lambda: syncs[2].step(producer_stream=prod, produce=produce))
+    time.sleep(0.01)
     ms_serial = wall(lambda: syncs[1].step(producer_stream=prod, produce=produce))
     for s_ in syncs.values():
         s_.close()
@@ -461,8 +465,11 @@ def bench_zero3_prefetch(args):
     rate = gather_bytes / (ms_gather * 1e-3)   # bytes per second, host loop included
     compute_us = [args.compute_ratio * sum(numels[p] for p in st) * 2 * (K + 1) / rate * 1e6
                   for st in steps]
+    # the phases are 10 ms apart (idle, untimed), so a kernel trace shows them apart
     ms_compute, _ = walk(compute_us=compute_us, gathers=False, passes=passes)
+    time.sleep(0.01)
     ms_overlap, st = walk(compute_us=compute_us, passes=passes)
+    time.sleep(0.01)
     ms_serial, _ = walk(serial=True, compute_us=compute_us, passes=passes)
     exposed = max(0.0, ms_overlap - ms_compute)
     return {
