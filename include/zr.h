@@ -72,7 +72,16 @@ typedef enum {
                                cannot hold what must be live */
 } zr_status;
 
-typedef enum { ZR_BF16 = 0, ZR_FP32 = 1 } zr_dtype;
+/* The _MIN_/_MAX_ enumerators make every int a value of the enum type in C
+ * and C++ alike, so any int a caller passes is well defined; the library
+ * rejects values other than the named ones with ZR_ERR_UNSUPPORTED (dtypes)
+ * or ZR_ERR_INVALID (orders). */
+typedef enum {
+    ZR_BF16 = 0,
+    ZR_FP32 = 1,
+    ZR_DTYPE_MIN_ = -2147483647 - 1,
+    ZR_DTYPE_MAX_ = 2147483647
+} zr_dtype;
 
 /* ZR_ORDER_RING: the ring order above, bit-exact and deterministic.
  * ZR_ORDER_FREE: ranks summed in an order of the library's choosing (fp32
@@ -83,7 +92,13 @@ typedef enum { ZR_BF16 = 0, ZR_FP32 = 1 } zr_dtype;
  * partial sums between ranks (the issue page's setup communicates in bf16):
  * acc = x_j; acc = RNE_bf16(acc + x_{j+1}); ...; bit-exact and deterministic.
  * For fp32 input it is the same as ZR_ORDER_RING. */
-typedef enum { ZR_ORDER_RING = 0, ZR_ORDER_FREE = 1, ZR_ORDER_RING_WIRE = 2 } zr_order;
+typedef enum {
+    ZR_ORDER_RING = 0,
+    ZR_ORDER_FREE = 1,
+    ZR_ORDER_RING_WIRE = 2,
+    ZR_ORDER_MIN_ = -2147483647 - 1,
+    ZR_ORDER_MAX_ = 2147483647
+} zr_order;
 
 /* One tensor of an all-gather: its shard starts at element shard_off of
  * every rank's shard buffer and holds C = ceil(numel / K) elements; the

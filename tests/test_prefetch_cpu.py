@@ -37,7 +37,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = os.path.join(KIT, "libpf_sim.so")
+        # PF_SIM_LIBRARY may name another build of the same simulator (the sanitizer
+        # test runs this module against one)
+        path = os.environ.get("PF_SIM_LIBRARY") or os.path.join(KIT, "libpf_sim.so")
         if not os.path.exists(path):
             import sys
             sys.path.insert(0, os.path.join(ROOT, "tests"))

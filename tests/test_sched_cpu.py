@@ -30,7 +30,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = os.path.join(KIT, "libsched_sim.so")
+        # SCHED_SIM_LIBRARY may name another build of the same simulator (the sanitizer
+        # test runs this module against one)
+        path = os.environ.get("SCHED_SIM_LIBRARY") or os.path.join(KIT, "libsched_sim.so")
         if not os.path.exists(path):
             import sys
             sys.path.insert(0, os.path.join(ROOT, "tests"))
