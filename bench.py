@@ -134,6 +134,8 @@ def bench_zero2(args, accumulate=False):
     cpu = None
     if not args.no_cpu_baseline and not accumulate:
         cpu = cpu_baseline_zero2(grads, parts, buckets[0], K, args)
+        if cpu and cpu.get("value"):
+            cpu["gpu_over_oracle"] = round(value / cpu["value"], 1)
     sync.close()
     if accumulate:
         metric = ("reduce-scatter+avg+accumulate GB/s (gradient-accumulation micro-step), K=8, "
