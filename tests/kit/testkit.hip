@@ -80,3 +80,21 @@ extern "C" int tk_read(const void* src, void* sink, long long bytes, int blocks,
                        (const uint4*)src, (uint4*)sink, bytes / 16);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
+
+// tk_xcd: every block of a one-block-per-tile launch copies one 4 KiB tile
+// (so blocks retire at varying times, as in the library's kernels) and
+// records the XCD it ran on, read from the XCC_ID hardware register (bits
+// 3:0), in xcd[blockIdx.x]. src and dst hold blocks * 4 KiB.
+__global__ void __launch_bounds__(256) tk_xcd_kernel(const uint4* __restrict__ src,
+                                                     uint4* __restrict__ dst, int* __restrict__ xcd) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    dst[i] = src[i];
+    if (threadIdx.x == 0) xcd[blockIdx.x] = (int)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15);
+}
+
+extern "C" int tk_xcd(const void* src, void* dst, void* xcd, int blocks, void* stream) {
+    if (blocks < 1 || !src || !dst || !xcd) return 1;
+    hipLaunchKernelGGL(tk_xcd_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const uint4*)src, (uint4*)dst, (int*)xcd);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
