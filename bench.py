@@ -126,6 +126,10 @@ def bench_zero2(args, accumulate=False):
     full = sorted(ms for ms, b in zip(launch_ms, launch_bytes) if b == max(launch_bytes))
     full_med, full_min = full[len(full) // 2], full[0]
     bytes_per_launch = sum(launch_bytes) / len(launch_bytes)
+    # each bucket's rate over the timed steps (its launches are every nb-th)
+    nb = len(buckets)
+    per_bucket = [round(launch_bytes[b] * (len(launch_ms) // nb) / (sum(launch_ms[b::nb]) * 1e-3) / 1e9, 1)
+                  for b in range(nb)]
     src = kernel_source_hash(["zr_rs.hip", "zr_fold.hpp", "zr_device.hpp"])
     traffic = read_traffic("rs_ring_bf16_f32_k8_zero2.counters.txt", src, bytes_per_launch)
     print(f"# zero2: {ms_step:.3f} ms/step, kernel avg {avg_launch_ms:.3f} ms", file=sys.stderr,
@@ -165,6 +169,7 @@ def bench_zero2(args, accumulate=False):
                      "traffic": traffic, "avg_launch_ms": round(avg_launch_ms, 4),
                      "full_bucket_launch_ms_median": round(full_med, 4),
                      "full_bucket_launch_ms_min": round(full_min, 4),
+                     "per_bucket_GBps": per_bucket,
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
                      "kernel_source_sha256_16": src},
         "cpu_baseline": cpu,
