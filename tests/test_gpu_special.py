@@ -118,28 +118,34 @@ def assert_match(got: np.ndarray, want: np.ndarray, what: str):
     assert not diff.any(), f"{what}: {int(np.sum(diff))} of {int(np.sum(~wn))} non-NaN outputs differ"
 
 
+SMALL = None        # K * 2048 * 3 + 37 * K + 5: a few tiles, one slice per wave
+FOUR = 8 * 300000 + 13  # enough tiles for the four-slice tiles of large buckets
+
 RS_CASES = [
-    # K, in_bf16, out_bf16, average, order, offset, accumulate
-    (8, True, False, True, RING, 0, False),
-    (8, True, True, True, RING, 0, False),
-    (8, False, False, True, RING, 0, False),
-    (8, False, True, False, RING, 0, False),   # bf16 rounding of exact sums, overflow ties
-    (8, False, True, True, RING, 0, False),
-    (5, True, False, True, RING, 0, False),    # IEEE divide of subnormal sums
-    (5, False, False, True, RING, 0, False),
-    (8, True, False, True, RING, 1, False),    # element-wise path
-    (8, True, False, True, WIRE, 0, False),
-    (5, True, True, True, WIRE, 0, False),
-    (8, True, False, True, RING, 0, True),     # accumulate into special partitions
-    (8, False, False, False, RING, 1, True),
-    (64, True, False, True, RING, 0, False),   # generic-K fold
+    # K, N, in_bf16, out_bf16, average, order, offset, accumulate
+    (8, SMALL, True, False, True, RING, 0, False),
+    (8, SMALL, True, True, True, RING, 0, False),
+    (8, SMALL, False, False, True, RING, 0, False),
+    (8, SMALL, False, True, False, RING, 0, False),   # bf16 rounding of exact sums, overflow ties
+    (8, SMALL, False, True, True, RING, 0, False),
+    (5, SMALL, True, False, True, RING, 0, False),    # IEEE divide of subnormal sums
+    (5, SMALL, False, False, True, RING, 0, False),
+    (8, SMALL, True, False, True, RING, 1, False),    # element-wise path
+    (8, SMALL, True, False, True, WIRE, 0, False),
+    (5, SMALL, True, True, True, WIRE, 0, False),
+    (8, SMALL, True, False, True, RING, 0, True),     # accumulate into special partitions
+    (8, SMALL, False, False, False, RING, 1, True),
+    (64, SMALL, True, False, True, RING, 0, False),   # generic-K fold
+    (8, FOUR, True, False, True, RING, 0, False),     # the large-bucket kernel
+    (8, FOUR, True, False, True, RING, 0, True),
+    (8, FOUR, True, True, True, WIRE, 0, False),
 ]
 
 
-@pytest.mark.parametrize("K,in_bf16,out_bf16,average,order,offset,acc", RS_CASES)
-def test_reduce_scatter_special_values(K, in_bf16, out_bf16, average, order, offset, acc):
+@pytest.mark.parametrize("K,N,in_bf16,out_bf16,average,order,offset,acc", RS_CASES)
+def test_reduce_scatter_special_values(K, N, in_bf16, out_bf16, average, order, offset, acc):
     import torch
-    N = K * 2048 * 3 + 37 * K + 5
+    N = N or K * 2048 * 3 + 37 * K + 5
     C = -(-N // K)
     rng = np.random.default_rng(K * 131 + N + 7 * order + offset + (3 if acc else 0))
     xs = special(rng, K, N, fp32=not in_bf16)
@@ -199,6 +205,7 @@ def test_allreduce_special_values(K, bf16, average, order, fused):
     (8, [5, 2049, 7, 40000, 33], 11, True, False, RING),
     (5, [77, 30001, 1], 4, False, False, RING),
     (8, [30001, 40000, 9], 0, True, True, WIRE),
+    (8, [1000000, 1500001, 3], 5, True, False, RING),   # four-slice tiles
 ])
 def test_reduce_scatter_frags_special_values(K, sizes, extra, in_bf16, out_bf16, order):
     import torch
