@@ -3,7 +3,8 @@
 The library's calls allocate nothing, issue no memset and never synchronise
 the device, so a caller can capture them. One graph holds a reduce-scatter,
 an accumulating reduce-scatter, a discrete reduce-scatter (the one-shot call
-and a prepared plan) and an all-gather. It is replayed several times; before
+and a prepared plan), a bucket flatten, a fused and a composed all-reduce
+(out of place) and an all-gather. It is replayed several times; before
 each replay the program rewrites the inputs eagerly and synchronises, and
 after it every output is compared bit for bit with the same calls made
 eagerly on the same inputs.
@@ -39,6 +40,10 @@ def test_graph_replays_match_eager_calls():
                     acc=[torch.empty(C, dtype=torch.float32, device="cuda") for _ in range(K)],
                     frag=[torch.empty(CF, dtype=torch.float32, device="cuda") for _ in range(K)],
                     plan=[torch.empty(CF, dtype=torch.float32, device="cuda") for _ in range(K)],
+                    flat=[torch.empty(NF, dtype=torch.bfloat16, device="cuda") for _ in range(K)],
+                    ar=[torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(K)],
+                    arc=[torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(K)],
+                    scratch=torch.empty(K * C, dtype=torch.bfloat16, device="cuda"),
                     ag=[torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(K)])
 
     g_out, e_out = outputs(), outputs()
@@ -50,6 +55,9 @@ def test_graph_replays_match_eager_calls():
         zr.zr_reduce_scatter_avg(x, N, o["acc"], chunk_shift=1, average=True, accumulate=True)
         zr.zr_reduce_scatter_frags(frags, SIZES, NF, o["frag"], chunk_shift=1, average=True)
         plan.launch()
+        zr.zr_flatten_bucket(frags, SIZES, o["flat"], NF)
+        zr.zr_allreduce(x, o["ar"], N, average=False, fused=True)
+        zr.zr_allreduce(x, o["arc"], N, average=True, fused=False, scratch=o["scratch"])
         zr.zr_all_gather(shards, o["ag"], segs, chunk_shift=0)
 
     def fill(tag):
@@ -80,11 +88,11 @@ def test_graph_replays_match_eager_calls():
         torch.cuda.synchronize()
         work(e_out, e_plan)
         torch.cuda.synchronize()
-        for key in ("rs", "acc", "frag", "plan", "ag"):
+        for key in ("rs", "acc", "frag", "plan", "flat", "ar", "arc", "ag"):
             for r in range(K):
                 got = g_out[key][r].cpu()
                 want = e_out[key][r].cpu()
-                if key == "ag":
+                if got.dtype == torch.bfloat16:
                     got, want = got.view(torch.int16), want.view(torch.int16)
                 assert np.array_equal(bits(got.numpy()), bits(want.numpy())), (tag, key, r)
     g_plan.close()
