@@ -50,7 +50,8 @@ def kernel_source_hash(files):
 def read_traffic(name, src_hash, algorithmic, key="hbm_bytes_per_launch"):
     """HBM bytes per launch (or per step) from a committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known size),
-    or None when it is missing or was taken on a different kernel source."""
+    or None when it is missing, was taken on a different kernel source, or
+    measured a workload whose algorithmic bytes differ from `algorithmic`."""
     path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
@@ -61,7 +62,10 @@ def read_traffic(name, src_hash, algorithmic, key="hbm_bytes_per_launch"):
             kv[k.strip()] = v.strip()
     if kv.get("kernel_source_sha256_16") != src_hash:
         return None
+    algo_key = key.replace("hbm_bytes", "algorithmic_bytes")
     try:
+        if abs(float(kv[algo_key]) - algorithmic) > 1e-3 * algorithmic:
+            return None
         return int(float(kv[key]))
     except (KeyError, ValueError):
         return None
@@ -131,7 +135,8 @@ def bench_zero2(args, accumulate=False):
     per_bucket = [round(launch_bytes[b] * (len(launch_ms) // nb) / (sum(launch_ms[b::nb]) * 1e-3) / 1e9, 1)
                   for b in range(nb)]
     src = kernel_source_hash(["zr_rs.hip", "zr_fold.hpp", "zr_device.hpp"])
-    traffic = read_traffic("rs_ring_bf16_f32_k8_zero2.counters.txt", src, bytes_per_launch)
+    traffic = read_traffic("rs_ring_bf16_f32_k8_zero2" + ("_accum" if accumulate else "") +
+                           ".counters.txt", src, bytes_per_launch)
     print(f"# zero2: {ms_step:.3f} ms/step, kernel avg {avg_launch_ms:.3f} ms", file=sys.stderr,
           flush=True)
 

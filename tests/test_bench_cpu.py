@@ -38,12 +38,17 @@ def test_traffic_is_read_only_for_matching_sources(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     src = bench.kernel_source_hash(["zr_rs.hip", "zr_fold.hpp", "zr_device.hpp"])
     (tmp_path / "k.counters.txt").write_text(
-        "# a summary\nkernel_source_sha256_16 = %s\nhbm_bytes_per_launch = 12345.0\n" % src)
-    assert bench.read_traffic("k.counters.txt", src, 1) == 12345
-    assert bench.read_traffic("k.counters.txt", "0" * 16, 1) is None   # kernel changed since
-    assert bench.read_traffic("missing.txt", src, 1) is None
+        "# a summary\nkernel_source_sha256_16 = %s\nhbm_bytes_per_launch = 12345.0\n"
+        "algorithmic_bytes_per_launch = 12000\n" % src)
+    assert bench.read_traffic("k.counters.txt", src, 12000) == 12345
+    assert bench.read_traffic("k.counters.txt", "0" * 16, 12000) is None   # kernel changed since
+    assert bench.read_traffic("k.counters.txt", src, 14400) is None   # another workload's bytes
+    assert bench.read_traffic("missing.txt", src, 12000) is None
     (tmp_path / "bad.counters.txt").write_text("kernel_source_sha256_16 = %s\n" % src)
-    assert bench.read_traffic("bad.counters.txt", src, 1) is None      # no byte count
+    assert bench.read_traffic("bad.counters.txt", src, 12000) is None      # no byte count
+    (tmp_path / "old.counters.txt").write_text(
+        "kernel_source_sha256_16 = %s\nhbm_bytes_per_launch = 12345.0\n" % src)
+    assert bench.read_traffic("old.counters.txt", src, 12000) is None      # no byte model
 
 
 def test_committed_counter_summaries_carry_what_the_bench_reads():
@@ -57,4 +62,5 @@ def test_committed_counter_summaries_carry_what_the_bench_reads():
                 kv[k.strip()] = v.strip()
         assert len(kv.get("kernel_source_sha256_16", "")) == 16, n
         assert any(k.startswith("hbm_bytes_per_") for k in kv), n
+        assert any(k.startswith("algorithmic_bytes_per_") for k in kv), n
         assert "rocprofv3" in open(os.path.join(bench.PROFILES, n)).read(), n  # the command that made it
