@@ -22,13 +22,16 @@
 // has one block per tile of the launch, in order, so blocks stay balanced
 // however unequal the fragments are, and the blocks in flight work on one
 // compact window of memory (a persistent grid striding over the tiles ran
-// 7-15% slower). A segment whose rank buffers share one
-// quad phase starts its vector tiles at rank j's next 128-byte line: the
-// first tile also folds the head element by element, the last folds its whole
-// quads as vectors and the last few elements one by one, and the stores fall
-// back to single elements when the partition side is not quad aligned. Other
-// segments fold element by element, 1024 elements per tile. The padding entry
-// has null pointers and writes +0 (old + 0 when accumulating).
+// 7-15% slower). A segment whose rank buffers share one quad phase starts
+// its vector tiles at a 128-byte line of rank j whose output lies less than
+// a line after a 16 KiB boundary of the partition, as the contiguous kernel
+// does: the first tile also folds the head before it (as quads, and its
+// edge elements one by one), the last folds its whole quads as vectors and
+// the last few elements one by one, and the stores fall back to single
+// elements when the partition side is not quad aligned. Other segments fold
+// element by element, 1024 elements per tile. The padding entry has null
+// pointers, starts its tiles on a 16 KiB boundary of the partition and
+// writes +0 (old + 0 when accumulating).
 #include <new>
 #include <vector>
 
@@ -145,9 +148,20 @@ __global__ void __launch_bounds__(kThreads) rsf_kernel(const RsfArgs a) {
             }
         };
         // tiles cover [h, len), the last one possibly partial; tile 0 also
-        // folds the head [0, h)
-        if (tt == 0)
-            for (int64_t o = threadIdx.x; o < h && o < len; o += kThreads) elem(o);
+        // folds the head [0, h): as quads from the first offset on the
+        // tiles' quad grid (h mod 4), its other elements one by one
+        if (tt == 0) {
+            const int64_t hc = h < len ? h : len;
+            const int64_t q0 = h & 3;
+            for (int64_t o = threadIdx.x; o < q0 && o < hc; o += kThreads) elem(o);
+            const int64_t qe = hc > q0 ? q0 + ((hc - q0) & ~(int64_t)3) : q0;
+            for (int64_t q = q0 + (int64_t)threadIdx.x * 4; q < qe; q += kThreads * 4) {
+                float acc[1][4];
+                fold(q, acc, std::integral_constant<int, 1>{});
+                emit(q, acc, std::integral_constant<int, 1>{});
+            }
+            for (int64_t o = qe + threadIdx.x; o < hc; o += kThreads) elem(o);
+        }
         const int64_t ot = h + tt * T;
         if (ot >= len) continue;
         const int64_t o0 = ot + (int64_t)wave * (S * 256) + lane * 4;
@@ -209,14 +223,28 @@ LaunchFn pick_avg(int K, int avg, int order, bool small) {
     }
 }
 
-// Head of a segment whose K rank runs start at byte addresses addr[r]: the
-// elements before rank j's next 128-byte line, or -1 when the runs do not
-// share one quad phase (no offset aligns them all for quad loads).
-int16_t segment_head(const uintptr_t* addr, int K, int j, uintptr_t es) {
+// Output block the vector tiles' writes are aligned to (bytes): tiles whose
+// writes straddle 16 KiB blocks streamed 2-4% slower.
+constexpr uintptr_t kOutBlock = 16384;
+
+// Elements from the partition-side address `out` to the next kOutBlock
+// boundary.
+int64_t to_block(uintptr_t out, uintptr_t out_es) { return (int64_t)((kOutBlock - out % kOutBlock) % kOutBlock / out_es); }
+
+// Head of a segment whose K rank runs start at byte addresses addr[r] and
+// whose output starts at `out`: the offset of the first 128-byte line of
+// rank j at or after the output's next kOutBlock boundary, or -1 when the
+// runs do not share one quad phase (no offset aligns them all for quad
+// loads).
+int16_t segment_head(const uintptr_t* addr, int K, int j, uintptr_t es, uintptr_t out,
+                     uintptr_t out_es) {
     const uintptr_t quad = 4 * es;
     for (int r = 1; r < K; ++r)
         if ((addr[r] - addr[0]) % quad != 0) return -1;
-    return (int16_t)(((128 - addr[j] % 128) % 128) / es);
+    const int64_t line = (int64_t)(128 / es);
+    const int64_t to_line = (int64_t)(((128 - addr[j] % 128) % 128) / es);
+    const int64_t b = to_block(out, out_es);
+    return (int16_t)(b + ((to_line - b) % line + line) % line);
 }
 
 // Cuts the entries into launches: each fills one argument block with up to
@@ -263,15 +291,15 @@ void build_typed(RsfArgs& a, const FragEntry* entries, int n_entries, int64_t T,
             const int64_t len = hi - lo;
             uintptr_t addr[kMaxRanks];
             int16_t h;
+            const int q = ((j - a.shift) % K + K) % K;  // holder
+            const uintptr_t o = (uintptr_t)a.out.p[q] + (uintptr_t)(lo - jc) * sizeof(TOut);
             if (pad) {
-                // no input: align the partition side to its 128-byte lines
-                const int q = ((j - a.shift) % K + K) % K;
-                const uintptr_t o = (uintptr_t)a.out.p[q] + (uintptr_t)(lo - jc) * sizeof(TOut);
-                h = (int16_t)(((128 - o % 128) % 128) / sizeof(TOut));
+                // no input: align the partition side to its 16 KiB blocks
+                h = (int16_t)to_block(o, sizeof(TOut));
             } else {
                 for (int r = 0; r < K; ++r)
                     addr[r] = (uintptr_t)f.ptr[r] + (uintptr_t)(lo - f.off) * sizeof(TIn);
-                h = segment_head(addr, K, j, sizeof(TIn));
+                h = segment_head(addr, K, j, sizeof(TIn), o, sizeof(TOut));
             }
             const int s = a.nseg++;
             a.seg_m[s] = (uint8_t)m;

@@ -61,6 +61,9 @@ class Zero2GradSync:
         for p in self.partitions:
             if p.numel() < poff:
                 raise ValueError(f"partition holds {p.numel()} elements, needs {poff}")
+        if reduction_stream is None:
+            import torch
+            reduction_stream = torch.cuda.current_stream()  # what the scheduler then takes
         self.reduction_stream = reduction_stream
         self.sched = Sched(n_buffers=n_buffers, max_producers=1,
                            reduction_stream=reduction_stream)
@@ -72,7 +75,8 @@ class Zero2GradSync:
         stream, after the stream has waited for the buffer to be free and
         before the bucket's reduction, which waits for it. `timing`, if given,
         receives (start, end) torch events recorded on the reduction stream
-        around each bucket's launch. Micro-step 0 overwrites the partitions;
+        around each bucket's launch, after the reduction stream has waited for the
+        producer. Micro-step 0 overwrites the partitions;
         later micro-steps of a gradient-accumulation window add to them
         ("DeepSpeed ZeRO-3 源码解析", 5.3 and 6)."""
         import torch
@@ -85,6 +89,10 @@ class Zero2GradSync:
             if timing is not None:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
+                # the reduction's wait on the producer comes before the start
+                # event, so the pair brackets the launch alone (the launch's
+                # own wait then finds the producer's work done)
+                self.reduction_stream.wait_stream(prod)
                 e0.record(self.reduction_stream)
             self.sched.submit_rs(buf, [prod], ins, n, outs, chunk_shift=self.shift,
                                  average=self.average, order=self.order, in_dtype=self.in_dt,
