@@ -546,3 +546,69 @@ def test_zero_sized_calls_enqueue_nothing():
     m.zr_all_gather([t] * 4, [t] * 4, [])
     m.zr_flatten_bucket([[] for _ in range(4)], [], [t] * 4, 0)
     torch.cuda.synchronize()
+
+
+# Output offsets (elements) across the 16 KiB blocks the vector tiles align
+# to: the head before the first tile runs from nothing to a whole block plus
+# a line, and can exceed a small chunk.
+HEAD_CASES = [
+    # K, N, out_bf16, out offset
+    (8, 8 * 40000 + 13, False, 0),
+    (8, 8 * 40000 + 13, False, 4),
+    (8, 8 * 40000 + 13, False, 1000),
+    (8, 8 * 40000 + 13, False, 4092),
+    (8, 8 * 40000 + 13, True, 8188),
+    (8, 8 * 40000 + 13, True, 3000),
+    (8, 8 * 3000 + 5, False, 2048),      # odd C: only some chunks take the vector path
+    (8, 8 * 40000 - 5, False, 1000),     # C a multiple of 4: every chunk vector, padded tail
+    (8, 8 * 1000 - 3, False, 2048),      # heads longer than the chunk (and its padding)
+    (8, 8 * 1000 - 3, True, 100),
+    (5, 5 * 20000 + 3, False, 777),
+    (64, 64 * 9000 + 1, True, 5000),
+    (8, 8 * 300000 + 13, False, 2500),   # four-slice tiles
+]
+
+
+@pytest.mark.parametrize("K,N,out_bf16,out_off", HEAD_CASES)
+def test_reduce_scatter_heads_across_output_blocks(K, N, out_bf16, out_off):
+    import torch
+    case = K * 7919 + N + out_off
+    xs = make_inputs(K, N, True, case)
+    C = -(-N // K)
+    ins = [Guarded(N, torch.bfloat16, 0, xs[r]) for r in range(K)]
+    outs = [Guarded(C, torch_dt(out_bf16), out_off) for _ in range(K)]
+    zr().zr_reduce_scatter_avg([g.ptr() for g in ins], N, [g.ptr() for g in outs], chunk_shift=1,
+                               average=True, in_dtype=torch.bfloat16, out_dtype=torch_dt(out_bf16))
+    torch.cuda.synchronize()
+    want = oracle.reduce_scatter(xs, N, np.uint16 if out_bf16 else np.float32, shift=1, average=True)
+    for r in range(K):
+        assert np.array_equal(bits(outs[r].get()), bits(want[r])), f"rank {r}"
+        assert outs[r].guards_intact()
+
+
+@pytest.mark.parametrize("K,sizes,out_bf16,out_off", [
+    (8, [5000, 3, 70000, 40001], False, 1000),
+    (8, [5000, 3, 70000, 40001], True, 8000),
+    (8, [30001, 1, 2], False, 4096 - 3),
+    (5, [12345, 67890], False, 333),
+    (8, [1000000, 1500001, 3], False, 2500),   # four-slice tiles
+])
+def test_reduce_scatter_frags_heads_across_output_blocks(K, sizes, out_bf16, out_off):
+    import torch
+    total = sum(sizes)
+    N = total + 7
+    C = -(-N // K)
+    frags_np = [[synth.host_normal_bf16(SEED + 91, r * 64 + p, 0, n, 1.0, 0.01, 1e4)
+                 for p, n in enumerate(sizes)] for r in range(K)]
+    frags = [[Guarded(n, torch.bfloat16, 0, frags_np[r][p]) for p, n in enumerate(sizes)]
+             for r in range(K)]
+    outs = [Guarded(C, torch_dt(out_bf16), out_off) for _ in range(K)]
+    zr().zr_reduce_scatter_frags([[g.ptr() for g in row] for row in frags], sizes, N,
+                                 [g.ptr() for g in outs], chunk_shift=1, average=True,
+                                 in_dtype=torch.bfloat16, out_dtype=torch_dt(out_bf16))
+    torch.cuda.synchronize()
+    want = oracle.reduce_scatter(oracle.flatten(frags_np, sizes, N), N,
+                                 np.uint16 if out_bf16 else np.float32, shift=1, average=True)
+    for r in range(K):
+        assert np.array_equal(bits(outs[r].get()), bits(want[r])), f"rank {r}"
+        assert outs[r].guards_intact()
