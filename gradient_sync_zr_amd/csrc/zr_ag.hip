@@ -8,14 +8,16 @@
 // (j - shift) mod K, copied to every rank's full buffer.
 //
 // Grid: one block per tile of the launch. The tiles of a segment (one
-// tensor) are its (chunk, 2048-element tile) pairs, chunk by chunk, and the
-// segments' tiles follow each other, so blocks stay balanced however unequal
-// the tensors are; a block finds its segment by a uniform binary search over
-// the segments' first tiles. (A persistent grid striding over the tiles ran
-// 10-15% slower.) A lane loads its 8 shard
-// elements once (16 bytes) and stores them to all K full buffers, so each
-// shard byte is read once and written K times. Chunk starts that are not
-// 16-byte aligned on either side, and ragged ends, copy element by element.
+// tensor) are its (chunk, tile) pairs, chunk by chunk, and the segments'
+// tiles follow each other, so blocks stay balanced however unequal the
+// tensors are; a block finds its segment by a uniform binary search over the
+// segments' first tiles. (A persistent grid striding over the tiles ran
+// 10-15% slower.) A tile writes 16 KiB to every full buffer: each lane loads
+// kAgSub groups of 8 shard elements (16 bytes each for bf16), all before its
+// first store, and stores each to all K full buffers, so each shard byte is
+// read once and written K times. (Tiles of 16 KiB per destination ran 1% faster
+// than tiles of 4, 8 or 32 KiB.) Chunk starts that are not 16-byte aligned on
+// either side, and ragged ends, copy element by element.
 #include "zr_device.hpp"
 #include "zr_internal.hpp"
 
@@ -38,8 +40,15 @@ struct AgArgs {
 };
 static_assert(sizeof(AgArgs) <= 4096, "all-gather arguments exceed 4 KB");
 
+// Groups of kGroup elements per lane in one tile: 16 KiB per destination.
+template <typename T>
+constexpr int kAgSub = 16384 / (kTile * (int)sizeof(T));
+template <typename T>
+constexpr int64_t kAgTile = (int64_t)kAgSub<T> * kTile;
+
 template <typename T, int KS, bool NT>
 __global__ void __launch_bounds__(kThreads) ag_kernel(const AgArgs a) {
+    constexpr int SUB = kAgSub<T>;
     const int K = KS > 0 ? KS : a.K;
     for (int64_t u = blockIdx.x; u < a.unit0[a.nseg]; u += gridDim.x) {
         // the tile's segment: the last s with unit0[s] <= u (uniform)
@@ -57,26 +66,38 @@ __global__ void __launch_bounds__(kThreads) ag_kernel(const AgArgs a) {
         const int t = ul - j * sg.tiles_per_chunk;
         int holder = j - a.shift;
         if (holder < 0) holder += K;
-        const int64_t o = (int64_t)t * kTile + (int64_t)threadIdx.x * kGroup;
-        const int64_t g = (int64_t)j * sg.C + o;
-        if (o >= sg.C || g >= sg.numel) continue;
-        const T* src = static_cast<const T*>(a.shards.p[holder]) + sg.shard_off + o;
-        const int64_t dst_off = sg.full_off + g;
-        if (((sg.vec_mask >> j) & 1ull) && o + kGroup <= sg.C && g + kGroup <= sg.numel) {
-            const Group<T> v = load_group<T, NT>(src);
-            if constexpr (KS > 0) {
+        const bool vec_chunk = (sg.vec_mask >> j) & 1ull;
+        const T* shard = static_cast<const T*>(a.shards.p[holder]) + sg.shard_off;
+        // group k of this lane: chunk offset (t * SUB + k) * kTile + lane * kGroup
+        Group<T> v[SUB];
+        bool whole[SUB];
 #pragma unroll
-                for (int r = 0; r < KS; ++r) store_group<T, NT>(static_cast<T*>(a.fulls.p[r]) + dst_off, v);
-            } else {
-                for (int r = 0; r < K; ++r) store_group<T, NT>(static_cast<T*>(a.fulls.p[r]) + dst_off, v);
-            }
-        } else {
-            int64_t n = sg.C - o;
-            if (sg.numel - g < n) n = sg.numel - g;
-            if (n > kGroup) n = kGroup;
-            for (int e = 0; e < (int)n; ++e) {
-                const T v = src[e];
-                for (int r = 0; r < K; ++r) static_cast<T*>(a.fulls.p[r])[dst_off + e] = v;
+        for (int k = 0; k < SUB; ++k) {
+            const int64_t o = ((int64_t)t * SUB + k) * kTile + (int64_t)threadIdx.x * kGroup;
+            const int64_t g = (int64_t)j * sg.C + o;
+            whole[k] = vec_chunk && o + kGroup <= sg.C && g + kGroup <= sg.numel;
+            if (whole[k]) v[k] = load_group<T, NT>(shard + o);
+        }
+#pragma unroll
+        for (int k = 0; k < SUB; ++k) {
+            const int64_t o = ((int64_t)t * SUB + k) * kTile + (int64_t)threadIdx.x * kGroup;
+            const int64_t g = (int64_t)j * sg.C + o;
+            const int64_t dst_off = sg.full_off + g;
+            if (whole[k]) {
+                if constexpr (KS > 0) {
+#pragma unroll
+                    for (int r = 0; r < KS; ++r) store_group<T, NT>(static_cast<T*>(a.fulls.p[r]) + dst_off, v[k]);
+                } else {
+                    for (int r = 0; r < K; ++r) store_group<T, NT>(static_cast<T*>(a.fulls.p[r]) + dst_off, v[k]);
+                }
+            } else if (o < sg.C && g < sg.numel) {
+                int64_t n = sg.C - o;
+                if (sg.numel - g < n) n = sg.numel - g;
+                if (n > kGroup) n = kGroup;
+                for (int e = 0; e < (int)n; ++e) {
+                    const T x = shard[o + e];
+                    for (int r = 0; r < K; ++r) static_cast<T*>(a.fulls.p[r])[dst_off + e] = x;
+                }
             }
         }
     }
@@ -112,6 +133,7 @@ hipError_t launch_all_gather(int K, const ConstPtrs& shards, const MutPtrs& full
     a.K = K;
     a.shift = shift;
     const int es = dt == ZR_BF16 ? 2 : 4;
+    const int64_t tile = dt == ZR_BF16 ? kAgTile<uint16_t> : kAgTile<float>;  // elements per tile
     bool bases = true;
     for (int r = 0; r < K; ++r)
         bases = bases && (((uintptr_t)shards.p[r]) & 15) == 0 && (((uintptr_t)fulls.p[r]) & 15) == 0;
@@ -125,7 +147,7 @@ hipError_t launch_all_gather(int K, const ConstPtrs& shards, const MutPtrs& full
         d.full_off = segs[s].full_off;
         d.numel = segs[s].numel;
         d.C = (d.numel + K - 1) / K;
-        d.tiles_per_chunk = (int)((d.C + kTile - 1) / kTile);
+        d.tiles_per_chunk = (int)((d.C + tile - 1) / tile);
         d.pad_ = 0;
         d.vec_mask = 0;
         for (int j = 0; j < K; ++j) {
