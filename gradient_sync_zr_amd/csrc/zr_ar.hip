@@ -12,7 +12,8 @@
 // Tiles are 4 waves x S slices x 256 global indices, lanes on 4-element quads
 // (as in the reduce-scatter kernel, so every store instruction writes one
 // contiguous span), one block per tile in index order (a persistent grid
-// striding over the tiles ran a few percent slower). A tile that lies inside one chunk and below N takes the
+// striding over the tiles ran a few percent slower). S makes a tile write
+// 16 KiB to every rank: at K = 64, 8 slices of bf16 ran 0.9% faster than 4. A tile that lies inside one chunk and below N takes the
 // vector path with the chunk (hence the fold's first rank) uniform across the
 // block; a tile that straddles a chunk boundary or the end of the buffer (at
 // most K of them) folds element by element, reading the rank pointers from an
@@ -32,7 +33,7 @@ struct ArArgs {
 };
 
 template <typename T>
-constexpr int kArSlices = sizeof(T) == 2 ? 4 : 2;
+constexpr int kArSlices = sizeof(T) == 2 ? 8 : 4;  // 16 KiB of output per rank per tile
 template <typename T>
 constexpr int64_t kArTile = (int64_t)(kThreads / 64) * kArSlices<T> * 256;
 
