@@ -178,7 +178,7 @@ hipError_t launch_t(const RsArgs& a, hipStream_t stream) {
 // launches in the ring order use one slice per wave.
 template <typename TIn, typename TOut, int AVG>
 hipError_t pick_k(const RsArgs& a, int order, bool small, hipStream_t s) {
-    constexpr int S = kSlices<TIn>;
+    constexpr int S = kSlices<TIn, TOut>;
     constexpr bool NT = kRsNontemporal;
     if (order == kFree) return launch_t<TIn, TOut, 0, AVG, kFree, NT, S>(a, s);
     if (order == kWire && sizeof(TIn) == 2) {
@@ -201,7 +201,7 @@ hipError_t pick_avg(const RsArgs& a, int avg_mode, int order, bool small, hipStr
 
 template <typename TIn, typename TOut>
 hipError_t launch_typed(RsArgs& a, int avg_mode, int order, hipStream_t s) {
-    constexpr int64_t T = kRsTile<TIn>;
+    constexpr int64_t T = kRsTile<TIn, TOut>;
     const bool small = order == kRing && ((a.C + T - 1) / T) * a.K < 2LL * device_cu_count();
     const int64_t Tl = small ? kRsTileOf<1> : T;
     // Vector path: every base aligned for quad access (8 bytes for bf16

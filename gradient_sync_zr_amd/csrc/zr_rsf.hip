@@ -203,7 +203,7 @@ using LaunchFn = hipError_t (*)(const RsfArgs&, hipStream_t);
 // Small plans in the ring order use one slice per wave.
 template <typename TIn, typename TOut, int AVG>
 LaunchFn pick_k(int K, int order, bool small) {
-    constexpr int S = kSlices<TIn>;
+    constexpr int S = kSlices<TIn, TOut>;
     constexpr bool NT = kRsNontemporal;
     if (order == kFree) return &launch_t<TIn, TOut, 0, AVG, kFree, NT, S>;
     if (order == kWire && sizeof(TIn) == 2) {
@@ -342,7 +342,7 @@ RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t 
     auto build = [&](auto tin, auto tout) {
         using TIn = decltype(tin);
         using TOut = decltype(tout);
-        build_typed<TIn, TOut>(a, entries, n_entries, kRsTile<TIn>, &plan->launches);
+        build_typed<TIn, TOut>(a, entries, n_entries, kRsTile<TIn, TOut>, &plan->launches);
         int64_t most = 0;
         for (const RsfArgs& l : plan->launches) most = most > l.tile0[l.nseg] ? most : l.tile0[l.nseg];
         const bool small = ord == kRing && most < 2LL * device_cu_count();
