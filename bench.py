@@ -83,6 +83,36 @@ def events_ms(pairs):
     return [a.elapsed_time(b) for a, b in pairs]
 
 
+def copy_ceiling_gbps(gib=4, reps=10):
+    """A plain streaming copy's read + write rate on this GPU, measured now:
+    the practical ceiling of a bandwidth-bound kernel (the test kit's
+    tk_copy, one block per 4 KiB). None when the test kit is not built."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "tests", "kit", "libtestkit.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.tk_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                            ctypes.c_void_p]
+    nbytes = gib << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    s = torch.cuda.current_stream().cuda_stream
+    ms = []
+    for i in range(reps + 2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        if lib.tk_copy(src.data_ptr(), dst.data_ptr(), nbytes, nbytes // 4096, s) != 0:
+            return None
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            ms.append(e0.elapsed_time(e1))
+    del src, dst
+    return round(2 * nbytes / (sum(ms) / len(ms) * 1e-3) / 1e9, 1)
+
+
 # ----------------------------------------------------------------- zero2
 def bench_zero2(args, accumulate=False):
     import numpy as np
@@ -146,6 +176,7 @@ def bench_zero2(args, accumulate=False):
         if cpu and cpu.get("value"):
             cpu["gpu_over_oracle"] = round(value / cpu["value"], 1)
     sync.close()
+    copy = copy_ceiling_gbps()
     if accumulate:
         metric = ("reduce-scatter+avg+accumulate GB/s (gradient-accumulation micro-step), K=8, "
                   "2.38B-elem bf16 grads")
@@ -175,6 +206,8 @@ def bench_zero2(args, accumulate=False):
                      "full_bucket_launch_ms_median": round(full_med, 4),
                      "full_bucket_launch_ms_min": round(full_min, 4),
                      "per_bucket_GBps": per_bucket,
+                     "copy_ceiling_GBps": copy,
+                     "of_copy_ceiling": round(achieved / copy, 4) if copy else None,
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
                      "kernel_source_sha256_16": src},
         "cpu_baseline": cpu,
