@@ -70,7 +70,7 @@ zr_status check_table(const void* const* t, int K, int64_t es, const char* name)
     if (!t) return fail(ZR_ERR_INVALID, "%s table is NULL", name);
     for (int r = 0; r < K; ++r) {
         if (!t[r]) return fail(ZR_ERR_INVALID, "%s[%d] is NULL", name, r);
-        if (((uintptr_t)t[r]) % (uintptr_t)es)
+        if (((uintptr_t)t[r]) & (uintptr_t)(es - 1))  // element sizes are powers of two
             return fail(ZR_ERR_ALIGN, "%s[%d]=%p is not aligned to %lld bytes", name, r, t[r],
                         (long long)es);
     }
@@ -86,12 +86,24 @@ zr_status check_distinct(const std::vector<Range>& rs, const char* name) {
     return ok();
 }
 
+// xs must already be pairwise disjoint (check_distinct). Sorted by start,
+// their ends then increase too, so the only x that can overlap a range y is
+// the first one ending after y starts: one binary search per y instead of a
+// test against every x (the fragment tables hold up to K * F ranges).
 zr_status check_disjoint(const std::vector<Range>& xs, const char* xn, const std::vector<Range>& ys,
                          const char* yn) {
+    std::vector<size_t> ord;  // the non-empty xs, by start
+    ord.reserve(xs.size());
     for (size_t a = 0; a < xs.size(); ++a)
-        for (size_t b = 0; b < ys.size(); ++b)
-            if (overlaps(xs[a], ys[b]))
-                return fail(ZR_ERR_ALIAS, "%s[%zu] overlaps %s[%zu]", xn, a, yn, b);
+        if (xs[a].lo < xs[a].hi) ord.push_back(a);
+    std::sort(ord.begin(), ord.end(), [&](size_t p, size_t q) { return xs[p].lo < xs[q].lo; });
+    for (size_t b = 0; b < ys.size(); ++b) {
+        const Range& y = ys[b];
+        if (!(y.lo < y.hi)) continue;
+        const auto it = std::partition_point(ord.begin(), ord.end(), [&](size_t a) { return xs[a].hi <= y.lo; });
+        if (it != ord.end() && overlaps(xs[*it], y))
+            return fail(ZR_ERR_ALIAS, "%s[%zu] overlaps %s[%zu]", xn, *it, yn, b);
+    }
     return ok();
 }
 
@@ -365,7 +377,7 @@ zr_status zr_allreduce(int K, const void* const* in, void* const* out, zr_dtype 
             return ok();
         }
         if (!scratch) return fail(ZR_ERR_INVALID, "scratch is NULL (needed when fused == 0)");
-        if (((uintptr_t)scratch) % (uintptr_t)es) return fail(ZR_ERR_ALIGN, "scratch is not aligned");
+        if (((uintptr_t)scratch) & (uintptr_t)(es - 1)) return fail(ZR_ERR_ALIGN, "scratch is not aligned");
         const Range rsc = range_of(scratch, K * C, es);
         for (int r = 0; r < K; ++r)
             if (overlaps(rsc, ri[r]) || overlaps(rsc, ro[r]))
@@ -396,6 +408,7 @@ zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const i
         if (padded_numel == 0) return ok();
         ZR_TRY(check_table(const_cast<const void* const*>(buckets), K, es, "buckets"));
         std::vector<Range> rb(K), rf;
+        rf.reserve((size_t)K * n_frag);
         for (int r = 0; r < K; ++r) rb[r] = range_of(buckets[r], padded_numel, es);
         ZR_TRY(check_distinct(rb, "buckets"));
         for (int r = 0; r < K; ++r)
@@ -403,7 +416,7 @@ zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const i
                 const void* f = frags[(size_t)r * n_frag + p];
                 if (numels[p] == 0) continue;
                 if (!f) return fail(ZR_ERR_INVALID, "fragment %d of rank %d is NULL", p, r);
-                if (((uintptr_t)f) % (uintptr_t)es)
+                if (((uintptr_t)f) & (uintptr_t)(es - 1))
                     return fail(ZR_ERR_ALIGN, "fragment %d of rank %d is not aligned", p, r);
                 rf.push_back(range_of(f, numels[p], es));
             }
@@ -413,6 +426,7 @@ zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const i
         // into pieces of that many, so tile numbers fit the kernel's 32 bits
         const int64_t piece = ((1LL << 28) / K) * (4096 / es);
         std::vector<FragEntry> entries;
+        entries.reserve((size_t)n_frag + 1);
         auto add = [&](const void* const* ptrs, int64_t off, int64_t n) {
             for (int64_t o = 0; o < n; o += piece) {
                 FragEntry f{};
@@ -481,7 +495,7 @@ zr_status make_frags_plan(int K, int n_frag, const void* const* frags, const int
             if (numels[p] == 0) continue;
             const void* f = frags[(size_t)r * n_frag + p];
             if (!f) return fail(ZR_ERR_INVALID, "fragment %d of rank %d is NULL", p, r);
-            if (((uintptr_t)f) % (uintptr_t)ies)
+            if (((uintptr_t)f) & (uintptr_t)(ies - 1))
                 return fail(ZR_ERR_ALIGN, "fragment %d of rank %d is not aligned", p, r);
             rf.push_back(range_of(f, numels[p], ies));
         }

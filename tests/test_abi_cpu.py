@@ -169,6 +169,53 @@ def test_flatten_validation():
     assert call([1, 2, 3], 8, frags=frags) == zr.ZR_ERR_INVALID
 
 
+def test_overlap_checks_on_a_large_fragment_table():
+    # 8 ranks x 500 fragments, laid end to end with every partition in a gap
+    # between two fragments; the plan is validated and built on the host alone.
+    # Partitions that touch their neighbours pass; one element of overlap with
+    # any fragment, deep in the table or at either end, is an alias; an empty
+    # fragment whose address lies inside a partition is ignored.
+    lib = zr.lib()
+    K, F = 8, 500
+    numels = [2 * (1 + (p * 37) % 97) for p in range(F)]  # even: partitions stay 4-byte aligned
+    N = -(-sum(numels) // K) * K + 16
+    C = N // K
+    addrs, cur = [], A
+    outs = []
+    for r in range(K):
+        for p in range(F):
+            addrs.append(cur)
+            cur += numels[p] * 2             # bf16 fragments, back to back
+            if p == 250:                     # a partition (fp32) in the middle of rank r's run
+                outs.append(cur)
+                cur += C * 4
+    nm = (ctypes.c_int64 * F)(*numels)
+
+    def plan(frags, o, numels_arr=nm):
+        fr = (ctypes.c_void_p * (K * F))(*frags)
+        ot = (ctypes.c_void_p * K)(*o)
+        h = ctypes.c_void_p()
+        st = lib.zr_rsf_plan_create(K, F, fr, numels_arr, N, 0, ot, 1, 1, 1, 0, ctypes.byref(h))
+        if st == zr.ZR_OK:
+            assert lib.zr_rsf_plan_destroy(h) == zr.ZR_OK
+        return st
+
+    assert plan(addrs, outs) == zr.ZR_OK
+    for r, delta in ((0, -4), (5, 4), (7, -4), (2, 4)):
+        o = list(outs)
+        o[r] = outs[r] + delta                # 4 bytes into fragment 250 or 251 of rank r
+        assert plan(addrs, o) == zr.ZR_ERR_ALIAS, (r, delta)
+    o = list(outs)
+    o[3] = addrs[3 * F] - 4                   # over rank 2's last fragment and rank 3's first ones
+    assert plan(addrs, o) == zr.ZR_ERR_ALIAS
+    # an empty fragment whose address lies inside partition 2 is not a buffer
+    nm0 = list(numels)
+    nm0[499] = 0
+    fr = list(addrs)
+    fr[2 * F + 499] = outs[2] + 64
+    assert plan(fr, outs, (ctypes.c_int64 * F)(*nm0)) == zr.ZR_OK
+
+
 @pytest.mark.parametrize("entry", ["call", "plan"])
 def test_reduce_scatter_frags_validation(entry):
     # the one-shot call and the plan share their validation; a valid plan is
