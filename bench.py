@@ -760,7 +760,7 @@ def main():
                     help="element indices in the CPU-baseline sample (default: all of bucket 0)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build simulates the K ranks on one GPU; --gpus {args.gpus} is not "
+        print(f"bench.py: the K ranks are simulated on one GPU; --gpus {args.gpus} is not "
               "supported (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
