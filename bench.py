@@ -306,6 +306,7 @@ def bench_zero3(args):
     kernel_ms = e0.elapsed_time(e1) / args.steps
     src = kernel_source_hash(["zr_ag.hip", "zr_device.hpp"])
     traffic = read_traffic("ag_bf16_k8_zero3.counters.txt", src, step_bytes, key="hbm_bytes_per_step")
+    copy = copy_ceiling_gbps()
     return {
         "metric": "all-gather GB/s (shard read + K full writes), K=8, 6.74B-param transformer",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -320,6 +321,8 @@ def bench_zero3(args):
         "roofline": {"bound": "hbm", "kernel": "ag_kernel<bf16,K=8> (162 launches per step)",
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "achieved": round(step_bytes / (kernel_ms * 1e-3) / 1e9, 1),
+                     "copy_ceiling_GBps": copy,
+                     "of_copy_ceiling": round(step_bytes / (kernel_ms * 1e-3) / 1e9 / copy, 4) if copy else None,
                      "frac": round(step_bytes / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "traffic_unit": "bytes per step",
                      "kernel_source_sha256_16": src},
@@ -581,6 +584,7 @@ def bench_allreduce64(args):
     value = step_bytes / (ms_step * 1e-3) / 1e9
     src = kernel_source_hash(["zr_ar.hip", "zr_fold.hpp", "zr_device.hpp"])
     traffic = read_traffic("ar_ring_bf16_k64_allreduce64.counters.txt", src, step_bytes)
+    copy = copy_ceiling_gbps()
     return {
         "metric": "fused all-reduce GB/s (K reads + K writes), K=64, 1e9 bf16 elements",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -594,6 +598,8 @@ def bench_allreduce64(args):
                    "K": K, "N": N, "bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "kernel": "ar_kernel<bf16,K=64,ring>", "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "achieved": round(value, 1),
+                     "copy_ceiling_GBps": copy,
+                     "of_copy_ceiling": round(value / copy, 4) if copy else None,
                      "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": step_bytes,
                      "kernel_source_sha256_16": src},
@@ -654,6 +660,7 @@ def bench_frags_layer(args):
     value = step_bytes / (ms * 1e-3) / 1e9
     src = kernel_source_hash(["zr_rsf.hip", "zr_fold.hpp", "zr_device.hpp"])
     traffic = read_traffic("rsf_ring_bf16_f32_k8_frags_layer.counters.txt", src, step_bytes)
+    copy = copy_ceiling_gbps()
     return {
         "metric": "discrete reduce-scatter+avg+cast GB/s from 7 fragments per rank, K=8",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -668,6 +675,8 @@ def bench_frags_layer(args):
                    "K": K, "N": N, "bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "kernel": "rsf_kernel<bf16,f32,avg,ring>", "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "achieved": round(value, 1),
+                     "copy_ceiling_GBps": copy,
+                     "of_copy_ceiling": round(value / copy, 4) if copy else None,
                      "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel_source_sha256_16": src},
         "cpu_baseline": None,
