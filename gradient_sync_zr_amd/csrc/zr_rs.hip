@@ -10,12 +10,14 @@
 // once, in fp32 or rounded once to bf16 (the single bf16 -> fp32 cast of the
 // ZeRO-3 data flow, section 1, moved into the reduction's only write).
 //
-// Grid: one block per tile, tiles numbered chunk by chunk (all of chunk 0's
-// tiles, then chunk 1's, ...), so the blocks the dispatcher has in flight
-// work on one compact window of the address space; a block finds its chunk
-// j, and with it the holder and every rank pointer, uniformly from the
-// chunks' first tiles. (A persistent grid striding over the tiles ran 7-8%
-// slower: its blocks drift apart over the chunk.) A tile is 4 waves x S
+// Grid: one block per tile, tiles numbered by pairs of chunks (chunks 0
+// and 1, then 2 and 3, ...), consecutive blocks alternating between the
+// pair's two chunks, so the blocks the dispatcher has in flight work on two
+// compact windows of the address space; a block finds its chunk j, and with
+// it the holder and every rank pointer, uniformly from the pairs' first
+// tiles. (Two chunks at a time ran 1-2% faster than one; four or eight ran
+// 2-4% slower. A persistent grid striding over the tiles ran 7-8% slower:
+// its blocks drift apart over the chunk.) A tile is 4 waves x S
 // slices x 256 elements; lane l of a wave owns elements 4l..4l+3 of each of
 // its slices, so each load instruction reads, and each store instruction
 // writes, one contiguous span of whole cache lines. All K ranks' loads of
@@ -32,6 +34,8 @@
 // below N as vectors and the few elements after them one by one. Chunks
 // whose start does not allow quad access fold element by element tile by
 // tile. Positions g >= N are padding and receive +0.
+#include <algorithm>
+
 #include "zr_fold.hpp"
 
 namespace zr {
@@ -46,11 +50,14 @@ struct RsArgs {
     int64_t N, C;
     uint64_t vec_mask;         // bit j: chunk j takes the vector path
     int16_t head[kMaxRanks];   // chunk j's vector tiles start at chunk offset head[j]
-    int64_t tile0[kMaxRanks + 1];  // first tile of chunk j; tile0[K] = all tiles
+    int64_t tile0[kMaxRanks / 2 + 1];  // first tile of chunk pair q; tile0[npairs] = all tiles
+    int64_t ntile[kMaxRanks];          // tiles of chunk j
+    int npairs;                        // ceil(K / 2)
     int K, shift;
     int accumulate;            // 1: out = old + result (gradient accumulation)
     float inv_k, kf;
 };
+static_assert(sizeof(RsArgs) <= 4096, "reduce-scatter arguments exceed 4 KB");
 
 template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
 __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
@@ -63,17 +70,22 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
     const int wave = threadIdx.x >> 6;
 
     // one tile per block; a launch capped below the tile count strides
-    for (int64_t i = blockIdx.x; i < a.tile0[K]; i += gridDim.x) {
-        // the tile's chunk: the last j with tile0[j] <= i (uniform)
-        int j = 0;
-        for (int hi = K; hi - j > 1;) {
-            const int mid = (j + hi) >> 1;
+    for (int64_t i = blockIdx.x; i < a.tile0[a.npairs]; i += gridDim.x) {
+        // the tile's chunk pair: the last q with tile0[q] <= i (uniform);
+        // the pair's two chunks take alternate blocks
+        int q = 0;
+        for (int hi = a.npairs; hi - q > 1;) {
+            const int mid = (q + hi) >> 1;
             if (a.tile0[mid] <= i)
-                j = mid;
+                q = mid;
             else
                 hi = mid;
         }
-        const int64_t t = i - a.tile0[j];
+        const int64_t w = i - a.tile0[q];
+        const bool two = 2 * q + 1 < K;
+        const int j = two ? 2 * q + (int)(w & 1) : 2 * q;
+        const int64_t t = two ? (w >> 1) : w;
+        if (t >= a.ntile[j]) continue;  // the pair's shorter chunk has run out
         const int holder = wrap(j - a.shift + K, K);
         const bool vec = (a.vec_mask >> j) & 1ull;
         const int64_t chunk_base = (int64_t)j * C;
@@ -127,10 +139,10 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
             // vectors (one slice per pass), its other elements one by one
             const int64_t hc = h < C ? h : C;
             const int64_t lim = (valid < hc ? valid : hc) & ~(int64_t)3;  // < 0: all padding
-            for (int64_t q = (int64_t)threadIdx.x * 4; q + 4 <= lim; q += kThreads * 4) {
+            for (int64_t o4 = (int64_t)threadIdx.x * 4; o4 + 4 <= lim; o4 += kThreads * 4) {
                 float acc[1][4];
-                fold_quads<TIn, KS, NT, 1, ORDER, kStatic>(bases, ptr, K, j, chunk_base + q, acc);
-                emit(q, acc, std::integral_constant<int, 1>{});
+                fold_quads<TIn, KS, NT, 1, ORDER, kStatic>(bases, ptr, K, j, chunk_base + o4, acc);
+                emit(o4, acc, std::integral_constant<int, 1>{});
             }
             for (int64_t o = (lim > 0 ? lim : 0) + threadIdx.x; o < hc; o += kThreads) elem(o);
         }
@@ -164,7 +176,7 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
 // One block per tile, up to tuning().max_grid blocks (beyond that they stride).
 template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
 hipError_t launch_t(const RsArgs& a, hipStream_t stream) {
-    const int64_t total = a.tile0[a.K];
+    const int64_t total = a.tile0[a.npairs];
     const int gx = grid_for(total);
     hipLaunchKernelGGL((rs_kernel<TIn, TOut, KS, AVG, ORDER, NT, S>), dim3(gx), dim3(kThreads), 0,
                        stream, a);
@@ -231,15 +243,20 @@ hipError_t launch_typed(RsArgs& a, int avg_mode, int order, hipStream_t s) {
         const int64_t to_block = (int64_t)((kOutBlock - ob % kOutBlock) % kOutBlock / sizeof(TOut));
         a.head[j] = (int16_t)(to_block + ((to_line - to_block) % line + line) % line);
     }
-    // tiles, chunk by chunk: a vector chunk's cover [head, C) (at least one,
-    // which folds the head), another chunk's cover [0, C)
-    int64_t tiles = 0;
+    // tiles of each chunk: a vector chunk's cover [head, C) (at least one,
+    // which folds the head), another chunk's cover [0, C); chunks go in
+    // pairs, a pair's blocks alternating between its two chunks
     for (int j = 0; j < a.K; ++j) {
-        a.tile0[j] = tiles;
         const int64_t h = ((a.vec_mask >> j) & 1ull) ? a.head[j] : 0;
-        tiles += ((a.vec_mask >> j) & 1ull) ? (a.C > h ? (a.C - h + Tl - 1) / Tl : 1) : (a.C + Tl - 1) / Tl;
+        a.ntile[j] = ((a.vec_mask >> j) & 1ull) ? (a.C > h ? (a.C - h + Tl - 1) / Tl : 1) : (a.C + Tl - 1) / Tl;
     }
-    a.tile0[a.K] = tiles;
+    a.npairs = (a.K + 1) / 2;
+    int64_t tiles = 0;
+    for (int q = 0; q < a.npairs; ++q) {
+        a.tile0[q] = tiles;
+        tiles += 2 * q + 1 < a.K ? 2 * std::max(a.ntile[2 * q], a.ntile[2 * q + 1]) : a.ntile[2 * q];
+    }
+    a.tile0[a.npairs] = tiles;
     return pick_avg<TIn, TOut>(a, avg_mode, order, small, s);
 }
 
