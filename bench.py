@@ -72,11 +72,12 @@ def read_traffic(name, src_hash, algorithmic, key="hbm_bytes_per_launch"):
 
 
 def host_cores():
+    """Cores this process may run on (its affinity mask), all of them."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    return max(1, n)
 
 
 def events_ms(pairs):
@@ -113,6 +114,19 @@ def copy_ceiling_gbps(gib=4, reps=10):
     return round(2 * nbytes / (sum(ms) / len(ms) * 1e-3) / 1e9, 1)
 
 
+def mix_ceiling(reps=10):
+    """The test kit's matched-mix stream (tests/kit/mix_probe.py: the
+    reduce-scatter's loads and stores at one bucket's shape, no arithmetic),
+    measured now: {"mix", "reads", "writes"} rates, or None when the kit is
+    not built."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("mix_probe", os.path.join(ROOT, "tests", "kit",
+                                                                            "mix_probe.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.measure(reps=reps)
+
+
 # ----------------------------------------------------------------- zero2
 def bench_zero2(args, accumulate=False):
     import numpy as np
@@ -143,15 +157,29 @@ def bench_zero2(args, accumulate=False):
     for _ in range(args.warmup):
         sync.step(micro_step=micro)
     torch.cuda.synchronize()
-    timing = []
+    # the timed steps: nothing but the sync itself; one event per step boundary
+    # on the producer stream (each step ends with the producer waiting for the
+    # reduction stream) gives every step's device time for the median and min
+    prod = torch.cuda.current_stream()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        sync.step(timing=timing, micro_step=micro)
+    marks[0].record(prod)
+    for i in range(args.steps):
+        sync.step(micro_step=micro)
+        marks[i + 1].record(prod)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     step_bytes = sum(n * per_elem for _, n in buckets)
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    # a separate instrumented pass of as many steps: an event pair around each
+    # launch on the reduction stream, after the stream has waited for the
+    # producer, so each pair brackets the kernel alone
+    timing = []
+    for _ in range(args.steps):
+        sync.step(timing=timing, micro_step=micro)
+    torch.cuda.synchronize()
     launch_ms = events_ms(timing)
     launch_bytes = [n * per_elem for _, n in buckets] * args.steps
     achieved = sum(launch_bytes) / (sum(launch_ms) * 1e-3) / 1e9
@@ -160,15 +188,15 @@ def bench_zero2(args, accumulate=False):
     full = sorted(ms for ms, b in zip(launch_ms, launch_bytes) if b == max(launch_bytes))
     full_med, full_min = full[len(full) // 2], full[0]
     bytes_per_launch = sum(launch_bytes) / len(launch_bytes)
-    # each bucket's rate over the timed steps (its launches are every nb-th)
+    # each bucket's rate over the instrumented steps (its launches are every nb-th)
     nb = len(buckets)
     per_bucket = [round(launch_bytes[b] * (len(launch_ms) // nb) / (sum(launch_ms[b::nb]) * 1e-3) / 1e9, 1)
                   for b in range(nb)]
     src = kernel_source_hash(["zr_rs.hip", "zr_fold.hpp", "zr_device.hpp"])
     traffic = read_traffic("rs_ring_bf16_f32_k8_zero2" + ("_accum" if accumulate else "") +
                            ".counters.txt", src, bytes_per_launch)
-    print(f"# zero2: {ms_step:.3f} ms/step, kernel avg {avg_launch_ms:.3f} ms", file=sys.stderr,
-          flush=True)
+    print(f"# zero2: {ms_step:.3f} ms/step (median {step_ms[len(step_ms) // 2]:.3f}, min "
+          f"{step_ms[0]:.3f}), kernel avg {avg_launch_ms:.3f} ms", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline and not accumulate:
@@ -176,7 +204,9 @@ def bench_zero2(args, accumulate=False):
         if cpu and cpu.get("value"):
             cpu["gpu_over_oracle"] = round(value / cpu["value"], 1)
     sync.close()
+    del sync, grads, parts
     copy = copy_ceiling_gbps()
+    mix = mix_ceiling() if not accumulate else None
     if accumulate:
         metric = ("reduce-scatter+avg+accumulate GB/s (gradient-accumulation micro-step), K=8, "
                   "2.38B-elem bf16 grads")
@@ -189,6 +219,9 @@ def bench_zero2(args, accumulate=False):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic: seeded counter-based generator on the device, bf16 ~N(0,1e-3)",
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "step_ms_median": round(step_ms[len(step_ms) // 2], 4),
+        "step_ms_min": round(step_ms[0], 4),
+        "value_at_median_step_GBps": round(step_bytes / (step_ms[len(step_ms) // 2] * 1e-3) / 1e9, 1),
         "reads_only_GBps": round(K * N * 2 / (ms_step * 1e-3) / 1e9, 1),
         "config": {"workload": "zero2_grad_sync: K=8 simulated ranks in one HBM, "
                                "2,376,274,560 bf16 grad elements per rank, 5 buckets of "
@@ -208,6 +241,13 @@ def bench_zero2(args, accumulate=False):
                      "per_bucket_GBps": per_bucket,
                      "copy_ceiling_GBps": copy,
                      "of_copy_ceiling": round(achieved / copy, 4) if copy else None,
+                     "mix_ceiling_GBps": mix["mix"]["GBps"] if mix else None,
+                     "of_mix_ceiling": round(achieved / mix["mix"]["GBps"], 4) if mix else None,
+                     "mix_reads_only_GBps": mix["reads"]["GBps"] if mix else None,
+                     "mix_writes_only_GBps": mix["writes"]["GBps"] if mix else None,
+                     "timing": "per-launch event pairs from a separate instrumented pass of "
+                               "the same number of steps; value and the step median/min come "
+                               "from the uninstrumented steps",
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
                      "kernel_source_sha256_16": src},
         "cpu_baseline": cpu,
@@ -216,8 +256,9 @@ def bench_zero2(args, accumulate=False):
 
 def cpu_baseline_zero2(grads, parts, first_bucket, K, args):
     """The oracle on bucket 0 of the same resident inputs (copied to the host,
-    not timed), split over host threads by chunk offset; also checks the GPU
-    partitions of that bucket bit for bit."""
+    not timed), split by chunk offset over every host core this process may
+    use; then the same bucket on one core. Also checks the GPU partitions of
+    that bucket bit for bit."""
     import numpy as np
     import torch
 
@@ -226,7 +267,7 @@ def cpu_baseline_zero2(grads, parts, first_bucket, K, args):
     C = -(-n // K)
     M = min(C, args.cpu_sample_elems // K) if args.cpu_sample_elems else C
     # the sample: offsets [0, M) of every chunk of bucket 0, as its own
-    # reduce-scatter problem with chunk size M
+    # reduce-scatter problem with chunk size M (M = C: the whole bucket)
     xs = []
     for r in range(K):
         rows = [grads[r][start + j * C:start + j * C + M].view(torch.int16).cpu().numpy()
@@ -247,20 +288,22 @@ def cpu_baseline_zero2(grads, parts, first_bucket, K, args):
     for t in th:
         t.join()
     dt = time.perf_counter() - t0
-    gbs = K * M * (2 * K + 4) / dt / 1e9
-    # one host core on the first 1/16 of the same offsets
-    M1 = max(1, M // 16)
-    t1 = time.perf_counter()
-    oracle.reduce_scatter(xs, K * M, np.float32, shift=1, average=True, o_range=(0, M1), out=outs)
-    gbs1 = K * M1 * (2 * K + 4) / (time.perf_counter() - t1) / 1e9
+    model_bytes = K * M * (2 * K + 4)
+    gbs = model_bytes / dt / 1e9
     exact = all(np.array_equal(parts[q][:M].cpu().numpy().view(np.uint32), outs[q].view(np.uint32))
                 for q in range(K))
+    # one core on the same sample, whole
+    t1 = time.perf_counter()
+    oracle.reduce_scatter(xs, K * M, np.float32, shift=1, average=True, o_range=(0, M), out=outs)
+    dt1 = time.perf_counter() - t1
+    sample = ("all of bucket 0" if M == C else f"offsets [0,{M}) of each of the {K} chunks of bucket 0")
     return {"value": round(gbs, 2), "unit": "GB/s", "cores": T, "kind": "oracle",
-            "seconds": round(dt, 3), "single_core_GBps": round(gbs1, 2),
-            "single_core_sample": f"offsets [0,{M1}) of each chunk of bucket 0",
-            "sample": f"offsets [0,{M}) of each of the 8 chunks of bucket 0 "
-                      f"({K * M} element indices, {K * M * (2 * K + 4) / 1e9:.2f} GB under "
-                      f"the same byte model); GPU partitions bit-exact on it: {exact}"}
+            "host_cores": T, "threads_used": T, "seconds": round(dt, 3),
+            "single_core_GBps": round(model_bytes / dt1 / 1e9, 2),
+            "single_core_seconds": round(dt1, 3),
+            "single_core_sample": sample,
+            "sample": f"{sample} ({K * M} element indices, {model_bytes / 1e9:.2f} GB under the same "
+                      f"byte model); GPU partitions bit-exact on it: {exact}"}
 
 
 # ----------------------------------------------------------------- zero3

@@ -81,20 +81,89 @@ extern "C" int tk_read(const void* src, void* sink, long long bytes, int blocks,
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
-// tk_xcd: every block of a one-block-per-tile launch copies one 4 KiB tile
-// (so blocks retire at varying times, as in the library's kernels) and
-// records the XCD it ran on, read from the XCC_ID hardware register (bits
-// 3:0), in xcd[blockIdx.x]. src and dst hold blocks * 4 KiB.
-__global__ void __launch_bounds__(256) tk_xcd_kernel(const uint4* __restrict__ src,
-                                                     uint4* __restrict__ dst, int* __restrict__ xcd) {
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    dst[i] = src[i];
-    if (threadIdx.x == 0) xcd[blockIdx.x] = (int)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15);
+// tk_mix: the reduce-scatter's memory access pattern with no arithmetic, the
+// practical ceiling of a stream with its read:write mix. K = 8 bf16 input
+// streams of n = 8 * C elements and 8 fp32 output streams of C elements; C is a
+// multiple of 4096, so every tile is whole, starts on a 128-byte line of every
+// input and writes an aligned 16 KiB block of its output. Tiles are numbered
+// as the reduce-scatter numbers them: by pairs of chunks, consecutive blocks
+// alternating between the pair's two chunks, one block per tile. A tile is
+// 4 waves x 4 slices x 256 elements; lane l owns elements 4l..4l+3 of each
+// slice and loads them from every input with one 8-byte non-temporal load
+// (all 32 loads issued before the first use), then writes one 16-byte
+// non-temporal store per slice to out_j. The stored words are the XOR of the
+// loaded ones, so no load can be removed and no floating-point add is made.
+//   mode 0: loads and stores (the reduce-scatter's 16 B read : 4 B written)
+//   mode 1: loads only (one 16-byte word per tile, written only when the
+//           XOR of the tile's data hits a fixed value, keeps the loads live)
+//   mode 2: stores only (the same 16 KiB output blocks, no loads)
+typedef unsigned int tk_u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int tk_u32x4 __attribute__((ext_vector_type(4)));
+
+struct TkMixArgs {
+    const tk_u32x2* in[8];  // 8 inputs, n bf16 each (4 per 8-byte word)
+    tk_u32x4* out[8];       // 8 outputs, C fp32 each (4 per 16-byte word)
+    tk_u32x4* sink;         // mode 1: one word per tile
+    long long C;            // chunk size (elements), a multiple of 4096
+    long long tpc;          // tiles per chunk, C / 4096
+    int mode;
+};
+
+__global__ void __launch_bounds__(256) tk_mix_kernel(const TkMixArgs a) {
+    const long long i = blockIdx.x;
+    const long long per_pair = 2 * a.tpc;
+    const int q = (int)(i / per_pair);
+    const long long w = i - q * per_pair;
+    const int j = 2 * q + (int)(w & 1);
+    const long long t = w >> 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const long long o0 = t * 4096 + wave * 1024 + lane * 4;  // element offset in the chunk
+    const long long g0 = (long long)j * a.C + o0;              // element index in the inputs
+    tk_u32x4* out = a.out[j];
+    if (a.mode == 2) {
+        const tk_u32x4 v = {(unsigned)o0, (unsigned)j, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(v, out + (o0 + 256 * k) / 4);
+        return;
+    }
+    tk_u32x2 v[4][8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int h = 0; h < 8; ++h) v[k][h] = __builtin_nontemporal_load(a.in[h] + (g0 + 256 * k) / 4);
+    tk_u32x4 x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        tk_u32x2 y = v[k][0];
+#pragma unroll
+        for (int h = 1; h < 8; ++h) y ^= v[k][h];
+        x[k] = tk_u32x4{y.x, y.y, y.x ^ y.y, y.y + 1u};
+    }
+    if (a.mode == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(x[k], out + (o0 + 256 * k) / 4);
+        return;
+    }
+    const tk_u32x4 z = x[0] ^ x[1] ^ x[2] ^ x[3];
+    if (z.x == 0x9E3779B9u && z.y == 0x7F4A7C15u) a.sink[i] = z;
 }
 
-extern "C" int tk_xcd(const void* src, void* dst, void* xcd, int blocks, void* stream) {
-    if (blocks < 1 || !src || !dst || !xcd) return 1;
-    hipLaunchKernelGGL(tk_xcd_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
-                       (const uint4*)src, (uint4*)dst, (int*)xcd);
+extern "C" int tk_mix(const void* const* in, void* const* out, void* sink, long long C, int mode,
+                      void* stream) {
+    if (!in || !out || C <= 0 || (C % 4096) != 0 || mode < 0 || mode > 2) return 1;
+    if (mode == 1 && !sink) return 1;
+    TkMixArgs a;
+    for (int r = 0; r < 8; ++r) {
+        if (!in[r] || !out[r]) return 1;
+        a.in[r] = (const tk_u32x2*)in[r];
+        a.out[r] = (tk_u32x4*)out[r];
+    }
+    a.sink = (tk_u32x4*)sink;
+    a.C = C;
+    a.tpc = C / 4096;
+    a.mode = mode;
+    const long long blocks = 8 * a.tpc;
+    if (blocks > (1LL << 30)) return 1;
+    hipLaunchKernelGGL(tk_mix_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
