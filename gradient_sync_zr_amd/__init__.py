@@ -20,7 +20,11 @@ streams default to torch's current stream):
   and ``.launch()`` repeats it.
 * ``zr_all_gather(shards, fulls, segs, chunk_shift=0)`` and
   ``zr_allreduce(inputs, outputs, N, average=False, fused=True)``.
-* ``zr_flatten_bucket(frags, numels, buckets, padded_numel)``.
+* ``zr_flatten_bucket(frags, numels, buckets, padded_numel)``; ``FlatPlan``
+  builds it once.
+* ``zr_workspace_bytes(K, n)``: the device workspace (a uint8 tensor, or an
+  ``(address, bytes)`` pair, passed as ``workspace=``) that lets a call with
+  ``n`` fragments or segments go out as one launch.
 * ``Sched``: ping-pong bucket buffers with per-buffer completion events
   (``acquire``, ``submit_rs``, ``flush``).
 * ``Prefetcher``: ZeRO-3 fetch and prefetch of full parameters into per-rank
@@ -47,25 +51,28 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # with the same ABI); by default the in-tree build is used.
 LIB_PATH = os.environ.get("ZR_LIBRARY") or os.path.join(_HERE, "libzr.so")
 
-ZR_OK, ZR_ERR_INVALID, ZR_ERR_ALIGN, ZR_ERR_ALIAS, ZR_ERR_UNSUPPORTED, ZR_ERR_HIP, ZR_ERR_NOMEM = range(7)
+(ZR_OK, ZR_ERR_INVALID, ZR_ERR_ALIGN, ZR_ERR_ALIAS, ZR_ERR_UNSUPPORTED, ZR_ERR_WORKSPACE, ZR_ERR_HIP,
+ ZR_ERR_NOMEM) = range(8)
 ZR_BF16, ZR_FP32 = 0, 1
 ZR_ORDER_RING, ZR_ORDER_FREE, ZR_ORDER_RING_WIRE = 0, 1, 2
 ZR_AVERAGE, ZR_ACCUMULATE = 1, 2
 ZR_MAX_RANKS, ZR_MAX_ELEMS = 64, 1 << 40
 STATUS_NAMES = {0: "ZR_OK", 1: "ZR_ERR_INVALID", 2: "ZR_ERR_ALIGN", 3: "ZR_ERR_ALIAS",
-                4: "ZR_ERR_UNSUPPORTED", 5: "ZR_ERR_HIP", 6: "ZR_ERR_NOMEM"}
+                4: "ZR_ERR_UNSUPPORTED", 5: "ZR_ERR_WORKSPACE", 6: "ZR_ERR_HIP", 7: "ZR_ERR_NOMEM"}
 
 COST_EXPORTS = ("zr_cost_ring_allreduce", "zr_cost_ring_reduce_scatter", "zr_cost_tree_allreduce",
                 "zr_cost_naive_allreduce", "zr_cost_pipelined_broadcast",
                 "zr_cost_best_broadcast_segments", "zr_cost_ring_tree_crossover",
                 "zr_cost_ring_naive_crossover", "zr_cost_dp_speedup")
-RSF_PLAN_EXPORTS = ("zr_rsf_plan_create", "zr_rsf_plan_launch", "zr_rsf_plan_destroy")
+RSF_PLAN_EXPORTS = ("zr_rsf_plan_create", "zr_rsf_plan_launch", "zr_rsf_plan_info", "zr_rsf_plan_destroy")
+FLAT_PLAN_EXPORTS = ("zr_flatten_plan_create", "zr_flatten_plan_launch", "zr_flatten_plan_info",
+                     "zr_flatten_plan_destroy")
 PF_EXPORTS = ("zr_pf_create", "zr_pf_fetch", "zr_pf_release", "zr_pf_full", "zr_pf_get_stats",
               "zr_pf_destroy", "zr_pf_plan")
-EXPORTS = ("zr_last_error", "zr_version", "zr_flatten_bucket", "zr_reduce_scatter_avg",
+EXPORTS = ("zr_last_error", "zr_version", "zr_workspace_bytes", "zr_flatten_bucket", "zr_reduce_scatter_avg",
            "zr_reduce_scatter_frags", "zr_all_gather", "zr_allreduce", "zr_plan_buckets", "zr_sched_create",
            "zr_sched_acquire", "zr_sched_submit_rs", "zr_sched_flush",
-           "zr_sched_destroy") + COST_EXPORTS + PF_EXPORTS + RSF_PLAN_EXPORTS
+           "zr_sched_destroy") + COST_EXPORTS + PF_EXPORTS + RSF_PLAN_EXPORTS + FLAT_PLAN_EXPORTS
 
 
 class ZrError(RuntimeError):
@@ -104,7 +111,7 @@ class zr_pf_stats(ctypes.Structure):
 
 
 _lib = None
-_i32, _i64, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+_i32, _i64, _vp, _sz = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 _PP = ctypes.POINTER(ctypes.c_void_p)
 
 
@@ -118,11 +125,14 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.zr_last_error.restype = ctypes.c_char_p
         L.zr_version.restype = ctypes.c_int
-        L.zr_flatten_bucket.argtypes = [_i32, _i32, _PP, ctypes.POINTER(_i64), _PP, _i64, _i32, _vp]
+        L.zr_workspace_bytes.argtypes = [_i32, _i32]
+        L.zr_workspace_bytes.restype = _sz
+        L.zr_flatten_bucket.argtypes = [_i32, _i32, _PP, ctypes.POINTER(_i64), _PP, _i64, _i32, _vp, _sz, _vp]
         L.zr_reduce_scatter_avg.argtypes = [_i32, _PP, _i32, _i64, _PP, _i32, _i32, _i32, _i32, _vp]
-        L.zr_all_gather.argtypes = [_i32, _PP, _PP, _i32, ctypes.POINTER(zr_seg), _i32, _i32, _vp]
+        L.zr_all_gather.argtypes = [_i32, _PP, _PP, _i32, ctypes.POINTER(zr_seg), _i32, _i32, _vp, _sz,
+                                    _vp]
         L.zr_reduce_scatter_frags.argtypes = [_i32, _i32, _PP, ctypes.POINTER(_i64), _i64, _i32, _PP,
-                                              _i32, _i32, _i32, _i32, _vp]
+                                              _i32, _i32, _i32, _i32, _vp, _sz, _vp]
         L.zr_allreduce.argtypes = [_i32, _PP, _PP, _i32, _i64, _i32, _i32, _i32, _vp, _vp]
         L.zr_plan_buckets.argtypes = [_i32, ctypes.POINTER(_i64), _i64, ctypes.POINTER(ctypes.c_int32),
                                       ctypes.POINTER(ctypes.c_int32)]
@@ -133,9 +143,15 @@ def lib() -> ctypes.CDLL:
         L.zr_sched_flush.argtypes = [_vp, _vp]
         L.zr_sched_destroy.argtypes = [_vp]
         L.zr_rsf_plan_create.argtypes = [_i32, _i32, _PP, ctypes.POINTER(_i64), _i64, _i32, _PP, _i32,
-                                         _i32, _i32, _i32, ctypes.POINTER(_vp)]
+                                         _i32, _i32, _i32, _vp, _sz, ctypes.POINTER(_vp)]
         L.zr_rsf_plan_launch.argtypes = [_vp, _vp]
+        L.zr_rsf_plan_info.argtypes = [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_sz)]
         L.zr_rsf_plan_destroy.argtypes = [_vp]
+        L.zr_flatten_plan_create.argtypes = [_i32, _i32, _PP, ctypes.POINTER(_i64), _PP, _i64, _i32, _vp,
+                                             _sz, ctypes.POINTER(_vp)]
+        L.zr_flatten_plan_launch.argtypes = [_vp, _vp]
+        L.zr_flatten_plan_info.argtypes = [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_sz)]
+        L.zr_flatten_plan_destroy.argtypes = [_vp]
         _cfgp = ctypes.POINTER(zr_pf_config)
         L.zr_pf_create.argtypes = [_cfgp, ctypes.POINTER(_vp)]
         L.zr_pf_fetch.argtypes = [_vp, _i32]
@@ -144,7 +160,7 @@ def lib() -> ctypes.CDLL:
         L.zr_pf_get_stats.argtypes = [_vp, ctypes.POINTER(zr_pf_stats)]
         L.zr_pf_destroy.argtypes = [_vp]
         L.zr_pf_plan.argtypes = [_cfgp, _i32, ctypes.POINTER(zr_pf_stats)]
-        for f in EXPORTS[2:]:
+        for f in EXPORTS[3:]:
             getattr(L, f).restype = ctypes.c_int
         _d = ctypes.c_double
         for f in ("zr_cost_ring_allreduce", "zr_cost_ring_reduce_scatter",
@@ -215,6 +231,15 @@ def _dtype(x) -> int:
     raise TypeError(f"unsupported dtype {dt}: bfloat16 or float32")
 
 
+def _workspace(ws):
+    """(device address, bytes) of a workspace: None, a tensor, or a pair."""
+    if ws is None:
+        return None, 0
+    if isinstance(ws, tuple):
+        return ws[0], ws[1]
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
 def _stream(stream) -> int:
     """hipStream_t of a torch stream (None = torch's current stream)."""
     if isinstance(stream, int):
@@ -234,8 +259,12 @@ def zr_last_error() -> str:
     return lib().zr_last_error().decode(errors="replace")
 
 
+def zr_workspace_bytes(K: int, n: int) -> int:
+    return lib().zr_workspace_bytes(K, n)
+
+
 def zr_flatten_bucket(frags: Sequence[Sequence], numels: Sequence[int], buckets: Sequence,
-                      padded_numel: int, dtype=None, stream=None) -> None:
+                      padded_numel: int, dtype=None, stream=None, workspace=None) -> None:
     """frags[r][p] = fragment p of rank r; buckets[r] = rank r's flat bucket."""
     K = len(buckets)
     F = len(numels)
@@ -244,8 +273,48 @@ def zr_flatten_bucket(frags: Sequence[Sequence], numels: Sequence[int], buckets:
         raise ValueError("frags must be K lists of len(numels) tensors")
     dt = _dtype(dtype if dtype is not None else buckets[0])
     nums = _int64s(numels)
-    _check(lib().zr_flatten_bucket(K, F, _table(flat), nums, _table(buckets), padded_numel, dt,
+    ws, wsb = _workspace(workspace)
+    _check(lib().zr_flatten_bucket(K, F, _table(flat), nums, _table(buckets), padded_numel, dt, ws, wsb,
                                    _stream(stream)))
+
+
+class FlatPlan:
+    """zr_flatten_plan_*: a bucket flatten validated and built once (its table
+    staged in `workspace` when it needs one); launch() enqueues it."""
+
+    def __init__(self, frags: Sequence[Sequence], numels: Sequence[int], buckets: Sequence,
+                 padded_numel: int, dtype=None, workspace=None):
+        K = len(buckets)
+        F = len(numels)
+        flat = [f for row in frags for f in row]
+        if len(flat) != K * F:
+            raise ValueError("frags must be K lists of len(numels) tensors")
+        dt = _dtype(dtype if dtype is not None else buckets[0])
+        ws, wsb = _workspace(workspace)
+        h = ctypes.c_void_p()
+        _check(lib().zr_flatten_plan_create(K, F, _table(flat), _int64s(numels), _table(buckets),
+                                            padded_numel, dt, ws, wsb, ctypes.byref(h)))
+        self._h = h
+        self.workspace = workspace  # used by every launch
+
+    def launch(self, stream=None) -> None:
+        _check(lib().zr_flatten_plan_launch(self._h, _stream(stream)))
+
+    def info(self) -> dict:
+        n, b = ctypes.c_int(0), ctypes.c_size_t(0)
+        _check(lib().zr_flatten_plan_info(self._h, ctypes.byref(n), ctypes.byref(b)))
+        return {"launches": n.value, "table_bytes": b.value}
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().zr_flatten_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def _flags(average: bool, accumulate: bool) -> int:
@@ -266,7 +335,7 @@ def zr_reduce_scatter_avg(inputs: Sequence, N: int, outputs: Sequence, chunk_shi
 def zr_reduce_scatter_frags(frags: Sequence[Sequence], numels: Sequence[int], N: int,
                             outputs: Sequence, chunk_shift: int = 1, average: bool = True,
                             order: int = ZR_ORDER_RING, in_dtype=None, out_dtype=None,
-                            stream=None, accumulate: bool = False) -> None:
+                            stream=None, accumulate: bool = False, workspace=None) -> None:
     """frags[r][p] = fragment p of rank r (same numels on every rank)."""
     K = len(outputs)
     F = len(numels)
@@ -276,9 +345,10 @@ def zr_reduce_scatter_frags(frags: Sequence[Sequence], numels: Sequence[int], N:
     in_dt = _dtype(in_dtype if in_dtype is not None else flat[0])
     out_dt = _dtype(out_dtype if out_dtype is not None else outputs[0])
     nums = _int64s(numels)
+    ws, wsb = _workspace(workspace)
     _check(lib().zr_reduce_scatter_frags(K, F, _table(flat), nums, N, in_dt, _table(outputs),
                                          out_dt, chunk_shift, _flags(average, accumulate), order,
-                                         _stream(stream)))
+                                         ws, wsb, _stream(stream)))
 
 
 class RsfPlan:
@@ -287,7 +357,7 @@ class RsfPlan:
 
     def __init__(self, frags: Sequence[Sequence], numels: Sequence[int], N: int, outputs: Sequence,
                  chunk_shift: int = 1, average: bool = True, order: int = ZR_ORDER_RING,
-                 in_dtype=None, out_dtype=None, accumulate: bool = False):
+                 in_dtype=None, out_dtype=None, accumulate: bool = False, workspace=None):
         K = len(outputs)
         F = len(numels)
         flat = [f for row in frags for f in row]
@@ -295,14 +365,22 @@ class RsfPlan:
             raise ValueError("frags must be K lists of len(numels) tensors")
         in_dt = _dtype(in_dtype if in_dtype is not None else flat[0])
         out_dt = _dtype(out_dtype if out_dtype is not None else outputs[0])
+        ws, wsb = _workspace(workspace)
         h = ctypes.c_void_p()
         _check(lib().zr_rsf_plan_create(K, F, _table(flat), _int64s(numels), N, in_dt,
                                         _table(outputs), out_dt, chunk_shift,
-                                        _flags(average, accumulate), order, ctypes.byref(h)))
+                                        _flags(average, accumulate), order, ws, wsb,
+                                        ctypes.byref(h)))
         self._h = h
+        self.workspace = workspace  # used by every launch
 
     def launch(self, stream=None) -> None:
         _check(lib().zr_rsf_plan_launch(self._h, _stream(stream)))
+
+    def info(self) -> dict:
+        n, b = ctypes.c_int(0), ctypes.c_size_t(0)
+        _check(lib().zr_rsf_plan_info(self._h, ctypes.byref(n), ctypes.byref(b)))
+        return {"launches": n.value, "table_bytes": b.value}
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:
@@ -317,13 +395,14 @@ class RsfPlan:
 
 
 def zr_all_gather(shards: Sequence, fulls: Sequence, segs: Sequence, chunk_shift: int = 0,
-                  dtype=None, stream=None) -> None:
+                  dtype=None, stream=None, workspace=None) -> None:
     """segs: (shard_off, full_off, numel) triples."""
     K = len(shards)
     dt = _dtype(dtype if dtype is not None else shards[0])
     arr = (zr_seg * max(1, len(segs)))(*[zr_seg(*s) for s in segs])
+    ws, wsb = _workspace(workspace)
     _check(lib().zr_all_gather(K, _table(shards), _table(fulls), dt, arr, len(segs), chunk_shift,
-                               _stream(stream)))
+                               ws, wsb, _stream(stream)))
 
 
 def zr_allreduce(inputs: Sequence, outputs: Sequence, N: int, average: bool = False,

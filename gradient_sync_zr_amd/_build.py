@@ -6,9 +6,15 @@ correctly rounded fp32 division, and packed-fp32 instructions disabled.
 Objects go to _build/ at the repository root; the library lands next to this
 file so that tests, the smoke check and the benchmark load it from the tree.
 
-The build fails if any kernel needs private (scratch) memory: every kernel
-here streams HBM from registers, and a scratch frame means the compiler spilled
-or copied the kernel-argument block to memory, which costs bandwidth silently.
+The build fails if any kernel touches private (scratch) memory: every kernel
+here streams HBM from registers, and a scratch access means the compiler
+spilled registers or copied the kernel-argument block to memory, which costs
+bandwidth silently. The check reads each kernel's machine code (kept from the
+same compile) for scratch loads and stores, and the resource remarks for VGPR
+spills. A kernel may still reserve a small frame that no instruction uses:
+the compiler keeps one when it parks scalar registers in vector-register
+lanes (generic-K variants under high scalar pressure); that costs nothing and
+is allowed.
 """
 import concurrent.futures as cf
 import os
@@ -32,12 +38,13 @@ SOURCES = ["zr_rs.hip", "zr_rsf.hip", "zr_ar.hip", "zr_ag.hip", "zr_flatten.hip"
            "zr_prefetch.cpp", "zr_cost.cpp"]
 
 
-_REMARK = re.compile(r"remark:\s+(Function Name: (\S+)|ScratchSize \[bytes/lane\]: (\d+))")
+_REMARK = re.compile(r"remark:\s+(Function Name: (\S+)|VGPRs Spill: (\d+))")
+_SCRATCH_OP = re.compile(r"^\s+(scratch_|buffer_)(load|store)", re.M)
 
 
-def scratch_kernels(remarks: str):
-    """(kernel, bytes per lane) for every kernel the resource-usage remarks
-    report with a nonzero scratch size."""
+def spilling_kernels(remarks: str):
+    """(kernel, VGPRs spilled) for every kernel the resource-usage remarks
+    report with VGPR spills."""
     bad, name = [], None
     for m in _REMARK.finditer(remarks):
         if m.group(2):
@@ -47,20 +54,48 @@ def scratch_kernels(remarks: str):
     return bad
 
 
+def scratch_access_kernels(asm: str):
+    """Kernels whose machine code (the device assembly of the compile) holds a
+    scratch load or store."""
+    bad = []
+    for m in re.finditer(r"^(\S+):\s*(?:;.*)?$", asm, re.M):
+        name = m.group(1)
+        if name.startswith("."):
+            continue
+        end = asm.find(".Lfunc_end", m.end())
+        if end < 0:
+            continue
+        if _SCRATCH_OP.search(asm, m.end(), end):
+            bad.append(name)
+    return bad
+
+
 def _compile(src, verbose):
-    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+    stem = os.path.splitext(src)[0]
+    out = os.path.join(OBJ, stem + ".o")
     cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", out]
     if src.endswith(".hip"):
-        cmd.append("-Rpass-analysis=kernel-resource-usage")
+        cmd += ["-Rpass-analysis=kernel-resource-usage", "-save-temps=obj"]
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=OBJ)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-    bad = scratch_kernels(r.stderr)
-    if bad:
-        listing = "\n".join(f"  {k}: {b} bytes/lane" for k, b in bad)
-        raise RuntimeError(f"{src}: kernels with a scratch frame:\n{listing}")
+    if src.endswith(".hip"):
+        bad = spilling_kernels(r.stderr)
+        if bad:
+            listing = "\n".join(f"  {k}: {b} VGPRs spilled" for k, b in bad)
+            raise RuntimeError(f"{src}: kernels that spill VGPRs:\n{listing}")
+        asm_path = os.path.join(OBJ, f"{stem}-hip-amdgcn-amd-amdhsa-{ARCH}.s")
+        with open(asm_path) as fh:
+            bad = scratch_access_kernels(fh.read())
+        if bad:
+            raise RuntimeError(f"{src}: kernels that access scratch memory:\n  " + "\n  ".join(bad))
+        # the other temporaries are not needed
+        for f in os.listdir(OBJ):
+            if (f.startswith(stem + "-") or f.startswith(stem + ".hip-")) and \
+                    f != os.path.basename(asm_path):
+                os.remove(os.path.join(OBJ, f))
     return out
 
 

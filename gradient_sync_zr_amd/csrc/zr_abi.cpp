@@ -125,7 +125,47 @@ zr_status check_sizes(const int64_t* numels, int n, int64_t* total) {
         if (st_ != ZR_OK) return st_;      \
     } while (0)
 
+// A workspace argument: NULL (no staging), or an 8-byte-aligned device
+// buffer of ws_bytes bytes.
+zr_status check_workspace(const void* ws, size_t ws_bytes) {
+    if (!ws) return ok();
+    if (((uintptr_t)ws) & 7) return fail(ZR_ERR_ALIGN, "workspace %p is not 8-byte aligned", ws);
+    if (ws_bytes == 0) return fail(ZR_ERR_WORKSPACE, "workspace of 0 bytes");
+    return ok();
+}
+
+// A staged table of `need` bytes must fit the workspace and must not overlap
+// any buffer the call reads or writes.
+zr_status check_staging(const void* ws, size_t ws_bytes, size_t need, const std::vector<Range>& a,
+                        const char* an, const std::vector<Range>& b, const char* bn) {
+    if (need > ws_bytes)
+        return fail(ZR_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu-byte table", ws_bytes,
+                    need);
+    const Range w{(uintptr_t)ws, (uintptr_t)ws + need};
+    for (size_t i = 0; i < a.size(); ++i)
+        if (overlaps(w, a[i])) return fail(ZR_ERR_ALIAS, "workspace overlaps %s[%zu]", an, i);
+    for (size_t i = 0; i < b.size(); ++i)
+        if (overlaps(w, b[i])) return fail(ZR_ERR_ALIAS, "workspace overlaps %s[%zu]", bn, i);
+    return ok();
+}
+
+// Whether work enqueued on `s` would be recorded into a graph. A table staged
+// by an asynchronous copy from a host buffer must not be recorded (a replay
+// would read the buffer after the call freed it), so such calls go out as
+// argument launches instead. A failing query counts as capturing.
+bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) return true;
+    return st != hipStreamCaptureStatusNone;
+}
+
 }  // namespace
+
+hipError_t stage_table(void* ws, const void* image, size_t bytes, hipStream_t stream, bool stream_order) {
+    if (bytes == 0) return hipSuccess;
+    if (stream_order) return hipMemcpyAsync(ws, image, bytes, hipMemcpyHostToDevice, stream);
+    return hipMemcpy(ws, image, bytes, hipMemcpyHostToDevice);
+}
 
 zr_status set_error(zr_status st, const char* msg) {
     g_err = msg ? msg : "";
@@ -329,12 +369,42 @@ zr_status zr_reduce_scatter_avg(int K, const void* const* in, zr_dtype in_dt, in
 }
 
 zr_status zr_all_gather(int K, const void* const* shards, void* const* fulls, zr_dtype dt,
-                        const zr_seg* segs, int n_segs, int chunk_shift, void* stream) {
+                        const zr_seg* segs, int n_segs, int chunk_shift, void* workspace,
+                        size_t ws_bytes, void* stream) {
     return zr::guarded([&]() -> zr_status {
         bool no_work = false;
         ZR_TRY(validate_ag(K, shards, fulls, dt, segs, n_segs, chunk_shift, &no_work));
+        ZR_TRY(check_workspace(workspace, ws_bytes));
         if (no_work) return ok();
-        return run_ag(K, shards, fulls, dt, segs, n_segs, chunk_shift, (hipStream_t)stream);
+        hipStream_t s = (hipStream_t)stream;
+        if (!workspace || n_segs <= kAgSegsPerLaunch)
+            return run_ag(K, shards, fulls, dt, segs, n_segs, chunk_shift, s);
+        // the staged table must not overlap the written full extents or the shards
+        const int64_t es = dt_bytes(dt);
+        int64_t full_lo = INT64_MAX, full_hi = 0, shard_lo = INT64_MAX, shard_hi = 0;
+        for (int i = 0; i < n_segs; ++i) {
+            if (segs[i].numel == 0) continue;
+            full_lo = std::min(full_lo, segs[i].full_off);
+            full_hi = std::max(full_hi, segs[i].full_off + segs[i].numel);
+            shard_lo = std::min(shard_lo, segs[i].shard_off);
+            shard_hi = std::max(shard_hi, segs[i].shard_off + (segs[i].numel + K - 1) / K);
+        }
+        std::vector<Range> rf(K), rsh(K);
+        for (int r = 0; r < K; ++r) {
+            rf[r] = Range{(uintptr_t)fulls[r] + (uintptr_t)(full_lo * es), (uintptr_t)fulls[r] + (uintptr_t)(full_hi * es)};
+            rsh[r] = Range{(uintptr_t)shards[r] + (uintptr_t)(shard_lo * es), (uintptr_t)shards[r] + (uintptr_t)(shard_hi * es)};
+        }
+        ZR_TRY(check_staging(workspace, ws_bytes, ag_table_bytes(n_segs), rf, "fulls", rsh, "shards"));
+        if (capturing(s)) return run_ag(K, shards, fulls, dt, segs, n_segs, chunk_shift, s);
+        ConstPtrs sp{};
+        MutPtrs fp{};
+        for (int r = 0; r < K; ++r) {
+            sp.p[r] = shards[r];
+            fp.p[r] = fulls[r];
+        }
+        hipError_t e = launch_all_gather_ws(K, sp, fp, dt, segs, n_segs, chunk_shift, workspace, s);
+        if (e != hipSuccess) return hip_fail(e, "all-gather launch");
+        return ok();
     });
 }
 
@@ -390,82 +460,92 @@ zr_status zr_allreduce(int K, const void* const* in, void* const* out, zr_dtype 
     });
 }
 
-zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const int64_t* numels,
-                            void* const* buckets, int64_t padded_numel, zr_dtype dt, void* stream) {
-    return zr::guarded([&]() -> zr_status {
-        ZR_TRY(check_k(K));
-        if (n_frag < 0) return fail(ZR_ERR_INVALID, "n_frag=%d is negative", n_frag);
-        if (!dt_valid(dt)) return fail(ZR_ERR_UNSUPPORTED, "dtype %d not supported", (int)dt);
-        if (n_frag > 0 && (!frags || !numels)) return fail(ZR_ERR_INVALID, "frags or numels is NULL");
-        const int64_t es = dt_bytes(dt);
-        int64_t total = 0;
-        ZR_TRY(check_sizes(numels, n_frag, &total));
-        if (padded_numel > kMaxElems)
-            return fail(ZR_ERR_INVALID, "padded_numel=%lld too large", (long long)padded_numel);
-        if (padded_numel < total)
-            return fail(ZR_ERR_INVALID, "padded_numel=%lld < total fragment size %lld", (long long)padded_numel,
-                        (long long)total);
-        if (padded_numel == 0) return ok();
-        ZR_TRY(check_table(const_cast<const void* const*>(buckets), K, es, "buckets"));
-        std::vector<Range> rb(K), rf;
-        rf.reserve((size_t)K * n_frag);
-        for (int r = 0; r < K; ++r) rb[r] = range_of(buckets[r], padded_numel, es);
-        ZR_TRY(check_distinct(rb, "buckets"));
-        for (int r = 0; r < K; ++r)
-            for (int p = 0; p < n_frag; ++p) {
-                const void* f = frags[(size_t)r * n_frag + p];
-                if (numels[p] == 0) continue;
-                if (!f) return fail(ZR_ERR_INVALID, "fragment %d of rank %d is NULL", p, r);
-                if (((uintptr_t)f) & (uintptr_t)(es - 1))
-                    return fail(ZR_ERR_ALIGN, "fragment %d of rank %d is not aligned", p, r);
-                rf.push_back(range_of(f, numels[p], es));
-            }
-        ZR_TRY(check_disjoint(rb, "buckets", rf, "fragment"));
-        // one entry per fragment (every rank's copy of it), then the padding;
-        // a fragment of more than 2^28 / K tiles of 4 KiB per rank is cut
-        // into pieces of that many, so tile numbers fit the kernel's 32 bits
-        const int64_t piece = ((1LL << 28) / K) * (4096 / es);
-        std::vector<FragEntry> entries;
-        entries.reserve((size_t)n_frag + 1);
-        auto add = [&](const void* const* ptrs, int64_t off, int64_t n) {
-            for (int64_t o = 0; o < n; o += piece) {
-                FragEntry f{};
-                if (ptrs)
-                    for (int r = 0; r < K; ++r) f.ptr[r] = static_cast<const char*>(ptrs[r]) + o * es;
-                f.off = off + o;
-                f.n = std::min(piece, n - o);
-                entries.push_back(f);
-            }
-        };
-        std::vector<const void*> rp(K);
-        int64_t off = 0;
-        for (int p = 0; p < n_frag; ++p) {
-            if (numels[p] > 0) {
-                for (int r = 0; r < K; ++r) rp[r] = frags[(size_t)r * n_frag + p];
-                add(rp.data(), off, numels[p]);
-            }
-            off += numels[p];
-        }
-        if (padded_numel > off) add(nullptr, off, padded_numel - off);
-        MutPtrs bp{};
-        for (int r = 0; r < K; ++r) bp.p[r] = buckets[r];
-        hipStream_t s = (hipStream_t)stream;
-        hipError_t e = launch_flatten(K, entries.data(), (int)entries.size(), bp, (int)es, s);
-        if (e != hipSuccess) return hip_fail(e, "flatten launch");
-        return ok();
-    });
-}
-
 }  // extern "C"
 
 namespace zr {
 namespace {
 
-// Validates a discrete reduce-scatter and builds its launches. *plan is NULL
-// (with ZR_OK) when there is nothing to do (N == 0).
+// Validates a bucket flatten and builds its launches (with `ws`: one launch
+// over a table to be staged there, when more than one argument launch would
+// be needed). *plan is NULL (with ZR_OK) when there is nothing to do. On
+// success with a staged table, *rw holds the ranges the table must not
+// overlap (buckets then fragments, split at *n_buckets).
+zr_status make_flat_plan(int K, int n_frag, const void* const* frags, const int64_t* numels,
+                         void* const* buckets, int64_t padded_numel, zr_dtype dt, void* ws,
+                         size_t ws_bytes, FlatPlan** plan, std::vector<Range>* rb, std::vector<Range>* rf) {
+    *plan = nullptr;
+    ZR_TRY(check_k(K));
+    if (n_frag < 0) return fail(ZR_ERR_INVALID, "n_frag=%d is negative", n_frag);
+    if (!dt_valid(dt)) return fail(ZR_ERR_UNSUPPORTED, "dtype %d not supported", (int)dt);
+    if (n_frag > 0 && (!frags || !numels)) return fail(ZR_ERR_INVALID, "frags or numels is NULL");
+    ZR_TRY(check_workspace(ws, ws_bytes));
+    const int64_t es = dt_bytes(dt);
+    int64_t total = 0;
+    ZR_TRY(check_sizes(numels, n_frag, &total));
+    if (padded_numel > kMaxElems)
+        return fail(ZR_ERR_INVALID, "padded_numel=%lld too large", (long long)padded_numel);
+    if (padded_numel < total)
+        return fail(ZR_ERR_INVALID, "padded_numel=%lld < total fragment size %lld", (long long)padded_numel,
+                    (long long)total);
+    if (padded_numel == 0) return ok();
+    ZR_TRY(check_table(const_cast<const void* const*>(buckets), K, es, "buckets"));
+    rb->assign(K, Range{});
+    rf->clear();
+    rf->reserve((size_t)K * n_frag);
+    for (int r = 0; r < K; ++r) (*rb)[r] = range_of(buckets[r], padded_numel, es);
+    ZR_TRY(check_distinct(*rb, "buckets"));
+    for (int r = 0; r < K; ++r)
+        for (int p = 0; p < n_frag; ++p) {
+            const void* f = frags[(size_t)r * n_frag + p];
+            if (numels[p] == 0) continue;
+            if (!f) return fail(ZR_ERR_INVALID, "fragment %d of rank %d is NULL", p, r);
+            if (((uintptr_t)f) & (uintptr_t)(es - 1))
+                return fail(ZR_ERR_ALIGN, "fragment %d of rank %d is not aligned", p, r);
+            rf->push_back(range_of(f, numels[p], es));
+        }
+    ZR_TRY(check_disjoint(*rb, "buckets", *rf, "fragment"));
+    // one entry per non-empty fragment (every rank's copy of it), then the padding
+    std::vector<FragEntry> entries;
+    entries.reserve((size_t)n_frag + 1);
+    int64_t off = 0;
+    for (int p = 0; p < n_frag; ++p) {
+        if (numels[p] > 0) {
+            FragEntry f{};
+            for (int r = 0; r < K; ++r) f.ptr[r] = frags[(size_t)r * n_frag + p];
+            f.off = off;
+            f.n = numels[p];
+            entries.push_back(f);
+        }
+        off += numels[p];
+    }
+    if (padded_numel > off) {
+        FragEntry f{};
+        f.off = off;
+        f.n = padded_numel - off;
+        entries.push_back(f);
+    }
+    MutPtrs bp{};
+    for (int r = 0; r < K; ++r) bp.p[r] = buckets[r];
+    *plan = flat_plan_build(K, entries.data(), (int)entries.size(), bp, (int)es, ws);
+    if (!*plan) return fail(ZR_ERR_NOMEM, "out of host memory");
+    const size_t need = flat_plan_table_bytes(*plan);
+    if (need > 0) {
+        const zr_status st = check_staging(ws, ws_bytes, need, *rb, "buckets", *rf, "fragment");
+        if (st != ZR_OK) {
+            flat_plan_free(*plan);
+            *plan = nullptr;
+            return st;
+        }
+    }
+    return ok();
+}
+
+// Validates a discrete reduce-scatter and builds its launches, as
+// make_flat_plan does. *plan is NULL (with ZR_OK) when N == 0.
 zr_status make_frags_plan(int K, int n_frag, const void* const* frags, const int64_t* numels,
                           int64_t N, zr_dtype in_dt, void* const* out, zr_dtype out_dt,
-                          int chunk_shift, int flags, zr_order order, RsfPlan** plan) {
+                          int chunk_shift, int flags, zr_order order, void* ws, size_t ws_bytes,
+                          RsfPlan** plan) {
     *plan = nullptr;
     ZR_TRY(check_k(K));
     if (n_frag < 0) return fail(ZR_ERR_INVALID, "n_frag=%d is negative", n_frag);
@@ -478,6 +558,7 @@ zr_status make_frags_plan(int K, int n_frag, const void* const* frags, const int
     if (order != ZR_ORDER_RING && order != ZR_ORDER_FREE && order != ZR_ORDER_RING_WIRE)
         return fail(ZR_ERR_INVALID, "order=%d is not a zr_order", (int)order);
     if (n_frag > 0 && (!frags || !numels)) return fail(ZR_ERR_INVALID, "frags or numels is NULL");
+    ZR_TRY(check_workspace(ws, ws_bytes));
     int64_t total = 0;
     ZR_TRY(check_sizes(numels, n_frag, &total));
     if (N < total)
@@ -524,8 +605,39 @@ zr_status make_frags_plan(int K, int n_frag, const void* const* frags, const int
     MutPtrs op{};
     for (int r = 0; r < K; ++r) op.p[r] = out[r];
     *plan = rsf_plan_build(K, entries.data(), (int)entries.size(), N, in_dt, op, out_dt, chunk_shift,
-                           flags, order);
+                           flags, order, ws);
     if (!*plan) return fail(ZR_ERR_NOMEM, "out of host memory");
+    const size_t need = rsf_plan_table_bytes(*plan);
+    if (need > 0) {
+        const zr_status st = check_staging(ws, ws_bytes, need, ro, "out", rf, "fragment");
+        if (st != ZR_OK) {
+            rsf_plan_free(*plan);
+            *plan = nullptr;
+            return st;
+        }
+    }
+    return ok();
+}
+
+// A plan built for one call: launched once (after staging its table on the
+// stream), then freed.
+template <typename Plan, typename Build, typename Bytes, typename Image, typename Launch, typename Free>
+zr_status run_once(Build build, Bytes bytes, Image image, Launch launch, Free free_plan, void* ws,
+                   hipStream_t s, const char* what) {
+    Plan* plan = nullptr;
+    ZR_TRY(build(ws, &plan));
+    if (!plan) return ok();
+    if (bytes(plan) > 0 && capturing(s)) {
+        // no asynchronous copy from a host buffer into a graph: argument launches
+        free_plan(plan);
+        plan = nullptr;
+        ZR_TRY(build(nullptr, &plan));
+        if (!plan) return ok();
+    }
+    hipError_t e = stage_table(ws, image(plan), bytes(plan), s, true);
+    if (e == hipSuccess) e = launch(plan, s);
+    free_plan(plan);
+    if (e != hipSuccess) return hip_fail(e, what);
     return ok();
 }
 
@@ -536,33 +648,119 @@ struct zr_rsf_plan {
     zr::RsfPlan* plan;  // NULL: nothing to launch
 };
 
+struct zr_flatten_plan {
+    zr::FlatPlan* plan;  // NULL: nothing to launch
+};
+
 extern "C" {
+
+size_t zr_workspace_bytes(int K, int n) {
+    if (K < 1 || K > kMaxRanks || n < 0) return 0;
+    // the flatten and the discrete reduce-scatter carry min(32, 256 / K)
+    // fragments per argument block, the all-gather 32 segments
+    const int fit = std::min(kRsfEntriesPerLaunch, kRsfPtrsPerLaunch / K);
+    if (n <= fit) return 0;
+    const int64_t nent = (int64_t)n + 1;  // the fragments and the padding
+    const int64_t nseg = (int64_t)n + K;  // each of the K - 1 chunk boundaries splits one entry at most
+    const size_t b = std::max({rsf_table_bytes(K, nent, nseg), flatten_table_bytes(K, nent), ag_table_bytes(n)});
+    return (b + kWsAlign - 1) / kWsAlign * kWsAlign;
+}
+
+zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const int64_t* numels,
+                            void* const* buckets, int64_t padded_numel, zr_dtype dt, void* workspace,
+                            size_t ws_bytes, void* stream) {
+    return zr::guarded([&]() -> zr_status {
+        std::vector<Range> rb, rf;
+        auto build = [&](void* ws, FlatPlan** p) {
+            return make_flat_plan(K, n_frag, frags, numels, buckets, padded_numel, dt, ws, ws_bytes, p, &rb, &rf);
+        };
+        return run_once<FlatPlan>(build, flat_plan_table_bytes, flat_plan_table_image, flat_plan_launch,
+                                  flat_plan_free, workspace, (hipStream_t)stream, "flatten launch");
+    });
+}
+
+zr_status zr_flatten_plan_create(int K, int n_frag, const void* const* frags, const int64_t* numels,
+                                 void* const* buckets, int64_t padded_numel, zr_dtype dt, void* workspace,
+                                 size_t ws_bytes, zr_flatten_plan** plan) {
+    return zr::guarded([&]() -> zr_status {
+        if (!plan) return fail(ZR_ERR_INVALID, "plan is NULL");
+        *plan = nullptr;
+        FlatPlan* p = nullptr;
+        std::vector<Range> rb, rf;
+        ZR_TRY(make_flat_plan(K, n_frag, frags, numels, buckets, padded_numel, dt, workspace, ws_bytes, &p, &rb,
+                              &rf));
+        if (p && flat_plan_table_bytes(p) > 0) {
+            const hipError_t e = stage_table(workspace, flat_plan_table_image(p), flat_plan_table_bytes(p), nullptr,
+                                             false);
+            if (e != hipSuccess) {
+                flat_plan_free(p);
+                return hip_fail(e, "staging the flatten table");
+            }
+        }
+        zr_flatten_plan* h = new (std::nothrow) zr_flatten_plan{p};
+        if (!h) {
+            if (p) flat_plan_free(p);
+            return fail(ZR_ERR_NOMEM, "out of host memory");
+        }
+        *plan = h;
+        return ok();
+    });
+}
+
+zr_status zr_flatten_plan_launch(const zr_flatten_plan* plan, void* stream) {
+    if (!plan) return fail(ZR_ERR_INVALID, "plan is NULL");
+    if (!plan->plan) return ok();
+    const hipError_t e = flat_plan_launch(plan->plan, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "flatten launch");
+    return ok();
+}
+
+zr_status zr_flatten_plan_info(const zr_flatten_plan* plan, int* launches, size_t* table_bytes) {
+    if (!plan) return fail(ZR_ERR_INVALID, "plan is NULL");
+    if (launches) *launches = plan->plan ? flat_plan_launch_count(plan->plan) : 0;
+    if (table_bytes) *table_bytes = plan->plan ? flat_plan_table_bytes(plan->plan) : 0;
+    return ok();
+}
+
+zr_status zr_flatten_plan_destroy(zr_flatten_plan* plan) {
+    if (!plan) return ok();
+    if (plan->plan) flat_plan_free(plan->plan);
+    delete plan;
+    return ok();
+}
 
 zr_status zr_reduce_scatter_frags(int K, int n_frag, const void* const* frags,
                                   const int64_t* numels, int64_t N, zr_dtype in_dt,
                                   void* const* out, zr_dtype out_dt, int chunk_shift, int flags,
-                                  zr_order order, void* stream) {
+                                  zr_order order, void* workspace, size_t ws_bytes, void* stream) {
     return zr::guarded([&]() -> zr_status {
-        RsfPlan* plan = nullptr;
-        ZR_TRY(make_frags_plan(K, n_frag, frags, numels, N, in_dt, out, out_dt, chunk_shift, flags, order,
-                               &plan));
-        if (!plan) return ok();
-        const hipError_t e = rsf_plan_launch(plan, (hipStream_t)stream);
-        rsf_plan_free(plan);
-        if (e != hipSuccess) return hip_fail(e, "discrete reduce-scatter launch");
-        return ok();
+        auto build = [&](void* ws, RsfPlan** p) {
+            return make_frags_plan(K, n_frag, frags, numels, N, in_dt, out, out_dt, chunk_shift, flags, order, ws,
+                                   ws_bytes, p);
+        };
+        return run_once<RsfPlan>(build, rsf_plan_table_bytes, rsf_plan_table_image, rsf_plan_launch, rsf_plan_free,
+                                 workspace, (hipStream_t)stream, "discrete reduce-scatter launch");
     });
 }
 
 zr_status zr_rsf_plan_create(int K, int n_frag, const void* const* frags, const int64_t* numels,
                              int64_t N, zr_dtype in_dt, void* const* out, zr_dtype out_dt,
-                             int chunk_shift, int flags, zr_order order, zr_rsf_plan** plan) {
+                             int chunk_shift, int flags, zr_order order, void* workspace,
+                             size_t ws_bytes, zr_rsf_plan** plan) {
     return zr::guarded([&]() -> zr_status {
         if (!plan) return fail(ZR_ERR_INVALID, "plan is NULL");
         *plan = nullptr;
         RsfPlan* p = nullptr;
         ZR_TRY(make_frags_plan(K, n_frag, frags, numels, N, in_dt, out, out_dt, chunk_shift, flags, order,
-                               &p));
+                               workspace, ws_bytes, &p));
+        if (p && rsf_plan_table_bytes(p) > 0) {
+            const hipError_t e = stage_table(workspace, rsf_plan_table_image(p), rsf_plan_table_bytes(p), nullptr,
+                                             false);
+            if (e != hipSuccess) {
+                rsf_plan_free(p);
+                return hip_fail(e, "staging the discrete reduce-scatter table");
+            }
+        }
         zr_rsf_plan* h = new (std::nothrow) zr_rsf_plan{p};
         if (!h) {
             if (p) rsf_plan_free(p);
@@ -578,6 +776,13 @@ zr_status zr_rsf_plan_launch(const zr_rsf_plan* plan, void* stream) {
     if (!plan->plan) return ok();
     const hipError_t e = rsf_plan_launch(plan->plan, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "discrete reduce-scatter launch");
+    return ok();
+}
+
+zr_status zr_rsf_plan_info(const zr_rsf_plan* plan, int* launches, size_t* table_bytes) {
+    if (!plan) return fail(ZR_ERR_INVALID, "plan is NULL");
+    if (launches) *launches = plan->plan ? rsf_plan_launch_count(plan->plan) : 0;
+    if (table_bytes) *table_bytes = plan->plan ? rsf_plan_table_bytes(plan->plan) : 0;
     return ok();
 }
 

@@ -11,13 +11,18 @@
 // tensor) are its (chunk, tile) pairs, chunk by chunk, and the segments'
 // tiles follow each other, so blocks stay balanced however unequal the
 // tensors are; a block finds its segment by a uniform binary search over the
-// segments' first tiles. (A persistent grid striding over the tiles ran
+// segments' first tiles. The segment table rides in the kernel arguments, 32
+// segments per launch; given a workspace, any number of segments go out as
+// one launch that reads a table staged there (scalar loads, wave-wide
+// search). (A persistent grid striding over the tiles ran
 // 10-15% slower.) A tile writes 16 KiB to every full buffer: each lane loads
 // kAgSub groups of 8 shard elements (16 bytes each for bf16), all before its
 // first store, and stores each to all K full buffers, so each shard byte is
 // read once and written K times. (Tiles of 16 KiB per destination ran 1% faster
 // than tiles of 4, 8 or 32 KiB.) Chunk starts that are not 16-byte aligned on
 // either side, and ragged ends, copy element by element.
+#include <vector>
+
 #include "zr_device.hpp"
 #include "zr_internal.hpp"
 
@@ -30,28 +35,37 @@ struct AgSeg {
     int tiles_per_chunk;
     int pad_;
 };
+static_assert(sizeof(AgSeg) == kAgSegBytes, "staged all-gather records are kAgSegBytes each");
 
-struct AgArgs {
+// Fields every launch carries, whichever table it reads.
+struct AgCommon {
     ConstPtrs shards;
     MutPtrs fulls;
+    int K, shift;
+};
+
+// A launch whose segment table rides in its kernel arguments.
+struct AgArgs {
+    AgCommon c;
     AgSeg seg[kAgSegsPerLaunch];
     int64_t unit0[kAgSegsPerLaunch + 1];  // first tile of segment s; unit0[nseg] = all tiles
-    int K, shift, nseg;
+    int nseg;
 };
 static_assert(sizeof(AgArgs) <= 4096, "all-gather arguments exceed 4 KB");
 
-// Groups of kGroup elements per lane in one tile: 16 KiB per destination.
-template <typename T>
-constexpr int kAgSub = 16384 / (kTile * (int)sizeof(T));
-template <typename T>
-constexpr int64_t kAgTile = (int64_t)kAgSub<T> * kTile;
+// A launch whose table is staged in a workspace (the layout of ag_table_bytes).
+struct AgWsArgs {
+    AgCommon c;
+    uint64_t unit0;  // int64_t[nseg + 1]
+    uint64_t seg;    // AgSeg[nseg]
+    int64_t nseg;
+};
 
-template <typename T, int KS, bool NT>
-__global__ void __launch_bounds__(kThreads) ag_kernel(const AgArgs a) {
-    constexpr int SUB = kAgSub<T>;
-    const int K = KS > 0 ? KS : a.K;
-    for (int64_t u = blockIdx.x; u < a.unit0[a.nseg]; u += gridDim.x) {
-        // the tile's segment: the last s with unit0[s] <= u (uniform)
+struct AgArgTable {
+    const AgArgs& a;
+    __device__ __forceinline__ int64_t total() const { return a.unit0[a.nseg]; }
+    // the last s with unit0[s] <= u (uniform binary search)
+    __device__ __forceinline__ int64_t find(int64_t u) const {
         int s = 0;
         for (int hi = a.nseg; hi - s > 1;) {
             const int mid = (s + hi) >> 1;
@@ -60,8 +74,51 @@ __global__ void __launch_bounds__(kThreads) ag_kernel(const AgArgs a) {
             else
                 hi = mid;
         }
-        const AgSeg& sg = a.seg[s];
-        const int ul = (int)(u - a.unit0[s]);  // < K * tiles_per_chunk <= 2^29: 32-bit division
+        return s;
+    }
+    __device__ __forceinline__ int64_t first(int64_t s) const { return a.unit0[s]; }
+    __device__ __forceinline__ AgSeg seg(int64_t s) const { return a.seg[s]; }
+};
+
+struct AgWsTable {
+    cptr<int64_t> unit0;
+    cptr<AgSeg> segs;
+    int64_t nseg;
+    __device__ __forceinline__ explicit AgWsTable(const AgWsArgs& a)
+        : unit0(table_at<int64_t>(a.unit0)), segs(table_at<AgSeg>(a.seg)), nseg(a.nseg) {}
+    __device__ __forceinline__ int64_t total() const { return unit0[nseg]; }
+    __device__ __forceinline__ int64_t find(int64_t u) const { return find_slot64(unit0, nseg, u); }
+    __device__ __forceinline__ int64_t first(int64_t s) const { return unit0[s]; }
+    __device__ __forceinline__ AgSeg seg(int64_t s) const {
+        const cptr<AgSeg> p = segs + s;  // field by field: the record lives in the constant space
+        AgSeg r;
+        r.shard_off = p->shard_off;
+        r.full_off = p->full_off;
+        r.numel = p->numel;
+        r.C = p->C;
+        r.vec_mask = p->vec_mask;
+        r.tiles_per_chunk = p->tiles_per_chunk;
+        r.pad_ = 0;
+        return r;
+    }
+};
+
+// Groups of kGroup elements per lane in one tile: 16 KiB per destination.
+template <typename T>
+constexpr int kAgSub = 16384 / (kTile * (int)sizeof(T));
+template <typename T>
+constexpr int64_t kAgTile = (int64_t)kAgSub<T> * kTile;
+
+template <typename T, int KS, bool NT, typename Tab>
+__device__ __forceinline__ void ag_body(const AgCommon& a, const Tab& tab) {
+    constexpr int SUB = kAgSub<T>;
+    const int K = KS > 0 ? KS : a.K;
+    const int64_t total = tab.total();
+    for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
+        // the tile's segment: the last s with unit0[s] <= u (uniform)
+        const int64_t s = tab.find(u);
+        const AgSeg sg = tab.seg(s);
+        const int ul = (int)(u - tab.first(s));  // < K * tiles_per_chunk <= 2^29: 32-bit division
         const int j = ul / sg.tiles_per_chunk;
         const int t = ul - j * sg.tiles_per_chunk;
         int holder = j - a.shift;
@@ -104,45 +161,57 @@ __global__ void __launch_bounds__(kThreads) ag_kernel(const AgArgs a) {
 }
 
 template <typename T, int KS, bool NT>
+__global__ void __launch_bounds__(kThreads) ag_kernel(const AgArgs a) {
+    ag_body<T, KS, NT>(a.c, AgArgTable{a});
+}
+
+template <typename T, int KS, bool NT>
+__global__ void __launch_bounds__(kThreads) ag_ws_kernel(const AgWsArgs a) {
+    ag_body<T, KS, NT>(a.c, AgWsTable(a));
+}
+
+template <typename T, int KS, bool NT>
 hipError_t launch_t(const AgArgs& a, hipStream_t stream) {
     const int gx = grid_for(a.unit0[a.nseg]);  // one block per tile
     hipLaunchKernelGGL((ag_kernel<T, KS, NT>), dim3(gx), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-template <typename T, int KS>
-hipError_t pick_nt(const AgArgs& a, hipStream_t s) {
-    return tuning().ag_nontemporal ? launch_t<T, KS, true>(a, s) : launch_t<T, KS, false>(a, s);
+template <typename T, int KS, bool NT>
+hipError_t launch_t(const AgWsArgs& a, int64_t tiles, hipStream_t stream) {
+    const int gx = grid_for(tiles);  // one block per tile, striding beyond the cap
+    hipLaunchKernelGGL((ag_ws_kernel<T, KS, NT>), dim3(gx), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
 }
 
-template <typename T>
-hipError_t pick_k(const AgArgs& a, hipStream_t s) {
-    switch (a.K) {
-        case 8: return pick_nt<T, 8>(a, s);
-        default: return pick_nt<T, 0>(a, s);
+template <typename T, int KS, typename... Args>
+hipError_t pick_nt(const Args&... a) {
+    return tuning().ag_nontemporal ? launch_t<T, KS, true>(a...) : launch_t<T, KS, false>(a...);
+}
+
+template <typename T, typename... Args>
+hipError_t pick_k(int K, const Args&... a) {
+    switch (K) {
+        case 8: return pick_nt<T, 8>(a...);
+        default: return pick_nt<T, 0>(a...);
     }
 }
 
-}  // namespace
-
-hipError_t launch_all_gather(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype dt,
-                             const zr_seg* segs, int n_segs, int shift, hipStream_t stream) {
-    AgArgs a;
-    a.shards = shards;
-    a.fulls = fulls;
-    a.K = K;
-    a.shift = shift;
+// The segment records of a launch (empty segments dropped): vector mask and
+// tiles per chunk of each, and the running first tile.
+int64_t describe(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype dt, const zr_seg* segs,
+                 int n_segs, AgSeg* out, int64_t* unit0, int* used) {
     const int es = dt == ZR_BF16 ? 2 : 4;
     const int64_t tile = dt == ZR_BF16 ? kAgTile<uint16_t> : kAgTile<float>;  // elements per tile
     bool bases = true;
     for (int r = 0; r < K; ++r)
         bases = bases && (((uintptr_t)shards.p[r]) & 15) == 0 && (((uintptr_t)fulls.p[r]) & 15) == 0;
-    int used = 0;
+    int n = 0;
     int64_t units = 0;
     for (int s = 0; s < n_segs; ++s) {
         if (segs[s].numel == 0) continue;
-        a.unit0[used] = units;
-        AgSeg& d = a.seg[used++];
+        unit0[n] = units;
+        AgSeg& d = out[n++];
         d.shard_off = segs[s].shard_off;
         d.full_off = segs[s].full_off;
         d.numel = segs[s].numel;
@@ -157,11 +226,51 @@ hipError_t launch_all_gather(int K, const ConstPtrs& shards, const MutPtrs& full
         }
         units += (int64_t)K * d.tiles_per_chunk;
     }
-    if (used == 0) return hipSuccess;
-    a.unit0[used] = units;
+    unit0[n] = units;
+    *used = n;
+    return units;
+}
+
+}  // namespace
+
+hipError_t launch_all_gather(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype dt,
+                             const zr_seg* segs, int n_segs, int shift, hipStream_t stream) {
+    AgArgs a;
+    a.c.shards = shards;
+    a.c.fulls = fulls;
+    a.c.K = K;
+    a.c.shift = shift;
+    int used = 0;
+    if (describe(K, shards, fulls, dt, segs, n_segs, a.seg, a.unit0, &used) == 0) return hipSuccess;
     a.nseg = used;
-    if (dt == ZR_BF16) return pick_k<uint16_t>(a, stream);
-    return pick_k<float>(a, stream);
+    if (dt == ZR_BF16) return pick_k<uint16_t>(K, a, stream);
+    return pick_k<float>(K, a, stream);
+}
+
+hipError_t launch_all_gather_ws(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype dt,
+                                const zr_seg* segs, int n_segs, int shift, void* ws,
+                                hipStream_t stream) {
+    std::vector<uint8_t> image(ag_table_bytes(n_segs));
+    int64_t* unit0 = reinterpret_cast<int64_t*>(image.data());
+    AgSeg* recs = reinterpret_cast<AgSeg*>(image.data() + 8 * (size_t)(n_segs + 1));
+    int used = 0;
+    const int64_t tiles = describe(K, shards, fulls, dt, segs, n_segs, recs, unit0, &used);
+    if (tiles == 0) return hipSuccess;
+    // the records were written compactly after n_segs + 1 first-tile slots; the
+    // kernel reads used + 1 of them and used records
+    AgWsArgs a;
+    a.c.shards = shards;
+    a.c.fulls = fulls;
+    a.c.K = K;
+    a.c.shift = shift;
+    a.unit0 = (uint64_t)(uintptr_t)ws;
+    a.seg = (uint64_t)(uintptr_t)ws + 8 * (uint64_t)(n_segs + 1);
+    a.nseg = used;
+    const size_t bytes = 8 * (size_t)(n_segs + 1) + sizeof(AgSeg) * (size_t)used;
+    hipError_t e = stage_table(ws, image.data(), bytes, stream, true);
+    if (e != hipSuccess) return e;
+    if (dt == ZR_BF16) return pick_k<uint16_t>(K, a, tiles, stream);
+    return pick_k<float>(K, a, tiles, stream);
 }
 
 }  // namespace zr

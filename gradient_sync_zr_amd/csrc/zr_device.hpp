@@ -169,6 +169,37 @@ __device__ __forceinline__ int find_slot(const int32_t* start, int n, int m, int
     }
 }
 
+// A pointer into a descriptor table staged in device memory, in the constant
+// address space: the table is read-only while a kernel runs, so loads at a
+// block-uniform index become scalar loads. Tables pass their device address
+// as an integer in the kernel arguments.
+template <typename T>
+using cptr = const __attribute__((address_space(4))) T*;
+template <typename T>
+__device__ __forceinline__ cptr<T> table_at(uint64_t addr) {
+    return reinterpret_cast<cptr<T>>(addr);
+}
+
+// The slot holding item t of a flat item space cut into n slots, where
+// start[0..n] (a staged table) is nondecreasing, start[0] = 0 <= t < start[n]:
+// the last s with start[s] <= t. The wave narrows [lo, hi) 64 candidates at
+// a time (one load per lane, a ballot counts those <= t), so any n is found in
+// ceil(log64 n) rounds. t is uniform across the wave.
+__device__ __forceinline__ int64_t find_slot64(cptr<int64_t> start, int64_t n, int64_t t) {
+    const int lane = threadIdx.x & 63;
+    int64_t lo = 0, hi = n;  // start[lo] <= t < start[hi]
+    while (hi - lo > 1) {
+        const int64_t step = (hi - lo + 63) / 64;
+        const int64_t idx = lo + (int64_t)lane * step;
+        const bool le = idx < hi && start[idx] <= t;  // true on a prefix of the lanes
+        const int c = __popcll(__ballot(le));        // >= 1: lane 0 reads start[lo]
+        const int64_t nhi = lo + (int64_t)c * step;
+        lo += (int64_t)(c - 1) * step;
+        hi = nhi < hi ? nhi : hi;
+    }
+    return lo;
+}
+
 // Average: AVG 0 = none, 1 = multiply by the exact reciprocal (K a power of
 // two, identical to dividing), 2 = IEEE correctly rounded divide by K.
 template <int AVG>

@@ -5,12 +5,15 @@
 // message instead of one per parameter).
 //
 // Every rank has the same fragment sizes, so a fragment is one entry: its
-// bucket offset and size, shared by the ranks, and its K source pointers. A
-// launch carries up to 32 entries' pointers (256 pointers, so 4 entries at
-// K = 64), the zero padding in a spare slot after them (it has no source),
-// the K bucket bases and each entry's first tile, all in its kernel
-// arguments: no device descriptor table, no staging copy. Entry m owns K
-// runs of tiles_per_rank[m] tiles, rank by rank. The grid has one block per
+// bucket offset and size, shared by the ranks, and its K source pointers.
+// Entry m owns K runs of tiles_per_rank[m] tiles, rank by rank. The table of
+// entries rides in the kernel arguments when it fits one argument block: up
+// to 32 entries' pointers (256 pointers, so 4 entries at K = 64), the zero
+// padding in a spare slot after them (it has no source), and each entry's
+// first tile; more entries go out as further launches. Given a workspace, a
+// larger table is staged there and one launch copies every fragment (the
+// bucket as one operation, section 3.1); the kernel reads it with scalar loads
+// and finds a tile's entry with a wave-wide search. The grid has one block per
 // tile of the launch, in order, so blocks stay balanced however unequal the
 // fragments are, and the blocks in flight work on one compact window of
 // memory (a persistent grid striding over the tiles ran 15-20% slower on a
@@ -26,6 +29,10 @@
 // partial unit, and every unit of a copy that is not aligned so (possible
 // inside a bucket, where offsets are prefix sums of arbitrary sizes), copies
 // element by element.
+#include <cstring>
+#include <new>
+#include <vector>
+
 #include "zr_device.hpp"
 #include "zr_internal.hpp"
 
@@ -39,31 +46,81 @@ constexpr int64_t kFlatTileBytes = (int64_t)kThreads * 16 * kUnits;
 // Entry slots: fragments with source pointers, plus one for the padding.
 constexpr int kFlatSlots = kFlatEntriesPerLaunch + 1;
 
+// Fields every launch carries, whichever table it reads.
+struct FlatCommon {
+    MutPtrs bucket;  // rank r's bucket
+    int K;
+    int pad_m;       // the padding entry (writes zeros), -1: none
+};
+
+// A launch whose table rides in its kernel arguments.
 struct FlatArgs {
+    FlatCommon c;
     const void* src[kFlatPtrsPerLaunch];  // entry-major: src[m * K + r]
-    void* bucket[kMaxRanks];               // rank r's bucket
     int64_t off[kFlatSlots];               // bucket offset of entry m (elements)
     int64_t n[kFlatSlots];                 // elements of entry m
     int32_t tile0[kFlatSlots + 1];         // first tile of entry m; tile0[nent] = all tiles
     int32_t tpr[kFlatSlots];               // tiles of entry m per rank
-    int K, nent, pad_m;                    // pad_m: the padding entry (writes zeros), -1: none
+    int nent;
 };
 static_assert(sizeof(FlatArgs) <= 4096, "flatten arguments exceed 4 KB");
 
-template <typename T>
-__global__ void __launch_bounds__(kThreads) flatten_kernel(const FlatArgs a) {
+// A launch whose table is staged in a workspace (the layout of flatten_table_bytes).
+struct FlatWsArgs {
+    FlatCommon c;
+    uint64_t tile0;  // int64_t[nent + 1]: first tile of entry m; tile0[nent] = all tiles
+    uint64_t tpr;    // int64_t[nent]: tiles of entry m per rank
+    uint64_t ent;    // int64_t[2 * nent]: bucket offset and size of entry m at 2m
+    uint64_t src;    // const void*[K * nent], entry-major (null for the padding entry)
+    int64_t nent;
+};
+
+struct FlatEnt {
+    int64_t off, n, tpr;
+};
+
+struct FlatArgTable {
+    using Index = int;  // argument launches keep tile numbers within 32 bits
+    const FlatArgs& a;
+    __device__ __forceinline__ int total() const { return a.tile0[a.nent]; }
+    // a block's tiles only grow, so its last entry is a lower bound
+    __device__ __forceinline__ int find(int from, int t) const { return find_slot(a.tile0, a.nent, from, t); }
+    __device__ __forceinline__ int first(int m) const { return a.tile0[m]; }
+    __device__ __forceinline__ FlatEnt ent(int m) const { return {a.off[m], a.n[m], a.tpr[m]}; }
+    __device__ __forceinline__ const void* src(int m, int K, int r) const { return a.src[m * K + r]; }
+};
+
+struct FlatWsTable {
+    using Index = int64_t;
+    cptr<int64_t> tile0, tpr, en;
+    cptr<const void*> srcs;
+    int64_t nent;
+    __device__ __forceinline__ explicit FlatWsTable(const FlatWsArgs& a)
+        : tile0(table_at<int64_t>(a.tile0)), tpr(table_at<int64_t>(a.tpr)), en(table_at<int64_t>(a.ent)),
+          srcs(table_at<const void*>(a.src)), nent(a.nent) {}
+    __device__ __forceinline__ int64_t total() const { return tile0[nent]; }
+    __device__ __forceinline__ int64_t find(int64_t, int64_t t) const { return find_slot64(tile0, nent, t); }
+    __device__ __forceinline__ int64_t first(int64_t m) const { return tile0[m]; }
+    __device__ __forceinline__ FlatEnt ent(int64_t m) const { return {en[2 * m], en[2 * m + 1], tpr[m]}; }
+    __device__ __forceinline__ const void* src(int64_t m, int K, int r) const { return srcs[m * K + r]; }
+};
+
+template <typename T, typename Tab>
+__device__ __forceinline__ void flatten_body(const FlatCommon& c, const Tab& tab) {
     constexpr int per = 16 / sizeof(T);  // elements per 16-byte unit
+    using Index = typename Tab::Index;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int total = a.tile0[a.nent];
-    int m = 0;
-    for (int t = blockIdx.x; t < total; t += gridDim.x) {
-        m = find_slot(a.tile0, a.nent, m, t);  // a block's tiles only grow: entries in order
-        const int tt = t - a.tile0[m];
-        const int r = tt / a.tpr[m];            // the entry's tiles run rank by rank
-        const int64_t lt = tt - (int64_t)r * a.tpr[m];
-        const int64_t n = a.n[m];
-        const T* src = m == a.pad_m ? nullptr : static_cast<const T*>(a.src[m * a.K + r]);
-        T* dst = static_cast<T*>(a.bucket[r]) + a.off[m];
+    const Index total = tab.total();
+    Index m = 0;
+    for (Index t = blockIdx.x; t < total; t += gridDim.x) {
+        m = tab.find(m, t);
+        const FlatEnt fe = tab.ent(m);
+        const Index tt = t - tab.first(m);
+        const int r = (int)(tt / (Index)fe.tpr);  // the entry's tiles run rank by rank
+        const int64_t lt = tt - (int64_t)r * fe.tpr;
+        const int64_t n = fe.n;
+        const T* src = m == c.pad_m ? nullptr : static_cast<const T*>(tab.src(m, c.K, r));
+        T* dst = static_cast<T*>(c.bucket.p[r]) + fe.off;
         const bool vec = ((((uintptr_t)dst) & 15) == 0) && (src == nullptr || (((uintptr_t)src) & 15) == 0);
         const int64_t u0 = lt * (kFlatTileBytes / 16) + wave * 64 * kUnits + lane;  // first unit
         if (vec && (u0 + 64 * (kUnits - 1) + 1) * per <= n) {
@@ -111,66 +168,155 @@ __global__ void __launch_bounds__(kThreads) flatten_kernel(const FlatArgs a) {
 }
 
 template <typename T>
-hipError_t launch_batch(const FlatArgs& a, hipStream_t stream) {
-    const int64_t tiles = a.tile0[a.nent];
-    const int gx = grid_for(tiles);  // one block per tile
-    hipLaunchKernelGGL((flatten_kernel<T>), dim3(gx), dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+__global__ void __launch_bounds__(kThreads) flatten_kernel(const FlatArgs a) {
+    flatten_body<T>(a.c, FlatArgTable{a});
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads) flatten_ws_kernel(const FlatWsArgs a) {
+    flatten_body<T>(a.c, FlatWsTable(a));
 }
 
 int64_t tiles_of(int64_t bytes, int64_t tile) { return (bytes + tile - 1) / tile; }
 
-}  // namespace
-
-// Entries go out in launches of at most 32 fragments (256 source pointers)
-// plus the padding entry if it comes next, and about 2^29 tiles; a larger
-// entry has already been split by the caller, so tile numbers fit in 32 bits.
-hipError_t launch_flatten(int K, const FragEntry* entries, int n_entries, const MutPtrs& buckets,
-                          int elem_bytes, hipStream_t stream) {
+// Cuts the entries into argument launches of at most 32 fragments (256
+// source pointers) plus the padding entry if it comes next, and about 2^29
+// tiles; an entry of more than 2^28 / K tiles per rank is cut into pieces of
+// that many first, so tile numbers fit in 32 bits.
+void cut_args(const FlatCommon& c, const FragEntry* entries, int n_entries, int elem_bytes,
+              std::vector<FlatArgs>* out) {
+    const int K = c.K;
     const int max_entries = (kFlatPtrsPerLaunch / K) < kFlatEntriesPerLaunch ? (kFlatPtrsPerLaunch / K)
                                                                            : kFlatEntriesPerLaunch;
+    const int64_t piece = ((1LL << 28) / K) * (kFlatTileBytes / elem_bytes);  // elements
     FlatArgs a;
-    a.K = K;
-    for (int r = 0; r < K; ++r) a.bucket[r] = buckets.p[r];
-    int first = 0, count = 0, pad = -1;
-    int64_t batch = 0;  // tiles of the batch
-    auto flush = [&]() -> hipError_t {
-        if (count == 0) return hipSuccess;
-        const int64_t tile = kFlatTileBytes;
-        int64_t tiles = 0;
-        for (int i = 0; i < count; ++i) {
-            const FragEntry& f = entries[first + i];
-            a.off[i] = f.off;
-            a.n[i] = f.n;
-            if (i != pad)
-                for (int r = 0; r < K; ++r) a.src[i * K + r] = f.ptr[r];
-            a.tpr[i] = (int32_t)tiles_of(f.n * elem_bytes, tile);
-            a.tile0[i] = (int32_t)tiles;
-            tiles += (int64_t)K * a.tpr[i];
-        }
+    std::memset(&a, 0, sizeof(a));
+    a.c = c;
+    a.c.pad_m = -1;
+    int count = 0;
+    int64_t tiles = 0;
+    auto flush = [&]() {
+        if (count == 0) return;
         a.tile0[count] = (int32_t)tiles;
         a.nent = count;
-        a.pad_m = pad;
-        hipError_t e = hipSuccess;
-        if (tiles > 0)
-            e = elem_bytes == 2 ? launch_batch<uint16_t>(a, stream) : launch_batch<uint32_t>(a, stream);
-        first += count;
+        if (tiles > 0) out->push_back(a);
         count = 0;
-        pad = -1;
-        batch = 0;
-        return e;
+        tiles = 0;
+        a.c.pad_m = -1;
     };
     for (int i = 0; i < n_entries; ++i) {
-        const bool is_pad = entries[i].ptr[0] == nullptr;
-        if (count == (is_pad ? max_entries + 1 : max_entries) || pad >= 0 || batch > (1LL << 28)) {
-            hipError_t e = flush();
-            if (e != hipSuccess) return e;
+        const FragEntry& f = entries[i];
+        const bool is_pad = f.ptr[0] == nullptr;
+        for (int64_t o = 0; o < f.n; o += piece) {
+            const int64_t pn = f.n - o < piece ? f.n - o : piece;
+            const int64_t tpr = tiles_of(pn * elem_bytes, kFlatTileBytes);
+            if (count == (is_pad ? max_entries + 1 : max_entries) || a.c.pad_m >= 0 ||
+                tiles + (int64_t)K * tpr > (1LL << 29))
+                flush();
+            a.off[count] = f.off + o;
+            a.n[count] = pn;
+            if (is_pad)
+                a.c.pad_m = count;
+            else
+                for (int r = 0; r < K; ++r) a.src[count * K + r] = static_cast<const char*>(f.ptr[r]) + o * elem_bytes;
+            a.tpr[count] = (int32_t)tpr;
+            a.tile0[count] = (int32_t)tiles;
+            tiles += (int64_t)K * tpr;
+            ++count;
         }
-        if (is_pad) pad = count;
-        batch += (int64_t)K * tiles_of(entries[i].n * elem_bytes, kFlatTileBytes);
-        ++count;
     }
-    return flush();
+    flush();
 }
+
+}  // namespace
+
+struct FlatPlan {
+    std::vector<FlatArgs> launches;  // argument launches, or
+    bool staged = false;             // one launch over the table staged in the workspace
+    FlatWsArgs wsa;
+    int64_t ws_tiles = 0;
+    std::vector<uint8_t> image;
+    int elem_bytes = 2;
+};
+
+FlatPlan* flat_plan_build(int K, const FragEntry* entries, int n_entries, const MutPtrs& buckets,
+                          int elem_bytes, void* ws) {
+    FlatPlan* plan = new (std::nothrow) FlatPlan();
+    if (!plan) return nullptr;
+    try {
+        FlatCommon c;
+        c.bucket = buckets;
+        c.K = K;
+        c.pad_m = -1;
+        plan->elem_bytes = elem_bytes;
+        cut_args(c, entries, n_entries, elem_bytes, &plan->launches);
+        if (ws != nullptr && plan->launches.size() > 1) {
+            plan->launches.clear();
+            plan->staged = true;
+            const FlatLayout L(K, n_entries);
+            plan->image.assign(L.bytes, 0);
+            uint8_t* base = plan->image.data();
+            int64_t* tile0 = reinterpret_cast<int64_t*>(base + L.tile0);
+            int64_t* tpr = reinterpret_cast<int64_t*>(base + L.tpr);
+            int64_t* en = reinterpret_cast<int64_t*>(base + L.ent);
+            uint64_t* src = reinterpret_cast<uint64_t*>(base + L.src);
+            int64_t tiles = 0;
+            for (int m = 0; m < n_entries; ++m) {
+                const FragEntry& f = entries[m];
+                if (f.ptr[0] == nullptr) c.pad_m = m;
+                tile0[m] = tiles;
+                tpr[m] = tiles_of(f.n * elem_bytes, kFlatTileBytes);
+                en[2 * m] = f.off;
+                en[2 * m + 1] = f.n;
+                for (int r = 0; r < K; ++r) src[(size_t)m * K + r] = (uint64_t)(uintptr_t)f.ptr[r];
+                tiles += (int64_t)K * tpr[m];
+            }
+            tile0[n_entries] = tiles;
+            const uintptr_t w = (uintptr_t)ws;
+            plan->wsa = FlatWsArgs{};
+            plan->wsa.c = c;
+            plan->wsa.tile0 = w + L.tile0;
+            plan->wsa.tpr = w + L.tpr;
+            plan->wsa.ent = w + L.ent;
+            plan->wsa.src = w + L.src;
+            plan->wsa.nent = n_entries;
+            plan->ws_tiles = tiles;
+        }
+    } catch (...) {
+        delete plan;
+        return nullptr;
+    }
+    return plan;
+}
+
+size_t flat_plan_table_bytes(const FlatPlan* plan) { return plan->staged ? plan->image.size() : 0; }
+const void* flat_plan_table_image(const FlatPlan* plan) { return plan->image.data(); }
+int flat_plan_launch_count(const FlatPlan* plan) {
+    return plan->staged ? (plan->ws_tiles > 0 ? 1 : 0) : (int)plan->launches.size();
+}
+
+hipError_t flat_plan_launch(const FlatPlan* plan, hipStream_t stream) {
+    if (plan->staged) {
+        if (plan->ws_tiles == 0) return hipSuccess;
+        const int gx = grid_for(plan->ws_tiles);  // one block per tile, striding beyond the cap
+        if (plan->elem_bytes == 2)
+            hipLaunchKernelGGL((flatten_ws_kernel<uint16_t>), dim3(gx), dim3(kThreads), 0, stream, plan->wsa);
+        else
+            hipLaunchKernelGGL((flatten_ws_kernel<uint32_t>), dim3(gx), dim3(kThreads), 0, stream, plan->wsa);
+        return hipGetLastError();
+    }
+    for (const FlatArgs& a : plan->launches) {
+        const int gx = grid_for(a.tile0[a.nent]);  // one block per tile
+        if (plan->elem_bytes == 2)
+            hipLaunchKernelGGL((flatten_kernel<uint16_t>), dim3(gx), dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((flatten_kernel<uint32_t>), dim3(gx), dim3(kThreads), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+void flat_plan_free(FlatPlan* plan) { delete plan; }
 
 }  // namespace zr

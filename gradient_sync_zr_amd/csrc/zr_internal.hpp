@@ -61,19 +61,84 @@ hipError_t launch_allreduce_fused(int K, const ConstPtrs& in, const MutPtrs& out
 // segs: up to kAgSegsPerLaunch segments per call.
 hipError_t launch_all_gather(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype dt,
                              const zr_seg* segs, int n_segs, int shift, hipStream_t stream);
+// Any number of segments in one launch, their table staged to `ws` (at least
+// ag_table_bytes(n_segs) bytes) on `stream` first.
+hipError_t launch_all_gather_ws(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype dt,
+                                const zr_seg* segs, int n_segs, int shift, void* ws,
+                                hipStream_t stream);
 
-// Discrete reduce-scatter over fragment entries (any count): the launches'
-// argument blocks are built once into a plan and can be launched many times.
-// rsf_plan_build returns NULL when host memory runs out.
+// Device descriptor tables. A call whose fragment (or segment) table does not
+// fit one kernel-argument block either goes out as several argument launches
+// or, given a workspace, as one launch that reads the whole table from it.
+// The host builds the table as a byte image whose internal pointers already
+// hold the workspace's device addresses; staging copies the image there.
+// Every table is laid out in 8-byte words (sizes below in bytes).
+constexpr size_t kWsAlign = 256;
+
+// Discrete reduce-scatter: first tiles int64[nseg + 1], segment records
+// int32[3 * nseg] (entry, chunk, head), entry records int64[2 * nent]
+// (offset, size), rank pointers [K * nent].
+struct RsfLayout {
+    size_t tile0, seg, ent, ptr, bytes;
+    RsfLayout(int K, int64_t nent, int64_t nseg) {
+        tile0 = 0;
+        seg = tile0 + 8 * (size_t)(nseg + 1);
+        ent = seg + ((12 * (size_t)nseg + 7) & ~(size_t)7);
+        ptr = ent + 16 * (size_t)nent;
+        bytes = ptr + 8 * (size_t)K * (size_t)nent;
+    }
+};
+// Flatten: first tiles int64[nent + 1], tiles per rank int64[nent], entry
+// records int64[2 * nent] (offset, size), source pointers [K * nent].
+struct FlatLayout {
+    size_t tile0, tpr, ent, src, bytes;
+    FlatLayout(int K, int64_t nent) {
+        tile0 = 0;
+        tpr = tile0 + 8 * (size_t)(nent + 1);
+        ent = tpr + 8 * (size_t)nent;
+        src = ent + 16 * (size_t)nent;
+        bytes = src + 8 * (size_t)K * (size_t)nent;
+    }
+};
+// All-gather: first tiles int64[nseg + 1], then kAgSegBytes per segment record.
+constexpr size_t kAgSegBytes = 48;
+inline size_t rsf_table_bytes(int K, int64_t n_entries, int64_t n_segs) {
+    return RsfLayout(K, n_entries, n_segs).bytes;
+}
+inline size_t flatten_table_bytes(int K, int64_t n_entries) { return FlatLayout(K, n_entries).bytes; }
+inline size_t ag_table_bytes(int64_t n_segs) { return 8 * (size_t)(n_segs + 1) + kAgSegBytes * (size_t)n_segs; }
+// Copies a table image to the workspace: asynchronously on `stream`, or with a
+// blocking copy when `stream_order` is false (plan creation).
+hipError_t stage_table(void* ws, const void* image, size_t bytes, hipStream_t stream, bool stream_order);
+
+// Discrete reduce-scatter over fragment entries (any count): a plan holds the
+// launches' argument blocks, built once and launched many times. With `ws`
+// non-null and more than one argument launch needed, the plan instead holds
+// one launch whose table image (table_bytes, host copy in table_image) is to
+// be staged to `ws` before the launch. rsf_plan_build returns NULL when host
+// memory runs out.
 struct RsfPlan;
 RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t N, zr_dtype in_dt,
-                        const MutPtrs& out, zr_dtype out_dt, int shift, int flags, zr_order order);
+                        const MutPtrs& out, zr_dtype out_dt, int shift, int flags, zr_order order,
+                        void* ws);
+size_t rsf_plan_table_bytes(const RsfPlan* plan);   // 0: argument launches only
+const void* rsf_plan_table_image(const RsfPlan* plan);
+int rsf_plan_launch_count(const RsfPlan* plan);
 hipError_t rsf_plan_launch(const RsfPlan* plan, hipStream_t stream);
 void rsf_plan_free(RsfPlan* plan);
 
-// Any number of entries, each with at most 2^28 / K tiles of 4 KiB per
-// rank; launched kFlatEntriesPerLaunch (or fewer) at a time.
-hipError_t launch_flatten(int K, const FragEntry* entries, int n_entries, const MutPtrs& buckets,
-                          int elem_bytes, hipStream_t stream);
+// Bucket flatten over fragment entries, planned the same way: argument
+// launches of kFlatEntriesPerLaunch (or fewer) entries, an entry of more than
+// 2^28 / K tiles of 4 KiB per rank cut into pieces of that many (so tile
+// numbers fit 32 bits), or, with `ws`, one launch over a staged table of the
+// uncut entries.
+struct FlatPlan;
+FlatPlan* flat_plan_build(int K, const FragEntry* entries, int n_entries, const MutPtrs& buckets,
+                          int elem_bytes, void* ws);
+size_t flat_plan_table_bytes(const FlatPlan* plan);
+const void* flat_plan_table_image(const FlatPlan* plan);
+int flat_plan_launch_count(const FlatPlan* plan);
+hipError_t flat_plan_launch(const FlatPlan* plan, hipStream_t stream);
+void flat_plan_free(FlatPlan* plan);
 
 }  // namespace zr

@@ -16,13 +16,19 @@
 // lands contiguously in one holder's partition, so it is reduced like a chunk
 // of the contiguous kernel: the same 4-wave x S-slice x 256-element tiles of
 // lane-owned quads, every rank's loads in flight before the ring-order adds,
-// non-temporal streams. A launch carries up to 32 fragments' rank pointers
-// (the padding entry, which has none, takes a spare slot after them), their
-// segments and each segment's first tile in its kernel arguments. The grid
-// has one block per tile of the launch, in order, so blocks stay balanced
-// however unequal the fragments are, and the blocks in flight work on one
-// compact window of memory (a persistent grid striding over the tiles ran
-// 7-15% slower). A segment whose rank buffers share one quad phase starts
+// non-temporal streams. The descriptor table (each fragment's rank pointers,
+// offset and size; each segment's fragment, chunk, head and first tile)
+// rides in the kernel arguments when it fits one argument block: up to 32
+// fragments and 256 rank pointers (the padding entry, which has none, takes a
+// spare slot after them) and 96 segments, more going out as further
+// launches. Given a workspace, a larger table is staged there instead and one
+// launch covers every fragment, however many there are (the pages' point in
+// bucketing: one operation per bucket, not one per parameter, section 3.1);
+// the kernel then reads it with scalar loads and finds a tile's segment with
+// a wave-wide search. The grid has one block per tile of the launch, in
+// order, so blocks stay balanced however unequal the fragments are, and the
+// blocks in flight work on one compact window of memory (a persistent grid
+// striding over the tiles ran 7-15% slower). A segment whose rank buffers share one quad phase starts
 // its vector tiles at a 128-byte line of rank j whose output lies less than
 // a line after a 16 KiB boundary of the partition, as the contiguous kernel
 // does: the first tile also folds the head before it (as quads, and its
@@ -32,6 +38,8 @@
 // element by element, 1024 elements per tile. The padding entry has null
 // pointers, starts its tiles on a 16 KiB boundary of the partition and
 // writes +0 (old + 0 when accumulating).
+#include <climits>
+#include <cstring>
 #include <new>
 #include <vector>
 
@@ -44,53 +52,115 @@ namespace {
 // more for the padding entry, which has none.
 constexpr int kRsfSlots = kRsfEntriesPerLaunch + 1;
 
+// Fields every launch carries, whichever table it reads.
+struct RsfCommon {
+    MutPtrs out;
+    int64_t C;
+    int K, shift, accumulate;
+    int pad_m;  // the padding entry (writes +0), -1: none
+    float inv_k, kf;
+};
+
+// A launch whose table rides in its kernel arguments.
 struct RsfArgs {
+    RsfCommon c;
     const void* ptr[kRsfPtrsPerLaunch];    // entry-major: ptr[m * K + r]
     int64_t off[kRsfSlots];                // virtual-bucket offset of entry m
     int64_t n[kRsfSlots];                  // elements of entry m
-    MutPtrs out;
     int32_t tile0[kRsfSegsPerLaunch + 1];  // first tile of segment s; tile0[nseg] = all tiles
     uint8_t seg_m[kRsfSegsPerLaunch];      // entry of segment s
     uint8_t seg_j[kRsfSegsPerLaunch];      // chunk of segment s
     int16_t seg_head[kRsfSegsPerLaunch];   // vector tiles start at this offset; -1: element-wise
-    int64_t C;
-    int K, shift, accumulate, nseg;
-    int pad_m;                             // the padding entry (writes +0), -1: none
-    float inv_k, kf;
+    int nseg;
 };
 static_assert(sizeof(RsfArgs) <= 4096, "discrete reduce-scatter arguments exceed 4 KB");
+
+// A launch whose table is staged in a workspace: device addresses of its
+// arrays (the layout of rsf_table_bytes).
+struct RsfWsArgs {
+    RsfCommon c;
+    uint64_t tile0;  // int64_t[nseg + 1]: first tile of segment s; tile0[nseg] = all tiles
+    uint64_t seg;    // int32_t[3 * nseg]: entry, chunk and head of segment s at 3s
+    uint64_t ent;    // int64_t[2 * nent]: virtual-bucket offset and size of entry m at 2m
+    uint64_t ptr;    // const void*[K * nent], entry-major (null for the padding entry)
+    int64_t nseg;
+};
+
+// One segment's record and one entry's record.
+struct SegRec {
+    int m, j, h;  // entry, chunk, head
+};
+struct EntRec {
+    int64_t off, n;
+};
+
+// The two table sources behind one interface.
+struct ArgTable {
+    using Index = int;  // argument launches keep tile numbers within 32 bits
+    const RsfArgs& a;
+    __device__ __forceinline__ int64_t total() const { return a.tile0[a.nseg]; }
+    // a block's tiles only grow, so its last segment is a lower bound
+    __device__ __forceinline__ int64_t find(int64_t from, int64_t t) const {
+        return find_slot(a.tile0, a.nseg, (int)from, (int)t);
+    }
+    __device__ __forceinline__ int64_t first(int64_t s) const { return a.tile0[s]; }
+    __device__ __forceinline__ SegRec seg(int64_t s) const { return {a.seg_m[s], a.seg_j[s], a.seg_head[s]}; }
+    __device__ __forceinline__ EntRec ent(int m) const { return {a.off[m], a.n[m]}; }
+    __device__ __forceinline__ const void* ptr(int m, int K, int r) const { return a.ptr[m * K + r]; }
+};
+
+struct WsTable {
+    using Index = int64_t;
+    cptr<int64_t> tile0;
+    cptr<int32_t> sg;
+    cptr<int64_t> en;
+    cptr<const void*> ptrs;
+    int64_t nseg;
+    __device__ __forceinline__ explicit WsTable(const RsfWsArgs& a)
+        : tile0(table_at<int64_t>(a.tile0)), sg(table_at<int32_t>(a.seg)), en(table_at<int64_t>(a.ent)),
+          ptrs(table_at<const void*>(a.ptr)), nseg(a.nseg) {}
+    __device__ __forceinline__ int64_t total() const { return tile0[nseg]; }
+    __device__ __forceinline__ int64_t find(int64_t, int64_t t) const { return find_slot64(tile0, nseg, t); }
+    __device__ __forceinline__ int64_t first(int64_t s) const { return tile0[s]; }
+    __device__ __forceinline__ SegRec seg(int64_t s) const { return {sg[3 * s], sg[3 * s + 1], sg[3 * s + 2]}; }
+    __device__ __forceinline__ EntRec ent(int m) const { return {en[2 * (int64_t)m], en[2 * (int64_t)m + 1]}; }
+    __device__ __forceinline__ const void* ptr(int m, int K, int r) const { return ptrs[(int64_t)m * K + r]; }
+};
 
 // Elements per tile of a segment that folds element by element (4 per thread).
 constexpr int64_t kElemTile = kThreads * 4;
 
-template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
-__global__ void __launch_bounds__(kThreads) rsf_kernel(const RsfArgs a) {
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S, typename Tab>
+__device__ __forceinline__ void rsf_body(const RsfCommon& c, const Tab& tab) {
     constexpr int64_t T = kRsTileOf<S>;
     constexpr bool kStatic = ORDER != kFree && KS > 0 && KS <= 8;
-    const int K = KS > 0 ? KS : a.K;
+    const int K = KS > 0 ? KS : c.K;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int total = a.tile0[a.nseg];
-    int s = 0;
-    for (int t = blockIdx.x; t < total; t += gridDim.x) {
-        s = find_slot(a.tile0, a.nseg, s, t);  // a block's tiles only grow: segments in order
-        const int m = a.seg_m[s], j = a.seg_j[s];
-        const int64_t jc = (int64_t)j * a.C;
-        const int64_t f0 = a.off[m], f1 = a.off[m] + a.n[m];
+    using Index = typename Tab::Index;
+    const Index total = (Index)tab.total();
+    Index s = 0;
+    for (Index t = blockIdx.x; t < total; t += gridDim.x) {
+        s = (Index)tab.find(s, t);
+        const SegRec sr = tab.seg(s);
+        const int m = sr.m, j = sr.j;
+        const EntRec er = tab.ent(m);
+        const int64_t jc = (int64_t)j * c.C;
+        const int64_t f0 = er.off, f1 = er.off + er.n;
         const int64_t lo = f0 > jc ? f0 : jc;
-        const int64_t hi = f1 < jc + a.C ? f1 : jc + a.C;
+        const int64_t hi = f1 < jc + c.C ? f1 : jc + c.C;
         const int64_t l_lo = lo - f0, len = hi - lo;  // fragment-local start, length
-        TOut* outp = static_cast<TOut*>(a.out.p[wrap(j - a.shift + K, K)]) + (lo - jc);
-        auto ptr = [&](int r) __attribute__((always_inline)) { return a.ptr[m * K + r]; };
-        const bool pad = m == a.pad_m;
-        const int64_t tt = t - a.tile0[s];
-        const int64_t h = a.seg_head[s];
+        TOut* outp = static_cast<TOut*>(c.out.p[wrap(j - c.shift + K, K)]) + (lo - jc);
+        auto ptr = [=](int r) __attribute__((always_inline)) { return tab.ptr(m, K, r); };
+        const bool pad = m == c.pad_m;
+        const int64_t tt = t - tab.first(s);
+        const int64_t h = sr.h;
 
         // one output element (segment offset o), folded element-wise
         auto elem = [&](int64_t o) __attribute__((always_inline)) {
             float v = 0.0f;
-            if (!pad) v = average<AVG>(fold_elem<TIn, KS, ORDER>(ptr, K, j, l_lo + o), a.inv_k, a.kf);
-            if (a.accumulate) v = __fadd_rn(load_elem(outp + o), v);
+            if (!pad) v = average<AVG>(fold_elem<TIn, KS, ORDER>(ptr, K, j, l_lo + o), c.inv_k, c.kf);
+            if (c.accumulate) v = __fadd_rn(load_elem(outp + o), v);
             store_elem(outp + o, v);
         };
         if (h < 0) {
@@ -108,10 +178,10 @@ __global__ void __launch_bounds__(kThreads) rsf_kernel(const RsfArgs a) {
 #pragma unroll
                 for (int k = 0; k < SS; ++k)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[k][e] = average<AVG>(acc[k][e], a.inv_k, a.kf);
+                    for (int e = 0; e < 4; ++e) acc[k][e] = average<AVG>(acc[k][e], c.inv_k, c.kf);
             }
             if (out_quad) {
-                if (a.accumulate) {
+                if (c.accumulate) {
 #pragma unroll
                     for (int k = 0; k < SS; ++k) {
                         float old[4];
@@ -129,7 +199,7 @@ __global__ void __launch_bounds__(kThreads) rsf_kernel(const RsfArgs a) {
                     for (int e = 0; e < 4; ++e) {
                         TOut* o = outp + o0 + 256 * k + e;
                         float v = acc[k][e];
-                        if (a.accumulate) v = __fadd_rn(load_elem(o), v);
+                        if (c.accumulate) v = __fadd_rn(load_elem(o), v);
                         store_elem(o, v);
                     }
             }
@@ -188,34 +258,61 @@ __global__ void __launch_bounds__(kThreads) rsf_kernel(const RsfArgs a) {
 }
 
 template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
+__global__ void __launch_bounds__(kThreads) rsf_kernel(const RsfArgs a) {
+    rsf_body<TIn, TOut, KS, AVG, ORDER, NT, S>(a.c, ArgTable{a});
+}
+
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
+__global__ void __launch_bounds__(kThreads) rsf_ws_kernel(const RsfWsArgs a) {
+    rsf_body<TIn, TOut, KS, AVG, ORDER, NT, S>(a.c, WsTable(a));
+}
+
+using LaunchFn = hipError_t (*)(const RsfArgs&, hipStream_t);
+using WsLaunchFn = hipError_t (*)(const RsfWsArgs&, int64_t, hipStream_t);
+
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
 hipError_t launch_t(const RsfArgs& a, hipStream_t stream) {
-    const int total = a.tile0[a.nseg];
-    const int gx = grid_for(total);  // one block per tile
+    const int gx = grid_for(a.tile0[a.nseg]);  // one block per tile
     hipLaunchKernelGGL((rsf_kernel<TIn, TOut, KS, AVG, ORDER, NT, S>), dim3(gx), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
 }
 
-using LaunchFn = hipError_t (*)(const RsfArgs&, hipStream_t);
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
+hipError_t launch_ws_t(const RsfWsArgs& a, int64_t tiles, hipStream_t stream) {
+    const int gx = grid_for(tiles);  // one block per tile, striding beyond the cap
+    hipLaunchKernelGGL((rsf_ws_kernel<TIn, TOut, KS, AVG, ORDER, NT, S>), dim3(gx), dim3(kThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+struct Fns {
+    LaunchFn args;
+    WsLaunchFn ws;
+};
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
+constexpr Fns fns() {
+    return {&launch_t<TIn, TOut, KS, AVG, ORDER, NT, S>, &launch_ws_t<TIn, TOut, KS, AVG, ORDER, NT, S>};
+}
 
 // Ring and wire order at K = 8 specialised, the rest generic (batches of
 // eight ranks in flight); fp32 input makes the wire order the ring order.
 // Small plans in the ring order use one slice per wave.
 template <typename TIn, typename TOut, int AVG>
-LaunchFn pick_k(int K, int order, bool small) {
+Fns pick_k(int K, int order, bool small) {
     constexpr int S = kSlices<TIn, TOut>;
     constexpr bool NT = kRsNontemporal;
-    if (order == kFree) return &launch_t<TIn, TOut, 0, AVG, kFree, NT, S>;
+    if (order == kFree) return fns<TIn, TOut, 0, AVG, kFree, NT, S>();
     if (order == kWire && sizeof(TIn) == 2) {
-        if (K == 8) return &launch_t<TIn, TOut, 8, AVG, kWire, NT, S>;
-        return &launch_t<TIn, TOut, 0, AVG, kWire, NT, S>;
+        if (K == 8) return fns<TIn, TOut, 8, AVG, kWire, NT, S>();
+        return fns<TIn, TOut, 0, AVG, kWire, NT, S>();
     }
-    if (K == 8) return small ? &launch_t<TIn, TOut, 8, AVG, kRing, NT, 1> : &launch_t<TIn, TOut, 8, AVG, kRing, NT, S>;
-    return small ? &launch_t<TIn, TOut, 0, AVG, kRing, NT, 1> : &launch_t<TIn, TOut, 0, AVG, kRing, NT, S>;
+    if (K == 8) return small ? fns<TIn, TOut, 8, AVG, kRing, NT, 1>() : fns<TIn, TOut, 8, AVG, kRing, NT, S>();
+    return small ? fns<TIn, TOut, 0, AVG, kRing, NT, 1>() : fns<TIn, TOut, 0, AVG, kRing, NT, S>();
 }
 
 template <typename TIn, typename TOut>
-LaunchFn pick_avg(int K, int avg, int order, bool small) {
+Fns pick_avg(int K, int avg, int order, bool small) {
     switch (avg) {
         case 1: return pick_k<TIn, TOut, 1>(K, order, small);
         case 2: return pick_k<TIn, TOut, 2>(K, order, small);
@@ -247,21 +344,67 @@ int16_t segment_head(const uintptr_t* addr, int K, int j, uintptr_t es, uintptr_
     return (int16_t)(b + ((to_line - b) % line + line) % line);
 }
 
-// Cuts the entries into launches: each fills one argument block with up to
-// kRsfEntriesPerLaunch fragments (and kRsfPtrsPerLaunch rank pointers), the
-// padding entry if it comes next (it takes no pointers), and the segments
-// they form with the chunks.
+// One (fragment, chunk) segment of the virtual bucket.
+struct SegDesc {
+    int m;       // entry
+    int j;       // chunk
+    int head;    // vector tiles start here; -1: element-wise
+    int64_t tiles;
+};
+
+// Every entry's segments in order (entry ei's are [first[ei], first[ei+1])),
+// with their heads and tile counts for vector tiles of T elements.
 template <typename TIn, typename TOut>
-void build_typed(RsfArgs& a, const FragEntry* entries, int n_entries, int64_t T,
-                 std::vector<RsfArgs>* out) {
-    const int K = a.K;
-    const int64_t C = a.C;
+void segments_of(const RsfCommon& c, const FragEntry* entries, int n_entries, int64_t T,
+                 std::vector<SegDesc>* segs, std::vector<int64_t>* first) {
+    const int K = c.K;
+    const int64_t C = c.C;
+    segs->clear();
+    first->assign(1, 0);
+    for (int ei = 0; ei < n_entries; ++ei) {
+        const FragEntry& f = entries[ei];
+        const bool pad = f.ptr[0] == nullptr;
+        const int j0 = (int)(f.off / C), j1 = (int)((f.off + f.n - 1) / C);
+        for (int j = j0; j <= j1; ++j) {
+            const int64_t jc = (int64_t)j * C;
+            const int64_t lo = f.off > jc ? f.off : jc;
+            const int64_t hi = (f.off + f.n) < jc + C ? (f.off + f.n) : jc + C;
+            const int64_t len = hi - lo;
+            const int q = ((j - c.shift) % K + K) % K;  // holder
+            const uintptr_t o = (uintptr_t)c.out.p[q] + (uintptr_t)(lo - jc) * sizeof(TOut);
+            int h;
+            if (pad) {
+                // no input: align the partition side to its 16 KiB blocks
+                h = (int)to_block(o, sizeof(TOut));
+            } else {
+                uintptr_t addr[kMaxRanks];
+                for (int r = 0; r < K; ++r)
+                    addr[r] = (uintptr_t)f.ptr[r] + (uintptr_t)(lo - f.off) * sizeof(TIn);
+                h = segment_head(addr, K, j, sizeof(TIn), o, sizeof(TOut));
+            }
+            const int64_t tiles = h < 0 ? (len + kElemTile - 1) / kElemTile : (len > h ? (len - h + T - 1) / T : 1);
+            segs->push_back(SegDesc{ei, j, h, tiles});
+        }
+        first->push_back((int64_t)segs->size());
+    }
+}
+
+// Cuts the entries into argument launches: each fills one argument block with
+// up to kRsfEntriesPerLaunch fragments (and kRsfPtrsPerLaunch rank pointers),
+// the padding entry if it comes next (it takes no pointers), and the segments
+// they form with the chunks, keeping tile numbers within 32 bits.
+void cut_args(const RsfCommon& c, const FragEntry* entries, int n_entries,
+              const std::vector<SegDesc>& segs, const std::vector<int64_t>& first,
+              std::vector<RsfArgs>* out) {
+    const int K = c.K;
     const int max_entries = (kRsfPtrsPerLaunch / K) < kRsfEntriesPerLaunch ? (kRsfPtrsPerLaunch / K)
                                                                          : kRsfEntriesPerLaunch;
+    RsfArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.c = c;
+    a.c.pad_m = -1;
     int m = 0;
     int64_t tiles = 0;
-    a.nseg = 0;
-    a.pad_m = -1;
     auto flush = [&]() {
         if (m == 0) return;
         a.tile0[a.nseg] = (int32_t)tiles;
@@ -269,86 +412,126 @@ void build_typed(RsfArgs& a, const FragEntry* entries, int n_entries, int64_t T,
         m = 0;
         tiles = 0;
         a.nseg = 0;
-        a.pad_m = -1;
+        a.c.pad_m = -1;
     };
     for (int ei = 0; ei < n_entries; ++ei) {
         const FragEntry& f = entries[ei];
         const bool pad = f.ptr[0] == nullptr;
-        const int j0 = (int)(f.off / C), j1 = (int)((f.off + f.n - 1) / C);
-        if (m == (pad ? max_entries + 1 : max_entries) || a.pad_m >= 0 ||
-            a.nseg + (j1 - j0 + 1) > kRsfSegsPerLaunch)
+        const int64_t s0 = first[ei], s1 = first[ei + 1];
+        int64_t et = 0;
+        for (int64_t s = s0; s < s1; ++s) et += segs[s].tiles;
+        if (m == (pad ? max_entries + 1 : max_entries) || a.c.pad_m >= 0 ||
+            a.nseg + (s1 - s0) > kRsfSegsPerLaunch || tiles + et > INT32_MAX / 2)
             flush();
         a.off[m] = f.off;
         a.n[m] = f.n;
         if (pad)
-            a.pad_m = m;
+            a.c.pad_m = m;
         else
             for (int r = 0; r < K; ++r) a.ptr[m * K + r] = f.ptr[r];
-        for (int j = j0; j <= j1; ++j) {
-            const int64_t jc = (int64_t)j * C;
-            const int64_t lo = f.off > jc ? f.off : jc;
-            const int64_t hi = (f.off + f.n) < jc + C ? (f.off + f.n) : jc + C;
-            const int64_t len = hi - lo;
-            uintptr_t addr[kMaxRanks];
-            int16_t h;
-            const int q = ((j - a.shift) % K + K) % K;  // holder
-            const uintptr_t o = (uintptr_t)a.out.p[q] + (uintptr_t)(lo - jc) * sizeof(TOut);
-            if (pad) {
-                // no input: align the partition side to its 16 KiB blocks
-                h = (int16_t)to_block(o, sizeof(TOut));
-            } else {
-                for (int r = 0; r < K; ++r)
-                    addr[r] = (uintptr_t)f.ptr[r] + (uintptr_t)(lo - f.off) * sizeof(TIn);
-                h = segment_head(addr, K, j, sizeof(TIn), o, sizeof(TOut));
-            }
-            const int s = a.nseg++;
-            a.seg_m[s] = (uint8_t)m;
-            a.seg_j[s] = (uint8_t)j;
-            a.seg_head[s] = h;
-            a.tile0[s] = (int32_t)tiles;
-            tiles += h < 0 ? (len + kElemTile - 1) / kElemTile : (len > h ? (len - h + T - 1) / T : 1);
+        for (int64_t s = s0; s < s1; ++s) {
+            const int d = a.nseg++;
+            a.seg_m[d] = (uint8_t)m;
+            a.seg_j[d] = (uint8_t)segs[s].j;
+            a.seg_head[d] = (int16_t)segs[s].head;
+            a.tile0[d] = (int32_t)tiles;
+            tiles += segs[s].tiles;
         }
         ++m;
-        if (tiles > INT32_MAX / 2) flush();
     }
     flush();
+}
+
+// The staged table's image for workspace `ws` (device addresses filled in).
+void build_image(const RsfCommon& c, const FragEntry* entries, int n_entries,
+                 const std::vector<SegDesc>& segs, uintptr_t ws, RsfWsArgs* wa, int64_t* tiles,
+                 std::vector<uint8_t>* image) {
+    const int K = c.K;
+    const RsfLayout L(K, n_entries, (int64_t)segs.size());
+    image->assign(L.bytes, 0);
+    uint8_t* base = image->data();
+    int64_t* tile0 = reinterpret_cast<int64_t*>(base + L.tile0);
+    int32_t* sg = reinterpret_cast<int32_t*>(base + L.seg);
+    int64_t* en = reinterpret_cast<int64_t*>(base + L.ent);
+    uint64_t* pt = reinterpret_cast<uint64_t*>(base + L.ptr);
+    *wa = RsfWsArgs{};
+    wa->c = c;
+    wa->c.pad_m = -1;
+    for (int m = 0; m < n_entries; ++m) {
+        en[2 * m] = entries[m].off;
+        en[2 * m + 1] = entries[m].n;
+        if (entries[m].ptr[0] == nullptr) wa->c.pad_m = m;
+        for (int r = 0; r < K; ++r) pt[(size_t)m * K + r] = (uint64_t)(uintptr_t)entries[m].ptr[r];
+    }
+    int64_t t = 0;
+    for (size_t s = 0; s < segs.size(); ++s) {
+        tile0[s] = t;
+        sg[3 * s] = segs[s].m;
+        sg[3 * s + 1] = segs[s].j;
+        sg[3 * s + 2] = segs[s].head;
+        t += segs[s].tiles;
+    }
+    tile0[segs.size()] = t;
+    *tiles = t;
+    wa->tile0 = ws + L.tile0;
+    wa->seg = ws + L.seg;
+    wa->ent = ws + L.ent;
+    wa->ptr = ws + L.ptr;
+    wa->nseg = (int64_t)segs.size();
 }
 
 }  // namespace
 
 struct RsfPlan {
-    std::vector<RsfArgs> launches;
-    LaunchFn fn = nullptr;
+    std::vector<RsfArgs> launches;  // argument launches, or
+    bool staged = false;            // one launch over the table staged in the workspace
+    RsfWsArgs wsa;
+    int64_t ws_tiles = 0;
+    std::vector<uint8_t> image;
+    Fns fn{nullptr, nullptr};
 };
 
 RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t N, zr_dtype in_dt,
-                        const MutPtrs& out, zr_dtype out_dt, int shift, int flags, zr_order order) {
+                        const MutPtrs& out, zr_dtype out_dt, int shift, int flags, zr_order order,
+                        void* ws) {
     RsfPlan* plan = new (std::nothrow) RsfPlan();
     if (!plan) return nullptr;
-    RsfArgs a;
-    a.out = out;
-    a.K = K;
-    a.C = (N + K - 1) / K;
-    a.shift = shift;
-    a.accumulate = (flags & ZR_ACCUMULATE) ? 1 : 0;
-    a.nseg = 0;
-    a.inv_k = 1.0f / (float)K;
-    a.kf = (float)K;
+    RsfCommon c;
+    c.out = out;
+    c.K = K;
+    c.C = (N + K - 1) / K;
+    c.shift = shift;
+    c.accumulate = (flags & ZR_ACCUMULATE) ? 1 : 0;
+    c.pad_m = -1;
+    c.inv_k = 1.0f / (float)K;
+    c.kf = (float)K;
     const bool pow2 = (K & (K - 1)) == 0;
     const int avg = !(flags & ZR_AVERAGE) ? 0 : (pow2 ? 1 : 2);
     const int ord = order == ZR_ORDER_FREE ? kFree : (order == ZR_ORDER_RING_WIRE ? kWire : kRing);
-    // the tiles at full size decide the tile: plans whose launches would give
-    // fewer than two tiles per CU (ring order) use one slice per wave
+    // the tiles at full size decide the tile: launches that would give fewer
+    // than two tiles per CU (ring order) use one slice per wave
     auto build = [&](auto tin, auto tout) {
         using TIn = decltype(tin);
         using TOut = decltype(tout);
-        build_typed<TIn, TOut>(a, entries, n_entries, kRsTile<TIn, TOut>, &plan->launches);
+        std::vector<SegDesc> segs;
+        std::vector<int64_t> first;
+        segments_of<TIn, TOut>(c, entries, n_entries, kRsTile<TIn, TOut>, &segs, &first);
+        cut_args(c, entries, n_entries, segs, first, &plan->launches);
+        plan->staged = ws != nullptr && plan->launches.size() > 1;
         int64_t most = 0;
-        for (const RsfArgs& l : plan->launches) most = most > l.tile0[l.nseg] ? most : l.tile0[l.nseg];
+        if (plan->staged) {
+            for (const SegDesc& d : segs) most += d.tiles;
+        } else {
+            for (const RsfArgs& l : plan->launches) most = most > l.tile0[l.nseg] ? most : l.tile0[l.nseg];
+        }
         const bool small = ord == kRing && most < 2LL * device_cu_count();
-        if (small) {
+        if (small) segments_of<TIn, TOut>(c, entries, n_entries, kRsTileOf<1>, &segs, &first);
+        if (plan->staged) {
             plan->launches.clear();
-            build_typed<TIn, TOut>(a, entries, n_entries, kRsTileOf<1>, &plan->launches);
+            build_image(c, entries, n_entries, segs, (uintptr_t)ws, &plan->wsa, &plan->ws_tiles, &plan->image);
+        } else if (small) {
+            plan->launches.clear();
+            cut_args(c, entries, n_entries, segs, first, &plan->launches);
         }
         plan->fn = pick_avg<TIn, TOut>(K, avg, ord, small);
     };
@@ -368,9 +551,16 @@ RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t 
     return plan;
 }
 
+size_t rsf_plan_table_bytes(const RsfPlan* plan) { return plan->staged ? plan->image.size() : 0; }
+const void* rsf_plan_table_image(const RsfPlan* plan) { return plan->image.data(); }
+int rsf_plan_launch_count(const RsfPlan* plan) {
+    return plan->staged ? (plan->ws_tiles > 0 ? 1 : 0) : (int)plan->launches.size();
+}
+
 hipError_t rsf_plan_launch(const RsfPlan* plan, hipStream_t stream) {
+    if (plan->staged) return plan->ws_tiles > 0 ? plan->fn.ws(plan->wsa, plan->ws_tiles, stream) : hipSuccess;
     for (const RsfArgs& a : plan->launches) {
-        hipError_t e = plan->fn(a, stream);
+        hipError_t e = plan->fn.args(a, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

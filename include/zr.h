@@ -45,6 +45,21 @@
  *  - Streams are hipStream_t passed as void*; NULL is the null stream. Work
  *    is enqueued asynchronously [L14 2.1]; buffers must stay alive until
  *    the stream has finished with them. No call allocates device memory.
+ *  - Workspaces: the calls that take a table of fragments or segments
+ *    (flatten, discrete reduce-scatter and its plans, all-gather) carry up
+ *    to min(32, 256 / K) fragments (32 segments) per launch in kernel
+ *    arguments; a larger table goes out as several launches, or, when the
+ *    caller passes a device workspace (owned by the caller, at least
+ *    zr_workspace_bytes(K, n) bytes, 8-byte aligned, not overlapping any
+ *    buffer of the call), is copied into it and the whole call is one launch
+ *    [ZERO3 3.1: one operation per bucket, not one per parameter]. A one-shot
+ *    call copies its table with hipMemcpyAsync on `stream` from a host
+ *    buffer, which HIP performs synchronously for pageable memory (the call
+ *    returns once `stream` has reached the copy); a plan copies it once, at
+ *    creation. Calls on one stream may share a workspace; calls on different
+ *    streams that run at the same time must not. Under stream capture a
+ *    one-shot call never records the copy: it goes out as argument launches
+ *    (plans are created outside capture and may then be captured).
  *  - Errors: every call returns a zr_status; nothing throws or aborts across
  *    the boundary. Arguments are validated before any HIP call, so a bad
  *    argument enqueues nothing. zr_last_error() describes the last failure
@@ -67,8 +82,9 @@ typedef enum {
     ZR_ERR_ALIGN = 2,       /* pointer not aligned to its element size */
     ZR_ERR_ALIAS = 3,       /* overlapping buffers that must not overlap */
     ZR_ERR_UNSUPPORTED = 4, /* dtype or dtype pair not supported */
-    ZR_ERR_HIP = 5,         /* a HIP runtime call or launch failed */
-    ZR_ERR_NOMEM = 6        /* host memory ran out, or a caller-provided arena
+    ZR_ERR_WORKSPACE = 5,   /* workspace too small for the table it must hold */
+    ZR_ERR_HIP = 6,         /* a HIP runtime call or launch failed */
+    ZR_ERR_NOMEM = 7        /* host memory ran out, or a caller-provided arena
                                cannot hold what must be live */
 } zr_status;
 
@@ -119,6 +135,15 @@ const char* zr_last_error(void);
 /* Library version, major * 10000 + minor * 100 + patch. */
 int zr_version(void);
 
+/* Bytes of device workspace that let a flatten, discrete reduce-scatter (or
+ * its plan) with n fragments, or an all-gather with n segments, go out as one
+ * launch on K ranks; 0 when such a call always fits one kernel-argument block
+ * (n <= min(32, 256 / K)) and needs none. Host only. A multiple of 256; 0 for
+ * K outside [1, ZR_MAX_RANKS] or n < 0. (A flatten fragment larger than
+ * 2^28 / K tiles of 4 KiB per rank still takes more than one launch without
+ * a workspace.) */
+size_t zr_workspace_bytes(int K, int n);
+
 /*
  * Bucket flatten [ZERO3 3.2, 5.1]: on every rank r, fragment p is copied to
  * bucket_r at element offset n_0 + ... + n_{p-1}, then positions
@@ -134,14 +159,34 @@ int zr_version(void);
  *  padded_numel >= sum(numels); callers pad to a multiple of K for the
  *               reduce-scatter that follows
  *  dt           ZR_BF16 or ZR_FP32 (a bitwise copy either way)
+ *  workspace    NULL, or a device workspace of ws_bytes bytes (see the
+ *               conventions above): with more than min(32, 256 / K)
+ *               fragments the table is staged there and the flatten is one
+ *               launch; without it, min(32, 256 / K) fragments per launch
  * Buckets must not overlap each other or any fragment (ZR_ERR_ALIAS).
- * Fragment tables travel in kernel arguments: a launch carries up to 32
- * fragments' rank pointers (256 at most, so 4 fragments at K = 64) and the
- * zero padding when it comes next.
+ * ZR_ERR_WORKSPACE when the workspace is smaller than the table.
  */
 zr_status zr_flatten_bucket(int K, int n_frag, const void* const* frags, const int64_t* numels,
                             void* const* buckets, int64_t padded_numel, zr_dtype dt,
-                            void* stream);
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/* A bucket flatten prepared once and launched many times (fragments and
+ * buckets at fixed addresses): validation, entries and launch arguments are
+ * built at create; with a workspace (needed only above min(32, 256 / K)
+ * fragments) the table is copied into it at create, with a blocking copy,
+ * and every launch is one kernel. The plan keeps the buffers' addresses and
+ * the workspace, which it uses until destroyed. Arguments and results are
+ * those of zr_flatten_bucket. zr_flatten_plan_info reports the kernel
+ * launches per zr_flatten_plan_launch and the staged table's size (either
+ * pointer may be NULL). */
+typedef struct zr_flatten_plan zr_flatten_plan;
+
+zr_status zr_flatten_plan_create(int K, int n_frag, const void* const* frags, const int64_t* numels,
+                                 void* const* buckets, int64_t padded_numel, zr_dtype dt,
+                                 void* workspace, size_t ws_bytes, zr_flatten_plan** plan);
+zr_status zr_flatten_plan_launch(const zr_flatten_plan* plan, void* stream);
+zr_status zr_flatten_plan_info(const zr_flatten_plan* plan, int* launches, size_t* table_bytes);
+zr_status zr_flatten_plan_destroy(zr_flatten_plan* plan);
 
 /* Flags of the reduce-scatter calls. */
 #define ZR_AVERAGE 1    /* divide the sum by K */
@@ -188,16 +233,19 @@ zr_status zr_reduce_scatter_avg(int K, const void* const* in, zr_dtype in_dt, in
  *  numels    host array [n_frag]; N >= sum(numels); positions past the last
  *            fragment are zero padding
  *  out, flags, order, chunk_shift: as zr_reduce_scatter_avg
+ *  workspace NULL, or a device workspace of ws_bytes bytes (see the
+ *            conventions above): with more than min(32, 256 / K) fragments
+ *            the table (fragments and their (fragment, chunk) pieces) is
+ *            staged there and the call is one launch; without it, each
+ *            launch carries min(32, 256 / K) fragments, the zero padding
+ *            when it comes next, and the pieces they form
  * Outputs must be distinct and must not overlap any fragment (ZR_ERR_ALIAS).
- * Fragment tables travel in kernel arguments: a launch carries up to 32
- * fragments (256 rank pointers at most, so 4 fragments at K = 64), the zero
- * padding when it comes next (it has no pointers), and the at most 96
- * (fragment, chunk) pieces they form.
+ * ZR_ERR_WORKSPACE when the workspace is smaller than the table.
  */
 zr_status zr_reduce_scatter_frags(int K, int n_frag, const void* const* frags,
                                   const int64_t* numels, int64_t N, zr_dtype in_dt,
                                   void* const* out, zr_dtype out_dt, int chunk_shift, int flags,
-                                  zr_order order, void* stream);
+                                  zr_order order, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * All-gather of sharded tensors into full tensors [RING Phase 2; L14 3.2;
@@ -208,15 +256,19 @@ zr_status zr_reduce_scatter_frags(int K, int n_frag, const void* const* frags,
  *
  *  shards    host array [K] of device pointers
  *  fulls     host array [K] of device pointers
- *  segs      host array [n_segs], n_segs >= 0 (32 segments per launch);
- *            numel >= 0, offsets >= 0; segments must not write overlapping
- *            full ranges; each shard buffer must hold shard_off + C elements
+ *  segs      host array [n_segs], n_segs >= 0; numel >= 0, offsets >= 0;
+ *            segments must not write overlapping full ranges; each shard
+ *            buffer must hold shard_off + C elements
+ *  workspace NULL (32 segments per launch), or a device workspace of
+ *            ws_bytes bytes: above 32 segments the segment table is staged
+ *            there and the call is one launch
  * The written extent of each full buffer (lowest full_off to highest
  * full_off + numel) must not overlap another rank's, nor any shard extent
  * (ZR_ERR_ALIAS). Reads each shard element once and writes it K times.
  */
 zr_status zr_all_gather(int K, const void* const* shards, void* const* fulls, zr_dtype dt,
-                        const zr_seg* segs, int n_segs, int chunk_shift, void* stream);
+                        const zr_seg* segs, int n_segs, int chunk_shift, void* workspace,
+                        size_t ws_bytes, void* stream);
 
 /*
  * All-reduce = reduce-scatter followed by all-gather [L14 2.2; RING].
@@ -277,17 +329,24 @@ double zr_cost_dp_speedup(int K, double t1, double grad_bytes, double alpha, dou
  * bucket whose fragments stay at the same addresses from step to step (the
  * usual ZeRO layout), zr_rsf_plan_create validates everything and builds the
  * launches' kernel arguments, and each zr_rsf_plan_launch only enqueues
- * them. Arguments and results are exactly those of zr_reduce_scatter_frags
- * with the same arguments (the flags, including ZR_ACCUMULATE, are fixed at
- * create). The plan keeps the fragment and output addresses, not their
- * contents: the buffers must stay allocated while the plan is launched. The
- * plan owns only host memory; N == 0 gives a plan that launches nothing. */
+ * them. With a workspace (needed only above min(32, 256 / K) fragments) the
+ * table is copied into it at create, with a blocking copy, and every launch
+ * is one kernel; the plan uses the workspace until destroyed. Arguments and
+ * results are exactly those of zr_reduce_scatter_frags with the same
+ * arguments (the flags, including ZR_ACCUMULATE, are fixed at create). The
+ * plan keeps the fragment and output addresses, not their contents: the
+ * buffers must stay allocated while the plan is launched. The plan owns only
+ * host memory; N == 0 gives a plan that launches nothing. zr_rsf_plan_info
+ * reports the kernel launches per zr_rsf_plan_launch and the staged table's
+ * size (either pointer may be NULL). */
 typedef struct zr_rsf_plan zr_rsf_plan;
 
 zr_status zr_rsf_plan_create(int K, int n_frag, const void* const* frags, const int64_t* numels,
                              int64_t N, zr_dtype in_dt, void* const* out, zr_dtype out_dt,
-                             int chunk_shift, int flags, zr_order order, zr_rsf_plan** plan);
+                             int chunk_shift, int flags, zr_order order, void* workspace,
+                             size_t ws_bytes, zr_rsf_plan** plan);
 zr_status zr_rsf_plan_launch(const zr_rsf_plan* plan, void* stream);
+zr_status zr_rsf_plan_info(const zr_rsf_plan* plan, int* launches, size_t* table_bytes);
 zr_status zr_rsf_plan_destroy(zr_rsf_plan* plan);
 
 /* ------------------------------------------------------------- scheduler

@@ -133,7 +133,7 @@ def test_all_gather_validation():
         s = (ctypes.c_void_p * K)(*(shards or ranks(K)))
         f = (ctypes.c_void_p * K)(*(fulls or ranks(K, base=A + (1 << 40))))
         arr = (zr.zr_seg * max(1, len(segs)))(*[zr.zr_seg(*x) for x in segs])
-        return lib.zr_all_gather(K, s, f, dt, arr, len(segs), shift, None)
+        return lib.zr_all_gather(K, s, f, dt, arr, len(segs), shift, None, 0, None)
 
     assert call([]) == zr.ZR_OK
     assert call([(0, 0, 0)]) == zr.ZR_OK
@@ -154,7 +154,7 @@ def test_flatten_validation():
         fr = (ctypes.c_void_p * (K * F))(*(frags or ranks(K * F)))
         nm = (ctypes.c_int64 * F)(*numels)
         b = (ctypes.c_void_p * K)(*(buckets or ranks(K, base=A + (1 << 40))))
-        return lib.zr_flatten_bucket(K, F, fr, nm, b, padded, dt, None)
+        return lib.zr_flatten_bucket(K, F, fr, nm, b, padded, dt, None, 0, None)
 
     assert call([0, 0, 0], 0) == zr.ZR_OK
     assert call([1, 2, 3], 5) == zr.ZR_ERR_INVALID          # padded < total
@@ -195,7 +195,7 @@ def test_overlap_checks_on_a_large_fragment_table():
         fr = (ctypes.c_void_p * (K * F))(*frags)
         ot = (ctypes.c_void_p * K)(*o)
         h = ctypes.c_void_p()
-        st = lib.zr_rsf_plan_create(K, F, fr, numels_arr, N, 0, ot, 1, 1, 1, 0, ctypes.byref(h))
+        st = lib.zr_rsf_plan_create(K, F, fr, numels_arr, N, 0, ot, 1, 1, 1, 0, None, 0, ctypes.byref(h))
         if st == zr.ZR_OK:
             assert lib.zr_rsf_plan_destroy(h) == zr.ZR_OK
         return st
@@ -229,9 +229,9 @@ def test_reduce_scatter_frags_validation(entry):
         o = (ctypes.c_void_p * K)(*(outs or ranks(K, base=A + (1 << 40))))
         if entry == "call":
             return lib.zr_reduce_scatter_frags(K, F, fr, nm, N, in_dt, o, out_dt, shift, flags,
-                                               order, None)
+                                               order, None, 0, None)
         h = ctypes.c_void_p(1234)
-        st = lib.zr_rsf_plan_create(K, F, fr, nm, N, in_dt, o, out_dt, shift, flags, order,
+        st = lib.zr_rsf_plan_create(K, F, fr, nm, N, in_dt, o, out_dt, shift, flags, order, None, 0,
                                     ctypes.byref(h))
         if st == zr.ZR_OK:
             if N == 0:
@@ -320,11 +320,12 @@ def test_sizes_above_the_element_limit_are_rejected():
 
     def flatten(numels, padded):
         nm = (ctypes.c_int64 * F)(*numels)
-        return lib.zr_flatten_bucket(K, F, fr, nm, o, padded, zr.ZR_BF16, None)
+        return lib.zr_flatten_bucket(K, F, fr, nm, o, padded, zr.ZR_BF16, None, 0, None)
 
     def frags(numels, N):
         nm = (ctypes.c_int64 * F)(*numels)
-        return lib.zr_reduce_scatter_frags(K, F, fr, nm, N, zr.ZR_BF16, o, zr.ZR_FP32, 1, 1, 0, None)
+        return lib.zr_reduce_scatter_frags(K, F, fr, nm, N, zr.ZR_BF16, o, zr.ZR_FP32, 1, 1, 0, None, 0,
+                                           None)
 
     for fn in (flatten, frags):
         assert fn([1, big + 1, 3], big + 8) == zr.ZR_ERR_INVALID       # one fragment too large
@@ -335,7 +336,7 @@ def test_sizes_above_the_element_limit_are_rejected():
     f = (ctypes.c_void_p * 8)(*ranks(8, base=A + (1 << 41)))
     for seg in ((big + 1, 0, 10), (0, big + 1, 10), (0, 0, big + 1)):
         arr = (zr.zr_seg * 1)(zr.zr_seg(*seg))
-        assert lib.zr_all_gather(8, s, f, zr.ZR_BF16, arr, 1, 0, None) == zr.ZR_ERR_INVALID
+        assert lib.zr_all_gather(8, s, f, zr.ZR_BF16, arr, 1, 0, None, 0, None) == zr.ZR_ERR_INVALID
     t = (ctypes.c_void_p * 8)(*ranks(8))
     assert lib.zr_reduce_scatter_avg(8, t, 0, big + 1, f, 1, 1, 1, 0, None) == zr.ZR_ERR_INVALID
 
@@ -391,3 +392,97 @@ def test_prefetch_plan_on_the_host():
     with pytest.raises(zr.ZrError) as e:
         zr.zr_pf_plan(numels, steps, 30, 60, 40, max_reuse_numel=0)  # step 1 needs 50
     assert e.value.status == zr.ZR_ERR_NOMEM
+
+
+# ------------------------------------------------------------- workspaces
+def test_workspace_bytes():
+    # zero while a call's table fits one argument block: min(32, 256 / K)
+    # fragments (and the all-gather's 32 segments); above that, room for the
+    # largest of the three staged tables with n fragments (plus the padding
+    # entry) and n + K (fragment, chunk) pieces, in whole 256-byte units
+    f = zr.zr_workspace_bytes
+    for K in (1, 2, 8, 16, 64):
+        fit = min(32, 256 // K)
+        assert f(K, 0) == 0 and f(K, fit) == 0
+        b = f(K, fit + 1)
+        assert b > 0 and b % 256 == 0
+        n = 1000
+        need_rsf = 8 * (n + K + 1) + ((12 * (n + K) + 7) // 8) * 8 + 16 * (n + 1) + 8 * K * (n + 1)
+        need_flat = 8 * (n + 2) + 8 * (n + 1) + 16 * (n + 1) + 8 * K * (n + 1)
+        need_ag = 8 * (n + 1) + 48 * n
+        assert f(K, n) == -(-max(need_rsf, need_flat, need_ag) // 256) * 256
+        assert f(K, n + 1) >= f(K, n)
+    assert f(0, 100) == 0 and f(65, 100) == 0 and f(8, -1) == 0
+
+
+def _frag_tables(K, F):
+    fr = (ctypes.c_void_p * (K * F))(*[A + i * (1 << 24) for i in range(K * F)])
+    nm = (ctypes.c_int64 * F)(*([1000] * F))
+    o = (ctypes.c_void_p * K)(*ranks(K, base=A + (1 << 42), stride=1 << 24))
+    return fr, nm, o
+
+
+@pytest.mark.parametrize("entry", ["call", "plan", "flatten", "flatten_plan"])
+def test_workspace_errors_come_before_any_work(entry):
+    # a workspace too small for the staged table, misaligned, or overlapping
+    # a buffer of the call is rejected on the host (no GPU here: a call that
+    # got as far as staging would fail with ZR_ERR_HIP instead)
+    lib = zr.lib()
+    K, F = 64, 10
+    fr, nm, o = _frag_tables(K, F)
+    N = F * 1000 + 24
+    ws_ok = A + (1 << 43)
+
+    def call(ws, wsb):
+        h = ctypes.c_void_p()
+        if entry == "call":
+            return lib.zr_reduce_scatter_frags(K, F, fr, nm, N, 0, o, 1, 1, 1, 0, ws, wsb, None)
+        if entry == "plan":
+            return lib.zr_rsf_plan_create(K, F, fr, nm, N, 0, o, 1, 1, 1, 0, ws, wsb, ctypes.byref(h))
+        if entry == "flatten":
+            return lib.zr_flatten_bucket(K, F, fr, nm, o, N, 0, ws, wsb, None)
+        return lib.zr_flatten_plan_create(K, F, fr, nm, o, N, 0, ws, wsb, ctypes.byref(h))
+
+    need = zr.zr_workspace_bytes(K, F)
+    assert need > 0
+    assert call(ws_ok, 64) == zr.ZR_ERR_WORKSPACE
+    assert "workspace" in zr.zr_last_error()
+    assert call(ws_ok + 4, need) == zr.ZR_ERR_ALIGN
+    assert call(ws_ok, 0) == zr.ZR_ERR_WORKSPACE
+    assert call(o[3], need) == zr.ZR_ERR_ALIAS          # the table would overwrite an output
+    assert call(fr[5], need) == zr.ZR_ERR_ALIAS         # ... or a fragment
+
+
+def test_all_gather_workspace_errors():
+    lib = zr.lib()
+    K, n = 8, 40
+    s = (ctypes.c_void_p * K)(*ranks(K))
+    f = (ctypes.c_void_p * K)(*ranks(K, base=A + (1 << 40)))
+    segs = [(i * 100, i * 800, 800) for i in range(n)]
+    arr = (zr.zr_seg * n)(*[zr.zr_seg(*x) for x in segs])
+    ws = A + (1 << 43)
+    assert lib.zr_all_gather(K, s, f, 0, arr, n, 0, ws, 64, None) == zr.ZR_ERR_WORKSPACE
+    assert lib.zr_all_gather(K, s, f, 0, arr, n, 0, ws + 2, 1 << 20, None) == zr.ZR_ERR_ALIGN
+    assert lib.zr_all_gather(K, s, f, 0, arr, n, 0, f[2], 1 << 20, None) == zr.ZR_ERR_ALIAS
+
+
+@pytest.mark.parametrize("K,F", [(8, 32), (8, 33), (8, 64), (64, 4), (64, 5), (64, 300), (16, 100)])
+def test_plans_without_workspace_count_their_launches(K, F):
+    # without a workspace a plan takes min(32, 256 / K) fragments per launch
+    # (the padding entry rides in a spare slot of the last one); plans are
+    # built on the host, so the count is visible without a GPU
+    fr, nm, o = _frag_tables(K, F)
+    N = F * 1000 + K
+    per = min(32, 256 // K)
+    lib = zr.lib()
+    for create, info, destroy, args in (
+            (lib.zr_rsf_plan_create, lib.zr_rsf_plan_info, lib.zr_rsf_plan_destroy,
+             (K, F, fr, nm, N, 0, o, 1, 1, 1, 0, None, 0)),
+            (lib.zr_flatten_plan_create, lib.zr_flatten_plan_info, lib.zr_flatten_plan_destroy,
+             (K, F, fr, nm, o, N, 0, None, 0))):
+        h = ctypes.c_void_p()
+        assert create(*args, ctypes.byref(h)) == zr.ZR_OK, zr.zr_last_error()
+        n, b = ctypes.c_int(-1), ctypes.c_size_t(1)
+        assert info(h, ctypes.byref(n), ctypes.byref(b)) == zr.ZR_OK
+        assert n.value == -(-F // per) and b.value == 0
+        assert destroy(h) == zr.ZR_OK

@@ -24,6 +24,15 @@ def zr():
     return m
 
 
+def workspace(use, K, n):
+    """A device workspace for a call with n fragments or segments (None when
+    `use` is false): the size zr_workspace_bytes asks for, at least 256 bytes."""
+    import torch
+    if not use:
+        return None
+    return torch.empty(max(256, zr().zr_workspace_bytes(K, n)), dtype=torch.uint8, device="cuda")
+
+
 def torch_dt(is_bf16):
     import torch
     return torch.bfloat16 if is_bf16 else torch.float32
@@ -299,6 +308,7 @@ AG_CASES = [
     (8, [8 * 2048 * 2, 8 * 2048 * 3 + 8, 5000, 1, 7], 0, True, 0, 0),
     (8, [100003, 64, 3], 1, True, 0, 3),
     (8, [65536] * 40, 0, True, 0, 0),          # more than one launch of segments
+    (4, [1000 + 37 * i for i in range(150)], 1, True, 0, 1),  # 150 segments: one staged launch
     (3, [10, 30001, 2], 2, False, 1, 1),
     (64, [64 * 2048 + 5, 640, 63], 0, True, 0, 0),
     (1, [12345], 0, True, 0, 0),
@@ -306,8 +316,9 @@ AG_CASES = [
 ]
 
 
+@pytest.mark.parametrize("ws", [False, True], ids=["args", "workspace"])
 @pytest.mark.parametrize("K,sizes,shift,bf16,offset,gap", AG_CASES)
-def test_all_gather_bit_exact(K, sizes, shift, bf16, offset, gap):
+def test_all_gather_bit_exact(K, sizes, shift, bf16, offset, gap, ws):
     import torch
     rng = np.random.default_rng(sum(sizes) + K)
     segs, soff, foff = [], 0, 0
@@ -322,7 +333,7 @@ def test_all_gather_bit_exact(K, sizes, shift, bf16, offset, gap):
     fill = np.zeros(foff, dtype=dt)
     fulls = [Guarded(foff, torch_dt(bf16), offset, fill) for _ in range(K)]
     zr().zr_all_gather([g.ptr() for g in shards], [g.ptr() for g in fulls], segs,
-                       chunk_shift=shift, dtype=torch_dt(bf16))
+                       chunk_shift=shift, dtype=torch_dt(bf16), workspace=workspace(ws, K, len(segs)))
     torch.cuda.synchronize()
     want = [np.zeros(foff, dtype=dt) for _ in range(K)]
     oracle.all_gather(shard_np, want, segs, shift)
@@ -346,8 +357,10 @@ def test_all_gather_bit_exact(K, sizes, shift, bf16, offset, gap):
     # launches large enough for 16 KiB tiles
     (8, [600000, 5, 700001], True, 0, 3),
     (4, [300001, 7, 500000], False, 1, 0),
+    (64, [1 + 97 * i for i in range(40)], True, 0, 5),  # ten argument launches, or one staged
 ])
-def test_flatten_bit_exact(K, sizes, bf16, offset, extra):
+@pytest.mark.parametrize("ws", [False, True], ids=["args", "workspace"])
+def test_flatten_bit_exact(K, sizes, bf16, offset, extra, ws):
     import torch
     from synth import workloads as W
     if sizes is None:
@@ -367,7 +380,8 @@ def test_flatten_bit_exact(K, sizes, bf16, offset, extra):
                        np.full(padded, 0x3F80 if bf16 else 1.0,
                                dtype=np.uint16 if bf16 else np.float32)) for _ in range(K)]
     zr().zr_flatten_bucket([[g.ptr() for g in row] for row in frags], sizes,
-                           [b.ptr() for b in buckets], padded, dtype=torch_dt(bf16))
+                           [b.ptr() for b in buckets], padded, dtype=torch_dt(bf16),
+                           workspace=workspace(ws, K, len(sizes)))
     torch.cuda.synchronize()
     want = oracle.flatten(frags_np, sizes, padded)
     for r in range(K):
@@ -399,13 +413,17 @@ FRAG_CASES = [
     (8, [97 * (i + 1) for i in range(32)], 20000, True, False, 1, True, 0, 0, False),  # over 3 chunks
     (8, [50 + 13 * i for i in range(33)], 9, True, False, 1, True, 0, 0, True),  # 32 + (1 + padding)
     (64, [32000] * 6, 64 * 40, True, False, 1, True, 0, 0, False),     # 4 fragments per launch
+    # many fragments at K = 64: 16 argument launches, or one over a staged table
+    (64, [1 + 613 * i for i in range(64)], 64 * 7, True, False, 1, True, 0, 0, False),
+    (64, [1 + 613 * i for i in range(64)], 64 * 7, True, True, 1, True, 2, -1, True),
 ]
 
 
+@pytest.mark.parametrize("ws", [False, True], ids=["args", "workspace"])
 @pytest.mark.parametrize("K,sizes,extra,in_bf16,out_bf16,shift,average,order,offset,acc",
                          FRAG_CASES)
 def test_reduce_scatter_frags_bit_exact(K, sizes, extra, in_bf16, out_bf16, shift, average,
-                                        order, offset, acc):
+                                        order, offset, acc, ws):
     # the discrete path equals flatten-into-a-bucket then reduce-scatter;
     # offset -1: rank r's fragments at element offset r % 4 (the ranks' buffers
     # in different quad phases), every partition at offset 1
@@ -435,12 +453,15 @@ def test_reduce_scatter_frags_bit_exact(K, sizes, extra, in_bf16, out_bf16, shif
     zr().zr_reduce_scatter_frags([[g.ptr() for g in row] for row in frags], sizes, N,
                                  [g.ptr() for g in outs], chunk_shift=shift, average=average,
                                  order=order, accumulate=acc, in_dtype=torch_dt(in_bf16),
-                                 out_dtype=torch_dt(out_bf16))
+                                 out_dtype=torch_dt(out_bf16), workspace=workspace(ws, K, len(sizes)))
     torch.cuda.synchronize()
     bucket = oracle.flatten(frags_np, sizes, N) if sizes else \
         [np.zeros(N, dtype=np.uint16 if in_bf16 else np.float32) for _ in range(K)]
     if order == 1:
-        # free order: compare with the GPU's own contiguous free-order path
+        # free order: the discrete call, and the contiguous free-order call on
+        # the bucket the flatten would build, are each within the free-order
+        # bound of the oracle's exact (fp64) sum
+        assert not acc
         bt = [Guarded(N, torch_dt(in_bf16), 0, bucket[r]) for r in range(K)]
         ref = [Guarded(C, torch_dt(out_bf16), 0) for _ in range(K)]
         zr().zr_reduce_scatter_avg([g.ptr() for g in bt], N, [g.ptr() for g in ref],
@@ -454,11 +475,12 @@ def test_reduce_scatter_frags_bit_exact(K, sizes, extra, in_bf16, out_bf16, shif
         scale = 1.0 / K if average else 1.0
         for q in range(K):
             j = (q + shift) % K
-            got = outs[q].get()
-            gotf = (oracle.bf16_to_f32(got) if out_bf16 else got).astype(np.float64)
             ex = exact[j * C:(j + 1) * C] * scale
-            assert np.all(np.abs(gotf - ex) <= 1e-5 * absum[j * C:(j + 1) * C] * scale +
-                          (bf16_ulp(ex) if out_bf16 else 0))
+            bound = 1e-5 * absum[j * C:(j + 1) * C] * scale + (bf16_ulp(ex) if out_bf16 else 0)
+            for name, res in (("discrete", outs[q]), ("contiguous", ref[q])):
+                got = res.get()
+                gotf = (oracle.bf16_to_f32(got) if out_bf16 else got).astype(np.float64)
+                assert np.all(np.abs(gotf - ex) <= bound), f"{name} free order, rank {q}"
         return
     want = [x.copy() for x in init]
     oracle.reduce_scatter(bucket, N, odt, shift=shift, average=average, out=want,
