@@ -57,6 +57,7 @@ ZR_BF16, ZR_FP32 = 0, 1
 ZR_ORDER_RING, ZR_ORDER_FREE, ZR_ORDER_RING_WIRE = 0, 1, 2
 ZR_AVERAGE, ZR_ACCUMULATE = 1, 2
 ZR_MAX_RANKS, ZR_MAX_ELEMS = 64, 1 << 40
+ZR_NOALLOC_TABLE_BYTES = 1 << 20
 STATUS_NAMES = {0: "ZR_OK", 1: "ZR_ERR_INVALID", 2: "ZR_ERR_ALIGN", 3: "ZR_ERR_ALIAS",
                 4: "ZR_ERR_UNSUPPORTED", 5: "ZR_ERR_WORKSPACE", 6: "ZR_ERR_HIP", 7: "ZR_ERR_NOMEM"}
 
@@ -72,7 +73,8 @@ PF_EXPORTS = ("zr_pf_create", "zr_pf_fetch", "zr_pf_release", "zr_pf_full", "zr_
 EXPORTS = ("zr_last_error", "zr_version", "zr_workspace_bytes", "zr_flatten_bucket", "zr_reduce_scatter_avg",
            "zr_reduce_scatter_frags", "zr_all_gather", "zr_allreduce", "zr_plan_buckets", "zr_sched_create",
            "zr_sched_acquire", "zr_sched_submit_rs", "zr_sched_flush",
-           "zr_sched_destroy") + COST_EXPORTS + PF_EXPORTS + RSF_PLAN_EXPORTS + FLAT_PLAN_EXPORTS
+           "zr_sched_destroy", "zr_reduce_scatter_frags_noalloc") + COST_EXPORTS + PF_EXPORTS + \
+    RSF_PLAN_EXPORTS + FLAT_PLAN_EXPORTS
 
 
 class ZrError(RuntimeError):
@@ -133,6 +135,8 @@ def lib() -> ctypes.CDLL:
                                     _vp]
         L.zr_reduce_scatter_frags.argtypes = [_i32, _i32, _PP, ctypes.POINTER(_i64), _i64, _i32, _PP,
                                               _i32, _i32, _i32, _i32, _vp, _sz, _vp]
+        L.zr_reduce_scatter_frags_noalloc.argtypes = [_i32, _i32, _PP, ctypes.POINTER(_i64), _i64, _i32,
+                                                      _PP, _i32, _i32, _i32, _i32, _vp]
         L.zr_allreduce.argtypes = [_i32, _PP, _PP, _i32, _i64, _i32, _i32, _i32, _vp, _vp]
         L.zr_plan_buckets.argtypes = [_i32, ctypes.POINTER(_i64), _i64, ctypes.POINTER(ctypes.c_int32),
                                       ctypes.POINTER(ctypes.c_int32)]
@@ -349,6 +353,24 @@ def zr_reduce_scatter_frags(frags: Sequence[Sequence], numels: Sequence[int], N:
     _check(lib().zr_reduce_scatter_frags(K, F, _table(flat), nums, N, in_dt, _table(outputs),
                                          out_dt, chunk_shift, _flags(average, accumulate), order,
                                          ws, wsb, _stream(stream)))
+
+
+def zr_reduce_scatter_frags_noalloc(frags: Sequence[Sequence], numels: Sequence[int], N: int,
+                                    outputs: Sequence, chunk_shift: int = 1, average: bool = True,
+                                    order: int = ZR_ORDER_RING, in_dtype=None, out_dtype=None,
+                                    stream=None, accumulate: bool = False) -> None:
+    """zr_reduce_scatter_frags staging its table in the library's own device
+    array (no workspace, nothing allocated)."""
+    K = len(outputs)
+    F = len(numels)
+    flat = [f for row in frags for f in row]
+    if len(flat) != K * F:
+        raise ValueError("frags must be K lists of len(numels) tensors")
+    in_dt = _dtype(in_dtype if in_dtype is not None else flat[0])
+    out_dt = _dtype(out_dtype if out_dtype is not None else outputs[0])
+    _check(lib().zr_reduce_scatter_frags_noalloc(K, F, _table(flat), _int64s(numels), N, in_dt,
+                                                 _table(outputs), out_dt, chunk_shift,
+                                                 _flags(average, accumulate), order, _stream(stream)))
 
 
 class RsfPlan:

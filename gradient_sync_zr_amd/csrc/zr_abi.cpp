@@ -743,6 +743,38 @@ zr_status zr_reduce_scatter_frags(int K, int n_frag, const void* const* frags,
     });
 }
 
+zr_status zr_reduce_scatter_frags_noalloc(int K, int n_frag, const void* const* frags,
+                                          const int64_t* numels, int64_t N, zr_dtype in_dt,
+                                          void* const* out, zr_dtype out_dt, int chunk_shift,
+                                          int flags, zr_order order, void* stream) {
+    return zr::guarded([&]() -> zr_status {
+        // validation first: the same checks as the one-shot call, on the host
+        RsfPlan* probe = nullptr;
+        ZR_TRY(make_frags_plan(K, n_frag, frags, numels, N, in_dt, out, out_dt, chunk_shift, flags, order, nullptr,
+                               0, &probe));
+        if (!probe) return ok();
+        const bool one_launch = rsf_plan_launch_count(probe) <= 1;
+        rsf_plan_free(probe);
+        void* ws = nullptr;
+        if (!one_launch) {
+            const hipError_t e = noalloc_scratch(&ws);
+            if (e != hipSuccess) return hip_fail(e, "looking up the staging array");
+        }
+        auto build = [&](void* w, RsfPlan** p) {
+            const zr_status st = make_frags_plan(K, n_frag, frags, numels, N, in_dt, out, out_dt, chunk_shift, flags,
+                                                 order, w, ZR_NOALLOC_TABLE_BYTES, p);
+            if (st == ZR_ERR_WORKSPACE)
+                return fail(ZR_ERR_WORKSPACE,
+                            "the table of %d fragments at K=%d needs more than the %d bytes this entry point "
+                            "stages (zr_workspace_bytes(K, n_frag) <= %d is always accepted)",
+                            n_frag, K, ZR_NOALLOC_TABLE_BYTES, ZR_NOALLOC_TABLE_BYTES);
+            return st;
+        };
+        return run_once<RsfPlan>(build, rsf_plan_table_bytes, rsf_plan_table_image, rsf_plan_launch, rsf_plan_free,
+                                 ws, (hipStream_t)stream, "discrete reduce-scatter launch");
+    });
+}
+
 zr_status zr_rsf_plan_create(int K, int n_frag, const void* const* frags, const int64_t* numels,
                              int64_t N, zr_dtype in_dt, void* const* out, zr_dtype out_dt,
                              int chunk_shift, int flags, zr_order order, void* workspace,

@@ -127,6 +127,12 @@ int rsf_plan_launch_count(const RsfPlan* plan);
 hipError_t rsf_plan_launch(const RsfPlan* plan, hipStream_t stream);
 void rsf_plan_free(RsfPlan* plan);
 
+// Device address, on the current device, of the file-scope staging array of
+// ZR_NOALLOC_TABLE_BYTES bytes that zr_reduce_scatter_frags_noalloc stages its
+// table in (looked up once per device with hipGetSymbolAddress).
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(void** ptr);
+
 // Bucket flatten over fragment entries, planned the same way: argument
 // launches of kFlatEntriesPerLaunch (or fewer) entries, an entry of more than
 // 2^28 / K tiles of 4 KiB per rank cut into pieces of that many (so tile

@@ -40,6 +40,7 @@
 // writes +0 (old + 0 when accumulating).
 #include <climits>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -567,5 +568,31 @@ hipError_t rsf_plan_launch(const RsfPlan* plan, hipStream_t stream) {
 }
 
 void rsf_plan_free(RsfPlan* plan) { delete plan; }
+
+// The table staging area of the entry point that allocates nothing: one
+// array per GPU, held until the process ends. Host code never uses the name
+// `scratch` as an address; it uses the device address looked up per device.
+static __device__ __align__(256) unsigned char scratch[ZR_NOALLOC_TABLE_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 }  // namespace zr

@@ -248,6 +248,28 @@ zr_status zr_reduce_scatter_frags(int K, int n_frag, const void* const* frags,
                                   zr_order order, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * zr_reduce_scatter_frags for callers that cannot allocate device memory or
+ * hold a workspace (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, the same
+ * results bit for bit. A table that needs staging is copied into a staging
+ * array of ZR_NOALLOC_TABLE_BYTES bytes that the library keeps on every GPU
+ * it runs on until the process ends (a file-scope device array; nothing is
+ * allocated at run time: no hipMalloc, no hipFree). A table larger than that
+ * is ZR_ERR_WORKSPACE, with nothing enqueued; zr_workspace_bytes(K, n_frag)
+ * <= ZR_NOALLOC_TABLE_BYTES is always accepted (up to 1,910 fragments at
+ * K = 64, 10,483 at K = 8). Every call on one GPU shares that GPU's array:
+ * calls on one stream are ordered, but calls that overlap in time on
+ * different streams of one GPU race for it. Each call rewrites the part it
+ * uses, so no contents need clearing between calls. Under stream capture the
+ * call goes out as argument launches, as zr_reduce_scatter_frags does.
+ */
+#define ZR_NOALLOC_TABLE_BYTES (1 << 20)
+zr_status zr_reduce_scatter_frags_noalloc(int K, int n_frag, const void* const* frags,
+                                          const int64_t* numels, int64_t N, zr_dtype in_dt,
+                                          void* const* out, zr_dtype out_dt, int chunk_shift,
+                                          int flags, zr_order order, void* stream);
+
+/*
  * All-gather of sharded tensors into full tensors [RING Phase 2; L14 3.2;
  * ZERO3 1, 2.1]. For each segment and every destination rank r:
  *     full_r[full_off + j*C + o] = shard_{(j - chunk_shift) mod K}[shard_off + o]

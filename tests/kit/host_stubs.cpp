@@ -90,4 +90,6 @@ int flat_plan_launch_count(const FlatPlan* p) { return p->launches; }
 hipError_t flat_plan_launch(const FlatPlan*, hipStream_t) { return hipErrorNotSupported; }
 void flat_plan_free(FlatPlan* plan) { delete plan; }
 
+hipError_t noalloc_scratch(void**) { return hipErrorNotSupported; }
+
 }  // namespace zr
