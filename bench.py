@@ -21,6 +21,9 @@ Other workloads (--workload):
   flatten8        the 64-fragment bucket: flatten + reduce-scatter against the
                   discrete path, in microseconds per call (cache-resident)
   frags_layer     the discrete reduce-scatter over one layer's seven gradients
+  flatten_layer   the bucket flatten of those seven gradients (bandwidth scale)
+  frags_k64       256 fragments on K = 64: calls and plans with and without a
+                  workspace-staged table (microseconds and launches per call)
 
 Prints one JSON line. Only one GPU is used; --gpus above 1 exits.
 """
@@ -727,6 +730,20 @@ def bench_frags_layer(args):
 
 
 # -------------------------------------------------------------- flatten8
+def wall_us(fn, steps, warmup):
+    """Host wall time per call of `fn` (microseconds), the device drained
+    before and after: what a caller's loop of such calls costs."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e6 / steps
+
+
 def bench_flatten8(args):
     import torch
 
@@ -745,52 +762,211 @@ def bench_flatten8(args):
     buckets = [torch.empty(P, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
     parts = [torch.empty(P // K, dtype=torch.float32, device="cuda") for _ in range(K)]
     fp = [[t.data_ptr() for t in row] for row in frags]
-    bp = [t.data_ptr() for t in buckets]
-    pp = [t.data_ptr() for t in parts]
+    bp = zr.table([t.data_ptr() for t in buckets])
+    pp = zr.table([t.data_ptr() for t in parts])
+    ws = torch.empty(zr.zr_workspace_bytes(K, F), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(zr.zr_workspace_bytes(K, F), dtype=torch.uint8, device="cuda")
+    bf, f32 = torch.bfloat16, torch.float32
+
+    def rs():
+        zr.zr_reduce_scatter_avg(bp, P, pp, chunk_shift=1, average=True, in_dtype=bf, out_dtype=f32)
 
     def step():
-        zr.zr_flatten_bucket(fp, sizes, bp, P, dtype=torch.bfloat16)
-        zr.zr_reduce_scatter_avg(bp, P, pp, chunk_shift=1, average=True, in_dtype=torch.bfloat16,
-                                 out_dtype=torch.float32)
+        zr.zr_flatten_bucket(fp, sizes, bp, P, dtype=bf)
+        rs()
 
     def step_discrete():
-        zr.zr_reduce_scatter_frags(fp, sizes, P, pp, chunk_shift=1, average=True,
-                                   in_dtype=torch.bfloat16, out_dtype=torch.float32)
+        zr.zr_reduce_scatter_frags(fp, sizes, P, pp, chunk_shift=1, average=True, in_dtype=bf,
+                                   out_dtype=f32)
 
-    def wall_us(fn):
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            fn()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e6 / args.steps
-
-    plan = zr.RsfPlan(fp, sizes, P, pp, chunk_shift=1, average=True, in_dtype=torch.bfloat16,
-                      out_dtype=torch.float32)
-    us = wall_us(step)
-    us_discrete = wall_us(step_discrete)
-    us_plan = wall_us(plan.launch)
+    flat_args = zr.FlatPlan(fp, sizes, bp, P, dtype=bf)
+    flat_ws = zr.FlatPlan(fp, sizes, bp, P, dtype=bf, workspace=ws)
+    plan = zr.RsfPlan(fp, sizes, P, pp, chunk_shift=1, average=True, in_dtype=bf, out_dtype=f32)
+    plan_ws = zr.RsfPlan(fp, sizes, P, pp, chunk_shift=1, average=True, in_dtype=bf, out_dtype=f32,
+                         workspace=ws2)
+    us = wall_us(step, args.steps, args.warmup)
+    us_discrete = wall_us(step_discrete, args.steps, args.warmup)
+    us_flatplan_rs = wall_us(lambda: (flat_args.launch(), rs()), args.steps, args.warmup)
+    us_flatplan_ws_rs = wall_us(lambda: (flat_ws.launch(), rs()), args.steps, args.warmup)
+    us_plan = wall_us(plan.launch, args.steps, args.warmup)
+    us_plan_ws = wall_us(plan_ws.launch, args.steps, args.warmup)
     # the plan's launches captured once in a HIP graph and replayed
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         plan.launch()
-    us_graph = wall_us(graph.replay)
-    plan.close()
+    us_graph = wall_us(graph.replay, args.steps, args.warmup)
+    launches = {"flatten": flat_args.info()["launches"], "flatten_ws": flat_ws.info()["launches"],
+                "discrete": plan.info()["launches"], "discrete_ws": plan_ws.info()["launches"],
+                "reduce_scatter": 1}
+    for p_ in (flat_args, flat_ws, plan, plan_ws):
+        p_.close()
     return {
         "metric": "flatten + reduce-scatter-avg microseconds per bucket, K=8, 64 fragments",
         "value": round(us, 2), "unit": "us", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic: seeded generator, bf16 ~N(0,1e-3)",
+        "flatten_plan_then_rs_us": round(us_flatplan_rs, 2),
+        "flatten_plan_ws_then_rs_us": round(us_flatplan_ws_rs, 2),
         "discrete_path_us": round(us_discrete, 2),
         "discrete_plan_us": round(us_plan, 2),
+        "discrete_plan_ws_us": round(us_plan_ws, 2),
         "discrete_plan_graph_us": round(us_graph, 2),
+        "launches": launches,
         "config": {"workload": f"flatten8: K=8, 64 log-uniform fragments ({sum(sizes)} elements), "
                                f"bucket padded to {P}, then RS + /8 + fp32 cast (cache-resident, "
-                               "launch-bound)", "K": K},
+                               "launch-bound; host wall time per call)", "K": K},
         "roofline": None, "cpu_baseline": None,
+    }
+
+
+# ------------------------------------------------------------- frags_k64
+def bench_frags_k64(args):
+    """A bucket of 256 log-uniform fragments on K = 64 ranks: the discrete
+    reduce-scatter and the flatten, as one-shot calls and as plans, without a
+    workspace (4 fragments per launch) and with one (the table staged, one
+    launch): microseconds per call and launches per call."""
+    import torch
+
+    import synth
+    import gradient_sync_zr_amd as zr
+    from synth import log_uniform_sizes
+    from synth import workloads as W
+
+    K, F = 64, 256
+    seed = W.seed_of(2)
+    sizes = log_uniform_sizes(seed + 64, F)
+    N = -(-sum(sizes) // K) * K
+    frags = [[torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in sizes] for _ in range(K)]
+    for r in range(K):
+        for p in range(F):
+            synth.dev_normal_bf16(frags[r][p], seed + 64, r * 4096 + p, 0, 1e-3)
+    parts = [torch.empty(N // K, dtype=torch.float32, device="cuda") for _ in range(K)]
+    buckets = [torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    fp = [[t.data_ptr() for t in row] for row in frags]
+    pp = zr.table([t.data_ptr() for t in parts])
+    bp = zr.table([t.data_ptr() for t in buckets])
+    need = zr.zr_workspace_bytes(K, F)
+    ws = [torch.empty(need, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    kw = dict(chunk_shift=1, average=True, in_dtype=torch.bfloat16, out_dtype=torch.float32)
+    plan = zr.RsfPlan(fp, sizes, N, pp, **kw)
+    plan_ws = zr.RsfPlan(fp, sizes, N, pp, workspace=ws[0], **kw)
+    fplan = zr.FlatPlan(fp, sizes, bp, N, dtype=torch.bfloat16)
+    fplan_ws = zr.FlatPlan(fp, sizes, bp, N, dtype=torch.bfloat16, workspace=ws[1])
+    steps, warm = max(10, args.steps), max(3, args.warmup)
+
+    def device_ms(fn, reps=20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = {
+        "discrete_call_us": wall_us(lambda: zr.zr_reduce_scatter_frags(fp, sizes, N, pp, **kw), steps, warm),
+        "discrete_call_ws_us": wall_us(lambda: zr.zr_reduce_scatter_frags(fp, sizes, N, pp, workspace=ws[2], **kw),
+                                       steps, warm),
+        "discrete_plan_us": wall_us(plan.launch, steps, warm),
+        "discrete_plan_ws_us": wall_us(plan_ws.launch, steps, warm),
+        "flatten_plan_us": wall_us(fplan.launch, steps, warm),
+        "flatten_plan_ws_us": wall_us(fplan_ws.launch, steps, warm),
+        "discrete_plan_device_ms": device_ms(plan.launch),
+        "discrete_plan_ws_device_ms": device_ms(plan_ws.launch),
+    }
+    launches = {"discrete": plan.info()["launches"], "discrete_ws": plan_ws.info()["launches"],
+                "flatten": fplan.info()["launches"], "flatten_ws": fplan_ws.info()["launches"],
+                "staged_table_bytes": plan_ws.info()["table_bytes"], "workspace_bytes": need}
+    for p_ in (plan, plan_ws, fplan, fplan_ws):
+        p_.close()
+    return {
+        "metric": "discrete reduce-scatter microseconds per call, K=64, 256 fragments, plan with a "
+                  "workspace-staged table",
+        "value": round(res["discrete_plan_ws_us"], 2), "unit": "us", "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": round(res["discrete_plan_ws_us"] / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic: seeded generator, bf16 ~N(0,1e-3)",
+        **{k: round(v, 4 if k.endswith("_ms") else 2) for k, v in res.items()},
+        "launches": launches,
+        "config": {"workload": f"frags_k64: K=64, {F} log-uniform fragments in [1, 65536] "
+                               f"({sum(sizes)} elements per rank), N padded to {N}; host wall time "
+                               "per call, device time per plan launch", "K": K, "n_frag": F},
+        "roofline": None, "cpu_baseline": None,
+    }
+
+
+# ---------------------------------------------------------- flatten_layer
+def bench_flatten_layer(args):
+    """The bucket flatten at bandwidth scale: one transformer layer's seven
+    gradients per rank (q, k, v, o: 4096x4096; gate, up, down: 4096x11008)
+    copied into a flat bucket per rank, K = 8. Every byte is read once and
+    written once: K * N * 2 bytes each way."""
+    import torch
+
+    import synth
+    import gradient_sync_zr_amd as zr
+    from synth import workloads as W
+
+    cfg = W.FRAGS_LAYER
+    K = cfg["K"]
+    sizes = W.frags_layer_numels()
+    N = sum(sizes)
+    seed = W.seed_of(cfg["seed_cfg"])
+    frags = [[torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in sizes] for _ in range(K)]
+    for r in range(K):
+        for p in range(len(sizes)):
+            synth.dev_normal_bf16(frags[r][p], seed, W.frags_layer_stream(r, p), 0, cfg["sigma"])
+    buckets = [torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    fp = [[t.data_ptr() for t in row] for row in frags]
+    plan = zr.FlatPlan(fp, sizes, [t.data_ptr() for t in buckets], N, dtype=torch.bfloat16)
+    for _ in range(args.warmup):
+        plan.launch()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[2 * i].record(s)
+        plan.launch()
+        ev[2 * i + 1].record(s)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    launch_ms = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps))
+    avg = sum(launch_ms) / len(launch_ms)
+    step_bytes = 2 * K * N * 2
+    ok = all(torch.equal(buckets[r][sum(sizes[:p]):sum(sizes[:p + 1])], frags[r][p])
+             for r in range(K) for p in range(len(sizes)))
+    plan.close()
+    del frags, buckets
+    src = kernel_source_hash(["zr_flatten.hip", "zr_device.hpp"])
+    traffic = read_traffic("flatten_bf16_k8_flatten_layer.counters.txt", src, step_bytes)
+    copy = copy_ceiling_gbps()
+    achieved = step_bytes / (avg * 1e-3) / 1e9
+    return {
+        "metric": "bucket flatten GB/s (K fragment reads + K bucket writes), K=8, one layer's 7 "
+                  "gradients per rank",
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded generator, bf16 ~N(0,1e-3)",
+        "launch_ms_median": round(launch_ms[len(launch_ms) // 2], 4),
+        "launch_ms_min": round(launch_ms[0], 4),
+        "copied_exactly": ok,
+        "config": {"workload": f"flatten_layer: K=8, 7 fragments per rank ({N} elements) into one "
+                               "bucket per rank (a plan: one launch)", "K": K, "N": N,
+                   "bytes_per_step": step_bytes},
+        "roofline": {"bound": "hbm", "kernel": "flatten_kernel<bf16>", "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "achieved": round(achieved, 1),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "avg_launch_ms": round(avg, 4),
+                     "copy_ceiling_GBps": copy,
+                     "of_copy_ceiling": round(achieved / copy, 4) if copy else None,
+                     "algorithmic_bytes_per_launch": step_bytes,
+                     "kernel_source_sha256_16": src},
+        "cpu_baseline": None,
     }
 
 
@@ -801,7 +977,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="zero2",
                     choices=["zero2", "zero2_accum", "zero2_overlap", "zero3_ag", "zero3_prefetch",
-                             "allreduce64", "flatten8", "frags_layer"])
+                             "allreduce64", "flatten8", "frags_layer", "frags_k64", "flatten_layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--compute-ratio", type=float, default=1.5,
                     help="zero3_prefetch, zero2_overlap: each step's synthetic compute, in units "
@@ -824,7 +1000,8 @@ def main():
           "zero2_overlap": bench_zero2_overlap,
           "zero3_ag": bench_zero3, "zero3_prefetch": bench_zero3_prefetch,
           "allreduce64": bench_allreduce64,
-          "flatten8": bench_flatten8, "frags_layer": bench_frags_layer}[args.workload]
+          "flatten8": bench_flatten8, "frags_layer": bench_frags_layer, "frags_k64": bench_frags_k64,
+          "flatten_layer": bench_flatten_layer}[args.workload]
     print(json.dumps(fn(args)), flush=True)
 
 

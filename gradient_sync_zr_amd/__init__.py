@@ -203,9 +203,12 @@ def _ptr(x) -> int:
 def _table(xs: Optional[Sequence]):
     """A C array of device addresses (void*[]), built through array.array: for
     hundreds of fragment pointers this is several times cheaper than filling
-    a ctypes array element by element."""
+    a ctypes array element by element. A table built once with ``table()``
+    passes through unchanged."""
     if xs is None:
         return None
+    if isinstance(xs, ctypes.Array):
+        return xs  # already a table (a caller that reuses one across calls)
     try:
         a = array.array("Q", xs or [0])  # a list of int addresses
     except TypeError:
@@ -213,6 +216,11 @@ def _table(xs: Optional[Sequence]):
     t = (ctypes.c_void_p * len(a)).from_buffer(a)
     t._keep = a  # the array owns the memory the C array views
     return t
+
+
+def table(xs: Sequence):
+    """A reusable C table of device addresses for the per-rank arguments."""
+    return _table(xs)
 
 
 def _int64s(xs: Sequence[int]):

@@ -10,7 +10,8 @@
 // entries rides in the kernel arguments when it fits one argument block: up
 // to 32 entries' pointers (256 pointers, so 4 entries at K = 64), the zero
 // padding in a spare slot after them (it has no source), and each entry's
-// first tile; more entries go out as further launches. Given a workspace, a
+// first tile; more entries go out as further launches (a block finds its
+// entry by a uniform binary search over the first tiles). Given a workspace, a
 // larger table is staged there and one launch copies every fragment (the
 // bucket as one operation, section 3.1); the kernel reads it with scalar loads
 // and finds a tile's entry with a wave-wide search. The grid has one block per
@@ -83,8 +84,21 @@ struct FlatArgTable {
     using Index = int;  // argument launches keep tile numbers within 32 bits
     const FlatArgs& a;
     __device__ __forceinline__ int total() const { return a.tile0[a.nent]; }
-    // a block's tiles only grow, so its last entry is a lower bound
-    __device__ __forceinline__ int find(int from, int t) const { return find_slot(a.tile0, a.nent, from, t); }
+    // the last m with tile0[m] <= t, by a uniform binary search on scalar
+    // loads of the arguments (a wave-wide search on vector loads of them ran
+    // the 4 KiB tiles 10% slower: it puts an extra vector-memory round trip
+    // ahead of every tile's one load)
+    __device__ __forceinline__ int find(int, int t) const {
+        int lo = 0, hi = a.nent;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.tile0[mid] <= t)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        return lo;
+    }
     __device__ __forceinline__ int first(int m) const { return a.tile0[m]; }
     __device__ __forceinline__ FlatEnt ent(int m) const { return {a.off[m], a.n[m], a.tpr[m]}; }
     __device__ __forceinline__ const void* src(int m, int K, int r) const { return a.src[m * K + r]; }
