@@ -788,6 +788,9 @@ def bench_flatten8(args):
     us_discrete = wall_us(step_discrete, args.steps, args.warmup)
     us_flatplan_rs = wall_us(lambda: (flat_args.launch(), rs()), args.steps, args.warmup)
     us_flatplan_ws_rs = wall_us(lambda: (flat_ws.launch(), rs()), args.steps, args.warmup)
+    rs_plan = zr.RsPlan(bp, P, pp, chunk_shift=1, average=True, in_dtype=bf, out_dtype=f32)
+    stream = torch.cuda.current_stream().cuda_stream
+    us_plans = wall_us(lambda: (flat_ws.launch(stream), rs_plan.launch(stream)), args.steps, args.warmup)
     us_plan = wall_us(plan.launch, args.steps, args.warmup)
     us_plan_ws = wall_us(plan_ws.launch, args.steps, args.warmup)
     # the plan's launches captured once in a HIP graph and replayed
@@ -798,7 +801,7 @@ def bench_flatten8(args):
     launches = {"flatten": flat_args.info()["launches"], "flatten_ws": flat_ws.info()["launches"],
                 "discrete": plan.info()["launches"], "discrete_ws": plan_ws.info()["launches"],
                 "reduce_scatter": 1}
-    for p_ in (flat_args, flat_ws, plan, plan_ws):
+    for p_ in (flat_args, flat_ws, plan, plan_ws, rs_plan):
         p_.close()
     return {
         "metric": "flatten + reduce-scatter-avg microseconds per bucket, K=8, 64 fragments",
@@ -808,6 +811,7 @@ def bench_flatten8(args):
         "data": "synthetic: seeded generator, bf16 ~N(0,1e-3)",
         "flatten_plan_then_rs_us": round(us_flatplan_rs, 2),
         "flatten_plan_ws_then_rs_us": round(us_flatplan_ws_rs, 2),
+        "flatten_plan_ws_then_rs_plan_us": round(us_plans, 2),
         "discrete_path_us": round(us_discrete, 2),
         "discrete_plan_us": round(us_plan, 2),
         "discrete_plan_ws_us": round(us_plan_ws, 2),

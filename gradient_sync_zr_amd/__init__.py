@@ -65,6 +65,7 @@ COST_EXPORTS = ("zr_cost_ring_allreduce", "zr_cost_ring_reduce_scatter", "zr_cos
                 "zr_cost_naive_allreduce", "zr_cost_pipelined_broadcast",
                 "zr_cost_best_broadcast_segments", "zr_cost_ring_tree_crossover",
                 "zr_cost_ring_naive_crossover", "zr_cost_dp_speedup")
+RS_PLAN_EXPORTS = ("zr_rs_plan_create", "zr_rs_plan_launch", "zr_rs_plan_destroy")
 RSF_PLAN_EXPORTS = ("zr_rsf_plan_create", "zr_rsf_plan_launch", "zr_rsf_plan_info", "zr_rsf_plan_destroy")
 FLAT_PLAN_EXPORTS = ("zr_flatten_plan_create", "zr_flatten_plan_launch", "zr_flatten_plan_info",
                      "zr_flatten_plan_destroy")
@@ -74,7 +75,7 @@ EXPORTS = ("zr_last_error", "zr_version", "zr_workspace_bytes", "zr_flatten_buck
            "zr_reduce_scatter_frags", "zr_all_gather", "zr_allreduce", "zr_plan_buckets", "zr_sched_create",
            "zr_sched_acquire", "zr_sched_submit_rs", "zr_sched_flush",
            "zr_sched_destroy", "zr_reduce_scatter_frags_noalloc") + COST_EXPORTS + PF_EXPORTS + \
-    RSF_PLAN_EXPORTS + FLAT_PLAN_EXPORTS
+    RSF_PLAN_EXPORTS + FLAT_PLAN_EXPORTS + RS_PLAN_EXPORTS
 
 
 class ZrError(RuntimeError):
@@ -148,6 +149,10 @@ def lib() -> ctypes.CDLL:
         L.zr_sched_destroy.argtypes = [_vp]
         L.zr_rsf_plan_create.argtypes = [_i32, _i32, _PP, ctypes.POINTER(_i64), _i64, _i32, _PP, _i32,
                                          _i32, _i32, _i32, _vp, _sz, ctypes.POINTER(_vp)]
+        L.zr_rs_plan_create.argtypes = [_i32, _PP, _i32, _i64, _PP, _i32, _i32, _i32, _i32,
+                                        ctypes.POINTER(_vp)]
+        L.zr_rs_plan_launch.argtypes = [_vp, _vp]
+        L.zr_rs_plan_destroy.argtypes = [_vp]
         L.zr_rsf_plan_launch.argtypes = [_vp, _vp]
         L.zr_rsf_plan_info.argtypes = [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_sz)]
         L.zr_rsf_plan_destroy.argtypes = [_vp]
@@ -342,6 +347,36 @@ def zr_reduce_scatter_avg(inputs: Sequence, N: int, outputs: Sequence, chunk_shi
     _check(lib().zr_reduce_scatter_avg(K, _table(inputs), in_dt, N, _table(outputs), out_dt,
                                        chunk_shift, _flags(average, accumulate), order,
                                        _stream(stream)))
+
+
+class RsPlan:
+    """zr_rs_plan_*: a reduce-scatter validated and built once; launch()
+    enqueues it on a stream (torch's current one by default)."""
+
+    def __init__(self, inputs: Sequence, N: int, outputs: Sequence, chunk_shift: int = 1,
+                 average: bool = True, order: int = ZR_ORDER_RING, in_dtype=None, out_dtype=None,
+                 accumulate: bool = False):
+        K = len(inputs)
+        in_dt = _dtype(in_dtype if in_dtype is not None else inputs[0])
+        out_dt = _dtype(out_dtype if out_dtype is not None else outputs[0])
+        h = ctypes.c_void_p()
+        _check(lib().zr_rs_plan_create(K, _table(inputs), in_dt, N, _table(outputs), out_dt, chunk_shift,
+                                       _flags(average, accumulate), order, ctypes.byref(h)))
+        self._h = h
+
+    def launch(self, stream=None) -> None:
+        _check(lib().zr_rs_plan_launch(self._h, _stream(stream)))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().zr_rs_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def zr_reduce_scatter_frags(frags: Sequence[Sequence], numels: Sequence[int], N: int,

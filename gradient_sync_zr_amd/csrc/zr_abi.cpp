@@ -652,6 +652,10 @@ struct zr_flatten_plan {
     zr::FlatPlan* plan;  // NULL: nothing to launch
 };
 
+struct zr_rs_plan {
+    zr::RsPlan* plan;  // NULL: nothing to launch (N == 0)
+};
+
 extern "C" {
 
 size_t zr_workspace_bytes(int K, int n) {
@@ -741,6 +745,49 @@ zr_status zr_reduce_scatter_frags(int K, int n_frag, const void* const* frags,
         return run_once<RsfPlan>(build, rsf_plan_table_bytes, rsf_plan_table_image, rsf_plan_launch, rsf_plan_free,
                                  workspace, (hipStream_t)stream, "discrete reduce-scatter launch");
     });
+}
+
+zr_status zr_rs_plan_create(int K, const void* const* in, zr_dtype in_dt, int64_t N, void* const* out,
+                            zr_dtype out_dt, int chunk_shift, int flags, zr_order order, zr_rs_plan** plan) {
+    return zr::guarded([&]() -> zr_status {
+        if (!plan) return fail(ZR_ERR_INVALID, "plan is NULL");
+        *plan = nullptr;
+        bool no_work = false;
+        ZR_TRY(validate_rs(K, in, in_dt, N, out, out_dt, chunk_shift, flags, order, &no_work));
+        RsPlan* p = nullptr;
+        if (!no_work) {
+            ConstPtrs ip{};
+            MutPtrs op{};
+            for (int r = 0; r < K; ++r) {
+                ip.p[r] = in[r];
+                op.p[r] = out[r];
+            }
+            p = rs_plan_build(K, ip, in_dt, N, op, out_dt, chunk_shift, flags, order);
+            if (!p) return fail(ZR_ERR_NOMEM, "out of host memory");
+        }
+        zr_rs_plan* h = new (std::nothrow) zr_rs_plan{p};
+        if (!h) {
+            if (p) rs_plan_free(p);
+            return fail(ZR_ERR_NOMEM, "out of host memory");
+        }
+        *plan = h;
+        return ok();
+    });
+}
+
+zr_status zr_rs_plan_launch(const zr_rs_plan* plan, void* stream) {
+    if (!plan) return fail(ZR_ERR_INVALID, "plan is NULL");
+    if (!plan->plan) return ok();
+    const hipError_t e = rs_plan_launch(plan->plan, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "reduce-scatter launch");
+    return ok();
+}
+
+zr_status zr_rs_plan_destroy(zr_rs_plan* plan) {
+    if (!plan) return ok();
+    if (plan->plan) rs_plan_free(plan->plan);
+    delete plan;
+    return ok();
 }
 
 zr_status zr_reduce_scatter_frags_noalloc(int K, int n_frag, const void* const* frags,

@@ -55,6 +55,14 @@ hipError_t launch_reduce_scatter(int K, const ConstPtrs& in, zr_dtype in_dt, int
                                  const MutPtrs& out, zr_dtype out_dt, int shift, int flags,
                                  zr_order order, hipStream_t stream);
 
+// A reduce-scatter prepared once (launch geometry and kernel chosen) and
+// launched many times. rs_plan_build returns NULL when host memory runs out.
+struct RsPlan;
+RsPlan* rs_plan_build(int K, const ConstPtrs& in, zr_dtype in_dt, int64_t N, const MutPtrs& out,
+                      zr_dtype out_dt, int shift, int flags, zr_order order);
+hipError_t rs_plan_launch(const RsPlan* plan, hipStream_t stream);
+void rs_plan_free(RsPlan* plan);
+
 hipError_t launch_allreduce_fused(int K, const ConstPtrs& in, const MutPtrs& out, zr_dtype dt,
                                   int64_t N, int average, zr_order order, hipStream_t stream);
 

@@ -28,13 +28,16 @@
 // vector tiles begin at an input element that starts a 128-byte line, so
 // the K input streams are read in whole lines, and whose output lies less
 // than a line after a 16 KiB boundary of the holder's partition, so the
-// tiles' writes fill aligned 16 KiB blocks. The first tile also folds the
-// head before it (at most 16 KiB of output plus a line) as quads and its
-// last few elements one by one, and the last tile folds its whole quads
-// below N as vectors and the few elements after them one by one. Chunks
+// tiles' writes fill aligned 16 KiB blocks. The head before that point (at
+// most 16 KiB of output plus a line) is cut into head tiles of its own, so
+// no block does more than a tile's work (one block folding the whole head
+// set the time of small launches): whole quads as vectors, its last few
+// elements one by one. The last tile folds its whole quads below N as
+// vectors and the few elements after them one by one. Chunks
 // whose start does not allow quad access fold element by element tile by
 // tile. Positions g >= N are padding and receive +0.
 #include <algorithm>
+#include <new>
 
 #include "zr_fold.hpp"
 
@@ -123,9 +126,9 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
             for (int k = 0; k < SS; ++k) store_quad<TOut, NT>(outp + o0 + 256 * k, pack4<TOut>(acc[k]));
         };
 
-        // a vector chunk's tiles cover [h, C), the last one possibly partial,
-        // and tile 0 also folds the head [0, h); other chunks go element-wise
-        // by tiles
+        // a vector chunk's tiles: first ceil(min(h, C) / T) head tiles over
+        // [0, h), then tiles over [h, C), the last one possibly partial;
+        // other chunks go element-wise by tiles
         if (!vec) {
             const int64_t lo = t * T;
             const int64_t hi = (lo + T < C) ? lo + T : C;
@@ -134,19 +137,34 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
         }
         const int64_t h = a.head[j];
         const int64_t valid = (N - chunk_base < C) ? N - chunk_base : C;  // non-padding extent
-        if (t == 0) {
-            // the head [0, h): its whole quads below the padding fold as
-            // vectors (one slice per pass), its other elements one by one
-            const int64_t hc = h < C ? h : C;
-            const int64_t lim = (valid < hc ? valid : hc) & ~(int64_t)3;  // < 0: all padding
-            for (int64_t o4 = (int64_t)threadIdx.x * 4; o4 + 4 <= lim; o4 += kThreads * 4) {
+        const int64_t hc = h < C ? h : C;
+        const int64_t nh = (hc + T - 1) / T;
+        if (t < nh) {
+            // head tile t covers [tT, min((t+1)T, hc)) on the tiles' quad grid
+            // (the chunk start is a quad boundary): a whole tile of whole quads
+            // below the padding folds as a main tile does; otherwise its whole
+            // quads below the padding fold as vectors (one slice per pass) and
+            // its other elements one by one
+            const int64_t lo = t * T;
+            const int64_t hi = lo + T < hc ? lo + T : hc;
+            if (hi - lo == T && hi <= valid) {
+                const int64_t o0 = lo + (int64_t)wave * (S * 256) + lane * 4;
+                float acc[S][4];
+                fold_quads<TIn, KS, NT, S, ORDER, kStatic>(bases, ptr, K, j, chunk_base + o0, acc);
+                emit(o0, acc, std::integral_constant<int, S>{});
+                continue;
+            }
+            const int64_t lim = (valid < hi ? valid : hi) & ~(int64_t)3;  // < lo: no whole quad
+#pragma unroll 1
+            for (int64_t o4 = lo + (int64_t)threadIdx.x * 4; o4 + 4 <= lim; o4 += kThreads * 4) {
                 float acc[1][4];
                 fold_quads<TIn, KS, NT, 1, ORDER, kStatic>(bases, ptr, K, j, chunk_base + o4, acc);
                 emit(o4, acc, std::integral_constant<int, 1>{});
             }
-            for (int64_t o = (lim > 0 ? lim : 0) + threadIdx.x; o < hc; o += kThreads) elem(o);
+            for (int64_t o = (lim > lo ? lim : lo) + threadIdx.x; o < hi; o += kThreads) elem(o);
+            continue;
         }
-        const int64_t ot = h + t * T;
+        const int64_t ot = h + (t - nh) * T;
         if (ot >= C) continue;
         const int64_t o0 = ot + (int64_t)wave * (S * 256) + lane * 4;
         if (ot + T <= valid) {
@@ -188,31 +206,34 @@ hipError_t launch_t(const RsArgs& a, hipStream_t stream) {
 // ranks in flight). With fp32 input the wire order is the ring order
 // (rounding every hop to fp32 is what the fp32 adds already do). Small
 // launches in the ring order use one slice per wave.
+using LaunchFn = hipError_t (*)(const RsArgs&, hipStream_t);
+
 template <typename TIn, typename TOut, int AVG>
-hipError_t pick_k(const RsArgs& a, int order, bool small, hipStream_t s) {
+LaunchFn pick_k(int K, int order, bool small) {
     constexpr int S = kSlices<TIn, TOut>;
     constexpr bool NT = kRsNontemporal;
-    if (order == kFree) return launch_t<TIn, TOut, 0, AVG, kFree, NT, S>(a, s);
+    if (order == kFree) return &launch_t<TIn, TOut, 0, AVG, kFree, NT, S>;
     if (order == kWire && sizeof(TIn) == 2) {
-        if (a.K == 8) return launch_t<TIn, TOut, 8, AVG, kWire, NT, S>(a, s);
-        return launch_t<TIn, TOut, 0, AVG, kWire, NT, S>(a, s);
+        if (K == 8) return &launch_t<TIn, TOut, 8, AVG, kWire, NT, S>;
+        return &launch_t<TIn, TOut, 0, AVG, kWire, NT, S>;
     }
-    if (a.K == 8)
-        return small ? launch_t<TIn, TOut, 8, AVG, kRing, NT, 1>(a, s) : launch_t<TIn, TOut, 8, AVG, kRing, NT, S>(a, s);
-    return small ? launch_t<TIn, TOut, 0, AVG, kRing, NT, 1>(a, s) : launch_t<TIn, TOut, 0, AVG, kRing, NT, S>(a, s);
+    if (K == 8) return small ? &launch_t<TIn, TOut, 8, AVG, kRing, NT, 1> : &launch_t<TIn, TOut, 8, AVG, kRing, NT, S>;
+    return small ? &launch_t<TIn, TOut, 0, AVG, kRing, NT, 1> : &launch_t<TIn, TOut, 0, AVG, kRing, NT, S>;
 }
 
 template <typename TIn, typename TOut>
-hipError_t pick_avg(const RsArgs& a, int avg_mode, int order, bool small, hipStream_t s) {
+LaunchFn pick_avg(int K, int avg_mode, int order, bool small) {
     switch (avg_mode) {
-        case 1: return pick_k<TIn, TOut, 1>(a, order, small, s);
-        case 2: return pick_k<TIn, TOut, 2>(a, order, small, s);
-        default: return pick_k<TIn, TOut, 0>(a, order, small, s);
+        case 1: return pick_k<TIn, TOut, 1>(K, order, small);
+        case 2: return pick_k<TIn, TOut, 2>(K, order, small);
+        default: return pick_k<TIn, TOut, 0>(K, order, small);
     }
 }
 
+// Fills the launch geometry of `a` (vector chunks, heads, tiles per chunk and
+// pair) and returns the kernel that runs it.
 template <typename TIn, typename TOut>
-hipError_t launch_typed(RsArgs& a, int avg_mode, int order, hipStream_t s) {
+LaunchFn prepare_typed(RsArgs& a, int avg_mode, int order) {
     constexpr int64_t T = kRsTile<TIn, TOut>;
     const bool small = order == kRing && ((a.C + T - 1) / T) * a.K < 2LL * device_cu_count();
     const int64_t Tl = small ? kRsTileOf<1> : T;
@@ -243,12 +264,17 @@ hipError_t launch_typed(RsArgs& a, int avg_mode, int order, hipStream_t s) {
         const int64_t to_block = (int64_t)((kOutBlock - ob % kOutBlock) % kOutBlock / sizeof(TOut));
         a.head[j] = (int16_t)(to_block + ((to_line - to_block) % line + line) % line);
     }
-    // tiles of each chunk: a vector chunk's cover [head, C) (at least one,
-    // which folds the head), another chunk's cover [0, C); chunks go in
-    // pairs, a pair's blocks alternating between its two chunks
+    // tiles of each chunk: a vector chunk's head tiles cover [0, min(head, C))
+    // and its other tiles [head, C); another chunk's cover [0, C); chunks go
+    // in pairs, a pair's blocks alternating between its two chunks
     for (int j = 0; j < a.K; ++j) {
-        const int64_t h = ((a.vec_mask >> j) & 1ull) ? a.head[j] : 0;
-        a.ntile[j] = ((a.vec_mask >> j) & 1ull) ? (a.C > h ? (a.C - h + Tl - 1) / Tl : 1) : (a.C + Tl - 1) / Tl;
+        if ((a.vec_mask >> j) & 1ull) {
+            const int64_t h = a.head[j];
+            const int64_t hc = h < a.C ? h : a.C;
+            a.ntile[j] = (hc + Tl - 1) / Tl + (a.C > h ? (a.C - h + Tl - 1) / Tl : 0);
+        } else {
+            a.ntile[j] = (a.C + Tl - 1) / Tl;
+        }
     }
     a.npairs = (a.K + 1) / 2;
     int64_t tiles = 0;
@@ -257,15 +283,16 @@ hipError_t launch_typed(RsArgs& a, int avg_mode, int order, hipStream_t s) {
         tiles += 2 * q + 1 < a.K ? 2 * std::max(a.ntile[2 * q], a.ntile[2 * q + 1]) : a.ntile[2 * q];
     }
     a.tile0[a.npairs] = tiles;
-    return pick_avg<TIn, TOut>(a, avg_mode, order, small, s);
+    return pick_avg<TIn, TOut>(a.K, avg_mode, order, small);
 }
 
 }  // namespace
 
-hipError_t launch_reduce_scatter(int K, const ConstPtrs& in, zr_dtype in_dt, int64_t N,
-                                 const MutPtrs& out, zr_dtype out_dt, int shift, int flags,
-                                 zr_order order, hipStream_t stream) {
-    RsArgs a;
+namespace {
+
+// The launch of one reduce-scatter: its arguments and the kernel that runs them.
+LaunchFn prepare(RsArgs& a, int K, const ConstPtrs& in, zr_dtype in_dt, int64_t N, const MutPtrs& out,
+                 zr_dtype out_dt, int shift, int flags, zr_order order) {
     a.in = in;
     a.out = out;
     a.N = N;
@@ -278,10 +305,37 @@ hipError_t launch_reduce_scatter(int K, const ConstPtrs& in, zr_dtype in_dt, int
     const bool pow2 = (K & (K - 1)) == 0;
     const int avg_mode = !(flags & ZR_AVERAGE) ? 0 : (pow2 ? 1 : 2);
     const int ord = order == ZR_ORDER_FREE ? kFree : (order == ZR_ORDER_RING_WIRE ? kWire : kRing);
-    if (in_dt == ZR_BF16 && out_dt == ZR_FP32) return launch_typed<uint16_t, float>(a, avg_mode, ord, stream);
-    if (in_dt == ZR_BF16 && out_dt == ZR_BF16) return launch_typed<uint16_t, uint16_t>(a, avg_mode, ord, stream);
-    if (in_dt == ZR_FP32 && out_dt == ZR_FP32) return launch_typed<float, float>(a, avg_mode, ord, stream);
-    return launch_typed<float, uint16_t>(a, avg_mode, ord, stream);
+    if (in_dt == ZR_BF16 && out_dt == ZR_FP32) return prepare_typed<uint16_t, float>(a, avg_mode, ord);
+    if (in_dt == ZR_BF16 && out_dt == ZR_BF16) return prepare_typed<uint16_t, uint16_t>(a, avg_mode, ord);
+    if (in_dt == ZR_FP32 && out_dt == ZR_FP32) return prepare_typed<float, float>(a, avg_mode, ord);
+    return prepare_typed<float, uint16_t>(a, avg_mode, ord);
+}
+
+}  // namespace
+
+struct RsPlan {
+    RsArgs a;
+    LaunchFn fn;
+};
+
+RsPlan* rs_plan_build(int K, const ConstPtrs& in, zr_dtype in_dt, int64_t N, const MutPtrs& out,
+                      zr_dtype out_dt, int shift, int flags, zr_order order) {
+    RsPlan* p = new (std::nothrow) RsPlan();
+    if (!p) return nullptr;
+    p->fn = prepare(p->a, K, in, in_dt, N, out, out_dt, shift, flags, order);
+    return p;
+}
+
+hipError_t rs_plan_launch(const RsPlan* p, hipStream_t stream) { return p->fn(p->a, stream); }
+
+void rs_plan_free(RsPlan* p) { delete p; }
+
+hipError_t launch_reduce_scatter(int K, const ConstPtrs& in, zr_dtype in_dt, int64_t N,
+                                 const MutPtrs& out, zr_dtype out_dt, int shift, int flags,
+                                 zr_order order, hipStream_t stream) {
+    RsArgs a;
+    const LaunchFn fn = prepare(a, K, in, in_dt, N, out, out_dt, shift, flags, order);
+    return fn(a, stream);
 }
 
 }  // namespace zr

@@ -31,9 +31,9 @@
 // striding over the tiles ran 7-15% slower). A segment whose rank buffers share one quad phase starts
 // its vector tiles at a 128-byte line of rank j whose output lies less than
 // a line after a 16 KiB boundary of the partition, as the contiguous kernel
-// does: the first tile also folds the head before it (as quads, and its
-// edge elements one by one), the last folds its whole quads as vectors and
-// the last few elements one by one, and the stores fall back to single
+// does: the head before it goes to head tiles of its own (as quads, and its
+// edge elements one by one), the last tile folds its whole quads as vectors
+// and the last few elements one by one, and the stores fall back to single
 // elements when the partition side is not quad aligned. Other segments fold
 // element by element, 1024 elements per tile. The padding entry has null
 // pointers, starts its tiles on a 16 KiB boundary of the partition and
@@ -218,22 +218,28 @@ __device__ __forceinline__ void rsf_body(const RsfCommon& c, const Tab& tab) {
                 fold_quads<TIn, KS, NT, SS, ORDER, kStatic>(bases, ptr, K, j, l_lo + o0, acc);
             }
         };
-        // tiles cover [h, len), the last one possibly partial; tile 0 also
-        // folds the head [0, h): as quads from the first offset on the
-        // tiles' quad grid (h mod 4), its other elements one by one
-        if (tt == 0) {
-            const int64_t hc = h < len ? h : len;
-            const int64_t q0 = h & 3;
-            for (int64_t o = threadIdx.x; o < q0 && o < hc; o += kThreads) elem(o);
-            const int64_t qe = hc > q0 ? q0 + ((hc - q0) & ~(int64_t)3) : q0;
+        // head tiles over [0, min(h, len)), ceil(that / T) of them, then tiles
+        // over [h, len), the last one possibly partial. Head tile tt covers
+        // [tt T, min((tt+1) T, hc)): quads on the tiles' quad grid (offsets
+        // congruent to h mod 4), its other elements one by one
+        const int64_t hc = h < len ? h : len;
+        const int64_t nh = (hc + T - 1) / T;
+        if (tt < nh) {
+            const int64_t lo = tt * T;
+            const int64_t hi = lo + T < hc ? lo + T : hc;
+            const int64_t q0 = lo + (h & 3);  // lo is a multiple of 4
+            for (int64_t o = lo + threadIdx.x; o < q0 && o < hi; o += kThreads) elem(o);
+            const int64_t qe = hi > q0 ? q0 + ((hi - q0) & ~(int64_t)3) : q0;
+#pragma unroll 1
             for (int64_t q = q0 + (int64_t)threadIdx.x * 4; q < qe; q += kThreads * 4) {
                 float acc[1][4];
                 fold(q, acc, std::integral_constant<int, 1>{});
                 emit(q, acc, std::integral_constant<int, 1>{});
             }
-            for (int64_t o = qe + threadIdx.x; o < hc; o += kThreads) elem(o);
+            for (int64_t o = (qe > lo ? qe : lo) + threadIdx.x; o < hi; o += kThreads) elem(o);
+            continue;
         }
-        const int64_t ot = h + tt * T;
+        const int64_t ot = h + (tt - nh) * T;
         if (ot >= len) continue;
         const int64_t o0 = ot + (int64_t)wave * (S * 256) + lane * 4;
         if (ot + T <= len) {
@@ -383,7 +389,9 @@ void segments_of(const RsfCommon& c, const FragEntry* entries, int n_entries, in
                     addr[r] = (uintptr_t)f.ptr[r] + (uintptr_t)(lo - f.off) * sizeof(TIn);
                 h = segment_head(addr, K, j, sizeof(TIn), o, sizeof(TOut));
             }
-            const int64_t tiles = h < 0 ? (len + kElemTile - 1) / kElemTile : (len > h ? (len - h + T - 1) / T : 1);
+            const int64_t hc = h < len ? h : len;
+            const int64_t tiles = h < 0 ? (len + kElemTile - 1) / kElemTile
+                                        : (hc + T - 1) / T + (len > h ? (len - h + T - 1) / T : 0);
             segs->push_back(SegDesc{ei, j, h, tiles});
         }
         first->push_back((int64_t)segs->size());

@@ -221,6 +221,21 @@ zr_status zr_reduce_scatter_avg(int K, const void* const* in, zr_dtype in_dt, in
                                 int flags /* ZR_AVERAGE | ZR_ACCUMULATE */, zr_order order,
                                 void* stream);
 
+/* A reduce-scatter prepared once and launched many times, for a bucket whose
+ * buffers keep their addresses from step to step: zr_rs_plan_create
+ * validates the arguments and builds the launch (vector chunks, heads, tile
+ * numbering, kernel), and each zr_rs_plan_launch only enqueues it. Arguments
+ * and results are exactly those of zr_reduce_scatter_avg (flags fixed at
+ * create). The plan keeps the buffers' addresses, not their contents; it owns
+ * only host memory; N == 0 gives a plan that launches nothing. */
+typedef struct zr_rs_plan zr_rs_plan;
+
+zr_status zr_rs_plan_create(int K, const void* const* in, zr_dtype in_dt, int64_t N, void* const* out,
+                            zr_dtype out_dt, int chunk_shift, int flags, zr_order order,
+                            zr_rs_plan** plan);
+zr_status zr_rs_plan_launch(const zr_rs_plan* plan, void* stream);
+zr_status zr_rs_plan_destroy(zr_rs_plan* plan);
+
 /*
  * Reduce-scatter straight from fragmented gradients, the discrete path
  * [ZERO3 5.2 (discrete path), 3.2]: bit for bit the result of

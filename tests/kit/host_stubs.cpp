@@ -17,6 +17,15 @@ hipError_t launch_reduce_scatter(int, const ConstPtrs&, zr_dtype, int64_t, const
     return hipErrorNotSupported;
 }
 
+struct RsPlan {
+    int K;
+};
+RsPlan* rs_plan_build(int K, const ConstPtrs&, zr_dtype, int64_t, const MutPtrs&, zr_dtype, int, int, zr_order) {
+    return new RsPlan{K};
+}
+hipError_t rs_plan_launch(const RsPlan*, hipStream_t) { return hipErrorNotSupported; }
+void rs_plan_free(RsPlan* plan) { delete plan; }
+
 hipError_t launch_allreduce_fused(int, const ConstPtrs&, const MutPtrs&, zr_dtype, int64_t, int, zr_order,
                                   hipStream_t) {
     return hipErrorNotSupported;

@@ -486,3 +486,24 @@ def test_plans_without_workspace_count_their_launches(K, F):
         assert info(h, ctypes.byref(n), ctypes.byref(b)) == zr.ZR_OK
         assert n.value == -(-F // per) and b.value == 0
         assert destroy(h) == zr.ZR_OK
+
+
+def test_rs_plan_validation_matches_the_call():
+    # a plan is validated exactly as the one-shot call; N == 0 plans launch nothing
+    lib = zr.lib()
+    K = 8
+    ins = (ctypes.c_void_p * K)(*ranks(K))
+    outs = (ctypes.c_void_p * K)(*ranks(K, base=A + (1 << 40)))
+    bad_outs = (ctypes.c_void_p * K)(*ranks(K, base=A + (1 << 40), stride=4))
+    for N, o, shift, flags, want in ((1000, outs, 1, 1, zr.ZR_OK), (0, outs, 1, 1, zr.ZR_OK),
+                                     (1000, bad_outs, 1, 1, zr.ZR_ERR_ALIAS), (1000, outs, 8, 1, zr.ZR_ERR_INVALID),
+                                     (1000, outs, 1, 4, zr.ZR_ERR_INVALID), (-1, outs, 1, 1, zr.ZR_ERR_INVALID)):
+        h = ctypes.c_void_p()
+        st = lib.zr_rs_plan_create(K, ins, 0, N, o, 1, shift, flags, 0, ctypes.byref(h))
+        assert st == want, (N, shift, flags, zr.zr_last_error())
+        if st == zr.ZR_OK:
+            if N == 0:
+                assert lib.zr_rs_plan_launch(h, None) == zr.ZR_OK
+            assert lib.zr_rs_plan_destroy(h) == zr.ZR_OK
+        else:
+            assert h.value is None

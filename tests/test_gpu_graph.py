@@ -4,7 +4,7 @@ The library's calls allocate nothing, issue no memset and never synchronise
 the device, so a caller can capture them. One graph holds a reduce-scatter,
 an accumulating reduce-scatter, a discrete reduce-scatter (the one-shot call
 and a prepared plan), a bucket flatten, a fused and a composed all-reduce
-(out of place) and an all-gather; and, for a bucket of more fragments than
+(out of place), an all-gather and a prepared reduce-scatter plan; and, for a bucket of more fragments than
 one argument block holds, a discrete plan and a flatten plan whose tables
 were staged in workspaces at creation (one launch each), and a one-shot
 discrete call given a workspace, which under capture goes out as argument
@@ -44,6 +44,7 @@ def test_graph_replays_match_eager_calls():
 
     def outputs():
         return dict(rs=[torch.empty(C, dtype=torch.float32, device="cuda") for _ in range(K)],
+                    rsplan=[torch.empty(C, dtype=torch.float32, device="cuda") for _ in range(K)],
                     acc=[torch.empty(C, dtype=torch.float32, device="cuda") for _ in range(K)],
                     frag=[torch.empty(CF, dtype=torch.float32, device="cuda") for _ in range(K)],
                     plan=[torch.empty(CF, dtype=torch.float32, device="cuda") for _ in range(K)],
@@ -60,6 +61,8 @@ def test_graph_replays_match_eager_calls():
         return torch.empty(zr.zr_workspace_bytes(K, len(MANY)), dtype=torch.uint8, device="cuda")
 
     g_out, e_out = outputs(), outputs()
+    g_rsplan = zr.RsPlan(x, N, g_out["rsplan"], chunk_shift=1, average=True)
+    e_rsplan = zr.RsPlan(x, N, e_out["rsplan"], chunk_shift=1, average=True)
     g_plan = zr.RsfPlan(frags, SIZES, NF, g_out["plan"], chunk_shift=1, average=True)
     e_plan = zr.RsfPlan(frags, SIZES, NF, e_out["plan"], chunk_shift=1, average=True)
     g_wsplan = zr.RsfPlan(many, MANY, NM, g_out["wsplan"], workspace=ws())
@@ -69,8 +72,9 @@ def test_graph_replays_match_eager_calls():
     assert g_wsplan.info()["launches"] == 1 and g_wsflat.info()["launches"] == 1
     g_ws, e_ws = ws(), ws()
 
-    def work(o, plan, wsplan, wsflat, wsbuf):
+    def work(o, plan, wsplan, wsflat, wsbuf, rsplan):
         zr.zr_reduce_scatter_avg(x, N, o["rs"], chunk_shift=1, average=True)
+        rsplan.launch()
         zr.zr_reduce_scatter_avg(x, N, o["acc"], chunk_shift=1, average=True, accumulate=True)
         zr.zr_reduce_scatter_frags(frags, SIZES, NF, o["frag"], chunk_shift=1, average=True)
         plan.launch()
@@ -100,25 +104,25 @@ def test_graph_replays_match_eager_calls():
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        work(g_out, g_plan, g_wsplan, g_wsflat, g_ws)  # warm-up outside the capture
+        work(g_out, g_plan, g_wsplan, g_wsflat, g_ws, g_rsplan)  # warm-up outside the capture
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
-        work(g_out, g_plan, g_wsplan, g_wsflat, g_ws)
+        work(g_out, g_plan, g_wsplan, g_wsflat, g_ws, g_rsplan)
     torch.cuda.synchronize()
     for tag in (1, 2, 3):
         fill(tag)
         graph.replay()
         torch.cuda.synchronize()
-        work(e_out, e_plan, e_wsplan, e_wsflat, e_ws)
+        work(e_out, e_plan, e_wsplan, e_wsflat, e_ws, e_rsplan)
         torch.cuda.synchronize()
-        for key in ("rs", "acc", "frag", "plan", "flat", "ar", "arc", "ag", "wsplan", "wscall",
-                    "wsflat"):
+        for key in ("rs", "rsplan", "acc", "frag", "plan", "flat", "ar", "arc", "ag", "wsplan",
+                    "wscall", "wsflat"):
             for r in range(K):
                 got = g_out[key][r].cpu()
                 want = e_out[key][r].cpu()
                 if got.dtype == torch.bfloat16:
                     got, want = got.view(torch.int16), want.view(torch.int16)
                 assert np.array_equal(bits(got.numpy()), bits(want.numpy())), (tag, key, r)
-    for p in (g_plan, e_plan, g_wsplan, e_wsplan, g_wsflat, e_wsflat):
+    for p in (g_plan, e_plan, g_wsplan, e_wsplan, g_wsflat, e_wsflat, g_rsplan, e_rsplan):
         p.close()

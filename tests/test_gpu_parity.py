@@ -79,17 +79,28 @@ RS_CASES = [
 ]
 
 
+@pytest.mark.parametrize("entry", ["call", "plan"])
 @pytest.mark.parametrize("K,N,in_bf16,out_bf16,shift,average,offset", RS_CASES)
-def test_reduce_scatter_ring_bit_exact(K, N, in_bf16, out_bf16, shift, average, offset):
+def test_reduce_scatter_ring_bit_exact(K, N, in_bf16, out_bf16, shift, average, offset, entry):
+    # the one-shot call, and a plan built once and launched twice
     import torch
     case = K * 1000003 + N
     xs = make_inputs(K, N, in_bf16, case)
     C = -(-N // K)
     ins = [Guarded(N, torch_dt(in_bf16), offset, xs[r]) for r in range(K)]
     outs = [Guarded(C, torch_dt(out_bf16), offset) for _ in range(K)]
-    zr().zr_reduce_scatter_avg([g.ptr() for g in ins], N, [g.ptr() for g in outs],
-                               chunk_shift=shift, average=average, in_dtype=torch_dt(in_bf16),
-                               out_dtype=torch_dt(out_bf16))
+    kw = dict(chunk_shift=shift, average=average, in_dtype=torch_dt(in_bf16),
+              out_dtype=torch_dt(out_bf16))
+    if entry == "call":
+        zr().zr_reduce_scatter_avg([g.ptr() for g in ins], N, [g.ptr() for g in outs], **kw)
+    else:
+        plan = zr().RsPlan([g.ptr() for g in ins], N, [g.ptr() for g in outs], **kw)
+        plan.launch()
+        torch.cuda.synchronize()
+        for g in outs:
+            g.t.view(torch.int16 if out_bf16 else torch.int32).fill_(-1)
+        plan.launch()
+        plan.close()
     torch.cuda.synchronize()
     want = oracle.reduce_scatter(xs, N, np.uint16 if out_bf16 else np.float32, shift=shift,
                                  average=average)
