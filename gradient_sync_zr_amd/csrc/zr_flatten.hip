@@ -21,14 +21,13 @@
 // plain copy).
 //
 // A tile is 4 KiB of destination: lane l of wave w moves the 16-byte unit
-// w*64 + l, so every load and store instruction of a wave covers 1 KiB
-// contiguously; loads and stores are non-temporal (each byte is touched
-// once). (At one block per tile a plain copy ran 10-15% faster with 4 KiB
-// tiles than with 16 KiB tiles of four units per lane; in the flatten the
-// two sizes measure the same, and one size needs no small-launch mode.) A copy whose source
-// and destination both start 16-byte aligned moves whole units; its last
-// partial unit, and every unit of a copy that is not aligned so (possible
-// inside a bucket, where offsets are prefix sums of arbitrary sizes), copies
+// w*64 + l, so every store instruction of a wave covers 1 KiB contiguously;
+// loads and stores are non-temporal (each byte is touched once). (At one
+// block per tile 4 KiB tiles ran 8% faster than 8 or 16 KiB tiles.) Units
+// are aligned to the destination, whose offsets inside a bucket are prefix
+// sums of arbitrary sizes; a source in another 16-byte phase is read as
+// aligned 16-byte blocks and realigned in registers, so every whole unit
+// moves with 16-byte accesses; only a copy's partial first and last units go
 // element by element.
 #include <cstring>
 #include <new>
@@ -40,9 +39,8 @@
 namespace zr {
 namespace {
 
-// 16-byte units per lane, and the tile they make.
-constexpr int kUnits = 1;
-constexpr int64_t kFlatTileBytes = (int64_t)kThreads * 16 * kUnits;
+// One 16-byte unit per lane: a tile is 4 KiB of destination.
+constexpr int64_t kFlatTileBytes = (int64_t)kThreads * 16;
 
 // Entry slots: fragments with source pointers, plus one for the padding.
 constexpr int kFlatSlots = kFlatEntriesPerLaunch + 1;
@@ -119,6 +117,36 @@ struct FlatWsTable {
     __device__ __forceinline__ const void* src(int64_t m, int K, int r) const { return srcs[m * K + r]; }
 };
 
+// 16 bytes starting `sig` bytes into the 32 bytes lo:hi (sig in 1..15, a
+// multiple of the element size): each output dword joins two neighbouring
+// input dwords with one byte-align instruction.
+__device__ __forceinline__ u32x4 shift16(const u32x4& lo, const u32x4& hi, uint32_t sig) {
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    const uint32_t b = sig & 3;
+    u32x4 r;
+#define ZR_SHIFT16(q)                                                   \
+    r = u32x4{__builtin_amdgcn_alignbyte(w[(q) + 1], w[(q)], b),          \
+              __builtin_amdgcn_alignbyte(w[(q) + 2], w[(q) + 1], b),      \
+              __builtin_amdgcn_alignbyte(w[(q) + 3], w[(q) + 2], b),      \
+              __builtin_amdgcn_alignbyte(w[(q) + 4], w[(q) + 3], b)}
+    switch (sig >> 2) {  // uniform: the phase of a whole (fragment, rank) copy
+        case 0: ZR_SHIFT16(0); break;
+        case 1: ZR_SHIFT16(1); break;
+        case 2: ZR_SHIFT16(2); break;
+        default: ZR_SHIFT16(3); break;
+    }
+#undef ZR_SHIFT16
+    return r;
+}
+
+// Units are 16-byte blocks of the destination, counted from the block that
+// holds the copy's first byte. A unit wholly inside the copy is stored as
+// one aligned 16-byte store; its 16 source bytes come from one aligned load
+// when source and destination share their phase within 16 bytes, else from
+// the two aligned 16-byte blocks that hold them (both hold bytes of the
+// fragment, so neither read leaves its pages), joined in registers. The
+// first and last units, when partial, copy element by element (all loads of
+// a lane before its stores).
 template <typename T, typename Tab>
 __device__ __forceinline__ void flatten_body(const FlatCommon& c, const Tab& tab) {
     constexpr int per = 16 / sizeof(T);  // elements per 16-byte unit
@@ -132,51 +160,35 @@ __device__ __forceinline__ void flatten_body(const FlatCommon& c, const Tab& tab
         const Index tt = t - tab.first(m);
         const int r = (int)(tt / (Index)fe.tpr);  // the entry's tiles run rank by rank
         const int64_t lt = tt - (int64_t)r * fe.tpr;
-        const int64_t n = fe.n;
         const T* src = m == c.pad_m ? nullptr : static_cast<const T*>(tab.src(m, c.K, r));
         T* dst = static_cast<T*>(c.bucket.p[r]) + fe.off;
-        const bool vec = ((((uintptr_t)dst) & 15) == 0) && (src == nullptr || (((uintptr_t)src) & 15) == 0);
-        const int64_t u0 = lt * (kFlatTileBytes / 16) + wave * 64 * kUnits + lane;  // first unit
-        if (vec && (u0 + 64 * (kUnits - 1) + 1) * per <= n) {
-            // every unit of this lane is whole
-            u32x4 v[kUnits];
-#pragma unroll
-            for (int k = 0; k < kUnits; ++k)
-                v[k] = src ? ld<true>(reinterpret_cast<const u32x4*>(src + (u0 + 64 * k) * per))
-                           : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int k = 0; k < kUnits; ++k)
-                st<true>(reinterpret_cast<u32x4*>(dst + (u0 + 64 * k) * per), v[k]);
-            continue;
-        }
-        // some unit of this lane is partial or unaligned: every load is issued
-        // before the first store (a store may not overtake the loads, so the
-        // lane waits on one memory latency, not one per element)
-        u32x4 vv[kUnits];
-        T ev[kUnits][per];
-        int cnt[kUnits];
-#pragma unroll
-        for (int k = 0; k < kUnits; ++k) {
-            const int64_t e0 = (u0 + 64 * k) * per;
-            cnt[k] = e0 >= n ? 0 : (int)((n - e0) < per ? (n - e0) : per);
-            if (vec && cnt[k] == per) {
-                vv[k] = src ? ld<true>(reinterpret_cast<const u32x4*>(src + e0)) : u32x4{0u, 0u, 0u, 0u};
-            } else {
-#pragma unroll
-                for (int e = 0; e < per; ++e)
-                    if (e < cnt[k]) ev[k][e] = src ? src[e0 + e] : T(0);
+        const uintptr_t d0 = (uintptr_t)dst, d1 = d0 + (uintptr_t)fe.n * sizeof(T);
+        const uintptr_t ub = (d0 & ~(uintptr_t)15) +
+                             16 * (uintptr_t)(lt * (kFlatTileBytes / 16) + wave * 64 + lane);
+        if (ub >= d0 && ub + 16 <= d1) {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (src) {
+                const uintptr_t sb = (uintptr_t)src + (ub - d0);
+                const uint32_t sig = (uint32_t)(sb & 15);
+                const u32x4* a = reinterpret_cast<const u32x4*>(sb & ~(uintptr_t)15);
+                if (sig == 0) {
+                    v = ld<true>(a);
+                } else {
+                    const u32x4 lo = ld<true>(a), hi = ld<true>(a + 1);
+                    v = shift16(lo, hi, sig);
+                }
             }
-        }
+            st<true>(reinterpret_cast<u32x4*>(ub), v);
+        } else if (ub < d1 && ub + 16 > d0) {
+            const int64_t e0 = (int64_t)(((ub > d0 ? ub : d0) - d0) / sizeof(T));
+            const int64_t e1 = (int64_t)(((ub + 16 < d1 ? ub + 16 : d1) - d0) / sizeof(T));
+            T ev[per];
 #pragma unroll
-        for (int k = 0; k < kUnits; ++k) {
-            const int64_t e0 = (u0 + 64 * k) * per;
-            if (vec && cnt[k] == per) {
-                st<true>(reinterpret_cast<u32x4*>(dst + e0), vv[k]);
-            } else {
+            for (int e = 0; e < per; ++e)
+                if (e0 + e < e1) ev[e] = src ? src[e0 + e] : T(0);
 #pragma unroll
-                for (int e = 0; e < per; ++e)
-                    if (e < cnt[k]) dst[e0 + e] = ev[k][e];
-            }
+            for (int e = 0; e < per; ++e)
+                if (e0 + e < e1) dst[e0 + e] = ev[e];
         }
     }
 }
@@ -192,6 +204,18 @@ __global__ void __launch_bounds__(kThreads) flatten_ws_kernel(const FlatWsArgs a
 }
 
 int64_t tiles_of(int64_t bytes, int64_t tile) { return (bytes + tile - 1) / tile; }
+
+// Tiles per rank of a copy of n elements to bucket offset `off` (elements):
+// its units start at the 16-byte block holding its first byte on every rank,
+// so a rank whose copy starts b bytes into a block needs room for b + n*es.
+int64_t tiles_per_rank(const MutPtrs& buckets, int K, int64_t off, int64_t n, int elem_bytes) {
+    int64_t lead = 0;
+    for (int r = 0; r < K; ++r) {
+        const int64_t b = (int64_t)(((uintptr_t)buckets.p[r] + (uintptr_t)off * elem_bytes) & 15);
+        lead = b > lead ? b : lead;
+    }
+    return tiles_of(lead + n * elem_bytes, kFlatTileBytes);
+}
 
 // Cuts the entries into argument launches of at most 32 fragments (256
 // source pointers) plus the padding entry if it comes next, and about 2^29
@@ -223,7 +247,7 @@ void cut_args(const FlatCommon& c, const FragEntry* entries, int n_entries, int 
         const bool is_pad = f.ptr[0] == nullptr;
         for (int64_t o = 0; o < f.n; o += piece) {
             const int64_t pn = f.n - o < piece ? f.n - o : piece;
-            const int64_t tpr = tiles_of(pn * elem_bytes, kFlatTileBytes);
+            const int64_t tpr = tiles_per_rank(c.bucket, K, f.off + o, pn, elem_bytes);
             if (count == (is_pad ? max_entries + 1 : max_entries) || a.c.pad_m >= 0 ||
                 tiles + (int64_t)K * tpr > (1LL << 29))
                 flush();
@@ -279,7 +303,7 @@ FlatPlan* flat_plan_build(int K, const FragEntry* entries, int n_entries, const 
                 const FragEntry& f = entries[m];
                 if (f.ptr[0] == nullptr) c.pad_m = m;
                 tile0[m] = tiles;
-                tpr[m] = tiles_of(f.n * elem_bytes, kFlatTileBytes);
+                tpr[m] = tiles_per_rank(buckets, K, f.off, f.n, elem_bytes);
                 en[2 * m] = f.off;
                 en[2 * m + 1] = f.n;
                 for (int r = 0; r < K; ++r) src[(size_t)m * K + r] = (uint64_t)(uintptr_t)f.ptr[r];

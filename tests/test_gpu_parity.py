@@ -400,6 +400,59 @@ def test_flatten_bit_exact(K, sizes, bf16, offset, extra, ws):
         assert buckets[r].guards_intact()
 
 
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("ws", [False, True], ids=["args", "workspace"])
+def test_flatten_every_phase_pair(bf16, ws):
+    # every (source, destination) phase within 16 bytes: fragments are views
+    # at element offsets 0..per-1 into one buffer per rank, and their bucket
+    # offsets (prefix sums of their sizes) fall in every phase; each pair is
+    # copied by whole realigned units between partial first and last units
+    import torch
+    K = 4
+    per = 8 if bf16 else 4
+    F = per * per
+    rng = np.random.default_rng(4242 + bf16)
+    # fragment p: source phase p % per, bucket phase p // per (sizes chosen so
+    # the prefix sums land there, gaps in the buffers so the views do)
+    sizes = []
+    for p_ in range(F):
+        delta = ((p_ + 1) // per - p_ // per) % per
+        sizes.append(per * int(rng.integers(0, 300)) + delta or per)
+    dt = np.uint16 if bf16 else np.float32
+    frags_np, fp, bufs, pairs = [], [], [], set()
+    for r in range(K):
+        row = [synth.host_normal_bf16(SEED + 17, r * 4096 + p_, 0, n, 1.0) for p_, n in enumerate(sizes)]
+        row = row if bf16 else [oracle.bf16_to_f32(h) for h in row]
+        frags_np.append(row)
+        offs, o = [], 0
+        for p_, n in enumerate(sizes):
+            o += (p_ - o) % per
+            offs.append(o)
+            o += n
+        host = np.zeros(o, dtype=dt)
+        for p_, n in enumerate(sizes):
+            host[offs[p_]:offs[p_] + n] = row[p_]
+        g = Guarded(o, torch_dt(bf16), 0, host)
+        bufs.append(g)
+        es = 2 if bf16 else 4
+        fp.append([g.ptr() + es * offs[p_] for p_ in range(F)])
+        boff = 0
+        for p_, n in enumerate(sizes):
+            pairs.add(((g.ptr() + es * offs[p_]) % 16 // es, (boff * es) % 16 // es))
+            boff += n
+    assert len(pairs) == per * per, sorted(pairs)  # the bucket and the buffers start 256-byte aligned
+    padded = sum(sizes) + 7
+    buckets = [Guarded(padded, torch_dt(bf16), 0, np.full(padded, 0x3F80 if bf16 else 1.0, dtype=dt))
+               for _ in range(K)]
+    zr().zr_flatten_bucket(fp, sizes, [b.ptr() for b in buckets], padded, dtype=torch_dt(bf16),
+                           workspace=workspace(ws, K, F))
+    torch.cuda.synchronize()
+    want = oracle.flatten(frags_np, sizes, padded)
+    for r in range(K):
+        assert np.array_equal(bits(buckets[r].get()), bits(want[r])), f"rank {r}"
+        assert buckets[r].guards_intact() and bufs[r].guards_intact()
+
+
 FRAG_CASES = [
     # K, sizes (None = the 64 log-uniform fragments), extra padding, in_bf16, out_bf16,
     # shift, average, order, offset, accumulate
