@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <string>
 #include <new>
 #include <vector>
@@ -58,6 +59,19 @@ int env_int(const char* name, int dflt, int lo, int hi) {
     if (!v || !*v) return dflt;
     int x = std::atoi(v);
     return x < lo ? lo : (x > hi ? hi : x);
+}
+
+// ZR_FORCE_PATH: "element", "small" or "large"; unset, empty or "auto" leaves
+// the choice to the kernels. Any other value is reported once on stderr and
+// ignored.
+int env_path(const char* name) {
+    const char* v = std::getenv(name);
+    if (!v || !*v || !std::strcmp(v, "auto")) return kPathAuto;
+    if (!std::strcmp(v, "element")) return kPathElement;
+    if (!std::strcmp(v, "small")) return kPathSmall;
+    if (!std::strcmp(v, "large")) return kPathLarge;
+    std::fprintf(stderr, "libzr: %s=%s is not one of element, small, large; ignored\n", name, v);
+    return kPathAuto;
 }
 
 zr_status check_k(int K) {
@@ -159,6 +173,15 @@ bool capturing(hipStream_t s) {
     return st != hipStreamCaptureStatusNone;
 }
 
+// The status of a call whose launches on `s` returned `e`. With ZR_DEBUG set
+// (and `s` not capturing) the call first waits for `s`, so an error the
+// kernels raise comes back from the call that launched them.
+zr_status launched(hipError_t e, hipStream_t s, const char* what) {
+    if (e == hipSuccess && tuning().debug && !capturing(s)) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, what);
+    return ok();
+}
+
 }  // namespace
 
 hipError_t stage_table(void* ws, const void* image, size_t bytes, hipStream_t stream, bool stream_order) {
@@ -177,6 +200,8 @@ const Tuning& tuning() {
         env_int("ZR_AR_NONTEMPORAL", 1, 0, 1),
         env_int("ZR_AG_NONTEMPORAL", 1, 0, 1),
         env_int("ZR_MAX_GRID", 1 << 30, 1, 1 << 30),
+        env_path("ZR_FORCE_PATH"),
+        env_int("ZR_DEBUG", 0, 0, 1),
     };
     return t;
 }
@@ -232,8 +257,7 @@ zr_status run_rs(int K, const void* const* in, zr_dtype in_dt, int64_t N, void* 
         op.p[r] = out[r];
     }
     hipError_t e = launch_reduce_scatter(K, ip, in_dt, N, op, out_dt, shift, flags, order, stream);
-    if (e != hipSuccess) return hip_fail(e, "reduce-scatter launch");
-    return ok();
+    return launched(e, stream, "reduce-scatter launch");
 }
 
 zr_status validate_ag(int K, const void* const* shards, void* const* fulls, zr_dtype dt,
@@ -344,7 +368,7 @@ zr_status run_ag(int K, const void* const* shards, void* const* fulls, zr_dtype 
         hipError_t e = launch_all_gather(K, sp, fp, dt, segs + s0, n, shift, stream);
         if (e != hipSuccess) return hip_fail(e, "all-gather launch");
     }
-    return ok();
+    return launched(hipSuccess, stream, "all-gather launch");
 }
 
 }  // namespace zr
@@ -403,8 +427,7 @@ zr_status zr_all_gather(int K, const void* const* shards, void* const* fulls, zr
             fp.p[r] = fulls[r];
         }
         hipError_t e = launch_all_gather_ws(K, sp, fp, dt, segs, n_segs, chunk_shift, workspace, s);
-        if (e != hipSuccess) return hip_fail(e, "all-gather launch");
-        return ok();
+        return launched(e, s, "all-gather launch");
     });
 }
 
@@ -443,8 +466,7 @@ zr_status zr_allreduce(int K, const void* const* in, void* const* out, zr_dtype 
                 op.p[r] = out[r];
             }
             hipError_t e = launch_allreduce_fused(K, ip, op, dt, N, average ? 1 : 0, order, s);
-            if (e != hipSuccess) return hip_fail(e, "all-reduce launch");
-            return ok();
+            return launched(e, s, "all-reduce launch");
         }
         if (!scratch) return fail(ZR_ERR_INVALID, "scratch is NULL (needed when fused == 0)");
         if (((uintptr_t)scratch) & (uintptr_t)(es - 1)) return fail(ZR_ERR_ALIGN, "scratch is not aligned");
@@ -637,8 +659,7 @@ zr_status run_once(Build build, Bytes bytes, Image image, Launch launch, Free fr
     hipError_t e = stage_table(ws, image(plan), bytes(plan), s, true);
     if (e == hipSuccess) e = launch(plan, s);
     free_plan(plan);
-    if (e != hipSuccess) return hip_fail(e, what);
-    return ok();
+    return launched(e, s, what);
 }
 
 }  // namespace
@@ -715,8 +736,7 @@ zr_status zr_flatten_plan_launch(const zr_flatten_plan* plan, void* stream) {
     if (!plan) return fail(ZR_ERR_INVALID, "plan is NULL");
     if (!plan->plan) return ok();
     const hipError_t e = flat_plan_launch(plan->plan, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "flatten launch");
-    return ok();
+    return launched(e, (hipStream_t)stream, "flatten launch");
 }
 
 zr_status zr_flatten_plan_info(const zr_flatten_plan* plan, int* launches, size_t* table_bytes) {
@@ -779,8 +799,7 @@ zr_status zr_rs_plan_launch(const zr_rs_plan* plan, void* stream) {
     if (!plan) return fail(ZR_ERR_INVALID, "plan is NULL");
     if (!plan->plan) return ok();
     const hipError_t e = rs_plan_launch(plan->plan, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "reduce-scatter launch");
-    return ok();
+    return launched(e, (hipStream_t)stream, "reduce-scatter launch");
 }
 
 zr_status zr_rs_plan_destroy(zr_rs_plan* plan) {
@@ -854,8 +873,7 @@ zr_status zr_rsf_plan_launch(const zr_rsf_plan* plan, void* stream) {
     if (!plan) return fail(ZR_ERR_INVALID, "plan is NULL");
     if (!plan->plan) return ok();
     const hipError_t e = rsf_plan_launch(plan->plan, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "discrete reduce-scatter launch");
-    return ok();
+    return launched(e, (hipStream_t)stream, "discrete reduce-scatter launch");
 }
 
 zr_status zr_rsf_plan_info(const zr_rsf_plan* plan, int* launches, size_t* table_bytes) {

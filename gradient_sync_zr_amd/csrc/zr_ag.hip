@@ -203,7 +203,7 @@ int64_t describe(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype 
                  int n_segs, AgSeg* out, int64_t* unit0, int* used) {
     const int es = dt == ZR_BF16 ? 2 : 4;
     const int64_t tile = dt == ZR_BF16 ? kAgTile<uint16_t> : kAgTile<float>;  // elements per tile
-    bool bases = true;
+    bool bases = tuning().force_path != kPathElement;  // ZR_FORCE_PATH=element: every chunk element-wise
     for (int r = 0; r < K; ++r)
         bases = bases && (((uintptr_t)shards.p[r]) & 15) == 0 && (((uintptr_t)fulls.p[r]) & 15) == 0;
     int n = 0;

@@ -140,7 +140,7 @@ hipError_t launch_allreduce_fused(int K, const ConstPtrs& in, const MutPtrs& out
     const int64_t tile = dt == ZR_BF16 ? kArTile<uint16_t> : kArTile<float>;
     a.n_tiles = (N + tile - 1) / tile;
     const uintptr_t al = dt == ZR_BF16 ? 8 : 16;  // quad size
-    bool vec = true;
+    bool vec = tuning().force_path != kPathElement;
     for (int r = 0; r < K; ++r)
         vec = vec && ((uintptr_t)in.p[r] % al) == 0 && ((uintptr_t)out.p[r] % al) == 0;
     a.vec = vec ? 1 : 0;

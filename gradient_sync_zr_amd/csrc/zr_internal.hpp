@@ -35,12 +35,25 @@ struct FragEntry {
 
 // Knobs read once from the environment (for tuning sweeps and tests);
 // defaults are the measured best.
+// Debugging aids among them: ZR_FORCE_PATH overrides the kernels' choice of
+// access path or tile shape where they have one, and ZR_DEBUG makes every call
+// wait for its stream after its launches (outside stream capture), so a fault
+// in a kernel is reported by the call that launched it.
+enum ForcePath {
+    kPathAuto = 0,     // each kernel's own choice
+    kPathElement = 1,  // element-wise folds and copies (reduce-scatter, discrete
+                       // reduce-scatter, all-reduce, all-gather)
+    kPathSmall = 2,    // one-slice tiles for every ring-order reduce-scatter
+    kPathLarge = 3,    // full tiles for every reduce-scatter, however small
+};
 struct Tuning {
     int ar_nontemporal;    // fused all-reduce: streaming (non-temporal) loads and stores
     int ag_nontemporal;    // all-gather
     int max_grid;          // blocks per launch at most (ZR_MAX_GRID, default 2^30): every
                            // kernel launches one block per tile up to it, and its blocks
                            // stride over the tiles beyond it
+    int force_path;        // ZR_FORCE_PATH: element | small | large (a ForcePath)
+    int debug;             // ZR_DEBUG: 1 = wait for the stream after each call's launches
 };
 const Tuning& tuning();
 // Blocks for a launch of `tiles` tiles: one per tile, at most tuning().max_grid.

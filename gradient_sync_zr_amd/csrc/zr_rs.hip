@@ -235,7 +235,9 @@ LaunchFn pick_avg(int K, int avg_mode, int order, bool small) {
 template <typename TIn, typename TOut>
 LaunchFn prepare_typed(RsArgs& a, int avg_mode, int order) {
     constexpr int64_t T = kRsTile<TIn, TOut>;
-    const bool small = order == kRing && ((a.C + T - 1) / T) * a.K < 2LL * device_cu_count();
+    const int fp = tuning().force_path;
+    const bool small = order == kRing && (fp == kPathSmall ||
+                                          (fp != kPathLarge && ((a.C + T - 1) / T) * a.K < 2LL * device_cu_count()));
     const int64_t Tl = small ? kRsTileOf<1> : T;
     // Vector path: every base aligned for quad access (8 bytes for bf16
     // quads, 16 for fp32 quads) and j*C a multiple of 4 elements, so that a
@@ -248,7 +250,7 @@ LaunchFn prepare_typed(RsArgs& a, int avg_mode, int order) {
     // blocks streamed 2-4% slower, worst at half a block off.)
     const uintptr_t in_al = sizeof(TIn) * 4, out_al = sizeof(TOut) * 4;
     const int64_t line = 128 / (int64_t)sizeof(TIn);
-    bool bases = true;
+    bool bases = fp != kPathElement;
     for (int r = 0; r < a.K; ++r) {
         bases = bases && ((uintptr_t)a.in.p[r] % in_al) == 0;
         bases = bases && ((uintptr_t)a.out.p[r] % out_al) == 0;

@@ -380,7 +380,9 @@ void segments_of(const RsfCommon& c, const FragEntry* entries, int n_entries, in
             const int q = ((j - c.shift) % K + K) % K;  // holder
             const uintptr_t o = (uintptr_t)c.out.p[q] + (uintptr_t)(lo - jc) * sizeof(TOut);
             int h;
-            if (pad) {
+            if (tuning().force_path == kPathElement) {
+                h = -1;  // element-wise folds, forced
+            } else if (pad) {
                 // no input: align the partition side to its 16 KiB blocks
                 h = (int)to_block(o, sizeof(TOut));
             } else {
@@ -533,7 +535,8 @@ RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t 
         } else {
             for (const RsfArgs& l : plan->launches) most = most > l.tile0[l.nseg] ? most : l.tile0[l.nseg];
         }
-        const bool small = ord == kRing && most < 2LL * device_cu_count();
+        const int fp = tuning().force_path;
+        const bool small = ord == kRing && (fp == kPathSmall || (fp != kPathLarge && most < 2LL * device_cu_count()));
         if (small) segments_of<TIn, TOut>(c, entries, n_entries, kRsTileOf<1>, &segs, &first);
         if (plan->staged) {
             plan->launches.clear();

@@ -65,6 +65,23 @@
  *    argument enqueues nothing. zr_last_error() describes the last failure
  *    on the calling thread. N == 0 (or no work) returns ZR_OK and enqueues
  *    nothing.
+ *  - Environment, read once, at the library's first launch or plan; for
+ *    debugging and tests only. Ring-order results are bit-identical under
+ *    every setting (ZR_ORDER_FREE results stay within their bound):
+ *      ZR_DEBUG=1        every call waits for its stream after its launches
+ *                        (not under stream capture), so an error a kernel
+ *                        raises is returned, as ZR_ERR_HIP, by the call that
+ *                        launched it;
+ *      ZR_FORCE_PATH=element | small | large
+ *                        element: the reduce-scatter, discrete reduce-scatter,
+ *                        all-reduce and all-gather fold or copy element by
+ *                        element even where their inputs allow 16-byte access
+ *                        (the flatten has no such choice: its whole 16-byte
+ *                        units always move as vectors); small: every ring-order
+ *                        reduce-scatter uses one-slice tiles; large: none does;
+ *                        other values are reported on stderr and ignored;
+ *      ZR_MAX_GRID=n     at most n blocks per launch (default 2^30), the
+ *                        blocks striding over the tiles beyond them.
  */
 #ifndef ZR_H
 #define ZR_H

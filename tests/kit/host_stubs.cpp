@@ -21,6 +21,7 @@ struct RsPlan {
     int K;
 };
 RsPlan* rs_plan_build(int K, const ConstPtrs&, zr_dtype, int64_t, const MutPtrs&, zr_dtype, int, int, zr_order) {
+    (void)tuning();  // the library's builder reads the environment settings here
     return new RsPlan{K};
 }
 hipError_t rs_plan_launch(const RsPlan*, hipStream_t) { return hipErrorNotSupported; }

@@ -507,3 +507,29 @@ def test_rs_plan_validation_matches_the_call():
             assert lib.zr_rs_plan_destroy(h) == zr.ZR_OK
         else:
             assert h.value is None
+
+
+def _plan_in_child(env):
+    # a reduce-scatter plan is built on the host (no GPU needed), which reads
+    # the library's environment settings
+    code = ("import ctypes, gradient_sync_zr_amd as zr\n"
+            "lib = zr.lib(); K = 8; A = %d\n"
+            "ins = (ctypes.c_void_p * K)(*[A + r * (1 << 30) for r in range(K)])\n"
+            "outs = (ctypes.c_void_p * K)(*[A + (1 << 40) + r * (1 << 30) for r in range(K)])\n"
+            "h = ctypes.c_void_p()\n"
+            "assert lib.zr_rs_plan_create(K, ins, 0, 100000, outs, 1, 1, 1, 0, ctypes.byref(h)) == 0\n"
+            "assert lib.zr_rs_plan_destroy(h) == 0\n" % A)
+    import subprocess
+    import sys
+    return subprocess.run([sys.executable, "-c", code], env=dict(os.environ, **env), cwd=ROOT,
+                          capture_output=True, text=True, timeout=120)
+
+
+def test_force_path_setting_is_read_and_a_bad_value_reported():
+    for value in ("element", "small", "large", "auto", ""):
+        r = _plan_in_child({"ZR_FORCE_PATH": value, "ZR_DEBUG": "1"})
+        assert r.returncode == 0, r.stderr
+        assert "libzr:" not in r.stderr, (value, r.stderr)
+    r = _plan_in_child({"ZR_FORCE_PATH": "vectorised"})
+    assert r.returncode == 0, r.stderr
+    assert "libzr: ZR_FORCE_PATH=vectorised is not one of element, small, large; ignored" in r.stderr
