@@ -117,17 +117,17 @@ def copy_ceiling_gbps(gib=4, reps=10):
     return round(2 * nbytes / (sum(ms) / len(ms) * 1e-3) / 1e9, 1)
 
 
-def mix_ceiling(reps=10):
+def mix_ceiling(reps=10, modes=("mix", "reads", "writes")):
     """The test kit's matched-mix stream (tests/kit/mix_probe.py: the
     reduce-scatter's loads and stores at one bucket's shape, no arithmetic),
-    measured now: {"mix", "reads", "writes"} rates, or None when the kit is
-    not built."""
+    measured now: the rates of the requested modes ("mix", "reads", "writes",
+    "accum"), or None when the kit is not built."""
     import importlib.util
     spec = importlib.util.spec_from_file_location("mix_probe", os.path.join(ROOT, "tests", "kit",
                                                                             "mix_probe.py"))
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
-    return mod.measure(reps=reps)
+    return mod.measure(reps=reps, modes=modes)
 
 
 # ----------------------------------------------------------------- zero2
@@ -209,7 +209,8 @@ def bench_zero2(args, accumulate=False):
     sync.close()
     del sync, grads, parts
     copy = copy_ceiling_gbps()
-    mix = mix_ceiling() if not accumulate else None
+    mix = mix_ceiling(modes=("accum",) if accumulate else ("mix", "reads", "writes"))
+    mix_key = "accum" if accumulate else "mix"
     if accumulate:
         metric = ("reduce-scatter+avg+accumulate GB/s (gradient-accumulation micro-step), K=8, "
                   "2.38B-elem bf16 grads")
@@ -244,10 +245,10 @@ def bench_zero2(args, accumulate=False):
                      "per_bucket_GBps": per_bucket,
                      "copy_ceiling_GBps": copy,
                      "of_copy_ceiling": round(achieved / copy, 4) if copy else None,
-                     "mix_ceiling_GBps": mix["mix"]["GBps"] if mix else None,
-                     "of_mix_ceiling": round(achieved / mix["mix"]["GBps"], 4) if mix else None,
-                     "mix_reads_only_GBps": mix["reads"]["GBps"] if mix else None,
-                     "mix_writes_only_GBps": mix["writes"]["GBps"] if mix else None,
+                     "mix_ceiling_GBps": mix[mix_key]["GBps"] if mix else None,
+                     "of_mix_ceiling": round(achieved / mix[mix_key]["GBps"], 4) if mix else None,
+                     "mix_reads_only_GBps": mix["reads"]["GBps"] if mix and "reads" in mix else None,
+                     "mix_writes_only_GBps": mix["writes"]["GBps"] if mix and "writes" in mix else None,
                      "timing": "per-launch event pairs from a separate instrumented pass of "
                                "the same number of steps; value and the step median/min come "
                                "from the uninstrumented steps",

@@ -5,12 +5,14 @@ tk_mix replays the reduce-scatter's memory access pattern at the shape of one
 multiple of 4096 next to 62.5M) with no arithmetic: every tile loads eight
 bf16 streams with 8-byte non-temporal loads and writes one 16 KiB fp32 block
 with 16-byte non-temporal stores, tiles numbered by pairs of chunks as the
-kernel numbers them. Three modes, each timed with events over `reps`
+kernel numbers them. Four modes, each timed with events over `reps`
 launches after 3 warm-ups:
 
   mix     loads + stores: 16 B read and 4 B written per element index
   reads   the loads alone (the reads' share of the ceiling)
   writes  the stores alone (the writes' share)
+  accum   loads + each output word read back before its store: 20 B read and
+          4 B written per element index, the accumulating reduce-scatter's mix
 
 The mix rate is the practical ceiling of a stream with the reduce-scatter's
 own traffic mix on this GPU, measured the way the kernel is measured.
@@ -44,8 +46,8 @@ def measure(reps=20, C=CHUNK, modes=("mix", "reads", "writes")):
     tin = (ctypes.c_void_p * K)(*[t.data_ptr() for t in ins])
     tout = (ctypes.c_void_p * K)(*[t.data_ptr() for t in outs])
     s = torch.cuda.current_stream().cuda_stream
-    moved = {"mix": n * (2 * K + 4), "reads": n * 2 * K, "writes": n * 4}
-    code = {"mix": 0, "reads": 1, "writes": 2}
+    moved = {"mix": n * (2 * K + 4), "reads": n * 2 * K, "writes": n * 4, "accum": n * (2 * K + 8)}
+    code = {"mix": 0, "reads": 1, "writes": 2, "accum": 3}
     res = {}
     for m in modes:
         def run():
@@ -74,7 +76,7 @@ def main():
     ap.add_argument("--reps", type=int, default=20)
     args = ap.parse_args()
     out = {"K": K, "C": CHUNK, "element_indices": K * CHUNK, "bytes_mix": K * CHUNK * (2 * K + 4)}
-    out.update(measure(args.reps))
+    out.update(measure(args.reps, modes=("mix", "reads", "writes", "accum")))
     print(json.dumps(out), flush=True)
 
 

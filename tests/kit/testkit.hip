@@ -97,6 +97,9 @@ extern "C" int tk_read(const void* src, void* sink, long long bytes, int blocks,
 //   mode 1: loads only (one 16-byte word per tile, written only when the
 //           XOR of the tile's data hits a fixed value, keeps the loads live)
 //   mode 2: stores only (the same 16 KiB output blocks, no loads)
+//   mode 3: mode 0 plus a 16-byte non-temporal load of each output word before
+//           its store, folded into the stored value (the accumulating
+//           reduce-scatter's 20 B read : 4 B written)
 typedef unsigned int tk_u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int tk_u32x4 __attribute__((ext_vector_type(4)));
 
@@ -144,13 +147,21 @@ __global__ void __launch_bounds__(256) tk_mix_kernel(const TkMixArgs a) {
         for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(x[k], out + (o0 + 256 * k) / 4);
         return;
     }
+    if (a.mode == 3) {
+        tk_u32x4 old[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) old[k] = __builtin_nontemporal_load(out + (o0 + 256 * k) / 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(x[k] ^ old[k], out + (o0 + 256 * k) / 4);
+        return;
+    }
     const tk_u32x4 z = x[0] ^ x[1] ^ x[2] ^ x[3];
     if (z.x == 0x9E3779B9u && z.y == 0x7F4A7C15u) a.sink[i] = z;
 }
 
 extern "C" int tk_mix(const void* const* in, void* const* out, void* sink, long long C, int mode,
                       void* stream) {
-    if (!in || !out || C <= 0 || (C % 4096) != 0 || mode < 0 || mode > 2) return 1;
+    if (!in || !out || C <= 0 || (C % 4096) != 0 || mode < 0 || mode > 3) return 1;
     if (mode == 1 && !sink) return 1;
     TkMixArgs a;
     for (int r = 0; r < 8; ++r) {
