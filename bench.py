@@ -75,7 +75,9 @@ def read_traffic(name, src_hash, algorithmic, key="hbm_bytes_per_launch"):
 
 
 def host_cores():
-    """Cores this process may run on (its affinity mask), all of them."""
+    """Cores this process may run on (its affinity mask), all of them. The
+    machine's hardware thread count (os.cpu_count()) is reported beside it:
+    the two differ when the process is confined to part of the host."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -302,7 +304,8 @@ def cpu_baseline_zero2(grads, parts, first_bucket, K, args):
     dt1 = time.perf_counter() - t1
     sample = ("all of bucket 0" if M == C else f"offsets [0,{M}) of each of the {K} chunks of bucket 0")
     return {"value": round(gbs, 2), "unit": "GB/s", "cores": T, "kind": "oracle",
-            "host_cores": T, "threads_used": T, "seconds": round(dt, 3),
+            "host_cores": T, "threads_used": T, "hardware_threads": os.cpu_count(),
+            "seconds": round(dt, 3),
             "single_core_GBps": round(model_bytes / dt1 / 1e9, 2),
             "single_core_seconds": round(dt1, 3),
             "single_core_sample": sample,
