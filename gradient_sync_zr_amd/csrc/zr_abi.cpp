@@ -201,6 +201,7 @@ const Tuning& tuning() {
         env_int("ZR_AG_NONTEMPORAL", 1, 0, 1),
         env_int("ZR_MAX_GRID", 1 << 30, 1, 1 << 30),
         env_path("ZR_FORCE_PATH"),
+        env_int("ZR_RS_PAIRS", 1, 0, 1),
         env_int("ZR_DEBUG", 0, 0, 1),
     };
     return t;

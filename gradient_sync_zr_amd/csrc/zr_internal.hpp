@@ -53,6 +53,7 @@ struct Tuning {
                            // kernel launches one block per tile up to it, and its blocks
                            // stride over the tiles beyond it
     int force_path;        // ZR_FORCE_PATH: element | small | large (a ForcePath)
+    int rs_pairs;          // ZR_RS_PAIRS: reduce-scatter tiles by pairs of chunks (1) or chunk by chunk (0)
     int debug;             // ZR_DEBUG: 1 = wait for the stream after each call's launches
 };
 const Tuning& tuning();

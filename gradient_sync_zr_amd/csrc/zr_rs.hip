@@ -53,9 +53,10 @@ struct RsArgs {
     int64_t N, C;
     uint64_t vec_mask;         // bit j: chunk j takes the vector path
     int16_t head[kMaxRanks];   // chunk j's vector tiles start at chunk offset head[j]
-    int64_t tile0[kMaxRanks / 2 + 1];  // first tile of chunk pair q; tile0[npairs] = all tiles
+    int64_t tile0[kMaxRanks + 1];      // first tile of chunk group q; tile0[ngroups] = all tiles
     int64_t ntile[kMaxRanks];          // tiles of chunk j
-    int npairs;                        // ceil(K / 2)
+    int ngroups;                       // ceil(K / group)
+    int group;                         // chunks per group: 1, or 2 (a pair's blocks alternate)
     int K, shift;
     int accumulate;            // 1: out = old + result (gradient accumulation)
     float inv_k, kf;
@@ -73,11 +74,11 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
     const int wave = threadIdx.x >> 6;
 
     // one tile per block; a launch capped below the tile count strides
-    for (int64_t i = blockIdx.x; i < a.tile0[a.npairs]; i += gridDim.x) {
-        // the tile's chunk pair: the last q with tile0[q] <= i (uniform);
-        // the pair's two chunks take alternate blocks
+    for (int64_t i = blockIdx.x; i < a.tile0[a.ngroups]; i += gridDim.x) {
+        // the tile's chunk group: the last q with tile0[q] <= i (uniform);
+        // the two chunks of a pair take alternate blocks
         int q = 0;
-        for (int hi = a.npairs; hi - q > 1;) {
+        for (int hi = a.ngroups; hi - q > 1;) {
             const int mid = (q + hi) >> 1;
             if (a.tile0[mid] <= i)
                 q = mid;
@@ -85,8 +86,9 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
                 hi = mid;
         }
         const int64_t w = i - a.tile0[q];
-        const bool two = 2 * q + 1 < K;
-        const int j = two ? 2 * q + (int)(w & 1) : 2 * q;
+        const int first = a.group * q;
+        const bool two = a.group == 2 && first + 1 < K;
+        const int j = two ? first + (int)(w & 1) : first;
         const int64_t t = two ? (w >> 1) : w;
         if (t >= a.ntile[j]) continue;  // the pair's shorter chunk has run out
         const int holder = wrap(j - a.shift + K, K);
@@ -194,7 +196,7 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
 // One block per tile, up to tuning().max_grid blocks (beyond that they stride).
 template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
 hipError_t launch_t(const RsArgs& a, hipStream_t stream) {
-    const int64_t total = a.tile0[a.npairs];
+    const int64_t total = a.tile0[a.ngroups];
     const int gx = grid_for(total);
     hipLaunchKernelGGL((rs_kernel<TIn, TOut, KS, AVG, ORDER, NT, S>), dim3(gx), dim3(kThreads), 0,
                        stream, a);
@@ -278,13 +280,16 @@ LaunchFn prepare_typed(RsArgs& a, int avg_mode, int order) {
             a.ntile[j] = (a.C + Tl - 1) / Tl;
         }
     }
-    a.npairs = (a.K + 1) / 2;
+    a.group = tuning().rs_pairs ? 2 : 1;
+    a.ngroups = (a.K + a.group - 1) / a.group;
     int64_t tiles = 0;
-    for (int q = 0; q < a.npairs; ++q) {
+    for (int q = 0; q < a.ngroups; ++q) {
         a.tile0[q] = tiles;
-        tiles += 2 * q + 1 < a.K ? 2 * std::max(a.ntile[2 * q], a.ntile[2 * q + 1]) : a.ntile[2 * q];
+        const int first = a.group * q;
+        tiles += a.group == 2 && first + 1 < a.K ? 2 * std::max(a.ntile[first], a.ntile[first + 1])
+                                                  : a.ntile[first];
     }
-    a.tile0[a.npairs] = tiles;
+    a.tile0[a.ngroups] = tiles;
     return pick_avg<TIn, TOut>(a.K, avg_mode, order, small);
 }
 
