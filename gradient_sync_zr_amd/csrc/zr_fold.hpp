@@ -108,12 +108,21 @@ __device__ __forceinline__ void fold_ring_quads_static(const RingBases<TIn, KS>&
     }
 }
 
-// Ring order for any K: batches of eight ranks, every slice's loads of a batch
-// in flight together, batches folded in ring order one after the other.
+// Ranks per batch of the ring fold for any K: the batch's loads of all S
+// slices are in flight together, about 64 VGPRs of data per lane (bf16 quads
+// take 2 VGPRs, fp32 quads 4), and never fewer than eight ranks. A tile of one
+// or two slices thus waits on K / 32 or K / 16 round trips to memory instead of
+// K / 8, which is what a launch with few tiles per CU (large K, a small bucket)
+// is bound by.
+template <typename TIn, int S>
+constexpr int kRingBatch = (64 / (S * (int)sizeof(TIn))) > 8 ? 64 / (S * (int)sizeof(TIn)) : 8;
+
+// Ring order for any K: batches of kRingBatch ranks, every slice's loads of a
+// batch in flight together, batches folded in ring order one after the other.
 template <typename TIn, int KS, bool NT, int S, bool WIRE = false, typename PtrFn>
 __device__ __forceinline__ void fold_ring_quads(PtrFn ptr, int K, int j, int64_t g0,
                                                 float acc[S][4]) {
-    constexpr int B = 8;
+    constexpr int B = kRingBatch<TIn, S>;
     const int Kr = KS > 0 ? KS : K;
     for (int h0 = 0; h0 < Kr; h0 += B) {
         Quad<TIn> v[S][B];

@@ -238,8 +238,11 @@ template <typename TIn, typename TOut>
 LaunchFn prepare_typed(RsArgs& a, int avg_mode, int order) {
     constexpr int64_t T = kRsTile<TIn, TOut>;
     const int fp = tuning().force_path;
+    // fewer than two full tiles per CU for each eight ranks (a tile's bytes
+    // grow with K): one-slice tiles, four times as many
+    const int64_t k8 = (a.K + 7) / 8;
     const bool small = order == kRing && (fp == kPathSmall ||
-                                          (fp != kPathLarge && ((a.C + T - 1) / T) * a.K < 2LL * device_cu_count()));
+                                          (fp != kPathLarge && ((a.C + T - 1) / T) * a.K < 2LL * k8 * device_cu_count()));
     const int64_t Tl = small ? kRsTileOf<1> : T;
     // Vector path: every base aligned for quad access (8 bytes for bf16
     // quads, 16 for fp32 quads) and j*C a multiple of 4 elements, so that a
@@ -318,11 +321,44 @@ LaunchFn prepare(RsArgs& a, int K, const ConstPtrs& in, zr_dtype in_dt, int64_t 
     return prepare_typed<float, uint16_t>(a, avg_mode, ord);
 }
 
+// Chunks whose start j*C is not a quad boundary (or whose bases are not quad
+// aligned) fold element by element here, and for K > 8 that costs one memory
+// round trip per eight ranks per element: 0.8-1.1 TB/s at K = 32 and 64
+// against 5-5.3 TB/s for the discrete reduce-scatter over the same data, which
+// reads quads on the input's own grid and stores single elements only where
+// the partition side is not quad aligned. Such a call therefore goes out as
+// that discrete reduce-scatter over one fragment per rank (the whole buffer)
+// and the zero padding up to K*C: the bucket it describes is the input itself,
+// so every ring-order result is the same. (For K <= 8 one batch holds every
+// rank and the element-wise chunks keep the rate.)
+bool via_fragments(const RsArgs& a) {
+    if (a.K <= 8) return false;
+    const uint64_t all = a.K >= 64 ? ~0ull : ((1ull << a.K) - 1);
+    return (a.vec_mask & all) != all;
+}
+
+RsfPlan* fragment_plan(int K, const ConstPtrs& in, zr_dtype in_dt, int64_t N, const MutPtrs& out,
+                       zr_dtype out_dt, int shift, int flags, zr_order order) {
+    const int64_t C = (N + K - 1) / K;
+    FragEntry e[2] = {};
+    for (int r = 0; r < K; ++r) e[0].ptr[r] = in.p[r];
+    e[0].off = 0;
+    e[0].n = N;
+    int n = 1;
+    if ((int64_t)K * C > N) {  // the padding: no pointers
+        e[1].off = N;
+        e[1].n = (int64_t)K * C - N;
+        n = 2;
+    }
+    return rsf_plan_build(K, e, n, N, in_dt, out, out_dt, shift, flags, order, nullptr);
+}
+
 }  // namespace
 
 struct RsPlan {
     RsArgs a;
     LaunchFn fn;
+    RsfPlan* frag = nullptr;  // set: the call goes out as this discrete reduce-scatter
 };
 
 RsPlan* rs_plan_build(int K, const ConstPtrs& in, zr_dtype in_dt, int64_t N, const MutPtrs& out,
@@ -330,19 +366,37 @@ RsPlan* rs_plan_build(int K, const ConstPtrs& in, zr_dtype in_dt, int64_t N, con
     RsPlan* p = new (std::nothrow) RsPlan();
     if (!p) return nullptr;
     p->fn = prepare(p->a, K, in, in_dt, N, out, out_dt, shift, flags, order);
+    if (via_fragments(p->a)) {
+        p->frag = fragment_plan(K, in, in_dt, N, out, out_dt, shift, flags, order);
+        if (!p->frag) {
+            delete p;
+            return nullptr;
+        }
+    }
     return p;
 }
 
-hipError_t rs_plan_launch(const RsPlan* p, hipStream_t stream) { return p->fn(p->a, stream); }
+hipError_t rs_plan_launch(const RsPlan* p, hipStream_t stream) {
+    if (p->frag) return rsf_plan_launch(p->frag, stream);
+    return p->fn(p->a, stream);
+}
 
-void rs_plan_free(RsPlan* p) { delete p; }
+void rs_plan_free(RsPlan* p) {
+    if (p && p->frag) rsf_plan_free(p->frag);
+    delete p;
+}
 
 hipError_t launch_reduce_scatter(int K, const ConstPtrs& in, zr_dtype in_dt, int64_t N,
                                  const MutPtrs& out, zr_dtype out_dt, int shift, int flags,
                                  zr_order order, hipStream_t stream) {
     RsArgs a;
     const LaunchFn fn = prepare(a, K, in, in_dt, N, out, out_dt, shift, flags, order);
-    return fn(a, stream);
+    if (!via_fragments(a)) return fn(a, stream);
+    RsfPlan* f = fragment_plan(K, in, in_dt, N, out, out_dt, shift, flags, order);
+    if (!f) return hipErrorOutOfMemory;
+    const hipError_t e = rsf_plan_launch(f, stream);
+    rsf_plan_free(f);
+    return e;
 }
 
 }  // namespace zr

@@ -536,7 +536,9 @@ RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t 
             for (const RsfArgs& l : plan->launches) most = most > l.tile0[l.nseg] ? most : l.tile0[l.nseg];
         }
         const int fp = tuning().force_path;
-        const bool small = ord == kRing && (fp == kPathSmall || (fp != kPathLarge && most < 2LL * device_cu_count()));
+        // fewer than two full tiles per CU for each eight ranks: one-slice tiles
+        const int64_t k8 = (K + 7) / 8;
+        const bool small = ord == kRing && (fp == kPathSmall || (fp != kPathLarge && most < 2LL * k8 * device_cu_count()));
         if (small) segments_of<TIn, TOut>(c, entries, n_entries, kRsTileOf<1>, &segs, &first);
         if (plan->staged) {
             plan->launches.clear();

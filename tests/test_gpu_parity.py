@@ -76,6 +76,11 @@ RS_CASES = [
     (8, 8 * 300000 + 13, True, False, 1, True, 0),
     (16, 16 * 150000 + 5, False, True, 1, True, 0),
     (64, 64 * 40000 + 7, True, False, 1, False, 0),
+    # K > 8 with chunk starts off the quad grid (C mod 4 = 2, 3, 2): these go
+    # out as a discrete reduce-scatter over one fragment per rank
+    (32, 32 * 50002, True, False, 1, True, 0),
+    (32, 32 * 50003 - 5, True, True, 3, True, 0),
+    (17, 17 * 20001 + 2, True, False, 1, True, 0),
 ]
 
 
