@@ -19,8 +19,14 @@
 // kAgSub groups of 8 shard elements (16 bytes each for bf16), all before its
 // first store, and stores each to all K full buffers, so each shard byte is
 // read once and written K times. (Tiles of 16 KiB per destination ran 1% faster
-// than tiles of 4, 8 or 32 KiB.) Chunk starts that are not 16-byte aligned on
-// either side, and ragged ends, copy element by element.
+// than tiles of 4, 8 or 32 KiB.) A chunk's groups are aligned to its
+// destination, whose start full_off + j*C may fall anywhere within 16 bytes
+// (full_off is a running sum of tensor sizes); when the source is in another
+// phase, each group is read as the aligned 16-byte blocks holding it and
+// shifted into place in registers, so every whole group moves with 16-byte
+// loads and stores (element-by-element copies of such chunks ran 4.5x slower).
+// Only a chunk's partial first and last groups, and every chunk when some
+// base is not 16-byte aligned, copy element by element.
 #include <vector>
 
 #include "zr_device.hpp"
@@ -31,7 +37,7 @@ namespace {
 
 struct AgSeg {
     int64_t shard_off, full_off, numel, C;
-    uint64_t vec_mask;  // bit j: chunk j is 16-byte aligned in shard and full
+    uint64_t vec_mask;  // bit j: chunk j moves whole groups with 16-byte accesses
     int tiles_per_chunk;
     int pad_;
 };
@@ -112,6 +118,7 @@ constexpr int64_t kAgTile = (int64_t)kAgSub<T> * kTile;
 template <typename T, int KS, bool NT, typename Tab>
 __device__ __forceinline__ void ag_body(const AgCommon& a, const Tab& tab) {
     constexpr int SUB = kAgSub<T>;
+    constexpr int kLeadMask = 16 / (int)sizeof(T) - 1;  // a destination's phase, in elements
     const int K = KS > 0 ? KS : a.K;
     const int64_t total = tab.total();
     for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
@@ -125,21 +132,25 @@ __device__ __forceinline__ void ag_body(const AgCommon& a, const Tab& tab) {
         if (holder < 0) holder += K;
         const bool vec_chunk = (sg.vec_mask >> j) & 1ull;
         const T* shard = static_cast<const T*>(a.shards.p[holder]) + sg.shard_off;
-        // group k of this lane: chunk offset (t * SUB + k) * kTile + lane * kGroup
+        const int64_t dst0 = sg.full_off + (int64_t)j * sg.C;  // the chunk's start in every full buffer
+        int64_t len = sg.numel - (int64_t)j * sg.C;            // its elements (<= 0: none)
+        if (len > sg.C) len = sg.C;
+        // group k of this lane covers chunk offsets [x, x + kGroup) with
+        // x = (t * SUB + k) * kTile + lane * kGroup - lead: groups start on
+        // the destination's 16-byte grid
+        const int64_t lead = vec_chunk ? (dst0 & kLeadMask) : 0;
         Group<T> v[SUB];
         bool whole[SUB];
 #pragma unroll
         for (int k = 0; k < SUB; ++k) {
-            const int64_t o = ((int64_t)t * SUB + k) * kTile + (int64_t)threadIdx.x * kGroup;
-            const int64_t g = (int64_t)j * sg.C + o;
-            whole[k] = vec_chunk && o + kGroup <= sg.C && g + kGroup <= sg.numel;
-            if (whole[k]) v[k] = load_group<T, NT>(shard + o);
+            const int64_t x = ((int64_t)t * SUB + k) * kTile + (int64_t)threadIdx.x * kGroup - lead;
+            whole[k] = vec_chunk && x >= 0 && x + kGroup <= len;
+            if (whole[k]) v[k] = load_group_any<T, NT>(shard + x);
         }
 #pragma unroll
         for (int k = 0; k < SUB; ++k) {
-            const int64_t o = ((int64_t)t * SUB + k) * kTile + (int64_t)threadIdx.x * kGroup;
-            const int64_t g = (int64_t)j * sg.C + o;
-            const int64_t dst_off = sg.full_off + g;
+            const int64_t x = ((int64_t)t * SUB + k) * kTile + (int64_t)threadIdx.x * kGroup - lead;
+            const int64_t dst_off = dst0 + x;
             if (whole[k]) {
                 if constexpr (KS > 0) {
 #pragma unroll
@@ -147,13 +158,12 @@ __device__ __forceinline__ void ag_body(const AgCommon& a, const Tab& tab) {
                 } else {
                     for (int r = 0; r < K; ++r) store_group<T, NT>(static_cast<T*>(a.fulls.p[r]) + dst_off, v[k]);
                 }
-            } else if (o < sg.C && g < sg.numel) {
-                int64_t n = sg.C - o;
-                if (sg.numel - g < n) n = sg.numel - g;
-                if (n > kGroup) n = kGroup;
-                for (int e = 0; e < (int)n; ++e) {
-                    const T x = shard[o + e];
-                    for (int r = 0; r < K; ++r) static_cast<T*>(a.fulls.p[r])[dst_off + e] = x;
+            } else if (x < len && x + kGroup > 0) {
+                const int64_t e0 = x > 0 ? x : 0;
+                const int64_t e1 = x + kGroup < len ? x + kGroup : len;
+                for (int64_t e = e0; e < e1; ++e) {
+                    const T val = shard[e];
+                    for (int r = 0; r < K; ++r) static_cast<T*>(a.fulls.p[r])[dst0 + e] = val;
                 }
             }
         }
@@ -216,14 +226,20 @@ int64_t describe(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype 
         d.full_off = segs[s].full_off;
         d.numel = segs[s].numel;
         d.C = (d.numel + K - 1) / K;
-        d.tiles_per_chunk = (int)((d.C + tile - 1) / tile);
         d.pad_ = 0;
+        // with 16-byte aligned bases every chunk moves whole groups, on its
+        // destination's grid: its groups start up to 16 / es - 1 elements
+        // before the chunk (the lead), which its tiles must also cover
         d.vec_mask = 0;
-        for (int j = 0; j < K; ++j) {
-            const bool ok = bases && ((d.shard_off * es) & 15) == 0 &&
-                            (((d.full_off + (int64_t)j * d.C) * es) & 15) == 0;
-            if (ok) d.vec_mask |= 1ull << j;
+        int64_t lead = 0;
+        if (bases) {
+            for (int j = 0; j < K; ++j) {
+                d.vec_mask |= 1ull << j;
+                const int64_t l = (d.full_off + (int64_t)j * d.C) & (16 / es - 1);
+                lead = l > lead ? l : lead;
+            }
         }
+        d.tiles_per_chunk = (int)((d.C + lead + tile - 1) / tile);
         units += (int64_t)K * d.tiles_per_chunk;
     }
     unit0[n] = units;

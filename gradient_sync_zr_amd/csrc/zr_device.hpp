@@ -77,6 +77,48 @@ __device__ __forceinline__ Group<float> load_group<float, true>(const float* p) 
     return {ld<true>(q), ld<true>(q + 1)};
 }
 
+// 16 bytes starting `sig` bytes into the 32 bytes lo:hi (sig in 1..15, a
+// multiple of the element size): each output dword joins two neighbouring
+// input dwords with one byte-align instruction.
+__device__ __forceinline__ u32x4 shift16(const u32x4& lo, const u32x4& hi, uint32_t sig) {
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    const uint32_t b = sig & 3;
+    u32x4 r;
+#define ZR_SHIFT16(q)                                                   \
+    r = u32x4{__builtin_amdgcn_alignbyte(w[(q) + 1], w[(q)], b),          \
+              __builtin_amdgcn_alignbyte(w[(q) + 2], w[(q) + 1], b),      \
+              __builtin_amdgcn_alignbyte(w[(q) + 3], w[(q) + 2], b),      \
+              __builtin_amdgcn_alignbyte(w[(q) + 4], w[(q) + 3], b)}
+    switch (sig >> 2) {  // uniform in every caller: the phase of a whole copy
+        case 0: ZR_SHIFT16(0); break;
+        case 1: ZR_SHIFT16(1); break;
+        case 2: ZR_SHIFT16(2); break;
+        default: ZR_SHIFT16(3); break;
+    }
+#undef ZR_SHIFT16
+    return r;
+}
+
+// The 8-element group at p, which need only be element aligned: one aligned
+// load per 16 bytes when p is 16-byte aligned, else the aligned 16-byte
+// blocks that hold the group's bytes (one more than the group spans), joined
+// in registers. Every block read holds at least one byte of the group, so no
+// read leaves the group's pages. The phase p & 15 must be uniform over the
+// wave (it selects the byte shift).
+template <typename T, bool NT>
+__device__ __forceinline__ Group<T> load_group_any(const T* p) {
+    const uintptr_t a = (uintptr_t)p;
+    const uint32_t sig = (uint32_t)(a & 15);
+    if (sig == 0) return load_group<T, NT>(p);
+    const u32x4* b = reinterpret_cast<const u32x4*>(a & ~(uintptr_t)15);
+    if constexpr (sizeof(T) == 2) {
+        return {shift16(ld<NT>(b), ld<NT>(b + 1), sig)};
+    } else {
+        const u32x4 b0 = ld<NT>(b), b1 = ld<NT>(b + 1), b2 = ld<NT>(b + 2);
+        return {__builtin_bit_cast(f32x4, shift16(b0, b1, sig)), __builtin_bit_cast(f32x4, shift16(b1, b2, sig))};
+    }
+}
+
 // Exact widening of a group to eight fp32 values.
 __device__ __forceinline__ void widen(const Group<uint16_t>& g, float f[8]) {
     f[0] = __uint_as_float(g.v.x << 16);

@@ -117,28 +117,6 @@ struct FlatWsTable {
     __device__ __forceinline__ const void* src(int64_t m, int K, int r) const { return srcs[m * K + r]; }
 };
 
-// 16 bytes starting `sig` bytes into the 32 bytes lo:hi (sig in 1..15, a
-// multiple of the element size): each output dword joins two neighbouring
-// input dwords with one byte-align instruction.
-__device__ __forceinline__ u32x4 shift16(const u32x4& lo, const u32x4& hi, uint32_t sig) {
-    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    const uint32_t b = sig & 3;
-    u32x4 r;
-#define ZR_SHIFT16(q)                                                   \
-    r = u32x4{__builtin_amdgcn_alignbyte(w[(q) + 1], w[(q)], b),          \
-              __builtin_amdgcn_alignbyte(w[(q) + 2], w[(q) + 1], b),      \
-              __builtin_amdgcn_alignbyte(w[(q) + 3], w[(q) + 2], b),      \
-              __builtin_amdgcn_alignbyte(w[(q) + 4], w[(q) + 3], b)}
-    switch (sig >> 2) {  // uniform: the phase of a whole (fragment, rank) copy
-        case 0: ZR_SHIFT16(0); break;
-        case 1: ZR_SHIFT16(1); break;
-        case 2: ZR_SHIFT16(2); break;
-        default: ZR_SHIFT16(3); break;
-    }
-#undef ZR_SHIFT16
-    return r;
-}
-
 // Units are 16-byte blocks of the destination, counted from the block that
 // holds the copy's first byte. A unit wholly inside the copy is stored as
 // one aligned 16-byte store; its 16 source bytes come from one aligned load

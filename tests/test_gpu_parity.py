@@ -358,6 +358,41 @@ def test_all_gather_bit_exact(K, sizes, shift, bf16, offset, gap, ws):
         assert fulls[r].guards_intact() and shards[r].guards_intact()
 
 
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("ws", [False, True], ids=["args", "workspace"])
+def test_all_gather_every_phase_pair(bf16, ws):
+    # one segment per (shard phase, full phase) within 16 bytes, each large
+    # enough that its chunks span two tiles with ragged ends, so whole groups
+    # are loaded from every source phase (one aligned block, or two or three
+    # joined in registers) and stored to every destination grid
+    import torch
+    K = 8
+    per = 8 if bf16 else 4  # elements per 16 bytes
+    n = 8 * (8192 if bf16 else 4096) + 13
+    segs, soff, foff = [], 0, 0
+    for ps in range(per):
+        for pf in range(per):
+            soff += (ps - soff) % per
+            foff += (pf - foff) % per
+            segs.append((soff, foff, n))
+            soff += -(-n // K)
+            foff += n
+    dt = np.uint16 if bf16 else np.float32
+    rng = np.random.default_rng(4242 + per)
+    shard_np = [(rng.integers(0, 65535, size=soff).astype(np.uint16) if bf16 else
+                 rng.standard_normal(soff).astype(np.float32)) for _ in range(K)]
+    shards = [Guarded(soff, torch_dt(bf16), 0, shard_np[r]) for r in range(K)]
+    fulls = [Guarded(foff, torch_dt(bf16), 0, np.zeros(foff, dtype=dt)) for _ in range(K)]
+    zr().zr_all_gather([g.ptr() for g in shards], [g.ptr() for g in fulls], segs, chunk_shift=1,
+                       dtype=torch_dt(bf16), workspace=workspace(ws, K, len(segs)))
+    torch.cuda.synchronize()
+    want = [np.zeros(foff, dtype=dt) for _ in range(K)]
+    oracle.all_gather(shard_np, want, segs, 1)
+    for r in range(K):
+        assert np.array_equal(bits(fulls[r].get()), bits(want[r])), f"rank {r}"
+        assert fulls[r].guards_intact() and shards[r].guards_intact()
+
+
 @pytest.mark.parametrize("K,sizes,bf16,offset,extra", [
     (8, None, True, 0, None),                      # the 64 log-uniform fragments
     (3, [5, 0, 1, 2049, 7, 4096, 33], True, 0, 11),
