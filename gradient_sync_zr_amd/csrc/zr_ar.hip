@@ -15,9 +15,13 @@
 // striding over the tiles ran a few percent slower). S makes a tile write
 // 16 KiB to every rank: at K = 64, 8 slices of bf16 ran 0.9% faster than 4. A tile that lies inside one chunk and below N takes the
 // vector path with the chunk (hence the fold's first rank) uniform across the
-// block; a tile that straddles a chunk boundary or the end of the buffer (at
-// most K of them) folds element by element, reading the rank pointers from an
-// LDS table.
+// block. In a tile that straddles a chunk boundary or the end of the buffer
+// (at most K of them) each lane folds its quads one slice at a time in the
+// ring order of the quad's own chunk, reading the rank pointers from an LDS
+// table; only a quad that a chunk boundary or the end of the buffer cuts folds
+// element by element. (Folding these tiles element by element, a lane waited
+// on K / 8 memory round trips per element, and the few such blocks set the
+// launch time: +21-55% at K = 16-64 and 16M elements.)
 #include "zr_fold.hpp"
 
 namespace zr {
@@ -77,9 +81,21 @@ __global__ void __launch_bounds__(kThreads) ar_kernel(const ArArgs a) {
                 for (int k = 0; k < S; ++k) store_quad<T, NT>(o + 256 * k, res[k]);
             }
         } else {
+#pragma unroll 1
             for (int k = 0; k < S; ++k) {
+                const int64_t q = g0 + 256 * k;  // this lane's quad in slice k
+                const int jq = (int)(q / C);
+                if (a.vec && q + 4 <= N && (q + 3) / C == jq) {
+                    float acc[1][4];
+                    fold_quads<T, KS, NT, 1, ORDER, false>(RingBases<T, 1>(lds_ptr, 0), lds_ptr, K, jq, q, acc);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[0][e] = average<AVG>(acc[0][e], a.inv_k, a.kf);
+                    const Quad<T> res = pack4<T>(acc[0]);
+                    for (int r = 0; r < K; ++r) store_quad<T, NT>(static_cast<T*>(a.out.p[r]) + q, res);
+                    continue;
+                }
                 for (int e = 0; e < 4; ++e) {
-                    const int64_t ge = g0 + 256 * k + e;
+                    const int64_t ge = q + e;
                     if (ge >= N) continue;
                     float s = fold_elem<T, KS, ORDER>(lds_ptr, K, (int)(ge / C), ge);
                     s = average<AVG>(s, a.inv_k, a.kf);
