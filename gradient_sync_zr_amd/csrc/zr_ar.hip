@@ -21,7 +21,12 @@
 // table; only a quad that a chunk boundary or the end of the buffer cuts folds
 // element by element. (Folding these tiles element by element, a lane waited
 // on K / 8 memory round trips per element, and the few such blocks set the
-// launch time: +21-55% at K = 16-64 and 16M elements.)
+// launch time: +21-55% at K = 16-64 and 16M elements.) When every input and
+// output base lies the same number of elements past a quad boundary, the tile
+// grid starts where they reach the next one (`lead` elements in; the next
+// 128-byte line when the bases agree within lines), so every quad is aligned;
+// block 0 folds the first `lead` (< 64) elements one by one. (Such views folded
+// element by element throughout ran 2.5-3.6x slower.)
 #include "zr_fold.hpp"
 
 namespace zr {
@@ -31,8 +36,9 @@ struct ArArgs {
     ConstPtrs in;
     MutPtrs out;
     int64_t N, C, n_tiles;
+    int64_t lead;  // tiles start at this global index (< 64): quads aligned in every buffer
     int K;
-    int vec;  // every in/out base aligned for quad access
+    int vec;  // every in/out base the same `lead` elements before a quad boundary
     float inv_k, kf;
 };
 
@@ -55,8 +61,17 @@ __global__ void __launch_bounds__(kThreads) ar_kernel(const ArArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 
+    if (blockIdx.x == 0 && threadIdx.x < a.lead && threadIdx.x < N) {
+        // the elements before the tile grid, one per thread
+        const int64_t ge = threadIdx.x;
+        float s = fold_elem<T, KS, ORDER>(lds_ptr, K, (int)(ge / C), ge);
+        s = average<AVG>(s, a.inv_k, a.kf);
+        T v;
+        store_elem(&v, s);
+        for (int r = 0; r < K; ++r) static_cast<T*>(a.out.p[r])[ge] = v;
+    }
     for (int64_t t = blockIdx.x; t < a.n_tiles; t += gridDim.x) {
-        const int64_t t0 = t * TT;
+        const int64_t t0 = a.lead + t * TT;
         const int64_t t1 = (t0 + TT < N) ? t0 + TT : N;
         const int j0 = (int)(t0 / C);
         const int j1 = (int)((t1 - 1) / C);
@@ -110,7 +125,8 @@ __global__ void __launch_bounds__(kThreads) ar_kernel(const ArArgs a) {
 
 template <typename T, int KS, int AVG, int ORDER, bool NT>
 hipError_t launch_t(const ArArgs& a, hipStream_t stream) {
-    const int gx = grid_for(a.n_tiles);  // one block per tile
+    // one block per tile; at least one, which also folds the elements before the tiles
+    const int gx = a.n_tiles > 0 ? grid_for(a.n_tiles) : 1;
     hipLaunchKernelGGL((ar_kernel<T, KS, AVG, ORDER, NT>), dim3(gx), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
@@ -154,12 +170,22 @@ hipError_t launch_allreduce_fused(int K, const ConstPtrs& in, const MutPtrs& out
     a.inv_k = 1.0f / (float)K;
     a.kf = (float)K;
     const int64_t tile = dt == ZR_BF16 ? kArTile<uint16_t> : kArTile<float>;
-    a.n_tiles = (N + tile - 1) / tile;
     const uintptr_t al = dt == ZR_BF16 ? 8 : 16;  // quad size
-    bool vec = tuning().force_path != kPathElement;
-    for (int r = 0; r < K; ++r)
-        vec = vec && ((uintptr_t)in.p[r] % al) == 0 && ((uintptr_t)out.p[r] % al) == 0;
+    const uintptr_t es = dt == ZR_BF16 ? 2 : 4;
+    // every base in the same phase within a quad: tiles start where that
+    // phase reaches the next quad boundary
+    // (within a 128-byte line when they all agree there too, so tiles also
+    // start on lines and no two tiles fetch the same line)
+    const uintptr_t phase = (uintptr_t)in.p[0] % al, line_phase = (uintptr_t)in.p[0] % 128;
+    bool vec = tuning().force_path != kPathElement, same_line = true;
+    for (int r = 0; r < K; ++r) {
+        vec = vec && ((uintptr_t)in.p[r] % al) == phase && ((uintptr_t)out.p[r] % al) == phase;
+        same_line = same_line && ((uintptr_t)in.p[r] % 128) == line_phase && ((uintptr_t)out.p[r] % 128) == line_phase;
+    }
     a.vec = vec ? 1 : 0;
+    a.lead = !vec ? 0 : (int64_t)((same_line ? (128 - line_phase) % 128 : (al - phase) % al) / es);
+    if (a.lead > N) a.lead = N;
+    a.n_tiles = (N - a.lead + tile - 1) / tile;
     const bool pow2 = (K & (K - 1)) == 0;
     const int avg_mode = !average ? 0 : (pow2 ? 1 : 2);
     const int ord = order == ZR_ORDER_FREE ? kFree : (order == ZR_ORDER_RING_WIRE ? kWire : kRing);

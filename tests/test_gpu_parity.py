@@ -246,7 +246,16 @@ AR_CASES = [
     (8, 8 * 2048 * 4 + 77, True, True, True, False, 0),
     (8, 8 * 2048 * 4 + 77, True, True, False, True, 0),
     (8, 123457, False, False, True, True, 0),
-    (8, 123457, True, False, True, True, 1),   # misaligned: element-wise fold
+    # bases off the quad grid, all in one phase: the tile grid starts `lead` in
+    (8, 123457, True, False, True, True, 1),
+    (8, 8 * 2048 * 4 + 77, True, True, True, False, 2),
+    (8, 8 * 2048 * 4 + 77, True, True, True, True, 3),
+    (8, 99999, False, False, True, False, 1),
+    (8, 99999, False, True, True, True, 2),
+    (8, 99999, False, False, True, True, 3),
+    (64, 64 * 2048 + 9, True, False, True, True, 1),
+    (4, 2, True, False, True, True, 1),        # N < lead: no tiles, one block
+    (4, 5, False, False, True, False, 3),
     (3, 30001, True, True, True, False, 0),
     (64, 64 * 2048 + 9, True, False, True, True, 0),
     (64, 200003, True, False, False, True, 0),
@@ -275,6 +284,24 @@ def test_allreduce_bit_exact(K, N, bf16, average, fused, inplace, offset):
         assert outs[r].guards_intact()
     if scratch is not None:
         assert scratch.guards_intact()
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_allreduce_ranks_in_different_phases(bf16):
+    # bases in different phases within a quad: no common tile grid, every
+    # element folds one by one
+    import torch
+    K, N = 8, 50003
+    xs = make_inputs(K, N, bf16, 777)
+    ins = [Guarded(N, torch_dt(bf16), r % 4, xs[r]) for r in range(K)]
+    outs = [Guarded(N, torch_dt(bf16), (r + 1) % 4) for r in range(K)]
+    zr().zr_allreduce([g.ptr() for g in ins], [g.ptr() for g in outs], N, average=True, fused=True,
+                      dtype=torch_dt(bf16))
+    torch.cuda.synchronize()
+    want = oracle.allreduce(xs, N, average=True)
+    for r in range(K):
+        assert np.array_equal(bits(outs[r].get()), bits(want[r])), f"rank {r}"
+        assert outs[r].guards_intact()
 
 
 @pytest.mark.parametrize("K,N,bf16", [(8, 99991, True), (64, 64 * 2048 * 2 + 5, True),
