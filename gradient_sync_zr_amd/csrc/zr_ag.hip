@@ -25,8 +25,9 @@
 // phase, each group is read as the aligned 16-byte blocks holding it and
 // shifted into place in registers, so every whole group moves with 16-byte
 // loads and stores (element-by-element copies of such chunks ran 4.5x slower).
-// Only a chunk's partial first and last groups, and every chunk when some
-// base is not 16-byte aligned, copy element by element.
+// The shards may sit at any phase (a chunk reads one shard); the full
+// buffers must share theirs. Only a chunk's partial first and last groups, and
+// every chunk when the full buffers' phases differ, copy element by element.
 #include <vector>
 
 #include "zr_device.hpp"
@@ -48,6 +49,7 @@ struct AgCommon {
     ConstPtrs shards;
     MutPtrs fulls;
     int K, shift;
+    int fphase;  // elements from the full buffers' common 16-byte phase (all equal when vec_mask is set)
 };
 
 // A launch whose segment table rides in its kernel arguments.
@@ -138,7 +140,7 @@ __device__ __forceinline__ void ag_body(const AgCommon& a, const Tab& tab) {
         // group k of this lane covers chunk offsets [x, x + kGroup) with
         // x = (t * SUB + k) * kTile + lane * kGroup - lead: groups start on
         // the destination's 16-byte grid
-        const int64_t lead = vec_chunk ? (dst0 & kLeadMask) : 0;
+        const int64_t lead = vec_chunk ? ((a.fphase + dst0) & kLeadMask) : 0;
         Group<T> v[SUB];
         bool whole[SUB];
 #pragma unroll
@@ -210,12 +212,16 @@ hipError_t pick_k(int K, const Args&... a) {
 // The segment records of a launch (empty segments dropped): vector mask and
 // tiles per chunk of each, and the running first tile.
 int64_t describe(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype dt, const zr_seg* segs,
-                 int n_segs, AgSeg* out, int64_t* unit0, int* used) {
+                 int n_segs, AgSeg* out, int64_t* unit0, int* used, int* fphase) {
     const int es = dt == ZR_BF16 ? 2 : 4;
     const int64_t tile = dt == ZR_BF16 ? kAgTile<uint16_t> : kAgTile<float>;  // elements per tile
-    bool bases = tuning().force_path != kPathElement;  // ZR_FORCE_PATH=element: every chunk element-wise
-    for (int r = 0; r < K; ++r)
-        bases = bases && (((uintptr_t)shards.p[r]) & 15) == 0 && (((uintptr_t)fulls.p[r]) & 15) == 0;
+    // whole groups need one destination grid for all K full buffers (their
+    // bases in one phase within 16 bytes); a chunk's source is one shard, so
+    // the shards may sit anywhere. ZR_FORCE_PATH=element: every chunk element-wise
+    const uintptr_t fph = (uintptr_t)fulls.p[0] & 15;
+    bool bases = tuning().force_path != kPathElement;
+    for (int r = 0; r < K; ++r) bases = bases && (((uintptr_t)fulls.p[r]) & 15) == fph;
+    if (fphase) *fphase = (int)(fph / es);
     int n = 0;
     int64_t units = 0;
     for (int s = 0; s < n_segs; ++s) {
@@ -235,7 +241,7 @@ int64_t describe(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype 
         if (bases) {
             for (int j = 0; j < K; ++j) {
                 d.vec_mask |= 1ull << j;
-                const int64_t l = (d.full_off + (int64_t)j * d.C) & (16 / es - 1);
+                const int64_t l = ((int64_t)(fph / es) + d.full_off + (int64_t)j * d.C) & (16 / es - 1);
                 lead = l > lead ? l : lead;
             }
         }
@@ -257,7 +263,7 @@ hipError_t launch_all_gather(int K, const ConstPtrs& shards, const MutPtrs& full
     a.c.K = K;
     a.c.shift = shift;
     int used = 0;
-    if (describe(K, shards, fulls, dt, segs, n_segs, a.seg, a.unit0, &used) == 0) return hipSuccess;
+    if (describe(K, shards, fulls, dt, segs, n_segs, a.seg, a.unit0, &used, &a.c.fphase) == 0) return hipSuccess;
     a.nseg = used;
     if (dt == ZR_BF16) return pick_k<uint16_t>(K, a, stream);
     return pick_k<float>(K, a, stream);
@@ -270,7 +276,8 @@ hipError_t launch_all_gather_ws(int K, const ConstPtrs& shards, const MutPtrs& f
     int64_t* unit0 = reinterpret_cast<int64_t*>(image.data());
     AgSeg* recs = reinterpret_cast<AgSeg*>(image.data() + 8 * (size_t)(n_segs + 1));
     int used = 0;
-    const int64_t tiles = describe(K, shards, fulls, dt, segs, n_segs, recs, unit0, &used);
+    int fphase = 0;
+    const int64_t tiles = describe(K, shards, fulls, dt, segs, n_segs, recs, unit0, &used, &fphase);
     if (tiles == 0) return hipSuccess;
     // the records were written compactly after n_segs + 1 first-tile slots; the
     // kernel reads used + 1 of them and used records
@@ -279,6 +286,7 @@ hipError_t launch_all_gather_ws(int K, const ConstPtrs& shards, const MutPtrs& f
     a.c.fulls = fulls;
     a.c.K = K;
     a.c.shift = shift;
+    a.c.fphase = fphase;
     a.unit0 = (uint64_t)(uintptr_t)ws;
     a.seg = (uint64_t)(uintptr_t)ws + 8 * (uint64_t)(n_segs + 1);
     a.nseg = used;

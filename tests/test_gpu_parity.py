@@ -420,6 +420,37 @@ def test_all_gather_every_phase_pair(bf16, ws):
         assert fulls[r].guards_intact() and shards[r].guards_intact()
 
 
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("full_offsets", ["shared", "mixed"])
+def test_all_gather_views_off_the_grid(bf16, full_offsets):
+    # every shard at its own phase (a chunk reads one shard, so any phase is
+    # shifted into place); the full buffers at one shared odd phase (whole
+    # groups on their common grid) or at mixed phases (element by element)
+    import torch
+    K = 8
+    sizes = [8 * 8192 * 2 + 13, 999, 8 * 4096 + 7]
+    segs, soff, foff = [], 0, 0
+    for n in sizes:
+        segs.append((soff, foff, n))
+        soff += -(-n // K) + 1
+        foff += n + 3
+    dt = np.uint16 if bf16 else np.float32
+    rng = np.random.default_rng(99 + K)
+    shard_np = [(rng.integers(0, 65535, size=soff).astype(np.uint16) if bf16 else
+                 rng.standard_normal(soff).astype(np.float32)) for _ in range(K)]
+    shards = [Guarded(soff, torch_dt(bf16), r % 8, shard_np[r]) for r in range(K)]
+    fo = (lambda r: 3) if full_offsets == "shared" else (lambda r: (r * 3) % 8)
+    fulls = [Guarded(foff, torch_dt(bf16), fo(r), np.zeros(foff, dtype=dt)) for r in range(K)]
+    zr().zr_all_gather([g.ptr() for g in shards], [g.ptr() for g in fulls], segs, chunk_shift=1,
+                       dtype=torch_dt(bf16))
+    torch.cuda.synchronize()
+    want = [np.zeros(foff, dtype=dt) for _ in range(K)]
+    oracle.all_gather(shard_np, want, segs, 1)
+    for r in range(K):
+        assert np.array_equal(bits(fulls[r].get()), bits(want[r])), f"rank {r}"
+        assert fulls[r].guards_intact() and shards[r].guards_intact()
+
+
 @pytest.mark.parametrize("K,sizes,bf16,offset,extra", [
     (8, None, True, 0, None),                      # the 64 log-uniform fragments
     (3, [5, 0, 1, 2049, 7, 4096, 33], True, 0, 11),
