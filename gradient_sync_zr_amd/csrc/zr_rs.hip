@@ -322,17 +322,17 @@ LaunchFn prepare(RsArgs& a, int K, const ConstPtrs& in, zr_dtype in_dt, int64_t 
 }
 
 // Chunks whose start j*C is not a quad boundary (or whose bases are not quad
-// aligned) fold element by element here, and for K > 8 that costs one memory
-// round trip per eight ranks per element: 0.8-1.1 TB/s at K = 32 and 64
-// against 5-5.3 TB/s for the discrete reduce-scatter over the same data, which
-// reads quads on the input's own grid and stores single elements only where
-// the partition side is not quad aligned. Such a call therefore goes out as
-// that discrete reduce-scatter over one fragment per rank (the whole buffer)
-// and the zero padding up to K*C: the bucket it describes is the input itself,
-// so every ring-order result is the same. (For K <= 8 one batch holds every
-// rank and the element-wise chunks keep the rate.)
+// aligned) would fold element by element here, a memory round trip per eight
+// ranks for every element a lane handles: 0.8-1.1 TB/s at K = 32 and 64, and
+// at small K, where a round trip carries little data, 0.7-3.3 TB/s at K = 2-5.
+// The discrete reduce-scatter over the same data reads quads on the input's
+// own grid and stores single elements only where the partition side is not
+// quad aligned (4.3-6.0 TB/s on the same shapes; at K = 8 and 1 GB, 10-46%
+// faster). Such a call therefore goes out as that discrete reduce-scatter over
+// one fragment per rank (the whole buffer) and the zero padding up to K*C:
+// the bucket it describes is the input itself, so every ring-order result is
+// the same.
 bool via_fragments(const RsArgs& a) {
-    if (a.K <= 8) return false;
     const uint64_t all = a.K >= 64 ? ~0ull : ((1ull << a.K) - 1);
     return (a.vec_mask & all) != all;
 }
