@@ -33,9 +33,11 @@
 // no block does more than a tile's work (one block folding the whole head
 // set the time of small launches): whole quads as vectors, its last few
 // elements one by one. The last tile folds its whole quads below N as
-// vectors and the few elements after them one by one. Chunks
-// whose start does not allow quad access fold element by element tile by
-// tile. Positions g >= N are padding and receive +0.
+// vectors and the few elements after them one by one. A call in which some
+// chunk's start does not allow quad access (or whose bases are not quad
+// aligned) never reaches this kernel: it goes out as the discrete
+// reduce-scatter over one fragment per rank (via_fragments, below).
+// Positions g >= N are padding and receive +0.
 #include <algorithm>
 #include <new>
 
@@ -51,7 +53,7 @@ struct RsArgs {
     ConstPtrs in;
     MutPtrs out;
     int64_t N, C;
-    uint64_t vec_mask;         // bit j: chunk j takes the vector path
+    uint64_t vec_mask;         // bit j: chunk j allows the vector path (all set, or the host routes the call)
     int16_t head[kMaxRanks];   // chunk j's vector tiles start at chunk offset head[j]
     int64_t tile0[kMaxRanks + 1];      // first tile of chunk group q; tile0[ngroups] = all tiles
     int64_t ntile[kMaxRanks];          // tiles of chunk j
@@ -92,7 +94,6 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
         const int64_t t = two ? (w >> 1) : w;
         if (t >= a.ntile[j]) continue;  // the pair's shorter chunk has run out
         const int holder = wrap(j - a.shift + K, K);
-        const bool vec = (a.vec_mask >> j) & 1ull;
         const int64_t chunk_base = (int64_t)j * C;
         TOut* outp = static_cast<TOut*>(a.out.p[holder]);
         const RingBases<TIn, kStatic ? KS : 1> bases(ptr, kStatic ? j : 0);
@@ -128,15 +129,8 @@ __global__ void __launch_bounds__(kThreads) rs_kernel(const RsArgs a) {
             for (int k = 0; k < SS; ++k) store_quad<TOut, NT>(outp + o0 + 256 * k, pack4<TOut>(acc[k]));
         };
 
-        // a vector chunk's tiles: first ceil(min(h, C) / T) head tiles over
-        // [0, h), then tiles over [h, C), the last one possibly partial;
-        // other chunks go element-wise by tiles
-        if (!vec) {
-            const int64_t lo = t * T;
-            const int64_t hi = (lo + T < C) ? lo + T : C;
-            for (int64_t o = lo + threadIdx.x; o < hi; o += kThreads) elem(o);
-            continue;
-        }
+        // the chunk's tiles: first ceil(min(h, C) / T) head tiles over
+        // [0, h), then tiles over [h, C), the last one possibly partial
         const int64_t h = a.head[j];
         const int64_t valid = (N - chunk_base < C) ? N - chunk_base : C;  // non-padding extent
         const int64_t hc = h < C ? h : C;
@@ -271,17 +265,13 @@ LaunchFn prepare_typed(RsArgs& a, int avg_mode, int order) {
         const int64_t to_block = (int64_t)((kOutBlock - ob % kOutBlock) % kOutBlock / sizeof(TOut));
         a.head[j] = (int16_t)(to_block + ((to_line - to_block) % line + line) % line);
     }
-    // tiles of each chunk: a vector chunk's head tiles cover [0, min(head, C))
-    // and its other tiles [head, C); another chunk's cover [0, C); chunks go
-    // in pairs, a pair's blocks alternating between its two chunks
+    // tiles of each chunk: head tiles over [0, min(head, C)), the others over
+    // [head, C); chunks go in pairs, a pair's blocks alternating between its
+    // two chunks
     for (int j = 0; j < a.K; ++j) {
-        if ((a.vec_mask >> j) & 1ull) {
-            const int64_t h = a.head[j];
-            const int64_t hc = h < a.C ? h : a.C;
-            a.ntile[j] = (hc + Tl - 1) / Tl + (a.C > h ? (a.C - h + Tl - 1) / Tl : 0);
-        } else {
-            a.ntile[j] = (a.C + Tl - 1) / Tl;
-        }
+        const int64_t h = a.head[j];
+        const int64_t hc = h < a.C ? h : a.C;
+        a.ntile[j] = (hc + Tl - 1) / Tl + (a.C > h ? (a.C - h + Tl - 1) / Tl : 0);
     }
     a.group = tuning().rs_pairs ? 2 : 1;
     a.ngroups = (a.K + a.group - 1) / a.group;
