@@ -138,6 +138,9 @@ __device__ __forceinline__ void rsf_body(const RsfCommon& c, const Tab& tab) {
     const int K = KS > 0 ? KS : c.K;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    // per wave, one full tile's results in span order (tiles whose partition
+    // side is off the quad grid)
+    __shared__ float stage[kThreads / 64][S * 256];
     using Index = typename Tab::Index;
     const Index total = (Index)tab.total();
     Index s = 0;
@@ -172,6 +175,64 @@ __device__ __forceinline__ void rsf_body(const RsfCommon& c, const Tab& tab) {
         // the partition side is quad aligned at the vector tiles' start or not
         // at all (the tiles advance in whole quads)
         const bool out_quad = (((uintptr_t)(outp + h)) & (4 * sizeof(TOut) - 1)) == 0;
+        // one result v for segment offset o: accumulate, store
+        auto put1 = [&](int64_t o, float v) __attribute__((always_inline)) {
+            if (c.accumulate) v = __fadd_rn(load_elem(outp + o), v);
+            store_elem(outp + o, v);
+        };
+        // A full tile's S folded quads at segment offsets o0 + 256k when the
+        // partition side is d = 1-3 elements past a quad boundary. A wave's S
+        // slices cover one contiguous span of S * 256 results: the wave puts
+        // them in its LDS stage in order, every lane reads back the aligned
+        // quad that starts 4 - d results into its own (the next lane's first
+        // results complete it) and stores it with one aligned store; the 4 - d
+        // results before the span's first boundary and the d after its last are
+        // then stored one by one by lanes 0 and 63. (Storing every result
+        // singly made these tiles store-bound: 4x the store instructions.)
+        auto emit_staged = [&](int64_t o0, float (&acc)[S][4]) __attribute__((always_inline)) {
+            if (!pad) {
+#pragma unroll
+                for (int k = 0; k < S; ++k)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[k][e] = average<AVG>(acc[k][e], c.inv_k, c.kf);
+            }
+            float* st = stage[wave];
+            __syncthreads();  // the stage's previous contents have been read
+#pragma unroll
+            for (int k = 0; k < S; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st[256 * k + 4 * lane + e] = acc[k][e];
+            __syncthreads();
+            const int d = (int)((((uintptr_t)(outp + h)) / sizeof(TOut)) & 3);  // uniform, 1..3
+            const int sh = 4 - d;
+            const int64_t ow = o0 - 4 * lane;  // the span's first result
+#pragma unroll
+            for (int k = 0; k < S; ++k) {
+                const int p = 256 * k + 4 * lane + sh;  // span index of this lane's aligned quad
+                if (p + 4 > S * 256) continue;           // lane 63 of the last slice: the tail
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = st[p + e];
+                TOut* dst = outp + ow + p;  // quad aligned
+                if (c.accumulate) {
+                    float old[4];
+                    widen4(load_quad<TOut, NT>(dst), old);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = __fadd_rn(old[e], v[e]);
+                }
+                store_quad<TOut, NT>(dst, pack4<TOut>(v));
+            }
+            if (lane == 0) {
+#pragma unroll
+                for (int e = 0; e < 3; ++e)
+                    if (e < sh) put1(ow + e, st[e]);
+            }
+            if (lane == 63) {
+#pragma unroll
+                for (int e = 1; e < 4; ++e)
+                    if (e >= sh) put1(ow + S * 256 - 4 + e, st[S * 256 - 4 + e]);
+            }
+        };
         // SS folded quads at segment offsets o0 + 256k: average, accumulate, store
         auto emit = [&](int64_t o0, auto& acc, auto slices) __attribute__((always_inline)) {
             constexpr int SS = decltype(slices)::value;
@@ -245,7 +306,10 @@ __device__ __forceinline__ void rsf_body(const RsfCommon& c, const Tab& tab) {
         if (ot + T <= len) {
             float acc[S][4];
             fold(o0, acc, std::integral_constant<int, S>{});
-            emit(o0, acc, std::integral_constant<int, S>{});
+            if (out_quad)
+                emit(o0, acc, std::integral_constant<int, S>{});
+            else
+                emit_staged(o0, acc);
         } else {
 #pragma unroll 1
             for (int k = 0; k < S; ++k) {
