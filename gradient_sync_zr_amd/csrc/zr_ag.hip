@@ -25,9 +25,12 @@
 // phase, each group is read as the aligned 16-byte blocks holding it and
 // shifted into place in registers, so every whole group moves with 16-byte
 // loads and stores (element-by-element copies of such chunks ran 4.5x slower).
-// The shards may sit at any phase (a chunk reads one shard); the full
-// buffers must share theirs. Only a chunk's partial first and last groups, and
-// every chunk when the full buffers' phases differ, copy element by element.
+// The shards may sit at any phase (a chunk reads one shard). When the full
+// buffers' phases differ, every destination has its own grid: the block
+// stages the tile's source bytes in LDS once (aligned 16-byte loads) and each
+// destination reads its groups from there, shifted for its own phase
+// (element-by-element copies of such gathers ran 5-7x slower). Only a chunk's
+// partial first and last groups copy element by element.
 #include <vector>
 
 #include "zr_device.hpp"
@@ -172,55 +175,150 @@ __device__ __forceinline__ void ag_body(const AgCommon& a, const Tab& tab) {
     }
 }
 
-template <typename T, int KS, bool NT>
+// The same tiles when the full buffers sit in different 16-byte phases.
+// Destination r's groups start on its own grid, lead_r = (its chunk start's
+// element index) mod 16 / sizeof(T) elements before the chunk's offsets, so
+// tile t covers chunk offsets [t tile - lead_r, (t+1) tile - lead_r) of it.
+// The block stages the source elements every destination's tile t needs,
+// [t tile - 16 / sizeof(T) + 1, (t+1) tile) within the chunk, as the aligned
+// 16-byte blocks of the shard that hold them; a destination's whole group is
+// then two (bf16) or three (fp32) of those blocks shifted into place.
+template <typename T, bool NT, typename Tab>
+__device__ __forceinline__ void ag_body_any(const AgCommon& a, const Tab& tab) {
+    constexpr int SUB = kAgSub<T>;
+    constexpr int64_t TILE = kAgTile<T>;
+    constexpr int kLeadMask = 16 / (int)sizeof(T) - 1;
+    constexpr int kBlocks = (int)(TILE * sizeof(T) / 16) + 2;  // 16-byte blocks a tile's span can touch
+    __shared__ u32x4 stage[kBlocks];
+    const int K = a.K;
+    const int64_t total = tab.total();
+    for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
+        const int64_t s = tab.find(u);
+        const AgSeg sg = tab.seg(s);
+        const int ul = (int)(u - tab.first(s));
+        const int j = ul / sg.tiles_per_chunk;
+        const int t = ul - j * sg.tiles_per_chunk;
+        int holder = j - a.shift;
+        if (holder < 0) holder += K;
+        const T* shard = static_cast<const T*>(a.shards.p[holder]) + sg.shard_off;
+        const int64_t dst0 = sg.full_off + (int64_t)j * sg.C;
+        int64_t len = sg.numel - (int64_t)j * sg.C;
+        if (len > sg.C) len = sg.C;
+        int64_t xs = (int64_t)t * TILE - kLeadMask, xe = (int64_t)(t + 1) * TILE;
+        xs = xs > 0 ? xs : 0;
+        xe = xe < len ? xe : len;
+        if (xs >= xe) continue;  // uniform: no element of this chunk in the tile
+        const uintptr_t base = (uintptr_t)(shard + xs) & ~(uintptr_t)15;
+        const int nb = (int)(((uintptr_t)(shard + xe) - base + 15) / 16);  // <= kBlocks
+        for (int i = threadIdx.x; i < nb; i += kThreads) stage[i] = ld<NT>(reinterpret_cast<const u32x4*>(base) + i);
+        __syncthreads();
+        for (int r = 0; r < K; ++r) {
+            T* full = static_cast<T*>(a.fulls.p[r]) + dst0;
+            const int64_t lead = (int64_t)(((uintptr_t)full / sizeof(T)) & kLeadMask);
+#pragma unroll
+            for (int k = 0; k < SUB; ++k) {
+                const int64_t x = ((int64_t)t * SUB + k) * kTile + (int64_t)threadIdx.x * kGroup - lead;
+                if (x >= 0 && x + kGroup <= len) {
+                    // [x, x + 8) lies in [xs, xe): its bytes are staged
+                    const uintptr_t off = (uintptr_t)(shard + x) - base;
+                    const int blk = (int)(off / 16);
+                    const uint32_t sig = (uint32_t)(off & 15);  // uniform: lanes step by whole groups
+                    // blocks past the group's last byte are never read: at
+                    // the span's end they lie beyond what was staged
+                    Group<T> g;
+                    if constexpr (sizeof(T) == 2) {
+                        if (sig == 0)
+                            g.v = stage[blk];
+                        else
+                            g.v = shift16(stage[blk], stage[blk + 1], sig);
+                    } else {
+                        const u32x4 b0 = stage[blk], b1 = stage[blk + 1];
+                        if (sig == 0) {
+                            g.a = __builtin_bit_cast(f32x4, b0);
+                            g.b = __builtin_bit_cast(f32x4, b1);
+                        } else {
+                            const u32x4 b2 = stage[blk + 2];
+                            g.a = __builtin_bit_cast(f32x4, shift16(b0, b1, sig));
+                            g.b = __builtin_bit_cast(f32x4, shift16(b1, b2, sig));
+                        }
+                    }
+                    store_group<T, NT>(full + x, g);
+                } else if (x < len && x + kGroup > 0) {
+                    const int64_t e0 = x > 0 ? x : 0;
+                    const int64_t e1 = x + kGroup < len ? x + kGroup : len;
+                    for (int64_t e = e0; e < e1; ++e) full[e] = shard[e];
+                }
+            }
+        }
+        __syncthreads();  // the stage is read before the next tile fills it
+    }
+}
+
+template <typename T, int KS, bool NT, bool ANY>
 __global__ void __launch_bounds__(kThreads) ag_kernel(const AgArgs a) {
-    ag_body<T, KS, NT>(a.c, AgArgTable{a});
+    if constexpr (ANY)
+        ag_body_any<T, NT>(a.c, AgArgTable{a});
+    else
+        ag_body<T, KS, NT>(a.c, AgArgTable{a});
 }
 
-template <typename T, int KS, bool NT>
+template <typename T, int KS, bool NT, bool ANY>
 __global__ void __launch_bounds__(kThreads) ag_ws_kernel(const AgWsArgs a) {
-    ag_body<T, KS, NT>(a.c, AgWsTable(a));
+    if constexpr (ANY)
+        ag_body_any<T, NT>(a.c, AgWsTable(a));
+    else
+        ag_body<T, KS, NT>(a.c, AgWsTable(a));
 }
 
-template <typename T, int KS, bool NT>
+template <typename T, int KS, bool NT, bool ANY>
 hipError_t launch_t(const AgArgs& a, hipStream_t stream) {
     const int gx = grid_for(a.unit0[a.nseg]);  // one block per tile
-    hipLaunchKernelGGL((ag_kernel<T, KS, NT>), dim3(gx), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((ag_kernel<T, KS, NT, ANY>), dim3(gx), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-template <typename T, int KS, bool NT>
+template <typename T, int KS, bool NT, bool ANY>
 hipError_t launch_t(const AgWsArgs& a, int64_t tiles, hipStream_t stream) {
     const int gx = grid_for(tiles);  // one block per tile, striding beyond the cap
-    hipLaunchKernelGGL((ag_ws_kernel<T, KS, NT>), dim3(gx), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((ag_ws_kernel<T, KS, NT, ANY>), dim3(gx), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-template <typename T, int KS, typename... Args>
+template <typename T, int KS, bool ANY, typename... Args>
 hipError_t pick_nt(const Args&... a) {
-    return tuning().ag_nontemporal ? launch_t<T, KS, true>(a...) : launch_t<T, KS, false>(a...);
+    return tuning().ag_nontemporal ? launch_t<T, KS, true, ANY>(a...) : launch_t<T, KS, false, ANY>(a...);
 }
 
+// K = 8 specialised; full buffers in different phases take the generic
+// kernel built for them
 template <typename T, typename... Args>
-hipError_t pick_k(int K, const Args&... a) {
+hipError_t pick_k(int K, bool any, const Args&... a) {
+    if (any) return pick_nt<T, 0, true>(a...);
     switch (K) {
-        case 8: return pick_nt<T, 8>(a...);
-        default: return pick_nt<T, 0>(a...);
+        case 8: return pick_nt<T, 8, false>(a...);
+        default: return pick_nt<T, 0, false>(a...);
     }
 }
 
 // The segment records of a launch (empty segments dropped): vector mask and
-// tiles per chunk of each, and the running first tile.
+// tiles per chunk of each, and the running first tile. *any: the full
+// buffers sit in different 16-byte phases (the kernels built for that).
 int64_t describe(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype dt, const zr_seg* segs,
-                 int n_segs, AgSeg* out, int64_t* unit0, int* used, int* fphase) {
+                 int n_segs, AgSeg* out, int64_t* unit0, int* used, int* fphase, bool* any) {
     const int es = dt == ZR_BF16 ? 2 : 4;
     const int64_t tile = dt == ZR_BF16 ? kAgTile<uint16_t> : kAgTile<float>;  // elements per tile
-    // whole groups need one destination grid for all K full buffers (their
-    // bases in one phase within 16 bytes); a chunk's source is one shard, so
-    // the shards may sit anywhere. ZR_FORCE_PATH=element: every chunk element-wise
+    // whole groups from registers need one destination grid for all K full
+    // buffers (their bases in one phase within 16 bytes); a chunk's source is
+    // one shard, so the shards may sit anywhere. Full buffers in different
+    // phases stage the source in LDS, and their tiles cover up to
+    // 16 / es - 1 elements before a chunk. ZR_FORCE_PATH=element: every chunk
+    // element-wise
     const uintptr_t fph = (uintptr_t)fulls.p[0] & 15;
-    bool bases = tuning().force_path != kPathElement;
-    for (int r = 0; r < K; ++r) bases = bases && (((uintptr_t)fulls.p[r]) & 15) == fph;
+    const bool allowed = tuning().force_path != kPathElement;
+    bool same = true;
+    for (int r = 0; r < K; ++r) same = same && (((uintptr_t)fulls.p[r]) & 15) == fph;
+    const bool bases = allowed && same;
+    *any = allowed && !same;
     if (fphase) *fphase = (int)(fph / es);
     int n = 0;
     int64_t units = 0;
@@ -237,7 +335,7 @@ int64_t describe(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype 
         // destination's grid: its groups start up to 16 / es - 1 elements
         // before the chunk (the lead), which its tiles must also cover
         d.vec_mask = 0;
-        int64_t lead = 0;
+        int64_t lead = *any ? 16 / es - 1 : 0;
         if (bases) {
             for (int j = 0; j < K; ++j) {
                 d.vec_mask |= 1ull << j;
@@ -263,10 +361,12 @@ hipError_t launch_all_gather(int K, const ConstPtrs& shards, const MutPtrs& full
     a.c.K = K;
     a.c.shift = shift;
     int used = 0;
-    if (describe(K, shards, fulls, dt, segs, n_segs, a.seg, a.unit0, &used, &a.c.fphase) == 0) return hipSuccess;
+    bool any = false;
+    if (describe(K, shards, fulls, dt, segs, n_segs, a.seg, a.unit0, &used, &a.c.fphase, &any) == 0)
+        return hipSuccess;
     a.nseg = used;
-    if (dt == ZR_BF16) return pick_k<uint16_t>(K, a, stream);
-    return pick_k<float>(K, a, stream);
+    if (dt == ZR_BF16) return pick_k<uint16_t>(K, any, a, stream);
+    return pick_k<float>(K, any, a, stream);
 }
 
 hipError_t launch_all_gather_ws(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype dt,
@@ -277,7 +377,8 @@ hipError_t launch_all_gather_ws(int K, const ConstPtrs& shards, const MutPtrs& f
     AgSeg* recs = reinterpret_cast<AgSeg*>(image.data() + 8 * (size_t)(n_segs + 1));
     int used = 0;
     int fphase = 0;
-    const int64_t tiles = describe(K, shards, fulls, dt, segs, n_segs, recs, unit0, &used, &fphase);
+    bool any = false;
+    const int64_t tiles = describe(K, shards, fulls, dt, segs, n_segs, recs, unit0, &used, &fphase, &any);
     if (tiles == 0) return hipSuccess;
     // the records were written compactly after n_segs + 1 first-tile slots; the
     // kernel reads used + 1 of them and used records
@@ -293,8 +394,8 @@ hipError_t launch_all_gather_ws(int K, const ConstPtrs& shards, const MutPtrs& f
     const size_t bytes = 8 * (size_t)(n_segs + 1) + sizeof(AgSeg) * (size_t)used;
     hipError_t e = stage_table(ws, image.data(), bytes, stream, true);
     if (e != hipSuccess) return e;
-    if (dt == ZR_BF16) return pick_k<uint16_t>(K, a, tiles, stream);
-    return pick_k<float>(K, a, tiles, stream);
+    if (dt == ZR_BF16) return pick_k<uint16_t>(K, any, a, tiles, stream);
+    return pick_k<float>(K, any, a, tiles, stream);
 }
 
 }  // namespace zr

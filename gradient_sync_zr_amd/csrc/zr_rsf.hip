@@ -28,23 +28,30 @@
 // a wave-wide search. The grid has one block per tile of the launch, in
 // order, so blocks stay balanced however unequal the fragments are, and the
 // blocks in flight work on one compact window of memory (a persistent grid
-// striding over the tiles ran 7-15% slower). A segment whose rank buffers share one quad phase starts
-// its vector tiles at a 128-byte line of rank j whose output lies less than
-// a line after a 16 KiB boundary of the partition, as the contiguous kernel
-// does: the head before it goes to head tiles of its own (as quads, and its
-// edge elements one by one), the last tile folds its whole quads as vectors
-// and the last few elements one by one, and the stores fall back to single
-// elements when the partition side is not quad aligned. Other segments fold
-// element by element, 1024 elements per tile. The padding entry has null
-// pointers, starts its tiles on a 16 KiB boundary of the partition and
-// writes +0 (old + 0 when accumulating).
+// striding over the tiles ran 7-15% slower). A segment starts its vector
+// tiles at a 128-byte line of rank j whose output lies less than a line
+// after a 16 KiB boundary of the partition, as the contiguous kernel does:
+// the head before it goes to head tiles of its own (as quads, and its edge
+// elements one by one), the last tile folds its whole quads as vectors and
+// the last few elements one by one, and a full tile whose partition side is
+// off the quad grid realigns its results through LDS. When the segment's
+// rank runs sit in different quad phases, the tiles lie on rank j's quads and
+// every other rank's quad is read as the two aligned quads holding it,
+// joined in registers (element by element, such segments ran 4.7-5x slower
+// at K = 16-64 and 13% slower at K = 8). A launch holding such a segment
+// runs kernels that read every segment this way, so the kernels of aligned
+// launches keep their register budget. The free order folds those
+// segments, and every segment under ZR_FORCE_PATH=element, element by
+// element, 1024 elements per tile. The padding entry has null pointers,
+// starts its tiles on a 16 KiB boundary of the partition and writes +0
+// (old + 0 when accumulating).
 #include <climits>
 #include <cstring>
 #include <mutex>
 #include <new>
 #include <vector>
 
-#include "zr_fold.hpp"
+#include "zr_fold_any.hpp"
 
 namespace zr {
 namespace {
@@ -52,6 +59,12 @@ namespace {
 // Entry slots: kRsfEntriesPerLaunch fragments with rank pointers, plus one
 // more for the padding entry, which has none.
 constexpr int kRsfSlots = kRsfEntriesPerLaunch + 1;
+
+// Flag in a segment's head: its rank runs sit in different quad phases, and
+// its vector tiles read each rank's quads as aligned pairs joined in
+// registers (a head is below 16 KiB / 2 + a line of elements, so the flag
+// never meets a head's own bits).
+constexpr int kAnyPhase = 1 << 14;
 
 // Fields every launch carries, whichever table it reads.
 struct RsfCommon {
@@ -71,7 +84,7 @@ struct RsfArgs {
     int32_t tile0[kRsfSegsPerLaunch + 1];  // first tile of segment s; tile0[nseg] = all tiles
     uint8_t seg_m[kRsfSegsPerLaunch];      // entry of segment s
     uint8_t seg_j[kRsfSegsPerLaunch];      // chunk of segment s
-    int16_t seg_head[kRsfSegsPerLaunch];   // vector tiles start at this offset; -1: element-wise
+    int16_t seg_head[kRsfSegsPerLaunch];   // vector tiles start at this offset (| kAnyPhase); -1: element-wise
     int nseg;
 };
 static_assert(sizeof(RsfArgs) <= 4096, "discrete reduce-scatter arguments exceed 4 KB");
@@ -131,7 +144,7 @@ struct WsTable {
 // Elements per tile of a segment that folds element by element (4 per thread).
 constexpr int64_t kElemTile = kThreads * 4;
 
-template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S, typename Tab>
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S, bool ANY, typename Tab>
 __device__ __forceinline__ void rsf_body(const RsfCommon& c, const Tab& tab) {
     constexpr int64_t T = kRsTileOf<S>;
     constexpr bool kStatic = ORDER != kFree && KS > 0 && KS <= 8;
@@ -158,7 +171,9 @@ __device__ __forceinline__ void rsf_body(const RsfCommon& c, const Tab& tab) {
         auto ptr = [=](int r) __attribute__((always_inline)) { return tab.ptr(m, K, r); };
         const bool pad = m == c.pad_m;
         const int64_t tt = t - tab.first(s);
-        const int64_t h = sr.h;
+        // the head without the flag of segments whose ranks sit in
+        // different quad phases (only the kernels built for them see it)
+        const int64_t h = (ANY && sr.h >= 0) ? (sr.h & (kAnyPhase - 1)) : sr.h;
 
         // one output element (segment offset o), folded element-wise
         auto elem = [&](int64_t o) __attribute__((always_inline)) {
@@ -274,6 +289,12 @@ __device__ __forceinline__ void rsf_body(const RsfCommon& c, const Tab& tab) {
                 for (int k = 0; k < SS; ++k)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[k][e] = 0.0f;
+            } else if constexpr (ANY) {
+                // every segment of such a launch, since a rank in the tiles'
+                // phase costs only a repeated load (one fold per call site
+                // keeps these kernels small); the tiles' quads sit at segment
+                // offsets congruent to h mod 4
+                fold_ring_quads_any<TIn, KS, NT, SS, ORDER == kWire>(ptr, K, j, l_lo + o0, l_lo + h, acc);
             } else {
                 const RingBases<TIn, kStatic ? KS : 1> bases(ptr, kStatic ? j : 0);
                 fold_quads<TIn, KS, NT, SS, ORDER, kStatic>(bases, ptr, K, j, l_lo + o0, acc);
@@ -328,31 +349,31 @@ __device__ __forceinline__ void rsf_body(const RsfCommon& c, const Tab& tab) {
     }
 }
 
-template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S, bool ANY>
 __global__ void __launch_bounds__(kThreads) rsf_kernel(const RsfArgs a) {
-    rsf_body<TIn, TOut, KS, AVG, ORDER, NT, S>(a.c, ArgTable{a});
+    rsf_body<TIn, TOut, KS, AVG, ORDER, NT, S, ANY>(a.c, ArgTable{a});
 }
 
-template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S, bool ANY>
 __global__ void __launch_bounds__(kThreads) rsf_ws_kernel(const RsfWsArgs a) {
-    rsf_body<TIn, TOut, KS, AVG, ORDER, NT, S>(a.c, WsTable(a));
+    rsf_body<TIn, TOut, KS, AVG, ORDER, NT, S, ANY>(a.c, WsTable(a));
 }
 
 using LaunchFn = hipError_t (*)(const RsfArgs&, hipStream_t);
 using WsLaunchFn = hipError_t (*)(const RsfWsArgs&, int64_t, hipStream_t);
 
-template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S, bool ANY>
 hipError_t launch_t(const RsfArgs& a, hipStream_t stream) {
     const int gx = grid_for(a.tile0[a.nseg]);  // one block per tile
-    hipLaunchKernelGGL((rsf_kernel<TIn, TOut, KS, AVG, ORDER, NT, S>), dim3(gx), dim3(kThreads), 0,
+    hipLaunchKernelGGL((rsf_kernel<TIn, TOut, KS, AVG, ORDER, NT, S, ANY>), dim3(gx), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
 }
 
-template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S, bool ANY>
 hipError_t launch_ws_t(const RsfWsArgs& a, int64_t tiles, hipStream_t stream) {
     const int gx = grid_for(tiles);  // one block per tile, striding beyond the cap
-    hipLaunchKernelGGL((rsf_ws_kernel<TIn, TOut, KS, AVG, ORDER, NT, S>), dim3(gx), dim3(kThreads), 0,
+    hipLaunchKernelGGL((rsf_ws_kernel<TIn, TOut, KS, AVG, ORDER, NT, S, ANY>), dim3(gx), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
 }
@@ -361,18 +382,24 @@ struct Fns {
     LaunchFn args;
     WsLaunchFn ws;
 };
-template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S>
+template <typename TIn, typename TOut, int KS, int AVG, int ORDER, bool NT, int S, bool ANY = false>
 constexpr Fns fns() {
-    return {&launch_t<TIn, TOut, KS, AVG, ORDER, NT, S>, &launch_ws_t<TIn, TOut, KS, AVG, ORDER, NT, S>};
+    return {&launch_t<TIn, TOut, KS, AVG, ORDER, NT, S, ANY>, &launch_ws_t<TIn, TOut, KS, AVG, ORDER, NT, S, ANY>};
 }
 
 // Ring and wire order at K = 8 specialised, the rest generic (batches of
 // eight ranks in flight); fp32 input makes the wire order the ring order.
-// Small plans in the ring order use one slice per wave.
+// Small plans in the ring order use one slice per wave. Plans with segments
+// whose ranks sit in different quad phases (ring or wire order) take the
+// generic kernels built to read them.
 template <typename TIn, typename TOut, int AVG>
-Fns pick_k(int K, int order, bool small) {
+Fns pick_k(int K, int order, bool small, bool any) {
     constexpr int S = kSlices<TIn, TOut>;
     constexpr bool NT = kRsNontemporal;
+    if (any) {
+        if (order == kWire && sizeof(TIn) == 2) return fns<TIn, TOut, 0, AVG, kWire, NT, S, true>();
+        return small ? fns<TIn, TOut, 0, AVG, kRing, NT, 1, true>() : fns<TIn, TOut, 0, AVG, kRing, NT, S, true>();
+    }
     if (order == kFree) return fns<TIn, TOut, 0, AVG, kFree, NT, S>();
     if (order == kWire && sizeof(TIn) == 2) {
         if (K == 8) return fns<TIn, TOut, 8, AVG, kWire, NT, S>();
@@ -383,11 +410,11 @@ Fns pick_k(int K, int order, bool small) {
 }
 
 template <typename TIn, typename TOut>
-Fns pick_avg(int K, int avg, int order, bool small) {
+Fns pick_avg(int K, int avg, int order, bool small, bool any) {
     switch (avg) {
-        case 1: return pick_k<TIn, TOut, 1>(K, order, small);
-        case 2: return pick_k<TIn, TOut, 2>(K, order, small);
-        default: return pick_k<TIn, TOut, 0>(K, order, small);
+        case 1: return pick_k<TIn, TOut, 1>(K, order, small, any);
+        case 2: return pick_k<TIn, TOut, 2>(K, order, small, any);
+        default: return pick_k<TIn, TOut, 0>(K, order, small, any);
     }
 }
 
@@ -401,32 +428,38 @@ int64_t to_block(uintptr_t out, uintptr_t out_es) { return (int64_t)((kOutBlock 
 
 // Head of a segment whose K rank runs start at byte addresses addr[r] and
 // whose output starts at `out`: the offset of the first 128-byte line of
-// rank j at or after the output's next kOutBlock boundary, or -1 when the
-// runs do not share one quad phase (no offset aligns them all for quad
-// loads).
-int16_t segment_head(const uintptr_t* addr, int K, int j, uintptr_t es, uintptr_t out,
-                     uintptr_t out_es) {
+// rank j at or after the output's next kOutBlock boundary. When the runs do
+// not share one quad phase, that head with the kAnyPhase flag if `any_ok`
+// (the tiles then read the other ranks as aligned pairs), else -1 (element
+// by element).
+int segment_head(const uintptr_t* addr, int K, int j, uintptr_t es, uintptr_t out, uintptr_t out_es,
+                 bool any_ok) {
     const uintptr_t quad = 4 * es;
-    for (int r = 1; r < K; ++r)
-        if ((addr[r] - addr[0]) % quad != 0) return -1;
+    bool same = true;
+    for (int r = 1; r < K; ++r) same = same && (addr[r] - addr[0]) % quad == 0;
+    if (!same && !any_ok) return -1;
     const int64_t line = (int64_t)(128 / es);
     const int64_t to_line = (int64_t)(((128 - addr[j] % 128) % 128) / es);
     const int64_t b = to_block(out, out_es);
-    return (int16_t)(b + ((to_line - b) % line + line) % line);
+    const int h = (int)(b + ((to_line - b) % line + line) % line);
+    return same ? h : (h | kAnyPhase);
 }
+static_assert(kOutBlock / 2 + 64 < (uintptr_t)kAnyPhase, "segment heads must stay below the flag bit");
 
 // One (fragment, chunk) segment of the virtual bucket.
 struct SegDesc {
     int m;       // entry
     int j;       // chunk
-    int head;    // vector tiles start here; -1: element-wise
+    int head;    // vector tiles start here (kAnyPhase: ranks in different quad phases); -1: element-wise
     int64_t tiles;
 };
 
 // Every entry's segments in order (entry ei's are [first[ei], first[ei+1])),
-// with their heads and tile counts for vector tiles of T elements.
+// with their heads and tile counts for vector tiles of T elements. `any_ok`:
+// segments whose ranks sit in different quad phases take vector tiles (ring
+// and wire orders), else they fold element by element.
 template <typename TIn, typename TOut>
-void segments_of(const RsfCommon& c, const FragEntry* entries, int n_entries, int64_t T,
+void segments_of(const RsfCommon& c, const FragEntry* entries, int n_entries, int64_t T, bool any_ok,
                  std::vector<SegDesc>* segs, std::vector<int64_t>* first) {
     const int K = c.K;
     const int64_t C = c.C;
@@ -453,11 +486,12 @@ void segments_of(const RsfCommon& c, const FragEntry* entries, int n_entries, in
                 uintptr_t addr[kMaxRanks];
                 for (int r = 0; r < K; ++r)
                     addr[r] = (uintptr_t)f.ptr[r] + (uintptr_t)(lo - f.off) * sizeof(TIn);
-                h = segment_head(addr, K, j, sizeof(TIn), o, sizeof(TOut));
+                h = segment_head(addr, K, j, sizeof(TIn), o, sizeof(TOut), any_ok);
             }
-            const int64_t hc = h < len ? h : len;
+            const int64_t hv = h < 0 ? h : (h & (kAnyPhase - 1));  // the head itself
+            const int64_t hc = hv < len ? hv : len;
             const int64_t tiles = h < 0 ? (len + kElemTile - 1) / kElemTile
-                                        : (hc + T - 1) / T + (len > h ? (len - h + T - 1) / T : 0);
+                                        : (hc + T - 1) / T + (len > hv ? (len - hv + T - 1) / T : 0);
             segs->push_back(SegDesc{ei, j, h, tiles});
         }
         first->push_back((int64_t)segs->size());
@@ -590,7 +624,8 @@ RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t 
         using TOut = decltype(tout);
         std::vector<SegDesc> segs;
         std::vector<int64_t> first;
-        segments_of<TIn, TOut>(c, entries, n_entries, kRsTile<TIn, TOut>, &segs, &first);
+        const bool any_ok = ord != kFree;
+        segments_of<TIn, TOut>(c, entries, n_entries, kRsTile<TIn, TOut>, any_ok, &segs, &first);
         cut_args(c, entries, n_entries, segs, first, &plan->launches);
         plan->staged = ws != nullptr && plan->launches.size() > 1;
         int64_t most = 0;
@@ -603,7 +638,9 @@ RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t 
         // fewer than two full tiles per CU for each eight ranks: one-slice tiles
         const int64_t k8 = (K + 7) / 8;
         const bool small = ord == kRing && (fp == kPathSmall || (fp != kPathLarge && most < 2LL * k8 * device_cu_count()));
-        if (small) segments_of<TIn, TOut>(c, entries, n_entries, kRsTileOf<1>, &segs, &first);
+        if (small) segments_of<TIn, TOut>(c, entries, n_entries, kRsTileOf<1>, any_ok, &segs, &first);
+        bool any = false;
+        for (const SegDesc& d : segs) any = any || (d.head >= 0 && (d.head & kAnyPhase) != 0);
         if (plan->staged) {
             plan->launches.clear();
             build_image(c, entries, n_entries, segs, (uintptr_t)ws, &plan->wsa, &plan->ws_tiles, &plan->image);
@@ -611,7 +648,7 @@ RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t 
             plan->launches.clear();
             cut_args(c, entries, n_entries, segs, first, &plan->launches);
         }
-        plan->fn = pick_avg<TIn, TOut>(K, avg, ord, small);
+        plan->fn = pick_avg<TIn, TOut>(K, avg, ord, small, any);
     };
     try {
         if (in_dt == ZR_BF16 && out_dt == ZR_FP32)
