@@ -632,7 +632,7 @@ def bench_allreduce64(args):
     ms_step = sum(times) / len(times)
     step_bytes = 2 * K * N * 2
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    src = kernel_source_hash(["zr_ar.hip", "zr_fold.hpp", "zr_device.hpp"])
+    src = kernel_source_hash(["zr_ar.hip", "zr_fold.hpp", "zr_fold_any.hpp", "zr_device.hpp"])
     traffic = read_traffic("ar_ring_bf16_k64_allreduce64.counters.txt", src, step_bytes)
     copy = copy_ceiling_gbps()
     return {
@@ -708,7 +708,7 @@ def bench_frags_layer(args):
     ms = timed(discrete)
     step_bytes = N * (2 * K + 4)  # one launch per step
     value = step_bytes / (ms * 1e-3) / 1e9
-    src = kernel_source_hash(["zr_rsf.hip", "zr_fold.hpp", "zr_device.hpp"])
+    src = kernel_source_hash(["zr_rsf_kernel.hpp", "zr_rsf.hip", "zr_fold.hpp", "zr_fold_any.hpp", "zr_device.hpp"])
     traffic = read_traffic("rsf_ring_bf16_f32_k8_frags_layer.counters.txt", src, step_bytes)
     copy = copy_ceiling_gbps()
     return {
