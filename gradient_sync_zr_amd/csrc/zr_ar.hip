@@ -34,8 +34,7 @@
 // holding it and joined in registers, and each wave's results go through LDS:
 // every rank reads back the quads aligned to its own output and stores them
 // whole, its at most 3 + 3 edge elements one by one. (Element-by-element
-// folds of such views ran 2.3-5.8x slower at K = 8-64.) The free order folds
-// them element by element.
+// folds of such views ran 2.3-5.8x slower at K = 8-64.)
 #include "zr_fold_any.hpp"
 
 namespace zr {
@@ -104,7 +103,10 @@ __device__ __forceinline__ void ar_tile_any(const ArArgs& a, PtrFn lds_ptr, T (*
         // uniform, so each rank's phase and base stay scalar
         float acc[S][4];
         auto ptr = [&](int r) { return a.in.p[r]; };
-        fold_ring_quads_any<T, KS, NT, S, WIRE>(ptr, K, j0, g0, t0, acc);
+        if constexpr (ORDER == kFree)
+            fold_free_quads_any<T, KS, NT, S>(ptr, K, g0, t0, acc);
+        else
+            fold_ring_quads_any<T, KS, NT, S, WIRE>(ptr, K, j0, g0, t0, acc);
 #pragma unroll
         for (int k = 0; k < S; ++k) put(k, acc[k]);
     } else {
@@ -114,7 +116,10 @@ __device__ __forceinline__ void ar_tile_any(const ArArgs& a, PtrFn lds_ptr, T (*
             const int jq = (int)(q / C);
             if (q + 4 <= N && (q + 3) / C == jq) {
                 float acc[1][4];
-                fold_ring_quads_any<T, KS, NT, 1, WIRE>(lds_ptr, K, jq, q, t0, acc);
+                if constexpr (ORDER == kFree)
+                    fold_free_quads_any<T, KS, NT, 1>(lds_ptr, K, q, t0, acc);
+                else
+                    fold_ring_quads_any<T, KS, NT, 1, WIRE>(lds_ptr, K, jq, q, t0, acc);
                 put(k, acc[0]);
                 continue;
             }
@@ -260,6 +265,7 @@ hipError_t pick_nt(const ArArgs& a, hipStream_t s) {
 template <typename T, int AVG>
 hipError_t pick_k(const ArArgs& a, int order, hipStream_t s) {
     if (a.any) {  // bases in different quad phases: the generic kernels built for them
+        if (order == kFree) return pick_nt<T, 0, AVG, kFree, true>(a, s);
         if (order == kWire && sizeof(T) == 2) return pick_nt<T, 0, AVG, kWire, true>(a, s);
         return pick_nt<T, 0, AVG, kRing, true>(a, s);
     }
@@ -308,9 +314,9 @@ hipError_t launch_allreduce_fused(int K, const ConstPtrs& in, const MutPtrs& out
     }
     const int ord = order == ZR_ORDER_FREE ? kFree : (order == ZR_ORDER_RING_WIRE ? kWire : kRing);
     a.vec = vec ? 1 : 0;
-    // bases in different quad phases (ring and wire orders): tiles on rank
-    // 0's input lines, every quad read as an aligned pair
-    a.any = !vec && tuning().force_path != kPathElement && ord != kFree ? 1 : 0;
+    // bases in different quad phases: tiles on rank 0's input lines, every
+    // quad read as an aligned pair
+    a.any = !vec && tuning().force_path != kPathElement ? 1 : 0;
     a.lead = a.any ? (int64_t)(((128 - line_phase) % 128) / es)
                    : !vec ? 0 : (int64_t)((same_line ? (128 - line_phase) % 128 : (al - phase) % al) / es);
     if (a.lead > N) a.lead = N;

@@ -1,4 +1,5 @@
-// Ring-order folds over rank buffers whose quad phases differ.
+// Folds over rank buffers whose quad phases differ (ring, wire and free
+// orders).
 //
 // The quad folds of zr_fold.hpp need every rank's buffer on one quad grid:
 // each lane loads a quad of every rank with one aligned access. When ranks
@@ -99,6 +100,64 @@ __device__ __forceinline__ void fold_ring_quads_any(PtrFn ptr, int K, int j, int
                         }
                     }
                 }
+            }
+        }
+    }
+}
+
+// Free order over ranks in any quad phases: the association of
+// fold_free_quads (ranks 0..K-1 in batches of eight, each batch summed as a
+// balanced pairwise tree, batches added in sequence), with every rank's quad
+// read as an aligned pair. The ranks' order does not depend on the chunk, so
+// the phases stay uniform whenever gu and the pointers are.
+template <typename TIn, int KS, bool NT, int S, typename PtrFn>
+__device__ __forceinline__ void fold_free_quads_any(PtrFn ptr, int K, int64_t g0, int64_t gu, float acc[S][4]) {
+    constexpr int SG = kAnySlices<TIn, S>;
+    constexpr int B = 8;
+    constexpr uintptr_t QB = 4 * sizeof(TIn);
+    const int Kr = KS > 0 ? KS : K;
+#pragma unroll
+    for (int k0 = 0; k0 < S; k0 += SG) {
+        for (int h0 = 0; h0 < Kr; h0 += B) {
+            Quad<TIn> lo[SG][B], hi[SG][B];
+            uint32_t sig[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                if (h0 + b < Kr) {
+                    const char* p = static_cast<const char*>(ptr(h0 + b));
+                    sig[b] = (uint32_t)(((uintptr_t)p + (uintptr_t)gu * sizeof(TIn)) & (QB - 1));
+                    const char* pl = p - sig[b];
+                    const char* ph = pl + (sig[b] ? QB : 0);
+#pragma unroll
+                    for (int k = 0; k < SG; ++k) {
+                        const int64_t off = (g0 + 256 * (k0 + k)) * (int64_t)sizeof(TIn);
+                        lo[k][b] = load_quad<TIn, NT>(reinterpret_cast<const TIn*>(pl + off));
+                        hi[k][b] = load_quad<TIn, NT>(reinterpret_cast<const TIn*>(ph + off));
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < SG; ++k) {
+                float f[B][4];
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    if (h0 + b < Kr) {
+                        widen4(join_quad(lo[k][b], hi[k][b], sig[b]), f[b]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) f[b][e] = 0.0f;
+                    }
+                }
+#pragma unroll
+                for (int st = 1; st < B; st *= 2)
+#pragma unroll
+                    for (int b = 0; b + st < B; b += 2 * st)
+                        if (h0 + b + st < Kr)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) f[b][e] = __fadd_rn(f[b][e], f[b + st][e]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[k0 + k][e] = (h0 == 0) ? f[0][e] : __fadd_rn(acc[k0 + k][e], f[0][e]);
             }
         }
     }

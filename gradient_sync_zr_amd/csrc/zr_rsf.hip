@@ -29,16 +29,13 @@ int64_t to_block(uintptr_t out, uintptr_t out_es) { return (int64_t)((kOutBlock 
 
 // Head of a segment whose K rank runs start at byte addresses addr[r] and
 // whose output starts at `out`: the offset of the first 128-byte line of
-// rank j at or after the output's next kOutBlock boundary. When the runs do
-// not share one quad phase, that head with the kAnyPhase flag if `any_ok`
-// (the tiles then read the other ranks as aligned pairs), else -1 (element
-// by element).
-int segment_head(const uintptr_t* addr, int K, int j, uintptr_t es, uintptr_t out, uintptr_t out_es,
-                 bool any_ok) {
+// rank j at or after the output's next kOutBlock boundary, with the
+// kAnyPhase flag when the runs do not share one quad phase (the tiles then
+// read the other ranks as aligned pairs).
+int segment_head(const uintptr_t* addr, int K, int j, uintptr_t es, uintptr_t out, uintptr_t out_es) {
     const uintptr_t quad = 4 * es;
     bool same = true;
     for (int r = 1; r < K; ++r) same = same && (addr[r] - addr[0]) % quad == 0;
-    if (!same && !any_ok) return -1;
     const int64_t line = (int64_t)(128 / es);
     const int64_t to_line = (int64_t)(((128 - addr[j] % 128) % 128) / es);
     const int64_t b = to_block(out, out_es);
@@ -56,11 +53,10 @@ struct SegDesc {
 };
 
 // Every entry's segments in order (entry ei's are [first[ei], first[ei+1])),
-// with their heads and tile counts for vector tiles of T elements. `any_ok`:
-// segments whose ranks sit in different quad phases take vector tiles (ring
-// and wire orders), else they fold element by element.
+// with their heads and tile counts for vector tiles of T elements (-1 heads,
+// element by element, only under ZR_FORCE_PATH=element).
 template <typename TIn, typename TOut>
-void segments_of(const RsfCommon& c, const FragEntry* entries, int n_entries, int64_t T, bool any_ok,
+void segments_of(const RsfCommon& c, const FragEntry* entries, int n_entries, int64_t T,
                  std::vector<SegDesc>* segs, std::vector<int64_t>* first) {
     const int K = c.K;
     const int64_t C = c.C;
@@ -87,7 +83,7 @@ void segments_of(const RsfCommon& c, const FragEntry* entries, int n_entries, in
                 uintptr_t addr[kMaxRanks];
                 for (int r = 0; r < K; ++r)
                     addr[r] = (uintptr_t)f.ptr[r] + (uintptr_t)(lo - f.off) * sizeof(TIn);
-                h = segment_head(addr, K, j, sizeof(TIn), o, sizeof(TOut), any_ok);
+                h = segment_head(addr, K, j, sizeof(TIn), o, sizeof(TOut));
             }
             const int64_t hv = h < 0 ? h : (h & (kAnyPhase - 1));  // the head itself
             const int64_t hc = hv < len ? hv : len;
@@ -225,8 +221,7 @@ RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t 
         using TOut = decltype(tout);
         std::vector<SegDesc> segs;
         std::vector<int64_t> first;
-        const bool any_ok = ord != kFree;
-        segments_of<TIn, TOut>(c, entries, n_entries, kRsTile<TIn, TOut>, any_ok, &segs, &first);
+        segments_of<TIn, TOut>(c, entries, n_entries, kRsTile<TIn, TOut>, &segs, &first);
         cut_args(c, entries, n_entries, segs, first, &plan->launches);
         plan->staged = ws != nullptr && plan->launches.size() > 1;
         int64_t most = 0;
@@ -239,7 +234,7 @@ RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t 
         // fewer than two full tiles per CU for each eight ranks: one-slice tiles
         const int64_t k8 = (K + 7) / 8;
         const bool small = ord == kRing && (fp == kPathSmall || (fp != kPathLarge && most < 2LL * k8 * device_cu_count()));
-        if (small) segments_of<TIn, TOut>(c, entries, n_entries, kRsTileOf<1>, any_ok, &segs, &first);
+        if (small) segments_of<TIn, TOut>(c, entries, n_entries, kRsTileOf<1>, &segs, &first);
         bool any = false;
         for (const SegDesc& d : segs) any = any || (d.head >= 0 && (d.head & kAnyPhase) != 0);
         if (plan->staged) {

@@ -40,9 +40,8 @@
 // joined in registers (element by element, such segments ran 4.7-5x slower
 // at K = 16-64 and 13% slower at K = 8). A launch holding such a segment
 // runs kernels that read every segment this way, so the kernels of aligned
-// launches keep their register budget. The free order folds those
-// segments, and every segment under ZR_FORCE_PATH=element, element by
-// element, 1024 elements per tile. The padding entry has null pointers,
+// launches keep their register budget. Under ZR_FORCE_PATH=element every
+// segment folds element by element, 1024 elements per tile. The padding entry has null pointers,
 // starts its tiles on a 16 KiB boundary of the partition and writes +0
 // (old + 0 when accumulating).
 //
@@ -297,7 +296,10 @@ __device__ __forceinline__ void rsf_body(const RsfCommon& c, const Tab& tab) {
                 // phase costs only a repeated load (one fold per call site
                 // keeps these kernels small); the tiles' quads sit at segment
                 // offsets congruent to h mod 4
-                fold_ring_quads_any<TIn, KS, NT, SS, ORDER == kWire>(ptr, K, j, l_lo + o0, l_lo + h, acc);
+                if constexpr (ORDER == kFree)
+                    fold_free_quads_any<TIn, KS, NT, SS>(ptr, K, l_lo + o0, l_lo + h, acc);
+                else
+                    fold_ring_quads_any<TIn, KS, NT, SS, ORDER == kWire>(ptr, K, j, l_lo + o0, l_lo + h, acc);
             } else {
                 const RingBases<TIn, kStatic ? KS : 1> bases(ptr, kStatic ? j : 0);
                 fold_quads<TIn, KS, NT, SS, ORDER, kStatic>(bases, ptr, K, j, l_lo + o0, acc);
@@ -393,13 +395,14 @@ constexpr Fns fns() {
 // Ring and wire order at K = 8 specialised, the rest generic (batches of
 // eight ranks in flight); fp32 input makes the wire order the ring order.
 // Small plans in the ring order use one slice per wave. Plans with segments
-// whose ranks sit in different quad phases (ring or wire order) take the
-// generic kernels built to read them.
+// whose ranks sit in different quad phases take the generic kernels built to
+// read them.
 template <typename TIn, typename TOut, int AVG>
 Fns pick_k(int K, int order, bool small, bool any) {
     constexpr int S = kSlices<TIn, TOut>;
     constexpr bool NT = kRsNontemporal;
     if (any) {
+        if (order == kFree) return fns<TIn, TOut, 0, AVG, kFree, NT, S, true>();
         if (order == kWire && sizeof(TIn) == 2) return fns<TIn, TOut, 0, AVG, kWire, NT, S, true>();
         return small ? fns<TIn, TOut, 0, AVG, kRing, NT, 1, true>() : fns<TIn, TOut, 0, AVG, kRing, NT, S, true>();
     }
