@@ -41,9 +41,9 @@
 // at K = 16-64 and 13% slower at K = 8). A launch holding such a segment
 // runs kernels that read every segment this way, so the kernels of aligned
 // launches keep their register budget. Under ZR_FORCE_PATH=element every
-// segment folds element by element, 1024 elements per tile. The padding entry has null pointers,
-// starts its tiles on a 16 KiB boundary of the partition and writes +0
-// (old + 0 when accumulating).
+// segment folds element by element, 1024 elements per tile. The padding
+// entry has null pointers, starts its tiles on a 16 KiB boundary of the
+// partition and writes +0 (old + 0 when accumulating).
 //
 // The kernels live in this header; each (input, output) dtype pair is
 // instantiated in a translation unit of its own (zr_rsf_<in>_<out>.hip) so

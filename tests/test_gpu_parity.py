@@ -1,6 +1,6 @@
 """GPU parity of every entry point against the CPU oracle, at sizes the oracle
 finishes in seconds: several 2048-element tiles plus ragged tails, misaligned
-bases (the element-wise paths), every dtype pair, chunk shifts, averaging,
+bases (tile grids shifted onto them), every dtype pair, chunk shifts, averaging,
 K from 1 to 64, and the degenerate cases (N = 0, N < K, K = 1).
 
 Ring order must match the oracle bit for bit; the free order must lie within
@@ -61,7 +61,7 @@ RS_CASES = [
     (8, 100003, True, True, 1, True, 0),
     (8, 100003, False, False, 0, True, 0),
     (8, 100003, False, True, 3, False, 0),
-    (8, 65536, True, False, 1, True, 1),         # misaligned bases: element-wise path
+    (8, 65536, True, False, 1, True, 1),         # bases off the quad grid: the discrete path's tiles
     (8, 65536 + 5, False, False, 1, True, 3),
     (5, 77777, True, False, 2, True, 0),         # non power of two: IEEE divide
     (3, 50001, False, True, 1, True, 0),
@@ -120,7 +120,7 @@ ACC_CASES = [
     (8, 8 * 4096 * 3 + 8 * 40, True, False, 1, True, 0),
     (8, 100003, True, True, 1, True, 0),
     (5, 77777, False, False, 2, True, 0),
-    (8, 65536 + 5, True, False, 0, False, 1),     # element-wise path
+    (8, 65536 + 5, True, False, 0, False, 1),     # bases off the quad grid
     (64, 64 * 4096 + 3, True, False, 1, True, 0),
     (3, 2, True, False, 1, True, 0),
     (8, 8 * 300000 + 13, True, False, 1, True, 0),   # four-slice tiles
@@ -154,7 +154,7 @@ WIRE_CASES = [
     # K, N, out_bf16, shift, average, offset
     (8, 8 * 4096 * 3 + 8 * 40, False, 1, True, 0),
     (8, 100003, True, 1, False, 0),
-    (8, 65536 + 5, False, 0, True, 1),          # element-wise path
+    (8, 65536 + 5, False, 0, True, 1),          # bases off the quad grid
     (5, 77777, False, 2, True, 0),
     (64, 64 * 4096 + 3, True, 1, False, 0),
 ]
@@ -288,8 +288,8 @@ def test_allreduce_bit_exact(K, N, bf16, average, fused, inplace, offset):
 
 @pytest.mark.parametrize("bf16", [True, False])
 def test_allreduce_ranks_in_different_phases(bf16):
-    # bases in different phases within a quad: no common tile grid, every
-    # element folds one by one
+    # bases in different phases within a quad: no common tile grid, so every
+    # rank's quad is read as an aligned pair and every output realigned in LDS
     import torch
     K, N = 8, 50003
     xs = make_inputs(K, N, bf16, 777)
@@ -425,7 +425,8 @@ def test_all_gather_every_phase_pair(bf16, ws):
 def test_all_gather_views_off_the_grid(bf16, full_offsets):
     # every shard at its own phase (a chunk reads one shard, so any phase is
     # shifted into place); the full buffers at one shared odd phase (whole
-    # groups on their common grid) or at mixed phases (element by element)
+    # groups on their common grid) or at mixed phases (each tile's source
+    # staged in LDS and shifted per destination)
     import torch
     K = 8
     sizes = [8 * 8192 * 2 + 13, 999, 8 * 4096 + 7]
