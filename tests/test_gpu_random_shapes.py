@@ -6,10 +6,15 @@ picked: K from 1 to 64, sizes from 1 element to several tiles with ragged
 tails, both dtypes and every dtype pair, chunk shifts, averaging, gradient
 accumulation and the bf16-wire order, base offsets shared by every rank or
 different per rank (which moves calls between the vector paths, the
-re-gridded paths and the element-by-element ones), one-shot calls and plans,
-with and without a workspace. K * N stays small, so the oracle finishes each
-case at once.
+re-gridded paths and the aligned-pair paths for ranks in different phases),
+one-shot calls and plans, with and without a workspace. K * N stays small, so
+the oracle finishes each case at once.
+
+ZR_RANDOM_SCALE multiplies the number of cases and ZR_RANDOM_SEED shifts the
+seed, for a longer sweep than the default run.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -19,7 +24,8 @@ from gpu_util import Guarded, bits
 
 pytestmark = pytest.mark.gpu
 
-SEED = 0x5A5200F0
+SEED = 0x5A5200F0 + int(os.environ.get("ZR_RANDOM_SEED", "0"))
+SCALE = int(os.environ.get("ZR_RANDOM_SCALE", "1"))
 KS = [1, 2, 3, 4, 5, 7, 8, 9, 16, 17, 31, 64]
 
 
@@ -61,7 +67,7 @@ def workspace(rng, K, n):
     return torch.empty(max(256, zr().zr_workspace_bytes(K, n)), dtype=torch.uint8, device="cuda")
 
 
-@pytest.mark.parametrize("case", range(80))
+@pytest.mark.parametrize("case", range(80 * SCALE))
 def test_random_reduce_scatter(case):
     import torch
     rng = np.random.default_rng(SEED + 1000 + case)
@@ -101,7 +107,7 @@ def test_random_reduce_scatter(case):
         assert outs[r].guards_intact() and ins[r].guards_intact()
 
 
-@pytest.mark.parametrize("case", range(60))
+@pytest.mark.parametrize("case", range(60 * SCALE))
 def test_random_reduce_scatter_frags(case):
     import torch
     rng = np.random.default_rng(SEED + 2000 + case)
@@ -147,7 +153,7 @@ def test_random_reduce_scatter_frags(case):
         assert outs[r].guards_intact()
 
 
-@pytest.mark.parametrize("case", range(60))
+@pytest.mark.parametrize("case", range(60 * SCALE))
 def test_random_all_gather(case):
     import torch
     rng = np.random.default_rng(SEED + 3000 + case)
@@ -182,7 +188,7 @@ def test_random_all_gather(case):
         assert fulls[r].guards_intact() and shards[r].guards_intact()
 
 
-@pytest.mark.parametrize("case", range(60))
+@pytest.mark.parametrize("case", range(60 * SCALE))
 def test_random_allreduce(case):
     import torch
     rng = np.random.default_rng(SEED + 4000 + case)
@@ -208,7 +214,7 @@ def test_random_allreduce(case):
         assert outs[r].guards_intact()
 
 
-@pytest.mark.parametrize("case", range(60))
+@pytest.mark.parametrize("case", range(60 * SCALE))
 def test_random_flatten(case):
     import torch
     rng = np.random.default_rng(SEED + 5000 + case)
