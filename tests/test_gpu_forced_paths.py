@@ -5,7 +5,8 @@ between 16-byte (quad) access and element-by-element folds or copies from
 their inputs' alignment, and the ring-order reduce-scatters choose one-slice
 tiles for launches too small to fill the GPU and four-slice tiles otherwise.
 ZR_FORCE_PATH overrides those choices (read once per process, so each
-setting runs the whole bit-exact parity module in a child process):
+setting runs the whole bit-exact parity module, and the module of ranks in
+different phases, in a child process):
 
   element  every aligned case also goes element by element (with ZR_DEBUG=1,
            so every call waits for its stream and reports a kernel error
@@ -33,6 +34,7 @@ pytestmark = pytest.mark.gpu
                          ids=["element_debug", "large", "small"])
 def test_parity_on_forced_paths(env):
     cmd = [sys.executable, "-u", "-m", "pytest", os.path.join(ROOT, "tests", "test_gpu_parity.py"),
+           os.path.join(ROOT, "tests", "test_gpu_mixed_phases.py"),
            "-x", "-q", "-m", "gpu", "-p", "no:cacheprovider", "--timeout", "300",
            "--timeout-method", "thread"]
     print(f"forced path: running the parity module with {env}", flush=True)
