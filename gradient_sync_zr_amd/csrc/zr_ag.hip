@@ -15,22 +15,26 @@
 // segments per launch; given a workspace, any number of segments go out as
 // one launch that reads a table staged there (scalar loads, wave-wide
 // search). (A persistent grid striding over the tiles ran
-// 10-15% slower.) A tile writes 16 KiB to every full buffer: each lane loads
-// kAgSub groups of 8 shard elements (16 bytes each for bf16), all before its
-// first store, and stores each to all K full buffers, so each shard byte is
-// read once and written K times. (Tiles of 16 KiB per destination ran 1% faster
-// than tiles of 4, 8 or 32 KiB.) A chunk's groups are aligned to its
-// destination, whose start full_off + j*C may fall anywhere within 16 bytes
-// (full_off is a running sum of tensor sizes); when the source is in another
-// phase, each group is read as the aligned 16-byte blocks holding it and
-// shifted into place in registers, so every whole group moves with 16-byte
-// loads and stores (element-by-element copies of such chunks ran 4.5x slower).
-// The shards may sit at any phase (a chunk reads one shard). When the full
-// buffers' phases differ, every destination has its own grid: the block
-// stages the tile's source bytes in LDS once (aligned 16-byte loads) and each
-// destination reads its groups from there, shifted for its own phase
-// (element-by-element copies of such gathers ran 5-7x slower). Only a chunk's
-// partial first and last groups copy element by element.
+// 10-15% slower.) A tile writes 16 KiB to every full buffer in 16-byte units
+// (8 bf16 or 4 fp32 elements): each lane loads kAgSub units of the shard, all
+// before its first store, and stores each to all K full buffers, so each
+// shard byte is read once and written K times. Lane l of a wave takes unit l
+// of each 1 KiB span, so every store instruction writes one contiguous 1 KiB.
+// (Tiles of 16 KiB per destination ran 1% faster than tiles of 4, 8 or
+// 32 KiB. With 32-byte fp32 groups per lane, each store instruction covered
+// its span at half density and fp32 gathers ran at 2.0-2.8 TB/s.) A chunk's
+// units are aligned to its destination, whose start full_off + j*C may fall
+// anywhere within 16 bytes (full_off is a running sum of tensor sizes); when
+// the source is in another phase, each unit is read as the two aligned
+// 16-byte blocks holding it and shifted into place in registers, so every
+// whole unit moves with 16-byte loads and stores (element-by-element copies
+// of such chunks ran 4.5x slower). The shards may sit at any phase (a chunk
+// reads one shard). When the full buffers' phases differ, every destination
+// has its own grid: the block stages the tile's source bytes in LDS once
+// (aligned 16-byte loads) and each destination reads its units from there,
+// shifted for its own phase (element-by-element copies of such gathers ran
+// 5-7x slower). Only a chunk's partial first and last units copy element by
+// element.
 #include <vector>
 
 #include "zr_device.hpp"
@@ -114,16 +118,31 @@ struct AgWsTable {
     }
 };
 
-// Groups of kGroup elements per lane in one tile: 16 KiB per destination.
+// 16-byte units per lane in one tile (16 KiB per destination), the elements
+// of a unit, and the elements of a tile.
+constexpr int kAgSub = 16384 / (kThreads * 16);
 template <typename T>
-constexpr int kAgSub = 16384 / (kTile * (int)sizeof(T));
+constexpr int kAgUnit = 16 / (int)sizeof(T);
 template <typename T>
-constexpr int64_t kAgTile = (int64_t)kAgSub<T> * kTile;
+constexpr int64_t kAgTile = (int64_t)kAgSub * kThreads * kAgUnit<T>;
+
+// The 16 bytes at p, which need only be element aligned: one aligned load,
+// or the two aligned 16-byte blocks that hold them (each holds at least one
+// of their bytes, so no read leaves their pages) joined in registers. The
+// phase p & 15 must be uniform over the wave.
+template <bool NT>
+__device__ __forceinline__ u32x4 load16_any(const void* p) {
+    const uintptr_t a = (uintptr_t)p;
+    const uint32_t sig = (uint32_t)(a & 15);
+    const u32x4* b = reinterpret_cast<const u32x4*>(a & ~(uintptr_t)15);
+    if (sig == 0) return ld<NT>(b);
+    return shift16(ld<NT>(b), ld<NT>(b + 1), sig);
+}
 
 template <typename T, int KS, bool NT, typename Tab>
 __device__ __forceinline__ void ag_body(const AgCommon& a, const Tab& tab) {
-    constexpr int SUB = kAgSub<T>;
-    constexpr int kLeadMask = 16 / (int)sizeof(T) - 1;  // a destination's phase, in elements
+    constexpr int SUB = kAgSub;
+    constexpr int E = kAgUnit<T>;
     const int K = KS > 0 ? KS : a.K;
     const int64_t total = tab.total();
     for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
@@ -140,32 +159,32 @@ __device__ __forceinline__ void ag_body(const AgCommon& a, const Tab& tab) {
         const int64_t dst0 = sg.full_off + (int64_t)j * sg.C;  // the chunk's start in every full buffer
         int64_t len = sg.numel - (int64_t)j * sg.C;            // its elements (<= 0: none)
         if (len > sg.C) len = sg.C;
-        // group k of this lane covers chunk offsets [x, x + kGroup) with
-        // x = (t * SUB + k) * kTile + lane * kGroup - lead: groups start on
-        // the destination's 16-byte grid
-        const int64_t lead = vec_chunk ? ((a.fphase + dst0) & kLeadMask) : 0;
-        Group<T> v[SUB];
+        // unit k of this lane covers chunk offsets [x, x + E) with
+        // x = ((t * SUB + k) * kThreads + tid) * E - lead: units start on the
+        // destination's 16-byte grid
+        const int64_t lead = vec_chunk ? ((a.fphase + dst0) & (E - 1)) : 0;
+        u32x4 v[SUB];
         bool whole[SUB];
 #pragma unroll
         for (int k = 0; k < SUB; ++k) {
-            const int64_t x = ((int64_t)t * SUB + k) * kTile + (int64_t)threadIdx.x * kGroup - lead;
-            whole[k] = vec_chunk && x >= 0 && x + kGroup <= len;
-            if (whole[k]) v[k] = load_group_any<T, NT>(shard + x);
+            const int64_t x = (((int64_t)t * SUB + k) * kThreads + threadIdx.x) * E - lead;
+            whole[k] = vec_chunk && x >= 0 && x + E <= len;
+            if (whole[k]) v[k] = load16_any<NT>(shard + x);
         }
 #pragma unroll
         for (int k = 0; k < SUB; ++k) {
-            const int64_t x = ((int64_t)t * SUB + k) * kTile + (int64_t)threadIdx.x * kGroup - lead;
+            const int64_t x = (((int64_t)t * SUB + k) * kThreads + threadIdx.x) * E - lead;
             const int64_t dst_off = dst0 + x;
             if (whole[k]) {
                 if constexpr (KS > 0) {
 #pragma unroll
-                    for (int r = 0; r < KS; ++r) store_group<T, NT>(static_cast<T*>(a.fulls.p[r]) + dst_off, v[k]);
+                    for (int r = 0; r < KS; ++r) st<NT>(reinterpret_cast<u32x4*>(static_cast<T*>(a.fulls.p[r]) + dst_off), v[k]);
                 } else {
-                    for (int r = 0; r < K; ++r) store_group<T, NT>(static_cast<T*>(a.fulls.p[r]) + dst_off, v[k]);
+                    for (int r = 0; r < K; ++r) st<NT>(reinterpret_cast<u32x4*>(static_cast<T*>(a.fulls.p[r]) + dst_off), v[k]);
                 }
-            } else if (x < len && x + kGroup > 0) {
+            } else if (x < len && x + E > 0) {
                 const int64_t e0 = x > 0 ? x : 0;
-                const int64_t e1 = x + kGroup < len ? x + kGroup : len;
+                const int64_t e1 = x + E < len ? x + E : len;
                 for (int64_t e = e0; e < e1; ++e) {
                     const T val = shard[e];
                     for (int r = 0; r < K; ++r) static_cast<T*>(a.fulls.p[r])[dst0 + e] = val;
@@ -181,13 +200,13 @@ __device__ __forceinline__ void ag_body(const AgCommon& a, const Tab& tab) {
 // tile t covers chunk offsets [t tile - lead_r, (t+1) tile - lead_r) of it.
 // The block stages the source elements every destination's tile t needs,
 // [t tile - 16 / sizeof(T) + 1, (t+1) tile) within the chunk, as the aligned
-// 16-byte blocks of the shard that hold them; a destination's whole group is
-// then two (bf16) or three (fp32) of those blocks shifted into place.
+// 16-byte blocks of the shard that hold them; a destination's whole unit is
+// then one of those blocks, or two shifted into place.
 template <typename T, bool NT, typename Tab>
 __device__ __forceinline__ void ag_body_any(const AgCommon& a, const Tab& tab) {
-    constexpr int SUB = kAgSub<T>;
+    constexpr int SUB = kAgSub;
+    constexpr int E = kAgUnit<T>;
     constexpr int64_t TILE = kAgTile<T>;
-    constexpr int kLeadMask = 16 / (int)sizeof(T) - 1;
     constexpr int kBlocks = (int)(TILE * sizeof(T) / 16) + 2;  // 16-byte blocks a tile's span can touch
     __shared__ u32x4 stage[kBlocks];
     const int K = a.K;
@@ -204,7 +223,7 @@ __device__ __forceinline__ void ag_body_any(const AgCommon& a, const Tab& tab) {
         const int64_t dst0 = sg.full_off + (int64_t)j * sg.C;
         int64_t len = sg.numel - (int64_t)j * sg.C;
         if (len > sg.C) len = sg.C;
-        int64_t xs = (int64_t)t * TILE - kLeadMask, xe = (int64_t)(t + 1) * TILE;
+        int64_t xs = (int64_t)t * TILE - (E - 1), xe = (int64_t)(t + 1) * TILE;
         xs = xs > 0 ? xs : 0;
         xe = xe < len ? xe : len;
         if (xs >= xe) continue;  // uniform: no element of this chunk in the tile
@@ -214,38 +233,26 @@ __device__ __forceinline__ void ag_body_any(const AgCommon& a, const Tab& tab) {
         __syncthreads();
         for (int r = 0; r < K; ++r) {
             T* full = static_cast<T*>(a.fulls.p[r]) + dst0;
-            const int64_t lead = (int64_t)(((uintptr_t)full / sizeof(T)) & kLeadMask);
+            const int64_t lead = (int64_t)(((uintptr_t)full / sizeof(T)) & (E - 1));
 #pragma unroll
             for (int k = 0; k < SUB; ++k) {
-                const int64_t x = ((int64_t)t * SUB + k) * kTile + (int64_t)threadIdx.x * kGroup - lead;
-                if (x >= 0 && x + kGroup <= len) {
-                    // [x, x + 8) lies in [xs, xe): its bytes are staged
+                const int64_t x = (((int64_t)t * SUB + k) * kThreads + threadIdx.x) * E - lead;
+                if (x >= 0 && x + E <= len) {
+                    // [x, x + E) lies in [xs, xe): its bytes are staged; a
+                    // block past the unit's last byte is never read (at the
+                    // span's end it lies beyond what was staged)
                     const uintptr_t off = (uintptr_t)(shard + x) - base;
                     const int blk = (int)(off / 16);
-                    const uint32_t sig = (uint32_t)(off & 15);  // uniform: lanes step by whole groups
-                    // blocks past the group's last byte are never read: at
-                    // the span's end they lie beyond what was staged
-                    Group<T> g;
-                    if constexpr (sizeof(T) == 2) {
-                        if (sig == 0)
-                            g.v = stage[blk];
-                        else
-                            g.v = shift16(stage[blk], stage[blk + 1], sig);
-                    } else {
-                        const u32x4 b0 = stage[blk], b1 = stage[blk + 1];
-                        if (sig == 0) {
-                            g.a = __builtin_bit_cast(f32x4, b0);
-                            g.b = __builtin_bit_cast(f32x4, b1);
-                        } else {
-                            const u32x4 b2 = stage[blk + 2];
-                            g.a = __builtin_bit_cast(f32x4, shift16(b0, b1, sig));
-                            g.b = __builtin_bit_cast(f32x4, shift16(b1, b2, sig));
-                        }
-                    }
-                    store_group<T, NT>(full + x, g);
-                } else if (x < len && x + kGroup > 0) {
+                    const uint32_t sig = (uint32_t)(off & 15);  // uniform: lanes step by whole units
+                    u32x4 v;
+                    if (sig == 0)
+                        v = stage[blk];
+                    else
+                        v = shift16(stage[blk], stage[blk + 1], sig);
+                    st<NT>(reinterpret_cast<u32x4*>(full + x), v);
+                } else if (x < len && x + E > 0) {
                     const int64_t e0 = x > 0 ? x : 0;
-                    const int64_t e1 = x + kGroup < len ? x + kGroup : len;
+                    const int64_t e1 = x + E < len ? x + E : len;
                     for (int64_t e = e0; e < e1; ++e) full[e] = shard[e];
                 }
             }

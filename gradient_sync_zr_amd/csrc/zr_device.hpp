@@ -1,6 +1,6 @@
-// Device helpers shared by the HIP kernels: the bf16 codec and 8-element
-// group loads/stores (one group = 16 bytes of bf16 or 32 bytes of fp32, the
-// unit one lane moves per rank).
+// Device helpers shared by the HIP kernels: the bf16 codec, streaming loads
+// and stores, the 16-byte realignment of copies between grids, quad loads and
+// stores, the tile searches and the average.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,9 +11,7 @@ namespace zr {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;          // threads per block (4 waves of 64)
-constexpr int kGroup = 8;              // elements per lane per rank
-constexpr int kTile = kThreads * kGroup;  // elements per block tile
+constexpr int kThreads = 256;  // threads per block (4 waves of 64)
 
 // bf16 <-> fp32. bf16 is the upper half of an IEEE binary32 word, so widening
 // appends 16 zero bits (exact). Narrowing rounds to nearest, ties to even;
@@ -42,41 +40,6 @@ __device__ __forceinline__ void st(V* p, V v) {
         *p = v;
 }
 
-// Raw registers of one 8-element group.
-template <typename T>
-struct Group;
-template <>
-struct Group<uint16_t> {
-    u32x4 v;
-};
-template <>
-struct Group<float> {
-    f32x4 a, b;
-};
-
-// p must be 16-byte aligned and hold 8 elements.
-template <typename T, bool NT>
-__device__ __forceinline__ Group<T> load_group(const T* p);
-
-template <>
-__device__ __forceinline__ Group<uint16_t> load_group<uint16_t, false>(const uint16_t* p) {
-    return {ld<false>(reinterpret_cast<const u32x4*>(p))};
-}
-template <>
-__device__ __forceinline__ Group<uint16_t> load_group<uint16_t, true>(const uint16_t* p) {
-    return {ld<true>(reinterpret_cast<const u32x4*>(p))};
-}
-template <>
-__device__ __forceinline__ Group<float> load_group<float, false>(const float* p) {
-    const f32x4* q = reinterpret_cast<const f32x4*>(p);
-    return {ld<false>(q), ld<false>(q + 1)};
-}
-template <>
-__device__ __forceinline__ Group<float> load_group<float, true>(const float* p) {
-    const f32x4* q = reinterpret_cast<const f32x4*>(p);
-    return {ld<true>(q), ld<true>(q + 1)};
-}
-
 // 16 bytes starting `sig` bytes into the 32 bytes lo:hi (sig in 1..15, a
 // multiple of the element size): each output dword joins two neighbouring
 // input dwords with one byte-align instruction.
@@ -97,95 +60,6 @@ __device__ __forceinline__ u32x4 shift16(const u32x4& lo, const u32x4& hi, uint3
     }
 #undef ZR_SHIFT16
     return r;
-}
-
-// The 8-element group at p, which need only be element aligned: one aligned
-// load per 16 bytes when p is 16-byte aligned, else the aligned 16-byte
-// blocks that hold the group's bytes (one more than the group spans), joined
-// in registers. Every block read holds at least one byte of the group, so no
-// read leaves the group's pages. The phase p & 15 must be uniform over the
-// wave (it selects the byte shift).
-template <typename T, bool NT>
-__device__ __forceinline__ Group<T> load_group_any(const T* p) {
-    const uintptr_t a = (uintptr_t)p;
-    const uint32_t sig = (uint32_t)(a & 15);
-    if (sig == 0) return load_group<T, NT>(p);
-    const u32x4* b = reinterpret_cast<const u32x4*>(a & ~(uintptr_t)15);
-    if constexpr (sizeof(T) == 2) {
-        return {shift16(ld<NT>(b), ld<NT>(b + 1), sig)};
-    } else {
-        const u32x4 b0 = ld<NT>(b), b1 = ld<NT>(b + 1), b2 = ld<NT>(b + 2);
-        return {__builtin_bit_cast(f32x4, shift16(b0, b1, sig)), __builtin_bit_cast(f32x4, shift16(b1, b2, sig))};
-    }
-}
-
-// Exact widening of a group to eight fp32 values.
-__device__ __forceinline__ void widen(const Group<uint16_t>& g, float f[8]) {
-    f[0] = __uint_as_float(g.v.x << 16);
-    f[1] = __uint_as_float(g.v.x & 0xFFFF0000u);
-    f[2] = __uint_as_float(g.v.y << 16);
-    f[3] = __uint_as_float(g.v.y & 0xFFFF0000u);
-    f[4] = __uint_as_float(g.v.z << 16);
-    f[5] = __uint_as_float(g.v.z & 0xFFFF0000u);
-    f[6] = __uint_as_float(g.v.w << 16);
-    f[7] = __uint_as_float(g.v.w & 0xFFFF0000u);
-}
-__device__ __forceinline__ void widen(const Group<float>& g, float f[8]) {
-    f[0] = g.a.x; f[1] = g.a.y; f[2] = g.a.z; f[3] = g.a.w;
-    f[4] = g.b.x; f[5] = g.b.y; f[6] = g.b.z; f[7] = g.b.w;
-}
-
-// acc[e] = acc[e] + widen(g)[e], one IEEE fp32 add per element.
-template <typename T>
-__device__ __forceinline__ void accumulate(float acc[8], const Group<T>& g) {
-    float f[8];
-    widen(g, f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = __fadd_rn(acc[e], f[e]);
-}
-
-// Pack eight fp32 results into a group of the output type (one RNE per
-// element for bf16).
-template <typename T>
-__device__ __forceinline__ Group<T> pack(const float f[8]);
-template <>
-__device__ __forceinline__ Group<uint16_t> pack<uint16_t>(const float f[8]) {
-    Group<uint16_t> g;
-    g.v.x = bf16_round(f[0]) | (bf16_round(f[1]) << 16);
-    g.v.y = bf16_round(f[2]) | (bf16_round(f[3]) << 16);
-    g.v.z = bf16_round(f[4]) | (bf16_round(f[5]) << 16);
-    g.v.w = bf16_round(f[6]) | (bf16_round(f[7]) << 16);
-    return g;
-}
-template <>
-__device__ __forceinline__ Group<float> pack<float>(const float f[8]) {
-    Group<float> g;
-    g.a = f32x4{f[0], f[1], f[2], f[3]};
-    g.b = f32x4{f[4], f[5], f[6], f[7]};
-    return g;
-}
-
-template <typename T, bool NT>
-__device__ __forceinline__ void store_group(T* p, const Group<T>& g);
-template <>
-__device__ __forceinline__ void store_group<uint16_t, false>(uint16_t* p, const Group<uint16_t>& g) {
-    st<false>(reinterpret_cast<u32x4*>(p), g.v);
-}
-template <>
-__device__ __forceinline__ void store_group<uint16_t, true>(uint16_t* p, const Group<uint16_t>& g) {
-    st<true>(reinterpret_cast<u32x4*>(p), g.v);
-}
-template <>
-__device__ __forceinline__ void store_group<float, false>(float* p, const Group<float>& g) {
-    f32x4* q = reinterpret_cast<f32x4*>(p);
-    st<false>(q, g.a);
-    st<false>(q + 1, g.b);
-}
-template <>
-__device__ __forceinline__ void store_group<float, true>(float* p, const Group<float>& g) {
-    f32x4* q = reinterpret_cast<f32x4*>(p);
-    st<true>(q, g.a);
-    st<true>(q + 1, g.b);
 }
 
 // Scalar element access for the unaligned / ragged paths.

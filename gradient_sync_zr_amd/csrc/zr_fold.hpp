@@ -79,6 +79,18 @@ template <int S>
 constexpr int64_t kRsTileOf = (int64_t)(kThreads / 64) * S * 256;
 template <typename TIn, typename TOut>
 constexpr int64_t kRsTile = kRsTileOf<kSlices<TIn, TOut>>;
+// Slices per wave of the generic-K kernels in the free and bf16-wire orders:
+// at most four (bf16 in and out would take eight, where those kernels needed
+// 236-256 VGPRs, ran one wave per SIMD and reached 2.4-4.5 TB/s).
+template <typename TIn, typename TOut>
+constexpr int kSlicesGeneric = kSlices<TIn, TOut> > 4 ? 4 : kSlices<TIn, TOut>;
+// Does a reduce-scatter launch at this K and fold order run those kernels?
+// (The free order always does; the wire order does with bf16 input and
+// K != 8, the one K it specialises.)
+template <typename TIn>
+__host__ __device__ constexpr bool rs_generic_narrow(int K, int order) {
+    return order == kFree || (order == kWire && sizeof(TIn) == 2 && K != 8);
+}
 
 // A wave owns S slices of 256 consecutive elements; lane l holds quad l of
 // each slice (elements 4l..4l+3), so every load and store instruction of the
@@ -116,13 +128,18 @@ __device__ __forceinline__ void fold_ring_quads_static(const RingBases<TIn, KS>&
 // is bound by.
 template <typename TIn, int S>
 constexpr int kRingBatch = (64 / (S * (int)sizeof(TIn))) > 8 ? 64 / (S * (int)sizeof(TIn)) : 8;
+// The wire order keeps four ranks per batch: its per-hop rounding needs
+// registers of its own, and with eight ranks the generic kernels ran at two
+// waves per SIMD and 4.7-4.9 TB/s, with four at three and 5.6-6.2 TB/s
+// (bf16 in, fp32 out).
+constexpr int kWireBatch = 4;
 
 // Ring order for any K: batches of kRingBatch ranks, every slice's loads of a
 // batch in flight together, batches folded in ring order one after the other.
 template <typename TIn, int KS, bool NT, int S, bool WIRE = false, typename PtrFn>
 __device__ __forceinline__ void fold_ring_quads(PtrFn ptr, int K, int j, int64_t g0,
                                                 float acc[S][4]) {
-    constexpr int B = kRingBatch<TIn, S>;
+    constexpr int B = WIRE ? kWireBatch : kRingBatch<TIn, S>;
     const int Kr = KS > 0 ? KS : K;
     for (int h0 = 0; h0 < Kr; h0 += B) {
         Quad<TIn> v[S][B];
@@ -154,18 +171,31 @@ __device__ __forceinline__ void fold_ring_quads(PtrFn ptr, int K, int j, int64_t
 }
 
 // Free order: ranks 0..K-1 in batches of eight, pairwise within a batch.
+// A batch's loads of every slice are in flight together before its trees
+// (loading and consuming one rank at a time waited on a memory round trip per
+// load: 2.3-5.3 TB/s with bf16 input, against 5.3-6.3 for the ring order).
 template <typename TIn, int KS, bool NT, int S, typename PtrFn>
 __device__ __forceinline__ void fold_free_quads(PtrFn ptr, int K, int64_t g0, float acc[S][4]) {
     constexpr int B = 8;
     const int Kr = KS > 0 ? KS : K;
     for (int h0 = 0; h0 < Kr; h0 += B) {
+        Quad<TIn> v[S][B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (h0 + b < Kr) {
+                const TIn* p = static_cast<const TIn*>(ptr(h0 + b));
+#pragma unroll
+                for (int k = 0; k < S; ++k) v[k][b] = load_quad<TIn, NT>(p + g0 + 256 * k);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < S; ++k) {
             float f[B][4];
 #pragma unroll
             for (int b = 0; b < B; ++b) {
                 if (h0 + b < Kr) {
-                    widen4(load_quad<TIn, NT>(static_cast<const TIn*>(ptr(h0 + b)) + g0 + 256 * k), f[b]);
+                    widen4(v[k][b], f[b]);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) f[b][e] = 0.0f;

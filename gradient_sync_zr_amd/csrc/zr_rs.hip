@@ -199,19 +199,22 @@ hipError_t launch_t(const RsArgs& a, hipStream_t stream) {
 
 // Orders: the free order has one generic instantiation; ring and wire orders
 // have K = 8 specialised, other K take the generic kernel (batches of eight
-// ranks in flight). With fp32 input the wire order is the ring order
-// (rounding every hop to fp32 is what the fp32 adds already do). Small
-// launches in the ring order use one slice per wave.
+// ranks in flight, four in the wire order). The free and generic wire
+// kernels keep at most four slices per wave (kSlicesGeneric). With fp32
+// input the wire order is the ring order (rounding every hop to fp32 is what
+// the fp32 adds already do). Small launches in the ring order use one slice
+// per wave.
 using LaunchFn = hipError_t (*)(const RsArgs&, hipStream_t);
 
 template <typename TIn, typename TOut, int AVG>
 LaunchFn pick_k(int K, int order, bool small) {
     constexpr int S = kSlices<TIn, TOut>;
+    constexpr int SG = kSlicesGeneric<TIn, TOut>;  // the tiles rs_generic_narrow() launches
     constexpr bool NT = kRsNontemporal;
-    if (order == kFree) return &launch_t<TIn, TOut, 0, AVG, kFree, NT, S>;
+    if (order == kFree) return &launch_t<TIn, TOut, 0, AVG, kFree, NT, SG>;
     if (order == kWire && sizeof(TIn) == 2) {
         if (K == 8) return &launch_t<TIn, TOut, 8, AVG, kWire, NT, S>;
-        return &launch_t<TIn, TOut, 0, AVG, kWire, NT, S>;
+        return &launch_t<TIn, TOut, 0, AVG, kWire, NT, SG>;
     }
     if (K == 8) return small ? &launch_t<TIn, TOut, 8, AVG, kRing, NT, 1> : &launch_t<TIn, TOut, 8, AVG, kRing, NT, S>;
     return small ? &launch_t<TIn, TOut, 0, AVG, kRing, NT, 1> : &launch_t<TIn, TOut, 0, AVG, kRing, NT, S>;
@@ -237,7 +240,8 @@ LaunchFn prepare_typed(RsArgs& a, int avg_mode, int order) {
     const int64_t k8 = (a.K + 7) / 8;
     const bool small = order == kRing && (fp == kPathSmall ||
                                           (fp != kPathLarge && ((a.C + T - 1) / T) * a.K < 2LL * k8 * device_cu_count()));
-    const int64_t Tl = small ? kRsTileOf<1> : T;
+    const int64_t Tl = small ? kRsTileOf<1>
+                             : (rs_generic_narrow<TIn>(a.K, order) ? kRsTileOf<kSlicesGeneric<TIn, TOut>> : T);
     // Vector path: every base aligned for quad access (8 bytes for bf16
     // quads, 16 for fp32 quads) and j*C a multiple of 4 elements, so that a
     // vector tile start j*C + head is a quad boundary on the input side and

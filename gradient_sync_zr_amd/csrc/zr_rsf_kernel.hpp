@@ -393,23 +393,26 @@ constexpr Fns fns() {
 }
 
 // Ring and wire order at K = 8 specialised, the rest generic (batches of
-// eight ranks in flight); fp32 input makes the wire order the ring order.
-// Small plans in the ring order use one slice per wave. Plans with segments
+// eight ranks in flight, four in the wire order; the free and generic wire
+// kernels keep at most four slices per wave); fp32 input makes the wire
+// order the ring order. Small plans in the ring order use one slice per wave. Plans with segments
 // whose ranks sit in different quad phases take the generic kernels built to
 // read them.
 template <typename TIn, typename TOut, int AVG>
 Fns pick_k(int K, int order, bool small, bool any) {
     constexpr int S = kSlices<TIn, TOut>;
+    constexpr int SG = kSlicesGeneric<TIn, TOut>;  // the tiles rs_generic_narrow() plans
     constexpr bool NT = kRsNontemporal;
     if (any) {
-        if (order == kFree) return fns<TIn, TOut, 0, AVG, kFree, NT, S, true>();
-        if (order == kWire && sizeof(TIn) == 2) return fns<TIn, TOut, 0, AVG, kWire, NT, S, true>();
+        if (order == kFree) return fns<TIn, TOut, 0, AVG, kFree, NT, SG, true>();
+        if (order == kWire && sizeof(TIn) == 2)
+            return K == 8 ? fns<TIn, TOut, 0, AVG, kWire, NT, S, true>() : fns<TIn, TOut, 0, AVG, kWire, NT, SG, true>();
         return small ? fns<TIn, TOut, 0, AVG, kRing, NT, 1, true>() : fns<TIn, TOut, 0, AVG, kRing, NT, S, true>();
     }
-    if (order == kFree) return fns<TIn, TOut, 0, AVG, kFree, NT, S>();
+    if (order == kFree) return fns<TIn, TOut, 0, AVG, kFree, NT, SG>();
     if (order == kWire && sizeof(TIn) == 2) {
         if (K == 8) return fns<TIn, TOut, 8, AVG, kWire, NT, S>();
-        return fns<TIn, TOut, 0, AVG, kWire, NT, S>();
+        return fns<TIn, TOut, 0, AVG, kWire, NT, SG>();
     }
     if (K == 8) return small ? fns<TIn, TOut, 8, AVG, kRing, NT, 1>() : fns<TIn, TOut, 8, AVG, kRing, NT, S>();
     return small ? fns<TIn, TOut, 0, AVG, kRing, NT, 1>() : fns<TIn, TOut, 0, AVG, kRing, NT, S>();
