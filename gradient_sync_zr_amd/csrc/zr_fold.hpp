@@ -79,9 +79,11 @@ template <int S>
 constexpr int64_t kRsTileOf = (int64_t)(kThreads / 64) * S * 256;
 template <typename TIn, typename TOut>
 constexpr int64_t kRsTile = kRsTileOf<kSlices<TIn, TOut>>;
-// Slices per wave of the generic-K kernels in the free and bf16-wire orders:
-// at most four (bf16 in and out would take eight, where those kernels needed
-// 236-256 VGPRs, ran one wave per SIMD and reached 2.4-4.5 TB/s).
+// Slices per wave of the generic-K kernels in the free and bf16-wire orders,
+// and of the discrete kernels for ranks in different phases: at most four
+// (bf16 in and out would take eight, where the generic kernels needed
+// 236-256 VGPRs, ran one wave per SIMD and reached 2.4-4.5 TB/s, and the
+// different-phase kernels ran 4-17% slower at K <= 16).
 template <typename TIn, typename TOut>
 constexpr int kSlicesGeneric = kSlices<TIn, TOut> > 4 ? 4 : kSlices<TIn, TOut>;
 // Does a reduce-scatter launch at this K and fold order run those kernels?

@@ -234,14 +234,16 @@ RsfPlan* rsf_plan_build(int K, const FragEntry* entries, int n_entries, int64_t 
         // fewer than two full tiles per CU for each eight ranks: one-slice tiles
         const int64_t k8 = (K + 7) / 8;
         const bool small = ord == kRing && (fp == kPathSmall || (fp != kPathLarge && most < 2LL * k8 * device_cu_count()));
-        // the free and generic wire kernels' tiles may hold fewer slices
-        const int64_t tile = small ? kRsTileOf<1>
-                                   : (rs_generic_narrow<TIn>(K, ord) ? kRsTileOf<kSlicesGeneric<TIn, TOut>>
-                                                                     : kRsTile<TIn, TOut>);
-        const bool retile = tile != kRsTile<TIn, TOut>;
-        if (retile) segments_of<TIn, TOut>(c, entries, n_entries, tile, &segs, &first);
+        // ranks in different phases (a flag of the heads, whatever the tile)
         bool any = false;
         for (const SegDesc& d : segs) any = any || (d.head >= 0 && (d.head & kAnyPhase) != 0);
+        // the free and generic wire kernels' tiles, and those of the kernels
+        // for ranks in different phases, may hold fewer slices
+        const bool narrow = any || rs_generic_narrow<TIn>(K, ord);
+        const int64_t tile = small ? kRsTileOf<1>
+                                   : (narrow ? kRsTileOf<kSlicesGeneric<TIn, TOut>> : kRsTile<TIn, TOut>);
+        const bool retile = tile != kRsTile<TIn, TOut>;
+        if (retile) segments_of<TIn, TOut>(c, entries, n_entries, tile, &segs, &first);
         if (plan->staged) {
             plan->launches.clear();
             build_image(c, entries, n_entries, segs, (uintptr_t)ws, &plan->wsa, &plan->ws_tiles, &plan->image);

@@ -403,11 +403,10 @@ Fns pick_k(int K, int order, bool small, bool any) {
     constexpr int S = kSlices<TIn, TOut>;
     constexpr int SG = kSlicesGeneric<TIn, TOut>;  // the tiles rs_generic_narrow() plans
     constexpr bool NT = kRsNontemporal;
-    if (any) {
+    if (any) {  // at most four slices per wave in every order (the planner's tiles)
         if (order == kFree) return fns<TIn, TOut, 0, AVG, kFree, NT, SG, true>();
-        if (order == kWire && sizeof(TIn) == 2)
-            return K == 8 ? fns<TIn, TOut, 0, AVG, kWire, NT, S, true>() : fns<TIn, TOut, 0, AVG, kWire, NT, SG, true>();
-        return small ? fns<TIn, TOut, 0, AVG, kRing, NT, 1, true>() : fns<TIn, TOut, 0, AVG, kRing, NT, S, true>();
+        if (order == kWire && sizeof(TIn) == 2) return fns<TIn, TOut, 0, AVG, kWire, NT, SG, true>();
+        return small ? fns<TIn, TOut, 0, AVG, kRing, NT, 1, true>() : fns<TIn, TOut, 0, AVG, kRing, NT, SG, true>();
     }
     if (order == kFree) return fns<TIn, TOut, 0, AVG, kFree, NT, SG>();
     if (order == kWire && sizeof(TIn) == 2) {
