@@ -45,7 +45,7 @@ namespace {
 
 struct AgSeg {
     int64_t shard_off, full_off, numel, C;
-    uint64_t vec_mask;  // bit j: chunk j moves whole groups with 16-byte accesses
+    uint64_t vec_mask;  // bit j: chunk j moves whole units with 16-byte accesses
     int tiles_per_chunk;
     int pad_;
 };
@@ -195,7 +195,7 @@ __device__ __forceinline__ void ag_body(const AgCommon& a, const Tab& tab) {
 }
 
 // The same tiles when the full buffers sit in different 16-byte phases.
-// Destination r's groups start on its own grid, lead_r = (its chunk start's
+// Destination r's units start on its own grid, lead_r = (its chunk start's
 // element index) mod 16 / sizeof(T) elements before the chunk's offsets, so
 // tile t covers chunk offsets [t tile - lead_r, (t+1) tile - lead_r) of it.
 // The block stages the source elements every destination's tile t needs,
@@ -314,7 +314,7 @@ int64_t describe(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype 
                  int n_segs, AgSeg* out, int64_t* unit0, int* used, int* fphase, bool* any) {
     const int es = dt == ZR_BF16 ? 2 : 4;
     const int64_t tile = dt == ZR_BF16 ? kAgTile<uint16_t> : kAgTile<float>;  // elements per tile
-    // whole groups from registers need one destination grid for all K full
+    // whole units from registers need one destination grid for all K full
     // buffers (their bases in one phase within 16 bytes); a chunk's source is
     // one shard, so the shards may sit anywhere. Full buffers in different
     // phases stage the source in LDS, and their tiles cover up to
@@ -338,8 +338,8 @@ int64_t describe(int K, const ConstPtrs& shards, const MutPtrs& fulls, zr_dtype 
         d.numel = segs[s].numel;
         d.C = (d.numel + K - 1) / K;
         d.pad_ = 0;
-        // with 16-byte aligned bases every chunk moves whole groups, on its
-        // destination's grid: its groups start up to 16 / es - 1 elements
+        // with 16-byte aligned bases every chunk moves whole units, on its
+        // destination's grid: its units start up to 16 / es - 1 elements
         // before the chunk (the lead), which its tiles must also cover
         d.vec_mask = 0;
         int64_t lead = *any ? 16 / es - 1 : 0;
