@@ -157,6 +157,11 @@ WIRE_CASES = [
     (8, 65536 + 5, False, 0, True, 1),          # bases off the quad grid
     (5, 77777, False, 2, True, 0),
     (64, 64 * 4096 + 3, True, 1, False, 0),
+    # full tiles of the generic wire kernels (four ranks per batch; bf16
+    # output on four-slice tiles)
+    (3, 3 * 400001, True, 1, True, 0),
+    (16, 16 * 150000 + 5, True, 1, True, 0),
+    (16, 16 * 150000 + 5, False, 2, False, 0),
 ]
 
 
@@ -205,7 +210,10 @@ def test_allreduce_bf16_wire_bit_exact(K, N, fused, average):
 
 @pytest.mark.parametrize("K,N,in_bf16,out_bf16,average", [
     (8, 100003, True, False, True), (64, 70001, True, True, False), (5, 30000, False, False, True),
-    (16, 16 * 2048 * 2, True, False, True)])
+    (16, 16 * 2048 * 2, True, False, True),
+    # full tiles: bf16 -> bf16 takes four-slice tiles in the free order
+    (8, 8 * 300000 + 13, True, True, True), (2, 2 * 500000 + 1, True, True, False),
+    (3, 3 * 200001, True, False, True), (64, 64 * 20000 + 5, False, True, True)])
 def test_reduce_scatter_free_order_within_tolerance(K, N, in_bf16, out_bf16, average):
     import torch
     xs = make_inputs(K, N, in_bf16, 77 + K)
@@ -329,10 +337,10 @@ def test_allreduce_fused_equals_rs_then_ag(K, N, bf16):
         assert np.array_equal(bits(a[r].get()), bits(ref))   # identical on every rank
 
 
-def test_allreduce_free_order_tolerance_and_identical_ranks():
+@pytest.mark.parametrize("K,N", [(64, 64 * 2048 + 999), (8, 8 * 8192 * 20 + 3), (3, 3 * 8192 * 9 + 1)])
+def test_allreduce_free_order_tolerance_and_identical_ranks(K, N):
     import torch
-    K, N = 64, 64 * 2048 + 999
-    xs = make_inputs(K, N, True, 31337)
+    xs = make_inputs(K, N, True, 31337 + K)
     ins = [Guarded(N, torch.bfloat16, 0, xs[r]) for r in range(K)]
     zr().zr_allreduce([g.ptr() for g in ins], [g.ptr() for g in ins], N,
                       order=zr().ZR_ORDER_FREE, dtype=torch.bfloat16)
@@ -356,6 +364,9 @@ AG_CASES = [
     (64, [64 * 2048 + 5, 640, 63], 0, True, 0, 0),
     (1, [12345], 0, True, 0, 0),
     (5, [0, 4, 0, 99999], 3, True, 1, 2),
+    # fp32 over several 4096-element tiles per chunk, odd sizes (16-byte units of 4 elements)
+    (8, [8 * 4096 * 3 + 5, 77, 8 * 1024 + 1], 1, False, 0, 1),
+    (16, [16 * 4096 * 2 + 3, 16 * 4096], 5, False, 3, 2),
 ]
 
 
