@@ -9,7 +9,9 @@ input byte offsets both pass 32 bits inside one call. The checks are:
     identical to rank 0 on every element;
   - the all-gather: every element of every rank's full buffer equal to the unsharded tensor. A second
     segment starts past 2^31 in the full buffers;
-  - the flatten: every element of every bucket equal to its fragment, and zero padding after them.
+  - the flatten: every element of every bucket equal to its fragment, and zero padding after them;
+  - ranks whose views sit in different phases: the reduce-scatter and the fused all-reduce, sampled
+    as above.
 """
 import gc
 import sys
@@ -221,3 +223,55 @@ def test_flatten_past_2e31():
             off += n
         assert bool((buckets[r][total:].view(torch.int16) == 0).all()), f"rank {r} padding"
     say("large flatten: every bucket element equals its fragment; padding zero")
+
+
+def test_ranks_in_mixed_phases_past_2e31():
+    # rank r's views start r mod 4 elements into their allocations: the reduce-scatter (through
+    # the discrete path's aligned-pair folds) and the fused all-reduce (aligned pairs and LDS-staged
+    # stores) past 2^31 elements per rank, sampled against the oracle
+    import torch
+    K, N, shift = 4, BIG, 1
+    C = -(-N // K)
+    say(f"large mixed phases: K={K} N={N}")
+    base = [torch.empty(N + 4, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    xs = [base[r][r % 4:r % 4 + N] for r in range(K)]
+    for r in range(K):
+        synth.dev_normal_bf16(xs[r], SEED + 5, r, 0, 1.0, 0.01, 1e4)
+    obase = [torch.empty(C + 4, dtype=torch.float32, device="cuda") for _ in range(K)]
+    outs = [obase[r][(r + 1) % 4:(r + 1) % 4 + C] for r in range(K)]
+    for o in outs:
+        o.view(torch.int32).fill_(-1)
+    zr().zr_reduce_scatter_avg([x.data_ptr() for x in xs], N, [o.data_ptr() for o in outs],
+                               chunk_shift=shift, average=True, in_dtype=torch.bfloat16,
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert not bool(torch.isnan(o).any())
+    rng = np.random.default_rng(35)
+
+    def value_at(r, g):
+        return synth.host_points_normal_bf16(SEED + 5, np.full(g.size, r), g, 1.0, 0.01, 1e4)
+
+    offs, want, M = sampled_rs_want(K, N, C, value_at, rng, shift, True)
+    for q in range(K):
+        j = (q + shift) % K
+        got = outs[q].index_select(0, torch.from_numpy(offs[j]).cuda()).cpu().numpy()
+        assert np.array_equal(bits(got), bits(want[q][:M])), f"rs rank {q}"
+    say("large mixed phases: reduce-scatter sampled outputs bit-exact")
+    del obase, outs
+    gc.collect()
+    torch.cuda.empty_cache()
+    # the fused all-reduce in place on the same views (sum, no average)
+    zr().zr_allreduce([x.data_ptr() for x in xs], [x.data_ptr() for x in xs], N, average=False,
+                      dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for r in range(1, K):
+        assert torch.equal(xs[r].view(torch.int16), xs[0].view(torch.int16)), f"ar rank {r}"
+    g = np.unique(np.concatenate([
+        rng.integers(0, N, 20000), np.arange(N - 16, N), np.arange((1 << 31) - 64, (1 << 31) + 64),
+        np.concatenate([np.arange(j * C - 4, j * C + 4) for j in range(1, K)])])).astype(np.int64)
+    pts = np.stack([value_at(r, g) for r in range(K)])
+    want_ar = oracle.f32_to_bf16(oracle.fold_points(oracle.bf16_to_f32(pts), g // C))
+    got = xs[0].view(torch.int16).index_select(0, torch.from_numpy(g).cuda()).cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), want_ar)
+    say("large mixed phases: all-reduce sampled outputs bit-exact, all ranks identical")
