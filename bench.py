@@ -178,6 +178,27 @@ def bench_zero2(args, accumulate=False):
     step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     step_bytes = sum(n * per_elem for _, n in buckets)
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    # the same steps with the reductions on the caller's own stream (the
+    # library's default, for a sync with no compute to overlap): the
+    # scheduler then enqueues no cross-stream waits
+    sync1 = Zero2GradSync(grads, parts, bucket, chunk_shift=cfg["shift"], average=True)
+    for _ in range(2):
+        sync1.step(micro_step=micro)
+    torch.cuda.synchronize()
+    marks1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    u0 = time.perf_counter()
+    marks1[0].record(prod)
+    for i in range(args.steps):
+        sync1.step(micro_step=micro)
+        marks1[i + 1].record(prod)
+    torch.cuda.synchronize()
+    u1 = time.perf_counter()
+    sync1.close()
+    ms_step1 = (u1 - u0) * 1e3 / args.steps
+    step_ms1 = sorted(marks1[i].elapsed_time(marks1[i + 1]) for i in range(args.steps))
+    one_stream = {"ms_per_step": round(ms_step1, 4), "step_ms_median": round(step_ms1[len(step_ms1) // 2], 4),
+                  "step_ms_min": round(step_ms1[0], 4),
+                  "GBps": round(step_bytes / (ms_step1 * 1e-3) / 1e9, 1)}
     # a separate instrumented pass of as many steps: an event pair around each
     # launch on the reduction stream, after the stream has waited for the
     # producer, so each pair brackets the kernel alone
@@ -228,6 +249,7 @@ def bench_zero2(args, accumulate=False):
         "step_ms_median": round(step_ms[len(step_ms) // 2], 4),
         "step_ms_min": round(step_ms[0], 4),
         "value_at_median_step_GBps": round(step_bytes / (step_ms[len(step_ms) // 2] * 1e-3) / 1e9, 1),
+        "one_stream": one_stream,
         "reads_only_GBps": round(K * N * 2 / (ms_step * 1e-3) / 1e9, 1),
         "config": {"workload": "zero2_grad_sync: K=8 simulated ranks in one HBM, "
                                "2,376,274,560 bf16 grad elements per rank, 5 buckets of "

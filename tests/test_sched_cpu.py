@@ -68,6 +68,8 @@ class Program:
         self.seen = 0
         self.version = {}   # event id -> latest version (id, n)
         self.work = []      # (label, stream, index in that stream)
+        self.waits = []     # (stream, event) of every wait the scheduler enqueued
+        self.records = []   # (event, stream) of every record
 
     def close(self):
         lib().sim_destroy(self.h)
@@ -83,10 +85,12 @@ class Program:
         for i in range(self.seen, n, 3):
             op, a, b = (int(x) for x in buf[i:i + 3])
             if op == RECORD:
+                self.records.append((a, b))
                 v = self.version.get(a, 0) + 1
                 self.version[a] = v
                 self._q(b).append(("record", (a, v)))
             elif op == WAIT:
+                self.waits.append((a, b))
                 v = self.version.get(b, 0)
                 if v:
                     self._q(a).append(("wait", (b, v)))
@@ -286,3 +290,84 @@ def test_flush_without_submit_is_noop_and_single_buffer_serializes():
     w = p.spans_of("write0")
     r = p.spans_of("reduce0")
     assert w[1][0] >= r[0][1] and w[2][0] >= r[1][1]
+
+
+def check_reuse_ordered(p):
+    """Every write of a buffer starts after that buffer's previous reduction
+    ended, and every reduction starts after its bucket's write ended."""
+    sp = p.replay()
+    for b in (0, 1):
+        w = [sp[(s, i)] for (lab, s, i) in p.work if lab == f"write{b}"]
+        r = [sp[(s, i)] for (lab, s, i) in p.work if lab == f"reduce{b}"]
+        for k in range(len(r)):
+            assert r[k][0] >= w[k][1]
+            if k + 1 < len(w):
+                assert w[k + 1][0] >= r[k][1]
+
+
+def test_waits_implied_by_a_flush_are_not_enqueued():
+    # steps of five buckets over two buffers, each ended by a flush into the
+    # producer stream: the first acquires of the next step are already ordered
+    # after every reduction (the producer waited on the tail), so they enqueue
+    # no wait; every other acquire still waits, and no write races a reduction
+    p = Program()
+    prod = 1
+    per_step = []
+    for step in range(3):
+        before = len([w for w in p.waits if w[0] == prod])
+        for i in range(5):
+            b = i % 2
+            assert p.acquire(b, prod) == OK
+            p.write(prod, b)
+            assert p.submit(b, [prod]) == OK
+        assert p.flush(prod) == OK
+        per_step.append(len([w for w in p.waits if w[0] == prod]) - before)
+    check_reuse_ordered(p)
+    # step 0: acquires of buckets 2, 3, 4 wait (buffers reused), plus the flush;
+    # later steps: buckets 0 and 1 reuse buffers the flush already covered
+    assert per_step == [4, 4, 4]
+    first = Program()
+    for i in range(5):
+        first.acquire(i % 2, prod)
+        first.write(prod, i % 2)
+        first.submit(i % 2, [prod])
+    first.flush(prod)
+    n0 = len(first.waits)
+    first.acquire(0, prod)
+    first.acquire(1, prod)
+    assert len(first.waits) == n0   # covered by the flush: nothing enqueued
+    first.close()
+    p.close()
+
+
+def test_a_flush_into_another_stream_does_not_cover_the_producer():
+    p = Program()
+    for i in range(2):
+        p.acquire(i, 1)
+        p.write(1, i)
+        p.submit(i, [1])
+    p.flush(3)                      # the caller is stream 3, not the producer
+    n = len(p.waits)
+    p.acquire(0, 1)
+    assert len(p.waits) == n + 1 and p.waits[-1][0] == 1
+    p.write(1, 0)
+    p.submit(0, [1])
+    check_reuse_ordered(p)
+    p.close()
+
+
+def test_producer_on_the_reduction_stream_needs_no_events():
+    # reductions on the caller's own stream: stream order covers every
+    # dependency, so only the buffers' completion events are recorded
+    p = Program()
+    for i in range(6):
+        b = i % 2
+        assert p.acquire(b, RED) == OK
+        p.write(RED, b)
+        assert p.submit(b, [RED]) == OK
+    assert p.flush(RED) == OK
+    assert p.waits == []
+    done_events = {e for (e, s) in p.records}
+    assert all(s == RED for (_, s) in p.records) and len(done_events) == 2
+    check_reuse_ordered(p)
+    p.close()
