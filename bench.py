@@ -150,58 +150,56 @@ def bench_zero2(args, accumulate=False):
     buckets = W.zero2_buckets(N, bucket)
     P = sum(-(-n // K) for _, n in buckets)
     parts = [torch.empty(P, dtype=torch.float32, device="cuda") for _ in range(K)]
-    red = torch.cuda.Stream()
-    sync = Zero2GradSync(grads, parts, bucket, chunk_shift=cfg["shift"], average=True,
-                         reduction_stream=red)
+    # the headline: the reductions on the caller's own stream, the library's
+    # default for a sync with no compute to overlap (the scheduler then
+    # enqueues no cross-stream waits)
+    sync = Zero2GradSync(grads, parts, bucket, chunk_shift=cfg["shift"], average=True)
     torch.cuda.synchronize()
     print(f"# zero2: K={K} N={N} buckets={len(buckets)} inputs resident", file=sys.stderr, flush=True)
     # an accumulation micro-step also reads the fp32 partition back
     per_elem = 2 * K + (8 if accumulate else 4)
     micro = 1 if accumulate else 0
-    sync.step()
-    for _ in range(args.warmup):
-        sync.step(micro_step=micro)
-    torch.cuda.synchronize()
-    # the timed steps: nothing but the sync itself; one event per step boundary
-    # on the producer stream (each step ends with the producer waiting for the
-    # reduction stream) gives every step's device time for the median and min
-    prod = torch.cuda.current_stream()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    t0 = time.perf_counter()
-    marks[0].record(prod)
-    for i in range(args.steps):
-        sync.step(micro_step=micro)
-        marks[i + 1].record(prod)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     step_bytes = sum(n * per_elem for _, n in buckets)
+    prod = torch.cuda.current_stream()
+
+    def timed_steps(s):
+        """W untimed steps, then K timed ones with nothing but the sync in
+        them; one event per step boundary on the caller's stream (each step
+        ends with that stream ordered after the step's reductions) gives
+        every step's device time for the median and minimum."""
+        s.step()
+        for _ in range(args.warmup):
+            s.step(micro_step=micro)
+        torch.cuda.synchronize()
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        t0 = time.perf_counter()
+        marks[0].record(prod)
+        for i in range(args.steps):
+            s.step(micro_step=micro)
+            marks[i + 1].record(prod)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return (t1 - t0) * 1e3 / args.steps, sorted(marks[i].elapsed_time(marks[i + 1])
+                                                     for i in range(args.steps))
+
+    ms_step, step_ms = timed_steps(sync)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    # the same steps with the reductions on the caller's own stream (the
-    # library's default, for a sync with no compute to overlap): the
-    # scheduler then enqueues no cross-stream waits
-    sync1 = Zero2GradSync(grads, parts, bucket, chunk_shift=cfg["shift"], average=True)
-    for _ in range(2):
-        sync1.step(micro_step=micro)
-    torch.cuda.synchronize()
-    marks1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    u0 = time.perf_counter()
-    marks1[0].record(prod)
-    for i in range(args.steps):
-        sync1.step(micro_step=micro)
-        marks1[i + 1].record(prod)
-    torch.cuda.synchronize()
-    u1 = time.perf_counter()
-    sync1.close()
-    ms_step1 = (u1 - u0) * 1e3 / args.steps
-    step_ms1 = sorted(marks1[i].elapsed_time(marks1[i + 1]) for i in range(args.steps))
-    one_stream = {"ms_per_step": round(ms_step1, 4), "step_ms_median": round(step_ms1[len(step_ms1) // 2], 4),
-                  "step_ms_min": round(step_ms1[0], 4),
-                  "GBps": round(step_bytes / (ms_step1 * 1e-3) / 1e9, 1)}
+    # the same steps with the reductions on a stream of their own, as a
+    # training step that overlaps them with the backward pass runs them: each
+    # bucket waits on the caller's stream and each step ends with the caller
+    # waiting on the reduction stream
+    red = torch.cuda.Stream()
+    sync2 = Zero2GradSync(grads, parts, bucket, chunk_shift=cfg["shift"], average=True,
+                          reduction_stream=red)
+    ms_step2, step_ms2 = timed_steps(sync2)
+    sync2.close()
+    reduction_stream = {"ms_per_step": round(ms_step2, 4),
+                        "step_ms_median": round(step_ms2[len(step_ms2) // 2], 4),
+                        "step_ms_min": round(step_ms2[0], 4),
+                        "GBps": round(step_bytes / (ms_step2 * 1e-3) / 1e9, 1)}
     # a separate instrumented pass of as many steps: an event pair around each
-    # launch on the reduction stream, after the stream has waited for the
-    # producer, so each pair brackets the kernel alone
+    # launch, after its stream has been ordered after the producer, so each
+    # pair brackets the kernel alone
     timing = []
     for _ in range(args.steps):
         sync.step(timing=timing, micro_step=micro)
@@ -249,7 +247,7 @@ def bench_zero2(args, accumulate=False):
         "step_ms_median": round(step_ms[len(step_ms) // 2], 4),
         "step_ms_min": round(step_ms[0], 4),
         "value_at_median_step_GBps": round(step_bytes / (step_ms[len(step_ms) // 2] * 1e-3) / 1e9, 1),
-        "one_stream": one_stream,
+        "reduction_stream": reduction_stream,
         "reads_only_GBps": round(K * N * 2 / (ms_step * 1e-3) / 1e9, 1),
         "config": {"workload": "zero2_grad_sync: K=8 simulated ranks in one HBM, "
                                "2,376,274,560 bf16 grad elements per rank, 5 buckets of "
