@@ -193,23 +193,34 @@ __device__ __forceinline__ void fold_free_quads(PtrFn ptr, int K, int64_t g0, fl
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < S; ++k) {
-            float f[B][4];
+            // the tree's first level straight from the loaded pairs (pair p
+            // sums ranks h0 + 2p and h0 + 2p + 1), so only half the batch is
+            // held widened: the generic kernel then fits three waves per SIMD
+            float f[B / 2][4];
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                if (h0 + b < Kr) {
-                    widen4(v[k][b], f[b]);
+            for (int q = 0; q < B / 2; ++q) {
+                if (h0 + 2 * q < Kr) {
+                    widen4(v[k][2 * q], f[q]);
+                    if (h0 + 2 * q + 1 < Kr) {
+                        float t[4];
+                        widen4(v[k][2 * q + 1], t);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) f[q][e] = __fadd_rn(f[q][e], t[e]);
+                    }
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) f[b][e] = 0.0f;
+                    for (int e = 0; e < 4; ++e) f[q][e] = 0.0f;
                 }
             }
+            // the levels above: pair q holds the sum over ranks h0 + 2q ..
+            // h0 + 2q + 1; level s adds the pair s further on, if present
 #pragma unroll
-            for (int s = 1; s < B; s *= 2)
+            for (int s = 1; s < B / 2; s *= 2)
 #pragma unroll
-                for (int b = 0; b + s < B; b += 2 * s)
-                    if (h0 + b + s < Kr)
+                for (int q = 0; q + s < B / 2; q += 2 * s)
+                    if (h0 + 2 * (q + s) < Kr)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) f[b][e] = __fadd_rn(f[b][e], f[b + s][e]);
+                        for (int e = 0; e < 4; ++e) f[q][e] = __fadd_rn(f[q][e], f[q + s][e]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[k][e] = (h0 == 0) ? f[0][e] : __fadd_rn(acc[k][e], f[0][e]);
         }

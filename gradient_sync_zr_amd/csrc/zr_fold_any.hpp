@@ -140,23 +140,31 @@ __device__ __forceinline__ void fold_free_quads_any(PtrFn ptr, int K, int64_t g0
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 0; k < SG; ++k) {
-                float f[B][4];
+                // as in fold_free_quads: the first level straight from the
+                // loaded pairs, the levels above over the pairs' sums
+                float f[B / 2][4];
 #pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    if (h0 + b < Kr) {
-                        widen4(join_quad(lo[k][b], hi[k][b], sig[b]), f[b]);
+                for (int q = 0; q < B / 2; ++q) {
+                    if (h0 + 2 * q < Kr) {
+                        widen4(join_quad(lo[k][2 * q], hi[k][2 * q], sig[2 * q]), f[q]);
+                        if (h0 + 2 * q + 1 < Kr) {
+                            float t[4];
+                            widen4(join_quad(lo[k][2 * q + 1], hi[k][2 * q + 1], sig[2 * q + 1]), t);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) f[q][e] = __fadd_rn(f[q][e], t[e]);
+                        }
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) f[b][e] = 0.0f;
+                        for (int e = 0; e < 4; ++e) f[q][e] = 0.0f;
                     }
                 }
 #pragma unroll
-                for (int st = 1; st < B; st *= 2)
+                for (int st = 1; st < B / 2; st *= 2)
 #pragma unroll
-                    for (int b = 0; b + st < B; b += 2 * st)
-                        if (h0 + b + st < Kr)
+                    for (int q = 0; q + st < B / 2; q += 2 * st)
+                        if (h0 + 2 * (q + st) < Kr)
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) f[b][e] = __fadd_rn(f[b][e], f[b + st][e]);
+                            for (int e = 0; e < 4; ++e) f[q][e] = __fadd_rn(f[q][e], f[q + st][e]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[k0 + k][e] = (h0 == 0) ? f[0][e] : __fadd_rn(acc[k0 + k][e], f[0][e]);
             }
