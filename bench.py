@@ -162,12 +162,16 @@ def bench_zero2(args, accumulate=False):
     step_bytes = sum(n * per_elem for _, n in buckets)
     prod = torch.cuda.current_stream()
 
-    def timed_steps(s):
+    def timed_steps(s, first):
         """W untimed steps, then K timed ones with nothing but the sync in
         them; one event per step boundary on the caller's stream (each step
         ends with that stream ordered after the step's reductions) gives
-        every step's device time for the median and minimum."""
-        s.step()
+        every step's device time for the median and minimum. The first
+        sync's first step writes the partitions (micro-step 0), so that an
+        accumulating run adds to defined values; every later launch is of
+        the timed kind."""
+        if first:
+            s.step()
         for _ in range(args.warmup):
             s.step(micro_step=micro)
         torch.cuda.synchronize()
@@ -182,7 +186,7 @@ def bench_zero2(args, accumulate=False):
         return (t1 - t0) * 1e3 / args.steps, sorted(marks[i].elapsed_time(marks[i + 1])
                                                      for i in range(args.steps))
 
-    ms_step, step_ms = timed_steps(sync)
+    ms_step, step_ms = timed_steps(sync, True)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     # the same steps with the reductions on a stream of their own, as a
     # training step that overlaps them with the backward pass runs them: each
@@ -191,7 +195,7 @@ def bench_zero2(args, accumulate=False):
     red = torch.cuda.Stream()
     sync2 = Zero2GradSync(grads, parts, bucket, chunk_shift=cfg["shift"], average=True,
                           reduction_stream=red)
-    ms_step2, step_ms2 = timed_steps(sync2)
+    ms_step2, step_ms2 = timed_steps(sync2, False)
     sync2.close()
     reduction_stream = {"ms_per_step": round(ms_step2, 4),
                         "step_ms_median": round(step_ms2[len(step_ms2) // 2], 4),
