@@ -119,17 +119,18 @@ def copy_ceiling_gbps(gib=4, reps=10):
     return round(2 * nbytes / (sum(ms) / len(ms) * 1e-3) / 1e9, 1)
 
 
-def mix_ceiling(reps=10, modes=("mix", "reads", "writes")):
+def mix_ceiling(reps=10, modes=("mix", "reads", "writes"), slices=4):
     """The test kit's matched-mix stream (tests/kit/mix_probe.py: the
-    reduce-scatter's loads and stores at one bucket's shape, no arithmetic),
-    measured now: the rates of the requested modes ("mix", "reads", "writes",
-    "accum"), or None when the kit is not built."""
+    reduce-scatter's loads and stores at one bucket's shape, no arithmetic,
+    in tiles of `slices` slices per wave), measured now: the rates of the
+    requested modes ("mix", "reads", "writes", "accum"), or None when the kit
+    is not built."""
     import importlib.util
     spec = importlib.util.spec_from_file_location("mix_probe", os.path.join(ROOT, "tests", "kit",
                                                                             "mix_probe.py"))
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
-    return mod.measure(reps=reps, modes=modes)
+    return mod.measure(reps=reps, modes=modes, slices=slices)
 
 
 # ----------------------------------------------------------------- zero2
@@ -234,7 +235,10 @@ def bench_zero2(args, accumulate=False):
     sync.close()
     del sync, grads, parts
     copy = copy_ceiling_gbps()
-    mix = mix_ceiling(modes=("accum",) if accumulate else ("mix", "reads", "writes"))
+    # the kernel's own tile shape: one slice per wave for the plain sync,
+    # four when the partitions are read back
+    mix_slices = 4 if accumulate else 1
+    mix = mix_ceiling(modes=("accum",) if accumulate else ("mix", "reads", "writes"), slices=mix_slices)
     mix_key = "accum" if accumulate else "mix"
     if accumulate:
         metric = ("reduce-scatter+avg+accumulate GB/s (gradient-accumulation micro-step), K=8, "
@@ -272,6 +276,7 @@ def bench_zero2(args, accumulate=False):
                      "copy_ceiling_GBps": copy,
                      "of_copy_ceiling": round(achieved / copy, 4) if copy else None,
                      "mix_ceiling_GBps": mix[mix_key]["GBps"] if mix else None,
+                     "mix_tile_slices": mix_slices,
                      "of_mix_ceiling": round(achieved / mix[mix_key]["GBps"], 4) if mix else None,
                      "mix_reads_only_GBps": mix["reads"]["GBps"] if mix and "reads" in mix else None,
                      "mix_writes_only_GBps": mix["writes"]["GBps"] if mix and "writes" in mix else None,

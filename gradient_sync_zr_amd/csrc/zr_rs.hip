@@ -231,15 +231,30 @@ LaunchFn pick_avg(int K, int avg_mode, int order, bool small) {
 
 // Fills the launch geometry of `a` (vector chunks, heads, tiles per chunk and
 // pair) and returns the kernel that runs it.
+// Ring-order reduce-scatters at K = 8 with bf16 input that overwrite their
+// partitions take one-slice tiles (1024 elements, 4 KiB of fp32 output) at
+// any size: the static K = 8 kernel then runs at 42-50 VGPRs, eight waves per
+// SIMD, and on 500M-element buckets streamed 2-3% faster than with 16 KiB
+// tiles (two slices per wave ran slower than either). With fp32 input, or
+// reading the partition back, the four-slice tiles stayed 2-7% ahead, and so
+// did they for the discrete reduce-scatter of one layer's gradients (6%).
+template <typename TIn>
+constexpr bool ring_one_slice(int K, int order, bool accumulate) {
+    return order == kRing && K == 8 && sizeof(TIn) == 2 && !accumulate;
+}
+
 template <typename TIn, typename TOut>
 LaunchFn prepare_typed(RsArgs& a, int avg_mode, int order) {
     constexpr int64_t T = kRsTile<TIn, TOut>;
     const int fp = tuning().force_path;
     // fewer than two full tiles per CU for each eight ranks (a tile's bytes
-    // grow with K): one-slice tiles, four times as many
+    // grow with K), or a shape that streams faster so at any size
+    // (ring_one_slice): one-slice tiles, four times as many
     const int64_t k8 = (a.K + 7) / 8;
-    const bool small = order == kRing && (fp == kPathSmall ||
-                                          (fp != kPathLarge && ((a.C + T - 1) / T) * a.K < 2LL * k8 * device_cu_count()));
+    const bool small = order == kRing &&
+                       (fp == kPathSmall ||
+                        (fp != kPathLarge && (ring_one_slice<TIn>(a.K, order, a.accumulate != 0) ||
+                                              ((a.C + T - 1) / T) * a.K < 2LL * k8 * device_cu_count())));
     const int64_t Tl = small ? kRsTileOf<1>
                              : (rs_generic_narrow<TIn>(a.K, order) ? kRsTileOf<kSlicesGeneric<TIn, TOut>> : T);
     // Vector path: every base aligned for quad access (8 bytes for bf16

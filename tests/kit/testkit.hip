@@ -85,18 +85,19 @@ extern "C" int tk_read(const void* src, void* sink, long long bytes, int blocks,
 // practical ceiling of a stream with its read:write mix. K = 8 bf16 input
 // streams of n = 8 * C elements and 8 fp32 output streams of C elements; C is a
 // multiple of 4096, so every tile is whole, starts on a 128-byte line of every
-// input and writes an aligned 16 KiB block of its output. Tiles are numbered
-// as the reduce-scatter numbers them: by pairs of chunks, consecutive blocks
+// input and writes an aligned block of its output. Tiles are numbered as the
+// reduce-scatter numbers them: by pairs of chunks, consecutive blocks
 // alternating between the pair's two chunks, one block per tile. A tile is
-// 4 waves x 4 slices x 256 elements; lane l owns elements 4l..4l+3 of each
+// 4 waves x S slices x 256 elements (S = 1: 4 KiB of output, S = 4: 16 KiB,
+// the reduce-scatter's two tile shapes); lane l owns elements 4l..4l+3 of each
 // slice and loads them from every input with one 8-byte non-temporal load
-// (all 32 loads issued before the first use), then writes one 16-byte
+// (all 8 S loads issued before the first use), then writes one 16-byte
 // non-temporal store per slice to out_j. The stored words are the XOR of the
 // loaded ones, so no load can be removed and no floating-point add is made.
 //   mode 0: loads and stores (the reduce-scatter's 16 B read : 4 B written)
 //   mode 1: loads only (one 16-byte word per tile, written only when the
 //           XOR of the tile's data hits a fixed value, keeps the loads live)
-//   mode 2: stores only (the same 16 KiB output blocks, no loads)
+//   mode 2: stores only (the same output blocks, no loads)
 //   mode 3: mode 0 plus a 16-byte non-temporal load of each output word before
 //           its store, folded into the stored value (the accumulating
 //           reduce-scatter's 20 B read : 4 B written)
@@ -108,10 +109,11 @@ struct TkMixArgs {
     tk_u32x4* out[8];       // 8 outputs, C fp32 each (4 per 16-byte word)
     tk_u32x4* sink;         // mode 1: one word per tile
     long long C;            // chunk size (elements), a multiple of 4096
-    long long tpc;          // tiles per chunk, C / 4096
+    long long tpc;          // tiles per chunk, C / (1024 S)
     int mode;
 };
 
+template <int S>
 __global__ void __launch_bounds__(256) tk_mix_kernel(const TkMixArgs a) {
     const long long i = blockIdx.x;
     const long long per_pair = 2 * a.tpc;
@@ -120,23 +122,23 @@ __global__ void __launch_bounds__(256) tk_mix_kernel(const TkMixArgs a) {
     const int j = 2 * q + (int)(w & 1);
     const long long t = w >> 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const long long o0 = t * 4096 + wave * 1024 + lane * 4;  // element offset in the chunk
-    const long long g0 = (long long)j * a.C + o0;              // element index in the inputs
+    const long long o0 = t * (1024 * S) + wave * (256 * S) + lane * 4;  // element offset in the chunk
+    const long long g0 = (long long)j * a.C + o0;                        // element index in the inputs
     tk_u32x4* out = a.out[j];
     if (a.mode == 2) {
         const tk_u32x4 v = {(unsigned)o0, (unsigned)j, 0u, 0u};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(v, out + (o0 + 256 * k) / 4);
+        for (int k = 0; k < S; ++k) __builtin_nontemporal_store(v, out + (o0 + 256 * k) / 4);
         return;
     }
-    tk_u32x2 v[4][8];
+    tk_u32x2 v[S][8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < S; ++k)
 #pragma unroll
         for (int h = 0; h < 8; ++h) v[k][h] = __builtin_nontemporal_load(a.in[h] + (g0 + 256 * k) / 4);
-    tk_u32x4 x[4];
+    tk_u32x4 x[S];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < S; ++k) {
         tk_u32x2 y = v[k][0];
 #pragma unroll
         for (int h = 1; h < 8; ++h) y ^= v[k][h];
@@ -144,24 +146,27 @@ __global__ void __launch_bounds__(256) tk_mix_kernel(const TkMixArgs a) {
     }
     if (a.mode == 0) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(x[k], out + (o0 + 256 * k) / 4);
+        for (int k = 0; k < S; ++k) __builtin_nontemporal_store(x[k], out + (o0 + 256 * k) / 4);
         return;
     }
     if (a.mode == 3) {
-        tk_u32x4 old[4];
+        tk_u32x4 old[S];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) old[k] = __builtin_nontemporal_load(out + (o0 + 256 * k) / 4);
+        for (int k = 0; k < S; ++k) old[k] = __builtin_nontemporal_load(out + (o0 + 256 * k) / 4);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(x[k] ^ old[k], out + (o0 + 256 * k) / 4);
+        for (int k = 0; k < S; ++k) __builtin_nontemporal_store(x[k] ^ old[k], out + (o0 + 256 * k) / 4);
         return;
     }
-    const tk_u32x4 z = x[0] ^ x[1] ^ x[2] ^ x[3];
+    tk_u32x4 z = x[0];
+#pragma unroll
+    for (int k = 1; k < S; ++k) z ^= x[k];
     if (z.x == 0x9E3779B9u && z.y == 0x7F4A7C15u) a.sink[i] = z;
 }
 
 extern "C" int tk_mix(const void* const* in, void* const* out, void* sink, long long C, int mode,
-                      void* stream) {
+                      int slices, void* stream) {
     if (!in || !out || C <= 0 || (C % 4096) != 0 || mode < 0 || mode > 3) return 1;
+    if (slices != 1 && slices != 4) return 1;
     if (mode == 1 && !sink) return 1;
     TkMixArgs a;
     for (int r = 0; r < 8; ++r) {
@@ -171,10 +176,13 @@ extern "C" int tk_mix(const void* const* in, void* const* out, void* sink, long 
     }
     a.sink = (tk_u32x4*)sink;
     a.C = C;
-    a.tpc = C / 4096;
+    a.tpc = C / (1024LL * slices);
     a.mode = mode;
-    const long long blocks = 8 * a.tpc;
+    const long long blocks = 8 * a.tpc;  // mode 1's sink holds one 16-byte word per block
     if (blocks > (1LL << 30)) return 1;
-    hipLaunchKernelGGL(tk_mix_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
+    if (slices == 1)
+        hipLaunchKernelGGL(tk_mix_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL(tk_mix_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
