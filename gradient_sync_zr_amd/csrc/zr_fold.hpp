@@ -60,10 +60,12 @@ struct RingBases {
 };
 
 // ------------------------------------------------------------------ quads
-// Slices per wave of the reduce-scatter tiles (4 waves x S x 256 elements):
-// a tile writes 16 KiB of output, the size that streamed best (bf16 -> bf16
-// ran 5% and fp32 -> fp32 4% faster than with 8 KiB tiles), except fp32 input
-// with bf16 output, which keeps 2 slices (4 measured no faster).
+// Slices per wave of the full reduce-scatter tiles (4 waves x S x 256
+// elements): a tile writes 16 KiB of output, which streamed better than 8 KiB
+// (bf16 -> bf16 by 5%, fp32 -> fp32 by 4%), except fp32 input with bf16 output,
+// which keeps 2 slices (4 measured no faster). One-slice tiles (kRsTileOf<1>)
+// serve small launches and the shapes that stream faster with them (the
+// ring order at K = 8 with bf16 input, overwriting: ring_one_slice).
 template <typename TIn, typename TOut>
 constexpr int kSlices = sizeof(TOut) == 4 ? 4 : (sizeof(TIn) == 2 ? 8 : 2);
 // Non-temporal (streaming) loads and stores in the reduce-scatter kernels:
@@ -72,9 +74,9 @@ constexpr int kSlices = sizeof(TOut) == 4 ? 4 : (sizeof(TIn) == 2 ? 8 : 2);
 #define ZR_RS_NONTEMPORAL 1
 #endif
 constexpr bool kRsNontemporal = ZR_RS_NONTEMPORAL != 0;
-// Elements per reduce-scatter tile of S slices: 4 waves x S x 256. Launches
-// too small to give every CU two tiles use one slice per wave (four times as
-// many, shorter tiles), in the ring order.
+// Elements per reduce-scatter tile of S slices: 4 waves x S x 256. Ring-order
+// launches too small to give every CU two tiles use one slice per wave (four
+// times as many, shorter tiles).
 template <int S>
 constexpr int64_t kRsTileOf = (int64_t)(kThreads / 64) * S * 256;
 template <typename TIn, typename TOut>
