@@ -213,7 +213,7 @@ LaunchFn pick_k(int K, int order, bool small) {
     constexpr bool NT = kRsNontemporal;
     if (order == kFree) return &launch_t<TIn, TOut, 0, AVG, kFree, NT, SG>;
     if (order == kWire && sizeof(TIn) == 2) {
-        if (K == 8) return &launch_t<TIn, TOut, 8, AVG, kWire, NT, S>;
+        if (K == 8) return small ? &launch_t<TIn, TOut, 8, AVG, kWire, NT, 1> : &launch_t<TIn, TOut, 8, AVG, kWire, NT, S>;
         return &launch_t<TIn, TOut, 0, AVG, kWire, NT, SG>;
     }
     if (K == 8) return small ? &launch_t<TIn, TOut, 8, AVG, kRing, NT, 1> : &launch_t<TIn, TOut, 8, AVG, kRing, NT, S>;
@@ -231,16 +231,17 @@ LaunchFn pick_avg(int K, int avg_mode, int order, bool small) {
 
 // Fills the launch geometry of `a` (vector chunks, heads, tiles per chunk and
 // pair) and returns the kernel that runs it.
-// Ring-order reduce-scatters at K = 8 with bf16 input that overwrite their
-// partitions take one-slice tiles (1024 elements, 4 KiB of fp32 output) at
-// any size: the static K = 8 kernel then runs at 42-50 VGPRs, eight waves per
-// SIMD, and on 500M-element buckets streamed 2-3% faster than with 16 KiB
-// tiles (two slices per wave ran slower than either). With fp32 input, or
-// reading the partition back, the four-slice tiles stayed 2-7% ahead, and so
-// did they for the discrete reduce-scatter of one layer's gradients (6%).
+// Reduce-scatters at K = 8 with bf16 input in the ring order or its bf16-wire
+// variant that overwrite their partitions take one-slice tiles (1024
+// elements, 4 KiB of fp32 output) at any size: the static K = 8 kernels then
+// run at 42-50 VGPRs, eight waves per SIMD, and on 500M-element buckets
+// streamed 2-6% faster than with 16 KiB tiles (two slices per wave ran slower
+// than either). With fp32 input, or reading the partition back, the
+// four-slice tiles stayed 2-7% ahead, and so did they for the discrete
+// reduce-scatter of one layer's gradients (6%).
 template <typename TIn>
 constexpr bool ring_one_slice(int K, int order, bool accumulate) {
-    return order == kRing && K == 8 && sizeof(TIn) == 2 && !accumulate;
+    return (order == kRing || order == kWire) && K == 8 && sizeof(TIn) == 2 && !accumulate;
 }
 
 template <typename TIn, typename TOut>
@@ -251,7 +252,9 @@ LaunchFn prepare_typed(RsArgs& a, int avg_mode, int order) {
     // grow with K), or a shape that streams faster so at any size
     // (ring_one_slice): one-slice tiles, four times as many
     const int64_t k8 = (a.K + 7) / 8;
-    const bool small = order == kRing &&
+    // (the ring order, and the wire order's static K = 8 kernels)
+    const bool one_ok = order == kRing || (order == kWire && a.K == 8 && sizeof(TIn) == 2);
+    const bool small = one_ok &&
                        (fp == kPathSmall ||
                         (fp != kPathLarge && (ring_one_slice<TIn>(a.K, order, a.accumulate != 0) ||
                                               ((a.C + T - 1) / T) * a.K < 2LL * k8 * device_cu_count())));
