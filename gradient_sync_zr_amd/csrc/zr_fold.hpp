@@ -64,8 +64,8 @@ struct RingBases {
 // elements): a tile writes 16 KiB of output, which streamed better than 8 KiB
 // (bf16 -> bf16 by 5%, fp32 -> fp32 by 4%), except fp32 input with bf16 output,
 // which keeps 2 slices (4 measured no faster). One-slice tiles (kRsTileOf<1>)
-// serve small launches and the shapes that stream faster with them (the
-// ring order at K = 8 with bf16 input, overwriting: ring_one_slice).
+// serve small launches and the shapes that stream faster with them
+// (ring_one_slice in the reduce-scatter's launch code lists those).
 template <typename TIn, typename TOut>
 constexpr int kSlices = sizeof(TOut) == 4 ? 4 : (sizeof(TIn) == 2 ? 8 : 2);
 // Non-temporal (streaming) loads and stores in the reduce-scatter kernels:

@@ -231,17 +231,25 @@ LaunchFn pick_avg(int K, int avg_mode, int order, bool small) {
 
 // Fills the launch geometry of `a` (vector chunks, heads, tiles per chunk and
 // pair) and returns the kernel that runs it.
-// Reduce-scatters at K = 8 with bf16 input in the ring order or its bf16-wire
-// variant that overwrite their partitions take one-slice tiles (1024
-// elements, 4 KiB of fp32 output) at any size: the static K = 8 kernels then
-// run at 42-50 VGPRs, eight waves per SIMD, and on 500M-element buckets
-// streamed 2-6% faster than with 16 KiB tiles (two slices per wave ran slower
-// than either). With fp32 input, or reading the partition back, the
-// four-slice tiles stayed 2-7% ahead, and so did they for the discrete
-// reduce-scatter of one layer's gradients (6%).
-template <typename TIn>
+// Reduce-scatters with bf16 input that overwrite their partitions take
+// one-slice tiles (1024 elements, 4 KiB of fp32 output) at any size where
+// that streamed faster on 500M-element buckets:
+//  - K = 8, in the ring order or its bf16-wire variant (the static K = 8
+//    kernels, 42-50 VGPRs, eight waves per SIMD): 2-6% faster than 16 KiB
+//    tiles, for fp32 and bf16 output (two slices per wave ran slower than
+//    either);
+//  - 8 < K <= 32 with fp32 output, in the ring order (the generic kernel,
+//    32 ranks' loads in flight per batch): 2-3% faster at K = 16 and 32. With
+//    bf16 output K = 16 ran 2% slower, and below K = 8 one-slice tiles carry
+//    too little per block (2.1-2.8 TB/s at K = 2-4 against 5.1-5.5).
+// With fp32 input, or reading the partition back, the four-slice tiles stayed
+// 2-7% ahead, and so did they for the discrete reduce-scatter of one layer's
+// gradients (6%).
+template <typename TIn, typename TOut>
 constexpr bool ring_one_slice(int K, int order, bool accumulate) {
-    return (order == kRing || order == kWire) && K == 8 && sizeof(TIn) == 2 && !accumulate;
+    if (sizeof(TIn) != 2 || accumulate) return false;
+    if (K == 8) return order == kRing || order == kWire;
+    return order == kRing && sizeof(TOut) == 4 && K > 8 && K <= 32;
 }
 
 template <typename TIn, typename TOut>
@@ -256,7 +264,7 @@ LaunchFn prepare_typed(RsArgs& a, int avg_mode, int order) {
     const bool one_ok = order == kRing || (order == kWire && a.K == 8 && sizeof(TIn) == 2);
     const bool small = one_ok &&
                        (fp == kPathSmall ||
-                        (fp != kPathLarge && (ring_one_slice<TIn>(a.K, order, a.accumulate != 0) ||
+                        (fp != kPathLarge && (ring_one_slice<TIn, TOut>(a.K, order, a.accumulate != 0) ||
                                               ((a.C + T - 1) / T) * a.K < 2LL * k8 * device_cu_count())));
     const int64_t Tl = small ? kRsTileOf<1>
                              : (rs_generic_narrow<TIn>(a.K, order) ? kRsTileOf<kSlicesGeneric<TIn, TOut>> : T);
