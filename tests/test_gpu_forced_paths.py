@@ -3,8 +3,9 @@
 The reduce-scatter, discrete reduce-scatter, all-reduce and all-gather choose
 between 16-byte (quad) access and element-by-element folds or copies from
 their inputs' alignment, and the ring-order reduce-scatters choose one-slice
-tiles for launches too small to fill the GPU, and for K = 8 with bf16 input
-when the partitions are overwritten, and four-slice tiles otherwise.
+tiles for launches too small to fill the GPU and for the shapes that stream
+faster so (bf16 input at K = 8, bf16 -> fp32 up to K = 32, when the partitions
+are overwritten), and four-slice tiles otherwise.
 ZR_FORCE_PATH overrides those choices (read once per process, so each
 setting runs the whole bit-exact parity module, and the module of ranks in
 different phases, in a child process):
@@ -12,7 +13,7 @@ different phases, in a child process):
   element  every aligned case also goes element by element (with ZR_DEBUG=1,
            so every call waits for its stream and reports a kernel error
            itself);
-  large    small launches, and K = 8 with bf16 input, take four-slice tiles;
+  large    small launches, and the one-slice shapes above, take four-slice tiles;
   small    large launches take one-slice tiles.
 
 Ring-order results do not depend on the path, so every case must still be
