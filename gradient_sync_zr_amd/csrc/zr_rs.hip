@@ -238,10 +238,10 @@ LaunchFn pick_avg(int K, int avg_mode, int order, bool small) {
 //    kernels, 42-50 VGPRs, eight waves per SIMD): 2-6% faster than 16 KiB
 //    tiles, for fp32 and bf16 output (two slices per wave ran slower than
 //    either);
-//  - 8 < K <= 32 with fp32 output, in the ring order (the generic kernel,
-//    32 ranks' loads in flight per batch): 2-3% faster at K = 16 and 32. With
-//    bf16 output K = 16 ran 2% slower, and below K = 8 one-slice tiles carry
-//    too little per block (2.1-2.8 TB/s at K = 2-4 against 5.1-5.5).
+//  - K > 8 with fp32 output, in the ring order (the generic kernel, 32
+//    ranks' loads in flight per batch): 2-3% faster at K = 16, 32 and 64.
+//    With bf16 output K = 16 ran 2% slower, and below K = 8 one-slice tiles
+//    carry too little per block (2.1-2.8 TB/s at K = 2-4 against 5.1-5.5).
 // With fp32 input, or reading the partition back, the four-slice tiles stayed
 // 2-7% ahead, and so did they for the discrete reduce-scatter of one layer's
 // gradients (6%).
@@ -249,7 +249,7 @@ template <typename TIn, typename TOut>
 constexpr bool ring_one_slice(int K, int order, bool accumulate) {
     if (sizeof(TIn) != 2 || accumulate) return false;
     if (K == 8) return order == kRing || order == kWire;
-    return order == kRing && sizeof(TOut) == 4 && K > 8 && K <= 32;
+    return order == kRing && sizeof(TOut) == 4 && K > 8;
 }
 
 template <typename TIn, typename TOut>

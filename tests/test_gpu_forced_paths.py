@@ -4,7 +4,7 @@ The reduce-scatter, discrete reduce-scatter, all-reduce and all-gather choose
 between 16-byte (quad) access and element-by-element folds or copies from
 their inputs' alignment, and the ring-order reduce-scatters choose one-slice
 tiles for launches too small to fill the GPU and for the shapes that stream
-faster so (bf16 input at K = 8, bf16 -> fp32 up to K = 32, when the partitions
+faster so (bf16 input at K = 8, bf16 -> fp32 above K = 8, when the partitions
 are overwritten), and four-slice tiles otherwise.
 ZR_FORCE_PATH overrides those choices (read once per process, so each
 setting runs the whole bit-exact parity module, and the module of ranks in
