@@ -76,8 +76,23 @@ def sampled_rs_want(K, N, C, value_at, rng, shift, average):
 
 
 def test_reduce_scatter_past_2e31():
+    _reduce_scatter_past_2e31(8, BIG)
+
+
+@pytest.mark.parametrize("K", [8, 16])
+def test_reduce_scatter_vector_path_past_2e31(K):
+    """Chunks on the quad grid (C a multiple of 4, N three short of K*C), so
+    every chunk takes the contiguous kernel's vector path: at K = 8 the static
+    one-slice kernel, at K = 16 the generic one. (BIG's chunks start off the
+    grid, which routes the call through the discrete kernel.)"""
+    C = -(-(1 << 31) // K)
+    C += (-C) % 4 + 4
+    _reduce_scatter_past_2e31(K, K * C - 3)
+
+
+def _reduce_scatter_past_2e31(K, N):
     import torch
-    K, N, shift = 8, BIG, 1
+    shift = 1
     C = -(-N // K)
     say(f"large rs: K={K} N={N}")
     xs = [torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
