@@ -13,9 +13,13 @@
 //
 // Waits that stream order already implies are not enqueued: a producer that
 // is the reduction stream itself, and a producer that waited in a flush on a
-// tail recorded after the buffer's reduction. (Every wait and record is a
-// packet its stream processes in order: skipping these took a 5-bucket sync
-// on the caller's stream from about 45 to 25 us per step above bare
+// tail recorded after the buffer's reduction. Until some other stream has
+// produced, no buffer's completion event is recorded either: if one later
+// must wait on a buffer whose event was never recorded, the event is
+// recorded at that point, after every reduction submitted so far (a wait
+// that may be longer than needed, once per buffer). (Every wait and record is
+// a packet its stream processes in order: skipping the waits took a 5-bucket
+// sync on the caller's stream from about 45 to 25 us per step above bare
 // back-to-back launches; on two streams the cross-stream waits cost about
 // 75 us per step.)
 //
@@ -84,8 +88,14 @@ class SchedCore {
         if (buf < 0 || buf >= (int)bufs_.size()) return SchedErr::kBadBuf;
         Buf& b = bufs_[buf];
         if (b.state == State::kAcquired) return SchedErr::kBadState;
-        if (b.state == State::kSubmitted && !ordered_after(producer, b.seq) && be_.wait(producer, b.done))
-            return SchedErr::kBackend;
+        if (b.state == State::kSubmitted && !ordered_after(producer, b.seq)) {
+            foreign_ = true;  // not the reduction stream, which is always ordered
+            if (!b.recorded) {
+                if (be_.record(b.done, red_)) return SchedErr::kBackend;
+                b.recorded = true;
+            }
+            if (be_.wait(producer, b.done)) return SchedErr::kBackend;
+        }
         b.state = State::kAcquired;
         return SchedErr::kOk;
     }
@@ -103,11 +113,16 @@ class SchedCore {
         if (n_prod > 0 && !producers) return SchedErr::kBadArg;
         for (int i = 0; i < n_prod; ++i) {
             if (producers[i] == red_) continue;  // the reduction stream itself: stream order
+            foreign_ = true;
             if (be_.record(b.prod[i], producers[i])) return SchedErr::kBackend;
             if (be_.wait(red_, b.prod[i])) return SchedErr::kBackend;
         }
         if (!launch(red_)) return SchedErr::kBackend;
-        if (be_.record(b.done, red_)) return SchedErr::kBackend;
+        b.recorded = false;
+        if (foreign_) {
+            if (be_.record(b.done, red_)) return SchedErr::kBackend;
+            b.recorded = true;
+        }
         b.state = State::kSubmitted;
         b.seq = ++seq_;
         any_submitted_ = true;
@@ -139,6 +154,7 @@ class SchedCore {
         unsigned long long seq = 0;  // submission number of its last reduction
         Event done{};
         bool has_done = false;
+        bool recorded = false;  // done holds a record made after the last reduction
         std::vector<Event> prod;
         int n_prod_created = 0;
     };
@@ -153,6 +169,7 @@ class SchedCore {
     Stream flushed_{};                    // the stream the last flush made wait
     unsigned long long flushed_seq_ = 0;  // ... for every reduction up to this one
     bool has_flushed_ = false;
+    bool foreign_ = false;  // a stream other than the reduction stream has produced
 };
 
 }  // namespace zr

@@ -358,7 +358,7 @@ def test_a_flush_into_another_stream_does_not_cover_the_producer():
 
 def test_producer_on_the_reduction_stream_needs_no_events():
     # reductions on the caller's own stream: stream order covers every
-    # dependency, so only the buffers' completion events are recorded
+    # dependency, so nothing is recorded and nothing waited on
     p = Program()
     for i in range(6):
         b = i % 2
@@ -366,8 +366,29 @@ def test_producer_on_the_reduction_stream_needs_no_events():
         p.write(RED, b)
         assert p.submit(b, [RED]) == OK
     assert p.flush(RED) == OK
-    assert p.waits == []
-    done_events = {e for (e, s) in p.records}
-    assert all(s == RED for (_, s) in p.records) and len(done_events) == 2
+    assert p.waits == [] and p.records == []
+    check_reuse_ordered(p)
+    p.close()
+
+
+def test_a_first_other_producer_waits_on_an_event_recorded_late():
+    # steps on the reduction stream record no completion events; when another
+    # stream then overwrites a buffer, the event is recorded at that point
+    # (after every reduction so far) and the reuse stays ordered; from then on
+    # completion events are recorded at submission again
+    p = Program()
+    for i in range(4):
+        b = i % 2
+        assert p.acquire(b, RED) == OK
+        p.write(RED, b)
+        assert p.submit(b, [RED]) == OK
+    assert p.records == []
+    for i in range(4):
+        b = i % 2
+        assert p.acquire(b, 1) == OK
+        p.write(1, b)
+        assert p.submit(b, [1]) == OK
+    assert p.flush(1) == OK
+    assert any(s == RED for (_, s) in p.records)
     check_reuse_ordered(p)
     p.close()
