@@ -411,11 +411,16 @@ zr_status zr_rsf_plan_destroy(zr_rsf_plan* plan);
  * name the physical IPG buffers (2 = ping-pong). Life of a buffer index:
  *   zr_sched_acquire(buf, producer): the producer stream waits on the event
  *       recorded after the last reduction that read this buffer, and on
- *       nothing else; the producer may then write the buffer;
+ *       nothing else (not at all when the producer is the reduction stream,
+ *       or a stream that a flush already ordered after that reduction); the
+ *       producer may then write the buffer;
  *   zr_sched_submit_rs(buf, producers, ...): the reduction stream waits on
- *       every listed producer stream (all streams that wrote the bucket),
- *       runs zr_reduce_scatter_avg, and records the buffer's completion
- *       event;
+ *       every listed producer stream (all streams that wrote the bucket;
+ *       the reduction stream itself needs no wait), runs
+ *       zr_reduce_scatter_avg, and records the buffer's completion event.
+ *       Until a stream other than the reduction stream has produced, no
+ *       completion event is recorded; an acquire that then needs one
+ *       records it at that point, after every reduction submitted so far;
  *   zr_sched_flush(caller): the caller stream waits for all reduction work
  *       submitted so far (epilogue of the backward pass).
  * acquire on a buffer already acquired, or submit on one not acquired, is
